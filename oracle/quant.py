@@ -1,0 +1,78 @@
+"""O1: 4-bit substitute weights (uniform, asymmetric, group-wise).
+
+Follows [SSN] Method details, "substitute layer generation": a substitute is
+the target layer itself with its weights held at low precision, built with a
+plain uniform quantiser that needs no calibration data; [SSR] section 2.2 step
+four fixes 4 bits.  The pages leave the group axis, group size, zero-point
+form and rounding open; the reading used here:
+
+  * groups of 64 consecutive weights along the input (K) axis of each row;
+  * lo = min, hi = max of the group (float32 values of the bf16 weights);
+  * scale s = fp16(fl32(fl32(hi - lo) / 15)); s := 1 when that is 0, and
+    saturates to the fp16 maximum instead of overflowing;
+  * offset m = fp16(lo) (saturating);
+  * code q = clamp(rint_even(fl32(fl32(x - m) / s)), 0, 15) with s, m the
+    *stored* fp16 values read back as float32 (no fused multiply-add);
+  * dequantised weight  w_hat = q * s + m.
+
+Storage: ``codes`` uint8 [N][K/2], byte j = q[2j] | q[2j+1] << 4;
+``meta`` float16 [N][K/64][2] = (s, m).
+
+Pinned by: the hand-built group whose values sit exactly on the 16 levels,
+the brute-force nearest level on small inputs, the round-trip bound
+|x - w_hat| <= s/2, the degenerate constant group and the byte packing.
+"""
+import numpy as np
+
+GROUP = 64
+LEVELS = 15
+FP16_MAX = np.float32(65504.0)
+
+
+def _to_fp16_saturating(v):
+    v = np.asarray(v, dtype=np.float32)
+    return np.clip(v, -FP16_MAX, FP16_MAX).astype(np.float16)
+
+
+def quantize(w, group=GROUP):
+    """Quantise a [N][K] matrix of bf16 values (given as float32/float64)."""
+    w = np.asarray(w, dtype=np.float32)
+    n, k = w.shape
+    if k % group != 0:
+        raise ValueError("K must be a multiple of the group size")
+    g = w.reshape(n, k // group, group)
+    lo = g.min(axis=2)
+    hi = g.max(axis=2)
+    span = (hi - lo).astype(np.float32)                       # fl32 subtraction
+    s32 = (span / np.float32(LEVELS)).astype(np.float32)       # fl32 division
+    s16 = _to_fp16_saturating(s32)
+    s16 = np.where(s16 == 0, np.float16(1.0), s16)
+    m16 = _to_fp16_saturating(lo)
+    s = s16.astype(np.float32)[:, :, None]
+    m = m16.astype(np.float32)[:, :, None]
+    t = ((g - m).astype(np.float32) / s).astype(np.float32)   # two fl32 ops, no FMA
+    q = np.clip(np.rint(t), 0, LEVELS).astype(np.uint8)       # rint rounds half to even
+    q = q.reshape(n, k)
+    codes = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    meta = np.stack([s16, m16], axis=2).astype(np.float16)
+    return codes, meta
+
+
+def unpack_codes(codes):
+    """uint8 [N][K/2] -> integer codes [N][K]."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    n, kh = codes.shape
+    q = np.empty((n, 2 * kh), dtype=np.uint8)
+    q[:, 0::2] = codes & 0x0F
+    q[:, 1::2] = codes >> 4
+    return q
+
+
+def dequantize(codes, meta, group=GROUP):
+    """w_hat = q * s + m, in float64."""
+    q = unpack_codes(codes).astype(np.float64)
+    n, k = q.shape
+    meta = np.asarray(meta, dtype=np.float16).astype(np.float64)
+    s = np.repeat(meta[:, :, 0], group, axis=1)
+    m = np.repeat(meta[:, :, 1], group, axis=1)
+    return q * s + m
