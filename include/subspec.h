@@ -1,0 +1,232 @@
+/*
+ * subspec.h - C ABI of libsubspec.so: the hot path of self-speculative decoding
+ * with a 4-bit (W4A16) substitute draft, for one AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   [SD]  "How speculative decoding makes LLMs go brrr" (digest): overall flow
+ *         and pseudo-code of one speculative step; Module 1 (drafter returns
+ *         gamma candidates and q(x)); Module 2 (one causal target forward over
+ *         gamma+1 positions, KV rollback); Module 3 (rejection sampling).
+ *   [SSN] "SubSpec: Speculate Deep and Accurate" (paper note), Method details:
+ *         substitute layers are the target's own layers quantised without
+ *         calibration data; resident layers and the KV cache are shared.
+ *   [SSR] "SubSpec: the target's own low-bit shadow as the draft" (report),
+ *         section 2.2 (4-bit substitutes, sharpened draft), section 3.2
+ *         (greedy verification, Table 1).
+ *
+ * Conventions shared by every entry point
+ *   - All buffer pointers are DEVICE pointers unless stated otherwise; the
+ *     caller allocates and frees them.  The library allocates nothing.
+ *   - bf16 values are passed as uint16_t bit patterns, fp16 as uint16_t.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns; outputs are valid after the stream
+ *     has been synchronised.
+ *   - Return value: SUBSPEC_OK (0) or a negative error code.  On an argument,
+ *     shape, capacity or workspace error NOTHING is enqueued and
+ *     subspec_last_error() describes the problem.  A HIP launch failure
+ *     returns SUBSPEC_EHIP (work enqueued before it is not rolled back).
+ *   - Scratch memory comes from the caller's workspace `ws` of `ws_bytes`
+ *     bytes (see subspec_workspace_bytes).  It must be zero-filled once with
+ *     subspec_workspace_init before first use; kernels leave the counters in
+ *     it at zero again.  Calls that share one workspace must be ordered on
+ *     one stream.
+ *   - Uniform random numbers are passed as integer codes U in [0, 2^24),
+ *     meaning u = U / 2^24.
+ */
+#ifndef SUBSPEC_H
+#define SUBSPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SUBSPEC_ABI_VERSION 1
+
+enum {
+  SUBSPEC_OK = 0,
+  SUBSPEC_EINVAL = -1,       /* NULL pointer or out-of-range scalar          */
+  SUBSPEC_ESHAPE = -2,       /* dimensions the kernels do not support        */
+  SUBSPEC_ECAPACITY = -3,    /* KV capacity or token buffer too small         */
+  SUBSPEC_EHIP = -4,         /* a HIP runtime call failed                     */
+  SUBSPEC_EUNSUPPORTED = -5, /* a parameter value this build does not handle  */
+  SUBSPEC_EWORKSPACE = -6    /* workspace NULL or smaller than required       */
+};
+
+/* status bits written by subspec_reject */
+enum {
+  SUBSPEC_STATUS_NONFINITE = 1,     /* a non-finite logit in a row that was read  */
+  SUBSPEC_STATUS_ZERO_RESIDUAL = 2, /* max(0,p-q) had no mass; drew from p        */
+  SUBSPEC_STATUS_Q_ZERO = 4         /* a draft token had q(x) = 0                  */
+};
+
+/* Library ABI version (SUBSPEC_ABI_VERSION of the build). */
+int subspec_abi_version(void);
+
+/* Message of the last failing call made by this host thread ("" if none). */
+const char *subspec_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Model description (host structs holding device pointers)                 */
+/* ------------------------------------------------------------------------ */
+
+/* One linear layer y = W x with W of shape [n][k] (row n = output n).
+ * Exactly one of the two forms is set:
+ *   bf16:  w     = bf16 [n][k] row-major, codes = meta = NULL;
+ *   W4:    codes = uint8 [n][k/2], byte j of a row = q[2j] | q[2j+1] << 4,
+ *          meta  = fp16 [n][k/64][2] = {scale, min} of each 64-group along k;
+ *          the weight is q * scale + min (see subspec_quantize); w = NULL.   */
+typedef struct {
+  const uint16_t *w;
+  const uint8_t *codes;
+  const uint16_t *meta;
+  int64_t n, k;
+} subspec_linear;
+
+/* One decoder layer ([SSN] Method details: a substitute keeps the layer's
+ * structure).  The target (verify) weights are always bf16.  The draft
+ * weights are the W4 substitutes, or the same bf16 pointers for a layer the
+ * draft shares with the target.
+ *   qkv     [(Hq + 2 Hkv) d][H]  rows: all q heads, then k heads, then v heads
+ *   o       [H][Hq d]
+ *   gate_up [2 F][H]             rows 0..F-1 gate, rows F..2F-1 up
+ *   down    [H][F]                                                         */
+typedef struct {
+  const uint16_t *attn_norm, *ffn_norm; /* bf16 [H] RMSNorm weights */
+  subspec_linear qkv, o, gate_up, down;
+  subspec_linear qkv_d, o_d, gate_up_d, down_d;
+} subspec_layer;
+
+typedef struct {
+  int32_t n_layers, hidden, ffn, n_q_heads, n_kv_heads, head_dim, vocab;
+  float rope_theta, rms_eps;
+  const uint16_t *embed;      /* bf16 [vocab][hidden]  */
+  const uint16_t *final_norm; /* bf16 [hidden]         */
+  const uint16_t *lm_head;    /* bf16 [vocab][hidden]  */
+  const subspec_layer *layers; /* HOST array [n_layers] */
+} subspec_model;
+
+/* Decode state shared by draft and verify ([SSN]: one KV cache).
+ *   k_cache, v_cache  bf16 [n_layers][Hkv][capacity][head_dim]
+ *   kv_len            device int32: positions [0, kv_len) hold committed
+ *                     target K/V; the last committed token is tokens[0] and
+ *                     has not been run yet (kv_len = committed - 1)
+ *   tokens            device int32 [gamma_max + 1]: [0] last committed token,
+ *                     [1..gamma] the draft tokens of the current cycle
+ *   draft_logits      device bf16 [gamma_max][vocab]: row i = logits the
+ *                     draft produced at step i (the distribution of tokens[i+1]) */
+typedef struct {
+  uint16_t *k_cache, *v_cache;
+  int32_t capacity;
+  int32_t *kv_len;
+  int32_t *tokens;
+  uint16_t *draft_logits;
+  int32_t gamma_max;
+} subspec_state;
+
+/* Bytes of workspace needed for calls on `m` with at most `max_tokens`
+ * positions per verify call and a KV capacity of `capacity`.  Returns 0 if
+ * the model description is invalid (see subspec_last_error). */
+size_t subspec_workspace_bytes(const subspec_model *m, int32_t max_tokens, int32_t capacity);
+
+/* Zero-fill a workspace (a fill kernel; safe inside stream capture). */
+int subspec_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Substitute construction  ([SSN] Method details; [SSR] section 2.2)        */
+/* ------------------------------------------------------------------------ */
+
+/* Quantise a bf16 [n][k] matrix to 4-bit uniform asymmetric codes, groups of
+ * `group` = 64 consecutive weights along k.  Per group: lo/hi = min/max,
+ * scale = fp16(fl32(fl32(hi-lo)/15)) (1 if that is 0; saturating), min =
+ * fp16(lo) (saturating), code = clamp(rint_even(fl32(fl32(x-min)/scale)),
+ * 0, 15) using the stored fp16 values, no fused multiply-add.
+ * Outputs: codes uint8 [n][k/2], meta fp16 [n][k/64][2].  k % 64 == 0,
+ * bits == 4, group == 64; otherwise SUBSPEC_EUNSUPPORTED / SUBSPEC_ESHAPE. */
+int subspec_quantize(const uint16_t *w, int64_t n, int64_t k, int32_t group, int32_t bits,
+                     uint8_t *codes, uint16_t *meta, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* The speculative cycle  ([SD] pseudo-code)                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Draft step `step` (0 <= step < gamma_max): run tokens[step] at position
+ * kv_len + step through the draft (substitute and shared layers), write its
+ * K/V into the shared cache at that position, store the logits in
+ * draft_logits[step] and the drawn token in tokens[step + 1].  The token is
+ * the argmax (lowest index on ties) when draft_temp == 0, else the inverse
+ * CDF of softmax(logits / draft_temp) at u = u_codes[step] / 2^24
+ * ([SSR] section 3.4: sharpened draft).  u_codes: device uint32 [> step].
+ * Needs kv_len + step < capacity (checked on the device: out-of-range
+ * positions are skipped and tokens[step+1] is set to -1). */
+int subspec_draft_step(const subspec_model *m, const subspec_state *st, int32_t step,
+                       float draft_temp, const uint32_t *u_codes, void *ws, size_t ws_bytes,
+                       void *stream);
+
+/* Verify ([SD] Module 2): run `n_tokens` tokens (device int32 [n_tokens]) at
+ * positions kv_len .. kv_len + n_tokens - 1 through the bf16 target in one
+ * causal pass (row j attends to [0, kv_len + j]); overwrite those K/V
+ * entries with the target's; write logits bf16 [n_tokens][vocab] unless
+ * `logits` is NULL (prefill).  1 <= n_tokens <= max_tokens of the workspace. */
+int subspec_verify(const subspec_model *m, const subspec_state *st, int32_t n_tokens,
+                   const int32_t *tokens, uint16_t *logits, void *ws, size_t ws_bytes,
+                   void *stream);
+
+/* One rejection round ([SD] Module 3; [SSR] section 3.2 for T = 0).
+ *   target_logits bf16 [gamma+1][vocab]; draft_logits bf16 [gamma][vocab];
+ *   draft_tokens int32 [gamma]; r_codes uint32 [gamma]; u_code uint32 [1].
+ * For i = 0..gamma-1 draft_tokens[i] is accepted iff r_i < p_i(x)/q_i(x),
+ * with p_i = softmax(target_logits[i]/temp) (one-hot argmax if temp == 0)
+ * and q_i = softmax(draft_logits[i]/draft_temp) (one-hot argmax if
+ * draft_temp == 0).  At the first rejection n = i and one token is drawn
+ * from norm(max(0, p_i - q_i)); if all are accepted n = gamma and the bonus
+ * token is drawn from p_gamma.  Weights are exp((z - max)/T) in float32,
+ * truncated to integers floor(w * 2^40) so that every sum and comparison is
+ * exact; draws use the inverse CDF at u_code.
+ * Outputs (device): n_accepted int32 [1]; out_tokens int32 [gamma+1], first
+ * n+1 valid; status int32 [1] (SUBSPEC_STATUS_* bits); probs float [gamma][2]
+ * = (p_i(x_i), q_i(x_i)) for i <= n (optional, may be NULL).
+ * 0 <= gamma <= 64, 1 <= vocab <= 2^24. */
+int subspec_reject(int32_t gamma, int32_t vocab, float temp, float draft_temp,
+                   const uint16_t *target_logits, const uint16_t *draft_logits,
+                   const int32_t *draft_tokens, const uint32_t *r_codes, const uint32_t *u_code,
+                   int32_t *n_accepted, int32_t *out_tokens, int32_t *status, float *probs,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/* Commit a round ([SD] Module 2: discard the K/V of rejected positions):
+ * kv_len += n + 1 and tokens[0] = out_tokens[n], n = *n_accepted (device). */
+int subspec_kv_rollback(const subspec_state *st, const int32_t *n_accepted,
+                        const int32_t *out_tokens, void *stream);
+
+/* kv_len += delta (device), e.g. after a prefill chunk run through verify. */
+int subspec_kv_advance(const subspec_state *st, int32_t delta, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Kernel-level entry points (single operations of the path)                 */
+/* ------------------------------------------------------------------------ */
+
+/* y[n] = bf16( sum_k (q[n][k] * scale + min) * x[k] ) at batch 1 (the draft's
+ * W4A16 GEMV).  x bf16 [k], y bf16 [n]; k % 64 == 0. */
+int subspec_w4_gemv(const uint8_t *codes, const uint16_t *meta, int64_t n, int64_t k,
+                    const uint16_t *x, uint16_t *y, void *stream);
+
+/* y[n] = bf16( sum_k w[n][k] x[k] ), bf16 weights at batch 1; k % 8 == 0. */
+int subspec_bf16_gemv(const uint16_t *w, int64_t n, int64_t k, const uint16_t *x, uint16_t *y,
+                      void *stream);
+
+/* Y[t][n] = bf16( sum_k X[t][k] W[n][k] ) for t < m <= 64 (the verify GEMM
+ * on matrix cores).  X bf16 [m][k], Y bf16 [m][n]; k % 128 == 0. */
+int subspec_bf16_gemm(const uint16_t *w, int64_t n, int64_t k, const uint16_t *x, int32_t m,
+                      uint16_t *y, void *ws, size_t ws_bytes, void *stream);
+
+/* Draw one token from bf16 logits [vocab] as subspec_draft_step does
+ * (argmax if temp == 0, else inverse CDF at u_code/2^24); token int32 [1]. */
+int subspec_sample(const uint16_t *logits, int32_t vocab, float temp, const uint32_t *u_code,
+                   int32_t *token, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SUBSPEC_H */

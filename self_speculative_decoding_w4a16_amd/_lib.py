@@ -1,0 +1,193 @@
+"""ctypes binding of libsubspec.so (include/subspec.h).
+
+Argument marshalling only: every function here forwards to the C ABI; the
+work runs in the library's HIP kernels.  Importing this module does not load
+the library; :func:`lib` does, and raises if it has not been built.
+"""
+import ctypes
+import os
+from ctypes import POINTER, c_float, c_int32, c_int64, c_size_t, c_uint32, c_void_p
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsubspec.so")
+
+OK = 0
+EINVAL = -1
+ESHAPE = -2
+ECAPACITY = -3
+EHIP = -4
+EUNSUPPORTED = -5
+EWORKSPACE = -6
+
+STATUS_NONFINITE = 1
+STATUS_ZERO_RESIDUAL = 2
+STATUS_Q_ZERO = 4
+
+
+class SubspecError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"libsubspec error {code}: {msg}")
+        self.code = code
+
+
+class Linear(ctypes.Structure):
+    _fields_ = [("w", c_void_p), ("codes", c_void_p), ("meta", c_void_p),
+                ("n", c_int64), ("k", c_int64)]
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("attn_norm", c_void_p), ("ffn_norm", c_void_p),
+                ("qkv", Linear), ("o", Linear), ("gate_up", Linear), ("down", Linear),
+                ("qkv_d", Linear), ("o_d", Linear), ("gate_up_d", Linear), ("down_d", Linear)]
+
+
+class Model(ctypes.Structure):
+    _fields_ = [("n_layers", c_int32), ("hidden", c_int32), ("ffn", c_int32),
+                ("n_q_heads", c_int32), ("n_kv_heads", c_int32), ("head_dim", c_int32),
+                ("vocab", c_int32), ("rope_theta", c_float), ("rms_eps", c_float),
+                ("embed", c_void_p), ("final_norm", c_void_p), ("lm_head", c_void_p),
+                ("layers", POINTER(Layer))]
+
+
+class State(ctypes.Structure):
+    _fields_ = [("k_cache", c_void_p), ("v_cache", c_void_p), ("capacity", c_int32),
+                ("kv_len", c_void_p), ("tokens", c_void_p), ("draft_logits", c_void_p),
+                ("gamma_max", c_int32)]
+
+
+_SIGS = {
+    "subspec_abi_version": (c_int32, []),
+    "subspec_last_error": (ctypes.c_char_p, []),
+    "subspec_workspace_bytes": (c_size_t, [POINTER(Model), c_int32, c_int32]),
+    "subspec_workspace_init": (c_int32, [c_void_p, c_size_t, c_void_p]),
+    "subspec_quantize": (c_int32, [c_void_p, c_int64, c_int64, c_int32, c_int32, c_void_p,
+                                   c_void_p, c_void_p]),
+    "subspec_draft_step": (c_int32, [POINTER(Model), POINTER(State), c_int32, c_float, c_void_p,
+                                     c_void_p, c_size_t, c_void_p]),
+    "subspec_verify": (c_int32, [POINTER(Model), POINTER(State), c_int32, c_void_p, c_void_p,
+                                 c_void_p, c_size_t, c_void_p]),
+    "subspec_reject": (c_int32, [c_int32, c_int32, c_float, c_float, c_void_p, c_void_p, c_void_p,
+                                 c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_void_p, c_size_t, c_void_p]),
+    "subspec_kv_rollback": (c_int32, [POINTER(State), c_void_p, c_void_p, c_void_p]),
+    "subspec_kv_advance": (c_int32, [POINTER(State), c_int32, c_void_p]),
+    "subspec_w4_gemv": (c_int32, [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p,
+                                  c_void_p]),
+    "subspec_bf16_gemv": (c_int32, [c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
+    "subspec_bf16_gemm": (c_int32, [c_void_p, c_int64, c_int64, c_void_p, c_int32, c_void_p,
+                                    c_void_p, c_size_t, c_void_p]),
+    "subspec_sample": (c_int32, [c_void_p, c_int32, c_float, c_void_p, c_void_p, c_void_p,
+                                 c_size_t, c_void_p]),
+}
+
+EXPORTS = tuple(_SIGS)
+
+_lib = None
+
+
+def lib():
+    """Load libsubspec.so (once).  Raises if the library has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m self_speculative_decoding_w4a16_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def last_error():
+    return lib().subspec_last_error().decode()
+
+
+def check(code):
+    if code != OK:
+        raise SubspecError(code, last_error())
+    return code
+
+
+def _p(t):
+    """Device (or host) pointer of a tensor, or None."""
+    return None if t is None else c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return c_void_p(torch.cuda.current_stream().cuda_stream)
+    return c_void_p(stream)
+
+
+# ---------------------------------------------------------------- entry points
+def abi_version():
+    return lib().subspec_abi_version()
+
+
+def workspace_bytes(model, max_tokens, capacity):
+    n = lib().subspec_workspace_bytes(ctypes.byref(model), max_tokens, capacity)
+    if n == 0:
+        raise SubspecError(EINVAL, last_error())
+    return n
+
+
+def workspace_init(ws, stream=None):
+    check(lib().subspec_workspace_init(_p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def quantize(w, codes, meta, group=64, bits=4, stream=None):
+    n, k = w.shape
+    check(lib().subspec_quantize(_p(w), n, k, group, bits, _p(codes), _p(meta), _stream(stream)))
+
+
+def draft_step(model, state, step, draft_temp, u_codes, ws, stream=None):
+    check(lib().subspec_draft_step(ctypes.byref(model), ctypes.byref(state), step, draft_temp,
+                                   _p(u_codes), _p(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)))
+
+
+def verify(model, state, n_tokens, tokens, logits, ws, stream=None):
+    check(lib().subspec_verify(ctypes.byref(model), ctypes.byref(state), n_tokens, _p(tokens),
+                               _p(logits), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def reject(gamma, vocab, temp, draft_temp, target_logits, draft_logits, draft_tokens, r_codes,
+           u_code, n_accepted, out_tokens, status, probs, ws, stream=None):
+    check(lib().subspec_reject(gamma, vocab, temp, draft_temp, _p(target_logits), _p(draft_logits),
+                               _p(draft_tokens), _p(r_codes), _p(u_code), _p(n_accepted),
+                               _p(out_tokens), _p(status), _p(probs), _p(ws),
+                               ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def kv_rollback(state, n_accepted, out_tokens, stream=None):
+    check(lib().subspec_kv_rollback(ctypes.byref(state), _p(n_accepted), _p(out_tokens),
+                                    _stream(stream)))
+
+
+def kv_advance(state, delta, stream=None):
+    check(lib().subspec_kv_advance(ctypes.byref(state), delta, _stream(stream)))
+
+
+def w4_gemv(codes, meta, n, k, x, y, stream=None):
+    check(lib().subspec_w4_gemv(_p(codes), _p(meta), n, k, _p(x), _p(y), _stream(stream)))
+
+
+def bf16_gemv(w, x, y, stream=None):
+    n, k = w.shape
+    check(lib().subspec_bf16_gemv(_p(w), n, k, _p(x), _p(y), _stream(stream)))
+
+
+def bf16_gemm(w, x, y, ws, stream=None):
+    n, k = w.shape
+    m = x.shape[0]
+    check(lib().subspec_bf16_gemm(_p(w), n, k, _p(x), m, _p(y), _p(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def sample(logits, temp, u_code, token, ws, stream=None):
+    check(lib().subspec_sample(_p(logits), logits.numel(), temp, _p(u_code), _p(token), _p(ws),
+                               ws.numel() * ws.element_size(), _stream(stream)))

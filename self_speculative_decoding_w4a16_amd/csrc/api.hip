@@ -1,0 +1,521 @@
+// Host side of libsubspec: argument validation, workspace carving and the
+// launch sequence of each entry point declared in include/subspec.h.
+//
+// Workspace layout (every entry point): a fixed 64 KiB block of arrival
+// counters at offset 0 (zero-filled once by subspec_workspace_init, left at
+// zero by every kernel that uses it), followed by call-local scratch whose
+// layout depends on the call (nothing in it survives between calls).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+
+#include "../../include/subspec.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return SUBSPEC_OK;
+}
+
+#define HIPCHK(expr)                                                                   \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess) return fail(SUBSPEC_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr size_t kCounterBytes = 64 * 1024;
+constexpr size_t kGemmCounterOff = 0;           // 4096 slots
+constexpr size_t kSampleCounterOff = 16 * 1024;
+constexpr size_t kRejectCounterOff = 16 * 1024 + 256;
+constexpr int kMaxGemmCounters = 4096;
+constexpr int kMaxTokens = 64;
+constexpr int kMaxGemvK = 28672;  // x (2 B) + half-group sums in 64 KiB of LDS
+constexpr int kMaxGamma = 64;
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Carver {
+  char* base;
+  size_t off;
+  void* take(size_t bytes) {
+    void* p = base ? base + off : nullptr;
+    off = align256(off + bytes);
+    return p;
+  }
+};
+
+hipStream_t hs(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// ------------------------------------------------------------------ validation
+bool lin_is_bf16(const subspec_linear& l) { return l.w && !l.codes && !l.meta; }
+bool lin_is_w4(const subspec_linear& l) { return !l.w && l.codes && l.meta; }
+
+int check_linear(const subspec_linear& l, int64_t n, int64_t k, bool allow_w4, const char* what,
+                 int layer) {
+  if (l.n != n || l.k != k)
+    return fail(SUBSPEC_ESHAPE, "layer %d %s: shape [%lld][%lld], expected [%lld][%lld]", layer,
+                what, (long long)l.n, (long long)l.k, (long long)n, (long long)k);
+  if (lin_is_bf16(l)) return SUBSPEC_OK;
+  if (allow_w4 && lin_is_w4(l)) return SUBSPEC_OK;
+  return fail(SUBSPEC_EINVAL, "layer %d %s: set exactly one of w (bf16)%s", layer, what,
+              allow_w4 ? " or codes+meta (W4)" : "");
+}
+
+int check_model(const subspec_model* m) {
+  if (!m) return fail(SUBSPEC_EINVAL, "model is NULL");
+  if (m->n_layers < 1 || m->hidden <= 0 || m->ffn <= 0 || m->vocab <= 0 || m->n_q_heads <= 0 ||
+      m->n_kv_heads <= 0)
+    return fail(SUBSPEC_EINVAL, "model dimensions must be positive");
+  if (m->head_dim != 128) return fail(SUBSPEC_EUNSUPPORTED, "head_dim must be 128");
+  if (m->n_q_heads % m->n_kv_heads != 0)
+    return fail(SUBSPEC_ESHAPE, "n_q_heads must be a multiple of n_kv_heads");
+  if (m->hidden % 128 != 0 || m->ffn % 128 != 0)
+    return fail(SUBSPEC_ESHAPE, "hidden and ffn must be multiples of 128");
+  if (m->hidden > kMaxGemvK || m->ffn > kMaxGemvK ||
+      (int64_t)m->n_q_heads * m->head_dim > kMaxGemvK)
+    return fail(SUBSPEC_EUNSUPPORTED, "GEMV input width above %d", kMaxGemvK);
+  if (m->vocab > (1 << 24)) return fail(SUBSPEC_EUNSUPPORTED, "vocab above 2^24");
+  if (!(m->rms_eps > 0.0f) || !(m->rope_theta > 1.0f))
+    return fail(SUBSPEC_EINVAL, "rms_eps must be > 0 and rope_theta > 1");
+  if (!m->embed || !m->final_norm || !m->lm_head || !m->layers)
+    return fail(SUBSPEC_EINVAL, "embed, final_norm, lm_head and layers must be set");
+  const int64_t H = m->hidden, F = m->ffn, qd = (int64_t)m->n_q_heads * m->head_dim;
+  const int64_t qkv = (int64_t)(m->n_q_heads + 2 * m->n_kv_heads) * m->head_dim;
+  for (int l = 0; l < m->n_layers; ++l) {
+    const subspec_layer& L = m->layers[l];
+    if (!L.attn_norm || !L.ffn_norm) return fail(SUBSPEC_EINVAL, "layer %d: norm weights NULL", l);
+    int r;
+    if ((r = check_linear(L.qkv, qkv, H, false, "qkv", l)) ||
+        (r = check_linear(L.o, H, qd, false, "o", l)) ||
+        (r = check_linear(L.gate_up, 2 * F, H, false, "gate_up", l)) ||
+        (r = check_linear(L.down, H, F, false, "down", l)) ||
+        (r = check_linear(L.qkv_d, qkv, H, true, "qkv_d", l)) ||
+        (r = check_linear(L.o_d, H, qd, true, "o_d", l)) ||
+        (r = check_linear(L.gate_up_d, 2 * F, H, true, "gate_up_d", l)) ||
+        (r = check_linear(L.down_d, H, F, true, "down_d", l)))
+      return r;
+  }
+  return SUBSPEC_OK;
+}
+
+int check_state(const subspec_model* m, const subspec_state* st) {
+  if (!st) return fail(SUBSPEC_EINVAL, "state is NULL");
+  if (!st->k_cache || !st->v_cache || !st->kv_len || !st->tokens)
+    return fail(SUBSPEC_EINVAL, "state buffers k_cache, v_cache, kv_len, tokens must be set");
+  if (st->capacity < 1) return fail(SUBSPEC_ECAPACITY, "capacity must be >= 1");
+  (void)m;
+  return SUBSPEC_OK;
+}
+
+// ------------------------------------------------------------------ layouts
+struct FwdWs {
+  uint32_t* gemm_counters;
+  uint32_t* sample_counter;
+  uint16_t *h, *xn, *qkv, *qrot, *attn, *act;
+  float* attn_part;
+  int attn_splits;
+  float* gemm_part;
+  float* logit_max;
+  int32_t* logit_arg;
+  unsigned long long* sample_sums;
+  int32_t* valid;
+};
+
+size_t max_gemm_partials(const subspec_model* m, int mt) {
+  const int64_t H = m->hidden, F = m->ffn, qd = (int64_t)m->n_q_heads * m->head_dim;
+  const int64_t qkv = (int64_t)(m->n_q_heads + 2 * m->n_kv_heads) * m->head_dim;
+  size_t b = 0;
+  b = std::max(b, gemm_partials_bytes(qkv, H, mt, GEPI_STORE));
+  b = std::max(b, gemm_partials_bytes(H, qd, mt, GEPI_RESID));
+  b = std::max(b, gemm_partials_bytes(F, H, mt, GEPI_SILU));
+  b = std::max(b, gemm_partials_bytes(H, F, mt, GEPI_RESID));
+  b = std::max(b, gemm_partials_bytes(m->vocab, H, mt, GEPI_STORE));
+  return b;
+}
+
+size_t carve_fwd(const subspec_model* m, int mt, int cap, void* ws, FwdWs* o) {
+  Carver c{(char*)ws, 0};
+  FwdWs w{};
+  char* base = (char*)ws;
+  w.gemm_counters = base ? (uint32_t*)(base + kGemmCounterOff) : nullptr;
+  w.sample_counter = base ? (uint32_t*)(base + kSampleCounterOff) : nullptr;
+  c.off = kCounterBytes;
+  const int64_t H = m->hidden, F = m->ffn, qd = (int64_t)m->n_q_heads * m->head_dim;
+  const int64_t qkv = (int64_t)(m->n_q_heads + 2 * m->n_kv_heads) * m->head_dim;
+  w.h = (uint16_t*)c.take((size_t)mt * H * 2);
+  w.xn = (uint16_t*)c.take((size_t)mt * H * 2);
+  w.qkv = (uint16_t*)c.take((size_t)mt * qkv * 2);
+  w.qrot = (uint16_t*)c.take((size_t)mt * qd * 2);
+  w.attn = (uint16_t*)c.take((size_t)mt * qd * 2);
+  w.act = (uint16_t*)c.take((size_t)mt * F * 2);
+  w.attn_splits = (cap + attn_keys_per_split() - 1) / attn_keys_per_split();
+  w.attn_part = (float*)c.take((size_t)m->n_q_heads * w.attn_splits * mt * (m->head_dim + 2) * 4);
+  w.gemm_part = (float*)c.take(max_gemm_partials(m, mt));
+  const int lm_blocks = (int)((m->vocab + gemv_rows_per_block(false, m->vocab, EPI_LOGITS) - 1) /
+                              gemv_rows_per_block(false, m->vocab, EPI_LOGITS));
+  w.logit_max = (float*)c.take((size_t)lm_blocks * 4);
+  w.logit_arg = (int32_t*)c.take((size_t)lm_blocks * 4);
+  w.sample_sums = (unsigned long long*)c.take(64 * 8);
+  w.valid = (int32_t*)c.take(4);
+  if (o) *o = w;
+  return c.off;
+}
+
+struct RejWsL {
+  RejectWs r;
+};
+size_t carve_reject(int gamma, int vocab, void* ws, RejectWs* o) {
+  Carver c{(char*)ws, kCounterBytes};
+  const size_t C = (size_t)reject_chunks(vocab), rows = (size_t)(2 * gamma + 1);
+  RejectWs r{};
+  r.counter = ws ? (uint32_t*)((char*)ws + kRejectCounterOff) : nullptr;
+  r.row_max = (float*)c.take(rows * C * 4);
+  r.row_arg = (int32_t*)c.take(rows * C * 4);
+  r.row_bad = (int32_t*)c.take(rows * C * 4);
+  r.row_sum = (unsigned long long*)c.take(rows * C * 8);
+  r.res_sum = (unsigned long long*)c.take(C * 8);
+  if (o) *o = r;
+  return c.off;
+}
+
+int need_ws(void* ws, size_t have, size_t need) {
+  if (!ws) return fail(SUBSPEC_EWORKSPACE, "workspace is NULL");
+  if (have < need)
+    return fail(SUBSPEC_EWORKSPACE, "workspace of %zu bytes, %zu needed", have, need);
+  return SUBSPEC_OK;
+}
+
+void set_linear(GemvArgs& a, const subspec_linear& l) {
+  a.w = l.w;
+  a.codes = l.codes;
+  a.meta = l.meta;
+}
+
+}  // namespace
+
+extern "C" {
+
+int subspec_abi_version(void) { return SUBSPEC_ABI_VERSION; }
+
+const char* subspec_last_error(void) { return g_err.c_str(); }
+
+size_t subspec_workspace_bytes(const subspec_model* m, int32_t max_tokens, int32_t capacity) {
+  if (check_model(m)) return 0;
+  if (max_tokens < 1 || max_tokens > kMaxTokens) {
+    fail(SUBSPEC_EINVAL, "max_tokens must be in [1, %d]", kMaxTokens);
+    return 0;
+  }
+  if (capacity < 1) {
+    fail(SUBSPEC_ECAPACITY, "capacity must be >= 1");
+    return 0;
+  }
+  size_t b = carve_fwd(m, max_tokens, capacity, nullptr, nullptr);
+  b = std::max(b, carve_reject(kMaxGamma, m->vocab, nullptr, nullptr));
+  ok();
+  return b;
+}
+
+int subspec_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws) return fail(SUBSPEC_EWORKSPACE, "workspace is NULL");
+  if (ws_bytes < kCounterBytes) return fail(SUBSPEC_EWORKSPACE, "workspace below %zu bytes", kCounterBytes);
+  HIPCHK(launch_zero(ws, ws_bytes & ~(size_t)15, hs(stream)));
+  return ok();
+}
+
+int subspec_quantize(const uint16_t* w, int64_t n, int64_t k, int32_t group, int32_t bits,
+                     uint8_t* codes, uint16_t* meta, void* stream) {
+  if (!w || !codes || !meta) return fail(SUBSPEC_EINVAL, "w, codes and meta must be set");
+  if (bits != 4) return fail(SUBSPEC_EUNSUPPORTED, "only bits = 4 is built");
+  if (group != 64) return fail(SUBSPEC_EUNSUPPORTED, "only group = 64 is built");
+  if (n < 1 || k < 1) return fail(SUBSPEC_EINVAL, "n and k must be positive");
+  if (k % 64 != 0) return fail(SUBSPEC_ESHAPE, "k must be a multiple of 64");
+  HIPCHK(launch_w4_quantize(w, n, k, codes, meta, hs(stream)));
+  return ok();
+}
+
+int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t step,
+                       float draft_temp, const uint32_t* u_codes, void* ws, size_t ws_bytes,
+                       void* stream) {
+  int r;
+  if ((r = check_model(m)) || (r = check_state(m, st))) return r;
+  if (!st->draft_logits) return fail(SUBSPEC_EINVAL, "state.draft_logits must be set");
+  if (step < 0 || step >= st->gamma_max)
+    return fail(SUBSPEC_EINVAL, "step %d outside [0, gamma_max = %d)", step, st->gamma_max);
+  if (!(draft_temp >= 0.0f)) return fail(SUBSPEC_EINVAL, "draft_temp must be >= 0");
+  if (draft_temp > 0.0f && !u_codes) return fail(SUBSPEC_EINVAL, "u_codes needed when draft_temp > 0");
+  if ((r = need_ws(ws, ws_bytes, carve_fwd(m, 1, st->capacity, nullptr, nullptr)))) return r;
+  FwdWs w;
+  carve_fwd(m, 1, st->capacity, ws, &w);
+  hipStream_t s = hs(stream);
+  const int64_t H = m->hidden, F = m->ffn, d = m->head_dim;
+  const int64_t qd = (int64_t)m->n_q_heads * d;
+  const int64_t qkv = (int64_t)(m->n_q_heads + 2 * m->n_kv_heads) * d;
+  int32_t* tok_out = st->tokens + step + 1;
+  HIPCHK(launch_pos_guard(st->kv_len, st->tokens + step, step, st->capacity, m->vocab, w.valid, tok_out, s));
+  for (int l = 0; l < m->n_layers; ++l) {
+    const subspec_layer& L = m->layers[l];
+    GemvArgs a{};
+    set_linear(a, L.qkv_d);
+    a.n = qkv;
+    a.k = H;
+    a.h = w.h;
+    a.norm_w = L.attn_norm;
+    a.eps = m->rms_eps;
+    a.embed = m->embed;
+    a.token = st->tokens + step;
+    a.h_out = w.h;
+    a.y = w.qkv;
+    a.valid = w.valid;
+    HIPCHK(launch_gemv(lin_is_w4(L.qkv_d), l == 0 ? PRO_EMBED_NORM : PRO_NORM, EPI_STORE, a, s, nullptr));
+
+    AttnArgs at{};
+    at.qkv = w.qkv;
+    at.q_rot = w.qrot;
+    at.k_cache = st->k_cache + (int64_t)l * m->n_kv_heads * st->capacity * d;
+    at.v_cache = st->v_cache + (int64_t)l * m->n_kv_heads * st->capacity * d;
+    at.kv_len = st->kv_len;
+    at.pos_offset = step;
+    at.m = 1;
+    at.n_q = m->n_q_heads;
+    at.n_kv = m->n_kv_heads;
+    at.d = (int)d;
+    at.cap = st->capacity;
+    at.theta = m->rope_theta;
+    at.part = w.attn_part;
+    at.splits = w.attn_splits;
+    at.out = w.attn;
+    HIPCHK(launch_rope_append(at, s));
+    HIPCHK(launch_attention(at, s));
+
+    GemvArgs o{};
+    set_linear(o, L.o_d);
+    o.n = H;
+    o.k = qd;
+    o.x = w.attn;
+    o.y = w.h;
+    o.resid = w.h;
+    o.valid = w.valid;
+    HIPCHK(launch_gemv(lin_is_w4(L.o_d), PRO_X, EPI_RESID, o, s, nullptr));
+
+    GemvArgs g{};
+    set_linear(g, L.gate_up_d);
+    g.n = F;
+    g.k = H;
+    g.h = w.h;
+    g.norm_w = L.ffn_norm;
+    g.eps = m->rms_eps;
+    g.y = w.act;
+    g.valid = w.valid;
+    HIPCHK(launch_gemv(lin_is_w4(L.gate_up_d), PRO_NORM, EPI_SILU, g, s, nullptr));
+
+    GemvArgs dn{};
+    set_linear(dn, L.down_d);
+    dn.n = H;
+    dn.k = F;
+    dn.x = w.act;
+    dn.y = w.h;
+    dn.resid = w.h;
+    dn.valid = w.valid;
+    HIPCHK(launch_gemv(lin_is_w4(L.down_d), PRO_X, EPI_RESID, dn, s, nullptr));
+  }
+  uint16_t* logits = st->draft_logits + (int64_t)step * m->vocab;
+  GemvArgs lm{};
+  lm.w = m->lm_head;
+  lm.n = m->vocab;
+  lm.k = H;
+  lm.h = w.h;
+  lm.norm_w = m->final_norm;
+  lm.eps = m->rms_eps;
+  lm.y = logits;
+  lm.part_max = w.logit_max;
+  lm.part_arg = w.logit_arg;
+  lm.valid = w.valid;
+  int lm_blocks = 0;
+  HIPCHK(launch_gemv(false, PRO_NORM, EPI_LOGITS, lm, s, &lm_blocks));
+  SampleWs sw{w.logit_max, w.logit_arg, w.sample_sums, w.sample_counter};
+  HIPCHK(launch_sample(logits, m->vocab, draft_temp, u_codes ? u_codes + step : nullptr, w.logit_max,
+                       w.logit_arg, lm_blocks, tok_out, w.valid, sw, s));
+  return ok();
+}
+
+int subspec_verify(const subspec_model* m, const subspec_state* st, int32_t n_tokens,
+                   const int32_t* tokens, uint16_t* logits, void* ws, size_t ws_bytes, void* stream) {
+  int r;
+  if ((r = check_model(m)) || (r = check_state(m, st))) return r;
+  if (!tokens) return fail(SUBSPEC_EINVAL, "tokens is NULL");
+  if (n_tokens < 1 || n_tokens > kMaxTokens)
+    return fail(SUBSPEC_EINVAL, "n_tokens %d outside [1, %d]", n_tokens, kMaxTokens);
+  if (n_tokens > st->capacity) return fail(SUBSPEC_ECAPACITY, "n_tokens above the KV capacity");
+  if ((r = need_ws(ws, ws_bytes, carve_fwd(m, n_tokens, st->capacity, nullptr, nullptr)))) return r;
+  FwdWs w;
+  carve_fwd(m, n_tokens, st->capacity, ws, &w);
+  hipStream_t s = hs(stream);
+  const int64_t H = m->hidden, F = m->ffn, d = m->head_dim;
+  const int64_t qd = (int64_t)m->n_q_heads * d;
+  const int64_t qkv = (int64_t)(m->n_q_heads + 2 * m->n_kv_heads) * d;
+  const int mt = n_tokens;
+  HIPCHK(launch_embed_rows(m->embed, tokens, mt, (int)H, m->vocab, w.h, s));
+  for (int l = 0; l < m->n_layers; ++l) {
+    const subspec_layer& L = m->layers[l];
+    HIPCHK(launch_rmsnorm_rows(w.h, L.attn_norm, m->rms_eps, mt, (int)H, w.xn, s));
+    GemmArgs q{L.qkv.w, qkv, H, w.xn, mt, w.qkv, qkv, nullptr, w.gemm_part, w.gemm_counters};
+    HIPCHK(launch_gemm(GEPI_STORE, q, s));
+    AttnArgs at{};
+    at.qkv = w.qkv;
+    at.q_rot = w.qrot;
+    at.k_cache = st->k_cache + (int64_t)l * m->n_kv_heads * st->capacity * d;
+    at.v_cache = st->v_cache + (int64_t)l * m->n_kv_heads * st->capacity * d;
+    at.kv_len = st->kv_len;
+    at.pos_offset = 0;
+    at.m = mt;
+    at.n_q = m->n_q_heads;
+    at.n_kv = m->n_kv_heads;
+    at.d = (int)d;
+    at.cap = st->capacity;
+    at.theta = m->rope_theta;
+    at.part = w.attn_part;
+    at.splits = w.attn_splits;
+    at.out = w.attn;
+    HIPCHK(launch_rope_append(at, s));
+    HIPCHK(launch_attention(at, s));
+    GemmArgs o{L.o.w, H, qd, w.attn, mt, w.h, H, w.h, w.gemm_part, w.gemm_counters};
+    HIPCHK(launch_gemm(GEPI_RESID, o, s));
+    HIPCHK(launch_rmsnorm_rows(w.h, L.ffn_norm, m->rms_eps, mt, (int)H, w.xn, s));
+    GemmArgs g{L.gate_up.w, F, H, w.xn, mt, w.act, F, nullptr, w.gemm_part, w.gemm_counters};
+    HIPCHK(launch_gemm(GEPI_SILU, g, s));
+    GemmArgs dn{L.down.w, H, F, w.act, mt, w.h, H, w.h, w.gemm_part, w.gemm_counters};
+    HIPCHK(launch_gemm(GEPI_RESID, dn, s));
+  }
+  if (logits) {
+    HIPCHK(launch_rmsnorm_rows(w.h, m->final_norm, m->rms_eps, mt, (int)H, w.xn, s));
+    GemmArgs lm{m->lm_head, m->vocab, H, w.xn, mt, logits, m->vocab, nullptr, w.gemm_part,
+                w.gemm_counters};
+    HIPCHK(launch_gemm(GEPI_STORE, lm, s));
+  }
+  return ok();
+}
+
+int subspec_reject(int32_t gamma, int32_t vocab, float temp, float draft_temp,
+                   const uint16_t* target_logits, const uint16_t* draft_logits,
+                   const int32_t* draft_tokens, const uint32_t* r_codes, const uint32_t* u_code,
+                   int32_t* n_accepted, int32_t* out_tokens, int32_t* status, float* probs,
+                   void* ws, size_t ws_bytes, void* stream) {
+  if (gamma < 0 || gamma > kMaxGamma) return fail(SUBSPEC_EINVAL, "gamma outside [0, %d]", kMaxGamma);
+  if (vocab < 1 || vocab > (1 << 24)) return fail(SUBSPEC_EINVAL, "vocab outside [1, 2^24]");
+  if (!(temp >= 0.0f) || !(draft_temp >= 0.0f)) return fail(SUBSPEC_EINVAL, "temperatures must be >= 0");
+  if (!target_logits || !n_accepted || !out_tokens || !status)
+    return fail(SUBSPEC_EINVAL, "target_logits, n_accepted, out_tokens and status must be set");
+  if (gamma > 0 && (!draft_logits || !draft_tokens))
+    return fail(SUBSPEC_EINVAL, "draft_logits and draft_tokens must be set when gamma > 0");
+  if (temp > 0.0f && (!u_code || (gamma > 0 && !r_codes)))
+    return fail(SUBSPEC_EINVAL, "r_codes and u_code must be set when temp > 0");
+  int r;
+  if ((r = need_ws(ws, ws_bytes, carve_reject(gamma, vocab, nullptr, nullptr)))) return r;
+  RejectWs rw;
+  carve_reject(gamma, vocab, ws, &rw);
+  HIPCHK(launch_reject(gamma, vocab, temp, draft_temp, target_logits, draft_logits, draft_tokens,
+                       r_codes, u_code, n_accepted, out_tokens, status, probs, rw, hs(stream)));
+  return ok();
+}
+
+int subspec_kv_rollback(const subspec_state* st, const int32_t* n_accepted,
+                        const int32_t* out_tokens, void* stream) {
+  if (!st || !st->kv_len || !st->tokens) return fail(SUBSPEC_EINVAL, "state kv_len/tokens NULL");
+  if (!n_accepted || !out_tokens) return fail(SUBSPEC_EINVAL, "n_accepted and out_tokens must be set");
+  HIPCHK(launch_kv_rollback(st->kv_len, st->tokens, n_accepted, out_tokens, hs(stream)));
+  return ok();
+}
+
+int subspec_kv_advance(const subspec_state* st, int32_t delta, void* stream) {
+  if (!st || !st->kv_len) return fail(SUBSPEC_EINVAL, "state kv_len NULL");
+  HIPCHK(launch_kv_advance(st->kv_len, delta, hs(stream)));
+  return ok();
+}
+
+int subspec_w4_gemv(const uint8_t* codes, const uint16_t* meta, int64_t n, int64_t k,
+                    const uint16_t* x, uint16_t* y, void* stream) {
+  if (!codes || !meta || !x || !y) return fail(SUBSPEC_EINVAL, "codes, meta, x and y must be set");
+  if (n < 1 || k < 1) return fail(SUBSPEC_EINVAL, "n and k must be positive");
+  if (k % 64 != 0) return fail(SUBSPEC_ESHAPE, "k must be a multiple of 64");
+  if (k > kMaxGemvK) return fail(SUBSPEC_EUNSUPPORTED, "k above %d", kMaxGemvK);
+  GemvArgs a{};
+  a.codes = codes;
+  a.meta = meta;
+  a.n = n;
+  a.k = k;
+  a.x = x;
+  a.y = y;
+  HIPCHK(launch_gemv(true, PRO_X, EPI_STORE, a, hs(stream), nullptr));
+  return ok();
+}
+
+int subspec_bf16_gemv(const uint16_t* w, int64_t n, int64_t k, const uint16_t* x, uint16_t* y,
+                      void* stream) {
+  if (!w || !x || !y) return fail(SUBSPEC_EINVAL, "w, x and y must be set");
+  if (n < 1 || k < 1) return fail(SUBSPEC_EINVAL, "n and k must be positive");
+  if (k % 8 != 0) return fail(SUBSPEC_ESHAPE, "k must be a multiple of 8");
+  if (k > kMaxGemvK) return fail(SUBSPEC_EUNSUPPORTED, "k above %d", kMaxGemvK);
+  GemvArgs a{};
+  a.w = w;
+  a.n = n;
+  a.k = k;
+  a.x = x;
+  a.y = y;
+  HIPCHK(launch_gemv(false, PRO_X, EPI_STORE, a, hs(stream), nullptr));
+  return ok();
+}
+
+int subspec_bf16_gemm(const uint16_t* w, int64_t n, int64_t k, const uint16_t* x, int32_t m,
+                      uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
+  if (!w || !x || !y) return fail(SUBSPEC_EINVAL, "w, x and y must be set");
+  if (n < 1 || k < 1) return fail(SUBSPEC_EINVAL, "n and k must be positive");
+  if (m < 1 || m > kMaxTokens) return fail(SUBSPEC_EINVAL, "m outside [1, %d]", kMaxTokens);
+  if (k % 128 != 0) return fail(SUBSPEC_ESHAPE, "k must be a multiple of 128");
+  if (gemm_counter_slots(n, k, m, GEPI_STORE) > (size_t)kMaxGemmCounters)
+    return fail(SUBSPEC_EUNSUPPORTED, "too many split-k row groups");
+  const size_t need = kCounterBytes + align256(gemm_partials_bytes(n, k, m, GEPI_STORE));
+  int r;
+  if ((r = need_ws(ws, ws_bytes, need))) return r;
+  GemmArgs a{w, n, k, x, m, y, n, nullptr, (float*)((char*)ws + kCounterBytes),
+             (uint32_t*)((char*)ws + kGemmCounterOff)};
+  HIPCHK(launch_gemm(GEPI_STORE, a, hs(stream)));
+  return ok();
+}
+
+int subspec_sample(const uint16_t* logits, int32_t vocab, float temp, const uint32_t* u_code,
+                   int32_t* token, void* ws, size_t ws_bytes, void* stream) {
+  if (!logits || !token) return fail(SUBSPEC_EINVAL, "logits and token must be set");
+  if (vocab < 1 || vocab > (1 << 24)) return fail(SUBSPEC_EINVAL, "vocab outside [1, 2^24]");
+  if (!(temp >= 0.0f)) return fail(SUBSPEC_EINVAL, "temp must be >= 0");
+  if (temp > 0.0f && !u_code) return fail(SUBSPEC_EINVAL, "u_code needed when temp > 0");
+  const int nc = sample_chunks(vocab);
+  Carver c{(char*)ws, kCounterBytes};
+  float* pm = (float*)c.take(nc * 4);
+  int32_t* pa = (int32_t*)c.take(nc * 4);
+  unsigned long long* sums = (unsigned long long*)c.take(64 * 8);
+  int r;
+  if ((r = need_ws(ws, ws_bytes, c.off))) return r;
+  hipStream_t s = hs(stream);
+  HIPCHK(launch_rowmax(logits, vocab, pm, pa, nc, s));
+  SampleWs sw{pm, pa, sums, (uint32_t*)((char*)ws + kSampleCounterOff)};
+  HIPCHK(launch_sample(logits, vocab, temp, u_code, pm, pa, nc, token, nullptr, sw, s));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+// Host-side declarations shared by the translation units of libsubspec.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// ------------------------------------------------------------------ GEMV (batch 1)
+// Prologue: where the input vector x comes from.
+enum GemvPro { PRO_X = 0, PRO_NORM = 1, PRO_EMBED_NORM = 2 };
+// Epilogue: what is written.
+enum GemvEpi { EPI_STORE = 0, EPI_RESID = 1, EPI_SILU = 2, EPI_LOGITS = 3 };
+
+struct GemvArgs {
+  // weights: bf16 w, or W4 codes + meta
+  const uint16_t* w;
+  const uint8_t* codes;
+  const uint16_t* meta;
+  int64_t n;  // output rows (F in EPI_SILU mode: physical rows are 2F)
+  int64_t k;
+  // prologue inputs
+  const uint16_t* x;         // PRO_X
+  const uint16_t* h;         // PRO_NORM: residual stream [k]
+  const uint16_t* norm_w;    // PRO_NORM / PRO_EMBED_NORM
+  float eps;
+  const uint16_t* embed;     // PRO_EMBED_NORM: embed table [V][k]
+  const int32_t* token;      // PRO_EMBED_NORM: device token id
+  uint16_t* h_out;           // PRO_EMBED_NORM: block 0 stores the embedded row here
+  // epilogue outputs
+  uint16_t* y;               // output [n]
+  const uint16_t* resid;     // EPI_RESID: y = bf16(resid + acc) (may alias y)
+  float* part_max;           // EPI_LOGITS: per-block max
+  int32_t* part_arg;         // EPI_LOGITS: per-block argmax
+  const int32_t* valid;      // optional device flag: skip everything if *valid == 0
+};
+
+int gemv_rows_per_block(bool w4, int64_t n, int epi);
+hipError_t launch_gemv(bool w4, int pro, int epi, const GemvArgs& a, hipStream_t s, int* blocks_out);
+
+// ------------------------------------------------------------------ GEMM (verify)
+enum GemmEpi { GEPI_STORE = 0, GEPI_RESID = 1, GEPI_SILU = 2 };
+struct GemmArgs {
+  const uint16_t* w;  // bf16 [N][K]
+  int64_t n;          // output columns (F in GEPI_SILU mode)
+  int64_t k;
+  const uint16_t* x;  // bf16 [m][K]
+  int m;
+  uint16_t* y;        // bf16 [m][ldy]
+  int64_t ldy;
+  const uint16_t* resid;  // GEPI_RESID: [m][ldy]
+  float* partials;        // split-K scratch
+  uint32_t* counters;     // split-K arrival counters (zero, self-resetting)
+};
+size_t gemm_partials_bytes(int64_t n, int64_t k, int m, int epi);
+size_t gemm_counter_slots(int64_t n, int64_t k, int m, int epi);
+hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------------ quantise
+hipError_t launch_w4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
+                              uint16_t* meta, hipStream_t s);
+
+// ------------------------------------------------------------------ attention
+struct AttnArgs {
+  const uint16_t* qkv;  // [m][(Hq+2Hkv) d] raw projections (pre-RoPE)
+  uint16_t* q_rot;      // [m][Hq d] rotated queries (bf16)
+  uint16_t* k_cache;    // [Hkv][cap][d] of this layer
+  uint16_t* v_cache;
+  const int32_t* kv_len;
+  int pos_offset;       // position of row j = kv_len + pos_offset + j
+  int m;                // query rows
+  int n_q, n_kv, d, cap;
+  float theta;
+  float* part;          // [Hq][splits][m][d + 2]
+  int splits;           // grid splits over keys
+  int keys_per_split;
+  uint16_t* out;        // [m][Hq d]
+};
+hipError_t launch_rope_append(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+int attn_keys_per_split();
+
+// ------------------------------------------------------------------ misc kernels
+hipError_t launch_rmsnorm_rows(const uint16_t* h, const uint16_t* g, float eps, int rows, int k,
+                               uint16_t* out, hipStream_t s);
+hipError_t launch_embed_rows(const uint16_t* embed, const int32_t* tokens, int rows, int k,
+                             int vocab, uint16_t* h, hipStream_t s);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_kv_rollback(int32_t* kv_len, int32_t* tokens, const int32_t* n_accepted,
+                              const int32_t* out_tokens, hipStream_t s);
+hipError_t launch_kv_advance(int32_t* kv_len, int32_t delta, hipStream_t s);
+hipError_t launch_pos_guard(const int32_t* kv_len, const int32_t* token_in, int step, int cap,
+                            int vocab, int32_t* valid, int32_t* token_out, hipStream_t s);
+
+// ------------------------------------------------------------------ sampling / rejection
+struct SampleWs {
+  float* part_max;
+  int32_t* part_arg;
+  unsigned long long* chunk_sum;
+  uint32_t* counter;
+};
+int sample_chunks(int vocab);
+hipError_t launch_sample(const uint16_t* logits, int vocab, float temp, const uint32_t* u_code,
+                         const float* pre_max, const int32_t* pre_arg, int n_pre,
+                         int32_t* token, const int32_t* valid, const SampleWs& ws, hipStream_t s);
+hipError_t launch_rowmax(const uint16_t* logits, int vocab, float* part_max, int32_t* part_arg,
+                         int n_chunks, hipStream_t s);
+
+struct RejectWs {
+  float* row_max;                    // [rows][chunks]
+  int32_t* row_arg;                  // [rows][chunks]
+  int32_t* row_bad;                  // [rows][chunks] non-finite flags
+  unsigned long long* row_sum;       // [rows][chunks]
+  unsigned long long* res_sum;       // [chunks]
+  uint32_t* counter;
+};
+int reject_chunks(int vocab);
+size_t reject_ws_bytes(int gamma, int vocab);
+hipError_t launch_reject(int gamma, int vocab, float temp, float draft_temp, const uint16_t* zt,
+                         const uint16_t* zd, const int32_t* toks, const uint32_t* r_codes,
+                         const uint32_t* u_code, int32_t* n_out, int32_t* out_tokens,
+                         int32_t* status, float* probs, const RejectWs& ws, hipStream_t s);

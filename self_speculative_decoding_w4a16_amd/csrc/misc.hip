@@ -1,0 +1,127 @@
+// Small kernels of the path: row RMSNorm and embedding gather for the verify
+// pass, workspace fill, and the device-side KV bookkeeping of a cycle
+// ("How speculative decoding makes LLMs go brrr", Module 2: after a round the
+// K/V of rejected positions are dropped - here by moving kv_len only).
+#include "common.h"
+#include "internal.h"
+
+namespace {
+
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t* __restrict__ h,
+                                                           const uint16_t* __restrict__ g,
+                                                           float eps, int k,
+                                                           uint16_t* __restrict__ out) {
+  __shared__ float red[4];
+  __shared__ float s_inv;
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const uint16_t* x = h + (int64_t)row * k;
+  float ss = 0.0f;
+  for (int q = tid; q < k / 8; q += 256) {
+    u32x4 v = reinterpret_cast<const u32x4*>(x)[q];
+    uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float lo = ss::lo_bf(wv[i]), hi = ss::hi_bf(wv[i]);
+      ss += lo * lo;
+      ss += hi * hi;
+    }
+  }
+  ss = ss::wave_sum(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  if (tid == 0) s_inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)k + eps);
+  __syncthreads();
+  const float inv = s_inv;
+  uint16_t* o = out + (int64_t)row * k;
+  for (int q = tid; q < k / 8; q += 256) {
+    u32x4 v = reinterpret_cast<const u32x4*>(x)[q];
+    u32x4 gv = reinterpret_cast<const u32x4*>(g)[q];
+    uint32_t wv[4] = {v.x, v.y, v.z, v.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
+    uint32_t ow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint16_t lo = ss::f2bf(ss::lo_bf(wv[i]) * inv * ss::lo_bf(gw[i]));
+      uint16_t hi = ss::f2bf(ss::hi_bf(wv[i]) * inv * ss::hi_bf(gw[i]));
+      ow[i] = ss::pack_bf(lo, hi);
+    }
+    reinterpret_cast<u32x4*>(o)[q] = u32x4{ow[0], ow[1], ow[2], ow[3]};
+  }
+}
+
+// Out-of-range token ids are clamped into [0, vocab) so a bad id cannot read
+// outside the table.
+__global__ __launch_bounds__(256) void embed_rows_kernel(const uint16_t* __restrict__ embed,
+                                                         const int32_t* __restrict__ tokens, int k,
+                                                         int vocab, uint16_t* __restrict__ h) {
+  const int row = blockIdx.x;
+  const int tok = min(max(tokens[row], 0), vocab - 1);
+  const u32x4* src = reinterpret_cast<const u32x4*>(embed + (int64_t)tok * k);
+  u32x4* dst = reinterpret_cast<u32x4*>(h + (int64_t)row * k);
+  for (int q = threadIdx.x; q < k / 8; q += 256) dst[q] = src[q];
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(u32x4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+__global__ void kv_rollback_kernel(int32_t* kv_len, int32_t* tokens, const int32_t* n_accepted,
+                                   const int32_t* out_tokens) {
+  const int n = *n_accepted;
+  *kv_len += n + 1;
+  tokens[0] = out_tokens[n];
+}
+
+__global__ void kv_advance_kernel(int32_t* kv_len, int32_t delta) { *kv_len += delta; }
+
+// valid = (0 <= kv_len + step < cap) and the input token is a vocabulary id;
+// when not, the draft step does nothing but set its output token to -1.
+__global__ void pos_guard_kernel(const int32_t* kv_len, const int32_t* token_in, int step, int cap,
+                                 int vocab, int32_t* valid, int32_t* token_out) {
+  const int pos = *kv_len + step, t = *token_in;
+  const int ok = pos >= 0 && pos < cap && t >= 0 && t < vocab;
+  *valid = ok;
+  if (!ok) *token_out = -1;
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm_rows(const uint16_t* h, const uint16_t* g, float eps, int rows, int k,
+                               uint16_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(rows), dim3(256), 0, s, h, g, eps, k, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed_rows(const uint16_t* embed, const int32_t* tokens, int rows, int k,
+                             int vocab, uint16_t* h, hipStream_t s) {
+  hipLaunchKernelGGL(embed_rows_kernel, dim3(rows), dim3(256), 0, s, embed, tokens, k, vocab, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (u32x4*)p, n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_rollback(int32_t* kv_len, int32_t* tokens, const int32_t* n_accepted,
+                              const int32_t* out_tokens, hipStream_t s) {
+  hipLaunchKernelGGL(kv_rollback_kernel, dim3(1), dim3(1), 0, s, kv_len, tokens, n_accepted,
+                     out_tokens);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_advance(int32_t* kv_len, int32_t delta, hipStream_t s) {
+  hipLaunchKernelGGL(kv_advance_kernel, dim3(1), dim3(1), 0, s, kv_len, delta);
+  return hipGetLastError();
+}
+
+hipError_t launch_pos_guard(const int32_t* kv_len, const int32_t* token_in, int step, int cap,
+                            int vocab, int32_t* valid, int32_t* token_out, hipStream_t s) {
+  hipLaunchKernelGGL(pos_guard_kernel, dim3(1), dim3(1), 0, s, kv_len, token_in, step, cap, vocab,
+                     valid, token_out);
+  return hipGetLastError();
+}

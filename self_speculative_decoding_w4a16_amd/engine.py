@@ -1,0 +1,102 @@
+"""The speculative cycle on one GPU ("How speculative decoding makes LLMs go
+brrr", overall flow and pseudo-code): gamma draft steps, one verify pass over
+gamma+1 positions, the rejection round, KV rollback.  Every step is a call
+into libsubspec; this class only owns the device buffers and the call order.
+State lives on the device (kv_len, tokens), so a cycle needs no host sync;
+the host reads back the emitted tokens once per cycle.
+"""
+import torch
+
+from . import _lib
+
+
+class SpecDecoder:
+    def __init__(self, model, capacity, gamma, temp=0.0, draft_temp=0.0, max_tokens=64,
+                 device="cuda"):
+        s = model.shape
+        self.model = model
+        self.gamma = gamma
+        self.temp = float(temp)
+        self.draft_temp = float(draft_temp)
+        self.capacity = capacity
+        self.max_tokens = max(max_tokens, gamma + 1)
+        L, V = model.n_layers, s.vocab
+        kv_shape = (L, s.n_kv_heads, capacity, s.head_dim)
+        self.k_cache = torch.zeros(kv_shape, dtype=torch.bfloat16, device=device)
+        self.v_cache = torch.zeros(kv_shape, dtype=torch.bfloat16, device=device)
+        self.kv_len = torch.zeros(1, dtype=torch.int32, device=device)
+        self.tokens = torch.zeros(gamma + 1, dtype=torch.int32, device=device)
+        self.draft_logits = torch.zeros((max(gamma, 1), V), dtype=torch.bfloat16, device=device)
+        self.target_logits = torch.zeros((gamma + 1, V), dtype=torch.bfloat16, device=device)
+        self.n_accepted = torch.zeros(1, dtype=torch.int32, device=device)
+        self.out_tokens = torch.zeros(gamma + 1, dtype=torch.int32, device=device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+        self.probs = torch.zeros((max(gamma, 1), 2), dtype=torch.float32, device=device)
+        self.prefill_tokens = torch.zeros(self.max_tokens, dtype=torch.int32, device=device)
+        nbytes = _lib.workspace_bytes(model.c, self.max_tokens, capacity)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _lib.workspace_init(self.ws)
+        self.c = _lib.State(self.k_cache.data_ptr(), self.v_cache.data_ptr(), capacity,
+                            self.kv_len.data_ptr(), self.tokens.data_ptr(),
+                            self.draft_logits.data_ptr(), gamma)
+
+    # ------------------------------------------------------------ state
+    def reset(self, kv_len, last_token):
+        self.kv_len.fill_(int(kv_len))
+        self.tokens[0] = int(last_token)
+
+    def prefill(self, prompt):
+        """Run prompt[:-1] through the target (chunks of max_tokens positions);
+        afterwards kv_len = len(prompt) - 1 and tokens[0] = prompt[-1]."""
+        prompt = [int(t) for t in prompt]
+        self.kv_len.zero_()
+        body = prompt[:-1]
+        for c0 in range(0, len(body), self.max_tokens):
+            chunk = body[c0:c0 + self.max_tokens]
+            self.prefill_tokens[:len(chunk)] = torch.tensor(chunk, dtype=torch.int32)
+            _lib.verify(self.model.c, self.c, len(chunk), self.prefill_tokens, None, self.ws)
+            _lib.kv_advance(self.c, len(chunk))
+        self.tokens[0] = prompt[-1]
+
+    # ------------------------------------------------------------ one cycle
+    def draft(self, u_draft=None):
+        for i in range(self.gamma):
+            _lib.draft_step(self.model.c, self.c, i, self.draft_temp, u_draft, self.ws)
+
+    def verify(self):
+        _lib.verify(self.model.c, self.c, self.gamma + 1, self.tokens, self.target_logits, self.ws)
+
+    def reject(self, r_codes=None, u_code=None):
+        _lib.reject(self.gamma, self.model.shape.vocab, self.temp, self.draft_temp,
+                    self.target_logits, self.draft_logits, self.tokens[1:], r_codes, u_code,
+                    self.n_accepted, self.out_tokens, self.status, self.probs, self.ws)
+
+    def commit(self):
+        _lib.kv_rollback(self.c, self.n_accepted, self.out_tokens)
+
+    def cycle(self, u_draft=None, r_codes=None, u_code=None):
+        self.draft(u_draft)
+        self.verify()
+        self.reject(r_codes, u_code)
+        self.commit()
+
+    def generate(self, prompt, n_generate, uniforms=None, on_cycle=None):
+        """Speculative decoding of at least n_generate tokens after ``prompt``.
+        ``uniforms`` = (U_draft [C][gamma], R [C][gamma], U_final [C]) uint32
+        device tensors, or None for greedy runs.  Returns (tokens, per-cycle n)."""
+        self.prefill(prompt)
+        out, ns = [], []
+        c = 0
+        while len(out) < n_generate:
+            if uniforms is not None:
+                ud, rr, uf = uniforms
+                self.cycle(ud[c], rr[c], uf[c:c + 1])
+            else:
+                self.cycle()
+            n = int(self.n_accepted.item())
+            out += self.out_tokens[:n + 1].tolist()
+            ns.append(n)
+            if on_cycle:
+                on_cycle(c, n)
+            c += 1
+        return out[:n_generate], ns

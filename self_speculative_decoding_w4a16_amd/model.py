@@ -1,0 +1,83 @@
+"""Device-resident model: bf16 target weights, 4-bit substitute copies built
+with the library's quantiser, and the C structs that describe them.
+
+The draft is the target itself with the layers [n_shared, n_layers) replaced
+by their 4-bit substitutes and the layers [0, n_shared) shared bit for bit
+("SubSpec: Speculate Deep and Accurate" paper note, Method details).  Torch
+only allocates device memory here; the quantisation runs in the HIP kernel.
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+
+MATS = ("qkv", "o", "gate_up", "down")
+
+
+class DeviceModel:
+    def __init__(self, shape, weights, substitute_layers=None, stream=None):
+        """``weights``: dict from synth.model_weights (bf16 tensors on the GPU).
+        ``substitute_layers``: indices quantised for the draft (default: all
+        layers from ``shape.n_shared`` on)."""
+        self.shape = shape
+        self.w = weights
+        L = len(weights["layers"])
+        if substitute_layers is None:
+            substitute_layers = range(shape.n_shared, L)
+        self.substitute_layers = sorted(set(substitute_layers))
+        self.q = [None] * L
+        for l in self.substitute_layers:
+            self.q[l] = {}
+            for name in MATS:
+                wt = weights["layers"][l][name]
+                n, k = wt.shape
+                codes = torch.empty((n, k // 2), dtype=torch.uint8, device=wt.device)
+                meta = torch.empty((n, k // 64, 2), dtype=torch.float16, device=wt.device)
+                _lib.quantize(wt, codes, meta, stream=stream)
+                self.q[l][name] = (codes, meta)
+        self._build_structs()
+
+    def _lin_bf16(self, t):
+        n, k = t.shape
+        return _lib.Linear(t.data_ptr(), None, None, n, k)
+
+    def _lin_w4(self, codes, meta):
+        n, kh = codes.shape
+        return _lib.Linear(None, codes.data_ptr(), meta.data_ptr(), n, 2 * kh)
+
+    def _build_structs(self):
+        s = self.shape
+        L = len(self.w["layers"])
+        self.layer_array = (_lib.Layer * L)()
+        for l, lw in enumerate(self.w["layers"]):
+            st = self.layer_array[l]
+            st.attn_norm = lw["attn_norm"].data_ptr()
+            st.ffn_norm = lw["ffn_norm"].data_ptr()
+            for name in MATS:
+                setattr(st, name, self._lin_bf16(lw[name]))
+                if self.q[l] is not None:
+                    setattr(st, name + "_d", self._lin_w4(*self.q[l][name]))
+                else:
+                    setattr(st, name + "_d", self._lin_bf16(lw[name]))
+        self.c = _lib.Model(L, s.hidden, s.ffn, s.n_q_heads, s.n_kv_heads, s.head_dim, s.vocab,
+                            s.rope_theta, s.rms_eps, self.w["embed"].data_ptr(),
+                            self.w["final_norm"].data_ptr(), self.w["lm_head"].data_ptr(),
+                            ctypes.cast(self.layer_array, ctypes.POINTER(_lib.Layer)))
+
+    @property
+    def n_layers(self):
+        return len(self.w["layers"])
+
+    def weight_bytes(self, draft):
+        """Bytes of weights one forward streams (draft: W4 codes + fp16 meta for
+        substitutes, bf16 otherwise; lm_head included)."""
+        total = 0
+        for l, lw in enumerate(self.w["layers"]):
+            for name in MATS:
+                if draft and self.q[l] is not None:
+                    c, m = self.q[l][name]
+                    total += c.numel() + 2 * m.numel()
+                else:
+                    total += 2 * lw[name].numel()
+        return total + 2 * self.w["lm_head"].numel()

@@ -1,0 +1,136 @@
+"""The C-ABI library loads, exports every symbol include/subspec.h declares,
+and rejects bad arguments on the host before enqueuing anything (CPU only:
+no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from self_speculative_decoding_w4a16_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "subspec.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(subspec_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_cycle_entry_points():
+    names = _declared()
+    for n in ("subspec_quantize", "subspec_draft_step", "subspec_verify", "subspec_reject",
+              "subspec_kv_rollback"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    l = _lib.lib()
+    for name in _declared():
+        assert hasattr(l, name), name
+    assert set(_declared()) == set(_lib.EXPORTS)
+    assert _lib.abi_version() == 1
+
+
+V = ctypes.c_void_p
+
+
+def test_quantize_argument_errors():
+    l = _lib.lib()
+    p = V(4096)
+    assert l.subspec_quantize(None, 4, 64, 64, 4, p, p, None) == _lib.EINVAL
+    assert l.subspec_quantize(p, 4, 64, 64, 3, p, p, None) == _lib.EUNSUPPORTED
+    assert "bits" in _lib.last_error()
+    assert l.subspec_quantize(p, 4, 64, 32, 4, p, p, None) == _lib.EUNSUPPORTED
+    assert l.subspec_quantize(p, 4, 96, 64, 4, p, p, None) == _lib.ESHAPE
+    assert l.subspec_quantize(p, 0, 64, 64, 4, p, p, None) == _lib.EINVAL
+
+
+def test_gemv_gemm_sample_argument_errors():
+    l = _lib.lib()
+    p = V(4096)
+    assert l.subspec_w4_gemv(p, p, 8, 96, p, p, None) == _lib.ESHAPE
+    assert l.subspec_w4_gemv(p, p, 8, 64 * 1024, p, p, None) == _lib.EUNSUPPORTED
+    assert l.subspec_bf16_gemv(p, 8, 12, p, p, None) == _lib.ESHAPE
+    assert l.subspec_bf16_gemm(p, 8, 128, p, 65, p, p, 1 << 20, None) == _lib.EINVAL
+    assert l.subspec_bf16_gemm(p, 8, 100, p, 4, p, p, 1 << 20, None) == _lib.ESHAPE
+    assert l.subspec_bf16_gemm(p, 4096, 4096, p, 17, p, None, 0, None) == _lib.EWORKSPACE
+    assert l.subspec_sample(p, 0, 1.0, p, p, p, 1 << 20, None) == _lib.EINVAL
+    assert l.subspec_sample(p, 100, 1.0, None, p, p, 1 << 20, None) == _lib.EINVAL
+    assert l.subspec_sample(p, 100, 1.0, p, p, p, 16, None) == _lib.EWORKSPACE
+
+
+def test_reject_argument_errors():
+    l = _lib.lib()
+    p = V(4096)
+    args = dict(vocab=100, T=1.0, Td=1.0)
+    assert l.subspec_reject(65, 100, 1.0, 1.0, p, p, p, p, p, p, p, p, None, p, 1 << 20, None) == _lib.EINVAL
+    assert l.subspec_reject(4, 100, -1.0, 1.0, p, p, p, p, p, p, p, p, None, p, 1 << 20, None) == _lib.EINVAL
+    assert l.subspec_reject(4, 100, 1.0, 1.0, p, p, p, None, p, p, p, p, None, p, 1 << 20, None) == _lib.EINVAL
+    assert l.subspec_reject(4, 100, 1.0, 1.0, p, p, p, p, p, p, p, p, None, p, 64, None) == _lib.EWORKSPACE
+    assert l.subspec_reject(4, 1 << 25, 1.0, 1.0, p, p, p, p, p, p, p, p, None, p, 1 << 20, None) == _lib.EINVAL
+    del args
+
+
+def _fake_model(n_layers=1, head_dim=128, hidden=256, ffn=512, w4_bad=False):
+    p = 4096
+    H, F, Hq, Hkv = hidden, ffn, 2, 1
+    qkv = (Hq + 2 * Hkv) * head_dim
+    layers = (_lib.Layer * n_layers)()
+    for l in range(n_layers):
+        L = layers[l]
+        L.attn_norm = L.ffn_norm = p
+        L.qkv = _lib.Linear(p, None, None, qkv, H)
+        L.o = _lib.Linear(p, None, None, H, Hq * head_dim)
+        L.gate_up = _lib.Linear(p, None, None, 2 * F, H)
+        L.down = _lib.Linear(p, None, None, H, F)
+        L.qkv_d = _lib.Linear(None, p, p, qkv, H)
+        L.o_d = _lib.Linear(None, p, p, H, Hq * head_dim)
+        L.gate_up_d = _lib.Linear(None, p, p, 2 * F, H) if not w4_bad else _lib.Linear(p, p, p, 2 * F, H)
+        L.down_d = _lib.Linear(p, None, None, H, F)
+    m = _lib.Model(n_layers, H, F, Hq, Hkv, head_dim, 1000, 1e6, 1e-6, p, p, p,
+                   ctypes.cast(layers, ctypes.POINTER(_lib.Layer)))
+    return m, layers
+
+
+def test_model_validation_and_workspace_size():
+    l = _lib.lib()
+    m, keep = _fake_model()
+    n1 = l.subspec_workspace_bytes(ctypes.byref(m), 1, 1024)
+    n17 = l.subspec_workspace_bytes(ctypes.byref(m), 17, 1024)
+    assert n1 > 64 * 1024 and n17 > n1
+    assert l.subspec_workspace_bytes(ctypes.byref(m), 65, 1024) == 0
+    bad, keep2 = _fake_model(head_dim=64)
+    assert l.subspec_workspace_bytes(ctypes.byref(bad), 1, 1024) == 0
+    assert "head_dim" in _lib.last_error()
+    bad2, keep3 = _fake_model(w4_bad=True)
+    assert l.subspec_workspace_bytes(ctypes.byref(bad2), 1, 1024) == 0
+    assert "gate_up_d" in _lib.last_error()
+
+
+def test_draft_verify_argument_errors():
+    l = _lib.lib()
+    m, keep = _fake_model()
+    p = 4096
+    st = _lib.State(p, p, 1024, p, p, p, 4)
+    ws = V(p)
+    assert l.subspec_draft_step(ctypes.byref(m), ctypes.byref(st), 4, 0.0, None, ws, 1 << 30, None) == _lib.EINVAL
+    assert l.subspec_draft_step(ctypes.byref(m), ctypes.byref(st), 0, 0.5, None, ws, 1 << 30, None) == _lib.EINVAL
+    assert l.subspec_draft_step(ctypes.byref(m), ctypes.byref(st), 0, 0.0, None, ws, 128, None) == _lib.EWORKSPACE
+    assert l.subspec_verify(ctypes.byref(m), ctypes.byref(st), 0, V(p), None, ws, 1 << 30, None) == _lib.EINVAL
+    assert l.subspec_verify(ctypes.byref(m), ctypes.byref(st), 65, V(p), None, ws, 1 << 30, None) == _lib.EINVAL
+    st_small = _lib.State(p, p, 8, p, p, p, 4)
+    assert l.subspec_verify(ctypes.byref(m), ctypes.byref(st_small), 17, V(p), None, ws, 1 << 30, None) == _lib.ECAPACITY
+    st_null = _lib.State(None, p, 1024, p, p, p, 4)
+    assert l.subspec_verify(ctypes.byref(m), ctypes.byref(st_null), 4, V(p), None, ws, 1 << 30, None) == _lib.EINVAL
+    assert l.subspec_kv_rollback(ctypes.byref(st), None, V(p), None) == _lib.EINVAL
+    assert l.subspec_kv_advance(None, 1, None) == _lib.EINVAL
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError):
+        _lib.lib()

@@ -1,0 +1,185 @@
+"""Model-level parity: draft step, verify pass and whole cycles on the GPU
+against the oracle forward, on seeded random-init models."""
+import numpy as np
+import pytest
+import torch
+
+from oracle.cycle import speculative_generate, autoregressive_generate
+from oracle.model import forward, new_kv
+from oracle.sampling import argmax_lowest
+from self_speculative_decoding_w4a16_amd import _lib
+from self_speculative_decoding_w4a16_amd.engine import SpecDecoder
+from self_speculative_decoding_w4a16_amd.model import DeviceModel
+from synth import model_weights, kv_history, token_ids, uniform_codes
+from synth.configs import QWEN7B
+from tests.gpu_util import codes_i32, log, rel_err
+from tests.helpers import host, oracle_model
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-2
+
+TINY = QWEN7B.with_(n_layers=3, hidden=256, ffn=512, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                    vocab=1000, n_shared=1)
+
+
+def _argmax_ok(gpu_tok, gpu_logits, ref_logits):
+    """GPU token is the argmax of its own logits, and the oracle's argmax unless
+    the oracle's top logits are tied within the logits tolerance."""
+    g = np.asarray(gpu_logits, np.float64)
+    r = np.asarray(ref_logits, np.float64)
+    assert gpu_tok == argmax_lowest(g)
+    ro = argmax_lowest(r)
+    if gpu_tok != ro:
+        assert r[ro] - r[gpu_tok] <= TOL * np.abs(r).max(), (gpu_tok, ro)
+    return gpu_tok == ro
+
+
+def _setup(shape, seed, cap, gamma, kv_len, subs=None, T=0.0, Td=0.0, device="cuda"):
+    w = model_weights(shape, seed, device)
+    dm = DeviceModel(shape, w, subs)
+    dec = SpecDecoder(dm, cap, gamma, T, Td)
+    K, V = kv_history(shape.n_layers, shape.n_kv_heads, kv_len, shape.head_dim, cap, seed + 7, device)
+    dec.k_cache.copy_(K)
+    dec.v_cache.copy_(V)
+    om = oracle_model(shape, w, dm.substitute_layers)
+    kv = (host(K).astype(np.float64), host(V).astype(np.float64))
+    return dm, dec, om, kv
+
+
+@pytest.mark.parametrize("shape_name", ["tiny", "layer7b"])
+def test_draft_step_and_verify_match_oracle(cuda, shape_name):
+    if shape_name == "tiny":
+        shape, kv_len, cap = TINY, 100, 256
+    else:
+        shape, kv_len, cap = QWEN7B.with_(n_layers=1, n_shared=0), 1024, 1088
+    gamma = 16
+    log(f"draft/verify parity {shape_name}")
+    dm, dec, om, kv = _setup(shape, 3, cap, gamma, kv_len)
+    toks = token_ids(gamma + 1, shape.vocab, 11)
+    dec.reset(kv_len, toks[0])
+    # draft step 0
+    _lib.draft_step(dm.c, dec.c, 0, 0.0, None, dec.ws)
+    torch.cuda.synchronize()
+    ref = forward(om, (kv[0].copy(), kv[1].copy()), kv_len, [int(toks[0])], draft=True)[0]
+    got = host(dec.draft_logits[0])
+    assert rel_err(got, ref) < TOL
+    _argmax_ok(int(dec.tokens[1].item()), got, ref)
+    # verify gamma+1 positions (synthetic draft tokens)
+    dec.tokens.copy_(torch.tensor(toks, dtype=torch.int32))
+    dec.verify()
+    torch.cuda.synchronize()
+    kv2 = (kv[0].copy(), kv[1].copy())
+    ref_v = forward(om, kv2, kv_len, [int(t) for t in toks], draft=False)
+    got_v = host(dec.target_logits)
+    for j in range(gamma + 1):
+        assert rel_err(got_v[j], ref_v[j]) < TOL, j
+    # committed target K/V of the verified positions
+    kc = host(dec.k_cache[:, :, kv_len:kv_len + gamma + 1])
+    vc = host(dec.v_cache[:, :, kv_len:kv_len + gamma + 1])
+    assert rel_err(kc, kv2[0][:, :, kv_len:kv_len + gamma + 1]) < TOL
+    assert rel_err(vc, kv2[1][:, :, kv_len:kv_len + gamma + 1]) < TOL
+    # history untouched
+    assert torch.equal(dec.k_cache[:, :, :kv_len].cpu(), torch.from_numpy(kv[0][:, :, :kv_len]).to(torch.bfloat16))
+
+
+def test_verify_row_equals_draft_decode_when_shared(cuda):
+    # with no substitutes, draft step i and verify row i run the same weights
+    shape = TINY.with_(n_shared=TINY.n_layers)
+    dm, dec, om, kv = _setup(shape, 5, 256, 4, 40, subs=[])
+    toks = token_ids(1, shape.vocab, 2)
+    dec.reset(40, toks[0])
+    dec.draft()
+    dec.verify()
+    torch.cuda.synchronize()
+    d = host(dec.draft_logits)
+    v = host(dec.target_logits)
+    for i in range(4):
+        assert rel_err(d[i], v[i]) < TOL
+    # the draft tokens were drawn greedily from the same model: verify accepts them all
+    dec.reject()
+    torch.cuda.synchronize()
+    assert int(dec.n_accepted.item()) == 4
+
+
+def test_greedy_generation_matches_oracle(cuda):
+    log("greedy generation tiny")
+    dm, dec, om, _ = _setup(TINY, 8, 256, 4, 0)
+    prompt = [int(t) for t in token_ids(9, TINY.vocab, 13)]
+    G = 24
+    got, ns = dec.generate(prompt, G)
+    ref_sd, ref_ns = speculative_generate(om, prompt, G, 4, 0.0, 0.0, None_uniforms(64, 4), 256)
+    ref_ar = autoregressive_generate(om, prompt, G, 0.0, np.zeros(G, np.int64), 256)
+    assert ref_sd == ref_ar
+    assert got == ref_sd
+    assert ns == ref_ns[:len(ns)]
+    assert int(dec.kv_len.item()) == len(prompt) - 1 + sum(n + 1 for n in ns)
+
+
+def None_uniforms(cycles, gamma):
+    z = np.zeros((cycles, gamma), np.int64)
+    return z, z, np.zeros(cycles, np.int64)
+
+
+def _exact_weights(shape, seed, device):
+    """A model whose forward is exact in float32 and float64 alike: zero layer
+    weights (every layer is the identity on the residual stream), embedding
+    rows of +-1 (RMSNorm maps them to +-1 exactly in bf16) and an lm_head of
+    small multiples of 2^-4, so every logit is an exact sum.  Draft and
+    target then see bit-identical logits and every stochastic decision must
+    agree exactly."""
+    w = model_weights(shape, seed, device)
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    for lw in w["layers"]:
+        for name in ("qkv", "o", "gate_up", "down"):
+            lw[name].zero_()
+    sign = torch.randint(0, 2, (shape.vocab, shape.hidden), generator=g) * 2 - 1
+    w["embed"].copy_(sign.to(torch.bfloat16))
+    lm = torch.randint(-1, 2, (shape.vocab, shape.hidden), generator=g).float() * 0.0625
+    w["lm_head"].copy_(lm.to(torch.bfloat16))
+    return w
+
+
+@pytest.mark.parametrize("T,Td", [(1.0, 1.0), (1.0, 0.5), (0.6, 0.0), (0.0, 0.2)])
+def test_stochastic_generation_exact_model(cuda, T, Td):
+    log(f"stochastic exact-model generation T={T} Td={Td}")
+    shape = TINY
+    gamma, G = 4, 24
+    w = _exact_weights(shape, 21, cuda)
+    dm = DeviceModel(shape, w)
+    dec = SpecDecoder(dm, 256, gamma, T, Td)
+    om = oracle_model(shape, w, dm.substitute_layers)
+    prompt = [int(t) for t in token_ids(5, shape.vocab, 23)]
+    cycles = G
+    Ud, _ = uniform_codes(cycles * gamma, 91)
+    R, _ = uniform_codes(cycles * gamma, 92)
+    Uf, _ = uniform_codes(cycles, 93)
+    Ud, R = Ud.reshape(cycles, gamma), R.reshape(cycles, gamma)
+    uni = (codes_i32(Ud, cuda), codes_i32(R, cuda), codes_i32(Uf, cuda))
+    got, ns = dec.generate(prompt, G, uni)
+    ref, ref_ns = speculative_generate(om, prompt, G, gamma, T, Td, (Ud, R, Uf), 256)
+    assert got == ref
+    assert ns == ref_ns[:len(ns)]
+    if T > 0 and Td != T:
+        assert min(ns) < gamma  # the residual path was taken
+
+
+@pytest.mark.parametrize("T,Td", [(1.0, 1.0), (0.0, 0.2), (0.6, 0.6)])
+def test_stochastic_cycles_random_model_properties(cuda, T, Td):
+    """Random-init model at T > 0: draws may part from the oracle's at CDF
+    boundaries (logits agree to the bf16 tolerance only), so this checks the
+    invariants of every cycle instead of tokens."""
+    log(f"stochastic cycles T={T} Td={Td}")
+    gamma, cycles = 4, 12
+    dm, dec, om, _ = _setup(TINY, 9, 256, gamma, 0, T=T, Td=Td)
+    prompt = [int(t) for t in token_ids(7, TINY.vocab, 17)]
+    Ud, _ = uniform_codes(cycles * gamma, 81)
+    R, _ = uniform_codes(cycles * gamma, 82)
+    Uf, _ = uniform_codes(cycles, 83)
+    Ud, R = Ud.reshape(cycles, gamma), R.reshape(cycles, gamma)
+    uni = (codes_i32(Ud, cuda), codes_i32(R, cuda), codes_i32(Uf, cuda))
+    G = 12
+    got, ns = dec.generate(prompt, G, uni)
+    assert len(got) == G and all(0 <= t < TINY.vocab for t in got)
+    assert all(0 <= n <= gamma for n in ns)
+    assert int(dec.kv_len.item()) == len(prompt) - 1 + sum(n + 1 for n in ns)
+    assert int(dec.status.item()) == 0
