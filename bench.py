@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Speculative-decoding throughput on one MI355X.
+
+Workload (default): the full 28-layer Qwen2.5-7B-shaped random-init model,
+vocab 152064; layers 0-10 shared in bf16, layers 11-27 replaced in the draft
+by 4-bit group-64 substitutes; chain draft gamma = 16, verify 17 positions,
+greedy (T = 0); a 512-token synthetic prompt (prefilled, not timed) and 256
+generated tokens.  One step = one generation of 256 tokens from the prompt
+state (every speculative cycle it takes: draft, verify, reject, rollback).
+
+Prints one JSON line: tokens/s, the roofline of the dominant kernel (HIP
+events around every launch of an extra, instrumented step), and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="full7b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ar", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the "
+              "multi-GPU design is described in DESIGN.md and is not built.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from self_speculative_decoding_w4a16_amd import _lib
+    from self_speculative_decoding_w4a16_amd.engine import SpecDecoder
+    from self_speculative_decoding_w4a16_amd.model import DeviceModel
+    from synth import CONFIGS, model_weights, token_ids, uniform_codes
+
+    wl = CONFIGS[args.config]
+    shape = wl.shape
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    _lib.lib()
+    log(f"building {shape.name}: {shape.n_layers} layers, vocab {shape.vocab}")
+    w = model_weights(shape, 0, dev)
+    dm = DeviceModel(shape, w)
+    torch.cuda.synchronize()
+    gamma, G = wl.gamma, wl.generate
+    cap = ((wl.prompt + G + gamma + 1 + 63) // 64) * 64 + 64
+    dec = SpecDecoder(dm, cap, gamma, wl.temp, wl.draft_temp)
+    prompt = [int(t) for t in token_ids(wl.prompt, shape.vocab, 5)]
+    t0 = time.time()
+    dec.prefill(prompt)
+    torch.cuda.synchronize()
+    log(f"prefill {len(prompt)} tokens in {time.time() - t0:.2f}s")
+    kv0, last = len(prompt) - 1, prompt[-1]
+
+    stochastic = wl.temp > 0 or wl.draft_temp > 0
+    uni = None
+    if stochastic:
+        C = G + 1
+        Ud, _ = uniform_codes(C * gamma, 101)
+        R, _ = uniform_codes(C * gamma, 102)
+        Uf, _ = uniform_codes(C, 103)
+        cvt = lambda a: torch.tensor(a.astype(np.int32), device=dev)
+        uni = (cvt(Ud).view(C, gamma), cvt(R).view(C, gamma), cvt(Uf))
+
+    def one_generation():
+        dec.reset(kv0, last)
+        out, ns = [], []
+        c = 0
+        while len(out) < G:
+            if uni is not None:
+                dec.cycle(uni[0][c], uni[1][c], uni[2][c:c + 1])
+            else:
+                dec.cycle()
+            n = int(dec.n_accepted.item())
+            out += dec.out_tokens[:n + 1].tolist()
+            ns.append(n)
+            c += 1
+        return out[:G], ns
+
+    for i in range(args.warmup):
+        one_generation()
+        log(f"warmup {i} done")
+    torch.cuda.synchronize()
+    all_ns = []
+    outs = []
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        o, ns = one_generation()
+        all_ns += ns
+        outs.append(o)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    tok_s = args.steps * G / elapsed
+    tau = float(np.mean([n + 1 for n in all_ns]))
+    cycles_per_gen = len(all_ns) / args.steps
+    log(f"timed {args.steps} steps: {tok_s:.2f} tok/s, tau {tau:.3f}, {cycles_per_gen:.1f} cycles/gen")
+    if not stochastic:
+        assert all(o == outs[0] for o in outs), "greedy generations differ between steps"
+
+    # ---------------------------------------------------------------- phases
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    dec.reset(kv0, last)
+    e = [ev() for _ in range(5)]
+    e[0].record()
+    dec.draft(uni[0][0] if uni else None)
+    e[1].record()
+    dec.verify()
+    e[2].record()
+    dec.reject(uni[1][0] if uni else None, uni[2][0:1] if uni else None)
+    e[3].record()
+    dec.commit()
+    e[4].record()
+    torch.cuda.synchronize()
+    draft_ms = e[0].elapsed_time(e[1])
+    verify_ms = e[1].elapsed_time(e[2])
+    reject_ms = e[2].elapsed_time(e[3])
+
+    # ---------------------------------------------------------------- kernels
+    _lib.profile_start(400000)
+    one_generation()
+    torch.cuda.synchronize()
+    _lib.profile_stop()
+    kern = {}
+    for k, name in enumerate(_lib.K_NAMES):
+        n, ms, by = _lib.profile_read(k)
+        kern[name] = {"launches": n, "ms": round(ms, 4),
+                      "avg_us": round(1000 * ms / n, 3) if n else None,
+                      "gbs": round(by / (ms * 1e-3) / 1e9, 1) if ms > 0 and by > 0 else None,
+                      "bytes_per_launch": round(by / n) if n else None}
+    log("kernels: " + json.dumps(kern))
+
+    def roof(name):
+        k = kern[name]
+        if not k["launches"] or not k["gbs"]:
+            return None
+        return {"bound": "hbm", "achieved": k["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(k["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": name, "avg_us": k["avg_us"], "bytes_per_launch": k["bytes_per_launch"]}
+
+    timed = [n for n in ("w4_gemv", "bf16_gemv", "verify_gemm") if kern[n]["launches"]]
+    dominant = max(timed, key=lambda n: kern[n]["ms"])
+
+    # ---------------------------------------------------------------- plain AR
+    ar = None
+    if not args.no_ar and not stochastic:
+        full = DeviceModel(shape, w, substitute_layers=[])
+        ar_dec = SpecDecoder(full, cap, 1, 0.0, 0.0)
+        ar_dec.k_cache.copy_(dec.k_cache)
+        ar_dec.v_cache.copy_(dec.v_cache)
+        ar_dec.reset(kv0, last)
+        for _ in range(4):
+            ar_dec.ar_step()
+        torch.cuda.synchronize()
+        ar_dec.reset(kv0, last)
+        n_ar = 64
+        t0 = time.perf_counter()
+        for _ in range(n_ar):
+            ar_dec.ar_step()
+        torch.cuda.synchronize()
+        ar = n_ar / (time.perf_counter() - t0)
+        del ar_dec, full
+        log(f"plain bf16 autoregressive decode: {ar:.2f} tok/s")
+
+    # ---------------------------------------------------------------- CPU oracle
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(shape, w, dm, wl, tau)
+
+    line = {
+        "metric": "spec-decode tokens/s @7B shape gamma=16; W4 GEMV & verify HBM GB/s vs peak",
+        "value": round(tok_s, 3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1000 * elapsed / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights, random prompt ids)",
+        "config": {"workload": f"{wl.name}: {shape.n_layers}-layer {shape.name} random-init, "
+                               f"{shape.n_shared} shared bf16 + {shape.n_layers - shape.n_shared} "
+                               f"W4 g64 substitute layers, vocab {shape.vocab}, gamma {gamma}, "
+                               f"T {wl.temp}, T_d {wl.draft_temp}, prompt {wl.prompt}, "
+                               f"generate {G}",
+                   "global_batch": 1, "seq_len": wl.prompt + G, "parallelism": "none (1 GPU)"},
+        "roofline": roof(dominant),
+        "roofline_w4_gemv": roof("w4_gemv"),
+        "roofline_verify_gemm": roof("verify_gemm"),
+        "roofline_bf16_gemv": roof("bf16_gemv"),
+        "cpu_baseline": cpu,
+        "tau": round(tau, 4),
+        "cycles_per_step": round(cycles_per_gen, 2),
+        "cycle_ms": {"draft_16_steps": round(draft_ms, 3), "verify": round(verify_ms, 3),
+                     "reject": round(reject_ms, 3)},
+        "plain_ar_tokens_s": round(ar, 3) if ar else None,
+        "kernels": kern,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(shape, w, dm, wl, tau):
+    """The oracle, untuned, on a bounded sample of the same workload: one
+    draft token through one shared bf16 layer, one W4 substitute layer and
+    the lm_head, and one 17-position verify through one layer and the
+    lm_head, all at full 7B shapes over a 600-position synthetic KV.  The
+    per-layer times are scaled to the 28-layer model, a cycle is 16 draft
+    steps + verify + reject, and tokens/s = tau (of the GPU run) / cycle."""
+    import numpy as np
+    import torch
+
+    from oracle.model import OracleModel, forward
+    from oracle.reject import reject
+    from synth import kv_history, logits_pair, token_ids
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count()
+    host = lambda t: t.detach().float().cpu().numpy()
+    log("cpu baseline: copying sampled layers to host")
+    base = dict(n_layers=0, hidden=shape.hidden, ffn=shape.ffn, n_q_heads=shape.n_q_heads,
+                n_kv_heads=shape.n_kv_heads, head_dim=shape.head_dim, vocab=shape.vocab,
+                rope_theta=shape.rope_theta, rms_eps=shape.rms_eps, embed=host(w["embed"]),
+                final_norm=host(w["final_norm"]), lm_head=host(w["lm_head"]), layers=[])
+    shared = {k: host(v) for k, v in w["layers"][0].items()}
+    subst = {k: host(v) for k, v in w["layers"][shape.n_shared].items()}
+    m0 = OracleModel(**base)
+    m_sh = OracleModel(**{**base, "n_layers": 1, "layers": [shared]})
+    m_w4 = OracleModel(**{**base, "n_layers": 1, "layers": [subst]})
+    t0 = time.perf_counter()
+    m_w4.make_substitutes([0])
+    t_quant = time.perf_counter() - t0
+    kv_len = 600
+    K, V = kv_history(1, shape.n_kv_heads, kv_len, shape.head_dim, kv_len + 32, 44, "cpu")
+    kv = lambda: (host(K).astype(np.float64), host(V).astype(np.float64))
+    toks = [int(t) for t in token_ids(17, shape.vocab, 45)]
+    K0 = np.zeros((0, shape.n_kv_heads, kv_len + 32, shape.head_dim))
+
+    def timed(fn):
+        t = time.perf_counter()
+        fn()
+        return time.perf_counter() - t
+
+    t_lm1 = timed(lambda: forward(m0, (K0, K0), kv_len, toks[:1], draft=True))
+    t_sh1 = timed(lambda: forward(m_sh, kv(), kv_len, toks[:1], draft=True))
+    t_w41 = timed(lambda: forward(m_w4, kv(), kv_len, toks[:1], draft=True))
+    t_lm17 = timed(lambda: forward(m0, (K0, K0), kv_len, toks, draft=False))
+    t_v17 = timed(lambda: forward(m_sh, kv(), kv_len, toks, draft=False))
+    zt, zd = logits_pair(wl.gamma, shape.vocab, 46)
+    zt, zd = host(zt), host(zd)
+    am = [int(np.argmax(zt[i])) for i in range(wl.gamma)]
+    t_rej = timed(lambda: reject(zt, zd, am, [0] * wl.gamma, 0, wl.temp, wl.draft_temp))
+    L, S = shape.n_layers, shape.n_shared
+    t_draft = S * max(t_sh1 - t_lm1, 0) + (L - S) * max(t_w41 - t_lm1, 0) + t_lm1
+    t_verify = L * max(t_v17 - t_lm17, 0) + t_lm17
+    cycle = wl.gamma * t_draft + t_verify + t_rej
+    sample_s = t_lm1 + t_sh1 + t_w41 + t_lm17 + t_v17 + t_rej
+    log(f"cpu baseline: draft step {t_draft:.2f}s, verify {t_verify:.2f}s, reject {t_rej:.2f}s "
+        f"(sample {sample_s:.1f}s, quantise {t_quant:.1f}s)")
+    return {"value": round(tau / cycle, 6), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"oracle (NumPy float64) timed on one shared bf16 layer, one W4 layer, the "
+                       f"lm_head and one reject round at full 7B shapes ({sample_s:.1f}s of CPU "
+                       f"work), scaled to {L} layers and a gamma={wl.gamma} cycle; tokens/s = "
+                       f"tau of the GPU run / oracle cycle time"),
+            "oracle_draft_step_s": round(t_draft, 3), "oracle_verify_s": round(t_verify, 3),
+            "oracle_reject_s": round(t_rej, 3)}
+
+
+if __name__ == "__main__":
+    main()

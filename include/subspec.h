@@ -226,6 +226,37 @@ int subspec_bf16_gemm(const uint16_t *w, int64_t n, int64_t k, const uint16_t *x
 int subspec_sample(const uint16_t *logits, int32_t vocab, float temp, const uint32_t *u_code,
                    int32_t *token, void *ws, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------------------ */
+/* Profiling (host side; off by default)                                     */
+/* ------------------------------------------------------------------------ */
+
+/* Kernel classes timed by the profiler. */
+enum {
+  SUBSPEC_K_W4_GEMV = 0,   /* draft GEMVs on 4-bit substitutes                  */
+  SUBSPEC_K_BF16_GEMV = 1, /* draft GEMVs on shared bf16 layers and lm_head     */
+  SUBSPEC_K_GEMM = 2,      /* verify GEMMs (matrix cores)                       */
+  SUBSPEC_K_ATTN = 3,      /* RoPE + KV append + attention                      */
+  SUBSPEC_K_SAMPLE = 4,    /* draft token draw                                  */
+  SUBSPEC_K_REJECT = 5,    /* rejection round                                   */
+  SUBSPEC_K_MISC = 6,      /* norms, embedding, KV bookkeeping                  */
+  SUBSPEC_K_CLASSES = 7
+};
+
+/* Start recording: from now on every launch made by this library on any
+ * stream is bracketed by a pair of HIP events on that stream, up to
+ * `max_records` launches (later launches are not recorded).  Creates the
+ * events (host-side objects; no device memory).  Returns SUBSPEC_EHIP if
+ * event creation fails. */
+int subspec_profile_start(int32_t max_records);
+
+/* Stop recording (events already recorded stay readable). */
+int subspec_profile_stop(void);
+
+/* Synchronise the recorded events and report, for kernel class `cls`, the
+ * number of launches, their summed duration in milliseconds and their summed
+ * algorithmic bytes (weights, activations and KV each counted once). */
+int subspec_profile_read(int32_t cls, int64_t *launches, double *total_ms, double *bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -78,7 +78,14 @@ _SIGS = {
                                     c_void_p, c_size_t, c_void_p]),
     "subspec_sample": (c_int32, [c_void_p, c_int32, c_float, c_void_p, c_void_p, c_void_p,
                                  c_size_t, c_void_p]),
+    "subspec_profile_start": (c_int32, [c_int32]),
+    "subspec_profile_stop": (c_int32, []),
+    "subspec_profile_read": (c_int32, [c_int32, POINTER(c_int64), POINTER(ctypes.c_double),
+                                       POINTER(ctypes.c_double)]),
 }
+
+K_W4_GEMV, K_BF16_GEMV, K_GEMM, K_ATTN, K_SAMPLE, K_REJECT, K_MISC = range(7)
+K_NAMES = ("w4_gemv", "bf16_gemv", "verify_gemm", "attention", "sample", "reject", "misc")
 
 EXPORTS = tuple(_SIGS)
 
@@ -191,3 +198,18 @@ def bf16_gemm(w, x, y, ws, stream=None):
 def sample(logits, temp, u_code, token, ws, stream=None):
     check(lib().subspec_sample(_p(logits), logits.numel(), temp, _p(u_code), _p(token), _p(ws),
                                ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def profile_start(max_records=200000):
+    check(lib().subspec_profile_start(max_records))
+
+
+def profile_stop():
+    check(lib().subspec_profile_stop())
+
+
+def profile_read(cls):
+    """(launches, total_ms, algorithmic bytes) recorded for kernel class cls."""
+    n, ms, b = c_int64(), ctypes.c_double(), ctypes.c_double()
+    check(lib().subspec_profile_read(cls, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(b)))
+    return n.value, ms.value, b.value

@@ -13,6 +13,7 @@
 
 #include "../../include/subspec.h"
 #include "internal.h"
+#include "profile.h"
 
 namespace {
 
@@ -43,10 +44,12 @@ constexpr size_t kCounterBytes = 64 * 1024;
 constexpr size_t kGemmCounterOff = 0;           // 4096 slots
 constexpr size_t kSampleCounterOff = 16 * 1024;
 constexpr size_t kRejectCounterOff = 16 * 1024 + 256;
+constexpr size_t kAttnCounterOff = 20 * 1024;  // one per kv head (<= 1024)
 constexpr int kMaxGemmCounters = 4096;
 constexpr int kMaxTokens = 64;
 constexpr int kMaxGemvK = 28672;  // x (2 B) + half-group sums in 64 KiB of LDS
 constexpr int kMaxGamma = 64;
+constexpr int kMaxNormK = 6144;  // 3 items of 8 values per thread, 256 threads
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -85,11 +88,15 @@ int check_model(const subspec_model* m) {
   if (m->head_dim != 128) return fail(SUBSPEC_EUNSUPPORTED, "head_dim must be 128");
   if (m->n_q_heads % m->n_kv_heads != 0)
     return fail(SUBSPEC_ESHAPE, "n_q_heads must be a multiple of n_kv_heads");
+  if (m->n_q_heads / m->n_kv_heads > 16 || m->n_kv_heads > 1024)
+    return fail(SUBSPEC_EUNSUPPORTED, "GQA group above 16 or more than 1024 kv heads");
   if (m->hidden % 128 != 0 || m->ffn % 128 != 0)
     return fail(SUBSPEC_ESHAPE, "hidden and ffn must be multiples of 128");
   if (m->hidden > kMaxGemvK || m->ffn > kMaxGemvK ||
       (int64_t)m->n_q_heads * m->head_dim > kMaxGemvK)
     return fail(SUBSPEC_EUNSUPPORTED, "GEMV input width above %d", kMaxGemvK);
+  if (m->hidden > kMaxNormK)
+    return fail(SUBSPEC_EUNSUPPORTED, "hidden above %d (norm-fused GEMV prologue)", kMaxNormK);
   if (m->vocab > (1 << 24)) return fail(SUBSPEC_EUNSUPPORTED, "vocab above 2^24");
   if (!(m->rms_eps > 0.0f) || !(m->rope_theta > 1.0f))
     return fail(SUBSPEC_EINVAL, "rms_eps must be > 0 and rope_theta > 1");
@@ -127,9 +134,9 @@ int check_state(const subspec_model* m, const subspec_state* st) {
 struct FwdWs {
   uint32_t* gemm_counters;
   uint32_t* sample_counter;
+  uint32_t* attn_counters;
   uint16_t *h, *xn, *qkv, *qrot, *attn, *act;
   float* attn_part;
-  int attn_splits;
   float* gemm_part;
   float* logit_max;
   int32_t* logit_arg;
@@ -155,6 +162,7 @@ size_t carve_fwd(const subspec_model* m, int mt, int cap, void* ws, FwdWs* o) {
   char* base = (char*)ws;
   w.gemm_counters = base ? (uint32_t*)(base + kGemmCounterOff) : nullptr;
   w.sample_counter = base ? (uint32_t*)(base + kSampleCounterOff) : nullptr;
+  w.attn_counters = base ? (uint32_t*)(base + kAttnCounterOff) : nullptr;
   c.off = kCounterBytes;
   const int64_t H = m->hidden, F = m->ffn, qd = (int64_t)m->n_q_heads * m->head_dim;
   const int64_t qkv = (int64_t)(m->n_q_heads + 2 * m->n_kv_heads) * m->head_dim;
@@ -164,11 +172,12 @@ size_t carve_fwd(const subspec_model* m, int mt, int cap, void* ws, FwdWs* o) {
   w.qrot = (uint16_t*)c.take((size_t)mt * qd * 2);
   w.attn = (uint16_t*)c.take((size_t)mt * qd * 2);
   w.act = (uint16_t*)c.take((size_t)mt * F * 2);
-  w.attn_splits = (cap + attn_keys_per_split() - 1) / attn_keys_per_split();
-  w.attn_part = (float*)c.take((size_t)m->n_q_heads * w.attn_splits * mt * (m->head_dim + 2) * 4);
+  // attention split partials [Hkv][ceil(cap/128)][mt][G][d + 4]
+  const size_t dsplits = (cap + decode_attn_keys_per_split() - 1) / decode_attn_keys_per_split();
+  const size_t part_floats = (size_t)m->n_q_heads * dsplits * mt * (m->head_dim + 4);
+  w.attn_part = (float*)c.take(part_floats * 4);
   w.gemm_part = (float*)c.take(max_gemm_partials(m, mt));
-  const int lm_blocks = (int)((m->vocab + gemv_rows_per_block(false, m->vocab, EPI_LOGITS) - 1) /
-                              gemv_rows_per_block(false, m->vocab, EPI_LOGITS));
+  const int lm_blocks = gemv_max_blocks(false, m->vocab, EPI_LOGITS);
   w.logit_max = (float*)c.take((size_t)lm_blocks * 4);
   w.logit_arg = (int32_t*)c.take((size_t)lm_blocks * 4);
   w.sample_sums = (unsigned long long*)c.take(64 * 8);
@@ -206,6 +215,18 @@ void set_linear(GemvArgs& a, const subspec_linear& l) {
   a.codes = l.codes;
   a.meta = l.meta;
 }
+
+// Algorithmic bytes of one launch: weights, input, output (and residual)
+// each counted once.
+double gemv_bytes(const subspec_linear& l, int64_t n_out, bool resid) {
+  const double n = (double)l.n, k = (double)l.k;
+  const double wb = lin_is_w4(l) ? n * k / 2 + n * (k / 64) * 4 : 2 * n * k;
+  return wb + 2 * k + 2 * (double)n_out * (resid ? 2 : 1);
+}
+double gemm_bytes(int64_t n_phys, int64_t k, int m, int64_t n_out, bool resid) {
+  return 2.0 * n_phys * k + 2.0 * m * k + 2.0 * m * n_out * (resid ? 2 : 1);
+}
+int gemv_class(const subspec_linear& l) { return lin_is_w4(l) ? SUBSPEC_K_W4_GEMV : SUBSPEC_K_BF16_GEMV; }
 
 }  // namespace
 
@@ -267,7 +288,10 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
   const int64_t qd = (int64_t)m->n_q_heads * d;
   const int64_t qkv = (int64_t)(m->n_q_heads + 2 * m->n_kv_heads) * d;
   int32_t* tok_out = st->tokens + step + 1;
-  HIPCHK(launch_pos_guard(st->kv_len, st->tokens + step, step, st->capacity, m->vocab, w.valid, tok_out, s));
+  {
+    prof::Scope ps(SUBSPEC_K_MISC, 0.0, s);
+    HIPCHK(launch_pos_guard(st->kv_len, st->tokens + step, step, st->capacity, m->vocab, w.valid, tok_out, s));
+  }
   for (int l = 0; l < m->n_layers; ++l) {
     const subspec_layer& L = m->layers[l];
     GemvArgs a{};
@@ -282,7 +306,10 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
     a.h_out = w.h;
     a.y = w.qkv;
     a.valid = w.valid;
-    HIPCHK(launch_gemv(lin_is_w4(L.qkv_d), l == 0 ? PRO_EMBED_NORM : PRO_NORM, EPI_STORE, a, s, nullptr));
+    {
+      prof::Scope ps(gemv_class(L.qkv_d), gemv_bytes(L.qkv_d, qkv, false), s);
+      HIPCHK(launch_gemv(lin_is_w4(L.qkv_d), l == 0 ? PRO_EMBED_NORM : PRO_NORM, EPI_STORE, a, s, nullptr));
+    }
 
     AttnArgs at{};
     at.qkv = w.qkv;
@@ -298,20 +325,31 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
     at.cap = st->capacity;
     at.theta = m->rope_theta;
     at.part = w.attn_part;
-    at.splits = w.attn_splits;
     at.out = w.attn;
-    HIPCHK(launch_rope_append(at, s));
-    HIPCHK(launch_attention(at, s));
+    at.splits = (st->capacity + decode_attn_keys_per_split() - 1) / decode_attn_keys_per_split();
+    {
+      prof::Scope ps(SUBSPEC_K_ATTN, 0.0, s);
+      HIPCHK(launch_decode_attention(at, w.valid, s));
+    }
 
     GemvArgs o{};
     set_linear(o, L.o_d);
     o.n = H;
     o.k = qd;
-    o.x = w.attn;
     o.y = w.h;
     o.resid = w.h;
     o.valid = w.valid;
-    HIPCHK(launch_gemv(lin_is_w4(L.o_d), PRO_X, EPI_RESID, o, s, nullptr));
+    o.attn_part = w.attn_part;
+    o.attn_splits = at.splits;
+    o.attn_kpb = decode_attn_keys_per_split();
+    o.n_kv = m->n_kv_heads;
+    o.attn_g = m->n_q_heads / m->n_kv_heads;
+    o.kv_len = st->kv_len;
+    o.pos_offset = step;
+    {
+      prof::Scope ps(gemv_class(L.o_d), gemv_bytes(L.o_d, H, true), s);
+      HIPCHK(launch_gemv(lin_is_w4(L.o_d), PRO_ATTN_MERGE, EPI_RESID, o, s, nullptr));
+    }
 
     GemvArgs g{};
     set_linear(g, L.gate_up_d);
@@ -322,7 +360,10 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
     g.eps = m->rms_eps;
     g.y = w.act;
     g.valid = w.valid;
-    HIPCHK(launch_gemv(lin_is_w4(L.gate_up_d), PRO_NORM, EPI_SILU, g, s, nullptr));
+    {
+      prof::Scope ps(gemv_class(L.gate_up_d), gemv_bytes(L.gate_up_d, F, false), s);
+      HIPCHK(launch_gemv(lin_is_w4(L.gate_up_d), PRO_NORM, EPI_SILU, g, s, nullptr));
+    }
 
     GemvArgs dn{};
     set_linear(dn, L.down_d);
@@ -332,7 +373,10 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
     dn.y = w.h;
     dn.resid = w.h;
     dn.valid = w.valid;
-    HIPCHK(launch_gemv(lin_is_w4(L.down_d), PRO_X, EPI_RESID, dn, s, nullptr));
+    {
+      prof::Scope ps(gemv_class(L.down_d), gemv_bytes(L.down_d, H, true), s);
+      HIPCHK(launch_gemv(lin_is_w4(L.down_d), PRO_X, EPI_RESID, dn, s, nullptr));
+    }
   }
   uint16_t* logits = st->draft_logits + (int64_t)step * m->vocab;
   GemvArgs lm{};
@@ -347,10 +391,17 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
   lm.part_arg = w.logit_arg;
   lm.valid = w.valid;
   int lm_blocks = 0;
-  HIPCHK(launch_gemv(false, PRO_NORM, EPI_LOGITS, lm, s, &lm_blocks));
+  {
+    const subspec_linear lml{m->lm_head, nullptr, nullptr, m->vocab, H};
+    prof::Scope ps(SUBSPEC_K_BF16_GEMV, gemv_bytes(lml, m->vocab, false), s);
+    HIPCHK(launch_gemv(false, PRO_NORM, EPI_LOGITS, lm, s, &lm_blocks));
+  }
   SampleWs sw{w.logit_max, w.logit_arg, w.sample_sums, w.sample_counter};
-  HIPCHK(launch_sample(logits, m->vocab, draft_temp, u_codes ? u_codes + step : nullptr, w.logit_max,
-                       w.logit_arg, lm_blocks, tok_out, w.valid, sw, s));
+  {
+    prof::Scope ps(SUBSPEC_K_SAMPLE, 2.0 * m->vocab, s);
+    HIPCHK(launch_sample(logits, m->vocab, draft_temp, u_codes ? u_codes + step : nullptr, w.logit_max,
+                         w.logit_arg, lm_blocks, tok_out, w.valid, sw, s));
+  }
   return ok();
 }
 
@@ -370,12 +421,21 @@ int subspec_verify(const subspec_model* m, const subspec_state* st, int32_t n_to
   const int64_t qd = (int64_t)m->n_q_heads * d;
   const int64_t qkv = (int64_t)(m->n_q_heads + 2 * m->n_kv_heads) * d;
   const int mt = n_tokens;
-  HIPCHK(launch_embed_rows(m->embed, tokens, mt, (int)H, m->vocab, w.h, s));
+  {
+    prof::Scope ps(SUBSPEC_K_MISC, 0.0, s);
+    HIPCHK(launch_embed_rows(m->embed, tokens, mt, (int)H, m->vocab, w.h, s));
+  }
   for (int l = 0; l < m->n_layers; ++l) {
     const subspec_layer& L = m->layers[l];
-    HIPCHK(launch_rmsnorm_rows(w.h, L.attn_norm, m->rms_eps, mt, (int)H, w.xn, s));
+    {
+      prof::Scope ps(SUBSPEC_K_MISC, 0.0, s);
+      HIPCHK(launch_rmsnorm_rows(w.h, L.attn_norm, m->rms_eps, mt, (int)H, w.xn, s));
+    }
     GemmArgs q{L.qkv.w, qkv, H, w.xn, mt, w.qkv, qkv, nullptr, w.gemm_part, w.gemm_counters};
-    HIPCHK(launch_gemm(GEPI_STORE, q, s));
+    {
+      prof::Scope ps(SUBSPEC_K_GEMM, gemm_bytes(qkv, H, mt, qkv, false), s);
+      HIPCHK(launch_gemm(GEPI_STORE, q, s));
+    }
     AttnArgs at{};
     at.qkv = w.qkv;
     at.q_rot = w.qrot;
@@ -390,22 +450,41 @@ int subspec_verify(const subspec_model* m, const subspec_state* st, int32_t n_to
     at.cap = st->capacity;
     at.theta = m->rope_theta;
     at.part = w.attn_part;
-    at.splits = w.attn_splits;
     at.out = w.attn;
-    HIPCHK(launch_rope_append(at, s));
-    HIPCHK(launch_attention(at, s));
+    at.splits = (st->capacity + decode_attn_keys_per_split() - 1) / decode_attn_keys_per_split();
+    {
+      prof::Scope ps(SUBSPEC_K_ATTN, 0.0, s);
+      HIPCHK(launch_rope_append(at, s));
+      HIPCHK(launch_rows_attention(at, s));
+    }
     GemmArgs o{L.o.w, H, qd, w.attn, mt, w.h, H, w.h, w.gemm_part, w.gemm_counters};
-    HIPCHK(launch_gemm(GEPI_RESID, o, s));
-    HIPCHK(launch_rmsnorm_rows(w.h, L.ffn_norm, m->rms_eps, mt, (int)H, w.xn, s));
+    {
+      prof::Scope ps(SUBSPEC_K_GEMM, gemm_bytes(H, qd, mt, H, true), s);
+      HIPCHK(launch_gemm(GEPI_RESID, o, s));
+    }
+    {
+      prof::Scope ps(SUBSPEC_K_MISC, 0.0, s);
+      HIPCHK(launch_rmsnorm_rows(w.h, L.ffn_norm, m->rms_eps, mt, (int)H, w.xn, s));
+    }
     GemmArgs g{L.gate_up.w, F, H, w.xn, mt, w.act, F, nullptr, w.gemm_part, w.gemm_counters};
-    HIPCHK(launch_gemm(GEPI_SILU, g, s));
+    {
+      prof::Scope ps(SUBSPEC_K_GEMM, gemm_bytes(2 * F, H, mt, F, false), s);
+      HIPCHK(launch_gemm(GEPI_SILU, g, s));
+    }
     GemmArgs dn{L.down.w, H, F, w.act, mt, w.h, H, w.h, w.gemm_part, w.gemm_counters};
-    HIPCHK(launch_gemm(GEPI_RESID, dn, s));
+    {
+      prof::Scope ps(SUBSPEC_K_GEMM, gemm_bytes(H, F, mt, H, true), s);
+      HIPCHK(launch_gemm(GEPI_RESID, dn, s));
+    }
   }
   if (logits) {
-    HIPCHK(launch_rmsnorm_rows(w.h, m->final_norm, m->rms_eps, mt, (int)H, w.xn, s));
+    {
+      prof::Scope ps(SUBSPEC_K_MISC, 0.0, s);
+      HIPCHK(launch_rmsnorm_rows(w.h, m->final_norm, m->rms_eps, mt, (int)H, w.xn, s));
+    }
     GemmArgs lm{m->lm_head, m->vocab, H, w.xn, mt, logits, m->vocab, nullptr, w.gemm_part,
                 w.gemm_counters};
+    prof::Scope ps(SUBSPEC_K_GEMM, gemm_bytes(m->vocab, H, mt, m->vocab, false), s);
     HIPCHK(launch_gemm(GEPI_STORE, lm, s));
   }
   return ok();
@@ -429,6 +508,7 @@ int subspec_reject(int32_t gamma, int32_t vocab, float temp, float draft_temp,
   if ((r = need_ws(ws, ws_bytes, carve_reject(gamma, vocab, nullptr, nullptr)))) return r;
   RejectWs rw;
   carve_reject(gamma, vocab, ws, &rw);
+  prof::Scope ps(SUBSPEC_K_REJECT, 2.0 * (2 * gamma + 1) * vocab, hs(stream));
   HIPCHK(launch_reject(gamma, vocab, temp, draft_temp, target_logits, draft_logits, draft_tokens,
                        r_codes, u_code, n_accepted, out_tokens, status, probs, rw, hs(stream)));
   return ok();
@@ -438,6 +518,7 @@ int subspec_kv_rollback(const subspec_state* st, const int32_t* n_accepted,
                         const int32_t* out_tokens, void* stream) {
   if (!st || !st->kv_len || !st->tokens) return fail(SUBSPEC_EINVAL, "state kv_len/tokens NULL");
   if (!n_accepted || !out_tokens) return fail(SUBSPEC_EINVAL, "n_accepted and out_tokens must be set");
+  prof::Scope ps(SUBSPEC_K_MISC, 0.0, hs(stream));
   HIPCHK(launch_kv_rollback(st->kv_len, st->tokens, n_accepted, out_tokens, hs(stream)));
   return ok();
 }

@@ -4,20 +4,19 @@
 // draft and target read and write one cache ("SubSpec: Speculate Deep and
 // Accurate" paper note, Method details, KV-cache sharing).
 //
-// Three kernels:
-//  rope_append  rotate-half RoPE of q and k (angles in float64, applied in
-//               float32), q -> q_rot, k/v -> cache at their positions.
-//  attn_part    grid (kv head, key split): the GQA group's query rows against
-//               up to 64 keys staged in LDS; per row a partial (max, sum, o[d]).
-//  attn_combine grid (q head, row): merges the splits in split order.
+// Kernels:
+//  rope_append        rotate-half RoPE of q and k for the verify rows (angles
+//                     in float64, applied in float32); q -> q_rot, k/v -> cache.
+//  decode_attn        grid (kv head, 128-key split[, row]): per split partial
+//                     (max, sum, o[d]) for every query head of the GQA group.
+//  rows_merge         merges the verify partials in split order.
+// The draft step's partials are merged by the output projection's prologue.
 #include "common.h"
 #include "internal.h"
 
 namespace {
 
-constexpr int KPS = 64;    // keys per split
 constexpr int D = 128;     // head dim handled by these kernels
-constexpr int QB = 32;     // query rows per pass inside a block
 
 __global__ __launch_bounds__(64) void rope_append_kernel(AttnArgs a) {
   const int j = blockIdx.x;          // query row
@@ -53,152 +52,250 @@ __global__ __launch_bounds__(64) void rope_append_kernel(AttnArgs a) {
   }
 }
 
-// rows of the GQA group: r = g * m + j  (g: q head within the group, j: position row)
-__global__ __launch_bounds__(256) void attn_part_kernel(AttnArgs a) {
-  __shared__ u32x4 ks[KPS][D / 8 + 1];  // padded: conflict-free 16-byte reads
-  __shared__ u32x4 vs[KPS][D / 8 + 1];
-  __shared__ float qs[QB][D];          // 16 KB
-  __shared__ float sc[QB][KPS + 1];    // 8.3 KB
-  __shared__ float rmax[QB], rsum[QB];
+// ----------------------------------------------------------------------------
+// Decode attention for one query position (the draft step): grid (kv head,
+// key split of DKPB keys), 512 threads.  Every block rotates the GQA group's
+// queries itself; the block whose split holds the new position rotates the
+// new key, appends K/V to the cache and uses them directly (no other block
+// reads that position in this launch).  Thread (key j, quarter c) holds 32
+// dims of K[j] and V[j]; scores are reduced over the 4 quarters with lane
+// shuffles.  Each block writes, per query head of its group, the partial
+// (max m, sum l, o[d] = sum_j exp(s_j - m) V[j][d]) of its split; the
+// consumer (the output projection's prologue) merges the splits, so no
+// block waits on another.
+constexpr int DKPB = 128;
+constexpr int DREC = 4 + D;  // partial record: m, l, 2 pad, o[D] (16-byte aligned o)
 
-  const int hk = blockIdx.x, split = blockIdx.y;
-  const int tid = threadIdx.x;
+// CACHED = false: the draft step (one row, q and the new k/v rotated and
+// appended here).  CACHED = true: verify rows (blockIdx.z = row j at position
+// kv_len + j; rope_append already wrote q_rot and the cache), causal limit
+// kv_len + j, partials at [kv head][split][row][group head].
+template <bool CACHED>
+__global__ __launch_bounds__(512) void decode_attn_kernel(AttnArgs a, const int32_t* valid) {
+  constexpr int GMAX = 16;
+  constexpr int NW = 8;                    // waves per block
+  __shared__ float qs[GMAX][D];            // rotated queries (float)
+  __shared__ float kn[D];                  // rotated new key
+  __shared__ u32x4 vs[DKPB][D / 8 + 1];    // V tile (padded rows)
+  __shared__ float ps[GMAX][DKPB];         // probabilities p[h][key]
+  __shared__ float wmax[NW][GMAX], wsum[NW][GMAX];
+  __shared__ float hmax[GMAX];
+  __shared__ float rc[D / 2], rs[D / 2];
+
+  if (valid && *valid == 0) return;
+  const int hk = blockIdx.x, split = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int G = a.n_q / a.n_kv;
-  const int base = *a.kv_len + a.pos_offset;      // position of row 0
-  int n_keys = base + a.m;                         // keys visible to the last row
-  if (n_keys > a.cap) n_keys = a.cap;
-  const int k0 = split * KPS;
-  if (k0 >= n_keys) return;
-  const int nk = min(KPS, n_keys - k0);
-  const float scale = 0.088388347648318440f;  // 1/sqrt(128)
+  const int row = CACHED ? (int)blockIdx.z : 0;
+  const int pos = *a.kv_len + a.pos_offset + row;  // position of this query (its last key)
+  if (pos < 0 || pos >= a.cap) return;
+  const int n_keys = pos + 1;
+  const int active = (n_keys + DKPB - 1) / DKPB;
+  if (split >= active) return;
+  const int k0 = split * DKPB;
+  const int nk = min(DKPB, n_keys - k0);
+  const bool has_new = !CACHED && (k0 + nk - 1) == pos;
 
-  const u32x4* kg = reinterpret_cast<const u32x4*>(a.k_cache + ((int64_t)hk * a.cap + k0) * D);
-  const u32x4* vg = reinterpret_cast<const u32x4*>(a.v_cache + ((int64_t)hk * a.cap + k0) * D);
-  for (int e = tid; e < nk * (D / 8); e += 256) {
-    ks[e / (D / 8)][e % (D / 8)] = kg[e];
-    vs[e / (D / 8)][e % (D / 8)] = vg[e];
+  // ---- loads: thread (key j, quarter c) takes 32 dims of K[j] and V[j]
+  const int j = tid >> 2, c = tid & 3;
+  const bool kvalid = j < nk && (CACHED || (k0 + j) != pos);
+  u32x4 kr[4], vr[4];
+  {
+    const int64_t row = (int64_t)hk * a.cap + k0 + (kvalid ? j : 0);
+    const u32x4* kp = reinterpret_cast<const u32x4*>(a.k_cache + row * D) + 4 * c;
+    const u32x4* vp = reinterpret_cast<const u32x4*>(a.v_cache + row * D) + 4 * c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kr[i] = kvalid ? kp[i] : u32x4{0u, 0u, 0u, 0u};
+      vr[i] = kvalid ? vp[i] : u32x4{0u, 0u, 0u, 0u};
+    }
   }
-
-  const int total_rows = G * a.m;
-  for (int r0 = 0; r0 < total_rows; r0 += QB) {
-    const int nr = min(QB, total_rows - r0);
-    __syncthreads();
-    for (int e = tid; e < nr * D; e += 256) {
-      const int rr = e / D, dd = e % D;
-      const int r = r0 + rr, g = r / a.m, j = r % a.m;
-      qs[rr][dd] = ss::bf2f(a.q_rot[((int64_t)j * a.n_q + hk * G + g) * D + dd]);
+  // ---- RoPE: the 64 angles once per block in float64, applied in float32
+  const int half = D / 2;
+  if (CACHED) {
+    for (int e = tid; e < G * D; e += 512) {
+      const int h = e / D, i = e % D;
+      qs[h][i] = ss::bf2f(a.q_rot[((int64_t)row * a.n_q + hk * G + h) * D + i]);
     }
-    __syncthreads();
-    // scores: thread -> (key, row group of 8)
-    {
-      const int key = tid & 63, rg = tid >> 6;
-      float acc[8];
+  } else if (tid < half) {
+    const double inv_freq = exp(-(2.0 * tid / D) * log((double)a.theta));
+    double sd, cd;
+    sincos((double)pos * inv_freq, &sd, &cd);
+    rc[tid] = (float)cd;
+    rs[tid] = (float)sd;
+  }
+  __syncthreads();
+  for (int e = tid; !CACHED && e < (G + (has_new ? 1 : 0)) * half; e += 512) {
+    const int h = e / half, i = e % half;
+    const float cs = rc[i], sn = rs[i];
+    const uint16_t* x = (h < G) ? a.qkv + (hk * G + h) * D : a.qkv + (a.n_q + hk) * D;
+    const float x1 = ss::bf2f(x[i]), x2 = ss::bf2f(x[i + half]);
+    const uint16_t r1 = ss::f2bf(x1 * cs - x2 * sn), r2 = ss::f2bf(x2 * cs + x1 * sn);
+    if (h < G) {
+      qs[h][i] = ss::bf2f(r1);
+      qs[h][i + half] = ss::bf2f(r2);
+    } else {
+      kn[i] = ss::bf2f(r1);
+      kn[i + half] = ss::bf2f(r2);
+      uint16_t* kc = a.k_cache + ((int64_t)hk * a.cap + pos) * D;
+      kc[i] = r1;
+      kc[i + half] = r2;
+    }
+  }
+  if (has_new && tid < D / 8) {
+    const u32x4* vsrc = reinterpret_cast<const u32x4*>(a.qkv + (a.n_q + a.n_kv + hk) * D);
+    u32x4* vdst = reinterpret_cast<u32x4*>(a.v_cache + ((int64_t)hk * a.cap + pos) * D);
+    const u32x4 v = vsrc[tid];
+    vdst[tid] = v;
+    vs[nk - 1][tid] = v;
+  }
+  if (kvalid) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) acc[t] = 0.0f;
-      if (key < nk) {
-        for (int dc = 0; dc < D / 8; ++dc) {
-          const u32x4 kv = ks[key][dc];
-          const float kf[8] = {ss::lo_bf(kv.x), ss::hi_bf(kv.x), ss::lo_bf(kv.y), ss::hi_bf(kv.y),
-                               ss::lo_bf(kv.z), ss::hi_bf(kv.z), ss::lo_bf(kv.w), ss::hi_bf(kv.w)};
+    for (int i = 0; i < 4; ++i) vs[j][4 * c + i] = vr[i];
+  }
+  __syncthreads();
+  // ---- scores: 32-dim partial dots, reduced over the 4 quarters of a key
+  float kf[32];
+  if (!CACHED && j < nk && (k0 + j) == pos) {
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const int rr = rg + 4 * t;
-            if (rr < nr) {
+    for (int i = 0; i < 32; ++i) kf[i] = kn[32 * c + i];
+  } else {
 #pragma unroll
-              for (int e = 0; e < 8; ++e) acc[t] += qs[rr][dc * 8 + e] * kf[e];
-            }
-          }
-        }
-      }
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int rr = rg + 4 * t;
-        if (rr < nr) {
-          const int j = (r0 + rr) % a.m;
-          const bool ok = key < nk && (k0 + key) <= base + j;
-          sc[rr][key] = ok ? acc[t] * scale : -INFINITY;
-        }
+      for (int t = 0; t < 4; ++t) {
+        kf[8 * i + 2 * t] = ss::lo_bf(w[t]);
+        kf[8 * i + 2 * t + 1] = ss::hi_bf(w[t]);
       }
     }
-    __syncthreads();
-    // row max / exp / sum: one wave per row, lanes over keys
-    {
-      const int lane = tid & 63, w = tid >> 6;
-      for (int rr = w; rr < nr; rr += 4) {
-        const float v = sc[rr][lane];
-        const float mx = ss::wave_max(v);
-        const float e = (mx == -INFINITY) ? 0.0f : expf(v - mx);
-        sc[rr][lane] = e;
-        const float sm = ss::wave_sum(e);
-        if (lane == 0) {
-          rmax[rr] = mx;
-          rsum[rr] = sm;
-        }
-      }
+  }
+  const float scale = 0.088388347648318440f;  // 1/sqrt(128)
+  float sc[GMAX];
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) {
+    float d = 0.0f;
+    if (h < G) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) d += qs[h][32 * c + i] * kf[i];
     }
-    __syncthreads();
-    // o[row][d] = sum_key p * v: thread -> (row, 16 dims)
-    for (int e = tid; e < nr * (D / 16); e += 256) {
-      const int rr = e / (D / 16), dq = e % (D / 16);
-      float o[16];
+    d += __shfl_xor(d, 1, 64);
+    d += __shfl_xor(d, 2, 64);
+    sc[h] = (j < nk) ? d * scale : -INFINITY;
+  }
+  // ---- softmax statistics per head over the block's keys
 #pragma unroll
-      for (int t = 0; t < 16; ++t) o[t] = 0.0f;
-      for (int key = 0; key < nk; ++key) {
-        const float p = sc[rr][key];
-        const u32x4 v0 = vs[key][2 * dq], v1 = vs[key][2 * dq + 1];
-        const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  for (int h = 0; h < GMAX; ++h) {
+    if (h < G) {
+      float m = sc[h];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          o[2 * t] += p * ss::lo_bf(vw[t]);
-          o[2 * t + 1] += p * ss::hi_bf(vw[t]);
-        }
-      }
-      const int r = r0 + rr, g = r / a.m, j = r % a.m;
-      float* dst = a.part + ((((int64_t)(hk * G + g) * a.splits + split) * a.m + j) * (D + 2));
+      for (int o = 4; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      if (lane == 0) wmax[wave][h] = m;
+    }
+  }
+  __syncthreads();
+  if (tid < G) {
+    float m = wmax[0][tid];
+    for (int w = 1; w < NW; ++w) m = fmaxf(m, wmax[w][tid]);
+    hmax[tid] = m;
+  }
+  __syncthreads();
 #pragma unroll
-      for (int t = 0; t < 16; ++t) dst[2 + dq * 16 + t] = o[t];
-      if (dq == 0) {
-        dst[0] = rmax[rr];
-        dst[1] = rsum[rr];
-      }
+  for (int h = 0; h < GMAX; ++h) {
+    if (h < G) {
+      const float p = (j < nk) ? expf(sc[h] - hmax[h]) : 0.0f;
+      if (c == 0) ps[h][j] = p;
+      float sm = (c == 0) ? p : 0.0f;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) sm += __shfl_xor(sm, o, 64);
+      if (lane == 0) wsum[wave][h] = sm;
+    }
+  }
+  __syncthreads();
+  // ---- o[h][d] = sum_j p[h][j] V[j][d]: thread -> (head, 2 dims)
+  const uint32_t* vw = reinterpret_cast<const uint32_t*>(&vs[0][0]);
+  constexpr int VROW = (D / 8 + 1) * 4;  // words per padded V row
+  for (int e = tid; e < G * (D / 2); e += 512) {
+    const int h = e / (D / 2), dp = e % (D / 2);
+    float o0 = 0.f, o1 = 0.f;
+#pragma unroll 8
+    for (int jj = 0; jj < nk; ++jj) {
+      const float p = ps[h][jj];
+      const uint32_t v = vw[jj * VROW + dp];
+      o0 += p * ss::lo_bf(v);
+      o1 += p * ss::hi_bf(v);
+    }
+    float* dst = a.part + (((int64_t)(hk * a.splits + split) * (CACHED ? a.m : 1) + row) * G + h) * DREC;
+    dst[4 + 2 * dp] = o0;
+    dst[4 + 2 * dp + 1] = o1;
+    if (dp == 0) {
+      float l = 0.0f;
+      for (int w = 0; w < NW; ++w) l += wsum[w][h];
+      dst[0] = hmax[h];
+      dst[1] = l;
     }
   }
 }
 
-__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
-  const int hq = blockIdx.x, j = blockIdx.y, dd = threadIdx.x;
-  const int base = *a.kv_len + a.pos_offset;
-  int n_keys = base + a.m;
-  if (n_keys > a.cap) n_keys = a.cap;
-  const int active = (n_keys + KPS - 1) / KPS;
-  const float* p = a.part + (((int64_t)hq * a.splits) * a.m + j) * (D + 2);
-  const int64_t stride = (int64_t)a.m * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < active; ++s) M = fmaxf(M, p[s * stride]);
-  float l = 0.0f, o = 0.0f;
-  for (int s = 0; s < active; ++s) {
-    const float ms = p[s * stride];
-    if (ms == -INFINITY) continue;
-    const float f = expf(ms - M);
-    l += f * p[s * stride + 1];
-    o += f * p[s * stride + 2 + dd];
+// Merge of the verify partials: grid (q head, row), 128 threads (one per dim);
+// splits in order, batches of 4 independent loads.
+__global__ __launch_bounds__(128) void rows_merge_kernel(AttnArgs a) {
+  const int hq = blockIdx.x, row = blockIdx.y, dd = threadIdx.x;
+  const int G = a.n_q / a.n_kv, hk = hq / G, g = hq % G;
+  const int pos = *a.kv_len + a.pos_offset + row;
+  if (pos < 0 || pos >= a.cap) return;
+  const int active = (pos + DKPB) / DKPB;
+  const int64_t sstride = (int64_t)a.m * G * DREC;
+  const float* base = a.part + (((int64_t)hk * a.splits * a.m + row) * G + g) * DREC;
+  float M = -INFINITY, L = 0.0f, o = 0.0f;
+  for (int s0 = 0; s0 < active; s0 += 4) {
+    float mv[4], lv[4], ov[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bool ok = s0 + t < active;
+      const float* q = base + (ok ? s0 + t : 0) * sstride;
+      mv[t] = ok ? q[0] : -INFINITY;
+      lv[t] = ok ? q[1] : 0.0f;
+      ov[t] = ok ? q[4 + dd] : 0.0f;
+    }
+    float Mb = M;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) Mb = fmaxf(Mb, mv[t]);
+    const float r = (M == -INFINITY) ? 0.0f : expf(M - Mb);
+    L *= r;
+    o *= r;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float f = (mv[t] == -INFINITY) ? 0.0f : expf(mv[t] - Mb);
+      L += f * lv[t];
+      o += f * ov[t];
+    }
+    M = Mb;
   }
-  a.out[((int64_t)j * a.n_q + hq) * D + dd] = ss::f2bf(o / l);
+  a.out[((int64_t)row * a.n_q + hq) * D + dd] = ss::f2bf(o / L);
 }
 
 }  // namespace
-
-int attn_keys_per_split() { return KPS; }
 
 hipError_t launch_rope_append(const AttnArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(rope_append_kernel, dim3(a.m, a.n_q + a.n_kv), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(attn_part_kernel, dim3(a.n_kv, a.splits), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.n_q, a.m), dim3(D), 0, s, a);
+hipError_t launch_decode_attention(const AttnArgs& a, const int32_t* valid, hipStream_t s) {
+  if (a.n_q / a.n_kv > 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(decode_attn_kernel<false>, dim3(a.n_kv, a.splits), dim3(512), 0, s, a, valid);
   return hipGetLastError();
 }
+
+hipError_t launch_rows_attention(const AttnArgs& a, hipStream_t s) {
+  if (a.n_q / a.n_kv > 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(decode_attn_kernel<true>, dim3(a.n_kv, a.splits, a.m), dim3(512), 0, s, a,
+                     (const int32_t*)nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(rows_merge_kernel, dim3(a.n_q, a.m), dim3(D), 0, s, a);
+  return hipGetLastError();
+}
+
+int decode_attn_keys_per_split() { return DKPB; }

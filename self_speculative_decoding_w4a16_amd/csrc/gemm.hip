@@ -6,18 +6,15 @@
 // matrix-core ridge).
 //
 //  * v_mfma_f32_16x16x32_bf16: A = 16 weight rows x 32 k, B = 32 k x 16
-//    positions, D = 16 rows x 16 positions.  A wave owns RT = 2 row tiles (32
-//    rows) and ceil(m/16) position tiles.
-//  * The reduction order inside the MFMA is free as long as A and B agree,
-//    so each lane loads 64 contiguous bytes of one weight row per 128-k step
-//    (lane group g takes k = kb + 32g .. kb + 32g + 31) and feeds them to 4
-//    MFMAs; B is loaded with the same k mapping.  A wave load therefore reads
-//    32 rows x 256 contiguous bytes.
-//  * Short matrices are split along k so that the launch has thousands of
-//    waves; partial sums go to scratch and the last wave to finish a row
-//    group adds them in split order (deterministic) and runs the epilogue:
-//    store, residual add or SiLU(gate)*up (gate tile and up tile in the same
-//    wave).
+//    positions, D = 16 rows x 16 positions (lane l holds rows 4(l/16)..+3 of
+//    column l%16).  A block owns RT 16-row tiles and ceil(m/16) position
+//    tiles; its 4 waves split k four ways and add their partial sums through
+//    LDS in wave order (deterministic), then wave 0 runs the epilogue: store,
+//    residual add, or SiLU(gate)*up with the gate tile and the up tile in the
+//    same block.
+//  * Lane (r, g) of MFMA step s feeds k = kb + 32 s + 8 g .. +7 of row r, so
+//    one load instruction reads 64 contiguous bytes of each of 16 rows; the
+//    next step's loads are issued before the current step's MFMAs.
 #include "common.h"
 #include "internal.h"
 
@@ -25,53 +22,72 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int RT = 2;        // 16-row tiles per wave
-constexpr int KSTEP = 128;   // k per inner step
+constexpr int KSTEP = 128;  // k per step: 4 MFMAs of 32
 
 struct Plan {
-  int64_t groups;  // row groups of 16*RT rows (out rows in SILU mode: 16 per group)
-  int splits;
-  int steps_per_split;
+  int64_t groups;  // blocks
+  int rt;          // 16-row tiles per block
   int tt;          // position tiles
 };
 
-Plan make_plan(int64_t n, int64_t k, int m, int epi) {
+Plan make_plan(int64_t n, int64_t /*k*/, int m, int epi) {
   Plan p;
-  const int64_t out_per_group = (epi == GEPI_SILU) ? 16 : 16 * RT;
-  p.groups = (n + out_per_group - 1) / out_per_group;
   p.tt = (m + 15) / 16;
-  const int ksteps = (int)(k / KSTEP);
-  int splits = 1;
-  const int64_t want_waves = 2048;
-  if (p.groups < want_waves) {
-    splits = (int)((want_waves + p.groups - 1) / p.groups);
-    const int max_splits = ksteps / 2 > 0 ? ksteps / 2 : 1;  // >= 2 steps per split
-    if (splits > max_splits) splits = max_splits;
+  if (epi == GEPI_SILU) {
+    p.rt = 2;  // tile 0: 16 gate rows, tile 1: the matching 16 up rows
+    p.groups = (n + 15) / 16;
+  } else {
+    p.rt = (n >= 65536) ? 2 : 1;
+    p.groups = (n + 16 * p.rt - 1) / (16 * p.rt);
   }
-  p.steps_per_split = (ksteps + splits - 1) / splits;
-  p.splits = (ksteps + p.steps_per_split - 1) / p.steps_per_split;
   return p;
 }
 
-template <int TT, int EPI>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a, Plan p) {
+template <int RT, int TT>
+__device__ __forceinline__ void load_step(const u32x4* const (&wp)[RT], const bool (&wv)[RT],
+                                          const u32x4* const (&xp)[TT], const bool (&xv)[TT],
+                                          int o, u32x4 (&av)[RT][4], u32x4 (&bv)[TT][4]) {
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      av[t][s] = wv[t] ? __builtin_nontemporal_load(wp[t] + o + 4 * s) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int u = 0; u < TT; ++u)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) bv[u][s] = xv[u] ? xp[u][o + 4 * s] : u32x4{0u, 0u, 0u, 0u};
+}
+
+template <int RT, int TT>
+__device__ __forceinline__ void mma_step(const u32x4 (&av)[RT][4], const u32x4 (&bv)[TT][4],
+                                         f32x4_t (&acc)[RT][TT]) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int u = 0; u < TT; ++u)
+        acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[t][s]),
+                                                            __builtin_bit_cast(bf16x8_t, bv[u][s]),
+                                                            acc[t][u], 0, 0, 0);
+}
+
+template <int RT, int TT, int EPI>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a) {
+  __shared__ f32x4_t red[kWaves - 1][RT][TT][SS_WAVE];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t item = (int64_t)blockIdx.x * kWaves + wave;
-  if (item >= p.groups * p.splits) return;
-  const int64_t grp = item / p.splits;
-  const int split = (int)(item - grp * p.splits);
+  const int64_t grp = blockIdx.x;
   const int K = (int)a.k;
   const int r16 = lane & 15, g4 = lane >> 4;
 
-  // physical weight rows of the two tiles for this lane
   int64_t wrow[RT];
   bool wvalid[RT];
-  int64_t obase;  // first output column of the group
+  int64_t obase;
   if (EPI == GEPI_SILU) {
     obase = grp * 16;
-    wvalid[0] = wvalid[1] = (obase + r16) < a.n;
+    wvalid[0] = wvalid[RT - 1] = (obase + r16) < a.n;
     wrow[0] = obase + r16;
-    wrow[1] = a.n + obase + r16;
+    wrow[RT - 1] = a.n + obase + r16;
   } else {
     obase = grp * 16 * RT;
 #pragma unroll
@@ -80,9 +96,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a, Plan p) {
       wvalid[t] = wrow[t] < a.n;
     }
   }
-  const int kb0 = split * p.steps_per_split * KSTEP;
-  int kb1 = kb0 + p.steps_per_split * KSTEP;
-  if (kb1 > K) kb1 = K;
+  const int ksteps = K / KSTEP;
+  const int s0 = (ksteps * wave) / kWaves, s1 = (ksteps * (wave + 1)) / kWaves;
 
   f32x4_t acc[RT][TT];
 #pragma unroll
@@ -93,90 +108,53 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a, Plan p) {
   const u32x4* wp[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t)
-    wp[t] = reinterpret_cast<const u32x4*>(a.w + (wvalid[t] ? wrow[t] : 0) * (int64_t)K + 32 * g4);
+    wp[t] = reinterpret_cast<const u32x4*>(a.w + (wvalid[t] ? wrow[t] : 0) * (int64_t)K) + g4;
   const u32x4* xp[TT];
   bool xvalid[TT];
 #pragma unroll
   for (int u = 0; u < TT; ++u) {
     const int tok = 16 * u + r16;
     xvalid[u] = tok < a.m;
-    xp[u] = reinterpret_cast<const u32x4*>(a.x + (int64_t)(xvalid[u] ? tok : 0) * K + 32 * g4);
+    xp[u] = reinterpret_cast<const u32x4*>(a.x + (int64_t)(xvalid[u] ? tok : 0) * K) + g4;
   }
 
-  for (int kb = kb0; kb < kb1; kb += KSTEP) {
-    const int o = kb / 8;  // offset in 16-byte units
-    u32x4 av[RT][4], bv[TT][4];
+  if (s0 < s1) {
+    u32x4 av[RT][4], bv[TT][4], an[RT][4], bn[TT][4];
+    load_step<RT, TT>(wp, wvalid, xp, xvalid, s0 * (KSTEP / 8), av, bv);
+    for (int st = s0; st < s1; ++st) {
+      const bool more = st + 1 < s1;
+      if (more) load_step<RT, TT>(wp, wvalid, xp, xvalid, (st + 1) * (KSTEP / 8), an, bn);
+      mma_step<RT, TT>(av, bv, acc);
+      if (more) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) av[t][s] = an[t][s];
+#pragma unroll
+        for (int u = 0; u < TT; ++u)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) bv[u][s] = bn[u][s];
+      }
+    }
+  }
+
+  // k-split reduction across the block's waves, in wave order
+  if (wave > 0) {
 #pragma unroll
     for (int t = 0; t < RT; ++t)
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        av[t][s] = wvalid[t] ? __builtin_nontemporal_load(wp[t] + o + s) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int u = 0; u < TT; ++u)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) bv[u][s] = xvalid[u] ? xp[u][o + s] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int t = 0; t < RT; ++t)
-#pragma unroll
-        for (int u = 0; u < TT; ++u)
-          acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, av[t][s]), __builtin_bit_cast(bf16x8_t, bv[u][s]),
-              acc[t][u], 0, 0, 0);
+      for (int u = 0; u < TT; ++u) red[wave - 1][t][u][lane] = acc[t][u];
   }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < kWaves - 1; ++w)
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int u = 0; u < TT; ++u) acc[t][u] += red[w][t][u][lane];
 
-  // D layout: lane holds D[row 4*g4 + j][position r16], j = 0..3
-  if (p.splits > 1) {
-    // write partials [split][pos][row], then count arrivals of the group
-    const int64_t nrows = (EPI == GEPI_SILU) ? 2 * a.n : a.n;
-    float* part = a.partials + (int64_t)split * a.m * nrows;
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
-#pragma unroll
-      for (int u = 0; u < TT; ++u) {
-        const int tok = 16 * u + r16;
-        if (tok >= a.m) continue;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          int64_t row = (EPI == GEPI_SILU) ? (t == 0 ? obase : a.n + obase) + 4 * g4 + j
-                                           : obase + 16 * t + 4 * g4 + j;
-          bool ok = (EPI == GEPI_SILU) ? (obase + 4 * g4 + j) < a.n : row < a.n;
-          if (ok) part[(int64_t)tok * nrows + row] = acc[t][u][j];
-        }
-      }
-    }
-    __threadfence();
-    uint32_t old = 0;
-    if (lane == 0) old = atomicAdd(a.counters + grp, 1u);
-    old = __shfl(old, 0, 64);
-    if (old != (uint32_t)(p.splits - 1)) return;
-    __threadfence();
-    // last arrival: sum partials in split order
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
-#pragma unroll
-      for (int u = 0; u < TT; ++u) {
-        const int tok = 16 * u + r16;
-        if (tok >= a.m) continue;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          int64_t row = (EPI == GEPI_SILU) ? (t == 0 ? obase : a.n + obase) + 4 * g4 + j
-                                           : obase + 16 * t + 4 * g4 + j;
-          bool ok = (EPI == GEPI_SILU) ? (obase + 4 * g4 + j) < a.n : row < a.n;
-          float sum = 0.0f;
-          if (ok) {
-            for (int s = 0; s < p.splits; ++s)
-              sum += __builtin_nontemporal_load(a.partials + ((int64_t)s * a.m + tok) * nrows + row);
-          }
-          acc[t][u][j] = sum;
-        }
-      }
-    }
-    if (lane == 0) a.counters[grp] = 0u;
-  }
-
-  // epilogue
+  // epilogue: lane holds D[row 4*g4 + j][position r16]
 #pragma unroll
   for (int u = 0; u < TT; ++u) {
     const int tok = 16 * u + r16;
@@ -188,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a, Plan p) {
         const int64_t col = obase + 4 * g4 + j;
         if (col < a.n) {
           const float g = ss::bf2f(ss::f2bf(acc[0][u][j]));
-          const float up = ss::bf2f(ss::f2bf(acc[1][u][j]));
+          const float up = ss::bf2f(ss::f2bf(acc[RT - 1][u][j]));
           yrow[col] = ss::f2bf(g / (1.0f + expf(-g)) * up);
         }
       }
@@ -209,15 +187,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs a, Plan p) {
   }
 }
 
-template <int EPI>
+template <int RT, int EPI>
 hipError_t launch_tt(const GemmArgs& a, const Plan& p, hipStream_t s) {
-  const int64_t waves = p.groups * p.splits;
-  const unsigned blocks = (unsigned)((waves + kWaves - 1) / kWaves);
+  const dim3 grid((unsigned)p.groups), block(kThreads);
   switch (p.tt) {
-    case 1: hipLaunchKernelGGL((gemm_kernel<1, EPI>), dim3(blocks), dim3(kThreads), 0, s, a, p); break;
-    case 2: hipLaunchKernelGGL((gemm_kernel<2, EPI>), dim3(blocks), dim3(kThreads), 0, s, a, p); break;
-    case 3: hipLaunchKernelGGL((gemm_kernel<3, EPI>), dim3(blocks), dim3(kThreads), 0, s, a, p); break;
-    case 4: hipLaunchKernelGGL((gemm_kernel<4, EPI>), dim3(blocks), dim3(kThreads), 0, s, a, p); break;
+    case 1: hipLaunchKernelGGL((gemm_kernel<RT, 1, EPI>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gemm_kernel<RT, 2, EPI>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((gemm_kernel<RT, 3, EPI>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((gemm_kernel<RT, 4, EPI>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -225,24 +202,17 @@ hipError_t launch_tt(const GemmArgs& a, const Plan& p, hipStream_t s) {
 
 }  // namespace
 
-size_t gemm_partials_bytes(int64_t n, int64_t k, int m, int epi) {
-  Plan p = make_plan(n, k, m, epi);
-  if (p.splits <= 1) return 0;
-  const int64_t nrows = (epi == GEPI_SILU) ? 2 * n : n;
-  return (size_t)p.splits * (size_t)m * (size_t)nrows * sizeof(float);
-}
-
-size_t gemm_counter_slots(int64_t n, int64_t k, int m, int epi) {
-  Plan p = make_plan(n, k, m, epi);
-  return p.splits > 1 ? (size_t)p.groups : 0;
-}
+size_t gemm_partials_bytes(int64_t, int64_t, int, int) { return 0; }
+size_t gemm_counter_slots(int64_t, int64_t, int, int) { return 0; }
 
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s) {
   Plan p = make_plan(a.n, a.k, a.m, epi);
   switch (epi) {
-    case GEPI_STORE: return launch_tt<GEPI_STORE>(a, p, s);
-    case GEPI_RESID: return launch_tt<GEPI_RESID>(a, p, s);
-    case GEPI_SILU: return launch_tt<GEPI_SILU>(a, p, s);
+    case GEPI_STORE:
+      return p.rt == 2 ? launch_tt<2, GEPI_STORE>(a, p, s) : launch_tt<1, GEPI_STORE>(a, p, s);
+    case GEPI_RESID:
+      return p.rt == 2 ? launch_tt<2, GEPI_RESID>(a, p, s) : launch_tt<1, GEPI_RESID>(a, p, s);
+    case GEPI_SILU: return launch_tt<2, GEPI_SILU>(a, p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -24,16 +24,22 @@
 #include "common.h"
 #include "internal.h"
 
+#include <stdlib.h>
+
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / SS_WAVE;
 
-__device__ __forceinline__ float w4_word_dot(uint32_t cw, u32x4 xq, float d) {
-  d = ss::dot2((cw & 0x000F000Fu) | 0x43004300u, xq.x, d);
-  d = ss::dot2(((cw >> 4) & 0x000F000Fu) | 0x43004300u, xq.y, d);
-  d = ss::dot2(((cw >> 8) & 0x000F000Fu) | 0x43004300u, xq.z, d);
-  d = ss::dot2(((cw >> 12) & 0x000F000Fu) | 0x43004300u, xq.w, d);
+// (128 + q_a, 128 + q_b) bf16 pair of nibbles a, a+4 of a code word, dotted
+// with the matching x pair.  `mask` (0x000F000F) sits in an SGPR and `magic`
+// (0x43004300) in a VGPR so that each extraction is a single v_and_or_b32.
+__device__ __forceinline__ float w4_word_dot(uint32_t cw, u32x4 xq, float d, uint32_t mask,
+                                             uint32_t magic) {
+  d = ss::dot2((cw & mask) | magic, xq.x, d);
+  d = ss::dot2(((cw >> 4) & mask) | magic, xq.y, d);
+  d = ss::dot2(((cw >> 8) & mask) | magic, xq.z, d);
+  d = ss::dot2(((cw >> 12) & mask) | magic, xq.w, d);
   return d;
 }
 
@@ -45,254 +51,434 @@ __device__ __forceinline__ float bf16_chunk_dot(u32x4 w, u32x4 xq, float d) {
   return d;
 }
 
-// LDS slot (in 16-byte units) of quad w (0..3) of W4 chunk c: lanes of a wave
-// reading the same quad of consecutive chunks hit consecutive slots.
-__device__ __forceinline__ int w4_slot(int c, int w) { return ((c >> 6) << 8) + (w << 6) + (c & 63); }
-// LDS slots of x for W4: whole groups of 64 chunks (256 slots each).
-__host__ __device__ __forceinline__ int w4_slots(int K) { return ((K / 32 + 63) / 64) * 256; }
+// W4: x of 64-group gi, quad w (8 values) lives in LDS slot w4_slot(gi, w):
+// lanes of a wave reading the same quad of consecutive groups hit
+// consecutive 16-byte slots (no bank conflicts).
+__host__ __device__ __forceinline__ int w4_slot(int gi, int w) {
+  return ((gi >> 6) << 9) + (w << 6) + (gi & 63);
+}
+__host__ __device__ __forceinline__ int w4_slots(int K) { return ((K / 64 + 63) / 64) * 512; }
 
-template <int R, bool W4, int PRO, int EPI>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
-  extern __shared__ u32x4 smem4[];
-  __shared__ float red[kWaves];
-  __shared__ float red_v[kWaves];
-  __shared__ int red_i[kWaves];
-  __shared__ float s_inv;
-
-  if (a.valid && *a.valid == 0) return;
-  const int tid = threadIdx.x, lane = tid & (SS_WAVE - 1), wave = tid / SS_WAVE;
-  const int K = (int)a.k;
-  const int nq = K / 8;  // 8-element quads of x
-
-  // ---------------------------------------------------------------- prologue
-  const uint16_t* src = a.x;
-  if (PRO == PRO_NORM) src = a.h;
-  if (PRO == PRO_EMBED_NORM) src = a.embed + (int64_t)(*a.token) * K;
-  float inv = 1.0f;
-  if (PRO != PRO_X) {
-    float ss = 0.0f;
-    for (int q = tid; q < nq; q += kThreads) {
-      u32x4 v = reinterpret_cast<const u32x4*>(src)[q];
-      uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float lo = ss::lo_bf(wv[i]), hi = ss::hi_bf(wv[i]);
-        ss += lo * lo;
-        ss += hi * hi;
-      }
-    }
-    ss = ss::wave_sum(ss);
-    if (lane == 0) red[wave] = ss;
-    __syncthreads();
-    if (tid == 0) {
-      float t = 0.0f;
-      for (int i = 0; i < kWaves; ++i) t += red[i];
-      s_inv = 1.0f / sqrtf(t / (float)K + a.eps);
-    }
-    __syncthreads();
-    inv = s_inv;
-    if (PRO == PRO_EMBED_NORM && blockIdx.x == 0) {
-      for (int q = tid; q < nq; q += kThreads)
-        reinterpret_cast<u32x4*>(a.h_out)[q] = reinterpret_cast<const u32x4*>(src)[q];
-    }
-  }
-  for (int q = tid; q < nq; q += kThreads) {
-    u32x4 v = reinterpret_cast<const u32x4*>(src)[q];
-    uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-    uint16_t xb[8];
-    if (PRO != PRO_X) {
-      u32x4 g = reinterpret_cast<const u32x4*>(a.norm_w)[q];
-      uint32_t gv[4] = {g.x, g.y, g.z, g.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xb[2 * i] = ss::f2bf(ss::lo_bf(wv[i]) * inv * ss::lo_bf(gv[i]));
-        xb[2 * i + 1] = ss::f2bf(ss::hi_bf(wv[i]) * inv * ss::hi_bf(gv[i]));
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xb[2 * i] = (uint16_t)(wv[i] & 0xffffu);
-        xb[2 * i + 1] = (uint16_t)(wv[i] >> 16);
-      }
-    }
-    if (W4) {
-      u32x4 o = u32x4{ss::pack_bf(xb[0], xb[4]), ss::pack_bf(xb[1], xb[5]),
-                           ss::pack_bf(xb[2], xb[6]), ss::pack_bf(xb[3], xb[7])};
-      smem4[w4_slot(q >> 2, q & 3)] = o;
-    } else {
-      smem4[q] = u32x4{ss::pack_bf(xb[0], xb[1]), ss::pack_bf(xb[2], xb[3]),
-                            ss::pack_bf(xb[4], xb[5]), ss::pack_bf(xb[6], xb[7])};
-    }
-  }
-  float* xsum = reinterpret_cast<float*>(smem4 + (W4 ? w4_slots(K) : nq));
-  if (W4) {
-    __syncthreads();
-    for (int c = tid; c < K / 32; c += kThreads) {
-      float t = 0.0f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        u32x4 v = smem4[w4_slot(c, w)];
-        t += ss::lo_bf(v.x) + ss::hi_bf(v.x) + ss::lo_bf(v.y) + ss::hi_bf(v.y) +
-             ss::lo_bf(v.z) + ss::hi_bf(v.z) + ss::lo_bf(v.w) + ss::hi_bf(v.w);
-      }
-      xsum[c] = t;
-    }
-  }
-  __syncthreads();
-
-  // ---------------------------------------------------------------- rows
-  constexpr int RO = (EPI == EPI_SILU) ? R / 2 : R;  // output rows per wave
-  const int64_t out0 = ((int64_t)blockIdx.x * kWaves + wave) * RO;
-  int64_t prow[R];
-  bool rv[R];
+// Physical rows of row group g (R rows; in SiLU mode R/2 gate rows + the
+// matching R/2 up rows).  Rows past the end are clamped to row 0 (always a
+// valid address) and flagged invalid.
+template <int R, int EPI>
+__device__ __forceinline__ void group_rows(int64_t g, int64_t n, int64_t (&prow)[R], bool (&rv)[R],
+                                           int64_t& out0) {
+  constexpr int RO = (EPI == EPI_SILU) ? R / 2 : R;
+  out0 = g * RO;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if (EPI == EPI_SILU) {
       const int64_t o = out0 + (r % RO);
-      rv[r] = o < a.n;
-      prow[r] = (r < RO) ? o : a.n + o;
+      rv[r] = o < n;
+      prow[r] = rv[r] ? ((r < RO) ? o : n + o) : 0;
     } else {
       prow[r] = out0 + r;
-      rv[r] = prow[r] < a.n;
+      rv[r] = prow[r] < n;
+      if (!rv[r]) prow[r] = 0;
     }
   }
+}
 
-  float acc[R];
+// One step: unit u of row r is W4 group (gb + lane + 64u) (two 16-byte code
+// chunks + its fp16 {scale, min}) or bf16 chunk (cb + lane + 64u) (16 bytes).
+// Indices past the row end are clamped; their contribution is skipped.
+template <int R, int U, bool W4>
+struct Step {
+  u32x4 v[U][R][W4 ? 2 : 1];
+  uint32_t m[U][R];
+};
+
+template <int R, int U, bool W4>
+__device__ __forceinline__ void load_step(Step<R, U, W4>& b, const u32x4* const (&wp)[R],
+                                          const uint32_t* const (&mp)[R], int base, int lane, int n_units) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
-
-  constexpr int U = (8 / R) > 1 ? (8 / R) : 1;  // chunks per row in flight
-  if (W4) {
-    const int C = K / 32;  // 16-byte code chunks per row
-    const u32x4* crow[R];
-    const uint32_t* mrow[R];
+  for (int u = 0; u < U; ++u) {
+    int i = base + lane + u * SS_WAVE;
+    i = i < n_units ? i : n_units - 1;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int64_t pr = rv[r] ? prow[r] : 0;
-      crow[r] = reinterpret_cast<const u32x4*>(a.codes + pr * (K / 2));
-      mrow[r] = reinterpret_cast<const uint32_t*>(a.meta) + pr * (K / 64);
-    }
-    for (int c0 = lane; c0 < C; c0 += U * SS_WAVE) {
-      u32x4 cw[U][R];
-      uint32_t mt[U][R];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = c0 + u * SS_WAVE;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          if (c < C && rv[r]) {
-            cw[u][r] = __builtin_nontemporal_load(crow[r] + c);
-            mt[u][r] = mrow[r][c >> 1];
-          } else {
-            cw[u][r] = u32x4{0u, 0u, 0u, 0u};
-            mt[u][r] = 0;
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = c0 + u * SS_WAVE;
-        if (c < C) {
-          const u32x4 x0 = smem4[w4_slot(c, 0)], x1 = smem4[w4_slot(c, 1)];
-          const u32x4 x2 = smem4[w4_slot(c, 2)], x3 = smem4[w4_slot(c, 3)];
-          const float xs = xsum[c];
-#pragma unroll
-          for (int r = 0; r < R; ++r) {
-            float d = 0.0f;
-            d = w4_word_dot(cw[u][r].x, x0, d);
-            d = w4_word_dot(cw[u][r].y, x1, d);
-            d = w4_word_dot(cw[u][r].z, x2, d);
-            d = w4_word_dot(cw[u][r].w, x3, d);
-            const float s = ss::h2f((uint16_t)(mt[u][r] & 0xffffu));
-            const float m = ss::h2f((uint16_t)(mt[u][r] >> 16));
-            acc[r] += s * d + (m - 128.0f * s) * xs;
-          }
-        }
-      }
-    }
-  } else {
-    const int C = K / 8;  // 16-byte chunks of 8 bf16 weights
-    const u32x4* wrow[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int64_t pr = rv[r] ? prow[r] : 0;
-      wrow[r] = reinterpret_cast<const u32x4*>(a.w + pr * K);
-    }
-    for (int c0 = lane; c0 < C; c0 += U * SS_WAVE) {
-      u32x4 wv[U][R];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = c0 + u * SS_WAVE;
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-          wv[u][r] = (c < C && rv[r]) ? __builtin_nontemporal_load(wrow[r] + c) : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = c0 + u * SS_WAVE;
-        if (c < C) {
-          const u32x4 xq = smem4[c];
-#pragma unroll
-          for (int r = 0; r < R; ++r) acc[r] = bf16_chunk_dot(wv[u][r], xq, acc[r]);
-        }
-      }
-    }
-  }
-
-  // ---------------------------------------------------------------- epilogue
-#pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = ss::wave_sum(acc[r]);
-
-  if (EPI == EPI_SILU) {
-#pragma unroll
-    for (int r = 0; r < RO; ++r) {
-      if (lane == r && rv[r]) {
-        const float g = ss::bf2f(ss::f2bf(acc[r]));
-        const float u = ss::bf2f(ss::f2bf(acc[r + RO]));
-        const float sg = g / (1.0f + expf(-g));
-        a.y[out0 + r] = ss::f2bf(sg * u);
-      }
-    }
-  } else {
-    ss::ArgMax best = {-INFINITY, 0x7fffffff};
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (lane == r && rv[r]) {
-        float v = acc[r];
-        if (EPI == EPI_RESID) v = ss::bf2f(a.resid[prow[r]]) + v;
-        const uint16_t b = ss::f2bf(v);
-        a.y[prow[r]] = b;
-        if (EPI == EPI_LOGITS) {
-          ss::ArgMax c = {ss::bf2f(b), (int)prow[r]};
-          best = ss::better(best, c);
-        }
-      }
-    }
-    if (EPI == EPI_LOGITS) {
-      best = ss::wave_argmax(best);
-      if (lane == 0) {
-        red_v[wave] = best.v;
-        red_i[wave] = best.i;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        ss::ArgMax b = {red_v[0], red_i[0]};
-        for (int i = 1; i < kWaves; ++i) b = ss::better(b, ss::ArgMax{red_v[i], red_i[i]});
-        a.part_max[blockIdx.x] = b.v;
-        a.part_arg[blockIdx.x] = b.i;
+      if (W4) {
+        b.v[u][r][0] = __builtin_nontemporal_load(wp[r] + 2 * i);
+        b.v[u][r][W4 ? 1 : 0] = __builtin_nontemporal_load(wp[r] + 2 * i + 1);
+        b.m[u][r] = mp[r][i];
+      } else {
+        b.v[u][r][0] = __builtin_nontemporal_load(wp[r] + i);
       }
     }
   }
 }
 
+template <int R, bool W4>
+__device__ __forceinline__ void row_ptrs(const GemvArgs& a, const int64_t (&prow)[R], int K,
+                                         const u32x4* (&wp)[R], const uint32_t* (&mp)[R]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (W4) {
+      wp[r] = reinterpret_cast<const u32x4*>(a.codes + prow[r] * (K / 2));
+      mp[r] = reinterpret_cast<const uint32_t*>(a.meta) + prow[r] * (K / 64);
+    } else {
+      wp[r] = reinterpret_cast<const u32x4*>(a.w + prow[r] * K);
+      mp[r] = nullptr;
+    }
+  }
+}
+
+template <int R, bool W4, int PRO, int EPI>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int64_t n_groups, uint32_t mask_arg,
+                                                        uint32_t magic_arg) {
+  extern __shared__ u32x4 smem4[];
+  __shared__ float red[kWaves];
+  __shared__ float red_v[kWaves];
+  __shared__ int red_i[kWaves];
+
+  if (a.valid && *a.valid == 0) return;
+  const int tid = threadIdx.x, lane = tid & (SS_WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / SS_WAVE);  // wave-uniform: rows in SGPRs
+  const int K = (int)a.k;
+  const int n_units = W4 ? K / 64 : K / 8;  // per row: W4 groups or bf16 16-byte chunks
+  constexpr int U = W4 ? ((R >= 4) ? 1 : (R == 2 ? 2 : 4)) : ((R >= 4) ? 2 : (R == 2 ? 4 : 8));
+  constexpr int RO = (EPI == EPI_SILU) ? R / 2 : R;
+  const int64_t wave_stride = (int64_t)gridDim.x * kWaves;
+  const uint32_t mask = __builtin_amdgcn_readfirstlane(mask_arg);
+  uint32_t magic = magic_arg;
+  asm volatile("" : "+v"(magic));
+
+  // ------------------------------------------------ first weight loads, issued
+  // before the prologue so that their latency overlaps it
+  int64_t g = (int64_t)blockIdx.x * kWaves + wave;
+  int64_t prow[R], out0;
+  bool rv[R];
+  group_rows<R, EPI>(g < n_groups ? g : 0, a.n, prow, rv, out0);
+  const u32x4* wp[R];
+  const uint32_t* mp[R];
+  row_ptrs<R, W4>(a, prow, K, wp, mp);
+  int base = 0;  // wave-uniform first unit of the current step
+  Step<R, U, W4> cur;
+  load_step<R, U, W4>(cur, wp, mp, base, lane, n_units);
+
+  // ------------------------------------------------ prologue: x (and group sums) in LDS
+  const uint16_t* src = a.x;
+  if (PRO == PRO_NORM) src = a.h;
+  if (PRO == PRO_EMBED_NORM) src = a.embed + (int64_t)(*a.token) * K;
+  float* xsum = reinterpret_cast<float*>(smem4 + (W4 ? w4_slots(K) : K / 8));
+  // items: W4 -> 64-value groups (8 quads), bf16 -> 8-value quads
+  constexpr int QPI = W4 ? 8 : 1;
+  constexpr int NI = W4 ? 1 : 3;  // items per thread held in registers when normalising
+  const int n_items = W4 ? K / 64 : K / 8;
+  if (PRO == PRO_ATTN_MERGE) {
+    // x[h*128 + d] = sum_s f_s o_s[d] / sum_s f_s l_s, f_s = exp(m_s - max_s m_s),
+    // merged over the decode-attention splits in split order, batches of 4.
+    constexpr int DH = 128, REC = 4 + DH;
+    const int n_chunks = K / 16;  // 16 dims per chunk
+    const int pos = *a.kv_len + a.pos_offset;
+    int active = (pos + a.attn_kpb) / a.attn_kpb;
+    if (active > a.attn_splits) active = a.attn_splits;
+    const int G = a.attn_g;
+    const int64_t sstride = (int64_t)G * REC;
+    for (int ch0 = 0; ch0 < n_chunks; ch0 += kThreads) {
+      const int ch = ch0 + tid;
+      const bool ok = ch < n_chunks;
+      const int h = ok ? ch / 8 : 0, hk = h / G, gg = h % G, d0 = (ch % 8) * 16;
+      const float* base = a.attn_part + ((int64_t)hk * a.attn_splits * G + gg) * REC;
+      float M = -INFINITY, L = 0.0f, o[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[i] = 0.0f;
+      for (int s0 = 0; s0 < active; s0 += 4) {
+        float mv[4], lv[4];
+        f32x4_t ov[4][4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bool sok = ok && (s0 + t) < active;
+          const float* q = base + (sok ? (s0 + t) : 0) * sstride;
+          const f32x4_t ml = sok ? *reinterpret_cast<const f32x4_t*>(q) : f32x4_t{-INFINITY, 0.f, 0.f, 0.f};
+          mv[t] = ml[0];
+          lv[t] = ml[1];
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            ov[t][v] = sok ? reinterpret_cast<const f32x4_t*>(q + 4 + d0)[v] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        float Mb = M;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) Mb = fmaxf(Mb, mv[t]);
+        const float r = (M == -INFINITY) ? 0.0f : expf(M - Mb);
+        L *= r;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[i] *= r;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float f = (mv[t] == -INFINITY) ? 0.0f : expf(mv[t] - Mb);
+          L += f * lv[t];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[i] += f * ov[t][i >> 2][i & 3];
+        }
+        M = Mb;
+      }
+      uint16_t xb[16];
+      float xs = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        xb[i] = ss::f2bf(ok ? o[i] / L : 0.0f);
+        xs += ss::bf2f(xb[i]);
+      }
+      const int k0 = h * DH + d0;  // first input column of this chunk
+      if (W4) {
+        xs += __shfl_xor(xs, 1, SS_WAVE);
+        xs += __shfl_xor(xs, 2, SS_WAVE);
+        if (ok) {
+#pragma unroll
+          for (int qd = 0; qd < 2; ++qd) {
+            const uint16_t* xq = xb + 8 * qd;
+            smem4[w4_slot(k0 / 64, (k0 % 64) / 8 + qd)] =
+                u32x4{ss::pack_bf(xq[0], xq[4]), ss::pack_bf(xq[1], xq[5]), ss::pack_bf(xq[2], xq[6]),
+                      ss::pack_bf(xq[3], xq[7])};
+          }
+          if ((ch & 3) == 0) xsum[k0 / 64] = xs;
+        }
+      } else if (ok) {
+#pragma unroll
+        for (int qd = 0; qd < 2; ++qd) {
+          const uint16_t* xq = xb + 8 * qd;
+          smem4[k0 / 8 + qd] = u32x4{ss::pack_bf(xq[0], xq[1]), ss::pack_bf(xq[2], xq[3]),
+                                     ss::pack_bf(xq[4], xq[5]), ss::pack_bf(xq[6], xq[7])};
+        }
+      }
+    }
+  } else if (PRO != PRO_X) {
+    u32x4 hv[NI][QPI];
+    float ss = 0.0f;
+#pragma unroll
+    for (int t = 0; t < NI; ++t) {
+      const int it = tid + t * kThreads;
+#pragma unroll
+      for (int q = 0; q < QPI; ++q) {
+        hv[t][q] = it < n_items ? reinterpret_cast<const u32x4*>(src)[it * QPI + q] : u32x4{0u, 0u, 0u, 0u};
+        const uint32_t wv[4] = {hv[t][q].x, hv[t][q].y, hv[t][q].z, hv[t][q].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float lo = ss::lo_bf(wv[i]), hi = ss::hi_bf(wv[i]);
+          ss += lo * lo;
+          ss += hi * hi;
+        }
+      }
+    }
+    ss = ss::wave_sum(ss);
+    if (lane == 0) red[wave] = ss;
+    __syncthreads();
+    float tot = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) tot += red[i];
+    const float inv = 1.0f / sqrtf(tot / (float)K + a.eps);
+    if (PRO == PRO_EMBED_NORM && blockIdx.x == 0) {
+      for (int q = tid; q < K / 8; q += kThreads)
+        reinterpret_cast<u32x4*>(a.h_out)[q] = reinterpret_cast<const u32x4*>(src)[q];
+    }
+#pragma unroll
+    for (int t = 0; t < NI; ++t) {
+      const int it = tid + t * kThreads;
+      if (it >= n_items) continue;
+      float xs = 0.0f;
+#pragma unroll
+      for (int q = 0; q < QPI; ++q) {
+        const u32x4 gv = reinterpret_cast<const u32x4*>(a.norm_w)[it * QPI + q];
+        const uint32_t wv[4] = {hv[t][q].x, hv[t][q].y, hv[t][q].z, hv[t][q].w};
+        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+        uint16_t xb[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xb[2 * i] = ss::f2bf(ss::lo_bf(wv[i]) * inv * ss::lo_bf(gw[i]));
+          xb[2 * i + 1] = ss::f2bf(ss::hi_bf(wv[i]) * inv * ss::hi_bf(gw[i]));
+        }
+        if (W4) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) xs += ss::bf2f(xb[i]);
+          smem4[w4_slot(it, q)] = u32x4{ss::pack_bf(xb[0], xb[4]), ss::pack_bf(xb[1], xb[5]),
+                                        ss::pack_bf(xb[2], xb[6]), ss::pack_bf(xb[3], xb[7])};
+        } else {
+          smem4[it] = u32x4{ss::pack_bf(xb[0], xb[1]), ss::pack_bf(xb[2], xb[3]),
+                            ss::pack_bf(xb[4], xb[5]), ss::pack_bf(xb[6], xb[7])};
+        }
+      }
+      if (W4) xsum[it] = xs;
+    }
+  } else {
+    for (int it = tid; it < n_items; it += kThreads) {
+      float xs = 0.0f;
+#pragma unroll
+      for (int q = 0; q < QPI; ++q) {
+        const u32x4 v = reinterpret_cast<const u32x4*>(src)[it * QPI + q];
+        if (W4) {
+          const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+          uint16_t xb[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            xb[2 * i] = (uint16_t)(wv[i] & 0xffffu);
+            xb[2 * i + 1] = (uint16_t)(wv[i] >> 16);
+            xs += ss::lo_bf(wv[i]) + ss::hi_bf(wv[i]);
+          }
+          smem4[w4_slot(it, q)] = u32x4{ss::pack_bf(xb[0], xb[4]), ss::pack_bf(xb[1], xb[5]),
+                                        ss::pack_bf(xb[2], xb[6]), ss::pack_bf(xb[3], xb[7])};
+        } else {
+          smem4[it] = v;
+        }
+      }
+      if (W4) xsum[it] = xs;
+    }
+  }
+  __syncthreads();
+
+  // ------------------------------------------------ main loop over (row group, step)
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  ss::ArgMax best = {-INFINITY, 0x7fffffff};
+  while (g < n_groups) {
+    // coordinates of the next step (wave-uniform), and its loads, issued
+    // before the current step is consumed
+    int base1 = base + U * SS_WAVE;
+    int64_t g1 = g;
+    const bool end_of_group = base1 >= n_units;
+    int64_t prow1[R], out1 = out0;
+    bool rv1[R];
+    const u32x4* wp1[R];
+    const uint32_t* mp1[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      prow1[r] = prow[r];
+      rv1[r] = rv[r];
+      wp1[r] = wp[r];
+      mp1[r] = mp[r];
+    }
+    if (end_of_group) {
+      g1 = g + wave_stride;
+      base1 = 0;
+      group_rows<R, EPI>(g1 < n_groups ? g1 : 0, a.n, prow1, rv1, out1);
+      row_ptrs<R, W4>(a, prow1, K, wp1, mp1);
+    }
+    Step<R, U, W4> nxt;
+    if (g1 < n_groups) load_step<R, U, W4>(nxt, wp1, mp1, base1, lane, n_units);
+
+    // compute the current step
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + lane + u * SS_WAVE;
+      if (i < n_units) {
+        if (W4) {
+          const float xs = xsum[i];
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+            for (int hlf = 0; hlf < 2; ++hlf) {
+              const u32x4 c = cur.v[u][r][W4 ? hlf : 0];
+              d0 = w4_word_dot(c.x, smem4[w4_slot(i, 4 * hlf + 0)], d0, mask, magic);
+              d1 = w4_word_dot(c.y, smem4[w4_slot(i, 4 * hlf + 1)], d1, mask, magic);
+              d0 = w4_word_dot(c.z, smem4[w4_slot(i, 4 * hlf + 2)], d0, mask, magic);
+              d1 = w4_word_dot(c.w, smem4[w4_slot(i, 4 * hlf + 3)], d1, mask, magic);
+            }
+            const float sc = ss::h2f((uint16_t)(cur.m[u][r] & 0xffffu));
+            const float mn = ss::h2f((uint16_t)(cur.m[u][r] >> 16));
+            acc[r] += sc * (d0 + d1) + (mn - 128.0f * sc) * xs;
+          }
+        } else {
+          const u32x4 xq = smem4[i];
+#pragma unroll
+          for (int r = 0; r < R; ++r) acc[r] = bf16_chunk_dot(cur.v[u][r][0], xq, acc[r]);
+        }
+      }
+    }
+
+    if (end_of_group) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = ss::wave_sum(acc[r]);
+      if (EPI == EPI_SILU) {
+#pragma unroll
+        for (int r = 0; r < RO; ++r) {
+          if (lane == r && rv[r]) {
+            const float gt = ss::bf2f(ss::f2bf(acc[r]));
+            const float up = ss::bf2f(ss::f2bf(acc[r + RO]));
+            a.y[out0 + r] = ss::f2bf(gt / (1.0f + expf(-gt)) * up);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (lane == r && rv[r]) {
+            float v = acc[r];
+            if (EPI == EPI_RESID) v = ss::bf2f(a.resid[prow[r]]) + v;
+            const uint16_t b = ss::f2bf(v);
+            a.y[prow[r]] = b;
+            if (EPI == EPI_LOGITS) best = ss::better(best, ss::ArgMax{ss::bf2f(b), (int)prow[r]});
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+    }
+    g = g1;
+    base = base1;
+    out0 = out1;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      prow[r] = prow1[r];
+      rv[r] = rv1[r];
+      wp[r] = wp1[r];
+      mp[r] = mp1[r];
+    }
+    cur = nxt;
+  }
+  if (EPI == EPI_LOGITS) {
+    best = ss::wave_argmax(best);
+    if (lane == 0) {
+      red_v[wave] = best.v;
+      red_i[wave] = best.i;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      ss::ArgMax b = {red_v[0], red_i[0]};
+      for (int i = 1; i < kWaves; ++i) b = ss::better(b, ss::ArgMax{red_v[i], red_i[i]});
+      a.part_max[blockIdx.x] = b.v;
+      a.part_arg[blockIdx.x] = b.i;
+    }
+  }
+}
+
+int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  return cus;
+}
+
+// Blocks of a persistent launch: a few per compute unit, fewer when the
+// matrix has fewer row groups.
+int64_t gemv_blocks(int64_t n_groups, bool w4, int pro) {
+  static int per_cu = -1;
+  if (per_cu < 0) {
+    const char* e = getenv("SUBSPEC_GEMV_BLOCKS_PER_CU");
+    per_cu = e ? atoi(e) : 0;
+    if (per_cu <= 0) per_cu = 4;
+  }
+  // the attention-merge prologue is redone by every block: one block per CU
+  const int64_t cap = (int64_t)device_cus() * (pro == PRO_ATTN_MERGE ? 1 : per_cu * (w4 ? 1 : 2));
+  const int64_t need = (n_groups + kWaves - 1) / kWaves;
+  return need < cap ? need : cap;
+}
+
 template <int R, bool W4, int PRO, int EPI>
 hipError_t launch_one(const GemvArgs& a, hipStream_t s, int* blocks_out) {
   constexpr int RO = (EPI == EPI_SILU) ? R / 2 : R;
-  const int64_t rows_per_block = (int64_t)kWaves * RO;
-  const int64_t blocks = (a.n + rows_per_block - 1) / rows_per_block;
-  const size_t lds = W4 ? (size_t)w4_slots((int)a.k) * 16 + (size_t)(a.k / 32) * 4 : (size_t)a.k * 2;
+  const int64_t n_groups = (a.n + RO - 1) / RO;
+  const int64_t blocks = gemv_blocks(n_groups, W4, PRO);
+  const size_t lds = W4 ? (size_t)w4_slots((int)a.k) * 16 + (size_t)(a.k / 64) * 4 : (size_t)a.k * 2;
   if (blocks_out) *blocks_out = (int)blocks;
-  hipLaunchKernelGGL((gemv_kernel<R, W4, PRO, EPI>), dim3((unsigned)blocks), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((gemv_kernel<R, W4, PRO, EPI>), dim3((unsigned)blocks), dim3(kThreads), lds, s, a,
+                     n_groups, 0x000F000Fu, 0x43004300u);
   return hipGetLastError();
 }
 
@@ -312,6 +498,7 @@ template <bool W4>
 hipError_t launch_w(int R, int pro, int epi, const GemvArgs& a, hipStream_t s, int* b) {
   if (pro == PRO_X && epi == EPI_STORE) return launch_r<W4, PRO_X, EPI_STORE>(R, a, s, b);
   if (pro == PRO_X && epi == EPI_RESID) return launch_r<W4, PRO_X, EPI_RESID>(R, a, s, b);
+  if (pro == PRO_ATTN_MERGE && epi == EPI_RESID) return launch_r<W4, PRO_ATTN_MERGE, EPI_RESID>(R, a, s, b);
   if (pro == PRO_NORM && epi == EPI_STORE) return launch_r<W4, PRO_NORM, EPI_STORE>(R, a, s, b);
   if (pro == PRO_EMBED_NORM && epi == EPI_STORE) return launch_r<W4, PRO_EMBED_NORM, EPI_STORE>(R, a, s, b);
   if (pro == PRO_NORM && epi == EPI_SILU) return launch_r<W4, PRO_NORM, EPI_SILU>(R, a, s, b);
@@ -330,9 +517,10 @@ static int pick_r(int64_t n, int epi) {
   return 1;
 }
 
-int gemv_rows_per_block(bool /*w4*/, int64_t n, int epi) {
-  const int r = pick_r(n, epi);
-  return kWaves * ((epi == EPI_SILU) ? r / 2 : r);
+int gemv_max_blocks(bool w4, int64_t n, int epi) {
+  const int R = pick_r(n, epi);
+  const int RO = (epi == EPI_SILU) ? R / 2 : R;
+  return (int)gemv_blocks((n + RO - 1) / RO, w4, PRO_NORM);
 }
 
 hipError_t launch_gemv(bool w4, int pro, int epi, const GemvArgs& a, hipStream_t s, int* blocks_out) {

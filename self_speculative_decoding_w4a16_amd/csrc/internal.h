@@ -5,7 +5,7 @@
 
 // ------------------------------------------------------------------ GEMV (batch 1)
 // Prologue: where the input vector x comes from.
-enum GemvPro { PRO_X = 0, PRO_NORM = 1, PRO_EMBED_NORM = 2 };
+enum GemvPro { PRO_X = 0, PRO_NORM = 1, PRO_EMBED_NORM = 2, PRO_ATTN_MERGE = 3 };
 // Epilogue: what is written.
 enum GemvEpi { EPI_STORE = 0, EPI_RESID = 1, EPI_SILU = 2, EPI_LOGITS = 3 };
 
@@ -30,9 +30,14 @@ struct GemvArgs {
   float* part_max;           // EPI_LOGITS: per-block max
   int32_t* part_arg;         // EPI_LOGITS: per-block argmax
   const int32_t* valid;      // optional device flag: skip everything if *valid == 0
+  // PRO_ATTN_MERGE: x = merge of decode-attention partials
+  const float* attn_part;    // [n_kv][splits][G][d + 2]
+  int attn_splits, attn_kpb, n_kv, attn_g;
+  const int32_t* kv_len;
+  int pos_offset;
 };
 
-int gemv_rows_per_block(bool w4, int64_t n, int epi);
+int gemv_max_blocks(bool w4, int64_t n, int epi);  // blocks of one launch (logits partials)
 hipError_t launch_gemv(bool w4, int pro, int epi, const GemvArgs& a, hipStream_t s, int* blocks_out);
 
 // ------------------------------------------------------------------ GEMM (verify)
@@ -68,14 +73,19 @@ struct AttnArgs {
   int m;                // query rows
   int n_q, n_kv, d, cap;
   float theta;
-  float* part;          // [Hq][splits][m][d + 2]
-  int splits;           // grid splits over keys
-  int keys_per_split;
+  float* part;          // split partials [Hkv][splits][m][G][d + 4]
+  int splits;           // grid splits over keys (128 keys each)
   uint16_t* out;        // [m][Hq d]
 };
 hipError_t launch_rope_append(const AttnArgs& a, hipStream_t s);
-hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
-int attn_keys_per_split();
+// One query position: RoPE + KV append + per-split partials (m, l, o[d]) in
+// part[kv head][split][group head][d + 2]; the splits are merged by the output
+// projection's prologue (PRO_ATTN_MERGE).
+hipError_t launch_decode_attention(const AttnArgs& a, const int32_t* valid, hipStream_t s);
+int decode_attn_keys_per_split();
+// m query rows at positions kv_len + pos_offset + j (q_rot and the cache already
+// written by rope_append): per-row split partials, then a merge into out.
+hipError_t launch_rows_attention(const AttnArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------------ misc kernels
 hipError_t launch_rmsnorm_rows(const uint16_t* h, const uint16_t* g, float eps, int rows, int k,

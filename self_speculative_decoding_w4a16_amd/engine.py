@@ -33,6 +33,7 @@ class SpecDecoder:
         self.status = torch.zeros(1, dtype=torch.int32, device=device)
         self.probs = torch.zeros((max(gamma, 1), 2), dtype=torch.float32, device=device)
         self.prefill_tokens = torch.zeros(self.max_tokens, dtype=torch.int32, device=device)
+        self._zero = torch.zeros(1, dtype=torch.int32, device=device)
         nbytes = _lib.workspace_bytes(model.c, self.max_tokens, capacity)
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _lib.workspace_init(self.ws)
@@ -73,6 +74,14 @@ class SpecDecoder:
 
     def commit(self):
         _lib.kv_rollback(self.c, self.n_accepted, self.out_tokens)
+
+    def ar_step(self):
+        """One plain autoregressive step of the draft model (a full-precision
+        model when no layer is substituted): run tokens[0] at kv_len, draw
+        tokens[1], then commit it (kv_len += 1, tokens[0] = tokens[1])."""
+        _lib.draft_step(self.model.c, self.c, 0, self.draft_temp, None, self.ws)
+        self._zero.zero_()
+        _lib.kv_rollback(self.c, self._zero, self.tokens[1:])
 
     def cycle(self, u_draft=None, r_codes=None, u_code=None):
         self.draft(u_draft)

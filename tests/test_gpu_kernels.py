@@ -61,7 +61,7 @@ def test_quantize_full_shapes_sampled_rows(cuda, name):
 
 
 @pytest.mark.parametrize("n,k,seed", [(512, 512, 0), (1000, 640, 1), (3, 64, 2), (4608, 3584, 3),
-                                      (20000, 1024, 4)])
+                                      (20000, 1024, 4), (9001, 2112, 5), (70001, 2112, 6)])
 def test_w4_gemv(cuda, n, k, seed):
     log(f"w4 gemv {n}x{k}")
     w = normal_tensor((n, k), 0.02, seed, cuda)
@@ -91,7 +91,8 @@ def test_w4_gemv_full_shapes_sampled_rows(cuda, name):
     assert rel_err(host(y)[rows], ref) < TOL
 
 
-@pytest.mark.parametrize("n,k,seed", [(512, 512, 0), (1000, 648, 1), (5, 8, 2), (152064, 3584, 3)])
+@pytest.mark.parametrize("n,k,seed", [(512, 512, 0), (1000, 648, 1), (5, 8, 2), (152064, 3584, 3),
+                                      (9001, 1032, 4), (70001, 520, 5)])
 def test_bf16_gemv(cuda, n, k, seed):
     log(f"bf16 gemv {n}x{k}")
     w = normal_tensor((n, k), 0.02, seed, cuda)
