@@ -81,6 +81,13 @@ __device__ __forceinline__ void group_rows(int64_t g, int64_t n, int64_t (&prow)
   }
 }
 
+// Weight pointers carried across loop iterations are kept in the global
+// address space explicitly, so loads through them are global_load (counted by
+// vmcnt only) and the next step's loads can stay in flight while the current
+// step is consumed.
+typedef const u32x4 __attribute__((address_space(1))) g_u32x4;
+typedef const uint32_t __attribute__((address_space(1))) g_u32;
+
 // One step: unit u of row r is W4 group (gb + lane + 64u) (two 16-byte code
 // chunks + its fp16 {scale, min}) or bf16 chunk (cb + lane + 64u) (16 bytes).
 // Indices past the row end are clamped; their contribution is skipped.
@@ -91,8 +98,8 @@ struct Step {
 };
 
 template <int R, int U, bool W4>
-__device__ __forceinline__ void load_step(Step<R, U, W4>& b, const u32x4* const (&wp)[R],
-                                          const uint32_t* const (&mp)[R], int base, int lane, int n_units) {
+__device__ __forceinline__ void load_step(Step<R, U, W4>& b, g_u32x4* const (&wp)[R],
+                                          g_u32* const (&mp)[R], int base, int lane, int n_units) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     int i = base + lane + u * SS_WAVE;
@@ -112,15 +119,15 @@ __device__ __forceinline__ void load_step(Step<R, U, W4>& b, const u32x4* const 
 
 template <int R, bool W4>
 __device__ __forceinline__ void row_ptrs(const GemvArgs& a, const int64_t (&prow)[R], int K,
-                                         const u32x4* (&wp)[R], const uint32_t* (&mp)[R]) {
+                                         g_u32x4* (&wp)[R], g_u32* (&mp)[R]) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if (W4) {
-      wp[r] = reinterpret_cast<const u32x4*>(a.codes + prow[r] * (K / 2));
-      mp[r] = reinterpret_cast<const uint32_t*>(a.meta) + prow[r] * (K / 64);
+      wp[r] = (g_u32x4*)(a.codes + prow[r] * (K / 2));
+      mp[r] = (g_u32*)(a.meta) + prow[r] * (K / 64);
     } else {
-      wp[r] = reinterpret_cast<const u32x4*>(a.w + prow[r] * K);
-      mp[r] = nullptr;
+      wp[r] = (g_u32x4*)(a.w + prow[r] * K);
+      mp[r] = (g_u32*)(a.meta);
     }
   }
 }
@@ -151,8 +158,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int64_t n_gr
   int64_t prow[R], out0;
   bool rv[R];
   group_rows<R, EPI>(g < n_groups ? g : 0, a.n, prow, rv, out0);
-  const u32x4* wp[R];
-  const uint32_t* mp[R];
+  g_u32x4* wp[R];
+  g_u32* mp[R];
   row_ptrs<R, W4>(a, prow, K, wp, mp);
   int base = 0;  // wave-uniform first unit of the current step
   Step<R, U, W4> cur;
@@ -341,8 +348,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int64_t n_gr
     const bool end_of_group = base1 >= n_units;
     int64_t prow1[R], out1 = out0;
     bool rv1[R];
-    const u32x4* wp1[R];
-    const uint32_t* mp1[R];
+    g_u32x4* wp1[R];
+    g_u32* mp1[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       prow1[r] = prow[r];
