@@ -137,17 +137,37 @@ def main():
     reject_ms = e[2].elapsed_time(e[3])
 
     # ---------------------------------------------------------------- kernels
+    # One more generation with every launch bracketed by HIP events on the
+    # launch stream.  Attention's algorithmic bytes depend on the device-side
+    # KV length, so they are added here from the host's record of it: a draft
+    # step at position p reads K and V of positions [0, p] once per layer, a
+    # verify pass reads [0, kv_len + gamma] once per layer.
     _lib.profile_start(400000)
-    one_generation()
+    _, ns_prof = one_generation()
     torch.cuda.synchronize()
     _lib.profile_stop()
+    kv_row = 2 * shape.n_kv_heads * shape.head_dim * 2 * shape.n_layers  # K+V bytes per position
+    attn_bytes = {"attn_draft": 0.0, "attn_verify": 0.0}
+    kv = kv0
+    for n in ns_prof:
+        attn_bytes["attn_draft"] += sum((kv + i + 1) * kv_row for i in range(gamma))
+        attn_bytes["attn_verify"] += (kv + gamma + 1) * kv_row
+        kv += n + 1
     kern = {}
     for k, name in enumerate(_lib.K_NAMES):
         n, ms, by = _lib.profile_read(k)
-        kern[name] = {"launches": n, "ms": round(ms, 4),
-                      "avg_us": round(1000 * ms / n, 3) if n else None,
-                      "gbs": round(by / (ms * 1e-3) / 1e9, 1) if ms > 0 and by > 0 else None,
-                      "bytes_per_launch": round(by / n) if n else None}
+        by += attn_bytes.get(name, 0.0)
+        kern[name] = {"launches": n, "ms": ms, "bytes": by}
+    for g, members in _lib.K_GROUPS.items():
+        kern[g] = {"launches": sum(kern[m]["launches"] for m in members),
+                   "ms": sum(kern[m]["ms"] for m in members),
+                   "bytes": sum(kern[m]["bytes"] for m in members)}
+    for name, k in kern.items():
+        n, ms, by = k["launches"], k["ms"], k["bytes"]
+        k.update({"ms": round(ms, 4), "avg_us": round(1000 * ms / n, 3) if n else None,
+                  "gbs": round(by / (ms * 1e-3) / 1e9, 1) if ms > 0 and by > 0 else None,
+                  "bytes_per_launch": round(by / n) if n else None})
+        del k["bytes"]
     log("kernels: " + json.dumps(kern))
 
     def roof(name):
@@ -158,8 +178,9 @@ def main():
                 "frac": round(k["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
                 "kernel": name, "avg_us": k["avg_us"], "bytes_per_launch": k["bytes_per_launch"]}
 
-    timed = [n for n in ("w4_gemv", "bf16_gemv", "verify_gemm") if kern[n]["launches"]]
-    dominant = max(timed, key=lambda n: kern[n]["ms"])
+    # dominant kernel: the single launch site with the most time in a step
+    sites = [n for n in _lib.K_NAMES if kern[n]["launches"] and kern[n]["gbs"]]
+    dominant = max(sites, key=lambda n: kern[n]["ms"])
 
     # ---------------------------------------------------------------- plain AR
     ar = None
@@ -210,6 +231,7 @@ def main():
         "roofline_w4_gemv": roof("w4_gemv"),
         "roofline_verify_gemm": roof("verify_gemm"),
         "roofline_bf16_gemv": roof("bf16_gemv"),
+        "roofline_attn_draft": roof("attn_draft"),
         "cpu_baseline": cpu,
         "tau": round(tau, 4),
         "cycles_per_step": round(cycles_per_gen, 2),

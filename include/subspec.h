@@ -230,16 +230,29 @@ int subspec_sample(const uint16_t *logits, int32_t vocab, float temp, const uint
 /* Profiling (host side; off by default)                                     */
 /* ------------------------------------------------------------------------ */
 
-/* Kernel classes timed by the profiler. */
+/* Launch sites timed by the profiler: one class per kernel and shape role, so
+ * that a class average is the average of one kernel at one shape. */
 enum {
-  SUBSPEC_K_W4_GEMV = 0,   /* draft GEMVs on 4-bit substitutes                  */
-  SUBSPEC_K_BF16_GEMV = 1, /* draft GEMVs on shared bf16 layers and lm_head     */
-  SUBSPEC_K_GEMM = 2,      /* verify GEMMs (matrix cores)                       */
-  SUBSPEC_K_ATTN = 3,      /* RoPE + KV append + attention                      */
-  SUBSPEC_K_SAMPLE = 4,    /* draft token draw                                  */
-  SUBSPEC_K_REJECT = 5,    /* rejection round                                   */
-  SUBSPEC_K_MISC = 6,      /* norms, embedding, KV bookkeeping                  */
-  SUBSPEC_K_CLASSES = 7
+  SUBSPEC_K_W4_QKV = 0,        /* draft QKV GEMV, 4-bit substitute layer           */
+  SUBSPEC_K_W4_O = 1,          /* draft O GEMV (+ attention split merge), 4-bit    */
+  SUBSPEC_K_W4_GATE_UP = 2,    /* draft gate/up GEMV with SiLU*up, 4-bit           */
+  SUBSPEC_K_W4_DOWN = 3,       /* draft down GEMV + residual, 4-bit                */
+  SUBSPEC_K_BF16_QKV = 4,      /* the same four on shared bf16 layers              */
+  SUBSPEC_K_BF16_O = 5,
+  SUBSPEC_K_BF16_GATE_UP = 6,
+  SUBSPEC_K_BF16_DOWN = 7,
+  SUBSPEC_K_LM_HEAD = 8,       /* draft lm_head GEMV (+ per-block max/argmax)      */
+  SUBSPEC_K_GEMM_QKV = 9,      /* verify GEMMs on the matrix cores                 */
+  SUBSPEC_K_GEMM_O = 10,
+  SUBSPEC_K_GEMM_GATE_UP = 11,
+  SUBSPEC_K_GEMM_DOWN = 12,
+  SUBSPEC_K_GEMM_LM_HEAD = 13,
+  SUBSPEC_K_ATTN_DRAFT = 14,   /* draft RoPE + KV append + split attention         */
+  SUBSPEC_K_ATTN_VERIFY = 15,  /* verify RoPE + KV append + causal attention       */
+  SUBSPEC_K_SAMPLE = 16,       /* draft token draw                                 */
+  SUBSPEC_K_REJECT = 17,       /* rejection round                                  */
+  SUBSPEC_K_MISC = 18,         /* norms, embedding, KV bookkeeping                 */
+  SUBSPEC_K_CLASSES = 19
 };
 
 /* Start recording: from now on every launch made by this library on any

@@ -84,8 +84,15 @@ _SIGS = {
                                        POINTER(ctypes.c_double)]),
 }
 
-K_W4_GEMV, K_BF16_GEMV, K_GEMM, K_ATTN, K_SAMPLE, K_REJECT, K_MISC = range(7)
-K_NAMES = ("w4_gemv", "bf16_gemv", "verify_gemm", "attention", "sample", "reject", "misc")
+# Profiler classes (launch sites), in the order of the SUBSPEC_K_* enum.
+K_NAMES = ("w4_qkv", "w4_o", "w4_gate_up", "w4_down",
+           "bf16_qkv", "bf16_o", "bf16_gate_up", "bf16_down", "lm_head",
+           "gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "gemm_lm_head",
+           "attn_draft", "attn_verify", "sample", "reject", "misc")
+K = {name: i for i, name in enumerate(K_NAMES)}
+# Groups of classes: every draft GEMV on a 4-bit substitute, every draft GEMV
+# on bf16 weights, and every verify GEMM.
+K_GROUPS = {"w4_gemv": K_NAMES[0:4], "bf16_gemv": K_NAMES[4:9], "verify_gemm": K_NAMES[9:14]}
 
 EXPORTS = tuple(_SIGS)
 

@@ -226,7 +226,10 @@ double gemv_bytes(const subspec_linear& l, int64_t n_out, bool resid) {
 double gemm_bytes(int64_t n_phys, int64_t k, int m, int64_t n_out, bool resid) {
   return 2.0 * n_phys * k + 2.0 * m * k + 2.0 * m * n_out * (resid ? 2 : 1);
 }
-int gemv_class(const subspec_linear& l) { return lin_is_w4(l) ? SUBSPEC_K_W4_GEMV : SUBSPEC_K_BF16_GEMV; }
+// site: 0 qkv, 1 o, 2 gate_up, 3 down
+int gemv_class(const subspec_linear& l, int site) {
+  return (lin_is_w4(l) ? SUBSPEC_K_W4_QKV : SUBSPEC_K_BF16_QKV) + site;
+}
 
 }  // namespace
 
@@ -307,7 +310,7 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
     a.y = w.qkv;
     a.valid = w.valid;
     {
-      prof::Scope ps(gemv_class(L.qkv_d), gemv_bytes(L.qkv_d, qkv, false), s);
+      prof::Scope ps(gemv_class(L.qkv_d, 0), gemv_bytes(L.qkv_d, qkv, false), s);
       HIPCHK(launch_gemv(lin_is_w4(L.qkv_d), l == 0 ? PRO_EMBED_NORM : PRO_NORM, EPI_STORE, a, s, nullptr));
     }
 
@@ -328,7 +331,7 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
     at.out = w.attn;
     at.splits = (st->capacity + decode_attn_keys_per_split() - 1) / decode_attn_keys_per_split();
     {
-      prof::Scope ps(SUBSPEC_K_ATTN, 0.0, s);
+      prof::Scope ps(SUBSPEC_K_ATTN_DRAFT, 0.0, s);
       HIPCHK(launch_decode_attention(at, w.valid, s));
     }
 
@@ -347,7 +350,7 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
     o.kv_len = st->kv_len;
     o.pos_offset = step;
     {
-      prof::Scope ps(gemv_class(L.o_d), gemv_bytes(L.o_d, H, true), s);
+      prof::Scope ps(gemv_class(L.o_d, 1), gemv_bytes(L.o_d, H, true), s);
       HIPCHK(launch_gemv(lin_is_w4(L.o_d), PRO_ATTN_MERGE, EPI_RESID, o, s, nullptr));
     }
 
@@ -361,7 +364,7 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
     g.y = w.act;
     g.valid = w.valid;
     {
-      prof::Scope ps(gemv_class(L.gate_up_d), gemv_bytes(L.gate_up_d, F, false), s);
+      prof::Scope ps(gemv_class(L.gate_up_d, 2), gemv_bytes(L.gate_up_d, F, false), s);
       HIPCHK(launch_gemv(lin_is_w4(L.gate_up_d), PRO_NORM, EPI_SILU, g, s, nullptr));
     }
 
@@ -374,7 +377,7 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
     dn.resid = w.h;
     dn.valid = w.valid;
     {
-      prof::Scope ps(gemv_class(L.down_d), gemv_bytes(L.down_d, H, true), s);
+      prof::Scope ps(gemv_class(L.down_d, 3), gemv_bytes(L.down_d, H, true), s);
       HIPCHK(launch_gemv(lin_is_w4(L.down_d), PRO_X, EPI_RESID, dn, s, nullptr));
     }
   }
@@ -393,7 +396,7 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
   int lm_blocks = 0;
   {
     const subspec_linear lml{m->lm_head, nullptr, nullptr, m->vocab, H};
-    prof::Scope ps(SUBSPEC_K_BF16_GEMV, gemv_bytes(lml, m->vocab, false), s);
+    prof::Scope ps(SUBSPEC_K_LM_HEAD, gemv_bytes(lml, m->vocab, false), s);
     HIPCHK(launch_gemv(false, PRO_NORM, EPI_LOGITS, lm, s, &lm_blocks));
   }
   SampleWs sw{w.logit_max, w.logit_arg, w.sample_sums, w.sample_counter};
@@ -433,7 +436,7 @@ int subspec_verify(const subspec_model* m, const subspec_state* st, int32_t n_to
     }
     GemmArgs q{L.qkv.w, qkv, H, w.xn, mt, w.qkv, qkv, nullptr, w.gemm_part, w.gemm_counters};
     {
-      prof::Scope ps(SUBSPEC_K_GEMM, gemm_bytes(qkv, H, mt, qkv, false), s);
+      prof::Scope ps(SUBSPEC_K_GEMM_QKV, gemm_bytes(qkv, H, mt, qkv, false), s);
       HIPCHK(launch_gemm(GEPI_STORE, q, s));
     }
     AttnArgs at{};
@@ -453,13 +456,13 @@ int subspec_verify(const subspec_model* m, const subspec_state* st, int32_t n_to
     at.out = w.attn;
     at.splits = (st->capacity + decode_attn_keys_per_split() - 1) / decode_attn_keys_per_split();
     {
-      prof::Scope ps(SUBSPEC_K_ATTN, 0.0, s);
+      prof::Scope ps(SUBSPEC_K_ATTN_VERIFY, 0.0, s);
       HIPCHK(launch_rope_append(at, s));
       HIPCHK(launch_rows_attention(at, s));
     }
     GemmArgs o{L.o.w, H, qd, w.attn, mt, w.h, H, w.h, w.gemm_part, w.gemm_counters};
     {
-      prof::Scope ps(SUBSPEC_K_GEMM, gemm_bytes(H, qd, mt, H, true), s);
+      prof::Scope ps(SUBSPEC_K_GEMM_O, gemm_bytes(H, qd, mt, H, true), s);
       HIPCHK(launch_gemm(GEPI_RESID, o, s));
     }
     {
@@ -468,12 +471,12 @@ int subspec_verify(const subspec_model* m, const subspec_state* st, int32_t n_to
     }
     GemmArgs g{L.gate_up.w, F, H, w.xn, mt, w.act, F, nullptr, w.gemm_part, w.gemm_counters};
     {
-      prof::Scope ps(SUBSPEC_K_GEMM, gemm_bytes(2 * F, H, mt, F, false), s);
+      prof::Scope ps(SUBSPEC_K_GEMM_GATE_UP, gemm_bytes(2 * F, H, mt, F, false), s);
       HIPCHK(launch_gemm(GEPI_SILU, g, s));
     }
     GemmArgs dn{L.down.w, H, F, w.act, mt, w.h, H, w.h, w.gemm_part, w.gemm_counters};
     {
-      prof::Scope ps(SUBSPEC_K_GEMM, gemm_bytes(H, F, mt, H, true), s);
+      prof::Scope ps(SUBSPEC_K_GEMM_DOWN, gemm_bytes(H, F, mt, H, true), s);
       HIPCHK(launch_gemm(GEPI_RESID, dn, s));
     }
   }
@@ -484,7 +487,7 @@ int subspec_verify(const subspec_model* m, const subspec_state* st, int32_t n_to
     }
     GemmArgs lm{m->lm_head, m->vocab, H, w.xn, mt, logits, m->vocab, nullptr, w.gemm_part,
                 w.gemm_counters};
-    prof::Scope ps(SUBSPEC_K_GEMM, gemm_bytes(m->vocab, H, mt, m->vocab, false), s);
+    prof::Scope ps(SUBSPEC_K_GEMM_LM_HEAD, gemm_bytes(m->vocab, H, mt, m->vocab, false), s);
     HIPCHK(launch_gemm(GEPI_STORE, lm, s));
   }
   return ok();

@@ -10,11 +10,12 @@
 //    computed in the prologue of every block, so it costs no extra launch.
 //  * Every lane streams 16-byte chunks of R rows (R = 1, 2, 4) with several
 //    chunks in flight; a wave covers whole rows, lane c takes chunks
-//    c, c+64, ...  Rows are contiguous, so each wave load touches R fully
-//    used 1 KiB segments.
+//    c, c+64, ...  Rows are contiguous, so each wave load reads R fully used,
+//    contiguous 1 KiB segments, for bf16 rows (8 weights a chunk) and W4 code
+//    rows (32 weights a chunk) alike.
 //  * W4 dequantisation happens in registers: a nibble pair becomes the bf16
 //    pair (128+q_a, 128+q_b) with one and-or, and v_dot2_f32_bf16 multiplies
-//    it by the x pair.  Per half-group (32 weights)
+//    it by the x pair.  Per chunk (32 weights of one 64-group)
 //        sum_k (q_k s + m) x_k = s * sum_k (128+q_k) x_k + (m - 128 s) * sum_k x_k
 //    so the scale and min are applied once per 32 weights; sum_k x_k comes
 //    from LDS.
@@ -25,6 +26,8 @@
 #include "internal.h"
 
 #include <stdlib.h>
+
+#include <mutex>
 
 namespace {
 
@@ -51,13 +54,13 @@ __device__ __forceinline__ float bf16_chunk_dot(u32x4 w, u32x4 xq, float d) {
   return d;
 }
 
-// W4: x of 64-group gi, quad w (8 values) lives in LDS slot w4_slot(gi, w):
-// lanes of a wave reading the same quad of consecutive groups hit
-// consecutive 16-byte slots (no bank conflicts).
-__host__ __device__ __forceinline__ int w4_slot(int gi, int w) {
-  return ((gi >> 6) << 9) + (w << 6) + (gi & 63);
+// W4: x[32c + 8w .. 32c + 8w + 7] (word w of 32-value chunk c) lives in LDS
+// slot w4_slot(c, w): lanes of a wave reading the same word of consecutive
+// chunks hit consecutive 16-byte slots (no bank conflicts).
+__host__ __device__ __forceinline__ int w4_slot(int c, int w) {
+  return ((c >> 6) << 8) + (w << 6) + (c & 63);
 }
-__host__ __device__ __forceinline__ int w4_slots(int K) { return ((K / 64 + 63) / 64) * 512; }
+__host__ __device__ __forceinline__ int w4_slots(int K) { return ((K / 32 + 63) / 64) * 256; }
 
 // Physical rows of row group g (R rows; in SiLU mode R/2 gate rows + the
 // matching R/2 up rows).  Rows past the end are clamped to row 0 (always a
@@ -88,12 +91,12 @@ __device__ __forceinline__ void group_rows(int64_t g, int64_t n, int64_t (&prow)
 typedef const u32x4 __attribute__((address_space(1))) g_u32x4;
 typedef const uint32_t __attribute__((address_space(1))) g_u32;
 
-// One step: unit u of row r is W4 group (gb + lane + 64u) (two 16-byte code
-// chunks + its fp16 {scale, min}) or bf16 chunk (cb + lane + 64u) (16 bytes).
-// Indices past the row end are clamped; their contribution is skipped.
+// One step: unit u of row r is the 16-byte chunk (base + lane + 64u) of the
+// row; for W4 also the fp16 {scale, min} of its 64-group.  Indices past the
+// row end are clamped; their contribution is skipped.
 template <int R, int U, bool W4>
 struct Step {
-  u32x4 v[U][R][W4 ? 2 : 1];
+  u32x4 v[U][R];
   uint32_t m[U][R];
 };
 
@@ -106,13 +109,8 @@ __device__ __forceinline__ void load_step(Step<R, U, W4>& b, g_u32x4* const (&wp
     i = i < n_units ? i : n_units - 1;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if (W4) {
-        b.v[u][r][0] = __builtin_nontemporal_load(wp[r] + 2 * i);
-        b.v[u][r][W4 ? 1 : 0] = __builtin_nontemporal_load(wp[r] + 2 * i + 1);
-        b.m[u][r] = mp[r][i];
-      } else {
-        b.v[u][r][0] = __builtin_nontemporal_load(wp[r] + i);
-      }
+      b.v[u][r] = __builtin_nontemporal_load(wp[r] + i);
+      if (W4) b.m[u][r] = mp[r][i >> 1];
     }
   }
 }
@@ -132,6 +130,29 @@ __device__ __forceinline__ void row_ptrs(const GemvArgs& a, const int64_t (&prow
   }
 }
 
+// Stores item `it` (x[8it .. 8it+7], bf16) into LDS: as consecutive pairs
+// for bf16 weights; for W4 as the pairs (x0,x4),(x1,x5),(x2,x6),(x3,x7) in
+// slot w4_slot(it/4, it%4), plus the sum of the chunk's 32 values, reduced
+// over the four lanes that hold the chunk.  Every lane of the wave calls it.
+template <bool W4>
+__device__ __forceinline__ void put_x(u32x4* smem4, float* xsum, int it, bool ok, const uint16_t (&xb)[8]) {
+  if (W4) {
+    float xs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xs += ss::bf2f(xb[i]);
+    xs += __shfl_xor(xs, 1, SS_WAVE);
+    xs += __shfl_xor(xs, 2, SS_WAVE);
+    if (ok) {
+      smem4[w4_slot(it >> 2, it & 3)] = u32x4{ss::pack_bf(xb[0], xb[4]), ss::pack_bf(xb[1], xb[5]),
+                                             ss::pack_bf(xb[2], xb[6]), ss::pack_bf(xb[3], xb[7])};
+      if ((it & 3) == 0) xsum[it >> 2] = xs;
+    }
+  } else if (ok) {
+    smem4[it] = u32x4{ss::pack_bf(xb[0], xb[1]), ss::pack_bf(xb[2], xb[3]), ss::pack_bf(xb[4], xb[5]),
+                      ss::pack_bf(xb[6], xb[7])};
+  }
+}
+
 template <int R, bool W4, int PRO, int EPI>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int64_t n_groups, uint32_t mask_arg,
                                                         uint32_t magic_arg) {
@@ -144,8 +165,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int64_t n_gr
   const int tid = threadIdx.x, lane = tid & (SS_WAVE - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / SS_WAVE);  // wave-uniform: rows in SGPRs
   const int K = (int)a.k;
-  const int n_units = W4 ? K / 64 : K / 8;  // per row: W4 groups or bf16 16-byte chunks
-  constexpr int U = W4 ? ((R >= 4) ? 1 : (R == 2 ? 2 : 4)) : ((R >= 4) ? 2 : (R == 2 ? 4 : 8));
+  const int n_units = W4 ? K / 32 : K / 8;  // 16-byte chunks per row
+  constexpr int U = (R >= 4) ? 2 : (R == 2 ? 4 : 8);
   constexpr int RO = (EPI == EPI_SILU) ? R / 2 : R;
   const int64_t wave_stride = (int64_t)gridDim.x * kWaves;
   const uint32_t mask = __builtin_amdgcn_readfirstlane(mask_arg);
@@ -170,10 +191,10 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int64_t n_gr
   if (PRO == PRO_NORM) src = a.h;
   if (PRO == PRO_EMBED_NORM) src = a.embed + (int64_t)(*a.token) * K;
   float* xsum = reinterpret_cast<float*>(smem4 + (W4 ? w4_slots(K) : K / 8));
-  // items: W4 -> 64-value groups (8 quads), bf16 -> 8-value quads
-  constexpr int QPI = W4 ? 8 : 1;
-  constexpr int NI = W4 ? 1 : 3;  // items per thread held in registers when normalising
-  const int n_items = W4 ? K / 64 : K / 8;
+  // items: 8 consecutive values of x (one 16-byte quad); for W4 the four
+  // items of a 32-value chunk sit in four consecutive lanes
+  constexpr int NI = 3;  // items per thread held in registers when normalising
+  const int n_items = K / 8;
   if (PRO == PRO_ATTN_MERGE) {
     // x[h*128 + d] = sum_s f_s o_s[d] / sum_s f_s l_s, f_s = exp(m_s - max_s m_s),
     // merged over the decode-attention splits in split order, batches of 4.
@@ -232,16 +253,15 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int64_t n_gr
       const int k0 = h * DH + d0;  // first input column of this chunk
       if (W4) {
         xs += __shfl_xor(xs, 1, SS_WAVE);
-        xs += __shfl_xor(xs, 2, SS_WAVE);
         if (ok) {
 #pragma unroll
           for (int qd = 0; qd < 2; ++qd) {
             const uint16_t* xq = xb + 8 * qd;
-            smem4[w4_slot(k0 / 64, (k0 % 64) / 8 + qd)] =
+            smem4[w4_slot(k0 / 32, (k0 % 32) / 8 + qd)] =
                 u32x4{ss::pack_bf(xq[0], xq[4]), ss::pack_bf(xq[1], xq[5]), ss::pack_bf(xq[2], xq[6]),
                       ss::pack_bf(xq[3], xq[7])};
           }
-          if ((ch & 3) == 0) xsum[k0 / 64] = xs;
+          if ((ch & 1) == 0) xsum[k0 / 32] = xs;
         }
       } else if (ok) {
 #pragma unroll
@@ -253,21 +273,22 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int64_t n_gr
       }
     }
   } else if (PRO != PRO_X) {
-    u32x4 hv[NI][QPI];
+    const u32x4* src4 = reinterpret_cast<const u32x4*>(src);
+    const u32x4* g4 = reinterpret_cast<const u32x4*>(a.norm_w);
+    u32x4 hv[NI], gv[NI];
     float ss = 0.0f;
 #pragma unroll
     for (int t = 0; t < NI; ++t) {
       const int it = tid + t * kThreads;
+      const bool ok = it < n_items;
+      hv[t] = ok ? src4[it] : u32x4{0u, 0u, 0u, 0u};
+      gv[t] = ok ? g4[it] : u32x4{0u, 0u, 0u, 0u};
+      const uint32_t wv[4] = {hv[t].x, hv[t].y, hv[t].z, hv[t].w};
 #pragma unroll
-      for (int q = 0; q < QPI; ++q) {
-        hv[t][q] = it < n_items ? reinterpret_cast<const u32x4*>(src)[it * QPI + q] : u32x4{0u, 0u, 0u, 0u};
-        const uint32_t wv[4] = {hv[t][q].x, hv[t][q].y, hv[t][q].z, hv[t][q].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float lo = ss::lo_bf(wv[i]), hi = ss::hi_bf(wv[i]);
-          ss += lo * lo;
-          ss += hi * hi;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const float lo = ss::lo_bf(wv[i]), hi = ss::hi_bf(wv[i]);
+        ss += lo * lo;
+        ss += hi * hi;
       }
     }
     ss = ss::wave_sum(ss);
@@ -278,59 +299,37 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int64_t n_gr
     for (int i = 0; i < kWaves; ++i) tot += red[i];
     const float inv = 1.0f / sqrtf(tot / (float)K + a.eps);
     if (PRO == PRO_EMBED_NORM && blockIdx.x == 0) {
-      for (int q = tid; q < K / 8; q += kThreads)
-        reinterpret_cast<u32x4*>(a.h_out)[q] = reinterpret_cast<const u32x4*>(src)[q];
+      for (int q = tid; q < n_items; q += kThreads) reinterpret_cast<u32x4*>(a.h_out)[q] = src4[q];
     }
 #pragma unroll
     for (int t = 0; t < NI; ++t) {
       const int it = tid + t * kThreads;
-      if (it >= n_items) continue;
-      float xs = 0.0f;
+      if (t * kThreads >= n_items) break;  // block-uniform
+      const bool ok = it < n_items;
+      const uint32_t wv[4] = {hv[t].x, hv[t].y, hv[t].z, hv[t].w};
+      const uint32_t gw[4] = {gv[t].x, gv[t].y, gv[t].z, gv[t].w};
+      uint16_t xb[8];
 #pragma unroll
-      for (int q = 0; q < QPI; ++q) {
-        const u32x4 gv = reinterpret_cast<const u32x4*>(a.norm_w)[it * QPI + q];
-        const uint32_t wv[4] = {hv[t][q].x, hv[t][q].y, hv[t][q].z, hv[t][q].w};
-        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-        uint16_t xb[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          xb[2 * i] = ss::f2bf(ss::lo_bf(wv[i]) * inv * ss::lo_bf(gw[i]));
-          xb[2 * i + 1] = ss::f2bf(ss::hi_bf(wv[i]) * inv * ss::hi_bf(gw[i]));
-        }
-        if (W4) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) xs += ss::bf2f(xb[i]);
-          smem4[w4_slot(it, q)] = u32x4{ss::pack_bf(xb[0], xb[4]), ss::pack_bf(xb[1], xb[5]),
-                                        ss::pack_bf(xb[2], xb[6]), ss::pack_bf(xb[3], xb[7])};
-        } else {
-          smem4[it] = u32x4{ss::pack_bf(xb[0], xb[1]), ss::pack_bf(xb[2], xb[3]),
-                            ss::pack_bf(xb[4], xb[5]), ss::pack_bf(xb[6], xb[7])};
-        }
+      for (int i = 0; i < 4; ++i) {
+        xb[2 * i] = ss::f2bf(ss::lo_bf(wv[i]) * inv * ss::lo_bf(gw[i]));
+        xb[2 * i + 1] = ss::f2bf(ss::hi_bf(wv[i]) * inv * ss::hi_bf(gw[i]));
       }
-      if (W4) xsum[it] = xs;
+      put_x<W4>(smem4, xsum, it, ok, xb);
     }
   } else {
-    for (int it = tid; it < n_items; it += kThreads) {
-      float xs = 0.0f;
+    const u32x4* src4 = reinterpret_cast<const u32x4*>(src);
+    for (int b0 = 0; b0 < n_items; b0 += kThreads) {  // block-uniform trip count
+      const int it = b0 + tid;
+      const bool ok = it < n_items;
+      const u32x4 v = ok ? src4[it] : u32x4{0u, 0u, 0u, 0u};
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+      uint16_t xb[8];
 #pragma unroll
-      for (int q = 0; q < QPI; ++q) {
-        const u32x4 v = reinterpret_cast<const u32x4*>(src)[it * QPI + q];
-        if (W4) {
-          const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-          uint16_t xb[8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            xb[2 * i] = (uint16_t)(wv[i] & 0xffffu);
-            xb[2 * i + 1] = (uint16_t)(wv[i] >> 16);
-            xs += ss::lo_bf(wv[i]) + ss::hi_bf(wv[i]);
-          }
-          smem4[w4_slot(it, q)] = u32x4{ss::pack_bf(xb[0], xb[4]), ss::pack_bf(xb[1], xb[5]),
-                                        ss::pack_bf(xb[2], xb[6]), ss::pack_bf(xb[3], xb[7])};
-        } else {
-          smem4[it] = v;
-        }
+      for (int i = 0; i < 4; ++i) {
+        xb[2 * i] = (uint16_t)(wv[i] & 0xffffu);
+        xb[2 * i + 1] = (uint16_t)(wv[i] >> 16);
       }
-      if (W4) xsum[it] = xs;
+      put_x<W4>(smem4, xsum, it, ok, xb);
     }
   }
   __syncthreads();
@@ -373,17 +372,15 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int64_t n_gr
       if (i < n_units) {
         if (W4) {
           const float xs = xsum[i];
+          const u32x4 x0 = smem4[w4_slot(i, 0)], x1 = smem4[w4_slot(i, 1)];
+          const u32x4 x2 = smem4[w4_slot(i, 2)], x3 = smem4[w4_slot(i, 3)];
 #pragma unroll
           for (int r = 0; r < R; ++r) {
-            float d0 = 0.0f, d1 = 0.0f;
-#pragma unroll
-            for (int hlf = 0; hlf < 2; ++hlf) {
-              const u32x4 c = cur.v[u][r][W4 ? hlf : 0];
-              d0 = w4_word_dot(c.x, smem4[w4_slot(i, 4 * hlf + 0)], d0, mask, magic);
-              d1 = w4_word_dot(c.y, smem4[w4_slot(i, 4 * hlf + 1)], d1, mask, magic);
-              d0 = w4_word_dot(c.z, smem4[w4_slot(i, 4 * hlf + 2)], d0, mask, magic);
-              d1 = w4_word_dot(c.w, smem4[w4_slot(i, 4 * hlf + 3)], d1, mask, magic);
-            }
+            const u32x4 c = cur.v[u][r];
+            float d0 = w4_word_dot(c.x, x0, 0.0f, mask, magic);
+            float d1 = w4_word_dot(c.y, x1, 0.0f, mask, magic);
+            d0 = w4_word_dot(c.z, x2, d0, mask, magic);
+            d1 = w4_word_dot(c.w, x3, d1, mask, magic);
             const float sc = ss::h2f((uint16_t)(cur.m[u][r] & 0xffffu));
             const float mn = ss::h2f((uint16_t)(cur.m[u][r] >> 16));
             acc[r] += sc * (d0 + d1) + (mn - 128.0f * sc) * xs;
@@ -391,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int64_t n_gr
         } else {
           const u32x4 xq = smem4[i];
 #pragma unroll
-          for (int r = 0; r < R; ++r) acc[r] = bf16_chunk_dot(cur.v[u][r][0], xq, acc[r]);
+          for (int r = 0; r < R; ++r) acc[r] = bf16_chunk_dot(cur.v[u][r], xq, acc[r]);
         }
       }
     }
@@ -462,9 +459,32 @@ int device_cus() {
   return cus;
 }
 
-// Blocks of a persistent launch: a few per compute unit, fewer when the
+// Resident blocks per compute unit of one kernel at one LDS size, from the
+// runtime's occupancy calculator (register and LDS limits), cached.
+struct Occupancy {
+  std::mutex mu;
+  size_t lds[8];
+  int fit[8];
+  int n = 0;
+  int get(const void* fn, size_t l) {
+    std::lock_guard<std::mutex> g(mu);
+    for (int i = 0; i < n; ++i)
+      if (lds[i] == l) return fit[i];
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kThreads, l) != hipSuccess || nb < 1) nb = 1;
+    if (n < 8) {
+      lds[n] = l;
+      fit[n] = nb;
+      ++n;
+    }
+    return nb;
+  }
+};
+
+// Blocks of a persistent launch: a few per compute unit, no more than fit on
+// a compute unit at once (so the grid runs in one round), fewer when the
 // matrix has fewer row groups.
-int64_t gemv_blocks(int64_t n_groups, bool w4, int pro) {
+int64_t gemv_blocks(int64_t n_groups, bool w4, int pro, int fit) {
   static int per_cu = -1;
   if (per_cu < 0) {
     const char* e = getenv("SUBSPEC_GEMV_BLOCKS_PER_CU");
@@ -472,17 +492,25 @@ int64_t gemv_blocks(int64_t n_groups, bool w4, int pro) {
     if (per_cu <= 0) per_cu = 4;
   }
   // the attention-merge prologue is redone by every block: one block per CU
-  const int64_t cap = (int64_t)device_cus() * (pro == PRO_ATTN_MERGE ? 1 : per_cu * (w4 ? 1 : 2));
+  int want = pro == PRO_ATTN_MERGE ? 1 : per_cu * (w4 ? 1 : 2);
+  if (fit > 0 && want > fit) want = fit;
+  const int64_t cap = (int64_t)device_cus() * want;
   const int64_t need = (n_groups + kWaves - 1) / kWaves;
   return need < cap ? need : cap;
+}
+
+size_t gemv_lds(bool w4, int64_t k) {
+  return w4 ? (size_t)w4_slots((int)k) * 16 + (size_t)(k / 32) * 4 : (size_t)k * 2;
 }
 
 template <int R, bool W4, int PRO, int EPI>
 hipError_t launch_one(const GemvArgs& a, hipStream_t s, int* blocks_out) {
   constexpr int RO = (EPI == EPI_SILU) ? R / 2 : R;
+  static Occupancy occ;
   const int64_t n_groups = (a.n + RO - 1) / RO;
-  const int64_t blocks = gemv_blocks(n_groups, W4, PRO);
-  const size_t lds = W4 ? (size_t)w4_slots((int)a.k) * 16 + (size_t)(a.k / 64) * 4 : (size_t)a.k * 2;
+  const size_t lds = gemv_lds(W4, a.k);
+  const int fit = occ.get(reinterpret_cast<const void*>(&gemv_kernel<R, W4, PRO, EPI>), lds);
+  const int64_t blocks = gemv_blocks(n_groups, W4, PRO, fit);
   if (blocks_out) *blocks_out = (int)blocks;
   hipLaunchKernelGGL((gemv_kernel<R, W4, PRO, EPI>), dim3((unsigned)blocks), dim3(kThreads), lds, s, a,
                      n_groups, 0x000F000Fu, 0x43004300u);
@@ -524,10 +552,11 @@ static int pick_r(int64_t n, int epi) {
   return 1;
 }
 
+// Upper bound on the blocks of a launch (sizes per-block partial buffers).
 int gemv_max_blocks(bool w4, int64_t n, int epi) {
   const int R = pick_r(n, epi);
   const int RO = (epi == EPI_SILU) ? R / 2 : R;
-  return (int)gemv_blocks((n + RO - 1) / RO, w4, PRO_NORM);
+  return (int)gemv_blocks((n + RO - 1) / RO, w4, PRO_NORM, 0);
 }
 
 hipError_t launch_gemv(bool w4, int pro, int epi, const GemvArgs& a, hipStream_t s, int* blocks_out) {
