@@ -216,6 +216,20 @@ int subspec_w4_gemv(const uint8_t *codes, const uint16_t *meta, int64_t n, int64
 int subspec_bf16_gemv(const uint16_t *w, int64_t n, int64_t k, const uint16_t *x, uint16_t *y,
                       void *stream);
 
+/* The draft step's fused GEMV, one launch (the kernels draft_step runs, at
+ * kernel level):
+ *   x' = norm_w ? bf16( x * rsqrt(mean(x^2) + eps) * norm_w ) : x   (RMSNorm)
+ *   epilogue 0: y[n] = bf16( W x' )[n]                 for n < w->n
+ *   epilogue 1: y[n] = bf16( resid[n] + (W x')[n] )    for n < w->n
+ *   epilogue 2: y[n] = bf16( SiLU(g) * u ), g = bf16((W x')[n]),
+ *               u = bf16((W x')[F + n]), for n < F = w->n / 2 (gate rows
+ *               first, then the up rows)
+ * w: bf16 (w set) or W4 (codes + meta set) weights [n][k]; x, norm_w bf16 [k];
+ * resid, y bf16.  k % 64 == 0, k <= 28672 (k <= 6144 with norm_w).  Errors:
+ * EINVAL for bad pointers, epilogue or linear; ESHAPE / EUNSUPPORTED for k. */
+int subspec_gemv(const subspec_linear *w, const uint16_t *x, const uint16_t *norm_w, float eps,
+                 int32_t epilogue, const uint16_t *resid, uint16_t *y, void *stream);
+
 /* Y[t][n] = bf16( sum_k X[t][k] W[n][k] ) for t < m <= 64 (the verify GEMM
  * on matrix cores).  X bf16 [m][k], Y bf16 [m][n]; k % 128 == 0. */
 int subspec_bf16_gemm(const uint16_t *w, int64_t n, int64_t k, const uint16_t *x, int32_t m,
@@ -255,19 +269,23 @@ enum {
   SUBSPEC_K_CLASSES = 19
 };
 
-/* Start recording: from now on every launch made by this library on any
- * stream is bracketed by a pair of HIP events on that stream, up to
- * `max_records` launches (later launches are not recorded).  Creates the
- * events (host-side objects; no device memory).  Returns SUBSPEC_EHIP if
- * event creation fails. */
+/* Start recording: from now on every kernel this library launches, on any
+ * stream, is launched with a pair of HIP events that take the dispatch's own
+ * start and end timestamps (hipExtLaunchKernel), up to `max_records` records
+ * (one per launch, or one per API step that makes several launches; later
+ * launches are not recorded).  Creates the events (host-side objects; no
+ * device memory).  Returns SUBSPEC_EHIP if event creation fails. */
 int subspec_profile_start(int32_t max_records);
 
 /* Stop recording (events already recorded stay readable). */
 int subspec_profile_stop(void);
 
 /* Synchronise the recorded events and report, for kernel class `cls`, the
- * number of launches, their summed duration in milliseconds and their summed
- * algorithmic bytes (weights, activations and KV each counted once). */
+ * number of records, their summed duration in milliseconds and their summed
+ * algorithmic bytes (weights, activations and KV each counted once; 0 where
+ * the host does not know them, as for attention, whose KV length lives on
+ * the device).  A record's duration runs from the end of the previous record
+ * on the same stream (or from its own start stamp, if later) to its end. */
 int subspec_profile_read(int32_t cls, int64_t *launches, double *total_ms, double *bytes);
 
 #ifdef __cplusplus

@@ -74,6 +74,8 @@ _SIGS = {
     "subspec_w4_gemv": (c_int32, [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p,
                                   c_void_p]),
     "subspec_bf16_gemv": (c_int32, [c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
+    "subspec_gemv": (c_int32, [POINTER(Linear), c_void_p, c_void_p, c_float, c_int32, c_void_p,
+                               c_void_p, c_void_p]),
     "subspec_bf16_gemm": (c_int32, [c_void_p, c_int64, c_int64, c_void_p, c_int32, c_void_p,
                                     c_void_p, c_size_t, c_void_p]),
     "subspec_sample": (c_int32, [c_void_p, c_int32, c_float, c_void_p, c_void_p, c_void_p,
@@ -193,6 +195,24 @@ def w4_gemv(codes, meta, n, k, x, y, stream=None):
 def bf16_gemv(w, x, y, stream=None):
     n, k = w.shape
     check(lib().subspec_bf16_gemv(_p(w), n, k, _p(x), _p(y), _stream(stream)))
+
+
+def linear(w=None, codes=None, meta=None, n=None, k=None):
+    """A subspec_linear for bf16 weights w [n][k] or W4 codes [n][k/2] + meta."""
+    if w is not None:
+        n, k = w.shape
+        return Linear(_p(w), None, None, n, k)
+    n = codes.shape[0] if n is None else n
+    k = 2 * codes.shape[1] if k is None else k
+    return Linear(None, _p(codes), _p(meta), n, k)
+
+
+GEMV_STORE, GEMV_RESID, GEMV_SILU = 0, 1, 2
+
+
+def gemv(lin, x, y, norm_w=None, eps=0.0, epilogue=GEMV_STORE, resid=None, stream=None):
+    check(lib().subspec_gemv(ctypes.byref(lin), _p(x), _p(norm_w), eps, epilogue, _p(resid), _p(y),
+                             _stream(stream)))
 
 
 def bf16_gemm(w, x, y, ws, stream=None):

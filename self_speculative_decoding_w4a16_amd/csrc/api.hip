@@ -549,6 +549,39 @@ int subspec_w4_gemv(const uint8_t* codes, const uint16_t* meta, int64_t n, int64
   return ok();
 }
 
+int subspec_gemv(const subspec_linear* w, const uint16_t* x, const uint16_t* norm_w, float eps,
+                 int32_t epilogue, const uint16_t* resid, uint16_t* y, void* stream) {
+  if (!w || !x || !y) return fail(SUBSPEC_EINVAL, "w, x and y must be set");
+  if (!lin_is_bf16(*w) && !lin_is_w4(*w))
+    return fail(SUBSPEC_EINVAL, "set exactly one of w (bf16) or codes+meta (W4)");
+  if (w->n < 1 || w->k < 1) return fail(SUBSPEC_EINVAL, "n and k must be positive");
+  if (w->k % 64 != 0) return fail(SUBSPEC_ESHAPE, "k must be a multiple of 64");
+  if (w->k > kMaxGemvK) return fail(SUBSPEC_EUNSUPPORTED, "k above %d", kMaxGemvK);
+  if (norm_w && w->k > kMaxNormK) return fail(SUBSPEC_EUNSUPPORTED, "k above %d with norm_w", kMaxNormK);
+  if (epilogue < 0 || epilogue > 2) return fail(SUBSPEC_EINVAL, "epilogue must be 0, 1 or 2");
+  if (epilogue == 1 && !resid) return fail(SUBSPEC_EINVAL, "resid must be set for epilogue 1");
+  if (epilogue == 2 && w->n % 2 != 0) return fail(SUBSPEC_ESHAPE, "epilogue 2 needs an even row count");
+  if (norm_w && !(eps >= 0.0f)) return fail(SUBSPEC_EINVAL, "eps must be >= 0");
+  GemvArgs a{};
+  set_linear(a, *w);
+  a.n = epilogue == 2 ? w->n / 2 : w->n;
+  a.k = w->k;
+  a.x = x;
+  a.h = x;
+  a.norm_w = norm_w;
+  a.eps = eps;
+  a.resid = resid;
+  a.y = y;
+  const int epi = epilogue == 0 ? EPI_STORE : epilogue == 1 ? EPI_RESID : EPI_SILU;
+  const int pro = norm_w ? PRO_NORM : PRO_X;
+  if (pro == PRO_X && epi == EPI_SILU)
+    return fail(SUBSPEC_EUNSUPPORTED, "epilogue 2 is fused with the norm prologue only");
+  if (pro == PRO_NORM && epi == EPI_RESID)
+    return fail(SUBSPEC_EUNSUPPORTED, "epilogue 1 is fused with the plain prologue only");
+  HIPCHK(launch_gemv(lin_is_w4(*w), pro, epi, a, hs(stream), nullptr));
+  return ok();
+}
+
 int subspec_bf16_gemv(const uint16_t* w, int64_t n, int64_t k, const uint16_t* x, uint16_t* y,
                       void* stream) {
   if (!w || !x || !y) return fail(SUBSPEC_EINVAL, "w, x and y must be set");

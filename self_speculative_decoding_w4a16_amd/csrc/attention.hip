@@ -13,6 +13,7 @@
 // The draft step's partials are merged by the output projection's prologue.
 #include "common.h"
 #include "internal.h"
+#include "profile.h"
 
 namespace {
 
@@ -278,23 +279,23 @@ __global__ __launch_bounds__(128) void rows_merge_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_rope_append(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(rope_append_kernel, dim3(a.m, a.n_q + a.n_kv), dim3(64), 0, s, a);
+  SS_LAUNCH(rope_append_kernel, dim3(a.m, a.n_q + a.n_kv), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_attention(const AttnArgs& a, const int32_t* valid, hipStream_t s) {
   if (a.n_q / a.n_kv > 16) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(decode_attn_kernel<false>, dim3(a.n_kv, a.splits), dim3(512), 0, s, a, valid);
+  SS_LAUNCH(decode_attn_kernel<false>, dim3(a.n_kv, a.splits), dim3(512), 0, s, a, valid);
   return hipGetLastError();
 }
 
 hipError_t launch_rows_attention(const AttnArgs& a, hipStream_t s) {
   if (a.n_q / a.n_kv > 16) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(decode_attn_kernel<true>, dim3(a.n_kv, a.splits, a.m), dim3(512), 0, s, a,
+  SS_LAUNCH(decode_attn_kernel<true>, dim3(a.n_kv, a.splits, a.m), dim3(512), 0, s, a,
                      (const int32_t*)nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(rows_merge_kernel, dim3(a.n_q, a.m), dim3(D), 0, s, a);
+  SS_LAUNCH(rows_merge_kernel, dim3(a.n_q, a.m), dim3(D), 0, s, a);
   return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@
 //    next step's loads are issued before the current step's MFMAs.
 #include "common.h"
 #include "internal.h"
+#include "profile.h"
 
 namespace {
 
@@ -191,10 +192,10 @@ template <int RT, int EPI>
 hipError_t launch_tt(const GemmArgs& a, const Plan& p, hipStream_t s) {
   const dim3 grid((unsigned)p.groups), block(kThreads);
   switch (p.tt) {
-    case 1: hipLaunchKernelGGL((gemm_kernel<RT, 1, EPI>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((gemm_kernel<RT, 2, EPI>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((gemm_kernel<RT, 3, EPI>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((gemm_kernel<RT, 4, EPI>), grid, block, 0, s, a); break;
+    case 1: SS_LAUNCH((gemm_kernel<RT, 1, EPI>), grid, block, 0, s, a); break;
+    case 2: SS_LAUNCH((gemm_kernel<RT, 2, EPI>), grid, block, 0, s, a); break;
+    case 3: SS_LAUNCH((gemm_kernel<RT, 3, EPI>), grid, block, 0, s, a); break;
+    case 4: SS_LAUNCH((gemm_kernel<RT, 4, EPI>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

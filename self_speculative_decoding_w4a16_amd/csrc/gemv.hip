@@ -24,6 +24,7 @@
 //    (max, argmax) partial for the sampler.
 #include "common.h"
 #include "internal.h"
+#include "profile.h"
 
 #include <stdlib.h>
 
@@ -512,7 +513,7 @@ hipError_t launch_one(const GemvArgs& a, hipStream_t s, int* blocks_out) {
   const int fit = occ.get(reinterpret_cast<const void*>(&gemv_kernel<R, W4, PRO, EPI>), lds);
   const int64_t blocks = gemv_blocks(n_groups, W4, PRO, fit);
   if (blocks_out) *blocks_out = (int)blocks;
-  hipLaunchKernelGGL((gemv_kernel<R, W4, PRO, EPI>), dim3((unsigned)blocks), dim3(kThreads), lds, s, a,
+  SS_LAUNCH((gemv_kernel<R, W4, PRO, EPI>), dim3((unsigned)blocks), dim3(kThreads), lds, s, a,
                      n_groups, 0x000F000Fu, 0x43004300u);
   return hipGetLastError();
 }

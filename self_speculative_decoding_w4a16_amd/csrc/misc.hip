@@ -4,6 +4,7 @@
 // K/V of rejected positions are dropped - here by moving kv_len only).
 #include "common.h"
 #include "internal.h"
+#include "profile.h"
 
 namespace {
 
@@ -88,13 +89,13 @@ __global__ void pos_guard_kernel(const int32_t* kv_len, const int32_t* token_in,
 
 hipError_t launch_rmsnorm_rows(const uint16_t* h, const uint16_t* g, float eps, int rows, int k,
                                uint16_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(rows), dim3(256), 0, s, h, g, eps, k, out);
+  SS_LAUNCH(rmsnorm_rows_kernel, dim3(rows), dim3(256), 0, s, h, g, eps, k, out);
   return hipGetLastError();
 }
 
 hipError_t launch_embed_rows(const uint16_t* embed, const int32_t* tokens, int rows, int k,
                              int vocab, uint16_t* h, hipStream_t s) {
-  hipLaunchKernelGGL(embed_rows_kernel, dim3(rows), dim3(256), 0, s, embed, tokens, k, vocab, h);
+  SS_LAUNCH(embed_rows_kernel, dim3(rows), dim3(256), 0, s, embed, tokens, k, vocab, h);
   return hipGetLastError();
 }
 
@@ -103,25 +104,25 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
   if (n16 == 0) return hipSuccess;
   size_t blocks = (n16 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (u32x4*)p, n16);
+  SS_LAUNCH(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (u32x4*)p, n16);
   return hipGetLastError();
 }
 
 hipError_t launch_kv_rollback(int32_t* kv_len, int32_t* tokens, const int32_t* n_accepted,
                               const int32_t* out_tokens, hipStream_t s) {
-  hipLaunchKernelGGL(kv_rollback_kernel, dim3(1), dim3(1), 0, s, kv_len, tokens, n_accepted,
+  SS_LAUNCH(kv_rollback_kernel, dim3(1), dim3(1), 0, s, kv_len, tokens, n_accepted,
                      out_tokens);
   return hipGetLastError();
 }
 
 hipError_t launch_kv_advance(int32_t* kv_len, int32_t delta, hipStream_t s) {
-  hipLaunchKernelGGL(kv_advance_kernel, dim3(1), dim3(1), 0, s, kv_len, delta);
+  SS_LAUNCH(kv_advance_kernel, dim3(1), dim3(1), 0, s, kv_len, delta);
   return hipGetLastError();
 }
 
 hipError_t launch_pos_guard(const int32_t* kv_len, const int32_t* token_in, int step, int cap,
                             int vocab, int32_t* valid, int32_t* token_out, hipStream_t s) {
-  hipLaunchKernelGGL(pos_guard_kernel, dim3(1), dim3(1), 0, s, kv_len, token_in, step, cap, vocab,
+  SS_LAUNCH(pos_guard_kernel, dim3(1), dim3(1), 0, s, kv_len, token_in, step, cap, vocab,
                      valid, token_out);
   return hipGetLastError();
 }

@@ -9,6 +9,7 @@
 // float32 operation (no contraction), so codes are reproducible bit for bit.
 #include "common.h"
 #include "internal.h"
+#include "profile.h"
 
 #pragma clang fp contract(off)
 
@@ -74,7 +75,7 @@ hipError_t launch_w4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* 
                               uint16_t* meta, hipStream_t s) {
   const int64_t total = n * (k / 64);
   const int64_t blocks = (total + 255) / 256;
-  hipLaunchKernelGGL(w4_quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, n, k, codes,
+  SS_LAUNCH(w4_quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, n, k, codes,
                      meta);
   return hipGetLastError();
 }

@@ -19,6 +19,7 @@
 // part over one chunk.
 #include "common.h"
 #include "internal.h"
+#include "profile.h"
 
 namespace {
 
@@ -427,14 +428,14 @@ int sample_chunks(int vocab) {
 
 hipError_t launch_rowmax(const uint16_t* logits, int vocab, float* part_max, int32_t* part_arg,
                          int n_chunks, hipStream_t s) {
-  hipLaunchKernelGGL(rowmax_kernel, dim3(n_chunks), dim3(kT), 0, s, logits, vocab, part_max, part_arg);
+  SS_LAUNCH(rowmax_kernel, dim3(n_chunks), dim3(kT), 0, s, logits, vocab, part_max, part_arg);
   return hipGetLastError();
 }
 
 hipError_t launch_sample(const uint16_t* logits, int vocab, float temp, const uint32_t* u_code,
                          const float* pre_max, const int32_t* pre_arg, int n_pre, int32_t* token,
                          const int32_t* valid, const SampleWs& ws, hipStream_t s) {
-  hipLaunchKernelGGL(sample_kernel, dim3(sample_chunks(vocab)), dim3(kT), 0, s, logits, vocab, temp,
+  SS_LAUNCH(sample_kernel, dim3(sample_chunks(vocab)), dim3(kT), 0, s, logits, vocab, temp,
                      u_code, pre_max, pre_arg, n_pre, token, valid, ws);
   return hipGetLastError();
 }
@@ -451,17 +452,17 @@ hipError_t launch_reject(int gamma, int vocab, float temp, float draft_temp, con
                          const uint32_t* u_code, int32_t* n_out, int32_t* out_tokens,
                          int32_t* status, float* probs, const RejectWs& ws, hipStream_t s) {
   const int C = reject_chunks(vocab), rows = 2 * gamma + 1;
-  hipLaunchKernelGGL(rej_rowmax_kernel, dim3(C, rows), dim3(kT), 0, s, zt, zd, gamma, vocab, ws);
+  SS_LAUNCH(rej_rowmax_kernel, dim3(C, rows), dim3(kT), 0, s, zt, zd, gamma, vocab, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (temp != 0.0f || draft_temp != 0.0f) {
-    hipLaunchKernelGGL(rej_rowsum_kernel, dim3(C, rows), dim3(kT), 0, s, zt, zd, gamma, vocab, temp,
+    SS_LAUNCH(rej_rowsum_kernel, dim3(C, rows), dim3(kT), 0, s, zt, zd, gamma, vocab, temp,
                        draft_temp, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int blocks = temp == 0.0f ? 1 : C;
-  hipLaunchKernelGGL(rej_decide_kernel, dim3(blocks), dim3(kT), 0, s, zt, zd, gamma, vocab, temp,
+  SS_LAUNCH(rej_decide_kernel, dim3(blocks), dim3(kT), 0, s, zt, zd, gamma, vocab, temp,
                      draft_temp, toks, r_codes, u_code, n_out, out_tokens, status, probs, ws);
   return hipGetLastError();
 }

@@ -29,8 +29,9 @@ def describe(name):
         rt, tt, epi = int(m[1]), int(m[2]), int(m[3])
         return (f"gemm_kernel<{rt},{tt},{epi}>",
                 f"MFMA GEMM, {16 * rt} rows x <= {16 * tt} positions, {_GEPI[epi]}")
-    short = re.sub(r"\(.*$", "", name)
-    short = re.sub(r"^void ", "", short).replace("(anonymous namespace)::", "")
+    short = name.replace("(anonymous namespace)::", "")
+    short = re.sub(r"\(.*$", "", short)
+    short = re.sub(r"^void ", "", short)
     return short[:60], ""
 
 

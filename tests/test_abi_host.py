@@ -62,6 +62,26 @@ def test_gemv_gemm_sample_argument_errors():
     assert l.subspec_sample(p, 100, 1.0, p, p, p, 16, None) == _lib.EWORKSPACE
 
 
+def test_fused_gemv_argument_errors():
+    import ctypes
+    l = _lib.lib()
+    p = V(4096)
+    bf = _lib.Linear(p, None, None, 8, 128)
+    both = _lib.Linear(p, p, p, 8, 128)
+    odd = _lib.Linear(p, None, None, 7, 128)
+    wide = _lib.Linear(p, None, None, 8, 8192)
+    g = lambda lin, *a: l.subspec_gemv(ctypes.byref(lin), *a)
+    assert g(both, p, None, 0.0, 0, None, p, None) == _lib.EINVAL
+    assert g(bf, p, None, 0.0, 3, None, p, None) == _lib.EINVAL
+    assert g(bf, p, None, 0.0, 1, None, p, None) == _lib.EINVAL       # resid missing
+    assert g(odd, p, p, 1e-6, 2, None, p, None) == _lib.ESHAPE        # odd gate/up rows
+    assert g(_lib.Linear(p, None, None, 8, 96), p, None, 0.0, 0, None, p, None) == _lib.ESHAPE
+    assert g(wide, p, p, 1e-6, 0, None, p, None) == _lib.EUNSUPPORTED  # norm above 6144
+    assert g(bf, p, None, 0.0, 2, None, p, None) == _lib.EUNSUPPORTED  # SiLU needs the norm
+    assert g(bf, None, p, 1e-6, 0, None, p, None) == _lib.EINVAL
+    assert l.subspec_gemv(None, p, p, 1e-6, 0, None, p, None) == _lib.EINVAL
+
+
 def test_reject_argument_errors():
     l = _lib.lib()
     p = V(4096)

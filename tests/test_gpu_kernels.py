@@ -3,7 +3,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle.model import linear
+from oracle.model import linear, rmsnorm, silu
+from oracle.bf16 import round_bf16
 from oracle.quant import quantize as oq, dequantize
 from oracle.sampling import sample as osample
 from oracle.reject import reject as oreject, acceptance_probabilities
@@ -102,6 +103,70 @@ def test_bf16_gemv(cuda, n, k, seed):
     torch.cuda.synchronize()
     rows = np.arange(n) if n <= 4096 else np.unique(np.r_[0, n - 1, np.random.default_rng(2).integers(0, n, 512)])
     ref = linear(host(x)[None, :], host(w[rows]))[0]
+    assert rel_err(host(y)[rows], ref) < TOL
+
+
+def _fused_ref(wd, x, g, eps, epilogue, resid):
+    """Oracle of the fused draft GEMV: RMSNorm prologue, then store / residual
+    add / SiLU(gate)*up, composed from the oracle's forward-pass steps."""
+    xn = rmsnorm(x[None, :], g, eps) if g is not None else x[None, :]
+    y = linear(xn, wd)[0]
+    if epilogue == 1:
+        return round_bf16(resid + y)
+    if epilogue == 2:
+        F = wd.shape[0] // 2
+        return round_bf16(silu(y[:F]) * y[F:])
+    return y
+
+
+@pytest.mark.parametrize("w4", [True, False])
+@pytest.mark.parametrize("n,k,norm,epilogue", [(1000, 640, True, 0), (1000, 640, True, 2),
+                                               (1000, 640, False, 1), (4608, 3584, True, 0),
+                                               (3584, 18944, False, 1), (778, 6144, True, 2),
+                                               (130, 64, True, 2)])
+def test_fused_gemv(cuda, w4, n, k, norm, epilogue):
+    log(f"fused gemv w4={w4} {n}x{k} norm={norm} epilogue={epilogue}")
+    w = normal_tensor((n, k), 0.02, 30, cuda)
+    x = normal_tensor((k,), 1.0, 31, cuda)
+    g = normal_tensor((k,), 1.0, 32, cuda) if norm else None
+    resid = normal_tensor((n,), 1.0, 33, cuda) if epilogue == 1 else None
+    if w4:
+        codes, meta = _quant_gpu(w)
+        lin = _lib.linear(codes=codes, meta=meta)
+        rc, rm = oq(host(w))
+        wd = dequantize(rc, rm)
+    else:
+        lin = _lib.linear(w=w)
+        wd = host(w)
+    y = torch.empty(n // 2 if epilogue == 2 else n, dtype=torch.bfloat16, device=cuda)
+    _lib.gemv(lin, x, y, norm_w=g, eps=1e-6, epilogue=epilogue, resid=resid)
+    torch.cuda.synchronize()
+    ref = _fused_ref(wd, host(x), None if g is None else host(g), 1e-6, epilogue,
+                     None if resid is None else host(resid))
+    assert rel_err(host(y), ref) < TOL
+
+
+@pytest.mark.parametrize("w4", [True, False])
+def test_fused_gemv_gate_up_full_shape_sampled_rows(cuda, w4):
+    F, k = 18944, 3584
+    log(f"fused gate_up full w4={w4}")
+    w = normal_tensor((2 * F, k), 0.02, 40, cuda)
+    x = normal_tensor((k,), 1.0, 41, cuda)
+    g = normal_tensor((k,), 1.0, 42, cuda)
+    if w4:
+        codes, meta = _quant_gpu(w)
+        lin = _lib.linear(codes=codes, meta=meta)
+    else:
+        lin = _lib.linear(w=w)
+    y = torch.empty(F, dtype=torch.bfloat16, device=cuda)
+    _lib.gemv(lin, x, y, norm_w=g, eps=1e-6, epilogue=2)
+    torch.cuda.synchronize()
+    rows = np.unique(np.r_[0, F - 1, np.random.default_rng(3).integers(0, F, 256)])
+    wr = host(w[np.r_[rows, F + rows]])
+    if w4:
+        rc, rm = oq(wr)
+        wr = dequantize(rc, rm)
+    ref = _fused_ref(wr, host(x), host(g), 1e-6, 2, None)
     assert rel_err(host(y)[rows], ref) < TOL
 
 
