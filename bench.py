@@ -24,6 +24,33 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 
+# HBM traffic per launch of a draft GEMV site, from two rocprofv3 --pmc runs of
+# `bench.py --site NAME` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each
+# scaled by what the same counter reads for a 1 GiB device-to-device copy in
+# the same run (FETCH_SIZE 524328 KiB -> x2.0, WRITE_SIZE 1048576 KiB -> x1.0).
+# Reported only while the kernel sources hash to the value they were taken on.
+TRAFFIC = {
+    "bf16_gate_up": {"fetch_kib": 132919.1, "write_kib": 74.2, "fetch_scale": 2.0,
+                     "write_scale": 1.0, "sources": "0a392b584608bf80"},
+}
+GEMV_SOURCES = ("csrc/gemv.hip", "csrc/common.h", "csrc/internal.h")
+
+
+def sources_hash(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "self_speculative_decoding_w4a16_amd", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_bytes(site):
+    t = TRAFFIC.get(site)
+    if not t or t["sources"] != sources_hash(GEMV_SOURCES):
+        return None
+    return round(1024 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]))
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -33,6 +60,9 @@ def parse():
     ap.add_argument("--config", default="full7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ar", action="store_true")
+    ap.add_argument("--site", default=None,
+                    help="only launch one draft GEMV site (e.g. bf16_gate_up) back to back, then "
+                         "copy 1 GiB device to device: the workload for HBM counter runs")
     return ap.parse_args()
 
 
@@ -63,6 +93,14 @@ def main():
     w = model_weights(shape, 0, dev)
     dm = DeviceModel(shape, w)
     torch.cuda.synchronize()
+    if args.site:
+        iso = isolated_gemvs(dm, shape, dev, reps=1, only=args.site, graph=False)
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"site": args.site, **iso[args.site], "copy_bytes": 1 << 30}), flush=True)
+        return
     gamma, G = wl.gamma, wl.generate
     cap = ((wl.prompt + G + gamma + 1 + 63) // 64) * 64 + 64
     dec = SpecDecoder(dm, cap, gamma, wl.temp, wl.draft_temp)
@@ -192,8 +230,8 @@ def main():
         out = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": label}
         if len(names) == 1:
-            out.update(avg_us=iso[names[0]]["avg_us"], bytes_per_launch=iso[names[0]]["bytes_per_launch"],
-                       symbol=iso[names[0]]["symbol"])
+            out.update(traffic=traffic_bytes(names[0]), avg_us=iso[names[0]]["avg_us"],
+                       bytes_per_launch=iso[names[0]]["bytes_per_launch"], symbol=iso[names[0]]["symbol"])
         return out
 
     # ---------------------------------------------------------------- plain AR
@@ -260,7 +298,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def isolated_gemvs(dm, shape, dev, reps=3):
+def isolated_gemvs(dm, shape, dev, reps=3, only=None, graph=True):
     """The draft step's GEMV kernels launched back to back through the fused
     GEMV entry point, timed with one pair of HIP events on the launch stream:
     the average duration of one kernel at one shape.  Each launch reads a
@@ -302,22 +340,30 @@ def isolated_gemvs(dm, shape, dev, reps=3):
         for lin in lins:
             run(lin)
         torch.cuda.synchronize()
-        # captured in a HIP graph, so that the launches reach the GPU faster
-        # than the kernels run (host launch cost would otherwise bound the
-        # small ones)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if not graph:
+            e0.record()
             for _ in range(reps):
                 for lin in lins:
                     run(lin)
-        graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return 1000.0 * e0.elapsed_time(e1) / (reps * len(lins))
+        # captured in a HIP graph, so that the launches reach the GPU faster
+        # than the kernels run (host launch cost would otherwise bound the
+        # small ones)
+        cg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cg):
+            for _ in range(reps):
+                for lin in lins:
+                    run(lin)
+        cg.replay()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        graph.replay()
+        cg.replay()
         e1.record()
         torch.cuda.synchronize()
-        del graph
+        del cg
         return 1000.0 * e0.elapsed_time(e1) / (reps * len(lins))
 
     out = {}
@@ -325,6 +371,8 @@ def isolated_gemvs(dm, shape, dev, reps=3):
         if not layers:
             continue
         for site, (name, k, n_out, norm, epi, sym) in spec.items():
+            if only and only != f"{kind}_{site}":
+                continue
             w4 = kind == "w4"
             mats = [dm.q[l][name] if w4 else (dm.w["layers"][l][name],) for l in layers]
             wb = n_out * (2 if epi == 2 else 1) * k * (0.5 + 4 / 64 if w4 else 2.0)
@@ -339,6 +387,8 @@ def isolated_gemvs(dm, shape, dev, reps=3):
             out[f"{kind}_{site}"] = {"avg_us": round(us, 3), "bytes_per_launch": round(by),
                                      "gbs": round(by / (us * 1e-6) / 1e9, 1), "per_step": len(layers),
                                      "symbol": sym.format(r=r, w="true" if w4 else "false")}
+    if only and only != "lm_head":
+        return out
     lm = _lib.linear(w=dm.w["lm_head"])
     by = 2.0 * shape.vocab * H + 2 * H + 2 * shape.vocab
     us = timed([lm], H, shape.vocab, True, 0)
