@@ -24,7 +24,7 @@ Sources (cited by page title and section):
   [SSL]  "The second ledger of speculative decoding" (SparseSpec-L blog),
          sections 1, 2, 3.1-3.3.
 
-Parity status of each part is listed in the module docstrings.  Parts with
-no pin: none in this module set; the sparse-KV index (sparse.py) is pinned
-only by its special cases (full budget == dense, brute-force top-K).
+Parity status of each part is listed in the module docstrings.  Every part
+has pins; the sparse-KV draft (sparse.py) is pinned by properties, special
+cases and brute force only, since the pages print no worked example of it.
 """

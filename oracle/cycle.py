@@ -22,6 +22,7 @@ import numpy as np
 from .model import forward, new_kv
 from .reject import reject
 from .sampling import sample
+from .sparse import build_index
 
 
 def prefill(model, kv, prompt):
@@ -31,11 +32,13 @@ def prefill(model, kv, prompt):
     return len(prompt) - 1
 
 
-def draft_tokens(model, kv, kv_len, last_token, gamma, draft_temp, U_draft):
+def draft_tokens(model, kv, kv_len, last_token, gamma, draft_temp, U_draft, index=None):
+    """gamma draft steps; with ``index`` the draft attends sparsely (sparse.py)."""
     toks = [int(last_token)]
     logits = []
+    sparse = None if index is None else (index, kv_len)
     for i in range(gamma):
-        z = forward(model, kv, kv_len + i, [toks[i]], draft=True)[0]
+        z = forward(model, kv, kv_len + i, [toks[i]], draft=True, sparse=sparse)[0]
         logits.append(z)
         toks.append(sample(z.astype(np.float32), draft_temp, U_draft[i]))
     return toks, np.array(logits)
@@ -46,6 +49,21 @@ def speculative_cycle(model, kv, kv_len, last_token, gamma, temp, draft_temp, U_
     tlogits = forward(model, kv, kv_len, toks, draft=False)
     n, out, status = reject(tlogits, dlogits, toks[1:], R, U_final, temp, draft_temp)
     return n, out, status, toks, dlogits, tlogits
+
+
+def sparse_speculative_cycle(model, kv, kv_len, last_token, gamma, temp, draft_temp, U_draft, R,
+                             U_final, index, n_sink, n_recent, window, budget_permille):
+    """One cycle with a sparse-KV draft ([SSL] sections 3.1-3.2): the draft
+    attends to ``index`` (None: dense, the first cycle), the verify pass
+    yields the importance scores of its last ``window`` rows, and the index
+    of the next cycle is rebuilt over the committed positions
+    [0, kv_len + n + 1)."""
+    toks, dlogits = draft_tokens(model, kv, kv_len, last_token, gamma, draft_temp, U_draft, index)
+    scores = []
+    tlogits = forward(model, kv, kv_len, toks, draft=False, scores=scores, score_window=window)
+    n, out, status = reject(tlogits, dlogits, toks[1:], R, U_final, temp, draft_temp)
+    new_index = build_index(scores, kv_len + n + 1, n_sink, n_recent, budget_permille)
+    return n, out, status, toks, dlogits, tlogits, scores, new_index
 
 
 def speculative_generate(model, prompt, n_generate, gamma, temp, draft_temp, uniforms, capacity):

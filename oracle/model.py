@@ -103,12 +103,19 @@ def attend(q, K, V, n_keys):
     return p @ V[:n_keys]
 
 
-def forward(model, kv, kv_len, tokens, draft=False, keep_logits=True):
+def forward(model, kv, kv_len, tokens, draft=False, keep_logits=True, sparse=None, scores=None,
+            score_window=16):
     """Run tokens[j] at position kv_len + j, j = 0..n-1, through the decoder.
 
     Writes the K/V of those positions into ``kv`` and returns the logits
     [n][V] (bf16 values as float64).  Row j attends to positions
     [0, kv_len + j].  ``draft`` selects the substitute weights.
+
+    ``sparse = (index, base)``: row j of layer l, query head h attends only
+    to the positions index[l][h // group] (ascending, all < base) and the
+    speculative positions [base, kv_len + j] (sparse.py).
+    ``scores``: a list that receives, per layer, the importance scores
+    [n_kv_heads][kv_len + n] of this pass (sparse.py, importance_scores).
     """
     K, V = kv
     n = len(tokens)
@@ -127,12 +134,25 @@ def forward(model, kv, kv_len, tokens, draft=False, keep_logits=True):
                 v = qkv[j, (Hq + Hkv + hk) * d:(Hq + Hkv + hk + 1) * d]
                 K[l, hk, pos] = round_bf16(rope(k, pos, model.rope_theta))
                 V[l, hk, pos] = v
+        if scores is not None:
+            from .sparse import attention_probs
+            sc = np.zeros((Hkv, kv_len + n))
         for j in range(n):
             pos = kv_len + j
             for hq in range(Hq):
                 q = round_bf16(rope(qkv[j, hq * d:(hq + 1) * d], pos, model.rope_theta))
                 hk = hq // group
-                attn[j, hq * d:(hq + 1) * d] = attend(q, K[l, hk], V[l, hk], pos + 1)
+                if sparse is None:
+                    attn[j, hq * d:(hq + 1) * d] = attend(q, K[l, hk], V[l, hk], pos + 1)
+                else:
+                    index, base = sparse
+                    keys = np.concatenate([np.asarray(index[l][hk], dtype=np.int64),
+                                           np.arange(base, pos + 1)])
+                    attn[j, hq * d:(hq + 1) * d] = attend(q, K[l, hk][keys], V[l, hk][keys], len(keys))
+                if scores is not None and j >= n - score_window:
+                    sc[hk, :pos + 1] += attention_probs(q, K[l, hk], pos + 1)
+        if scores is not None:
+            scores.append(sc)
         attn = round_bf16(attn)
         h = round_bf16(h + attn @ model.weight(l, "o", draft).T)
         x = rmsnorm(h, lw["ffn_norm"], model.rms_eps)
