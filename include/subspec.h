@@ -13,6 +13,11 @@
  *   [SSR] "SubSpec: the target's own low-bit shadow as the draft" (report),
  *         section 2.2 (4-bit substitutes, sharpened draft), section 3.2
  *         (greedy verification, Table 1).
+ *   [SSL] "The second ledger of speculative decoding" (SparseSpec-L blog),
+ *         section 3.1 (the draft reads a ~10% index of sink, recent and
+ *         important positions, gathered from the dense cache) and section
+ *         3.2 (importance = attention of the last W = 16 query positions of
+ *         the verify pass; the index is rebuilt after every verify).
  *
  * Conventions shared by every entry point
  *   - All buffer pointers are DEVICE pointers unless stated otherwise; the
@@ -116,7 +121,26 @@ typedef struct {
  *   tokens            device int32 [gamma_max + 1]: [0] last committed token,
  *                     [1..gamma] the draft tokens of the current cycle
  *   draft_logits      device bf16 [gamma_max][vocab]: row i = logits the
- *                     draft produced at step i (the distribution of tokens[i+1]) */
+ *                     draft produced at step i (the distribution of tokens[i+1])
+ * Sparse-KV drafting ([SSL] sections 3.1-3.2; leave kv_score and kv_index
+ * NULL for dense drafting):
+ *   kv_score          device fp32 [n_layers][Hkv][capacity]: written by every
+ *                     verify call: score[l][hk][j] = sum over the call's last
+ *                     min(score_window, n_tokens) rows r and the query heads
+ *                     h of KV head hk of the attention probability row r,
+ *                     head h gave position j (0 where j is past row r)
+ *   kv_index          device int32 [n_layers][Hkv][index_cap]: ascending
+ *                     positions, written by subspec_kv_select
+ *   kv_index_len      device int32 scalar: entries of every list
+ *   index_cap         capacity of each list; must be >= the count for
+ *                     kv_len = capacity (see subspec_kv_select)
+ *   use_index         host flag: nonzero -> draft_step attends, per layer and
+ *                     KV head, to the index plus the speculative positions
+ *                     [kv_len, kv_len + step]; zero -> dense (first cycle)
+ *   n_sink, n_recent  positions always kept at the start and the end
+ *   score_window      verify rows that feed the scores, 1..16
+ *   budget_permille   index size ceil(budget_permille * kv_len / 1000), in
+ *                     thousandths so that the count is exact integer math */
 typedef struct {
   uint16_t *k_cache, *v_cache;
   int32_t capacity;
@@ -124,6 +148,12 @@ typedef struct {
   int32_t *tokens;
   uint16_t *draft_logits;
   int32_t gamma_max;
+  float *kv_score;
+  int32_t *kv_index;
+  int32_t *kv_index_len;
+  int32_t index_cap;
+  int32_t use_index;
+  int32_t n_sink, n_recent, score_window, budget_permille;
 } subspec_state;
 
 /* Bytes of workspace needed for calls on `m` with at most `max_tokens`
@@ -200,6 +230,18 @@ int subspec_reject(int32_t gamma, int32_t vocab, float temp, float draft_temp,
 int subspec_kv_rollback(const subspec_state *st, const int32_t *n_accepted,
                         const int32_t *out_tokens, void *stream);
 
+/* Rebuild the sparse draft index ([SSL] sections 3.1-3.2) from the scores
+ * of the last verify, after the rollback, over the committed positions
+ * [0, L), L = kv_len (device).  For every layer and KV head the list is
+ * sink = [0, min(n_sink, L)), recent = [max(sink end, L - n_recent), L), and
+ * the K middle positions of highest score (score descending, position
+ * ascending on ties), K = ceil(budget_permille * L / 1000) - |sink| -
+ * |recent| clipped to [0, middle size]; i.e. min(L, max(ceil(budget * L),
+ * |sink| + |recent|)) entries, ascending, count in kv_index_len.  Needs
+ * kv_score, kv_index, kv_index_len set and index_cap >= that count at
+ * L = capacity (SUBSPEC_ECAPACITY otherwise). */
+int subspec_kv_select(const subspec_model *m, const subspec_state *st, void *stream);
+
 /* kv_len += delta (device), e.g. after a prefill chunk run through verify. */
 int subspec_kv_advance(const subspec_state *st, int32_t delta, void *stream);
 
@@ -266,7 +308,9 @@ enum {
   SUBSPEC_K_SAMPLE = 16,       /* draft token draw                                 */
   SUBSPEC_K_REJECT = 17,       /* rejection round                                  */
   SUBSPEC_K_MISC = 18,         /* norms, embedding, KV bookkeeping                 */
-  SUBSPEC_K_CLASSES = 19
+  SUBSPEC_K_SCORES = 19,       /* verify importance scores (sparse drafting)       */
+  SUBSPEC_K_SELECT = 20,       /* sparse index rebuild                             */
+  SUBSPEC_K_CLASSES = 21
 };
 
 /* Start recording: from now on every kernel this library launches, on any

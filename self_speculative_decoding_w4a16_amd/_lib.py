@@ -52,7 +52,11 @@ class Model(ctypes.Structure):
 class State(ctypes.Structure):
     _fields_ = [("k_cache", c_void_p), ("v_cache", c_void_p), ("capacity", c_int32),
                 ("kv_len", c_void_p), ("tokens", c_void_p), ("draft_logits", c_void_p),
-                ("gamma_max", c_int32)]
+                ("gamma_max", c_int32),
+                ("kv_score", c_void_p), ("kv_index", c_void_p), ("kv_index_len", c_void_p),
+                ("index_cap", c_int32), ("use_index", c_int32),
+                ("n_sink", c_int32), ("n_recent", c_int32), ("score_window", c_int32),
+                ("budget_permille", c_int32)]
 
 
 _SIGS = {
@@ -71,6 +75,7 @@ _SIGS = {
                                  c_void_p, c_size_t, c_void_p]),
     "subspec_kv_rollback": (c_int32, [POINTER(State), c_void_p, c_void_p, c_void_p]),
     "subspec_kv_advance": (c_int32, [POINTER(State), c_int32, c_void_p]),
+    "subspec_kv_select": (c_int32, [POINTER(Model), POINTER(State), c_void_p]),
     "subspec_w4_gemv": (c_int32, [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p,
                                   c_void_p]),
     "subspec_bf16_gemv": (c_int32, [c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
@@ -90,7 +95,7 @@ _SIGS = {
 K_NAMES = ("w4_qkv", "w4_o", "w4_gate_up", "w4_down",
            "bf16_qkv", "bf16_o", "bf16_gate_up", "bf16_down", "lm_head",
            "gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "gemm_lm_head",
-           "attn_draft", "attn_verify", "sample", "reject", "misc")
+           "attn_draft", "attn_verify", "sample", "reject", "misc", "scores", "select")
 K = {name: i for i, name in enumerate(K_NAMES)}
 # Groups of classes: every draft GEMV on a 4-bit substitute, every draft GEMV
 # on bf16 weights, and every verify GEMM.
@@ -182,6 +187,18 @@ def reject(gamma, vocab, temp, draft_temp, target_logits, draft_logits, draft_to
 def kv_rollback(state, n_accepted, out_tokens, stream=None):
     check(lib().subspec_kv_rollback(ctypes.byref(state), _p(n_accepted), _p(out_tokens),
                                     _stream(stream)))
+
+
+def kv_select(model, state, stream=None):
+    check(lib().subspec_kv_select(ctypes.byref(model), ctypes.byref(state), _stream(stream)))
+
+
+def index_count(L, n_sink, n_recent, budget_permille):
+    """Entries of every sparse index list at kv_len = L (as subspec_kv_select)."""
+    s = min(n_sink, L)
+    rec = min(n_recent, L - s)
+    total = (budget_permille * L + 999) // 1000
+    return min(L, max(total, s + rec))
 
 
 def kv_advance(state, delta, stream=None):

@@ -121,12 +121,35 @@ int check_model(const subspec_model* m) {
   return SUBSPEC_OK;
 }
 
+// Entries of every sparse index list at kv_len = L: min(L, max(ceil(budget
+// * L), |sink| + |recent|)), non-decreasing in L.
+int64_t index_count(int64_t L, const subspec_state* st) {
+  const int64_t sk = std::min<int64_t>(st->n_sink, L);
+  const int64_t rec = std::min<int64_t>(st->n_recent, L - sk);
+  const int64_t total = ((int64_t)st->budget_permille * L + 999) / 1000;
+  return std::min<int64_t>(L, std::max<int64_t>(total, sk + rec));
+}
+
 int check_state(const subspec_model* m, const subspec_state* st) {
   if (!st) return fail(SUBSPEC_EINVAL, "state is NULL");
   if (!st->k_cache || !st->v_cache || !st->kv_len || !st->tokens)
     return fail(SUBSPEC_EINVAL, "state buffers k_cache, v_cache, kv_len, tokens must be set");
   if (st->capacity < 1) return fail(SUBSPEC_ECAPACITY, "capacity must be >= 1");
-  (void)m;
+  if (st->kv_score || st->kv_index || st->use_index) {
+    if (!st->kv_score || !st->kv_index || !st->kv_index_len)
+      return fail(SUBSPEC_EINVAL, "sparse drafting needs kv_score, kv_index and kv_index_len");
+    if (st->n_sink < 0 || st->n_recent < 0) return fail(SUBSPEC_EINVAL, "n_sink and n_recent must be >= 0");
+    if (st->score_window < 1 || st->score_window > 16)
+      return fail(SUBSPEC_EINVAL, "score_window must be in [1, 16]");
+    if (st->budget_permille < 0 || st->budget_permille > 1000)
+      return fail(SUBSPEC_EINVAL, "budget_permille must be in [0, 1000]");
+    if (st->score_window * (m->n_q_heads / m->n_kv_heads) > attn_scores_max_pairs())
+      return fail(SUBSPEC_EUNSUPPORTED, "score_window x GQA group above %d", attn_scores_max_pairs());
+    const int64_t need = index_count(st->capacity, st);
+    if (st->index_cap < need)
+      return fail(SUBSPEC_ECAPACITY, "index_cap %d below the %lld entries of kv_len = capacity",
+                  st->index_cap, (long long)need);
+  }
   return SUBSPEC_OK;
 }
 
@@ -137,6 +160,7 @@ struct FwdWs {
   uint32_t* attn_counters;
   uint16_t *h, *xn, *qkv, *qrot, *attn, *act;
   float* attn_part;
+  float* attn_ml;
   float* gemm_part;
   float* logit_max;
   int32_t* logit_arg;
@@ -176,6 +200,7 @@ size_t carve_fwd(const subspec_model* m, int mt, int cap, void* ws, FwdWs* o) {
   const size_t dsplits = (cap + decode_attn_keys_per_split() - 1) / decode_attn_keys_per_split();
   const size_t part_floats = (size_t)m->n_q_heads * dsplits * mt * (m->head_dim + 4);
   w.attn_part = (float*)c.take(part_floats * 4);
+  w.attn_ml = (float*)c.take((size_t)mt * m->n_q_heads * 2 * 4);
   w.gemm_part = (float*)c.take(max_gemm_partials(m, mt));
   const int lm_blocks = gemv_max_blocks(false, m->vocab, EPI_LOGITS);
   w.logit_max = (float*)c.take((size_t)lm_blocks * 4);
@@ -291,6 +316,7 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
   const int64_t qd = (int64_t)m->n_q_heads * d;
   const int64_t qkv = (int64_t)(m->n_q_heads + 2 * m->n_kv_heads) * d;
   int32_t* tok_out = st->tokens + step + 1;
+  const bool sparse = st->use_index != 0;
   {
     prof::Scope ps(SUBSPEC_K_MISC, 0.0, s);
     HIPCHK(launch_pos_guard(st->kv_len, st->tokens + step, step, st->capacity, m->vocab, w.valid, tok_out, s));
@@ -329,7 +355,15 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
     at.theta = m->rope_theta;
     at.part = w.attn_part;
     at.out = w.attn;
-    at.splits = (st->capacity + decode_attn_keys_per_split() - 1) / decode_attn_keys_per_split();
+    const int kpb = decode_attn_keys_per_split();
+    at.splits = (st->capacity + kpb - 1) / kpb;
+    if (sparse) {
+      at.index = st->kv_index + (int64_t)l * m->n_kv_heads * st->index_cap;
+      at.n_index = st->kv_index_len;
+      at.index_cap = st->index_cap;
+      // slots: n_index + step + 1 <= min(index_cap + gamma_max, capacity)
+      at.splits = std::min(at.splits, (st->index_cap + st->gamma_max + kpb - 1) / kpb);
+    }
     {
       prof::Scope ps(SUBSPEC_K_ATTN_DRAFT, 0.0, s);
       HIPCHK(launch_decode_attention(at, w.valid, s));
@@ -349,6 +383,10 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
     o.attn_g = m->n_q_heads / m->n_kv_heads;
     o.kv_len = st->kv_len;
     o.pos_offset = step;
+    if (sparse) {
+      o.attn_nidx = st->kv_index_len;
+      o.attn_index_cap = st->index_cap;
+    }
     {
       prof::Scope ps(gemv_class(L.o_d, 1), gemv_bytes(L.o_d, H, true), s);
       HIPCHK(launch_gemv(lin_is_w4(L.o_d), PRO_ATTN_MERGE, EPI_RESID, o, s, nullptr));
@@ -455,10 +493,16 @@ int subspec_verify(const subspec_model* m, const subspec_state* st, int32_t n_to
     at.part = w.attn_part;
     at.out = w.attn;
     at.splits = (st->capacity + decode_attn_keys_per_split() - 1) / decode_attn_keys_per_split();
+    if (st->kv_score) at.ml = w.attn_ml;
     {
       prof::Scope ps(SUBSPEC_K_ATTN_VERIFY, 0.0, s);
       HIPCHK(launch_rope_append(at, s));
       HIPCHK(launch_rows_attention(at, s));
+    }
+    if (st->kv_score) {
+      prof::Scope ps(SUBSPEC_K_SCORES, 0.0, s);
+      HIPCHK(launch_attn_scores(at, st->kv_score + (int64_t)l * m->n_kv_heads * st->capacity,
+                                st->score_window, s));
     }
     GemmArgs o{L.o.w, H, qd, w.attn, mt, w.h, H, w.h, w.gemm_part, w.gemm_counters};
     {
@@ -523,6 +567,18 @@ int subspec_kv_rollback(const subspec_state* st, const int32_t* n_accepted,
   if (!n_accepted || !out_tokens) return fail(SUBSPEC_EINVAL, "n_accepted and out_tokens must be set");
   prof::Scope ps(SUBSPEC_K_MISC, 0.0, hs(stream));
   HIPCHK(launch_kv_rollback(st->kv_len, st->tokens, n_accepted, out_tokens, hs(stream)));
+  return ok();
+}
+
+int subspec_kv_select(const subspec_model* m, const subspec_state* st, void* stream) {
+  int r;
+  if ((r = check_model(m)) || (r = check_state(m, st))) return r;
+  if (!st->kv_score || !st->kv_index || !st->kv_index_len)
+    return fail(SUBSPEC_EINVAL, "kv_score, kv_index and kv_index_len must be set");
+  prof::Scope ps(SUBSPEC_K_SELECT, 0.0, hs(stream));
+  HIPCHK(launch_kv_select(st->kv_score, st->capacity, st->kv_len, m->n_layers * m->n_kv_heads, st->n_sink,
+                          st->n_recent, st->budget_permille, st->kv_index, st->index_cap, st->kv_index_len,
+                          hs(stream)));
   return ok();
 }
 

@@ -88,21 +88,29 @@ __global__ __launch_bounds__(512) void decode_attn_kernel(AttnArgs a, const int3
   const int lane = tid & 63, wave = tid >> 6;
   const int G = a.n_q / a.n_kv;
   const int row = CACHED ? (int)blockIdx.z : 0;
-  const int pos = *a.kv_len + a.pos_offset + row;  // position of this query (its last key)
+  const int kv0 = *a.kv_len;
+  const int pos = kv0 + a.pos_offset + row;  // position of this query (its last key)
   if (pos < 0 || pos >= a.cap) return;
-  const int n_keys = pos + 1;
+  // key slot t -> cache position: dense t; sparse draft index[t] for t < n_idx,
+  // then the speculative positions kv_len + (t - n_idx)
+  const bool sparse = !CACHED && a.index != nullptr;
+  const int n_idx = sparse ? min(max(*a.n_index, 0), a.index_cap) : 0;
+  const int32_t* ilist = sparse ? a.index + (int64_t)hk * a.index_cap : nullptr;
+  const int n_keys = sparse ? n_idx + a.pos_offset + 1 : pos + 1;
   const int active = (n_keys + DKPB - 1) / DKPB;
   if (split >= active) return;
   const int k0 = split * DKPB;
   const int nk = min(DKPB, n_keys - k0);
-  const bool has_new = !CACHED && (k0 + nk - 1) == pos;
+  const bool has_new = !CACHED && (k0 + nk - 1) == n_keys - 1;
 
   // ---- loads: thread (key j, quarter c) takes 32 dims of K[j] and V[j]
   const int j = tid >> 2, c = tid & 3;
-  const bool kvalid = j < nk && (CACHED || (k0 + j) != pos);
+  const bool kvalid = j < nk && (CACHED || (k0 + j) != n_keys - 1);
   u32x4 kr[4], vr[4];
   {
-    const int64_t row = (int64_t)hk * a.cap + k0 + (kvalid ? j : 0);
+    int t = k0 + (kvalid ? j : 0);
+    if (sparse) t = t < n_idx ? min(max(ilist[t], 0), a.cap - 1) : kv0 + (t - n_idx);
+    const int64_t row = (int64_t)hk * a.cap + t;
     const u32x4* kp = reinterpret_cast<const u32x4*>(a.k_cache + row * D) + 4 * c;
     const u32x4* vp = reinterpret_cast<const u32x4*>(a.v_cache + row * D) + 4 * c;
 #pragma unroll
@@ -157,7 +165,7 @@ __global__ __launch_bounds__(512) void decode_attn_kernel(AttnArgs a, const int3
   __syncthreads();
   // ---- scores: 32-dim partial dots, reduced over the 4 quarters of a key
   float kf[32];
-  if (!CACHED && j < nk && (k0 + j) == pos) {
+  if (!CACHED && j < nk && (k0 + j) == n_keys - 1) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) kf[i] = kn[32 * c + i];
   } else {
@@ -274,6 +282,72 @@ __global__ __launch_bounds__(128) void rows_merge_kernel(AttnArgs a) {
     M = Mb;
   }
   a.out[((int64_t)row * a.n_q + hq) * D + dd] = ss::f2bf(o / L);
+  if (a.ml && dd == 0) {
+    a.ml[((int64_t)row * a.n_q + hq) * 2] = M;
+    a.ml[((int64_t)row * a.n_q + hq) * 2 + 1] = L;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Importance scores of one layer ("The second ledger of speculative decoding",
+// section 3.2): score[hk][j] = sum over the last W verify rows r and the
+// query heads h of KV head hk of the attention probability
+// exp(q_{r,h} . k_j / sqrt(d) - M_{r,h}) / L_{r,h} (0 past row r's causal
+// limit), with (M, L) the softmax statistics the merge wrote.  Grid (KV head,
+// block of SKB keys), one thread per key: the thread holds k_j (64 bf16
+// pairs) and dots it with the W x G queries staged in LDS as bf16 pairs.
+constexpr int SKB = 256;
+constexpr int SMAXP = 240;  // W x G pairs that fit the 64 KiB of LDS
+
+__global__ __launch_bounds__(SKB) void attn_scores_kernel(AttnArgs a, float* score, int window) {
+  extern __shared__ uint32_t qsm[];  // [P][D/2] query pairs, then [P][2] (M, L)
+  const int hk = blockIdx.x, tid = threadIdx.x;
+  const int kv0 = *a.kv_len;
+  const int n_keys = min(kv0 + a.m, a.cap);
+  const int j0 = blockIdx.y * SKB;
+  if (kv0 < 0 || j0 >= n_keys) return;  // block-uniform
+  const int G = a.n_q / a.n_kv;
+  const int W = min(window, a.m), r0 = a.m - W;
+  const int P = W * G;
+  float* mls = reinterpret_cast<float*>(qsm + P * (D / 2));
+  for (int e = tid; e < P * (D / 2); e += SKB) {
+    const int p = e / (D / 2), w = e % (D / 2);
+    const int r = r0 + p / G, h = p % G;
+    qsm[e] = reinterpret_cast<const uint32_t*>(a.q_rot + ((int64_t)r * a.n_q + hk * G + h) * D)[w];
+  }
+  for (int p = tid; p < P; p += SKB) {
+    const int r = r0 + p / G, h = p % G;
+    mls[2 * p] = a.ml[((int64_t)r * a.n_q + hk * G + h) * 2];
+    mls[2 * p + 1] = a.ml[((int64_t)r * a.n_q + hk * G + h) * 2 + 1];
+  }
+  __syncthreads();
+  const int j = j0 + tid;
+  if (j >= n_keys) return;
+  uint32_t kw[D / 2];
+  const u32x4* kp = reinterpret_cast<const u32x4*>(a.k_cache + ((int64_t)hk * a.cap + j) * D);
+#pragma unroll
+  for (int i = 0; i < D / 8; ++i) {
+    const u32x4 v = kp[i];
+    kw[4 * i] = v.x;
+    kw[4 * i + 1] = v.y;
+    kw[4 * i + 2] = v.z;
+    kw[4 * i + 3] = v.w;
+  }
+  const float scale = 0.088388347648318440f;  // 1/sqrt(128)
+  float acc = 0.0f;
+  for (int p = 0; p < P; ++p) {
+    const int r = r0 + p / G;
+    if (j > kv0 + r) continue;  // past row r's causal limit
+    const uint32_t* q = qsm + p * (D / 2);
+    float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < D / 2; w += 2) {
+      d0 = ss::dot2(kw[w], q[w], d0);
+      d1 = ss::dot2(kw[w + 1], q[w + 1], d1);
+    }
+    acc += expf((d0 + d1) * scale - mls[2 * p]) / mls[2 * p + 1];
+  }
+  score[(int64_t)hk * a.cap + j] = acc;
 }
 
 }  // namespace
@@ -300,3 +374,14 @@ hipError_t launch_rows_attention(const AttnArgs& a, hipStream_t s) {
 }
 
 int decode_attn_keys_per_split() { return DKPB; }
+
+int attn_scores_max_pairs() { return SMAXP; }
+
+hipError_t launch_attn_scores(const AttnArgs& a, float* score, int window, hipStream_t s) {
+  const int G = a.n_q / a.n_kv;
+  const int P = (window < a.m ? window : a.m) * G;
+  if (P > SMAXP || P < 1 || !a.ml) return hipErrorInvalidValue;
+  const size_t lds = (size_t)P * (D / 2) * 4 + (size_t)P * 8;
+  SS_LAUNCH(attn_scores_kernel, dim3(a.n_kv, (a.cap + SKB - 1) / SKB), dim3(SKB), lds, s, a, score, window);
+  return hipGetLastError();
+}

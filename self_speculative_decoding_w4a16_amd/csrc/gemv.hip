@@ -201,8 +201,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int64_t n_gr
     // merged over the decode-attention splits in split order, batches of 4.
     constexpr int DH = 128, REC = 4 + DH;
     const int n_chunks = K / 16;  // 16 dims per chunk
-    const int pos = *a.kv_len + a.pos_offset;
-    int active = (pos + a.attn_kpb) / a.attn_kpb;
+    int n_keys = *a.kv_len + a.pos_offset + 1;
+    if (a.attn_nidx) n_keys = min(max(*a.attn_nidx, 0), a.attn_index_cap) + a.pos_offset + 1;
+    int active = (n_keys + a.attn_kpb - 1) / a.attn_kpb;
     if (active > a.attn_splits) active = a.attn_splits;
     const int G = a.attn_g;
     const int64_t sstride = (int64_t)G * REC;

@@ -35,6 +35,8 @@ struct GemvArgs {
   int attn_splits, attn_kpb, n_kv, attn_g;
   const int32_t* kv_len;
   int pos_offset;
+  const int32_t* attn_nidx;  // sparse draft: keys = *attn_nidx + pos_offset + 1 (else kv_len + pos_offset + 1)
+  int attn_index_cap;
 };
 
 int gemv_max_blocks(bool w4, int64_t n, int epi);  // blocks of one launch (logits partials)
@@ -76,6 +78,12 @@ struct AttnArgs {
   float* part;          // split partials [Hkv][splits][m][G][d + 4]
   int splits;           // grid splits over keys (128 keys each)
   uint16_t* out;        // [m][Hq d]
+  float* ml;            // optional [m][Hq][2]: softmax (max, sum) of each row and head
+  // sparse draft (draft step only; index == nullptr: dense): keys are
+  // index[hk][0 .. *n_index) followed by positions kv_len .. kv_len + pos_offset
+  const int32_t* index;  // [Hkv][index_cap] of this layer
+  const int32_t* n_index;
+  int index_cap;
 };
 hipError_t launch_rope_append(const AttnArgs& a, hipStream_t s);
 // One query position: RoPE + KV append + per-split partials (m, l, o[d]) in
@@ -86,6 +94,14 @@ int decode_attn_keys_per_split();
 // m query rows at positions kv_len + pos_offset + j (q_rot and the cache already
 // written by rope_append): per-row split partials, then a merge into out.
 hipError_t launch_rows_attention(const AttnArgs& a, hipStream_t s);
+// Importance scores of one layer after launch_rows_attention (a.ml set):
+// score[hk][j] for j < kv_len + m, over the last `window` rows.
+hipError_t launch_attn_scores(const AttnArgs& a, float* score, int window, hipStream_t s);
+int attn_scores_max_pairs();
+// Sparse index of every (layer, KV head) list from the scores.
+hipError_t launch_kv_select(const float* score, int cap, const int32_t* kv_len, int n_lists, int n_sink,
+                            int n_recent, int budget_permille, int32_t* index, int index_cap,
+                            int32_t* index_len, hipStream_t s);
 
 // ------------------------------------------------------------------ misc kernels
 hipError_t launch_rmsnorm_rows(const uint16_t* h, const uint16_t* g, float eps, int rows, int k,

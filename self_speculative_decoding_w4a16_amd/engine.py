@@ -4,6 +4,11 @@ gamma+1 positions, the rejection round, KV rollback.  Every step is a call
 into libsubspec; this class only owns the device buffers and the call order.
 State lives on the device (kv_len, tokens), so a cycle needs no host sync;
 the host reads back the emitted tokens once per cycle.
+
+With ``sparse`` the draft reads a sparse KV index ("The second ledger of
+speculative decoding", sections 3.1-3.2): every verify writes importance
+scores, and after the rollback the index is rebuilt; the first cycle after
+a reset drafts densely.
 """
 import torch
 
@@ -12,7 +17,9 @@ from . import _lib
 
 class SpecDecoder:
     def __init__(self, model, capacity, gamma, temp=0.0, draft_temp=0.0, max_tokens=64,
-                 device="cuda"):
+                 device="cuda", sparse=None):
+        """``sparse``: None (dense drafting) or dict(n_sink, n_recent, window,
+        budget_permille)."""
         s = model.shape
         self.model = model
         self.gamma = gamma
@@ -40,24 +47,53 @@ class SpecDecoder:
         self.c = _lib.State(self.k_cache.data_ptr(), self.v_cache.data_ptr(), capacity,
                             self.kv_len.data_ptr(), self.tokens.data_ptr(),
                             self.draft_logits.data_ptr(), gamma)
+        self.sparse = dict(sparse) if sparse else None
+        if self.sparse:
+            sp = self.sparse
+            self.index_cap = _lib.index_count(capacity, sp["n_sink"], sp["n_recent"],
+                                              sp["budget_permille"])
+            self.kv_score = torch.zeros((L, s.n_kv_heads, capacity), dtype=torch.float32, device=device)
+            self.kv_index = torch.zeros((L, s.n_kv_heads, self.index_cap), dtype=torch.int32,
+                                        device=device)
+            self.kv_index_len = torch.zeros(1, dtype=torch.int32, device=device)
+            c = self.c
+            c.kv_score = self.kv_score.data_ptr()
+            c.kv_index = self.kv_index.data_ptr()
+            c.kv_index_len = self.kv_index_len.data_ptr()
+            c.index_cap = self.index_cap
+            c.use_index = 0
+            c.n_sink, c.n_recent = sp["n_sink"], sp["n_recent"]
+            c.score_window, c.budget_permille = sp["window"], sp["budget_permille"]
 
     # ------------------------------------------------------------ state
     def reset(self, kv_len, last_token):
         self.kv_len.fill_(int(kv_len))
         self.tokens[0] = int(last_token)
+        self.c.use_index = 0  # the first cycle drafts densely
+
+    def load_kv(self, k, v, kv_len, last_token):
+        """Start from a given KV history (bf16 [L][Hkv][>= kv_len][d])."""
+        n = k.shape[2]
+        self.k_cache[:, :, :n].copy_(k)
+        self.v_cache[:, :, :n].copy_(v)
+        self.reset(kv_len, last_token)
 
     def prefill(self, prompt):
         """Run prompt[:-1] through the target (chunks of max_tokens positions);
         afterwards kv_len = len(prompt) - 1 and tokens[0] = prompt[-1]."""
         prompt = [int(t) for t in prompt]
-        self.kv_len.zero_()
+        self.reset(0, prompt[-1])
         body = prompt[:-1]
-        for c0 in range(0, len(body), self.max_tokens):
-            chunk = body[c0:c0 + self.max_tokens]
-            self.prefill_tokens[:len(chunk)] = torch.tensor(chunk, dtype=torch.int32)
-            _lib.verify(self.model.c, self.c, len(chunk), self.prefill_tokens, None, self.ws)
-            _lib.kv_advance(self.c, len(chunk))
-        self.tokens[0] = prompt[-1]
+        score = self.c.kv_score
+        self.c.kv_score = None  # no importance scores for prefill chunks
+        try:
+            for c0 in range(0, len(body), self.max_tokens):
+                chunk = body[c0:c0 + self.max_tokens]
+                self.prefill_tokens[:len(chunk)] = torch.tensor(chunk, dtype=torch.int32)
+                _lib.verify(self.model.c, self.c, len(chunk), self.prefill_tokens, None, self.ws)
+                _lib.kv_advance(self.c, len(chunk))
+        finally:
+            self.c.kv_score = score
 
     # ------------------------------------------------------------ one cycle
     def draft(self, u_draft=None):
@@ -74,6 +110,9 @@ class SpecDecoder:
 
     def commit(self):
         _lib.kv_rollback(self.c, self.n_accepted, self.out_tokens)
+        if self.sparse:
+            _lib.kv_select(self.model.c, self.c)
+            self.c.use_index = 1
 
     def ar_step(self):
         """One plain autoregressive step of the draft model (a full-precision

@@ -78,7 +78,7 @@ CONFIGS = {
     "full32b": Workload("full32b", QWEN32B, 48, 0.6, 0.6, 2048, 128),
     # long-context 8B shape with a gathered 10% KV index for the draft
     "longctx8b": Workload("longctx8b", LLAMA8B, 11, 0.0, 0.0, 60000, 128,
-                          {"n_sink": 4, "n_recent": 64, "budget": 0.1, "window": 16}),
+                          {"n_sink": 4, "n_recent": 64, "budget": 0.1, "budget_permille": 100, "window": 16}),
 }
 
 
