@@ -103,13 +103,28 @@ def main():
         return
     gamma, G = wl.gamma, wl.generate
     cap = ((wl.prompt + G + gamma + 1 + 63) // 64) * 64 + 64
-    dec = SpecDecoder(dm, cap, gamma, wl.temp, wl.draft_temp)
-    prompt = [int(t) for t in token_ids(wl.prompt, shape.vocab, 5)]
+    sparse = None
+    if "budget_permille" in wl.extra:
+        sparse = dict(n_sink=wl.extra["n_sink"], n_recent=wl.extra["n_recent"],
+                      window=wl.extra["window"], budget_permille=wl.extra["budget_permille"])
+    dec = SpecDecoder(dm, cap, gamma, wl.temp, wl.draft_temp, sparse=sparse)
     t0 = time.time()
-    dec.prefill(prompt)
-    torch.cuda.synchronize()
-    log(f"prefill {len(prompt)} tokens in {time.time() - t0:.2f}s")
-    kv0, last = len(prompt) - 1, prompt[-1]
+    if sparse:
+        # long context: a synthetic KV history (N(0,1) per layer and head)
+        # stands in for a prefilled document; there is no 60K-token prefill
+        from synth import kv_history
+        for l in range(shape.n_layers):
+            K, V = kv_history(1, shape.n_kv_heads, wl.prompt, shape.head_dim, wl.prompt, 600 + l, dev)
+            dec.k_cache[l, :, :wl.prompt].copy_(K[0])
+            dec.v_cache[l, :, :wl.prompt].copy_(V[0])
+        kv0, last = wl.prompt, int(token_ids(1, shape.vocab, 5)[0])
+        log(f"synthetic KV history of {wl.prompt} positions in {time.time() - t0:.2f}s")
+    else:
+        prompt = [int(t) for t in token_ids(wl.prompt, shape.vocab, 5)]
+        dec.prefill(prompt)
+        torch.cuda.synchronize()
+        log(f"prefill {len(prompt)} tokens in {time.time() - t0:.2f}s")
+        kv0, last = len(prompt) - 1, prompt[-1]
 
     stochastic = wl.temp > 0 or wl.draft_temp > 0
     uni = None
@@ -187,8 +202,12 @@ def main():
     kv_row = 2 * shape.n_kv_heads * shape.head_dim * 2 * shape.n_layers  # K+V bytes per position
     attn_bytes = {"attn_draft": 0.0, "attn_verify": 0.0}
     kv = kv0
-    for n in ns_prof:
-        attn_bytes["attn_draft"] += sum((kv + i + 1) * kv_row for i in range(gamma))
+    for c, n in enumerate(ns_prof):
+        if sparse and c > 0:  # the index plus the speculative positions
+            n_idx = _lib.index_count(kv, sparse["n_sink"], sparse["n_recent"], sparse["budget_permille"])
+            attn_bytes["attn_draft"] += sum((n_idx + i + 1) * kv_row for i in range(gamma))
+        else:
+            attn_bytes["attn_draft"] += sum((kv + i + 1) * kv_row for i in range(gamma))
         attn_bytes["attn_verify"] += (kv + gamma + 1) * kv_row
         kv += n + 1
     kern = {}
@@ -224,6 +243,8 @@ def main():
     log("isolated: " + json.dumps(iso))
 
     def roof_iso(names, label):
+        if not names:
+            return None
         ms = sum(iso[n]["avg_us"] * iso[n]["per_step"] for n in names) / 1000
         by = sum(iso[n]["bytes_per_launch"] * iso[n]["per_step"] for n in names)
         gbs = by / (ms * 1e-3) / 1e9
@@ -261,7 +282,7 @@ def main():
         cpu = cpu_baseline(shape, w, dm, wl, tau)
 
     line = {
-        "metric": "spec-decode tokens/s @7B shape gamma=16; W4 GEMV & verify HBM GB/s vs peak",
+        "metric": "spec-decode tokens/s @7B shape \u03b3=16; W4 GEMV & verify HBM GB/s vs peak",
         "value": round(tok_s, 3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -276,13 +297,19 @@ def main():
         "config": {"workload": f"{wl.name}: {shape.n_layers}-layer {shape.name} random-init, "
                                f"{shape.n_shared} shared bf16 + {shape.n_layers - shape.n_shared} "
                                f"W4 g64 substitute layers, vocab {shape.vocab}, gamma {gamma}, "
-                               f"T {wl.temp}, T_d {wl.draft_temp}, prompt {wl.prompt}, "
-                               f"generate {G}",
+                               f"T {wl.temp}, T_d {wl.draft_temp}, "
+                               + (f"synthetic KV history {wl.prompt} positions, draft over a sparse "
+                                  f"index (sink {sparse['n_sink']}, recent {sparse['n_recent']}, "
+                                  f"budget {sparse['budget_permille'] / 10:g}%, scores of the last "
+                                  f"{sparse['window']} verify rows), " if sparse else
+                                  f"prompt {wl.prompt}, ")
+                               + f"generate {G}",
                    "global_batch": 1, "seq_len": wl.prompt + G, "parallelism": "none (1 GPU)"},
         "roofline": roof_iso([dominant], dominant) if dominant in iso else roof(dominant),
-        "roofline_w4_gemv": roof_iso(["w4_qkv", "w4_o", "w4_gate_up", "w4_down"],
+        "roofline_w4_gemv": roof_iso([n for n in ("w4_qkv", "w4_o", "w4_gate_up", "w4_down") if n in iso],
                                      "w4_gemv (byte-weighted over one draft step's W4 GEMVs)"),
-        "roofline_bf16_gemv": roof_iso(["bf16_qkv", "bf16_o", "bf16_gate_up", "bf16_down", "lm_head"],
+        "roofline_bf16_gemv": roof_iso([n for n in ("bf16_qkv", "bf16_o", "bf16_gate_up", "bf16_down",
+                                                    "lm_head") if n in iso],
                                        "bf16_gemv (byte-weighted over one draft step's bf16 GEMVs)"),
         "roofline_verify_gemm": roof("verify_gemm"),
         "roofline_attn_draft": roof("attn_draft"),
@@ -400,16 +427,18 @@ def isolated_gemvs(dm, shape, dev, reps=3, only=None, graph=True):
 
 def cpu_baseline(shape, w, dm, wl, tau):
     """The oracle, untuned, on a bounded sample of the same workload: one
-    draft token through one shared bf16 layer, one W4 substitute layer and
-    the lm_head, and one 17-position verify through one layer and the
-    lm_head, all at full 7B shapes over a 600-position synthetic KV.  The
-    per-layer times are scaled to the 28-layer model, a cycle is 16 draft
-    steps + verify + reject, and tokens/s = tau (of the GPU run) / cycle."""
+    draft token through one shared bf16 layer (if the model has any), one W4
+    substitute layer and the lm_head, and one gamma+1-position verify through
+    one layer and the lm_head, at the workload's shapes and context length
+    (synthetic KV; the long-context workload drafts over its sparse index
+    and its verify also computes the importance scores).  The per-layer
+    times are scaled to the full model, a cycle is gamma draft steps +
+    verify + reject, and tokens/s = tau (of the GPU run) / cycle."""
     import numpy as np
-    import torch
 
     from oracle.model import OracleModel, forward
     from oracle.reject import reject
+    from oracle.sparse import select_index
     from synth import kv_history, logits_pair, token_ids
 
     try:
@@ -419,23 +448,36 @@ def cpu_baseline(shape, w, dm, wl, tau):
         cores = os.cpu_count()
     host = lambda t: t.detach().float().cpu().numpy()
     log("cpu baseline: copying sampled layers to host")
+    gamma = wl.gamma
+    L, S = shape.n_layers, shape.n_shared
     base = dict(n_layers=0, hidden=shape.hidden, ffn=shape.ffn, n_q_heads=shape.n_q_heads,
                 n_kv_heads=shape.n_kv_heads, head_dim=shape.head_dim, vocab=shape.vocab,
                 rope_theta=shape.rope_theta, rms_eps=shape.rms_eps, embed=host(w["embed"]),
                 final_norm=host(w["final_norm"]), lm_head=host(w["lm_head"]), layers=[])
-    shared = {k: host(v) for k, v in w["layers"][0].items()}
-    subst = {k: host(v) for k, v in w["layers"][shape.n_shared].items()}
     m0 = OracleModel(**base)
-    m_sh = OracleModel(**{**base, "n_layers": 1, "layers": [shared]})
-    m_w4 = OracleModel(**{**base, "n_layers": 1, "layers": [subst]})
+    m_sh = None
+    if S > 0:
+        m_sh = OracleModel(**{**base, "n_layers": 1,
+                              "layers": [{k: host(v) for k, v in w["layers"][0].items()}]})
+    m_w4 = OracleModel(**{**base, "n_layers": 1,
+                          "layers": [{k: host(v) for k, v in w["layers"][S].items()}]})
     t0 = time.perf_counter()
     m_w4.make_substitutes([0])
     t_quant = time.perf_counter() - t0
-    kv_len = 600
-    K, V = kv_history(1, shape.n_kv_heads, kv_len, shape.head_dim, kv_len + 32, 44, "cpu")
-    kv = lambda: (host(K).astype(np.float64), host(V).astype(np.float64))
-    toks = [int(t) for t in token_ids(17, shape.vocab, 45)]
-    K0 = np.zeros((0, shape.n_kv_heads, kv_len + 32, shape.head_dim))
+    kv_len = max(wl.prompt, 600)
+    cap = kv_len + gamma + 2
+    K, V = kv_history(1, shape.n_kv_heads, kv_len, shape.head_dim, cap, 44, "cpu")
+    K, V = host(K).astype(np.float64), host(V).astype(np.float64)
+    kv = lambda: (K.copy(), V.copy())
+    toks = [int(t) for t in token_ids(gamma + 1, shape.vocab, 45)]
+    K0 = np.zeros((0, shape.n_kv_heads, cap, shape.head_dim))
+    sparse, scores = None, None
+    ex = wl.extra
+    if "budget_permille" in ex:
+        rng = np.random.default_rng(46)
+        index = [[select_index(rng.random(kv_len), kv_len, ex["n_sink"], ex["n_recent"],
+                               ex["budget_permille"]) for _ in range(shape.n_kv_heads)]]
+        sparse, scores = (index, kv_len), []
 
     def timed(fn):
         t = time.perf_counter()
@@ -443,26 +485,26 @@ def cpu_baseline(shape, w, dm, wl, tau):
         return time.perf_counter() - t
 
     t_lm1 = timed(lambda: forward(m0, (K0, K0), kv_len, toks[:1], draft=True))
-    t_sh1 = timed(lambda: forward(m_sh, kv(), kv_len, toks[:1], draft=True))
-    t_w41 = timed(lambda: forward(m_w4, kv(), kv_len, toks[:1], draft=True))
-    t_lm17 = timed(lambda: forward(m0, (K0, K0), kv_len, toks, draft=False))
-    t_v17 = timed(lambda: forward(m_sh, kv(), kv_len, toks, draft=False))
-    zt, zd = logits_pair(wl.gamma, shape.vocab, 46)
+    t_sh1 = timed(lambda: forward(m_sh, kv(), kv_len, toks[:1], draft=True)) if m_sh else 0.0
+    t_w41 = timed(lambda: forward(m_w4, kv(), kv_len, toks[:1], draft=True, sparse=sparse))
+    t_lm = timed(lambda: forward(m0, (K0, K0), kv_len, toks, draft=False))
+    t_v = timed(lambda: forward(m_sh or m_w4, kv(), kv_len, toks, draft=False, scores=scores))
+    zt, zd = logits_pair(gamma, shape.vocab, 46)
     zt, zd = host(zt), host(zd)
-    am = [int(np.argmax(zt[i])) for i in range(wl.gamma)]
-    t_rej = timed(lambda: reject(zt, zd, am, [0] * wl.gamma, 0, wl.temp, wl.draft_temp))
-    L, S = shape.n_layers, shape.n_shared
+    am = [int(np.argmax(zt[i])) for i in range(gamma)]
+    t_rej = timed(lambda: reject(zt, zd, am, [0] * gamma, 0, wl.temp, wl.draft_temp))
     t_draft = S * max(t_sh1 - t_lm1, 0) + (L - S) * max(t_w41 - t_lm1, 0) + t_lm1
-    t_verify = L * max(t_v17 - t_lm17, 0) + t_lm17
-    cycle = wl.gamma * t_draft + t_verify + t_rej
-    sample_s = t_lm1 + t_sh1 + t_w41 + t_lm17 + t_v17 + t_rej
+    t_verify = L * max(t_v - t_lm, 0) + t_lm
+    cycle = gamma * t_draft + t_verify + t_rej
+    sample_s = t_lm1 + t_sh1 + t_w41 + t_lm + t_v + t_rej
     log(f"cpu baseline: draft step {t_draft:.2f}s, verify {t_verify:.2f}s, reject {t_rej:.2f}s "
         f"(sample {sample_s:.1f}s, quantise {t_quant:.1f}s)")
+    layers = (f"one shared bf16 layer, one W4 layer" if S else "one W4 layer")
     return {"value": round(tau / cycle, 6), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": (f"oracle (NumPy float64) timed on one shared bf16 layer, one W4 layer, the "
-                       f"lm_head and one reject round at full 7B shapes ({sample_s:.1f}s of CPU "
-                       f"work), scaled to {L} layers and a gamma={wl.gamma} cycle; tokens/s = "
-                       f"tau of the GPU run / oracle cycle time"),
+            "sample": (f"oracle (NumPy float64) timed on {layers}, the lm_head and one reject "
+                       f"round at full {shape.name} shapes over {kv_len} positions of KV "
+                       f"({sample_s:.1f}s of CPU work), scaled to {L} layers and a gamma={gamma} "
+                       f"cycle; tokens/s = tau of the GPU run / oracle cycle time"),
             "oracle_draft_step_s": round(t_draft, 3), "oracle_verify_s": round(t_verify, 3),
             "oracle_reject_s": round(t_rej, 3)}
 

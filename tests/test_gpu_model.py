@@ -11,7 +11,7 @@ from self_speculative_decoding_w4a16_amd import _lib
 from self_speculative_decoding_w4a16_amd.engine import SpecDecoder
 from self_speculative_decoding_w4a16_amd.model import DeviceModel
 from synth import model_weights, kv_history, token_ids, uniform_codes
-from synth.configs import QWEN7B
+from synth.configs import QWEN7B, QWEN32B
 from tests.gpu_util import codes_i32, log, rel_err
 from tests.helpers import host, oracle_model
 
@@ -46,13 +46,15 @@ def _setup(shape, seed, cap, gamma, kv_len, subs=None, T=0.0, Td=0.0, device="cu
     return dm, dec, om, kv
 
 
-@pytest.mark.parametrize("shape_name", ["tiny", "layer7b"])
+@pytest.mark.parametrize("shape_name", ["tiny", "layer7b", "layer32b"])
 def test_draft_step_and_verify_match_oracle(cuda, shape_name):
+    gamma = 16
     if shape_name == "tiny":
         shape, kv_len, cap = TINY, 100, 256
-    else:
+    elif shape_name == "layer7b":
         shape, kv_len, cap = QWEN7B.with_(n_layers=1, n_shared=0), 1024, 1088
-    gamma = 16
+    else:  # one 32B-shaped layer at the 32B workload's context and draft length
+        shape, kv_len, cap, gamma = QWEN32B.with_(n_layers=1, n_shared=0), 2048, 2112, 48
     log(f"draft/verify parity {shape_name}")
     dm, dec, om, kv = _setup(shape, 3, cap, gamma, kv_len)
     toks = token_ids(gamma + 1, shape.vocab, 11)
