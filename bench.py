@@ -107,7 +107,7 @@ def main():
     if "budget_permille" in wl.extra:
         sparse = dict(n_sink=wl.extra["n_sink"], n_recent=wl.extra["n_recent"],
                       window=wl.extra["window"], budget_permille=wl.extra["budget_permille"])
-    dec = SpecDecoder(dm, cap, gamma, wl.temp, wl.draft_temp, sparse=sparse)
+    dec = SpecDecoder(dm, cap, gamma, wl.temp, wl.draft_temp, sparse=sparse, graphs=True)
     t0 = time.time()
     if sparse:
         # long context: a synthetic KV history (N(0,1) per layer and head)
@@ -195,10 +195,12 @@ def main():
     # KV length, so they are added here from the host's record of it: a draft
     # step at position p reads K and V of positions [0, p] once per layer, a
     # verify pass reads [0, kv_len + gamma] once per layer.
+    dec.use_graphs = False  # recorded replays would bypass the launch profiler
     _lib.profile_start(400000)
     _, ns_prof = one_generation()
     torch.cuda.synchronize()
     _lib.profile_stop()
+    dec.use_graphs = True
     kv_row = 2 * shape.n_kv_heads * shape.head_dim * 2 * shape.n_layers  # K+V bytes per position
     attn_bytes = {"attn_draft": 0.0, "attn_verify": 0.0}
     kv = kv0

@@ -104,6 +104,10 @@ typedef struct {
   subspec_linear qkv_d, o_d, gate_up_d, down_d;
 } subspec_layer;
 
+/* Model description.  Supported: head_dim 128; hidden and ffn multiples of
+ * 128, hidden <= 6144, ffn <= 28672; n_q_heads a multiple of n_kv_heads
+ * with a group n_q_heads / n_kv_heads <= 8; vocab <= 2^24
+ * (SUBSPEC_EUNSUPPORTED / SUBSPEC_ESHAPE otherwise). */
 typedef struct {
   int32_t n_layers, hidden, ffn, n_q_heads, n_kv_heads, head_dim, vocab;
   float rope_theta, rms_eps;

@@ -88,8 +88,8 @@ int check_model(const subspec_model* m) {
   if (m->head_dim != 128) return fail(SUBSPEC_EUNSUPPORTED, "head_dim must be 128");
   if (m->n_q_heads % m->n_kv_heads != 0)
     return fail(SUBSPEC_ESHAPE, "n_q_heads must be a multiple of n_kv_heads");
-  if (m->n_q_heads / m->n_kv_heads > 16 || m->n_kv_heads > 1024)
-    return fail(SUBSPEC_EUNSUPPORTED, "GQA group above 16 or more than 1024 kv heads");
+  if (m->n_q_heads / m->n_kv_heads > 8 || m->n_kv_heads > 1024)
+    return fail(SUBSPEC_EUNSUPPORTED, "GQA group above 8 or more than 1024 kv heads");
   if (m->hidden % 128 != 0 || m->ffn % 128 != 0)
     return fail(SUBSPEC_ESHAPE, "hidden and ffn must be multiples of 128");
   if (m->hidden > kMaxGemvK || m->ffn > kMaxGemvK ||
@@ -161,6 +161,7 @@ struct FwdWs {
   uint16_t *h, *xn, *qkv, *qrot, *attn, *act;
   float* attn_part;
   float* attn_ml;
+  float* rope_cs;
   float* gemm_part;
   float* logit_max;
   int32_t* logit_arg;
@@ -196,11 +197,14 @@ size_t carve_fwd(const subspec_model* m, int mt, int cap, void* ws, FwdWs* o) {
   w.qrot = (uint16_t*)c.take((size_t)mt * qd * 2);
   w.attn = (uint16_t*)c.take((size_t)mt * qd * 2);
   w.act = (uint16_t*)c.take((size_t)mt * F * 2);
-  // attention split partials [Hkv][ceil(cap/128)][mt][G][d + 4]
-  const size_t dsplits = (cap + decode_attn_keys_per_split() - 1) / decode_attn_keys_per_split();
-  const size_t part_floats = (size_t)m->n_q_heads * dsplits * mt * (m->head_dim + 4);
+  // attention split partials: verify [Hkv][ceil(cap/128)][mt][G][d + 4],
+  // draft step [Hkv][ceil(cap/64)][G][d + 4]
+  const size_t vsplits = (cap + decode_attn_keys_per_split() - 1) / decode_attn_keys_per_split();
+  const size_t dsplits = (cap + draft_attn_keys_per_split() - 1) / draft_attn_keys_per_split();
+  const size_t part_floats = (size_t)m->n_q_heads * std::max(vsplits * mt, dsplits) * (m->head_dim + 4);
   w.attn_part = (float*)c.take(part_floats * 4);
   w.attn_ml = (float*)c.take((size_t)mt * m->n_q_heads * 2 * 4);
+  w.rope_cs = (float*)c.take((size_t)mt * m->head_dim * 4);
   w.gemm_part = (float*)c.take(max_gemm_partials(m, mt));
   const int lm_blocks = gemv_max_blocks(false, m->vocab, EPI_LOGITS);
   w.logit_max = (float*)c.take((size_t)lm_blocks * 4);
@@ -319,7 +323,8 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
   const bool sparse = st->use_index != 0;
   {
     prof::Scope ps(SUBSPEC_K_MISC, 0.0, s);
-    HIPCHK(launch_pos_guard(st->kv_len, st->tokens + step, step, st->capacity, m->vocab, w.valid, tok_out, s));
+    HIPCHK(launch_pos_guard(st->kv_len, st->tokens + step, step, st->capacity, m->vocab, w.valid, tok_out,
+                            (int)d, m->rope_theta, w.rope_cs, s));
   }
   for (int l = 0; l < m->n_layers; ++l) {
     const subspec_layer& L = m->layers[l];
@@ -353,9 +358,10 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
     at.d = (int)d;
     at.cap = st->capacity;
     at.theta = m->rope_theta;
+    at.rope_cs = w.rope_cs;
     at.part = w.attn_part;
     at.out = w.attn;
-    const int kpb = decode_attn_keys_per_split();
+    const int kpb = draft_attn_keys_per_split();
     at.splits = (st->capacity + kpb - 1) / kpb;
     if (sparse) {
       at.index = st->kv_index + (int64_t)l * m->n_kv_heads * st->index_cap;
@@ -376,20 +382,10 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
     o.y = w.h;
     o.resid = w.h;
     o.valid = w.valid;
-    o.attn_part = w.attn_part;
-    o.attn_splits = at.splits;
-    o.attn_kpb = decode_attn_keys_per_split();
-    o.n_kv = m->n_kv_heads;
-    o.attn_g = m->n_q_heads / m->n_kv_heads;
-    o.kv_len = st->kv_len;
-    o.pos_offset = step;
-    if (sparse) {
-      o.attn_nidx = st->kv_index_len;
-      o.attn_index_cap = st->index_cap;
-    }
+    o.x = w.attn;
     {
       prof::Scope ps(gemv_class(L.o_d, 1), gemv_bytes(L.o_d, H, true), s);
-      HIPCHK(launch_gemv(lin_is_w4(L.o_d), PRO_ATTN_MERGE, EPI_RESID, o, s, nullptr));
+      HIPCHK(launch_gemv(lin_is_w4(L.o_d), PRO_X, EPI_RESID, o, s, nullptr));
     }
 
     GemvArgs g{};
@@ -465,6 +461,7 @@ int subspec_verify(const subspec_model* m, const subspec_state* st, int32_t n_to
   {
     prof::Scope ps(SUBSPEC_K_MISC, 0.0, s);
     HIPCHK(launch_embed_rows(m->embed, tokens, mt, (int)H, m->vocab, w.h, s));
+    HIPCHK(launch_rope_table(st->kv_len, 0, mt, (int)d, m->rope_theta, w.rope_cs, s));
   }
   for (int l = 0; l < m->n_layers; ++l) {
     const subspec_layer& L = m->layers[l];
@@ -490,6 +487,7 @@ int subspec_verify(const subspec_model* m, const subspec_state* st, int32_t n_to
     at.d = (int)d;
     at.cap = st->capacity;
     at.theta = m->rope_theta;
+    at.rope_cs = w.rope_cs;
     at.part = w.attn_part;
     at.out = w.attn;
     at.splits = (st->capacity + decode_attn_keys_per_split() - 1) / decode_attn_keys_per_split();

@@ -4,13 +4,18 @@
 // draft and target read and write one cache ("SubSpec: Speculate Deep and
 // Accurate" paper note, Method details, KV-cache sharing).
 //
-// Kernels:
-//  rope_append        rotate-half RoPE of q and k for the verify rows (angles
-//                     in float64, applied in float32); q -> q_rot, k/v -> cache.
-//  decode_attn        grid (kv head, 128-key split[, row]): per split partial
-//                     (max, sum, o[d]) for every query head of the GQA group.
+// Kernels (RoPE angles come from a per-step / per-pass table computed in
+// float64 and applied in float32):
+//  rope_append        rotate-half RoPE of q and k for the verify rows;
+//                     q -> q_rot, k/v -> cache.
+//  rows_attn          verify: grid (kv head, 128-key split, row): per split
+//                     partial (max, sum, o[d]) for every query head of the
+//                     GQA group.
 //  rows_merge         merges the verify partials in split order.
-// The draft step's partials are merged by the output projection's prologue.
+//  draft_attn         draft step: RoPE + KV append + grid (kv head, 256-key
+//                     split) partials, merged by the output projection's
+//                     prologue; dense or over the sparse index.
+//  attn_scores        verify: importance scores for the sparse draft index.
 #include "common.h"
 #include "internal.h"
 #include "profile.h"
@@ -28,10 +33,7 @@ __global__ __launch_bounds__(64) void rope_append_kernel(AttnArgs a) {
   const int pos = *a.kv_len + a.pos_offset + j;
   const int rows = a.n_q + 2 * a.n_kv;
   const uint16_t* src = a.qkv + (int64_t)j * rows * a.d;
-  const double inv_freq = exp(-(2.0 * i / a.d) * log((double)a.theta));
-  double sd, cd;
-  sincos((double)pos * inv_freq, &sd, &cd);
-  const float c = (float)cd, s = (float)sd;
+  const float c = a.rope_cs[((int64_t)j * half + i) * 2], s = a.rope_cs[((int64_t)j * half + i) * 2 + 1];
   if (head < a.n_q) {
     const uint16_t* x = src + head * a.d;
     const float x1 = ss::bf2f(x[i]), x2 = ss::bf2f(x[i + half]);
@@ -54,109 +56,54 @@ __global__ __launch_bounds__(64) void rope_append_kernel(AttnArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// Decode attention for one query position (the draft step): grid (kv head,
-// key split of DKPB keys), 512 threads.  Every block rotates the GQA group's
-// queries itself; the block whose split holds the new position rotates the
-// new key, appends K/V to the cache and uses them directly (no other block
-// reads that position in this launch).  Thread (key j, quarter c) holds 32
-// dims of K[j] and V[j]; scores are reduced over the 4 quarters with lane
-// shuffles.  Each block writes, per query head of its group, the partial
-// (max m, sum l, o[d] = sum_j exp(s_j - m) V[j][d]) of its split; the
-// consumer (the output projection's prologue) merges the splits, so no
-// block waits on another.
+// Verify attention: grid (kv head, key split of DKPB keys, row), 512 threads.
+// Row j's query sits at position kv_len + j and sees keys [0, kv_len + j];
+// rope_append already wrote q_rot and the rows' K/V.  Thread (key j, quarter
+// c) holds 32 dims of K[j] and V[j]; scores are reduced over the 4 quarters
+// with lane shuffles.  Each block writes, per query head of its group, the
+// partial (max m, sum l, o[d] = sum_j exp(s_j - m) V[j][d]) of its split at
+// [kv head][split][row][group head]; rows_merge merges the splits.
 constexpr int DKPB = 128;
 constexpr int DREC = 4 + D;  // partial record: m, l, 2 pad, o[D] (16-byte aligned o)
 
-// CACHED = false: the draft step (one row, q and the new k/v rotated and
-// appended here).  CACHED = true: verify rows (blockIdx.z = row j at position
-// kv_len + j; rope_append already wrote q_rot and the cache), causal limit
-// kv_len + j, partials at [kv head][split][row][group head].
-template <bool CACHED>
-__global__ __launch_bounds__(512) void decode_attn_kernel(AttnArgs a, const int32_t* valid) {
+__global__ __launch_bounds__(512) void rows_attn_kernel(AttnArgs a) {
   constexpr int GMAX = 16;
   constexpr int NW = 8;                    // waves per block
   __shared__ float qs[GMAX][D];            // rotated queries (float)
-  __shared__ float kn[D];                  // rotated new key
   __shared__ u32x4 vs[DKPB][D / 8 + 1];    // V tile (padded rows)
   __shared__ float ps[GMAX][DKPB];         // probabilities p[h][key]
   __shared__ float wmax[NW][GMAX], wsum[NW][GMAX];
   __shared__ float hmax[GMAX];
-  __shared__ float rc[D / 2], rs[D / 2];
 
-  if (valid && *valid == 0) return;
   const int hk = blockIdx.x, split = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int G = a.n_q / a.n_kv;
-  const int row = CACHED ? (int)blockIdx.z : 0;
-  const int kv0 = *a.kv_len;
-  const int pos = kv0 + a.pos_offset + row;  // position of this query (its last key)
+  const int row = (int)blockIdx.z;
+  const int pos = *a.kv_len + a.pos_offset + row;  // position of this query (its last key)
   if (pos < 0 || pos >= a.cap) return;
-  // key slot t -> cache position: dense t; sparse draft index[t] for t < n_idx,
-  // then the speculative positions kv_len + (t - n_idx)
-  const bool sparse = !CACHED && a.index != nullptr;
-  const int n_idx = sparse ? min(max(*a.n_index, 0), a.index_cap) : 0;
-  const int32_t* ilist = sparse ? a.index + (int64_t)hk * a.index_cap : nullptr;
-  const int n_keys = sparse ? n_idx + a.pos_offset + 1 : pos + 1;
+  const int n_keys = pos + 1;
   const int active = (n_keys + DKPB - 1) / DKPB;
   if (split >= active) return;
   const int k0 = split * DKPB;
   const int nk = min(DKPB, n_keys - k0);
-  const bool has_new = !CACHED && (k0 + nk - 1) == n_keys - 1;
 
   // ---- loads: thread (key j, quarter c) takes 32 dims of K[j] and V[j]
   const int j = tid >> 2, c = tid & 3;
-  const bool kvalid = j < nk && (CACHED || (k0 + j) != n_keys - 1);
+  const bool kvalid = j < nk;
   u32x4 kr[4], vr[4];
   {
-    int t = k0 + (kvalid ? j : 0);
-    if (sparse) t = t < n_idx ? min(max(ilist[t], 0), a.cap - 1) : kv0 + (t - n_idx);
-    const int64_t row = (int64_t)hk * a.cap + t;
-    const u32x4* kp = reinterpret_cast<const u32x4*>(a.k_cache + row * D) + 4 * c;
-    const u32x4* vp = reinterpret_cast<const u32x4*>(a.v_cache + row * D) + 4 * c;
+    const int64_t krow = (int64_t)hk * a.cap + k0 + (kvalid ? j : 0);
+    const u32x4* kp = reinterpret_cast<const u32x4*>(a.k_cache + krow * D) + 4 * c;
+    const u32x4* vp = reinterpret_cast<const u32x4*>(a.v_cache + krow * D) + 4 * c;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       kr[i] = kvalid ? kp[i] : u32x4{0u, 0u, 0u, 0u};
       vr[i] = kvalid ? vp[i] : u32x4{0u, 0u, 0u, 0u};
     }
   }
-  // ---- RoPE: the 64 angles once per block in float64, applied in float32
-  const int half = D / 2;
-  if (CACHED) {
-    for (int e = tid; e < G * D; e += 512) {
-      const int h = e / D, i = e % D;
-      qs[h][i] = ss::bf2f(a.q_rot[((int64_t)row * a.n_q + hk * G + h) * D + i]);
-    }
-  } else if (tid < half) {
-    const double inv_freq = exp(-(2.0 * tid / D) * log((double)a.theta));
-    double sd, cd;
-    sincos((double)pos * inv_freq, &sd, &cd);
-    rc[tid] = (float)cd;
-    rs[tid] = (float)sd;
-  }
-  __syncthreads();
-  for (int e = tid; !CACHED && e < (G + (has_new ? 1 : 0)) * half; e += 512) {
-    const int h = e / half, i = e % half;
-    const float cs = rc[i], sn = rs[i];
-    const uint16_t* x = (h < G) ? a.qkv + (hk * G + h) * D : a.qkv + (a.n_q + hk) * D;
-    const float x1 = ss::bf2f(x[i]), x2 = ss::bf2f(x[i + half]);
-    const uint16_t r1 = ss::f2bf(x1 * cs - x2 * sn), r2 = ss::f2bf(x2 * cs + x1 * sn);
-    if (h < G) {
-      qs[h][i] = ss::bf2f(r1);
-      qs[h][i + half] = ss::bf2f(r2);
-    } else {
-      kn[i] = ss::bf2f(r1);
-      kn[i + half] = ss::bf2f(r2);
-      uint16_t* kc = a.k_cache + ((int64_t)hk * a.cap + pos) * D;
-      kc[i] = r1;
-      kc[i + half] = r2;
-    }
-  }
-  if (has_new && tid < D / 8) {
-    const u32x4* vsrc = reinterpret_cast<const u32x4*>(a.qkv + (a.n_q + a.n_kv + hk) * D);
-    u32x4* vdst = reinterpret_cast<u32x4*>(a.v_cache + ((int64_t)hk * a.cap + pos) * D);
-    const u32x4 v = vsrc[tid];
-    vdst[tid] = v;
-    vs[nk - 1][tid] = v;
+  for (int e = tid; e < G * D; e += 512) {
+    const int h = e / D, i = e % D;
+    qs[h][i] = ss::bf2f(a.q_rot[((int64_t)row * a.n_q + hk * G + h) * D + i]);
   }
   if (kvalid) {
 #pragma unroll
@@ -165,18 +112,13 @@ __global__ __launch_bounds__(512) void decode_attn_kernel(AttnArgs a, const int3
   __syncthreads();
   // ---- scores: 32-dim partial dots, reduced over the 4 quarters of a key
   float kf[32];
-  if (!CACHED && j < nk && (k0 + j) == n_keys - 1) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) kf[i] = kn[32 * c + i];
-  } else {
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t w[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        kf[8 * i + 2 * t] = ss::lo_bf(w[t]);
-        kf[8 * i + 2 * t + 1] = ss::hi_bf(w[t]);
-      }
+    for (int t = 0; t < 4; ++t) {
+      kf[8 * i + 2 * t] = ss::lo_bf(w[t]);
+      kf[8 * i + 2 * t + 1] = ss::hi_bf(w[t]);
     }
   }
   const float scale = 0.088388347648318440f;  // 1/sqrt(128)
@@ -234,7 +176,7 @@ __global__ __launch_bounds__(512) void decode_attn_kernel(AttnArgs a, const int3
       o0 += p * ss::lo_bf(v);
       o1 += p * ss::hi_bf(v);
     }
-    float* dst = a.part + (((int64_t)(hk * a.splits + split) * (CACHED ? a.m : 1) + row) * G + h) * DREC;
+    float* dst = a.part + (((int64_t)(hk * a.splits + split) * a.m + row) * G + h) * DREC;
     dst[4 + 2 * dp] = o0;
     dst[4 + 2 * dp + 1] = o1;
     if (dp == 0) {
@@ -244,6 +186,277 @@ __global__ __launch_bounds__(512) void decode_attn_kernel(AttnArgs a, const int3
       dst[1] = l;
     }
   }
+}
+
+// ----------------------------------------------------------------------------
+// Draft-step attention (one query position; the split-key decode of "How
+// speculative decoding makes LLMs go brrr", Module 2, memory-bound): grid
+// (kv head, split of DSK = 64 keys), 256 threads = 4 waves of 16 keys, G (the
+// GQA group size) a template constant.  Small splits keep many compute units
+// busy; draft_merge combines the splits afterwards.
+//  * Every load is issued first: lane (key l%16, quarter l/16) takes a
+//    quarter of its key's K row (64 B); lane l takes the 4-byte V slice
+//    (dims 2l, 2l+1) of each of its wave's 16 keys; thread e takes the q (or
+//    new k) pairs it rotates and their RoPE table entries.  Positions are
+//    clamped and masked, not branched.
+//  * Rotation of the group's queries and, in the block that holds it, the
+//    new key; the new K/V is appended to the cache.
+//  * Scores: each quarter dots its 32 dims with the G queries (v_dot2 on
+//    bf16 pairs in LDS), quarters added by two lane swaps; softmax
+//    statistics per wave over its 16 keys.
+//  * PV: lane = dimension pair over the wave's keys; the 4 waves combine in
+//    LDS into the block's partial (m, l, o[d]) per query head.
+//  * Sparse draft: key slots map to the index list, then to the speculative
+//    positions kv_len .. kv_len + step.
+constexpr int DSK = 64;
+
+struct DraftKeys {
+  int kv0, pos, n_idx, n_keys;
+  const int32_t* ilist;
+};
+
+// Key slots of the draft query of kv head hk (dense: slot t = position t).
+__device__ __forceinline__ DraftKeys draft_keys(const AttnArgs& a, int hk) {
+  DraftKeys k;
+  k.kv0 = *a.kv_len;
+  k.pos = k.kv0 + a.pos_offset;
+  const bool sparse = a.index != nullptr;
+  k.n_idx = sparse ? min(max(*a.n_index, 0), a.index_cap) : 0;
+  k.ilist = sparse ? a.index + (int64_t)hk * a.index_cap : nullptr;
+  k.n_keys = sparse ? k.n_idx + a.pos_offset + 1 : k.pos + 1;
+  return k;
+}
+
+template <int G>
+__global__ __launch_bounds__(256) void draft_attn_kernel(AttnArgs a, const int32_t* valid) {
+  constexpr int NWV = 4, KW = 16;
+  constexpr int NROT = (G + 1) * (D / 4);  // rotation items: pairs (2i, 2i+1) of q heads and new k
+  __shared__ __align__(16) uint32_t qp[G][D / 2];  // rotated queries, bf16 pairs
+  __shared__ __align__(16) uint32_t knew[D / 2];   // rotated new key, bf16 pairs
+  __shared__ uint32_t vnew[D / 2];                 // new value, bf16 pairs
+  __shared__ __align__(16) float ps[NWV][G][KW];   // probabilities per wave, head, key
+  __shared__ float wm[NWV][G], wl[NWV][G];
+  __shared__ float wo[NWV][G][D];
+
+  const int vflag = valid ? *valid : 1;
+  const int hk = blockIdx.x, split = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const DraftKeys ks = draft_keys(a, hk);
+  if (vflag == 0 || ks.pos < 0 || ks.pos >= a.cap) return;
+  const int active = (ks.n_keys + DSK - 1) / DSK;
+  if (split >= active) return;
+  const int k0 = split * DSK;
+  const int kend = min(k0 + DSK, ks.n_keys);  // slots [k0, kend) of this block
+  const bool has_new = kend == ks.n_keys;     // the new key is slot n_keys - 1
+  const int wk0 = k0 + KW * wave;             // first slot of this wave
+  auto slot_pos = [&](int t) {
+    if (!ks.ilist) return t;
+    const int ti = min(t, max(ks.n_idx - 1, 0));
+    const int ip = min(max(ks.ilist[ti], 0), a.cap - 1);
+    return t < ks.n_idx ? ip : ks.kv0 + (t - ks.n_idx);
+  };
+  const uint16_t* kc = a.k_cache + (int64_t)hk * a.cap * D;
+  const uint16_t* vc = a.v_cache + (int64_t)hk * a.cap * D;
+
+  // ---- loads
+  const int kl = lane & (KW - 1), kq = lane >> 4;
+  const int my_slot = wk0 + kl;
+  const bool kin = my_slot < kend;
+  const bool k_is_new = kin && my_slot == ks.n_keys - 1;
+  const bool kload = kin && !k_is_new;
+  u32x4 kr[D / 32];
+  {
+    const u32x4* kp =
+        reinterpret_cast<const u32x4*>(kc + (int64_t)slot_pos(kload ? my_slot : k0) * D) + kq * (D / 32);
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) kr[i] = kp[i];
+  }
+  uint32_t vv[KW];
+  const int last_old = min(kend, ks.n_keys - 1);  // V of slots [.., last_old) comes from the cache
+#pragma unroll
+  for (int kk = 0; kk < KW; ++kk) {
+    const int t = wk0 + kk;  // wave-uniform
+    vv[kk] = reinterpret_cast<const uint32_t*>(vc + (int64_t)slot_pos(t < last_old ? t : k0) * D)[lane];
+  }
+  // rotation inputs: item e = (head h, pair index i2): x[2 i2], x[2 i2 + 1] and
+  // x[64 + 2 i2], x[64 + 2 i2 + 1], with their (cos, sin)
+  const int half = D / 2;
+  uint32_t xlo[(NROT + 255) / 256], xhi[(NROT + 255) / 256];
+  f32x4_t cs[(NROT + 255) / 256];
+#pragma unroll
+  for (int r = 0; r < (NROT + 255) / 256; ++r) {
+    const int e = tid + 256 * r;
+    const int h = e / (half / 2), i2 = e % (half / 2);
+    const bool ok = e < NROT && (h < G || has_new);
+    const uint16_t* x = (h < G) ? a.qkv + (hk * G + h) * D : a.qkv + (a.n_q + hk) * D;
+    xlo[r] = ok ? reinterpret_cast<const uint32_t*>(x)[i2] : 0u;
+    xhi[r] = ok ? reinterpret_cast<const uint32_t*>(x + half)[i2] : 0u;
+    cs[r] = ok ? reinterpret_cast<const f32x4_t*>(a.rope_cs)[i2] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const uint32_t vn_src = (has_new && tid < D / 2)
+                              ? reinterpret_cast<const uint32_t*>(a.qkv + (a.n_q + a.n_kv + hk) * D)[tid]
+                              : 0u;
+
+  // ---- RoPE rotation of the group's queries (and the new key)
+#pragma unroll
+  for (int r = 0; r < (NROT + 255) / 256; ++r) {
+    const int e = tid + 256 * r;
+    const int h = e / (half / 2), i2 = e % (half / 2);
+    if (e < NROT && (h < G || has_new)) {
+      // cs = (cos_i, sin_i, cos_{i+1}, sin_{i+1}) for i = 2 i2
+      const float a1 = ss::lo_bf(xlo[r]), b1 = ss::hi_bf(xlo[r]);  // x[i], x[i+1]
+      const float a2 = ss::lo_bf(xhi[r]), b2 = ss::hi_bf(xhi[r]);  // x[i+64], x[i+65]
+      const uint32_t lo = ss::pack_bf(ss::f2bf(a1 * cs[r][0] - a2 * cs[r][1]),
+                                      ss::f2bf(b1 * cs[r][2] - b2 * cs[r][3]));
+      const uint32_t hi = ss::pack_bf(ss::f2bf(a2 * cs[r][0] + a1 * cs[r][1]),
+                                      ss::f2bf(b2 * cs[r][2] + b1 * cs[r][3]));
+      if (h < G) {
+        qp[h][i2] = lo;
+        qp[h][half / 2 + i2] = hi;
+      } else {
+        knew[i2] = lo;
+        knew[half / 2 + i2] = hi;
+        uint32_t* kdst = reinterpret_cast<uint32_t*>(a.k_cache + ((int64_t)hk * a.cap + ks.pos) * D);
+        kdst[i2] = lo;
+        kdst[half / 2 + i2] = hi;
+      }
+    }
+  }
+  if (has_new && tid < D / 2) {
+    vnew[tid] = vn_src;
+    reinterpret_cast<uint32_t*>(a.v_cache + ((int64_t)hk * a.cap + ks.pos) * D)[tid] = vn_src;
+  }
+  __syncthreads();
+
+  // ---- scores: lane (key, quarter) dots its 32 dims; quarters added by lane swaps
+  if (k_is_new) {
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      const int w = kq * (D / 8) + 4 * i;
+      kr[i] = u32x4{knew[w], knew[w + 1], knew[w + 2], knew[w + 3]};
+    }
+  }
+  const float scale = 0.088388347648318440f;  // 1/sqrt(128)
+  float sc[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      const u32x4 q = *reinterpret_cast<const u32x4*>(&qp[h][kq * (D / 8) + 4 * i]);
+      d0 = ss::dot2(kr[i].x, q.x, d0);
+      d1 = ss::dot2(kr[i].y, q.y, d1);
+      d0 = ss::dot2(kr[i].z, q.z, d0);
+      d1 = ss::dot2(kr[i].w, q.w, d1);
+    }
+    float d = d0 + d1;
+    d += __shfl_xor(d, 16, 64);
+    d += __shfl_xor(d, 32, 64);
+    sc[h] = kin ? d * scale : -INFINITY;
+  }
+  // ---- per-wave softmax statistics over the wave's 16 keys
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float m = sc[h];
+#pragma unroll
+    for (int o = 1; o < KW; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    const float p = kin ? expf(sc[h] - m) : 0.0f;
+    float l = p;
+#pragma unroll
+    for (int o = 1; o < KW; o <<= 1) l += __shfl_xor(l, o, 64);
+    if (kq == 0) ps[wave][h][kl] = p;
+    if (lane == 0) {
+      wm[wave][h] = m;
+      wl[wave][h] = l;
+    }
+  }
+  __syncthreads();
+  // ---- PV: lane = dimension pair over the wave's keys
+  const int new_kk = (has_new && ks.n_keys - 1 >= wk0 && ks.n_keys - 1 < wk0 + KW) ? ks.n_keys - 1 - wk0 : -1;
+  const uint32_t vn = vnew[lane];
+  float vlo[KW], vhi[KW];
+#pragma unroll
+  for (int kk = 0; kk < KW; ++kk) {
+    const uint32_t v = (kk == new_kk) ? vn : vv[kk];
+    vlo[kk] = ss::lo_bf(v);
+    vhi[kk] = ss::hi_bf(v);
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < KW; kk += 4) {
+      const f32x4_t p4 = *reinterpret_cast<const f32x4_t*>(&ps[wave][h][kk]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        o0 += p4[u] * vlo[kk + u];
+        o1 += p4[u] * vhi[kk + u];
+      }
+    }
+    wo[wave][h][2 * lane] = o0;
+    wo[wave][h][2 * lane + 1] = o1;
+  }
+  __syncthreads();
+  // ---- combine the 4 waves into the block's partial per query head
+  for (int e = tid; e < G * D; e += 256) {
+    const int h = e / D, dd = e % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) M = fmaxf(M, wm[w][h]);
+    float L = 0.0f, o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      const float f = (wm[w][h] == -INFINITY) ? 0.0f : expf(wm[w][h] - M);
+      L += f * wl[w][h];
+      o += f * wo[w][h][dd];
+    }
+    float* dst = a.part + ((int64_t)(hk * a.splits + split) * G + h) * DREC;
+    dst[4 + dd] = o;
+    if (dd == 0) {
+      dst[0] = M;
+      dst[1] = L;
+    }
+  }
+}
+
+// Merge of the draft step's split partials: grid (q head), 128 threads (one
+// per dim); splits in order, 8 independent loads at a time.  Writes the
+// attention output (bf16) that the output projection reads.
+__global__ __launch_bounds__(128) void draft_merge_kernel(AttnArgs a, const int32_t* valid) {
+  const int vflag = valid ? *valid : 1;
+  const int hq = blockIdx.x, dd = threadIdx.x;
+  const int G = a.n_q / a.n_kv, hk = hq / G, g = hq % G;
+  const DraftKeys ks = draft_keys(a, hk);
+  if (vflag == 0 || ks.pos < 0 || ks.pos >= a.cap) return;
+  const int active = min((ks.n_keys + DSK - 1) / DSK, a.splits);
+  const int64_t sstride = (int64_t)G * DREC;
+  const float* base = a.part + ((int64_t)hk * a.splits * G + g) * DREC;
+  float M = -INFINITY, L = 0.0f, o = 0.0f;
+  for (int s0 = 0; s0 < active; s0 += 8) {
+    float mv[8], lv[8], ov[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const bool ok = s0 + t < active;
+      const float* q = base + (ok ? s0 + t : 0) * sstride;
+      mv[t] = ok ? q[0] : -INFINITY;
+      lv[t] = ok ? q[1] : 0.0f;
+      ov[t] = ok ? q[4 + dd] : 0.0f;
+    }
+    float Mb = M;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) Mb = fmaxf(Mb, mv[t]);
+    const float r = (M == -INFINITY) ? 0.0f : expf(M - Mb);
+    L *= r;
+    o *= r;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float f = (mv[t] == -INFINITY) ? 0.0f : expf(mv[t] - Mb);
+      L += f * lv[t];
+      o += f * ov[t];
+    }
+    M = Mb;
+  }
+  a.out[(int64_t)hq * D + dd] = ss::f2bf(o / L);
 }
 
 // Merge of the verify partials: grid (q head, row), 128 threads (one per dim);
@@ -358,15 +571,23 @@ hipError_t launch_rope_append(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_decode_attention(const AttnArgs& a, const int32_t* valid, hipStream_t s) {
-  if (a.n_q / a.n_kv > 16) return hipErrorInvalidValue;
-  SS_LAUNCH(decode_attn_kernel<false>, dim3(a.n_kv, a.splits), dim3(512), 0, s, a, valid);
+  const dim3 grid(a.n_kv, a.splits), block(256);
+  switch (a.n_q / a.n_kv) {
+#define SS_G(g) \
+  case g: SS_LAUNCH(draft_attn_kernel<g>, grid, block, 0, s, a, valid); break;
+    SS_G(1) SS_G(2) SS_G(3) SS_G(4) SS_G(5) SS_G(6) SS_G(7) SS_G(8)
+#undef SS_G
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  SS_LAUNCH(draft_merge_kernel, dim3(a.n_q), dim3(D), 0, s, a, valid);
   return hipGetLastError();
 }
 
 hipError_t launch_rows_attention(const AttnArgs& a, hipStream_t s) {
   if (a.n_q / a.n_kv > 16) return hipErrorInvalidValue;
-  SS_LAUNCH(decode_attn_kernel<true>, dim3(a.n_kv, a.splits, a.m), dim3(512), 0, s, a,
-                     (const int32_t*)nullptr);
+  SS_LAUNCH(rows_attn_kernel, dim3(a.n_kv, a.splits, a.m), dim3(512), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SS_LAUNCH(rows_merge_kernel, dim3(a.n_q, a.m), dim3(D), 0, s, a);
@@ -374,6 +595,7 @@ hipError_t launch_rows_attention(const AttnArgs& a, hipStream_t s) {
 }
 
 int decode_attn_keys_per_split() { return DKPB; }
+int draft_attn_keys_per_split() { return DSK; }
 
 int attn_scores_max_pairs() { return SMAXP; }
 

@@ -196,85 +196,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int64_t n_gr
   // items of a 32-value chunk sit in four consecutive lanes
   constexpr int NI = 3;  // items per thread held in registers when normalising
   const int n_items = K / 8;
-  if (PRO == PRO_ATTN_MERGE) {
-    // x[h*128 + d] = sum_s f_s o_s[d] / sum_s f_s l_s, f_s = exp(m_s - max_s m_s),
-    // merged over the decode-attention splits in split order, batches of 4.
-    constexpr int DH = 128, REC = 4 + DH;
-    const int n_chunks = K / 16;  // 16 dims per chunk
-    int n_keys = *a.kv_len + a.pos_offset + 1;
-    if (a.attn_nidx) n_keys = min(max(*a.attn_nidx, 0), a.attn_index_cap) + a.pos_offset + 1;
-    int active = (n_keys + a.attn_kpb - 1) / a.attn_kpb;
-    if (active > a.attn_splits) active = a.attn_splits;
-    const int G = a.attn_g;
-    const int64_t sstride = (int64_t)G * REC;
-    for (int ch0 = 0; ch0 < n_chunks; ch0 += kThreads) {
-      const int ch = ch0 + tid;
-      const bool ok = ch < n_chunks;
-      const int h = ok ? ch / 8 : 0, hk = h / G, gg = h % G, d0 = (ch % 8) * 16;
-      const float* base = a.attn_part + ((int64_t)hk * a.attn_splits * G + gg) * REC;
-      float M = -INFINITY, L = 0.0f, o[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[i] = 0.0f;
-      for (int s0 = 0; s0 < active; s0 += 4) {
-        float mv[4], lv[4];
-        f32x4_t ov[4][4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const bool sok = ok && (s0 + t) < active;
-          const float* q = base + (sok ? (s0 + t) : 0) * sstride;
-          const f32x4_t ml = sok ? *reinterpret_cast<const f32x4_t*>(q) : f32x4_t{-INFINITY, 0.f, 0.f, 0.f};
-          mv[t] = ml[0];
-          lv[t] = ml[1];
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            ov[t][v] = sok ? reinterpret_cast<const f32x4_t*>(q + 4 + d0)[v] : f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-        float Mb = M;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) Mb = fmaxf(Mb, mv[t]);
-        const float r = (M == -INFINITY) ? 0.0f : expf(M - Mb);
-        L *= r;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[i] *= r;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float f = (mv[t] == -INFINITY) ? 0.0f : expf(mv[t] - Mb);
-          L += f * lv[t];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[i] += f * ov[t][i >> 2][i & 3];
-        }
-        M = Mb;
-      }
-      uint16_t xb[16];
-      float xs = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        xb[i] = ss::f2bf(ok ? o[i] / L : 0.0f);
-        xs += ss::bf2f(xb[i]);
-      }
-      const int k0 = h * DH + d0;  // first input column of this chunk
-      if (W4) {
-        xs += __shfl_xor(xs, 1, SS_WAVE);
-        if (ok) {
-#pragma unroll
-          for (int qd = 0; qd < 2; ++qd) {
-            const uint16_t* xq = xb + 8 * qd;
-            smem4[w4_slot(k0 / 32, (k0 % 32) / 8 + qd)] =
-                u32x4{ss::pack_bf(xq[0], xq[4]), ss::pack_bf(xq[1], xq[5]), ss::pack_bf(xq[2], xq[6]),
-                      ss::pack_bf(xq[3], xq[7])};
-          }
-          if ((ch & 1) == 0) xsum[k0 / 32] = xs;
-        }
-      } else if (ok) {
-#pragma unroll
-        for (int qd = 0; qd < 2; ++qd) {
-          const uint16_t* xq = xb + 8 * qd;
-          smem4[k0 / 8 + qd] = u32x4{ss::pack_bf(xq[0], xq[1]), ss::pack_bf(xq[2], xq[3]),
-                                     ss::pack_bf(xq[4], xq[5]), ss::pack_bf(xq[6], xq[7])};
-        }
-      }
-    }
-  } else if (PRO != PRO_X) {
+  if (PRO != PRO_X) {
     const u32x4* src4 = reinterpret_cast<const u32x4*>(src);
     const u32x4* g4 = reinterpret_cast<const u32x4*>(a.norm_w);
     u32x4 hv[NI], gv[NI];
@@ -493,8 +415,7 @@ int64_t gemv_blocks(int64_t n_groups, bool w4, int pro, int fit) {
     per_cu = e ? atoi(e) : 0;
     if (per_cu <= 0) per_cu = 4;
   }
-  // the attention-merge prologue is redone by every block: one block per CU
-  int want = pro == PRO_ATTN_MERGE ? 1 : per_cu * (w4 ? 1 : 2);
+  int want = per_cu * (w4 ? 1 : 2);
   if (fit > 0 && want > fit) want = fit;
   const int64_t cap = (int64_t)device_cus() * want;
   const int64_t need = (n_groups + kWaves - 1) / kWaves;
@@ -535,7 +456,6 @@ template <bool W4>
 hipError_t launch_w(int R, int pro, int epi, const GemvArgs& a, hipStream_t s, int* b) {
   if (pro == PRO_X && epi == EPI_STORE) return launch_r<W4, PRO_X, EPI_STORE>(R, a, s, b);
   if (pro == PRO_X && epi == EPI_RESID) return launch_r<W4, PRO_X, EPI_RESID>(R, a, s, b);
-  if (pro == PRO_ATTN_MERGE && epi == EPI_RESID) return launch_r<W4, PRO_ATTN_MERGE, EPI_RESID>(R, a, s, b);
   if (pro == PRO_NORM && epi == EPI_STORE) return launch_r<W4, PRO_NORM, EPI_STORE>(R, a, s, b);
   if (pro == PRO_EMBED_NORM && epi == EPI_STORE) return launch_r<W4, PRO_EMBED_NORM, EPI_STORE>(R, a, s, b);
   if (pro == PRO_NORM && epi == EPI_SILU) return launch_r<W4, PRO_NORM, EPI_SILU>(R, a, s, b);

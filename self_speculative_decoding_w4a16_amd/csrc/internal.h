@@ -5,7 +5,7 @@
 
 // ------------------------------------------------------------------ GEMV (batch 1)
 // Prologue: where the input vector x comes from.
-enum GemvPro { PRO_X = 0, PRO_NORM = 1, PRO_EMBED_NORM = 2, PRO_ATTN_MERGE = 3 };
+enum GemvPro { PRO_X = 0, PRO_NORM = 1, PRO_EMBED_NORM = 2 };
 // Epilogue: what is written.
 enum GemvEpi { EPI_STORE = 0, EPI_RESID = 1, EPI_SILU = 2, EPI_LOGITS = 3 };
 
@@ -30,13 +30,6 @@ struct GemvArgs {
   float* part_max;           // EPI_LOGITS: per-block max
   int32_t* part_arg;         // EPI_LOGITS: per-block argmax
   const int32_t* valid;      // optional device flag: skip everything if *valid == 0
-  // PRO_ATTN_MERGE: x = merge of decode-attention partials
-  const float* attn_part;    // [n_kv][splits][G][d + 2]
-  int attn_splits, attn_kpb, n_kv, attn_g;
-  const int32_t* kv_len;
-  int pos_offset;
-  const int32_t* attn_nidx;  // sparse draft: keys = *attn_nidx + pos_offset + 1 (else kv_len + pos_offset + 1)
-  int attn_index_cap;
 };
 
 int gemv_max_blocks(bool w4, int64_t n, int epi);  // blocks of one launch (logits partials)
@@ -75,6 +68,7 @@ struct AttnArgs {
   int m;                // query rows
   int n_q, n_kv, d, cap;
   float theta;
+  const float* rope_cs;  // [m][d/2][2] (cos, sin) of each row's position
   float* part;          // split partials [Hkv][splits][m][G][d + 4]
   int splits;           // grid splits over keys (128 keys each)
   uint16_t* out;        // [m][Hq d]
@@ -86,11 +80,12 @@ struct AttnArgs {
   int index_cap;
 };
 hipError_t launch_rope_append(const AttnArgs& a, hipStream_t s);
-// One query position: RoPE + KV append + per-split partials (m, l, o[d]) in
-// part[kv head][split][group head][d + 2]; the splits are merged by the output
-// projection's prologue (PRO_ATTN_MERGE).
+// One query position (the draft step): RoPE + KV append + per-split partials
+// (m, l, o[d]) in part[kv head][split][group head][d + 4], then a merge of
+// the splits into out [Hq d] (bf16).
 hipError_t launch_decode_attention(const AttnArgs& a, const int32_t* valid, hipStream_t s);
-int decode_attn_keys_per_split();
+int decode_attn_keys_per_split();  // verify rows
+int draft_attn_keys_per_split();   // draft step
 // m query rows at positions kv_len + pos_offset + j (q_rot and the cache already
 // written by rope_append): per-row split partials, then a merge into out.
 hipError_t launch_rows_attention(const AttnArgs& a, hipStream_t s);
@@ -112,8 +107,14 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_kv_rollback(int32_t* kv_len, int32_t* tokens, const int32_t* n_accepted,
                               const int32_t* out_tokens, hipStream_t s);
 hipError_t launch_kv_advance(int32_t* kv_len, int32_t delta, hipStream_t s);
+// Draft step: position check (valid, token_out = -1 when out of range) and
+// the RoPE table (cos, sin) [d/2][2] of position kv_len + step.
 hipError_t launch_pos_guard(const int32_t* kv_len, const int32_t* token_in, int step, int cap,
-                            int vocab, int32_t* valid, int32_t* token_out, hipStream_t s);
+                            int vocab, int32_t* valid, int32_t* token_out, int d, float theta,
+                            float* rope_cs, hipStream_t s);
+// RoPE table [m][d/2][2] of positions kv_len + pos_offset + j.
+hipError_t launch_rope_table(const int32_t* kv_len, int pos_offset, int m, int d, float theta,
+                             float* rope_cs, hipStream_t s);
 
 // ------------------------------------------------------------------ sampling / rejection
 struct SampleWs {

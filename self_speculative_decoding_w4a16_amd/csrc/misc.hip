@@ -77,12 +77,35 @@ __global__ void kv_advance_kernel(int32_t* kv_len, int32_t delta) { *kv_len += d
 
 // valid = (0 <= kv_len + step < cap) and the input token is a vocabulary id;
 // when not, the draft step does nothing but set its output token to -1.
+// RoPE angles of position p, pair i < d/2: p * theta^(-2i/d) in float64,
+// cos and sin stored as float32 (cs[2i], cs[2i+1]).
+__device__ __forceinline__ void rope_angle(int p, int i, int d, float theta, float* cs) {
+  const double inv_freq = exp(-(2.0 * i / d) * log((double)theta));
+  double sd, cd;
+  sincos((double)p * inv_freq, &sd, &cd);
+  cs[2 * i] = (float)cd;
+  cs[2 * i + 1] = (float)sd;
+}
+
+// One draft step's position check, and the RoPE table of its position that
+// every layer's attention uses: d/2 threads.
 __global__ void pos_guard_kernel(const int32_t* kv_len, const int32_t* token_in, int step, int cap,
-                                 int vocab, int32_t* valid, int32_t* token_out) {
-  const int pos = *kv_len + step, t = *token_in;
-  const int ok = pos >= 0 && pos < cap && t >= 0 && t < vocab;
-  *valid = ok;
-  if (!ok) *token_out = -1;
+                                 int vocab, int32_t* valid, int32_t* token_out, int d, float theta,
+                                 float* rope_cs) {
+  const int pos = *kv_len + step;
+  if (threadIdx.x < d / 2) rope_angle(pos, threadIdx.x, d, theta, rope_cs);
+  if (threadIdx.x == 0) {
+    const int t = *token_in;
+    const int ok = pos >= 0 && pos < cap && t >= 0 && t < vocab;
+    *valid = ok;
+    if (!ok) *token_out = -1;
+  }
+}
+
+// RoPE table of rows j < m at positions kv_len + pos_offset + j: grid m.
+__global__ void rope_table_kernel(const int32_t* kv_len, int pos_offset, int d, float theta, float* rope_cs) {
+  const int j = blockIdx.x;
+  if (threadIdx.x < d / 2) rope_angle(*kv_len + pos_offset + j, threadIdx.x, d, theta, rope_cs + (int64_t)j * d);
 }
 
 }  // namespace
@@ -121,8 +144,15 @@ hipError_t launch_kv_advance(int32_t* kv_len, int32_t delta, hipStream_t s) {
 }
 
 hipError_t launch_pos_guard(const int32_t* kv_len, const int32_t* token_in, int step, int cap,
-                            int vocab, int32_t* valid, int32_t* token_out, hipStream_t s) {
-  SS_LAUNCH(pos_guard_kernel, dim3(1), dim3(1), 0, s, kv_len, token_in, step, cap, vocab,
-                     valid, token_out);
+                            int vocab, int32_t* valid, int32_t* token_out, int d, float theta,
+                            float* rope_cs, hipStream_t s) {
+  SS_LAUNCH(pos_guard_kernel, dim3(1), dim3(64), 0, s, kv_len, token_in, step, cap, vocab, valid,
+            token_out, d, theta, rope_cs);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(const int32_t* kv_len, int pos_offset, int m, int d, float theta,
+                             float* rope_cs, hipStream_t s) {
+  SS_LAUNCH(rope_table_kernel, dim3(m), dim3(64), 0, s, kv_len, pos_offset, d, theta, rope_cs);
   return hipGetLastError();
 }

@@ -5,6 +5,12 @@ into libsubspec; this class only owns the device buffers and the call order.
 State lives on the device (kv_len, tokens), so a cycle needs no host sync;
 the host reads back the emitted tokens once per cycle.
 
+With ``graphs`` a whole cycle (every kernel of the draft steps, the verify
+pass, the rejection round, the rollback and the index rebuild) is recorded
+once in a HIP graph and replayed: launch arguments are fixed and all state
+lives on the device, so replays need no host work per kernel.  The first
+cycle of each kind runs eagerly (it also warms the library's caches).
+
 With ``sparse`` the draft reads a sparse KV index ("The second ledger of
 speculative decoding", sections 3.1-3.2): every verify writes importance
 scores, and after the rollback the index is rebuilt; the first cycle after
@@ -17,9 +23,9 @@ from . import _lib
 
 class SpecDecoder:
     def __init__(self, model, capacity, gamma, temp=0.0, draft_temp=0.0, max_tokens=64,
-                 device="cuda", sparse=None):
+                 device="cuda", sparse=None, graphs=False):
         """``sparse``: None (dense drafting) or dict(n_sink, n_recent, window,
-        budget_permille)."""
+        budget_permille).  ``graphs``: replay recorded cycles (see above)."""
         s = model.shape
         self.model = model
         self.gamma = gamma
@@ -41,6 +47,13 @@ class SpecDecoder:
         self.probs = torch.zeros((max(gamma, 1), 2), dtype=torch.float32, device=device)
         self.prefill_tokens = torch.zeros(self.max_tokens, dtype=torch.int32, device=device)
         self._zero = torch.zeros(1, dtype=torch.int32, device=device)
+        # fixed homes of a cycle's uniform codes (the recorded graph reads them)
+        self.ud_buf = torch.zeros(max(gamma, 1), dtype=torch.int32, device=device)
+        self.r_buf = torch.zeros(max(gamma, 1), dtype=torch.int32, device=device)
+        self.uf_buf = torch.zeros(1, dtype=torch.int32, device=device)
+        self.use_graphs = graphs
+        self._graphs = {}
+        self._warm = set()
         nbytes = _lib.workspace_bytes(model.c, self.max_tokens, capacity)
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _lib.workspace_init(self.ws)
@@ -122,11 +135,38 @@ class SpecDecoder:
         self._zero.zero_()
         _lib.kv_rollback(self.c, self._zero, self.tokens[1:])
 
-    def cycle(self, u_draft=None, r_codes=None, u_code=None):
-        self.draft(u_draft)
+    def _cycle_body(self, stochastic):
+        self.draft(self.ud_buf if stochastic else None)
         self.verify()
-        self.reject(r_codes, u_code)
+        self.reject(self.r_buf if stochastic else None, self.uf_buf if stochastic else None)
         self.commit()
+
+    def cycle(self, u_draft=None, r_codes=None, u_code=None):
+        """One speculative cycle; uniform codes (device int32) are copied into
+        the decoder's own buffers first."""
+        stochastic = u_draft is not None or r_codes is not None or u_code is not None
+        if stochastic:
+            if u_draft is not None:
+                self.ud_buf[:self.gamma].copy_(u_draft[:self.gamma])
+            if r_codes is not None:
+                self.r_buf[:self.gamma].copy_(r_codes[:self.gamma])
+            if u_code is not None:
+                self.uf_buf.copy_(u_code.reshape(-1)[:1])
+        key = (stochastic, int(self.c.use_index))
+        if not self.use_graphs or key not in self._warm:
+            self._cycle_body(stochastic)
+            self._warm.add(key)
+            return
+        g = self._graphs.get(key)
+        if g is None:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self._cycle_body(stochastic)
+            self.c.use_index = key[1]  # the recorded commit set it on the host
+            self._graphs[key] = g
+        g.replay()
+        if self.sparse:
+            self.c.use_index = 1
 
     def generate(self, prompt, n_generate, uniforms=None, on_cycle=None):
         """Speculative decoding of at least n_generate tokens after ``prompt``.
