@@ -32,8 +32,7 @@
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / SS_WAVE;
+constexpr int kThreads = 256;  // block size; 1024 for long inputs (see launch_one)
 
 // (128 + q_a, 128 + q_b) bf16 pair of nibbles a, a+4 of a code word, dotted
 // with the matching x pair.  `mask` (0x000F000F) sits in an SGPR and `magic`
@@ -154,10 +153,11 @@ __device__ __forceinline__ void put_x(u32x4* smem4, float* xsum, int it, bool ok
   }
 }
 
-template <int R, bool W4, int PRO, int EPI>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int64_t n_groups, uint32_t mask_arg,
+template <int R, bool W4, int PRO, int EPI, int NT>
+__global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, uint32_t mask_arg,
                                                         uint32_t magic_arg) {
   extern __shared__ u32x4 smem4[];
+  constexpr int kWaves = NT / SS_WAVE;
   __shared__ float red[kWaves];
   __shared__ float red_v[kWaves];
   __shared__ int red_i[kWaves];
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int64_t n_gr
   float* xsum = reinterpret_cast<float*>(smem4 + (W4 ? w4_slots(K) : K / 8));
   // items: 8 consecutive values of x (one 16-byte quad); for W4 the four
   // items of a 32-value chunk sit in four consecutive lanes
-  constexpr int NI = 3;  // items per thread held in registers when normalising
+  constexpr int NI = (3 * kThreads + NT - 1) / NT;  // items per thread held when normalising
   const int n_items = K / 8;
   if (PRO != PRO_X) {
     const u32x4* src4 = reinterpret_cast<const u32x4*>(src);
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int64_t n_gr
     float ss = 0.0f;
 #pragma unroll
     for (int t = 0; t < NI; ++t) {
-      const int it = tid + t * kThreads;
+      const int it = tid + t * NT;
       const bool ok = it < n_items;
       hv[t] = ok ? src4[it] : u32x4{0u, 0u, 0u, 0u};
       gv[t] = ok ? g4[it] : u32x4{0u, 0u, 0u, 0u};
@@ -223,12 +223,12 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int64_t n_gr
     for (int i = 0; i < kWaves; ++i) tot += red[i];
     const float inv = 1.0f / sqrtf(tot / (float)K + a.eps);
     if (PRO == PRO_EMBED_NORM && blockIdx.x == 0) {
-      for (int q = tid; q < n_items; q += kThreads) reinterpret_cast<u32x4*>(a.h_out)[q] = src4[q];
+      for (int q = tid; q < n_items; q += NT) reinterpret_cast<u32x4*>(a.h_out)[q] = src4[q];
     }
 #pragma unroll
     for (int t = 0; t < NI; ++t) {
-      const int it = tid + t * kThreads;
-      if (t * kThreads >= n_items) break;  // block-uniform
+      const int it = tid + t * NT;
+      if (t * NT >= n_items) break;  // block-uniform
       const bool ok = it < n_items;
       const uint32_t wv[4] = {hv[t].x, hv[t].y, hv[t].z, hv[t].w};
       const uint32_t gw[4] = {gv[t].x, gv[t].y, gv[t].z, gv[t].w};
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a, int64_t n_gr
     }
   } else {
     const u32x4* src4 = reinterpret_cast<const u32x4*>(src);
-    for (int b0 = 0; b0 < n_items; b0 += kThreads) {  // block-uniform trip count
+    for (int b0 = 0; b0 < n_items; b0 += NT) {  // block-uniform trip count
       const int it = b0 + tid;
       const bool ok = it < n_items;
       const u32x4 v = ok ? src4[it] : u32x4{0u, 0u, 0u, 0u};
@@ -390,12 +390,12 @@ struct Occupancy {
   size_t lds[8];
   int fit[8];
   int n = 0;
-  int get(const void* fn, size_t l) {
+  int get(const void* fn, int threads, size_t l) {
     std::lock_guard<std::mutex> g(mu);
     for (int i = 0; i < n; ++i)
       if (lds[i] == l) return fit[i];
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kThreads, l) != hipSuccess || nb < 1) nb = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, threads, l) != hipSuccess || nb < 1) nb = 1;
     if (n < 8) {
       lds[n] = l;
       fit[n] = nb;
@@ -408,17 +408,18 @@ struct Occupancy {
 // Blocks of a persistent launch: a few per compute unit, no more than fit on
 // a compute unit at once (so the grid runs in one round), fewer when the
 // matrix has fewer row groups.
-int64_t gemv_blocks(int64_t n_groups, bool w4, int pro, int fit) {
+int64_t gemv_blocks(int64_t n_groups, bool w4, int fit, int threads) {
   static int per_cu = -1;
   if (per_cu < 0) {
     const char* e = getenv("SUBSPEC_GEMV_BLOCKS_PER_CU");
     per_cu = e ? atoi(e) : 0;
     if (per_cu <= 0) per_cu = 4;
   }
-  int want = per_cu * (w4 ? 1 : 2);
+  const int waves = threads / SS_WAVE;
+  int want = threads == kThreads ? per_cu * (w4 ? 1 : 2) : 1;
   if (fit > 0 && want > fit) want = fit;
   const int64_t cap = (int64_t)device_cus() * want;
-  const int64_t need = (n_groups + kWaves - 1) / kWaves;
+  const int64_t need = (n_groups + waves - 1) / waves;
   return need < cap ? need : cap;
 }
 
@@ -426,18 +427,30 @@ size_t gemv_lds(bool w4, int64_t k) {
   return w4 ? (size_t)w4_slots((int)k) * 16 + (size_t)(k / 32) * 4 : (size_t)k * 2;
 }
 
-template <int R, bool W4, int PRO, int EPI>
-hipError_t launch_one(const GemvArgs& a, hipStream_t s, int* blocks_out) {
+template <int R, bool W4, int PRO, int EPI, int NT>
+hipError_t launch_nt(const GemvArgs& a, hipStream_t s, int* blocks_out) {
   constexpr int RO = (EPI == EPI_SILU) ? R / 2 : R;
   static Occupancy occ;
   const int64_t n_groups = (a.n + RO - 1) / RO;
   const size_t lds = gemv_lds(W4, a.k);
-  const int fit = occ.get(reinterpret_cast<const void*>(&gemv_kernel<R, W4, PRO, EPI>), lds);
-  const int64_t blocks = gemv_blocks(n_groups, W4, PRO, fit);
+  const int fit = occ.get(reinterpret_cast<const void*>(&gemv_kernel<R, W4, PRO, EPI, NT>), NT, lds);
+  const int64_t blocks = gemv_blocks(n_groups, W4, fit, NT);
   if (blocks_out) *blocks_out = (int)blocks;
-  SS_LAUNCH((gemv_kernel<R, W4, PRO, EPI>), dim3((unsigned)blocks), dim3(kThreads), lds, s, a,
-                     n_groups, 0x000F000Fu, 0x43004300u);
+  SS_LAUNCH((gemv_kernel<R, W4, PRO, EPI, NT>), dim3((unsigned)blocks), dim3(NT), lds, s, a, n_groups,
+            0x000F000Fu, 0x43004300u);
   return hipGetLastError();
+}
+
+// Long inputs (the down projection) use 1024-thread blocks, one per compute
+// unit: x is staged in LDS once per 16 waves instead of once per 4.
+constexpr int64_t kLongK = 8192;
+
+template <int R, bool W4, int PRO, int EPI>
+hipError_t launch_one(const GemvArgs& a, hipStream_t s, int* blocks_out) {
+  if constexpr (PRO == PRO_X && EPI != EPI_LOGITS) {
+    if (a.k > kLongK) return launch_nt<R, W4, PRO, EPI, 1024>(a, s, blocks_out);
+  }
+  return launch_nt<R, W4, PRO, EPI, kThreads>(a, s, blocks_out);
 }
 
 template <bool W4, int PRO, int EPI>
@@ -478,7 +491,7 @@ static int pick_r(int64_t n, int epi) {
 int gemv_max_blocks(bool w4, int64_t n, int epi) {
   const int R = pick_r(n, epi);
   const int RO = (epi == EPI_SILU) ? R / 2 : R;
-  return (int)gemv_blocks((n + RO - 1) / RO, w4, PRO_NORM, 0);
+  return (int)gemv_blocks((n + RO - 1) / RO, w4, 0, kThreads);
 }
 
 hipError_t launch_gemv(bool w4, int pro, int epi, const GemvArgs& a, hipStream_t s, int* blocks_out) {
