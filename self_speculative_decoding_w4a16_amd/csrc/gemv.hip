@@ -130,6 +130,33 @@ __device__ __forceinline__ void row_ptrs(const GemvArgs& a, const int64_t (&prow
   }
 }
 
+// Sums each of a wave's R per-lane row accumulators over the 64 lanes in one
+// butterfly: at xor 32 (and 16 for R = 4) the lanes trade half of their rows,
+// so R rows cost 6 + log2(R) lane swaps instead of 6 R.  Row r's total ends in
+// lanes [64 r / R, 64 (r + 1) / R).  Partners are added in the same xor order
+// as ss::wave_sum, so the sums are bit-identical to it.
+template <int R>
+__device__ __forceinline__ float reduce_rows(const float (&acc)[R], int lane) {
+  if constexpr (R == 4) {
+    const bool hi = lane & 32;
+    const float k0 = (hi ? acc[2] : acc[0]) + __shfl_xor(hi ? acc[0] : acc[2], 32, SS_WAVE);
+    const float k1 = (hi ? acc[3] : acc[1]) + __shfl_xor(hi ? acc[1] : acc[3], 32, SS_WAVE);
+    const bool h16 = lane & 16;
+    float v = (h16 ? k1 : k0) + __shfl_xor(h16 ? k0 : k1, 16, SS_WAVE);
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, SS_WAVE);
+    return v;
+  } else if constexpr (R == 2) {
+    const bool hi = lane & 32;
+    float v = (hi ? acc[1] : acc[0]) + __shfl_xor(hi ? acc[0] : acc[1], 32, SS_WAVE);
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) v += __shfl_xor(v, o, SS_WAVE);
+    return v;
+  } else {
+    return ss::wave_sum(acc[0]);
+  }
+}
+
 // Stores item `it` (x[8it .. 8it+7], bf16) into LDS: as consecutive pairs
 // for bf16 weights; for W4 as the pairs (x0,x4),(x1,x5),(x2,x6),(x3,x7) in
 // slot w4_slot(it/4, it%4), plus the sum of the chunk's 32 values, reduced
@@ -318,22 +345,23 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
     }
 
     if (end_of_group) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) acc[r] = ss::wave_sum(acc[r]);
+      constexpr int LPR = SS_WAVE / R;  // lanes per row after the butterfly
+      const float tot = reduce_rows<R>(acc, lane);
       if (EPI == EPI_SILU) {
+        const float up_tot = __shfl_xor(tot, 32, SS_WAVE);  // up row r + R/2 sits 32 lanes away
 #pragma unroll
         for (int r = 0; r < RO; ++r) {
-          if (lane == r && rv[r]) {
-            const float gt = ss::bf2f(ss::f2bf(acc[r]));
-            const float up = ss::bf2f(ss::f2bf(acc[r + RO]));
+          if (lane == LPR * r && rv[r]) {
+            const float gt = ss::bf2f(ss::f2bf(tot));
+            const float up = ss::bf2f(ss::f2bf(up_tot));
             a.y[out0 + r] = ss::f2bf(gt / (1.0f + expf(-gt)) * up);
           }
         }
       } else {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          if (lane == r && rv[r]) {
-            float v = acc[r];
+          if (lane == LPR * r && rv[r]) {
+            float v = tot;
             if (EPI == EPI_RESID) v = ss::bf2f(a.resid[prow[r]]) + v;
             const uint16_t b = ss::f2bf(v);
             a.y[prow[r]] = b;
