@@ -194,7 +194,9 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
   const int wave = __builtin_amdgcn_readfirstlane(tid / SS_WAVE);  // wave-uniform: rows in SGPRs
   const int K = (int)a.k;
   const int n_units = W4 ? K / 32 : K / 8;  // 16-byte chunks per row
-  constexpr int U = (R >= 4) ? 2 : (R == 2 ? 4 : 8);
+  // 16-byte chunks per lane and row in one step: W4 chunks carry 4x the VALU
+  // work of bf16 chunks, so W4 steps are shorter (better overlap)
+  constexpr int U = W4 ? ((R >= 4) ? 1 : (R == 2 ? 1 : 2)) : ((R >= 4) ? 2 : (R == 2 ? 4 : 8));
   constexpr int RO = (EPI == EPI_SILU) ? R / 2 : R;
   const int64_t wave_stride = (int64_t)gridDim.x * kWaves;
   const uint32_t mask = __builtin_amdgcn_readfirstlane(mask_arg);
