@@ -41,11 +41,9 @@ int ok() {
   } while (0)
 
 constexpr size_t kCounterBytes = 64 * 1024;
-constexpr size_t kGemmCounterOff = 0;           // 4096 slots
 constexpr size_t kSampleCounterOff = 16 * 1024;
 constexpr size_t kRejectCounterOff = 16 * 1024 + 256;
 constexpr size_t kAttnCounterOff = 20 * 1024;  // one per kv head (<= 1024)
-constexpr int kMaxGemmCounters = 4096;
 constexpr int kMaxTokens = 64;
 constexpr int kMaxGemvK = 28672;  // x (2 B) + half-group sums in 64 KiB of LDS
 constexpr int kMaxGamma = 64;
@@ -155,7 +153,6 @@ int check_state(const subspec_model* m, const subspec_state* st) {
 
 // ------------------------------------------------------------------ layouts
 struct FwdWs {
-  uint32_t* gemm_counters;
   uint32_t* sample_counter;
   uint32_t* attn_counters;
   uint16_t *h, *xn, *qkv, *qrot, *attn, *act;
@@ -185,7 +182,6 @@ size_t carve_fwd(const subspec_model* m, int mt, int cap, void* ws, FwdWs* o) {
   Carver c{(char*)ws, 0};
   FwdWs w{};
   char* base = (char*)ws;
-  w.gemm_counters = base ? (uint32_t*)(base + kGemmCounterOff) : nullptr;
   w.sample_counter = base ? (uint32_t*)(base + kSampleCounterOff) : nullptr;
   w.attn_counters = base ? (uint32_t*)(base + kAttnCounterOff) : nullptr;
   c.off = kCounterBytes;
@@ -463,19 +459,35 @@ int subspec_verify(const subspec_model* m, const subspec_state* st, int32_t n_to
     HIPCHK(launch_embed_rows(m->embed, tokens, mt, (int)H, m->vocab, w.h, s));
     HIPCHK(launch_rope_table(st->kv_len, 0, mt, (int)d, m->rope_theta, w.rope_cs, s));
   }
+  // Narrow GEMMs (QKV, O, down) split k over blocks and leave fp32 partial
+  // sums; their consumers add them: RoPE for QKV, the residual + RMSNorm
+  // kernel for O and down (h = bf16(h + sum), then the next norm).
+  const float* pend = nullptr;  // partial sums still to be added to h
+  int pend_splits = 0;
+  auto norm_into_xn = [&](const uint16_t* g) -> hipError_t {
+    const hipError_t e = launch_resid_rmsnorm_rows(w.h, pend, pend_splits, g, m->rms_eps, mt, (int)H, w.xn, s);
+    pend = nullptr;
+    pend_splits = 0;
+    return e;
+  };
   for (int l = 0; l < m->n_layers; ++l) {
     const subspec_layer& L = m->layers[l];
     {
       prof::Scope ps(SUBSPEC_K_MISC, 0.0, s);
-      HIPCHK(launch_rmsnorm_rows(w.h, L.attn_norm, m->rms_eps, mt, (int)H, w.xn, s));
+      HIPCHK(norm_into_xn(L.attn_norm));
     }
-    GemmArgs q{L.qkv.w, qkv, H, w.xn, mt, w.qkv, qkv, nullptr, w.gemm_part, w.gemm_counters};
+    GemmArgs q{L.qkv.w, qkv, H, w.xn, mt, w.qkv, qkv, nullptr, w.gemm_part};
+    int q_splits = 1;
     {
       prof::Scope ps(SUBSPEC_K_GEMM_QKV, gemm_bytes(qkv, H, mt, qkv, false), s);
-      HIPCHK(launch_gemm(GEPI_STORE, q, s));
+      HIPCHK(launch_gemm(GEPI_STORE, q, s, &q_splits));
     }
     AttnArgs at{};
     at.qkv = w.qkv;
+    if (q_splits > 1) {
+      at.qkv_part = w.gemm_part;
+      at.qkv_splits = q_splits;
+    }
     at.q_rot = w.qrot;
     at.k_cache = st->k_cache + (int64_t)l * m->n_kv_heads * st->capacity * d;
     at.v_cache = st->v_cache + (int64_t)l * m->n_kv_heads * st->capacity * d;
@@ -502,35 +514,38 @@ int subspec_verify(const subspec_model* m, const subspec_state* st, int32_t n_to
       HIPCHK(launch_attn_scores(at, st->kv_score + (int64_t)l * m->n_kv_heads * st->capacity,
                                 st->score_window, s));
     }
-    GemmArgs o{L.o.w, H, qd, w.attn, mt, w.h, H, w.h, w.gemm_part, w.gemm_counters};
+    GemmArgs o{L.o.w, H, qd, w.attn, mt, w.h, H, w.h, w.gemm_part};
     {
       prof::Scope ps(SUBSPEC_K_GEMM_O, gemm_bytes(H, qd, mt, H, true), s);
-      HIPCHK(launch_gemm(GEPI_RESID, o, s));
+      HIPCHK(launch_gemm(GEPI_RESID, o, s, &pend_splits));
     }
+    if (pend_splits > 1) pend = w.gemm_part;
     {
       prof::Scope ps(SUBSPEC_K_MISC, 0.0, s);
-      HIPCHK(launch_rmsnorm_rows(w.h, L.ffn_norm, m->rms_eps, mt, (int)H, w.xn, s));
+      HIPCHK(norm_into_xn(L.ffn_norm));
     }
-    GemmArgs g{L.gate_up.w, F, H, w.xn, mt, w.act, F, nullptr, w.gemm_part, w.gemm_counters};
+    GemmArgs g{L.gate_up.w, F, H, w.xn, mt, w.act, F, nullptr, w.gemm_part};
     {
       prof::Scope ps(SUBSPEC_K_GEMM_GATE_UP, gemm_bytes(2 * F, H, mt, F, false), s);
-      HIPCHK(launch_gemm(GEPI_SILU, g, s));
+      HIPCHK(launch_gemm(GEPI_SILU, g, s, nullptr));
     }
-    GemmArgs dn{L.down.w, H, F, w.act, mt, w.h, H, w.h, w.gemm_part, w.gemm_counters};
+    GemmArgs dn{L.down.w, H, F, w.act, mt, w.h, H, w.h, w.gemm_part};
     {
       prof::Scope ps(SUBSPEC_K_GEMM_DOWN, gemm_bytes(H, F, mt, H, true), s);
-      HIPCHK(launch_gemm(GEPI_RESID, dn, s));
+      HIPCHK(launch_gemm(GEPI_RESID, dn, s, &pend_splits));
     }
+    if (pend_splits > 1) pend = w.gemm_part;
   }
   if (logits) {
     {
       prof::Scope ps(SUBSPEC_K_MISC, 0.0, s);
-      HIPCHK(launch_rmsnorm_rows(w.h, m->final_norm, m->rms_eps, mt, (int)H, w.xn, s));
+      HIPCHK(norm_into_xn(m->final_norm));
     }
-    GemmArgs lm{m->lm_head, m->vocab, H, w.xn, mt, logits, m->vocab, nullptr, w.gemm_part,
-                w.gemm_counters};
+    GemmArgs lm{m->lm_head, m->vocab, H, w.xn, mt, logits, m->vocab, nullptr, w.gemm_part};
+    int lm_splits = 1;
     prof::Scope ps(SUBSPEC_K_GEMM_LM_HEAD, gemm_bytes(m->vocab, H, mt, m->vocab, false), s);
-    HIPCHK(launch_gemm(GEPI_STORE, lm, s));
+    HIPCHK(launch_gemm(GEPI_STORE, lm, s, &lm_splits));
+    if (lm_splits > 1) HIPCHK(launch_gemm_reduce(w.gemm_part, lm_splits, mt, m->vocab, logits, m->vocab, s));
   }
   return ok();
 }
@@ -658,14 +673,14 @@ int subspec_bf16_gemm(const uint16_t* w, int64_t n, int64_t k, const uint16_t* x
   if (n < 1 || k < 1) return fail(SUBSPEC_EINVAL, "n and k must be positive");
   if (m < 1 || m > kMaxTokens) return fail(SUBSPEC_EINVAL, "m outside [1, %d]", kMaxTokens);
   if (k % 128 != 0) return fail(SUBSPEC_ESHAPE, "k must be a multiple of 128");
-  if (gemm_counter_slots(n, k, m, GEPI_STORE) > (size_t)kMaxGemmCounters)
-    return fail(SUBSPEC_EUNSUPPORTED, "too many split-k row groups");
   const size_t need = kCounterBytes + align256(gemm_partials_bytes(n, k, m, GEPI_STORE));
   int r;
   if ((r = need_ws(ws, ws_bytes, need))) return r;
-  GemmArgs a{w, n, k, x, m, y, n, nullptr, (float*)((char*)ws + kCounterBytes),
-             (uint32_t*)((char*)ws + kGemmCounterOff)};
-  HIPCHK(launch_gemm(GEPI_STORE, a, hs(stream)));
+  float* part = (float*)((char*)ws + kCounterBytes);
+  GemmArgs a{w, n, k, x, m, y, n, nullptr, part};
+  int splits = 1;
+  HIPCHK(launch_gemm(GEPI_STORE, a, hs(stream), &splits));
+  if (splits > 1) HIPCHK(launch_gemm_reduce(part, splits, m, n, y, n, hs(stream)));
   return ok();
 }
 

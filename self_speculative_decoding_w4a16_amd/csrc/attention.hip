@@ -34,24 +34,30 @@ __global__ __launch_bounds__(64) void rope_append_kernel(AttnArgs a) {
   const int rows = a.n_q + 2 * a.n_kv;
   const uint16_t* src = a.qkv + (int64_t)j * rows * a.d;
   const float c = a.rope_cs[((int64_t)j * half + i) * 2], s = a.rope_cs[((int64_t)j * half + i) * 2 + 1];
+  // projection value of column col of row j: bf16, or bf16 of its split-k partial sums
+  auto val = [&](int col) -> uint16_t {
+    if (!a.qkv_part) return src[col];
+    float v = 0.0f;
+    for (int sp = 0; sp < a.qkv_splits; ++sp) v += a.qkv_part[((int64_t)sp * a.m + j) * rows * a.d + col];
+    return ss::f2bf(v);
+  };
   if (head < a.n_q) {
-    const uint16_t* x = src + head * a.d;
-    const float x1 = ss::bf2f(x[i]), x2 = ss::bf2f(x[i + half]);
+    const int xo = head * a.d;
+    const float x1 = ss::bf2f(val(xo + i)), x2 = ss::bf2f(val(xo + i + half));
     uint16_t* o = a.q_rot + (int64_t)j * a.n_q * a.d + head * a.d;
     o[i] = ss::f2bf(x1 * c - x2 * s);
     o[i + half] = ss::f2bf(x2 * c + x1 * s);
   } else {
     const int hk = head - a.n_q;
     if (pos < 0 || pos >= a.cap) return;
-    const uint16_t* k = src + (a.n_q + hk) * a.d;
-    const uint16_t* v = src + (a.n_q + a.n_kv + hk) * a.d;
-    const float x1 = ss::bf2f(k[i]), x2 = ss::bf2f(k[i + half]);
+    const int ko = (a.n_q + hk) * a.d, vo = (a.n_q + a.n_kv + hk) * a.d;
+    const float x1 = ss::bf2f(val(ko + i)), x2 = ss::bf2f(val(ko + i + half));
     uint16_t* kc = a.k_cache + ((int64_t)hk * a.cap + pos) * a.d;
     uint16_t* vc = a.v_cache + ((int64_t)hk * a.cap + pos) * a.d;
     kc[i] = ss::f2bf(x1 * c - x2 * s);
     kc[i + half] = ss::f2bf(x2 * c + x1 * s);
-    vc[i] = v[i];
-    vc[i + half] = v[i + half];
+    vc[i] = val(vo + i);
+    vc[i + half] = val(vo + i + half);
   }
 }
 

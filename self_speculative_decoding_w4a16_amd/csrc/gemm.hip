@@ -7,237 +7,295 @@
 //
 //  * v_mfma_f32_16x16x32_bf16: A = 16 weight rows x 32 k, B = 32 k x 16
 //    positions, D = 16 rows x 16 positions (lane l holds rows 4(l/16)..+3 of
-//    column l%16).  A block owns RT 16-row tiles and ceil(m/16) position
-//    tiles; its NW waves split k NW ways and add their partial sums through
-//    LDS in a fixed tree (deterministic), then wave 0 runs the epilogue:
-//    store, residual add, or SiLU(gate)*up with the gate tile and the up tile
-//    in the same block.  NW (4, 8 or 16) grows when the matrix has few row
-//    tiles, so that every launch keeps ~16 waves per compute unit streaming.
-//  * Lane (r, g) of MFMA step s feeds k = kb + 32 s + 8 g .. +7 of row r, so
-//    one load instruction reads 64 contiguous bytes of each of 16 rows; the
-//    next step's loads are issued before the current step's MFMAs.
+//    position l%16).
+//  * A block has NW waves (2, or 8 for the very wide lm_head); each wave
+//    owns one 16-row tile and all ceil(m/16) position tiles.  The block walks
+//    its k range in chunks of 128: the activation chunk X[0..16 TT)[kc..+128)
+//    is staged in LDS (double-buffered, one barrier a chunk) and read by all
+//    NW waves; each wave streams its weight rows straight into registers.
+//    Lane (r, g) of MFMA step s feeds k = kc + 32 s + 8 g .. +7 of row r.
+//  * Pipeline: the weights and activations of WD = 3 chunks are in flight per
+//    wave.  Every load in the loop is unconditional (buffer loads: offsets
+//    outside the resource return zeros), so the compiler's count of loads in
+//    flight is exact and each wait covers only the chunk about to be used.
+//    Plain (temporal) loads stream faster here than non-temporal ones.
+//  * Row tiles are few for the narrow matrices (QKV, O, down), so the k range
+//    is also split over `splits` blocks; those write fp32 partial sums
+//    [split][position][n] that the consumer adds in split order (the RoPE
+//    kernel for QKV, the residual + RMSNorm kernel for O and down), so no
+//    extra launch is spent on the reduction.  Otherwise the block runs the
+//    epilogue itself: store, residual add, or SiLU(gate)*up (gate tiles in
+//    the first NW/2 waves, the matching up tiles in the others).
 #include "common.h"
 #include "internal.h"
 #include "profile.h"
 
 namespace {
 
-constexpr int kTargetWaves = 4096;  // ~16 per compute unit
+constexpr int KC = 128;             // k per chunk
+constexpr int KS = KC / 32;         // MFMA steps (k = 32 each) per chunk
+constexpr int WD = 3;               // weight chunks in flight per wave
+constexpr int XROW = KC + 8;        // LDS row stride (bf16) of the staged activations
+constexpr int kTargetBlocks = 512;  // split k until the grid has two blocks per compute unit
+constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 (CDNA): raw 32-bit data
+constexpr int kOutside = 0x40000000;      // byte offset past every resource: loads zeros
 
 struct Plan {
-  int64_t groups;  // blocks
-  int rt;          // 16-row tiles per block
+  int64_t groups;  // row groups (blocks along n)
   int tt;          // position tiles
-  int nw;          // waves per block (k split)
+  int splits;      // k splits (blocks along k)
+  int nw;          // waves per block
 };
 
-Plan make_plan(int64_t n, int64_t /*k*/, int m, int epi) {
+// Waves per block.  Small blocks (2 waves) keep many independent blocks in
+// flight, which streams best; the very wide matrices (lm_head) take 8 so that
+// the activations are not staged again for every 32 rows.
+int block_waves(int64_t n, int epi) { return (n >= 65536 && epi != GEPI_SILU) ? 8 : 2; }
+
+int64_t rows_per_group(int64_t n, int epi) {
+  const int nw = block_waves(n, epi);
+  return epi == GEPI_SILU ? 16 * nw / 2 : 16 * nw;
+}
+
+Plan make_plan(int64_t n, int64_t k, int m, int epi) {
   Plan p;
   p.tt = (m + 15) / 16;
-  if (epi == GEPI_SILU) {
-    p.rt = 2;  // tile 0: 16 gate rows, tile 1: the matching 16 up rows
-    p.groups = (n + 15) / 16;
-  } else {
-    p.rt = (n >= 65536) ? 2 : 1;
-    p.groups = (n + 16 * p.rt - 1) / (16 * p.rt);
-  }
-  p.nw = 4;
-  if (p.groups * 4 < kTargetWaves) p.nw = 8;
-  if (p.groups * 8 < kTargetWaves && p.rt == 1) p.nw = 16;  // LDS: 8 x TT x 1 KiB
+  p.nw = block_waves(n, epi);
+  const int64_t rg = rows_per_group(n, epi);
+  p.groups = (n + rg - 1) / rg;
+  const int chunks = (int)(k / KC);
+  p.splits = 1;
+  if (epi != GEPI_SILU && p.groups < kTargetBlocks)
+    p.splits = (int)std::min<int64_t>(chunks, (kTargetBlocks + p.groups - 1) / p.groups);
   return p;
 }
 
-// k-substeps (MFMAs of k = 32) per pipeline step: fewer when many position
-// tiles are in flight, to bound the registers of the double buffer.
-template <int TT>
-constexpr int ksub() { return TT >= 3 ? 2 : 4; }
-
-template <int RT, int TT, int KS>
-__device__ __forceinline__ void load_step(const u32x4* const (&wp)[RT], const bool (&wv)[RT],
-                                          const u32x4* const (&xp)[TT], const bool (&xv)[TT],
-                                          int o, u32x4 (&av)[RT][KS], u32x4 (&bv)[TT][KS]) {
-#pragma unroll
-  for (int t = 0; t < RT; ++t)
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      av[t][s] = wv[t] ? __builtin_nontemporal_load(wp[t] + o + 4 * s) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int u = 0; u < TT; ++u)
-#pragma unroll
-    for (int s = 0; s < KS; ++s) bv[u][s] = xv[u] ? xp[u][o + 4 * s] : u32x4{0u, 0u, 0u, 0u};
-}
-
-template <int RT, int TT, int KS>
-__device__ __forceinline__ void mma_step(const u32x4 (&av)[RT][KS], const u32x4 (&bv)[TT][KS],
-                                         f32x4_t (&acc)[RT][TT]) {
-#pragma unroll
-  for (int s = 0; s < KS; ++s)
-#pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-      for (int u = 0; u < TT; ++u)
-        acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[t][s]),
-                                                            __builtin_bit_cast(bf16x8_t, bv[u][s]),
-                                                            acc[t][u], 0, 0, 0);
-}
-
-template <int RT, int TT, int EPI, int NW>
-__global__ __launch_bounds__(NW * SS_WAVE) void gemm_kernel(GemmArgs a) {
-  __shared__ f32x4_t red[NW / 2][RT][TT][SS_WAVE];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t grp = blockIdx.x;
-  const int K = (int)a.k;
+template <int NWR, int TT, int EPI>
+__global__ __launch_bounds__(NWR * SS_WAVE) void gemm_kernel(GemmArgs a, int splits) {
+  // staged activation rows: 16 TT positions, rounded up to what one pass of
+  // the block's threads covers (the extra rows are loaded as zeros)
+  constexpr int XPT = (16 * TT * KC / 8 + NWR * SS_WAVE - 1) / (NWR * SS_WAVE);  // 16-byte pieces per thread
+  constexpr int XR = XPT * NWR * SS_WAVE * 8 / KC;
+  __shared__ __align__(16) uint16_t xs[2][XR][XROW];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g4 = lane >> 4;
+  const int K = (int)a.k;
+  const int chunks = K / KC;
+  const int split = blockIdx.y;
+  const int c0 = (int)((int64_t)chunks * split / splits), c1 = (int)((int64_t)chunks * (split + 1) / splits);
 
-  int64_t wrow[RT];
-  bool wvalid[RT];
-  int64_t obase;
+  // this wave's 16 weight rows
+  int64_t row0;  // first physical row of the tile
+  int64_t out0;  // first output column of the tile
   if (EPI == GEPI_SILU) {
-    obase = grp * 16;
-    wvalid[0] = wvalid[RT - 1] = (obase + r16) < a.n;
-    wrow[0] = obase + r16;
-    wrow[RT - 1] = a.n + obase + r16;
+    const int half = NWR / 2;
+    out0 = (int64_t)blockIdx.x * 16 * half + 16 * (wave % half);
+    row0 = (wave < half) ? out0 : a.n + out0;
   } else {
-    obase = grp * 16 * RT;
+    out0 = (int64_t)blockIdx.x * 16 * NWR + 16 * wave;
+    row0 = out0;
+  }
+  // Every load of the main loop is unconditional, so the compiler can count
+  // the loads in flight exactly (a load skipped on one path makes it wait for
+  // all of them).  Both operands are read through buffer resources: an
+  // offset outside the resource loads zeros without touching memory, which
+  // covers rows past n, positions past m and chunks past the block's range.
+  const int rows = (int)std::max<int64_t>(0, std::min<int64_t>(16, a.n - out0));
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.w + row0 * (int64_t)K), 0, rows * K * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x), 0, a.m * K * 2, kBufferWord3);
+  const int wlane = (r16 * K + 8 * g4) * 2;  // byte offset of lane (r, g) in a chunk
+  auto chunk_off = [&](int c) { return c < c1 ? c * KC * 2 : kOutside; };
+
+  // activation staging: thread -> (position, 16 bytes) of the chunk
+  auto load_x = [&](int c, u32x4 (&xr)[XPT]) {
+    const int co = chunk_off(c);
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      wrow[t] = obase + 16 * t + r16;
-      wvalid[t] = wrow[t] < a.n;
+    for (int i = 0; i < XPT; ++i) {
+      const int e = tid + i * NWR * SS_WAVE;
+      const int pos = e / (KC / 8), q = e % (KC / 8);
+      xr[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, pos * K * 2 + 16 * q + co, 0, 0);
     }
+  };
+  auto store_x = [&](const u32x4 (&xr)[XPT], int buf) {
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int e = tid + i * NWR * SS_WAVE;
+      const int pos = e / (KC / 8), q = e % (KC / 8);
+      *reinterpret_cast<u32x4*>(&xs[buf][pos][8 * q]) = xr[i];
+    }
+  };
+  auto load_w = [&](int c, u32x4 (&av)[KS]) {
+    const int off = wlane + chunk_off(c);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) av[s] = __builtin_amdgcn_raw_buffer_load_b128(wrs, off + 64 * s, 0, 0);
+  };
+
+  f32x4_t acc[TT];
+#pragma unroll
+  for (int u = 0; u < TT; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Chunks c .. c + WD - 1 are in flight, each as its activations followed by
+  // its weights, in rings of WD register buffers: chunk c lives in slot
+  // (c - c0) % WD by name (the loop is unrolled by WD; a rotation by register
+  // copies would wait for the loads still in flight).  Loads complete in
+  // issue order, so waiting for the activations of chunk c + 1 (to stage
+  // them in LDS while chunk c is multiplied) also waits for the weights of
+  // chunk c, and for nothing later.
+  u32x4 wb[WD][KS], xb[WD][XPT];
+#pragma unroll
+  for (int j = 0; j < WD; ++j) {
+    load_x(c0 + j, xb[j]);
+    load_w(c0 + j, wb[j]);
   }
-  constexpr int KS = ksub<TT>();
-  constexpr int KSTEP = 32 * KS;
-  const int ksteps = K / KSTEP;
-  const int s0 = (ksteps * wave) / NW, s1 = (ksteps * (wave + 1)) / NW;
-
-  f32x4_t acc[RT][TT];
+  store_x(xb[0], 0);
+  __syncthreads();
+  auto step = [&](int c, u32x4 (&w)[KS], u32x4 (&xc)[XPT], const u32x4 (&xn)[XPT]) {
+    const int buf = (c - c0) & 1;
+    store_x(xn, buf ^ 1);  // chunk c + 1 (zeros past the range)
+    load_x(c + WD, xc);    // chunk c is already in LDS
 #pragma unroll
-  for (int t = 0; t < RT; ++t)
+    for (int s = 0; s < KS; ++s) {
 #pragma unroll
-    for (int u = 0; u < TT; ++u) acc[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const u32x4* wp[RT];
-#pragma unroll
-  for (int t = 0; t < RT; ++t)
-    wp[t] = reinterpret_cast<const u32x4*>(a.w + (wvalid[t] ? wrow[t] : 0) * (int64_t)K) + g4;
-  const u32x4* xp[TT];
-  bool xvalid[TT];
-#pragma unroll
-  for (int u = 0; u < TT; ++u) {
-    const int tok = 16 * u + r16;
-    xvalid[u] = tok < a.m;
-    xp[u] = reinterpret_cast<const u32x4*>(a.x + (int64_t)(xvalid[u] ? tok : 0) * K) + g4;
-  }
-
-  if (s0 < s1) {
-    u32x4 av[RT][KS], bv[TT][KS], an[RT][KS], bn[TT][KS];
-    load_step<RT, TT, KS>(wp, wvalid, xp, xvalid, s0 * (KSTEP / 8), av, bv);
-    for (int st = s0; st < s1; ++st) {
-      const bool more = st + 1 < s1;
-      if (more) load_step<RT, TT, KS>(wp, wvalid, xp, xvalid, (st + 1) * (KSTEP / 8), an, bn);
-      mma_step<RT, TT, KS>(av, bv, acc);
-      if (more) {
-#pragma unroll
-        for (int t = 0; t < RT; ++t)
-#pragma unroll
-          for (int s = 0; s < KS; ++s) av[t][s] = an[t][s];
-#pragma unroll
-        for (int u = 0; u < TT; ++u)
-#pragma unroll
-          for (int s = 0; s < KS; ++s) bv[u][s] = bn[u][s];
+      for (int u = 0; u < TT; ++u) {
+        const u32x4 b = *reinterpret_cast<const u32x4*>(&xs[buf][16 * u + r16][32 * s + 8 * g4]);
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w[s]),
+                                                         __builtin_bit_cast(bf16x8_t, b), acc[u], 0, 0, 0);
       }
     }
+    load_w(c + WD, w);
+    __syncthreads();
+  };
+  int c = c0;
+  for (; c + WD <= c1; c += WD) {
+#pragma unroll
+    for (int j = 0; j < WD; ++j) step(c + j, wb[j], xb[j], xb[(j + 1) % WD]);
   }
+#pragma unroll
+  for (int j = 0; j < WD - 1; ++j)
+    if (c + j < c1) step(c + j, wb[j], xb[j], xb[(j + 1) % WD]);
 
-  // k-split reduction across the block's waves: a fixed tree (waves
-  // [h, 2h) hand their sums to waves [0, h), h = NW/2, ..., 1)
+  // epilogue: lane holds D[row 4 g4 + j][position 16 u + r16]
+  if (EPI == GEPI_SILU) {
+    // up tiles (waves NWR/2..) hand their sums to the gate tiles through LDS
+    float* up = reinterpret_cast<float*>(&xs[0][0][0]);  // [NWR/2][TT][64][4] floats
+    const int half = NWR / 2;
+    if (wave >= half) {
 #pragma unroll
-  for (int h = NW / 2; h >= 1; h >>= 1) {
-    if (wave >= h && wave < 2 * h) {
-#pragma unroll
-      for (int t = 0; t < RT; ++t)
-#pragma unroll
-        for (int u = 0; u < TT; ++u) red[wave - h][t][u][lane] = acc[t][u];
+      for (int u = 0; u < TT; ++u)
+        *reinterpret_cast<f32x4_t*>(&up[(((wave - half) * TT + u) * SS_WAVE + lane) * 4]) = acc[u];
     }
     __syncthreads();
-    if (wave < h) {
+    if (wave >= half) return;
 #pragma unroll
-      for (int t = 0; t < RT; ++t)
+    for (int u = 0; u < TT; ++u) {
+      const int tok = 16 * u + r16;
+      if (tok >= a.m) continue;
+      const f32x4_t uv = *reinterpret_cast<const f32x4_t*>(&up[((wave * TT + u) * SS_WAVE + lane) * 4]);
 #pragma unroll
-        for (int u = 0; u < TT; ++u) acc[t][u] += red[wave][t][u][lane];
+      for (int j = 0; j < 4; ++j) {
+        const int64_t col = out0 + 4 * g4 + j;
+        if (col < a.n) {
+          const float gt = ss::bf2f(ss::f2bf(acc[u][j]));
+          const float upv = ss::bf2f(ss::f2bf(uv[j]));
+          a.y[(int64_t)tok * a.ldy + col] = ss::f2bf(gt / (1.0f + expf(-gt)) * upv);
+        }
+      }
     }
-    __syncthreads();
+    return;
   }
-  if (wave != 0) return;
-
-  // epilogue: lane holds D[row 4*g4 + j][position r16]
 #pragma unroll
   for (int u = 0; u < TT; ++u) {
     const int tok = 16 * u + r16;
     if (tok >= a.m) continue;
-    uint16_t* yrow = a.y + (int64_t)tok * a.ldy;
-    if (EPI == GEPI_SILU) {
+    const int64_t col = out0 + 4 * g4;
+    if (EPI == GEPI_PARTIAL) {
+      float* dst = a.partials + ((int64_t)split * a.m + tok) * a.n + col;
+      if (col + 3 < a.n && (a.n & 3) == 0) {
+        *reinterpret_cast<f32x4_t*>(dst) = acc[u];  // 16-byte aligned: n % 4 == 0, col % 4 == 0
+      } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t col = obase + 4 * g4 + j;
-        if (col < a.n) {
-          const float g = ss::bf2f(ss::f2bf(acc[0][u][j]));
-          const float up = ss::bf2f(ss::f2bf(acc[RT - 1][u][j]));
-          yrow[col] = ss::f2bf(g / (1.0f + expf(-g)) * up);
-        }
+        for (int j = 0; j < 4; ++j)
+          if (col + j < a.n) dst[j] = acc[u][j];
       }
-    } else {
+      continue;
+    }
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t col = obase + 16 * t + 4 * g4 + j;
-          if (col < a.n) {
-            float v = acc[t][u][j];
-            if (EPI == GEPI_RESID) v += ss::bf2f(a.resid[(int64_t)tok * a.ldy + col]);
-            yrow[col] = ss::f2bf(v);
-          }
-        }
+    for (int j = 0; j < 4; ++j) {
+      if (col + j < a.n) {
+        float v = acc[u][j];
+        if (EPI == GEPI_RESID) v += ss::bf2f(a.resid[(int64_t)tok * a.ldy + col + j]);
+        a.y[(int64_t)tok * a.ldy + col + j] = ss::f2bf(v);
       }
     }
   }
 }
 
-template <int RT, int EPI, int NW>
+// Y[t][n] = bf16(sum over splits of the partials), in split order (the
+// kernel-level GEMM entry point; the verify pass reduces in its consumers).
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* part, int splits, int m, int64_t n,
+                                                          uint16_t* y, int64_t ldy) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (int64_t)m * n) return;
+  const int64_t t = e / n, c = e % n;
+  float v = 0.0f;
+  for (int s = 0; s < splits; ++s) v += part[((int64_t)s * m + t) * n + c];
+  y[t * ldy + c] = ss::f2bf(v);
+}
+
+template <int NW, int EPI>
 hipError_t launch_nw(const GemmArgs& a, const Plan& p, hipStream_t s) {
-  const dim3 grid((unsigned)p.groups), block(NW * SS_WAVE);
+  const dim3 grid((unsigned)p.groups, (unsigned)p.splits), block(NW * SS_WAVE);
   switch (p.tt) {
-    case 1: SS_LAUNCH((gemm_kernel<RT, 1, EPI, NW>), grid, block, 0, s, a); break;
-    case 2: SS_LAUNCH((gemm_kernel<RT, 2, EPI, NW>), grid, block, 0, s, a); break;
-    case 3: SS_LAUNCH((gemm_kernel<RT, 3, EPI, NW>), grid, block, 0, s, a); break;
-    case 4: SS_LAUNCH((gemm_kernel<RT, 4, EPI, NW>), grid, block, 0, s, a); break;
+    case 1: SS_LAUNCH((gemm_kernel<NW, 1, EPI>), grid, block, 0, s, a, p.splits); break;
+    case 2: SS_LAUNCH((gemm_kernel<NW, 2, EPI>), grid, block, 0, s, a, p.splits); break;
+    case 3: SS_LAUNCH((gemm_kernel<NW, 3, EPI>), grid, block, 0, s, a, p.splits); break;
+    case 4: SS_LAUNCH((gemm_kernel<NW, 4, EPI>), grid, block, 0, s, a, p.splits); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int RT, int EPI>
+template <int EPI>
 hipError_t launch_tt(const GemmArgs& a, const Plan& p, hipStream_t s) {
-  if constexpr (RT == 1) {
-    if (p.nw == 16) return launch_nw<RT, EPI, 16>(a, p, s);
+  if (p.nw == 2) return launch_nw<2, EPI>(a, p, s);
+  if constexpr (EPI == GEPI_STORE || EPI == GEPI_PARTIAL) {
+    if (p.nw == 8) return launch_nw<8, EPI>(a, p, s);
   }
-  if (p.nw == 8) return launch_nw<RT, EPI, 8>(a, p, s);
-  return launch_nw<RT, EPI, 4>(a, p, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-size_t gemm_partials_bytes(int64_t, int64_t, int, int) { return 0; }
-size_t gemm_counter_slots(int64_t, int64_t, int, int) { return 0; }
+int gemm_splits(int64_t n, int64_t k, int m, int epi) { return make_plan(n, k, m, epi).splits; }
 
-hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s) {
-  Plan p = make_plan(a.n, a.k, a.m, epi);
+size_t gemm_partials_bytes(int64_t n, int64_t k, int m, int epi) {
+  const Plan p = make_plan(n, k, m, epi);
+  return p.splits > 1 ? (size_t)p.splits * m * n * 4 : 0;
+}
+
+hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s, int* splits_out) {
+  const Plan p = make_plan(a.n, a.k, a.m, epi);
+  if (splits_out) *splits_out = p.splits;
+  if (p.splits > 1) {
+    // the caller reduces a.partials [splits][m][n]
+    if (epi == GEPI_SILU || !a.partials) return hipErrorInvalidValue;
+    return launch_tt<GEPI_PARTIAL>(a, p, s);
+  }
   switch (epi) {
-    case GEPI_STORE:
-      return p.rt == 2 ? launch_tt<2, GEPI_STORE>(a, p, s) : launch_tt<1, GEPI_STORE>(a, p, s);
-    case GEPI_RESID:
-      return p.rt == 2 ? launch_tt<2, GEPI_RESID>(a, p, s) : launch_tt<1, GEPI_RESID>(a, p, s);
-    case GEPI_SILU: return launch_tt<2, GEPI_SILU>(a, p, s);
+    case GEPI_STORE: return launch_tt<GEPI_STORE>(a, p, s);
+    case GEPI_RESID: return launch_tt<GEPI_RESID>(a, p, s);
+    case GEPI_SILU: return launch_tt<GEPI_SILU>(a, p, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_reduce(const float* part, int splits, int m, int64_t n, uint16_t* y, int64_t ldy,
+                              hipStream_t s) {
+  const int64_t total = (int64_t)m * n;
+  SS_LAUNCH(gemm_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, part, splits, m, n, y,
+            ldy);
+  return hipGetLastError();
 }

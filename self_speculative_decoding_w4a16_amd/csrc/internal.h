@@ -36,7 +36,8 @@ int gemv_max_blocks(bool w4, int64_t n, int epi);  // blocks of one launch (logi
 hipError_t launch_gemv(bool w4, int pro, int epi, const GemvArgs& a, hipStream_t s, int* blocks_out);
 
 // ------------------------------------------------------------------ GEMM (verify)
-enum GemmEpi { GEPI_STORE = 0, GEPI_RESID = 1, GEPI_SILU = 2 };
+// GEPI_PARTIAL: fp32 partial sums [split][m][n] for the caller to reduce
+enum GemmEpi { GEPI_STORE = 0, GEPI_RESID = 1, GEPI_SILU = 2, GEPI_PARTIAL = 3 };
 struct GemmArgs {
   const uint16_t* w;  // bf16 [N][K]
   int64_t n;          // output columns (F in GEPI_SILU mode)
@@ -46,12 +47,17 @@ struct GemmArgs {
   uint16_t* y;        // bf16 [m][ldy]
   int64_t ldy;
   const uint16_t* resid;  // GEPI_RESID: [m][ldy]
-  float* partials;        // split-K scratch
-  uint32_t* counters;     // split-K arrival counters (zero, self-resetting)
+  float* partials;        // split-k partial sums [splits][m][n] (when splits > 1)
 };
+// k splits the GEMM of this shape uses (1: the epilogue runs in the kernel).
+int gemm_splits(int64_t n, int64_t k, int m, int epi);
 size_t gemm_partials_bytes(int64_t n, int64_t k, int m, int epi);
-size_t gemm_counter_slots(int64_t n, int64_t k, int m, int epi);
-hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s);
+// Launches the GEMM; with more than one split it writes a.partials instead
+// of running `epi`, and the caller reduces them (splits in *splits_out).
+hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s, int* splits_out);
+// y[t][c] = bf16(sum over splits of part[s][t][c]), splits in order.
+hipError_t launch_gemm_reduce(const float* part, int splits, int m, int64_t n, uint16_t* y, int64_t ldy,
+                              hipStream_t s);
 
 // ------------------------------------------------------------------ quantise
 hipError_t launch_w4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
@@ -60,6 +66,8 @@ hipError_t launch_w4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* 
 // ------------------------------------------------------------------ attention
 struct AttnArgs {
   const uint16_t* qkv;  // [m][(Hq+2Hkv) d] raw projections (pre-RoPE)
+  const float* qkv_part;  // or, when set: their fp32 partial sums [qkv_splits][m][(Hq+2Hkv) d]
+  int qkv_splits;
   uint16_t* q_rot;      // [m][Hq d] rotated queries (bf16)
   uint16_t* k_cache;    // [Hkv][cap][d] of this layer
   uint16_t* v_cache;
@@ -101,6 +109,10 @@ hipError_t launch_kv_select(const float* score, int cap, const int32_t* kv_len, 
 // ------------------------------------------------------------------ misc kernels
 hipError_t launch_rmsnorm_rows(const uint16_t* h, const uint16_t* g, float eps, int rows, int k,
                                uint16_t* out, hipStream_t s);
+// h[r] = bf16(h[r] + sum over splits of part[s][r]) in place (splits in
+// order; skipped when part is null), then out[r] = RMSNorm(h[r]) * g.  k <= 6144.
+hipError_t launch_resid_rmsnorm_rows(uint16_t* h, const float* part, int splits, const uint16_t* g, float eps,
+                                     int rows, int k, uint16_t* out, hipStream_t s);
 hipError_t launch_embed_rows(const uint16_t* embed, const int32_t* tokens, int rows, int k,
                              int vocab, uint16_t* h, hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);

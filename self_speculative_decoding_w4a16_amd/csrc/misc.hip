@@ -8,21 +8,50 @@
 
 namespace {
 
-__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t* __restrict__ h,
-                                                           const uint16_t* __restrict__ g,
-                                                           float eps, int k,
-                                                           uint16_t* __restrict__ out) {
+// Row RMSNorm, optionally after adding fp32 partial sums to the row first:
+// h = bf16(h + sum_s part[s]) (split order, written back), then
+// out = bf16(h / sqrt(mean(h^2) + eps) * g).  One block (256 threads) per row,
+// the row held in registers (k <= 3 * 256 * 8).
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(uint16_t* __restrict__ h,
+                                                           const float* __restrict__ part, int splits,
+                                                           int rows, const uint16_t* __restrict__ g,
+                                                           float eps, int k, uint16_t* __restrict__ out) {
+  constexpr int NI = 3;
   __shared__ float red[4];
   __shared__ float s_inv;
   const int row = blockIdx.x, tid = threadIdx.x;
-  const uint16_t* x = h + (int64_t)row * k;
+  uint16_t* x = h + (int64_t)row * k;
+  const int items = k / 8;
+  u32x4 hv[NI];
   float ss = 0.0f;
-  for (int q = tid; q < k / 8; q += 256) {
+#pragma unroll
+  for (int t = 0; t < NI; ++t) {
+    const int q = tid + 256 * t;
+    if (q >= items) continue;
     u32x4 v = reinterpret_cast<const u32x4*>(x)[q];
-    uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+    if (part) {
+      float add[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int sp = 0; sp < splits; ++sp) {
+        const f32x4_t* p = reinterpret_cast<const f32x4_t*>(part + ((int64_t)sp * rows + row) * k + 8 * q);
+        const f32x4_t a0 = p[0], a1 = p[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          add[i] += a0[i];
+          add[4 + i] += a1[i];
+        }
+      }
+      uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        wv[i] = ss::pack_bf(ss::f2bf(ss::lo_bf(wv[i]) + add[2 * i]), ss::f2bf(ss::hi_bf(wv[i]) + add[2 * i + 1]));
+      v = u32x4{wv[0], wv[1], wv[2], wv[3]};
+      reinterpret_cast<u32x4*>(x)[q] = v;
+    }
+    hv[t] = v;
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float lo = ss::lo_bf(wv[i]), hi = ss::hi_bf(wv[i]);
+      const float lo = ss::lo_bf(wv[i]), hi = ss::hi_bf(wv[i]);
       ss += lo * lo;
       ss += hi * hi;
     }
@@ -34,15 +63,18 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t* __res
   __syncthreads();
   const float inv = s_inv;
   uint16_t* o = out + (int64_t)row * k;
-  for (int q = tid; q < k / 8; q += 256) {
-    u32x4 v = reinterpret_cast<const u32x4*>(x)[q];
-    u32x4 gv = reinterpret_cast<const u32x4*>(g)[q];
-    uint32_t wv[4] = {v.x, v.y, v.z, v.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+  for (int t = 0; t < NI; ++t) {
+    const int q = tid + 256 * t;
+    if (q >= items) continue;
+    const u32x4 v = hv[t];
+    const u32x4 gv = reinterpret_cast<const u32x4*>(g)[q];
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
     uint32_t ow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint16_t lo = ss::f2bf(ss::lo_bf(wv[i]) * inv * ss::lo_bf(gw[i]));
-      uint16_t hi = ss::f2bf(ss::hi_bf(wv[i]) * inv * ss::hi_bf(gw[i]));
+      const uint16_t lo = ss::f2bf(ss::lo_bf(wv[i]) * inv * ss::lo_bf(gw[i]));
+      const uint16_t hi = ss::f2bf(ss::hi_bf(wv[i]) * inv * ss::hi_bf(gw[i]));
       ow[i] = ss::pack_bf(lo, hi);
     }
     reinterpret_cast<u32x4*>(o)[q] = u32x4{ow[0], ow[1], ow[2], ow[3]};
@@ -112,7 +144,16 @@ __global__ void rope_table_kernel(const int32_t* kv_len, int pos_offset, int d, 
 
 hipError_t launch_rmsnorm_rows(const uint16_t* h, const uint16_t* g, float eps, int rows, int k,
                                uint16_t* out, hipStream_t s) {
-  SS_LAUNCH(rmsnorm_rows_kernel, dim3(rows), dim3(256), 0, s, h, g, eps, k, out);
+  if (k > 3 * 256 * 8 || k % 8 != 0) return hipErrorInvalidValue;
+  SS_LAUNCH(rmsnorm_rows_kernel, dim3(rows), dim3(256), 0, s, const_cast<uint16_t*>(h), (const float*)nullptr, 0,
+            rows, g, eps, k, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_resid_rmsnorm_rows(uint16_t* h, const float* part, int splits, const uint16_t* g, float eps,
+                                     int rows, int k, uint16_t* out, hipStream_t s) {
+  if (k > 3 * 256 * 8 || k % 8 != 0) return hipErrorInvalidValue;
+  SS_LAUNCH(rmsnorm_rows_kernel, dim3(rows), dim3(256), 0, s, h, part, splits, rows, g, eps, k, out);
   return hipGetLastError();
 }
 
