@@ -215,6 +215,10 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
   int base = 0;  // wave-uniform first unit of the current step
   Step<R, U, W4> cur;
   load_step<R, U, W4>(cur, wp, mp, base, lane, n_units);
+  // residual inputs of the group's rows, loaded with its first weights
+  float rres[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rres[r] = (EPI == EPI_RESID) ? ss::bf2f(a.resid[prow[r]]) : 0.0f;
 
   // ------------------------------------------------ prologue: x (and group sums) in LDS
   const uint16_t* src = a.x;
@@ -270,19 +274,30 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
       put_x<W4>(smem4, xsum, it, ok, xb);
     }
   } else {
+    // up to XB items per thread are loaded together (one memory latency for
+    // x up to 8 XB NT values), then stored
+    constexpr int XB = 4;
     const u32x4* src4 = reinterpret_cast<const u32x4*>(src);
-    for (int b0 = 0; b0 < n_items; b0 += NT) {  // block-uniform trip count
-      const int it = b0 + tid;
-      const bool ok = it < n_items;
-      const u32x4 v = ok ? src4[it] : u32x4{0u, 0u, 0u, 0u};
-      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-      uint16_t xb[8];
+    for (int b0 = 0; b0 < n_items; b0 += XB * NT) {  // block-uniform trip count
+      u32x4 v[XB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xb[2 * i] = (uint16_t)(wv[i] & 0xffffu);
-        xb[2 * i + 1] = (uint16_t)(wv[i] >> 16);
+      for (int t = 0; t < XB; ++t) {
+        const int it = b0 + t * NT + tid;
+        v[t] = it < n_items ? src4[it] : u32x4{0u, 0u, 0u, 0u};
       }
-      put_x<W4>(smem4, xsum, it, ok, xb);
+#pragma unroll
+      for (int t = 0; t < XB; ++t) {
+        if (b0 + t * NT >= n_items) break;  // block-uniform
+        const int it = b0 + t * NT + tid;
+        const uint32_t wv[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+        uint16_t xb[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xb[2 * i] = (uint16_t)(wv[i] & 0xffffu);
+          xb[2 * i + 1] = (uint16_t)(wv[i] >> 16);
+        }
+        put_x<W4>(smem4, xsum, it, it < n_items, xb);
+      }
     }
   }
   __syncthreads();
@@ -302,18 +317,23 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
     bool rv1[R];
     g_u32x4* wp1[R];
     g_u32* mp1[R];
+    float rres1[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       prow1[r] = prow[r];
       rv1[r] = rv[r];
       wp1[r] = wp[r];
       mp1[r] = mp[r];
+      rres1[r] = rres[r];
     }
     if (end_of_group) {
       g1 = g + wave_stride;
       base1 = 0;
       group_rows<R, EPI>(g1 < n_groups ? g1 : 0, a.n, prow1, rv1, out1);
       row_ptrs<R, W4>(a, prow1, K, wp1, mp1);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (EPI == EPI_RESID) rres1[r] = ss::bf2f(a.resid[prow1[r]]);
     }
     Step<R, U, W4> nxt;
     if (g1 < n_groups) load_step<R, U, W4>(nxt, wp1, mp1, base1, lane, n_units);
@@ -364,7 +384,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
         for (int r = 0; r < R; ++r) {
           if (lane == LPR * r && rv[r]) {
             float v = tot;
-            if (EPI == EPI_RESID) v = ss::bf2f(a.resid[prow[r]]) + v;
+            if (EPI == EPI_RESID) v = rres[r] + v;
             const uint16_t b = ss::f2bf(v);
             a.y[prow[r]] = b;
             if (EPI == EPI_LOGITS) best = ss::better(best, ss::ArgMax{ss::bf2f(b), (int)prow[r]});
@@ -383,6 +403,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
       rv[r] = rv1[r];
       wp[r] = wp1[r];
       mp[r] = mp1[r];
+      rres[r] = rres1[r];
     }
     cur = nxt;
   }
