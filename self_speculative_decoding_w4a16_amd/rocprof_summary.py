@@ -4,35 +4,60 @@ Usage: python -m self_speculative_decoding_w4a16_amd.rocprof_summary DIR [TOP]
 
 Prints one row per kernel (calls, total ms, average / min / max microseconds,
 share of GPU time), with the library's template kernels named by the launch
-site they serve (for example ``gemv_kernel<4, false, 1, 2>`` is the bf16
-gate/up GEMV with the RMSNorm prologue and the SiLU*up epilogue).
+site they serve (for example ``gemv_kernel<4, false, 1, 2, 256>`` is the bf16
+gate/up GEMV with the RMSNorm prologue and the SiLU*up epilogue, 256-thread
+blocks; ``gemm_kernel<2, 2, 3>`` the verify GEMM with 2-wave blocks, up to 32
+positions, writing split-k partial sums).
 """
 import csv
 import glob
 import re
 import sys
 
-_PRO = {0: "x", 1: "norm", 2: "embed+norm", 3: "attn-merge"}
+_PRO = {0: "x", 1: "norm", 2: "embed+norm"}
 _EPI = {0: "store", 1: "resid", 2: "silu*up", 3: "logits"}
-_GEPI = {0: "store", 1: "resid", 2: "silu*up"}
+_GEPI = {0: "store", 1: "resid", 2: "silu*up", 3: "split-k partials"}
 
 
 def describe(name):
     """Short name and launch role of one kernel symbol."""
-    m = re.search(r"gemv_kernel<(\d+), (true|false), (\d+), (\d+)>", name)
+    m = re.search(r"gemv_kernel<(\d+), (true|false), (\d+), (\d+)(?:, (\d+))?>", name)
     if m:
         r, w4, pro, epi = int(m[1]), m[2] == "true", int(m[3]), int(m[4])
-        return (f"gemv_kernel<{r},{m[2]},{pro},{epi}>",
-                f"{'W4' if w4 else 'bf16'} GEMV, {r} rows/wave, {_PRO[pro]} -> {_EPI[epi]}")
+        nt = f",{m[5]}" if m[5] else ""
+        return (f"gemv_kernel<{r},{m[2]},{pro},{epi}{nt}>",
+                f"{'W4' if w4 else 'bf16'} GEMV, {r} rows/wave, {_PRO.get(pro, pro)} -> {_EPI.get(epi, epi)}")
     m = re.search(r"gemm_kernel<(\d+), (\d+), (\d+)>", name)
     if m:
-        rt, tt, epi = int(m[1]), int(m[2]), int(m[3])
-        return (f"gemm_kernel<{rt},{tt},{epi}>",
-                f"MFMA GEMM, {16 * rt} rows x <= {16 * tt} positions, {_GEPI[epi]}")
+        nw, tt, epi = int(m[1]), int(m[2]), int(m[3])
+        return (f"gemm_kernel<{nw},{tt},{epi}>",
+                f"MFMA GEMM, {nw}-wave blocks, <= {16 * tt} positions, {_GEPI.get(epi, epi)}")
     short = name.replace("(anonymous namespace)::", "")
     short = re.sub(r"\(.*$", "", short)
     short = re.sub(r"^void ", "", short)
-    return short[:60], ""
+    base = re.sub(r"<.*$", "", short)
+    return short[:60], _ROLES.get(base, "")
+
+
+_ROLES = {
+    "draft_attn_kernel": "draft attention: RoPE, KV append, 64-key split partials",
+    "draft_merge_kernel": "draft attention: merge of the split partials",
+    "rows_attn_kernel": "verify attention: per-row split partials",
+    "rows_merge_kernel": "verify attention: merge of the split partials",
+    "rope_append_kernel": "verify RoPE + KV append (sums QKV split-k partials)",
+    "rmsnorm_rows_kernel": "verify residual add of split-k partials + RMSNorm",
+    "gemm_reduce_kernel": "lm_head split-k reduction",
+    "sample_kernel": "draft token sampling (argmax / exact inverse CDF)",
+    "pos_guard_kernel": "draft step position check + RoPE table",
+    "rope_table_kernel": "verify RoPE table",
+    "rej_rowmax_kernel": "rejection: per-row max / argmax",
+    "rej_decide_kernel": "rejection: exact accept / resample decision",
+    "kv_rollback_kernel": "KV rollback (kv_len += accepted + 1)",
+    "embed_rows_kernel": "verify embedding gather",
+    "attn_scores_kernel": "sparse draft: importance scores",
+    "kv_select_kernel": "sparse draft: index rebuild (radix select)",
+    "w4_quantize_kernel": "W4 g64 quantiser",
+}
 
 
 def load(path):
