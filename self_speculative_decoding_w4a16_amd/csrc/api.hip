@@ -366,6 +366,9 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
       // slots: n_index + step + 1 <= min(index_cap + gamma_max, capacity)
       at.splits = std::min(at.splits, (st->index_cap + st->gamma_max + kpb - 1) / kpb);
     }
+    // keys of this launch: at most the capacity (dense), or the index plus the
+    // speculative positions (sparse)
+    at.max_keys = sparse ? std::min(st->capacity, st->index_cap + st->gamma_max) : st->capacity;
     {
       prof::Scope ps(SUBSPEC_K_ATTN_DRAFT, 0.0, s);
       HIPCHK(launch_decode_attention(at, w.valid, s));

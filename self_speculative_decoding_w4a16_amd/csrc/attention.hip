@@ -425,6 +425,210 @@ __global__ __launch_bounds__(256) void draft_attn_kernel(AttnArgs a, const int32
   }
 }
 
+// Draft-step attention with one block per query head (short contexts: no
+// split partials, no merge launch): 512 threads = 8 waves; wave w takes the
+// 16-key chunks w, w + 8, ...  Lane (key kl = lane / 4, quarter kq = lane % 4)
+// holds, for i = 0..3, dims 32 i + 8 kq .. +7 of its key's K and V rows (each
+// load instruction reads 64 contiguous bytes of 16 keys), so a score is the
+// lane's partial dot summed over its quad (two in-register DPP swaps).  Every
+// lane keeps its own running softmax (m, l) and output partial o[32] over the
+// keys it sees; lanes and waves are combined once at the end.  Loads run 3
+// chunks ahead in a ring named statically.  Every block of a kv head rotates
+// the new key itself (its score needs it); the group's first block appends
+// the new K/V to the cache (the others never read that slot from memory).
+constexpr int DQW = 8;            // waves
+constexpr int DQR = 3;            // chunks in flight per wave
+constexpr int DQ_MAXKEYS = 2048;  // keys up to which the per-head kernel is used
+
+// v summed (or maxed) over the lanes of a quad / of the lanes 4 apart in a row
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp<0xB1>(v);  // quad_perm [1,0,3,2]
+  return v + dpp<0x4E>(v);  // quad_perm [2,3,0,1]
+}
+
+__global__ __launch_bounds__(DQW * 64) void draft_attn_head_kernel(AttnArgs a, const int32_t* valid) {
+  constexpr int KW = 16;
+  constexpr int NP = DQW * 4;  // partials: 4 rows of 16 lanes per wave
+  __shared__ __align__(16) uint32_t qp[D / 2];    // rotated query, bf16 pairs
+  __shared__ __align__(16) uint32_t knew[D / 2];  // rotated new key
+  __shared__ __align__(16) uint32_t vnew[D / 2];
+  __shared__ float pm[NP], pl[NP], pf[NP];
+  __shared__ float po[NP][D];
+
+  const int vflag = valid ? *valid : 1;
+  const int hq = blockIdx.x, tid = threadIdx.x;
+  const int G = a.n_q / a.n_kv, hk = hq / G;
+  const int lane = tid & 63, wave = tid >> 6;
+  const DraftKeys ks = draft_keys(a, hk);
+  if (vflag == 0 || ks.pos < 0 || ks.pos >= a.cap) return;
+  auto slot_pos = [&](int t) {
+    if (!ks.ilist) return t;
+    const int ti = min(t, max(ks.n_idx - 1, 0));
+    const int ip = min(max(ks.ilist[ti], 0), a.cap - 1);
+    return t < ks.n_idx ? ip : ks.kv0 + (t - ks.n_idx);
+  };
+  const uint16_t* kc = a.k_cache + (int64_t)hk * a.cap * D;
+  const uint16_t* vc = a.v_cache + (int64_t)hk * a.cap * D;
+  const int kq = lane & 3, kl = lane >> 2;
+  const int last = ks.n_keys - 1;  // slot of the new key
+  const int n_chunks = (ks.n_keys + KW - 1) / KW;
+
+  // chunk loads: slots past the end (or the new key) read slot 0 and are masked
+  struct Chunk {
+    u32x4 k[4], v[4];
+  };
+  auto load_chunk = [&](int c, Chunk& b) {
+    const int t = c * KW + kl;
+    const int64_t row = (int64_t)slot_pos(t < last ? t : 0) * D;
+    const u32x4* kp = reinterpret_cast<const u32x4*>(kc + row) + kq;
+    const u32x4* vp = reinterpret_cast<const u32x4*>(vc + row) + kq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b.k[i] = kp[4 * i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b.v[i] = vp[4 * i];
+  };
+  Chunk ring[DQR];
+#pragma unroll
+  for (int j = 0; j < DQR; ++j) {
+    const int c = wave + j * DQW;
+    load_chunk(c < n_chunks ? c : 0, ring[j]);
+  }
+
+  // ---- RoPE of the query (threads 0-63) and the new key (64-127); new V (128-191)
+  if (tid < 128) {
+    const int i2 = tid & 63;  // pair (2 i2, 2 i2 + 1) of each half
+    const bool is_q = tid < 64;
+    const uint16_t* x = is_q ? a.qkv + (int64_t)hq * D : a.qkv + (int64_t)(a.n_q + hk) * D;
+    const int half = D / 2;
+    if (i2 < half / 2) {
+      const uint32_t xlo = reinterpret_cast<const uint32_t*>(x)[i2];
+      const uint32_t xhi = reinterpret_cast<const uint32_t*>(x + half)[i2];
+      const f32x4_t cs = reinterpret_cast<const f32x4_t*>(a.rope_cs)[i2];
+      const float a1 = ss::lo_bf(xlo), b1 = ss::hi_bf(xlo);
+      const float a2 = ss::lo_bf(xhi), b2 = ss::hi_bf(xhi);
+      const uint32_t lo = ss::pack_bf(ss::f2bf(a1 * cs[0] - a2 * cs[1]), ss::f2bf(b1 * cs[2] - b2 * cs[3]));
+      const uint32_t hi = ss::pack_bf(ss::f2bf(a2 * cs[0] + a1 * cs[1]), ss::f2bf(b2 * cs[2] + b1 * cs[3]));
+      uint32_t* dst = is_q ? qp : knew;
+      dst[i2] = lo;
+      dst[half / 2 + i2] = hi;
+      if (!is_q && hq % G == 0) {
+        uint32_t* kdst = reinterpret_cast<uint32_t*>(a.k_cache + ((int64_t)hk * a.cap + ks.pos) * D);
+        kdst[i2] = lo;
+        kdst[half / 2 + i2] = hi;
+      }
+    }
+  } else if (tid < 192) {
+    const int i = tid - 128;
+    const uint32_t v = reinterpret_cast<const uint32_t*>(a.qkv + (int64_t)(a.n_q + a.n_kv + hk) * D)[i];
+    vnew[i] = v;
+    if (hq % G == 0) reinterpret_cast<uint32_t*>(a.v_cache + ((int64_t)hk * a.cap + ks.pos) * D)[i] = v;
+  }
+  __syncthreads();
+
+  const float scale = 0.088388347648318440f;  // 1/sqrt(128)
+  u32x4 q4[4], kn4[4], vn4[4];  // this lane's dims of q and of the new K/V
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    q4[i] = reinterpret_cast<const u32x4*>(qp)[4 * i + kq];
+    kn4[i] = reinterpret_cast<const u32x4*>(knew)[4 * i + kq];
+    vn4[i] = reinterpret_cast<const u32x4*>(vnew)[4 * i + kq];
+  }
+  float m = -INFINITY, l = 0.0f, o[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) o[j] = 0.0f;
+
+  // consume chunk c from its buffer
+  auto step = [&](int c, const Chunk& b) {
+    const int t = c * KW + kl;
+    const bool kin = t < ks.n_keys, is_new = t == last;
+    float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 k4 = is_new ? kn4[i] : b.k[i];
+      d0 = ss::dot2(k4.x, q4[i].x, d0);
+      d1 = ss::dot2(k4.y, q4[i].y, d1);
+      d0 = ss::dot2(k4.z, q4[i].z, d0);
+      d1 = ss::dot2(k4.w, q4[i].w, d1);
+    }
+    const float sc = quad_sum(d0 + d1) * scale;
+    const float mn = kin ? fmaxf(m, sc) : m;
+    const float r = (mn == m) ? 1.0f : expf(m - mn);  // m = -inf: r = 0
+    const float p = kin ? expf(sc - mn) : 0.0f;
+    l = l * r + p;
+    m = mn;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 v4 = is_new ? vn4[i] : b.v[i];
+      const uint32_t w[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[8 * i + 2 * e] = o[8 * i + 2 * e] * r + p * ss::lo_bf(w[e]);
+        o[8 * i + 2 * e + 1] = o[8 * i + 2 * e + 1] * r + p * ss::hi_bf(w[e]);
+      }
+    }
+  };
+  // each buffer is refilled with chunk c + DQR * DQW right after use; the last
+  // pass may run past the wave's chunks: those are skipped, their loads (of
+  // chunk 0) still issued, so the loads in flight are the same on every path
+  for (int c = wave; c < n_chunks; c += DQR * DQW) {
+#pragma unroll
+    for (int j = 0; j < DQR; ++j) {
+      const int cj = c + j * DQW, cn = cj + DQR * DQW;
+      if (j == 0 || cj < n_chunks) step(cj, ring[j]);
+      load_chunk(cn < n_chunks ? cn : 0, ring[j]);
+    }
+  }
+
+  // ---- lanes 4 apart in a row (same quarter) combine: max, rescale, sum
+  float mr = fmaxf(m, dpp<0x124>(m));  // row_ror:4
+  mr = fmaxf(mr, dpp<0x128>(mr));      // row_ror:8
+  const float f = (m == -INFINITY) ? 0.0f : expf(m - mr);
+  l *= f;
+  l += dpp<0x124>(l);
+  l += dpp<0x128>(l);
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    float v = o[j] * f;
+    v += dpp<0x124>(v);
+    v += dpp<0x128>(v);
+    o[j] = v;
+  }
+  // lanes 0-3 of each row hold the row's partial for their quarter
+  const int row = lane >> 4, pidx = wave * 4 + row;
+  if ((lane & 15) < 4) {
+    if (kq == 0) {
+      pm[pidx] = mr;
+      pl[pidx] = l;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) po[pidx][32 * i + 8 * kq + j] = o[8 * i + j];
+  }
+  __syncthreads();
+  // ---- combine the partials (rows that saw no key have m = -inf)
+  if (tid < NP) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < NP; ++q) M = fmaxf(M, pm[q]);
+    pf[tid] = (pm[tid] == -INFINITY) ? 0.0f : expf(pm[tid] - M);
+  }
+  __syncthreads();
+  if (tid < D) {
+    float L = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      L += pf[q] * pl[q];
+      O += pf[q] * po[q][tid];
+    }
+    a.out[(int64_t)hq * D + tid] = ss::f2bf(O / L);
+  }
+}
+
 // Merge of the draft step's split partials: grid (q head), 128 threads (one
 // per dim); splits in order, 8 independent loads at a time.  Writes the
 // attention output (bf16) that the output projection reads.
@@ -577,6 +781,10 @@ hipError_t launch_rope_append(const AttnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_decode_attention(const AttnArgs& a, const int32_t* valid, hipStream_t s) {
+  if (a.max_keys <= DQ_MAXKEYS) {
+    SS_LAUNCH(draft_attn_head_kernel, dim3(a.n_q), dim3(DQW * 64), 0, s, a, valid);
+    return hipGetLastError();
+  }
   const dim3 grid(a.n_kv, a.splits), block(256);
   switch (a.n_q / a.n_kv) {
 #define SS_G(g) \

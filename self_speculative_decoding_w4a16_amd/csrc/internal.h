@@ -86,11 +86,13 @@ struct AttnArgs {
   const int32_t* index;  // [Hkv][index_cap] of this layer
   const int32_t* n_index;
   int index_cap;
+  int max_keys;  // draft step: bound on the keys of the launch (picks the kernel)
 };
 hipError_t launch_rope_append(const AttnArgs& a, hipStream_t s);
-// One query position (the draft step): RoPE + KV append + per-split partials
-// (m, l, o[d]) in part[kv head][split][group head][d + 4], then a merge of
-// the splits into out [Hq d] (bf16).
+// One query position (the draft step): RoPE + KV append + attention into
+// out [Hq d] (bf16).  Up to 2048 keys (a.max_keys) one block per query head
+// does it all; beyond, per-split partials (m, l, o[d]) in part[kv head][split]
+// [group head][d + 4] are merged by a second launch.
 hipError_t launch_decode_attention(const AttnArgs& a, const int32_t* valid, hipStream_t s);
 int decode_attn_keys_per_split();  // verify rows
 int draft_attn_keys_per_split();   // draft step
