@@ -427,27 +427,31 @@ __global__ __launch_bounds__(256) void draft_attn_kernel(AttnArgs a, const int32
 
 // Draft-step attention with one block per query head (short contexts: no
 // split partials, no merge launch): 512 threads = 8 waves; wave w takes the
-// 16-key chunks w, w + 8, ...  Lane (key kl = lane / 4, quarter kq = lane % 4)
-// holds, for i = 0..3, dims 32 i + 8 kq .. +7 of its key's K and V rows (each
-// load instruction reads 64 contiguous bytes of 16 keys), so a score is the
-// lane's partial dot summed over its quad (two in-register DPP swaps).  Every
-// lane keeps its own running softmax (m, l) and output partial o[32] over the
-// keys it sees; lanes and waves are combined once at the end.  Loads run 3
-// chunks ahead in a ring named statically.  Every block of a kv head rotates
-// the new key itself (its score needs it); the group's first block appends
-// the new K/V to the cache (the others never read that slot from memory).
+// 16-key chunks w, w + 8, ...  Lane (part kp = lane % 8, key kg = lane / 8)
+// holds 16 bytes of each half of the K and V rows of keys kg and 8 + kg of
+// the chunk, dims 8 kp .. +7 and 64 + 8 kp .. +7, so every load instruction
+// reads whole 128-byte rows of 8 keys; a score is the lane's partial dot
+// summed over its 8 lanes (three in-register DPP steps).  Every lane keeps a
+// running softmax (reference max m, sum l) and an output partial o[16] over
+// the keys it sees, rescaled only when a score exceeds m by more than 8 (in
+// log2 units; the weights stay below 2^8); lanes and waves are combined once
+// at the end.  Loads run 3 chunks ahead in a ring named statically.  Every
+// block of a kv head rotates the new key itself (its score needs it); the
+// group's first block appends the new K/V to the cache (the others never read
+// that slot from memory).
 constexpr int DQW = 8;            // waves
 constexpr int DQR = 3;            // chunks in flight per wave
 constexpr int DQ_MAXKEYS = 2048;  // keys up to which the per-head kernel is used
 
-// v summed (or maxed) over the lanes of a quad / of the lanes 4 apart in a row
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float quad_sum(float v) {
-  v += dpp<0xB1>(v);  // quad_perm [1,0,3,2]
-  return v + dpp<0x4E>(v);  // quad_perm [2,3,0,1]
+// v summed over the 8 lanes of a half-row (every lane gets the sum)
+__device__ __forceinline__ float oct_sum(float v) {
+  v += dpp<0xB1>(v);         // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);         // quad_perm [2,3,0,1]
+  return v + dpp<0x141>(v);  // row_half_mirror: lane i <-> 7 - i, the other quad
 }
 
 __global__ __launch_bounds__(DQW * 64) void draft_attn_head_kernel(AttnArgs a, const int32_t* valid) {
@@ -473,23 +477,27 @@ __global__ __launch_bounds__(DQW * 64) void draft_attn_head_kernel(AttnArgs a, c
   };
   const uint16_t* kc = a.k_cache + (int64_t)hk * a.cap * D;
   const uint16_t* vc = a.v_cache + (int64_t)hk * a.cap * D;
-  const int kq = lane & 3, kl = lane >> 2;
+  const int kp = lane & 7, kg = lane >> 3;
   const int last = ks.n_keys - 1;  // slot of the new key
   const int n_chunks = (ks.n_keys + KW - 1) / KW;
 
-  // chunk loads: slots past the end (or the new key) read slot 0 and are masked
+  // chunk loads: [key kg, key 8 + kg] x [half 0, half 1]; slots past the end
+  // (or the new key) read slot 0 and are masked
   struct Chunk {
     u32x4 k[4], v[4];
   };
   auto load_chunk = [&](int c, Chunk& b) {
-    const int t = c * KW + kl;
-    const int64_t row = (int64_t)slot_pos(t < last ? t : 0) * D;
-    const u32x4* kp = reinterpret_cast<const u32x4*>(kc + row) + kq;
-    const u32x4* vp = reinterpret_cast<const u32x4*>(vc + row) + kq;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) b.k[i] = kp[4 * i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) b.v[i] = vp[4 * i];
+    for (int e = 0; e < 2; ++e) {
+      const int t = c * KW + 8 * e + kg;
+      const int64_t row = (int64_t)slot_pos(t < last ? t : 0) * D;
+      const u32x4* kr = reinterpret_cast<const u32x4*>(kc + row) + kp;
+      const u32x4* vr = reinterpret_cast<const u32x4*>(vc + row) + kp;
+      b.k[2 * e] = kr[0];
+      b.k[2 * e + 1] = kr[8];
+      b.v[2 * e] = vr[0];
+      b.v[2 * e + 1] = vr[8];
+    }
   };
   Chunk ring[DQR];
 #pragma unroll
@@ -529,47 +537,50 @@ __global__ __launch_bounds__(DQW * 64) void draft_attn_head_kernel(AttnArgs a, c
   }
   __syncthreads();
 
-  const float scale = 0.088388347648318440f;  // 1/sqrt(128)
-  u32x4 q4[4], kn4[4], vn4[4];  // this lane's dims of q and of the new K/V
+  // scores in log2 units: exp(s / sqrt(128)) = 2^(s * log2(e) / sqrt(128))
+  const float scale = 0.088388347648318440f * 1.4426950408889634f;
+  const u32x4 q0 = reinterpret_cast<const u32x4*>(qp)[kp], q1 = reinterpret_cast<const u32x4*>(qp)[8 + kp];
+  float m = -INFINITY, l = 0.0f, o[16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    q4[i] = reinterpret_cast<const u32x4*>(qp)[4 * i + kq];
-    kn4[i] = reinterpret_cast<const u32x4*>(knew)[4 * i + kq];
-    vn4[i] = reinterpret_cast<const u32x4*>(vnew)[4 * i + kq];
-  }
-  float m = -INFINITY, l = 0.0f, o[32];
-#pragma unroll
-  for (int j = 0; j < 32; ++j) o[j] = 0.0f;
+  for (int j = 0; j < 16; ++j) o[j] = 0.0f;
 
-  // consume chunk c from its buffer
+  auto score = [&](const u32x4& k0, const u32x4& k1) {
+    float d0 = ss::dot2(k0.x, q0.x, 0.0f), d1 = ss::dot2(k0.y, q0.y, 0.0f);
+    d0 = ss::dot2(k0.z, q0.z, d0);
+    d1 = ss::dot2(k0.w, q0.w, d1);
+    d0 = ss::dot2(k1.x, q1.x, d0);
+    d1 = ss::dot2(k1.y, q1.y, d1);
+    d0 = ss::dot2(k1.z, q1.z, d0);
+    d1 = ss::dot2(k1.w, q1.w, d1);
+    return oct_sum(d0 + d1) * scale;
+  };
+  // keys with scores sa, sb (inactive: -inf) and V halves (va0, va1), (vb0, vb1)
+  auto update = [&](float sa, float sb, const u32x4& va0, const u32x4& va1, const u32x4& vb0,
+                    const u32x4& vb1) {
+    const float mx = fmaxf(sa, sb);
+    if (mx > m + 8.0f) {  // raise the reference (first key: m = -inf)
+      const float r = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - mx);
+      l *= r;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) o[j] *= r;
+      m = mx;
+    }
+    const float pa = (sa == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sa - m);
+    const float pb = (sb == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(sb - m);
+    l += pa + pb;
+    const uint32_t wa[8] = {va0.x, va0.y, va0.z, va0.w, va1.x, va1.y, va1.z, va1.w};
+    const uint32_t wb[8] = {vb0.x, vb0.y, vb0.z, vb0.w, vb1.x, vb1.y, vb1.z, vb1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      o[2 * e] += pa * ss::lo_bf(wa[e]) + pb * ss::lo_bf(wb[e]);
+      o[2 * e + 1] += pa * ss::hi_bf(wa[e]) + pb * ss::hi_bf(wb[e]);
+    }
+  };
+  // consume chunk c from its buffer (the new key is taken after the loop)
   auto step = [&](int c, const Chunk& b) {
-    const int t = c * KW + kl;
-    const bool kin = t < ks.n_keys, is_new = t == last;
-    float d0 = 0.0f, d1 = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4 k4 = is_new ? kn4[i] : b.k[i];
-      d0 = ss::dot2(k4.x, q4[i].x, d0);
-      d1 = ss::dot2(k4.y, q4[i].y, d1);
-      d0 = ss::dot2(k4.z, q4[i].z, d0);
-      d1 = ss::dot2(k4.w, q4[i].w, d1);
-    }
-    const float sc = quad_sum(d0 + d1) * scale;
-    const float mn = kin ? fmaxf(m, sc) : m;
-    const float r = (mn == m) ? 1.0f : expf(m - mn);  // m = -inf: r = 0
-    const float p = kin ? expf(sc - mn) : 0.0f;
-    l = l * r + p;
-    m = mn;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4 v4 = is_new ? vn4[i] : b.v[i];
-      const uint32_t w[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o[8 * i + 2 * e] = o[8 * i + 2 * e] * r + p * ss::lo_bf(w[e]);
-        o[8 * i + 2 * e + 1] = o[8 * i + 2 * e + 1] * r + p * ss::hi_bf(w[e]);
-      }
-    }
+    const int t = c * KW + kg;
+    const float sa = score(b.k[0], b.k[1]), sb = score(b.k[2], b.k[3]);
+    update(t < last ? sa : -INFINITY, t + 8 < last ? sb : -INFINITY, b.v[0], b.v[1], b.v[2], b.v[3]);
   };
   // each buffer is refilled with chunk c + DQR * DQW right after use; the last
   // pass may run past the wave's chunks: those are skipped, their loads (of
@@ -582,32 +593,36 @@ __global__ __launch_bounds__(DQW * 64) void draft_attn_head_kernel(AttnArgs a, c
       load_chunk(cn < n_chunks ? cn : 0, ring[j]);
     }
   }
+  // the new key, from LDS: the 8 lanes of key group 0 in wave 0
+  if (wave == 0 && kg == 0) {
+    const u32x4* kn = reinterpret_cast<const u32x4*>(knew);
+    const u32x4* vn = reinterpret_cast<const u32x4*>(vnew);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    update(score(kn[kp], kn[8 + kp]), -INFINITY, vn[kp], vn[8 + kp], z, z);
+  }
 
-  // ---- lanes 4 apart in a row (same quarter) combine: max, rescale, sum
-  float mr = fmaxf(m, dpp<0x124>(m));  // row_ror:4
-  mr = fmaxf(mr, dpp<0x128>(mr));      // row_ror:8
-  const float f = (m == -INFINITY) ? 0.0f : expf(m - mr);
+  // ---- the lanes 8 apart in a row (same dims) combine: max, rescale, sum
+  const float mr = fmaxf(m, dpp<0x128>(m));  // row_ror:8
+  const float f = (m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - mr);
   l *= f;
-  l += dpp<0x124>(l);
   l += dpp<0x128>(l);
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    float v = o[j] * f;
-    v += dpp<0x124>(v);
-    v += dpp<0x128>(v);
-    o[j] = v;
+  for (int j = 0; j < 16; ++j) {
+    const float v = o[j] * f;
+    o[j] = v + dpp<0x128>(v);
   }
-  // lanes 0-3 of each row hold the row's partial for their quarter
-  const int row = lane >> 4, pidx = wave * 4 + row;
-  if ((lane & 15) < 4) {
-    if (kq == 0) {
+  // lanes 0-7 of each row hold the row's partial for their dims
+  const int pidx = wave * 4 + (lane >> 4);
+  if ((lane & 15) < 8) {
+    if (kp == 0) {
       pm[pidx] = mr;
       pl[pidx] = l;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) po[pidx][32 * i + 8 * kq + j] = o[8 * i + j];
+    for (int j = 0; j < 8; ++j) {
+      po[pidx][8 * kp + j] = o[j];
+      po[pidx][64 + 8 * kp + j] = o[8 + j];
+    }
   }
   __syncthreads();
   // ---- combine the partials (rows that saw no key have m = -inf)
@@ -615,7 +630,7 @@ __global__ __launch_bounds__(DQW * 64) void draft_attn_head_kernel(AttnArgs a, c
     float M = -INFINITY;
 #pragma unroll
     for (int q = 0; q < NP; ++q) M = fmaxf(M, pm[q]);
-    pf[tid] = (pm[tid] == -INFINITY) ? 0.0f : expf(pm[tid] - M);
+    pf[tid] = (pm[tid] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(pm[tid] - M);
   }
   __syncthreads();
   if (tid < D) {
