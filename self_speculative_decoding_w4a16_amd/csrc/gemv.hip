@@ -203,8 +203,34 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
   uint32_t magic = magic_arg;
   asm volatile("" : "+v"(magic));
 
-  // ------------------------------------------------ first weight loads, issued
-  // before the prologue so that their latency overlaps it
+  // ------------------------------------------------ prologue inputs and first weights
+  // Loads complete in issue order.  A plain input x is issued before the
+  // first weights, so waiting for it does not wait for the weight burst of
+  // every wave at once; with the norm prologue (h and the norm weights,
+  // L2-resident) issuing the weights first measured faster.  Indices are
+  // clamped (every load issued), out-of-range items masked at use.
+  const uint16_t* src = a.x;
+  if (PRO == PRO_NORM) src = a.h;
+  if (PRO == PRO_EMBED_NORM) src = a.embed + (int64_t)(*a.token) * K;
+  const u32x4* src4 = reinterpret_cast<const u32x4*>(src);
+  const u32x4* g4 = reinterpret_cast<const u32x4*>(a.norm_w);
+  float* xsum = reinterpret_cast<float*>(smem4 + (W4 ? w4_slots(K) : K / 8));
+  // items: 8 consecutive values of x (one 16-byte quad); for W4 the four
+  // items of a 32-value chunk sit in four consecutive lanes
+  constexpr int NI = (3 * kThreads + NT - 1) / NT;  // items per thread held when normalising
+  constexpr int XB = (PRO == PRO_X) ? 4 : NI;        // items per thread loaded up front
+  const int n_items = K / 8;
+  u32x4 hv[XB], gv[XB];
+  auto load_prologue = [&]() {
+#pragma unroll
+    for (int t = 0; t < XB; ++t) {
+      const int it = min(tid + t * NT, n_items - 1);
+      hv[t] = src4[it];
+      if (PRO != PRO_X) gv[t] = g4[it];
+    }
+  };
+  if (PRO == PRO_X) load_prologue();
+
   int64_t g = (int64_t)blockIdx.x * kWaves + wave;
   int64_t prow[R], out0;
   bool rv[R];
@@ -219,31 +245,23 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
   float rres[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) rres[r] = (EPI == EPI_RESID) ? ss::bf2f(a.resid[prow[r]]) : 0.0f;
+  if (PRO != PRO_X) {
+    load_prologue();
+  } else {
+    // keep the prologue's arithmetic (and its wait) after the weight loads
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   // ------------------------------------------------ prologue: x (and group sums) in LDS
-  const uint16_t* src = a.x;
-  if (PRO == PRO_NORM) src = a.h;
-  if (PRO == PRO_EMBED_NORM) src = a.embed + (int64_t)(*a.token) * K;
-  float* xsum = reinterpret_cast<float*>(smem4 + (W4 ? w4_slots(K) : K / 8));
-  // items: 8 consecutive values of x (one 16-byte quad); for W4 the four
-  // items of a 32-value chunk sit in four consecutive lanes
-  constexpr int NI = (3 * kThreads + NT - 1) / NT;  // items per thread held when normalising
-  const int n_items = K / 8;
   if (PRO != PRO_X) {
-    const u32x4* src4 = reinterpret_cast<const u32x4*>(src);
-    const u32x4* g4 = reinterpret_cast<const u32x4*>(a.norm_w);
-    u32x4 hv[NI], gv[NI];
     float ss = 0.0f;
 #pragma unroll
     for (int t = 0; t < NI; ++t) {
-      const int it = tid + t * NT;
-      const bool ok = it < n_items;
-      hv[t] = ok ? src4[it] : u32x4{0u, 0u, 0u, 0u};
-      gv[t] = ok ? g4[it] : u32x4{0u, 0u, 0u, 0u};
+      const bool ok = tid + t * NT < n_items;
       const uint32_t wv[4] = {hv[t].x, hv[t].y, hv[t].z, hv[t].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float lo = ss::lo_bf(wv[i]), hi = ss::hi_bf(wv[i]);
+        const float lo = ok ? ss::lo_bf(wv[i]) : 0.0f, hi = ok ? ss::hi_bf(wv[i]) : 0.0f;
         ss += lo * lo;
         ss += hi * hi;
       }
@@ -274,22 +292,18 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
       put_x<W4>(smem4, xsum, it, ok, xb);
     }
   } else {
-    // up to XB items per thread are loaded together (one memory latency for
-    // x up to 8 XB NT values), then stored
-    constexpr int XB = 4;
-    const u32x4* src4 = reinterpret_cast<const u32x4*>(src);
+    // the first XB items per thread are the ones loaded up front (all of x up
+    // to 8 XB NT values); any further batch is loaded here
     for (int b0 = 0; b0 < n_items; b0 += XB * NT) {  // block-uniform trip count
-      u32x4 v[XB];
+      if (b0 > 0) {
 #pragma unroll
-      for (int t = 0; t < XB; ++t) {
-        const int it = b0 + t * NT + tid;
-        v[t] = it < n_items ? src4[it] : u32x4{0u, 0u, 0u, 0u};
+        for (int t = 0; t < XB; ++t) hv[t] = src4[min(b0 + t * NT + tid, n_items - 1)];
       }
 #pragma unroll
       for (int t = 0; t < XB; ++t) {
         if (b0 + t * NT >= n_items) break;  // block-uniform
         const int it = b0 + t * NT + tid;
-        const uint32_t wv[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+        const uint32_t wv[4] = {hv[t].x, hv[t].y, hv[t].z, hv[t].w};
         uint16_t xb[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
