@@ -62,134 +62,200 @@ __global__ __launch_bounds__(64) void rope_append_kernel(AttnArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// Verify attention: grid (kv head, key split of DKPB keys, row), 512 threads.
-// Row j's query sits at position kv_len + j and sees keys [0, kv_len + j];
-// rope_append already wrote q_rot and the rows' K/V.  Thread (key j, quarter
-// c) holds 32 dims of K[j] and V[j]; scores are reduced over the 4 quarters
-// with lane shuffles.  Each block writes, per query head of its group, the
-// partial (max m, sum l, o[d] = sum_j exp(s_j - m) V[j][d]) of its split at
-// [kv head][split][row][group head]; rows_merge merges the splits.
+// Verify attention on the matrix cores: grid (kv head, key split of DKPB =
+// 128 keys), 512 threads = 8 waves.  The block takes all m x G queries of
+// its kv head (query qi = row j * G + group head h), so the split's K and V
+// are read once per layer.  Row j's query sits at position kv_len + j and
+// sees keys [0, kv_len + j]; rope_append already wrote q_rot and the rows'
+// K/V.
+//  * LDS: the K tile [128 keys][d] (B operand of S = Q K^T), the V tile
+//    transposed [d][128 keys] (B operand of O = P V), and per wave a P tile
+//    [16 queries][128 keys] (A operand of PV, written from the S layout).
+//  * Tiles of 16 queries are spread over the waves.  Per tile: S in 8 key
+//    tiles x 4 k-steps of v_mfma_f32_16x16x32_bf16 (lane l of the result
+//    holds queries 4(l/16)..+3 of key l%16), causal mask, row max and sum over
+//    the 128 keys (the 16 lanes of a DPP row), P = exp(S - m) split into bf16
+//    hi and lo parts (two MFMAs each: products at fp32 level), O in 8 dim
+//    tiles x 4 key steps.
+//  * Partials (m, l, o[d]) per (split, row, group head) -- the layout
+//    rows_merge reads; rows with no key in the split write none.
 constexpr int DKPB = 128;
 constexpr int DREC = 4 + D;  // partial record: m, l, 2 pad, o[D] (16-byte aligned o)
 
-__global__ __launch_bounds__(512) void rows_attn_kernel(AttnArgs a) {
-  constexpr int GMAX = 16;
-  constexpr int NW = 8;                    // waves per block
-  __shared__ float qs[GMAX][D];            // rotated queries (float)
-  __shared__ u32x4 vs[DKPB][D / 8 + 1];    // V tile (padded rows)
-  __shared__ float ps[GMAX][DKPB];         // probabilities p[h][key]
-  __shared__ float wmax[NW][GMAX], wsum[NW][GMAX];
-  __shared__ float hmax[GMAX];
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// max / sum over the 16 lanes of a DPP row (every lane gets the result)
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror: the other quad of the half-row
+  return fmaxf(v, dpp_f<0x140>(v));  // row_mirror: the other half-row
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  return v + dpp_f<0x140>(v);
+}
+
+constexpr int RW = 8;  // waves per block of the verify attention
+
+__global__ __launch_bounds__(RW * 64) void rows_attn_kernel(AttnArgs a) {
+  constexpr int NT = 8;            // key tiles of 16 (= DKPB / 16) and dim tiles of 16 (= D / 16)
+  constexpr int KROW = D + 8;      // LDS row strides (bf16), padded
+  constexpr int VROW = DKPB + 8;
+  constexpr int NTH = RW * 64;
+  __shared__ __align__(16) uint16_t ks[DKPB][KROW];
+  __shared__ __align__(16) uint32_t vt[D][VROW / 2];   // V^T: bf16 pairs of consecutive keys
+  __shared__ __align__(16) uint16_t pt[RW][2][16][VROW];  // per wave: P hi, P lo
 
   const int hk = blockIdx.x, split = blockIdx.y, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int G = a.n_q / a.n_kv;
-  const int row = (int)blockIdx.z;
-  const int pos = *a.kv_len + a.pos_offset + row;  // position of this query (its last key)
-  if (pos < 0 || pos >= a.cap) return;
-  const int n_keys = pos + 1;
+  const int lane = tid & 63, wave = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
+  const int G = a.n_q / a.n_kv, Qn = a.m * G;
+  const int kv0 = *a.kv_len + a.pos_offset;       // position of row 0
+  const int n_keys = min(kv0 + a.m, a.cap);       // keys of the last row in range
+  if (kv0 < 0 || n_keys <= 0) return;
   const int active = (n_keys + DKPB - 1) / DKPB;
   if (split >= active) return;
   const int k0 = split * DKPB;
-  const int nk = min(DKPB, n_keys - k0);
+  const int n_tiles = (Qn + 15) / 16;
 
-  // ---- loads: thread (key j, quarter c) takes 32 dims of K[j] and V[j]
-  const int j = tid >> 2, c = tid & 3;
-  const bool kvalid = j < nk;
-  u32x4 kr[4], vr[4];
+  // A operand of a query tile: lane -> query 16 t + r16, dims 32 s + 8 g4 .. +7
+  auto load_q = [&](int t, u32x4 (&qa)[4]) {
+    const int qi = 16 * t + r16;
+    const bool qok = qi < Qn;
+    const int j = qok ? qi / G : 0, h = qok ? qi % G : 0;
+    const u32x4* qp = reinterpret_cast<const u32x4*>(a.q_rot + ((int64_t)j * a.n_q + hk * G + h) * D);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) qa[st] = qok ? qp[4 * st + g4] : u32x4{0u, 0u, 0u, 0u};
+  };
+  u32x4 qa[4];
+  load_q(wave < n_tiles ? wave : 0, qa);
+
+  // ---- K tile, and V^T as pairs of consecutive keys (keys past n_keys are
+  // zeros): thread -> (key pair kp, 16-byte piece q) with the 64 lanes of a
+  // wave on 64 consecutive pairs, so the transposed stores hit distinct banks
   {
-    const int64_t krow = (int64_t)hk * a.cap + k0 + (kvalid ? j : 0);
-    const u32x4* kp = reinterpret_cast<const u32x4*>(a.k_cache + krow * D) + 4 * c;
-    const u32x4* vp = reinterpret_cast<const u32x4*>(a.v_cache + krow * D) + 4 * c;
+    constexpr int PER = (DKPB / 2) * (D / 8) / NTH;  // (pair, piece) items per thread
+    u32x4 k2[PER][2], v2[PER][2];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + NTH * i, kp = e & (DKPB / 2 - 1), q = e / (DKPB / 2);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int key = k0 + 2 * kp + u;
+        const bool ok = key < n_keys;
+        const int64_t row = (int64_t)hk * a.cap + (ok ? key : 0);
+        k2[i][u] = ok ? reinterpret_cast<const u32x4*>(a.k_cache + row * D)[q] : u32x4{0u, 0u, 0u, 0u};
+        v2[i][u] = ok ? reinterpret_cast<const u32x4*>(a.v_cache + row * D)[q] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + NTH * i, kp = e & (DKPB / 2 - 1), q = e / (DKPB / 2);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x4*>(&ks[2 * kp + u][8 * q]) = k2[i][u];
+      const uint32_t w0[4] = {v2[i][0].x, v2[i][0].y, v2[i][0].z, v2[i][0].w};
+      const uint32_t w1[4] = {v2[i][1].x, v2[i][1].y, v2[i][1].z, v2[i][1].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        vt[8 * q + 2 * t][kp] = (w0[t] & 0xffffu) | (w1[t] << 16);
+        vt[8 * q + 2 * t + 1][kp] = (w0[t] >> 16) | (w1[t] & 0xffff0000u);
+      }
+    }
+  }
+  __syncthreads();
+
+  const float scale = 0.088388347648318440f;  // 1/sqrt(128)
+  const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(&vt[0][0]);
+  for (int t = wave; t < n_tiles; t += RW) {
+    if (t != wave) load_q(t, qa);
+    // S = Q K^T
+    f32x4_t sa[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      sa[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const u32x4 b = *reinterpret_cast<const u32x4*>(&ks[16 * n + r16][32 * st + 8 * g4]);
+        sa[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[st]),
+                                                        __builtin_bit_cast(bf16x8_t, b), sa[n], 0, 0, 0);
+      }
+    }
+    // causal mask, row max / sum; this lane's queries are 16 t + 4 g4 + i
+    float mx[4], sm[4];
+    int qrow[4];
+    bool qv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      kr[i] = kvalid ? kp[i] : u32x4{0u, 0u, 0u, 0u};
-      vr[i] = kvalid ? vp[i] : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  for (int e = tid; e < G * D; e += 512) {
-    const int h = e / D, i = e % D;
-    qs[h][i] = ss::bf2f(a.q_rot[((int64_t)row * a.n_q + hk * G + h) * D + i]);
-  }
-  if (kvalid) {
+      const int qi = 16 * t + 4 * g4 + i;
+      qv[i] = qi < Qn;
+      qrow[i] = qv[i] ? qi / G : 0;
+      const int last_key = kv0 + qrow[i];  // this row's own position
+      qv[i] = qv[i] && last_key < a.cap && k0 <= last_key;
+      float m = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vs[j][4 * c + i] = vr[i];
-  }
-  __syncthreads();
-  // ---- scores: 32-dim partial dots, reduced over the 4 quarters of a key
-  float kf[32];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      kf[8 * i + 2 * t] = ss::lo_bf(w[t]);
-      kf[8 * i + 2 * t + 1] = ss::hi_bf(w[t]);
-    }
-  }
-  const float scale = 0.088388347648318440f;  // 1/sqrt(128)
-  float sc[GMAX];
-#pragma unroll
-  for (int h = 0; h < GMAX; ++h) {
-    float d = 0.0f;
-    if (h < G) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) d += qs[h][32 * c + i] * kf[i];
-    }
-    d += __shfl_xor(d, 1, 64);
-    d += __shfl_xor(d, 2, 64);
-    sc[h] = (j < nk) ? d * scale : -INFINITY;
-  }
-  // ---- softmax statistics per head over the block's keys
-#pragma unroll
-  for (int h = 0; h < GMAX; ++h) {
-    if (h < G) {
-      float m = sc[h];
-#pragma unroll
-      for (int o = 4; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-      if (lane == 0) wmax[wave][h] = m;
-    }
-  }
-  __syncthreads();
-  if (tid < G) {
-    float m = wmax[0][tid];
-    for (int w = 1; w < NW; ++w) m = fmaxf(m, wmax[w][tid]);
-    hmax[tid] = m;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < GMAX; ++h) {
-    if (h < G) {
-      const float p = (j < nk) ? expf(sc[h] - hmax[h]) : 0.0f;
-      if (c == 0) ps[h][j] = p;
-      float sm = (c == 0) ? p : 0.0f;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) sm += __shfl_xor(sm, o, 64);
-      if (lane == 0) wsum[wave][h] = sm;
-    }
-  }
-  __syncthreads();
-  // ---- o[h][d] = sum_j p[h][j] V[j][d]: thread -> (head, 2 dims)
-  const uint32_t* vw = reinterpret_cast<const uint32_t*>(&vs[0][0]);
-  constexpr int VROW = (D / 8 + 1) * 4;  // words per padded V row
-  for (int e = tid; e < G * (D / 2); e += 512) {
-    const int h = e / (D / 2), dp = e % (D / 2);
-    float o0 = 0.f, o1 = 0.f;
-#pragma unroll 8
-    for (int jj = 0; jj < nk; ++jj) {
-      const float p = ps[h][jj];
-      const uint32_t v = vw[jj * VROW + dp];
-      o0 += p * ss::lo_bf(v);
-      o1 += p * ss::hi_bf(v);
-    }
-    float* dst = a.part + (((int64_t)(hk * a.splits + split) * a.m + row) * G + h) * DREC;
-    dst[4 + 2 * dp] = o0;
-    dst[4 + 2 * dp + 1] = o1;
-    if (dp == 0) {
+      for (int n = 0; n < NT; ++n) {
+        const bool ok = qv[i] && k0 + 16 * n + r16 <= last_key;
+        sa[n][i] = ok ? sa[n][i] * scale : -INFINITY;
+        m = fmaxf(m, sa[n][i]);
+      }
+      mx[i] = row16_max(m);
       float l = 0.0f;
-      for (int w = 0; w < NW; ++w) l += wsum[w][h];
-      dst[0] = hmax[h];
-      dst[1] = l;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {  // exp(x) as 2^(x log2 e)
+        const float p = (mx[i] == -INFINITY) ? 0.0f
+                                             : __builtin_amdgcn_exp2f((sa[n][i] - mx[i]) * 1.4426950408889634f);
+        sa[n][i] = p;
+        l += p;
+      }
+      sm[i] = row16_sum(l);
+    }
+    // P (hi, lo bf16) into this wave's tile: [query 4 g4 + i][key 16 n + r16]
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = sa[n][i];
+        const uint16_t hi = ss::f2bf(p);
+        pt[wave][0][4 * g4 + i][16 * n + r16] = hi;
+        pt[wave][1][4 * g4 + i][16 * n + r16] = ss::f2bf(p - ss::bf2f(hi));
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    // O = P V: A = P [query r16][keys 32 st + 8 g4 ..], B = V^T [dim 16 n + r16][keys ..]
+    f32x4_t oa[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) oa[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const u32x4 ph = *reinterpret_cast<const u32x4*>(&pt[wave][0][r16][32 * st + 8 * g4]);
+      const u32x4 pl = *reinterpret_cast<const u32x4*>(&pt[wave][1][r16][32 * st + 8 * g4]);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const u32x4 b = *reinterpret_cast<const u32x4*>(vt16 + (16 * n + r16) * VROW + 32 * st + 8 * g4);
+        oa[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ph),
+                                                        __builtin_bit_cast(bf16x8_t, b), oa[n], 0, 0, 0);
+        oa[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pl),
+                                                        __builtin_bit_cast(bf16x8_t, b), oa[n], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();  // the P tile is rewritten by the next query tile
+    // partials of this lane's queries: o[dim 16 n + r16]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (!qv[i]) continue;
+      const int qi = 16 * t + 4 * g4 + i, h = qi % G;
+      float* dst = a.part + (((int64_t)(hk * a.splits + split) * a.m + qrow[i]) * G + h) * DREC;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) dst[4 + 16 * n + r16] = oa[n][i];
+      if (r16 == 0) {
+        dst[0] = mx[i];
+        dst[1] = sm[i];
+      }
     }
   }
 }
@@ -815,8 +881,7 @@ hipError_t launch_decode_attention(const AttnArgs& a, const int32_t* valid, hipS
 }
 
 hipError_t launch_rows_attention(const AttnArgs& a, hipStream_t s) {
-  if (a.n_q / a.n_kv > 16) return hipErrorInvalidValue;
-  SS_LAUNCH(rows_attn_kernel, dim3(a.n_kv, a.splits, a.m), dim3(512), 0, s, a);
+  SS_LAUNCH(rows_attn_kernel, dim3(a.n_kv, a.splits), dim3(RW * 64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SS_LAUNCH(rows_merge_kernel, dim3(a.n_q, a.m), dim3(D), 0, s, a);

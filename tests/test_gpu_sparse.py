@@ -8,6 +8,7 @@ import torch
 
 from oracle.cycle import sparse_speculative_cycle
 from oracle.model import forward
+from oracle.sampling import argmax_lowest
 from oracle.sparse import index_bounds, select_index
 from self_speculative_decoding_w4a16_amd import _lib
 from self_speculative_decoding_w4a16_amd.engine import SpecDecoder
@@ -112,6 +113,26 @@ def test_full_budget_draft_is_the_dense_draft(cuda):
     assert torch.equal(dense, dec.draft_logits) and torch.equal(dense_t, dec.tokens)
 
 
+def _near_tie(dec, gamma, dlogits, tlogits):
+    """The first greedy choice where the GPU and the oracle part (a draft
+    token, else a target argmax row, on the same tokens) is a near-tie of the
+    oracle's logits (within TOL of their largest magnitude): float32 against
+    float64 can only pick either side of such a tie."""
+    g_draft = host(dec.tokens[1:gamma + 1]).astype(np.int64)
+    for k in range(gamma):
+        r = np.asarray(dlogits[k], np.float64)
+        o = argmax_lowest(r)
+        if int(g_draft[k]) != o:
+            return r[o] - r[int(g_draft[k])] <= TOL * np.abs(r).max()
+    g_t = host(dec.target_logits).astype(np.float64)
+    for i in range(gamma + 1):
+        r = np.asarray(tlogits[i], np.float64)
+        o, g = argmax_lowest(r), argmax_lowest(g_t[i])
+        if g != o:
+            return r[o] - r[g] <= TOL * np.abs(r).max()
+    return False
+
+
 def test_sparse_greedy_cycles_match_oracle(cuda):
     ctx, cap, gamma, cycles = 600, 700, 4, 4
     log("sparse tiny: greedy cycles")
@@ -126,10 +147,15 @@ def test_sparse_greedy_cycles_match_oracle(cuda):
         dec.cycle()
         n = int(dec.n_accepted.item())
         out = host(dec.out_tokens[:n + 1]).astype(np.int64).tolist()
-        rn, rout, _, _, _, _, _, index = sparse_speculative_cycle(
+        rn, rout, _, _, dl, tl, _, index = sparse_speculative_cycle(
             om, kv_o, kv_len, last, gamma, 0.0, 0.0, z, z, 0, index, sp["n_sink"], sp["n_recent"],
             sp["window"], sp["budget_permille"])
-        assert (n, out) == (rn, rout), c
+        if (n, out) != (rn, rout):
+            # later cycles would run on different tokens: stop at a parting
+            # that a near-tie explains, fail on any other
+            assert _near_tie(dec, gamma, dl, tl), (c, (n, out), (rn, rout))
+            log(f"cycle {c}: parted from the oracle at a near-tie")
+            break
         kv_len += n + 1
         last = out[-1]
         assert int(dec.kv_len.item()) == kv_len
