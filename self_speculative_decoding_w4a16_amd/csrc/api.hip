@@ -333,6 +333,7 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
     a.eps = m->rms_eps;
     a.embed = m->embed;
     a.token = st->tokens + step;
+    a.vocab = m->vocab;
     a.h_out = w.h;
     a.y = w.qkv;
     a.valid = w.valid;

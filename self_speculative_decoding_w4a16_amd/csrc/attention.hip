@@ -114,13 +114,11 @@ __global__ __launch_bounds__(RW * 64) void rows_attn_kernel(AttnArgs a) {
   const int hk = blockIdx.x, split = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
   const int G = a.n_q / a.n_kv, Qn = a.m * G;
-  const int kv0 = *a.kv_len + a.pos_offset;       // position of row 0
-  const int n_keys = min(kv0 + a.m, a.cap);       // keys of the last row in range
-  if (kv0 < 0 || n_keys <= 0) return;
-  const int active = (n_keys + DKPB - 1) / DKPB;
-  if (split >= active) return;
   const int k0 = split * DKPB;
   const int n_tiles = (Qn + 15) / 16;
+  // kv_len is read first and used after the tile loads are issued: the K/V
+  // rows are clamped to the cache (not to kv_len) and masked when staged
+  const int kv0 = *a.kv_len + a.pos_offset;  // position of row 0
 
   // A operand of a query tile: lane -> query 16 t + r16, dims 32 s + 8 g4 .. +7
   auto load_q = [&](int t, u32x4 (&qa)[4]) {
@@ -145,16 +143,23 @@ __global__ __launch_bounds__(RW * 64) void rows_attn_kernel(AttnArgs a) {
       const int e = tid + NTH * i, kp = e & (DKPB / 2 - 1), q = e / (DKPB / 2);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int key = k0 + 2 * kp + u;
-        const bool ok = key < n_keys;
-        const int64_t row = (int64_t)hk * a.cap + (ok ? key : 0);
-        k2[i][u] = ok ? reinterpret_cast<const u32x4*>(a.k_cache + row * D)[q] : u32x4{0u, 0u, 0u, 0u};
-        v2[i][u] = ok ? reinterpret_cast<const u32x4*>(a.v_cache + row * D)[q] : u32x4{0u, 0u, 0u, 0u};
+        const int64_t row = (int64_t)hk * a.cap + min(k0 + 2 * kp + u, a.cap - 1);
+        k2[i][u] = reinterpret_cast<const u32x4*>(a.k_cache + row * D)[q];
+        v2[i][u] = reinterpret_cast<const u32x4*>(a.v_cache + row * D)[q];
       }
     }
+    const int n_keys = min(kv0 + a.m, a.cap);  // keys of the last row in range
+    if (kv0 < 0 || n_keys <= 0 || split >= (n_keys + DKPB - 1) / DKPB) return;  // block-uniform
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = tid + NTH * i, kp = e & (DKPB / 2 - 1), q = e / (DKPB / 2);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (k0 + 2 * kp + u >= n_keys) {
+          k2[i][u] = u32x4{0u, 0u, 0u, 0u};
+          v2[i][u] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
 #pragma unroll
       for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x4*>(&ks[2 * kp + u][8 * q]) = k2[i][u];
       const uint32_t w0[4] = {v2[i][0].x, v2[i][0].y, v2[i][0].z, v2[i][0].w};
@@ -529,34 +534,23 @@ __global__ __launch_bounds__(DQW * 64) void draft_attn_head_kernel(AttnArgs a, c
   __shared__ float pm[NP], pl[NP], pf[NP];
   __shared__ float po[NP][D];
 
-  const int vflag = valid ? *valid : 1;
   const int hq = blockIdx.x, tid = threadIdx.x;
   const int G = a.n_q / a.n_kv, hk = hq / G;
   const int lane = tid & 63, wave = tid >> 6;
-  const DraftKeys ks = draft_keys(a, hk);
-  if (vflag == 0 || ks.pos < 0 || ks.pos >= a.cap) return;
-  auto slot_pos = [&](int t) {
-    if (!ks.ilist) return t;
-    const int ti = min(t, max(ks.n_idx - 1, 0));
-    const int ip = min(max(ks.ilist[ti], 0), a.cap - 1);
-    return t < ks.n_idx ? ip : ks.kv0 + (t - ks.n_idx);
-  };
   const uint16_t* kc = a.k_cache + (int64_t)hk * a.cap * D;
   const uint16_t* vc = a.v_cache + (int64_t)hk * a.cap * D;
   const int kp = lane & 7, kg = lane >> 3;
-  const int last = ks.n_keys - 1;  // slot of the new key
-  const int n_chunks = (ks.n_keys + KW - 1) / KW;
+  const bool sparse = a.index != nullptr;
 
-  // chunk loads: [key kg, key 8 + kg] x [half 0, half 1]; slots past the end
-  // (or the new key) read slot 0 and are masked
+  // chunk loads: [key kg, key 8 + kg] x [half 0, half 1] of the K/V rows at
+  // row(t) for slot t
   struct Chunk {
     u32x4 k[4], v[4];
   };
-  auto load_chunk = [&](int c, Chunk& b) {
+  auto load_rows = [&](int c, Chunk& b, auto row_of) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int t = c * KW + 8 * e + kg;
-      const int64_t row = (int64_t)slot_pos(t < last ? t : 0) * D;
+      const int64_t row = (int64_t)row_of(c * KW + 8 * e + kg) * D;
       const u32x4* kr = reinterpret_cast<const u32x4*>(kc + row) + kp;
       const u32x4* vr = reinterpret_cast<const u32x4*>(vc + row) + kp;
       b.k[2 * e] = kr[0];
@@ -565,11 +559,38 @@ __global__ __launch_bounds__(DQW * 64) void draft_attn_head_kernel(AttnArgs a, c
       b.v[2 * e + 1] = vr[8];
     }
   };
+  // Dense: slot t is cache row t, so the first chunks are loaded before
+  // kv_len is known (rows clamped to the cache; slots from the new key on
+  // are masked, and their V zeroed, when consumed).
   Chunk ring[DQR];
+  auto dense_row = [&](int t) { return min(t, a.cap - 1); };
+  if (!sparse) {
 #pragma unroll
-  for (int j = 0; j < DQR; ++j) {
-    const int c = wave + j * DQW;
-    load_chunk(c < n_chunks ? c : 0, ring[j]);
+    for (int j = 0; j < DQR; ++j) load_rows(wave + j * DQW, ring[j], dense_row);
+  }
+  const int vflag = valid ? *valid : 1;
+  const DraftKeys ks = draft_keys(a, hk);
+  if (vflag == 0 || ks.pos < 0 || ks.pos >= a.cap) return;
+  const int last = ks.n_keys - 1;  // slot of the new key
+  const int n_chunks = (ks.n_keys + KW - 1) / KW;
+  auto sparse_row = [&](int t) {  // slots past the index: the speculative positions
+    t = t < last ? t : 0;
+    const int ti = min(t, max(ks.n_idx - 1, 0));
+    const int ip = min(max(ks.ilist[ti], 0), a.cap - 1);
+    return t < ks.n_idx ? ip : ks.kv0 + (t - ks.n_idx);
+  };
+  auto load_chunk = [&](int c, Chunk& b) {
+    if (sparse)
+      load_rows(c, b, sparse_row);
+    else
+      load_rows(c, b, dense_row);
+  };
+  if (sparse) {
+#pragma unroll
+    for (int j = 0; j < DQR; ++j) {
+      const int c = wave + j * DQW;
+      load_chunk(c < n_chunks ? c : 0, ring[j]);
+    }
   }
 
   // ---- RoPE of the query (threads 0-63) and the new key (64-127); new V (128-191)
@@ -642,11 +663,19 @@ __global__ __launch_bounds__(DQW * 64) void draft_attn_head_kernel(AttnArgs a, c
       o[2 * e + 1] += pa * ss::hi_bf(wa[e]) + pb * ss::hi_bf(wb[e]);
     }
   };
-  // consume chunk c from its buffer (the new key is taken after the loop)
+  // consume chunk c from its buffer (the new key is taken after the loop); in
+  // the chunk holding the new key, the V rows of its slots and beyond may be
+  // stale (zero weight, but not necessarily finite): they are zeroed
   auto step = [&](int c, const Chunk& b) {
     const int t = c * KW + kg;
     const float sa = score(b.k[0], b.k[1]), sb = score(b.k[2], b.k[3]);
-    update(t < last ? sa : -INFINITY, t + 8 < last ? sb : -INFINITY, b.v[0], b.v[1], b.v[2], b.v[3]);
+    if (c == last / KW) {  // wave-uniform
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      update(t < last ? sa : -INFINITY, t + 8 < last ? sb : -INFINITY, t < last ? b.v[0] : z,
+             t < last ? b.v[1] : z, t + 8 < last ? b.v[2] : z, t + 8 < last ? b.v[3] : z);
+    } else {
+      update(sa, sb, b.v[0], b.v[1], b.v[2], b.v[3]);
+    }
   };
   // each buffer is refilled with chunk c + DQR * DQW right after use; the last
   // pass may run past the wave's chunks: those are skipped, their loads (of

@@ -189,7 +189,10 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
   __shared__ float red_v[kWaves];
   __shared__ int red_i[kWaves];
 
-  if (a.valid && *a.valid == 0) return;
+  // the draft step's position flag: read first, tested after this wave's
+  // first loads are issued (so its latency overlaps theirs; nothing is
+  // stored before the test)
+  const int vflag = a.valid ? *a.valid : 1;
   const int tid = threadIdx.x, lane = tid & (SS_WAVE - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / SS_WAVE);  // wave-uniform: rows in SGPRs
   const int K = (int)a.k;
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
   // clamped (every load issued), out-of-range items masked at use.
   const uint16_t* src = a.x;
   if (PRO == PRO_NORM) src = a.h;
-  if (PRO == PRO_EMBED_NORM) src = a.embed + (int64_t)(*a.token) * K;
+  if (PRO == PRO_EMBED_NORM) src = a.embed + (int64_t)min(max(*a.token, 0), a.vocab - 1) * K;
   const u32x4* src4 = reinterpret_cast<const u32x4*>(src);
   const u32x4* g4 = reinterpret_cast<const u32x4*>(a.norm_w);
   float* xsum = reinterpret_cast<float*>(smem4 + (W4 ? w4_slots(K) : K / 8));
@@ -251,6 +254,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
     // keep the prologue's arithmetic (and its wait) after the weight loads
     __builtin_amdgcn_sched_barrier(0);
   }
+  if (vflag == 0) return;  // block-uniform: the whole launch is skipped
 
   // ------------------------------------------------ prologue: x (and group sums) in LDS
   if (PRO != PRO_X) {

@@ -22,7 +22,8 @@ struct GemvArgs {
   const uint16_t* norm_w;    // PRO_NORM / PRO_EMBED_NORM
   float eps;
   const uint16_t* embed;     // PRO_EMBED_NORM: embed table [V][k]
-  const int32_t* token;      // PRO_EMBED_NORM: device token id
+  const int32_t* token;      // PRO_EMBED_NORM: device token id (clamped to [0, vocab))
+  int64_t vocab;             // PRO_EMBED_NORM: rows of the embed table
   uint16_t* h_out;           // PRO_EMBED_NORM: block 0 stores the embedded row here
   // epilogue outputs
   uint16_t* y;               // output [n]
