@@ -24,40 +24,76 @@ namespace {
 
 constexpr int D = 128;     // head dim handled by these kernels
 
+// RoPE + KV append of the verify rows: grid (row, head), 64 threads (pair
+// index i: values i and i + d/2).  With split-k partials of the QKV GEMM
+// (S of them; S < 0: a loop) the values are their sums in split order; every
+// load (kv_len, the RoPE table, the values) is issued before the first use.
+template <int S>
 __global__ __launch_bounds__(64) void rope_append_kernel(AttnArgs a) {
   const int j = blockIdx.x;          // query row
   const int head = blockIdx.y;       // 0..Hq-1: q heads, Hq..Hq+Hkv-1: kv heads
   const int i = threadIdx.x;         // pair index 0..d/2-1
   const int half = a.d / 2;
   if (i >= half) return;
-  const int pos = *a.kv_len + a.pos_offset + j;
+  const int kvl = *a.kv_len;
   const int rows = a.n_q + 2 * a.n_kv;
-  const uint16_t* src = a.qkv + (int64_t)j * rows * a.d;
   const float c = a.rope_cs[((int64_t)j * half + i) * 2], s = a.rope_cs[((int64_t)j * half + i) * 2 + 1];
-  // projection value of column col of row j: bf16, or bf16 of its split-k partial sums
-  auto val = [&](int col) -> uint16_t {
-    if (!a.qkv_part) return src[col];
-    float v = 0.0f;
-    for (int sp = 0; sp < a.qkv_splits; ++sp) v += a.qkv_part[((int64_t)sp * a.m + j) * rows * a.d + col];
-    return ss::f2bf(v);
-  };
-  if (head < a.n_q) {
-    const int xo = head * a.d;
-    const float x1 = ss::bf2f(val(xo + i)), x2 = ss::bf2f(val(xo + i + half));
-    uint16_t* o = a.q_rot + (int64_t)j * a.n_q * a.d + head * a.d;
-    o[i] = ss::f2bf(x1 * c - x2 * s);
-    o[i + half] = ss::f2bf(x2 * c + x1 * s);
+  const bool is_q = head < a.n_q;
+  const int hk = head - a.n_q;
+  // columns: x = (c0, c1) rotated; for a kv head also v = (c2, c3)
+  const int c0 = is_q ? head * a.d + i : (a.n_q + hk) * a.d + i, c1 = c0 + half;
+  const int c2 = is_q ? c0 : (a.n_q + a.n_kv + hk) * a.d + i, c3 = c2 + half;
+  float x[4];
+  if (S == 0) {
+    const uint16_t* src = a.qkv + (int64_t)j * rows * a.d;
+    x[0] = ss::bf2f(src[c0]);
+    x[1] = ss::bf2f(src[c1]);
+    x[2] = ss::bf2f(src[c2]);
+    x[3] = ss::bf2f(src[c3]);
   } else {
-    const int hk = head - a.n_q;
+    const int64_t rs = (int64_t)rows * a.d;  // one row of one split
+    const float* p = a.qkv_part + (int64_t)j * rs;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    if (S > 0) {
+      float pv[S > 0 ? S : 1][4];
+#pragma unroll
+      for (int sp = 0; sp < S; ++sp) {
+        const float* ps = p + (int64_t)sp * a.m * rs;
+        pv[sp][0] = ps[c0];
+        pv[sp][1] = ps[c1];
+        pv[sp][2] = ps[c2];
+        pv[sp][3] = ps[c3];
+      }
+#pragma unroll
+      for (int sp = 0; sp < S; ++sp)  // split order
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += pv[sp][e];
+    } else {
+      for (int sp = 0; sp < a.qkv_splits; ++sp) {
+        const float* ps = p + (int64_t)sp * a.m * rs;
+        acc[0] += ps[c0];
+        acc[1] += ps[c1];
+        acc[2] += ps[c2];
+        acc[3] += ps[c3];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = ss::bf2f(ss::f2bf(acc[e]));  // the projection output is bf16
+  }
+  const uint16_t r0 = ss::f2bf(x[0] * c - x[1] * s), r1 = ss::f2bf(x[1] * c + x[0] * s);
+  if (is_q) {
+    uint16_t* o = a.q_rot + (int64_t)j * a.n_q * a.d + head * a.d;
+    o[i] = r0;
+    o[i + half] = r1;
+  } else {
+    const int pos = kvl + a.pos_offset + j;
     if (pos < 0 || pos >= a.cap) return;
-    const int ko = (a.n_q + hk) * a.d, vo = (a.n_q + a.n_kv + hk) * a.d;
-    const float x1 = ss::bf2f(val(ko + i)), x2 = ss::bf2f(val(ko + i + half));
     uint16_t* kc = a.k_cache + ((int64_t)hk * a.cap + pos) * a.d;
     uint16_t* vc = a.v_cache + ((int64_t)hk * a.cap + pos) * a.d;
-    kc[i] = ss::f2bf(x1 * c - x2 * s);
-    kc[i + half] = ss::f2bf(x2 * c + x1 * s);
-    vc[i] = val(vo + i);
-    vc[i + half] = val(vo + i + half);
+    kc[i] = r0;
+    kc[i + half] = r1;
+    vc[i] = ss::f2bf(x[2]);
+    vc[i + half] = ss::f2bf(x[3]);
   }
 }
 
@@ -886,7 +922,14 @@ __global__ __launch_bounds__(SKB) void attn_scores_kernel(AttnArgs a, float* sco
 }  // namespace
 
 hipError_t launch_rope_append(const AttnArgs& a, hipStream_t s) {
-  SS_LAUNCH(rope_append_kernel, dim3(a.m, a.n_q + a.n_kv), dim3(64), 0, s, a);
+  const dim3 grid(a.m, a.n_q + a.n_kv), block(64);
+  switch (a.qkv_part ? a.qkv_splits : 0) {
+#define SS_S(n) \
+  case n: SS_LAUNCH(rope_append_kernel<n>, grid, block, 0, s, a); break;
+    SS_S(0) SS_S(1) SS_S(2) SS_S(3) SS_S(4) SS_S(5) SS_S(6) SS_S(7) SS_S(8)
+#undef SS_S
+    default: SS_LAUNCH(rope_append_kernel<-1>, grid, block, 0, s, a); break;
+  }
   return hipGetLastError();
 }
 

@@ -113,7 +113,7 @@ hipError_t launch_kv_select(const float* score, int cap, const int32_t* kv_len, 
 hipError_t launch_rmsnorm_rows(const uint16_t* h, const uint16_t* g, float eps, int rows, int k,
                                uint16_t* out, hipStream_t s);
 // h[r] = bf16(h[r] + sum over splits of part[s][r]) in place (splits in
-// order; skipped when part is null), then out[r] = RMSNorm(h[r]) * g.  k <= 6144.
+// order; skipped when part is null), then out[r] = RMSNorm(h[r]) * g.  k <= 8192.
 hipError_t launch_resid_rmsnorm_rows(uint16_t* h, const float* part, int splits, const uint16_t* g, float eps,
                                      int rows, int k, uint16_t* out, hipStream_t s);
 hipError_t launch_embed_rows(const uint16_t* embed, const int32_t* tokens, int rows, int k,

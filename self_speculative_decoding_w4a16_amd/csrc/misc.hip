@@ -10,44 +10,61 @@ namespace {
 
 // Row RMSNorm, optionally after adding fp32 partial sums to the row first:
 // h = bf16(h + sum_s part[s]) (split order, written back), then
-// out = bf16(h / sqrt(mean(h^2) + eps) * g).  One block (256 threads) per row,
-// the row held in registers (k <= 3 * 256 * 8).
-__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(uint16_t* __restrict__ h,
-                                                           const float* __restrict__ part, int splits,
-                                                           int rows, const uint16_t* __restrict__ g,
-                                                           float eps, int k, uint16_t* __restrict__ out) {
-  constexpr int NI = 3;
-  __shared__ float red[4];
-  __shared__ float s_inv;
+// out = bf16(h / sqrt(mean(h^2) + eps) * g).  One block of 1024 threads per
+// row, one 8-value item per thread (k <= 8192): every load (h, the S split
+// partials, the norm weights) is issued before the first is used.  S < 0: any
+// number of splits (a loop).
+template <int S>
+__global__ __launch_bounds__(1024) void rmsnorm_rows_kernel(uint16_t* __restrict__ h,
+                                                            const float* __restrict__ part, int splits,
+                                                            int rows, const uint16_t* __restrict__ g,
+                                                            float eps, int k, uint16_t* __restrict__ out) {
+  __shared__ float red[16];
   const int row = blockIdx.x, tid = threadIdx.x;
   uint16_t* x = h + (int64_t)row * k;
   const int items = k / 8;
-  u32x4 hv[NI];
-  float ss = 0.0f;
+  const bool act = tid < items;
+  const int q = act ? tid : 0;
+  u32x4 v = reinterpret_cast<const u32x4*>(x)[q];
+  const u32x4 gv = reinterpret_cast<const u32x4*>(g)[q];
+  float add[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto add_split = [&](int sp) {
+    const f32x4_t* p = reinterpret_cast<const f32x4_t*>(part + ((int64_t)sp * rows + row) * k + 8 * q);
+    const f32x4_t a0 = p[0], a1 = p[1];
 #pragma unroll
-  for (int t = 0; t < NI; ++t) {
-    const int q = tid + 256 * t;
-    if (q >= items) continue;
-    u32x4 v = reinterpret_cast<const u32x4*>(x)[q];
-    if (part) {
-      float add[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int sp = 0; sp < splits; ++sp) {
-        const f32x4_t* p = reinterpret_cast<const f32x4_t*>(part + ((int64_t)sp * rows + row) * k + 8 * q);
-        const f32x4_t a0 = p[0], a1 = p[1];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          add[i] += a0[i];
-          add[4 + i] += a1[i];
-        }
-      }
-      uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        wv[i] = ss::pack_bf(ss::f2bf(ss::lo_bf(wv[i]) + add[2 * i]), ss::f2bf(ss::hi_bf(wv[i]) + add[2 * i + 1]));
-      v = u32x4{wv[0], wv[1], wv[2], wv[3]};
-      reinterpret_cast<u32x4*>(x)[q] = v;
+    for (int i = 0; i < 4; ++i) {
+      add[i] += a0[i];
+      add[4 + i] += a1[i];
     }
-    hv[t] = v;
+  };
+  if (S > 0) {
+    f32x4_t pa[S > 0 ? S : 1][2];
+#pragma unroll
+    for (int sp = 0; sp < S; ++sp) {
+      const f32x4_t* p = reinterpret_cast<const f32x4_t*>(part + ((int64_t)sp * rows + row) * k + 8 * q);
+      pa[sp][0] = p[0];
+      pa[sp][1] = p[1];
+    }
+#pragma unroll
+    for (int sp = 0; sp < S; ++sp)  // split order
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        add[i] += pa[sp][0][i];
+        add[4 + i] += pa[sp][1][i];
+      }
+  } else if (S < 0) {
+    for (int sp = 0; sp < splits; ++sp) add_split(sp);
+  }
+  if (S != 0) {
+    uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      wv[i] = ss::pack_bf(ss::f2bf(ss::lo_bf(wv[i]) + add[2 * i]), ss::f2bf(ss::hi_bf(wv[i]) + add[2 * i + 1]));
+    v = u32x4{wv[0], wv[1], wv[2], wv[3]};
+    if (act) reinterpret_cast<u32x4*>(x)[q] = v;
+  }
+  float ss = 0.0f;
+  {
     const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -56,29 +73,25 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(uint16_t* __restrict_
       ss += hi * hi;
     }
   }
+  ss = act ? ss : 0.0f;
   ss = ss::wave_sum(ss);
   if ((tid & 63) == 0) red[tid >> 6] = ss;
   __syncthreads();
-  if (tid == 0) s_inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)k + eps);
-  __syncthreads();
-  const float inv = s_inv;
+  float tot = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) tot += red[w];
+  const float inv = 1.0f / sqrtf(tot / (float)k + eps);
+  if (!act) return;
   uint16_t* o = out + (int64_t)row * k;
+  const uint32_t wv[4] = {v.x, v.y, v.z, v.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
+  uint32_t ow[4];
 #pragma unroll
-  for (int t = 0; t < NI; ++t) {
-    const int q = tid + 256 * t;
-    if (q >= items) continue;
-    const u32x4 v = hv[t];
-    const u32x4 gv = reinterpret_cast<const u32x4*>(g)[q];
-    const uint32_t wv[4] = {v.x, v.y, v.z, v.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
-    uint32_t ow[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint16_t lo = ss::f2bf(ss::lo_bf(wv[i]) * inv * ss::lo_bf(gw[i]));
-      const uint16_t hi = ss::f2bf(ss::hi_bf(wv[i]) * inv * ss::hi_bf(gw[i]));
-      ow[i] = ss::pack_bf(lo, hi);
-    }
-    reinterpret_cast<u32x4*>(o)[q] = u32x4{ow[0], ow[1], ow[2], ow[3]};
+  for (int i = 0; i < 4; ++i) {
+    const uint16_t lo = ss::f2bf(ss::lo_bf(wv[i]) * inv * ss::lo_bf(gw[i]));
+    const uint16_t hi = ss::f2bf(ss::hi_bf(wv[i]) * inv * ss::hi_bf(gw[i]));
+    ow[i] = ss::pack_bf(lo, hi);
   }
+  reinterpret_cast<u32x4*>(o)[q] = u32x4{ow[0], ow[1], ow[2], ow[3]};
 }
 
 // Out-of-range token ids are clamped into [0, vocab) so a bad id cannot read
@@ -142,18 +155,34 @@ __global__ void rope_table_kernel(const int32_t* kv_len, int pos_offset, int d, 
 
 }  // namespace
 
+template <int S>
+static void launch_norm(uint16_t* h, const float* part, int splits, const uint16_t* g, float eps, int rows, int k,
+                        uint16_t* out, hipStream_t s) {
+  SS_LAUNCH(rmsnorm_rows_kernel<S>, dim3(rows), dim3(1024), 0, s, h, part, splits, rows, g, eps, k, out);
+}
+
 hipError_t launch_rmsnorm_rows(const uint16_t* h, const uint16_t* g, float eps, int rows, int k,
                                uint16_t* out, hipStream_t s) {
-  if (k > 3 * 256 * 8 || k % 8 != 0) return hipErrorInvalidValue;
-  SS_LAUNCH(rmsnorm_rows_kernel, dim3(rows), dim3(256), 0, s, const_cast<uint16_t*>(h), (const float*)nullptr, 0,
-            rows, g, eps, k, out);
+  if (k > 8 * 1024 || k % 8 != 0) return hipErrorInvalidValue;
+  launch_norm<0>(const_cast<uint16_t*>(h), nullptr, 0, g, eps, rows, k, out, s);
   return hipGetLastError();
 }
 
 hipError_t launch_resid_rmsnorm_rows(uint16_t* h, const float* part, int splits, const uint16_t* g, float eps,
                                      int rows, int k, uint16_t* out, hipStream_t s) {
-  if (k > 3 * 256 * 8 || k % 8 != 0) return hipErrorInvalidValue;
-  SS_LAUNCH(rmsnorm_rows_kernel, dim3(rows), dim3(256), 0, s, h, part, splits, rows, g, eps, k, out);
+  if (k > 8 * 1024 || k % 8 != 0) return hipErrorInvalidValue;
+  switch (part ? splits : 0) {
+    case 0: launch_norm<0>(h, part, splits, g, eps, rows, k, out, s); break;
+    case 1: launch_norm<1>(h, part, splits, g, eps, rows, k, out, s); break;
+    case 2: launch_norm<2>(h, part, splits, g, eps, rows, k, out, s); break;
+    case 3: launch_norm<3>(h, part, splits, g, eps, rows, k, out, s); break;
+    case 4: launch_norm<4>(h, part, splits, g, eps, rows, k, out, s); break;
+    case 5: launch_norm<5>(h, part, splits, g, eps, rows, k, out, s); break;
+    case 6: launch_norm<6>(h, part, splits, g, eps, rows, k, out, s); break;
+    case 7: launch_norm<7>(h, part, splits, g, eps, rows, k, out, s); break;
+    case 8: launch_norm<8>(h, part, splits, g, eps, rows, k, out, s); break;
+    default: launch_norm<-1>(h, part, splits, g, eps, rows, k, out, s); break;
+  }
   return hipGetLastError();
 }
 
