@@ -818,32 +818,45 @@ __global__ __launch_bounds__(128) void draft_merge_kernel(AttnArgs a, const int3
 // Merge of the verify partials: grid (q head, row), 128 threads (one per dim);
 // splits in order, batches of 4 independent loads.
 __global__ __launch_bounds__(128) void rows_merge_kernel(AttnArgs a) {
+  constexpr int B = 4;  // splits per batch of independent loads
   const int hq = blockIdx.x, row = blockIdx.y, dd = threadIdx.x;
   const int G = a.n_q / a.n_kv, hk = hq / G, g = hq % G;
+  const int64_t sstride = (int64_t)a.m * G * DREC;
+  const float* base = a.part + (((int64_t)hk * a.splits * a.m + row) * G + g) * DREC;
+  // the first batch is loaded before kv_len is known (splits clamped to the
+  // grid's), masked once the row's active splits are
+  float mv[B], lv[B], ov[B];
+  auto load = [&](int s0) {
+#pragma unroll
+    for (int t = 0; t < B; ++t) {
+      const float* q = base + min(s0 + t, a.splits - 1) * sstride;
+      mv[t] = q[0];
+      lv[t] = q[1];
+      ov[t] = q[4 + dd];
+    }
+  };
+  load(0);
   const int pos = *a.kv_len + a.pos_offset + row;
   if (pos < 0 || pos >= a.cap) return;
   const int active = (pos + DKPB) / DKPB;
-  const int64_t sstride = (int64_t)a.m * G * DREC;
-  const float* base = a.part + (((int64_t)hk * a.splits * a.m + row) * G + g) * DREC;
   float M = -INFINITY, L = 0.0f, o = 0.0f;
-  for (int s0 = 0; s0 < active; s0 += 4) {
-    float mv[4], lv[4], ov[4];
+  for (int s0 = 0; s0 < active; s0 += B) {
+    if (s0 > 0) load(s0);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < B; ++t) {
       const bool ok = s0 + t < active;
-      const float* q = base + (ok ? s0 + t : 0) * sstride;
-      mv[t] = ok ? q[0] : -INFINITY;
-      lv[t] = ok ? q[1] : 0.0f;
-      ov[t] = ok ? q[4 + dd] : 0.0f;
+      mv[t] = ok ? mv[t] : -INFINITY;
+      lv[t] = ok ? lv[t] : 0.0f;
+      ov[t] = ok ? ov[t] : 0.0f;
     }
     float Mb = M;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) Mb = fmaxf(Mb, mv[t]);
+    for (int t = 0; t < B; ++t) Mb = fmaxf(Mb, mv[t]);
     const float r = (M == -INFINITY) ? 0.0f : expf(M - Mb);
     L *= r;
     o *= r;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < B; ++t) {
       const float f = (mv[t] == -INFINITY) ? 0.0f : expf(mv[t] - Mb);
       L += f * lv[t];
       o += f * ov[t];

@@ -139,9 +139,24 @@ __global__ __launch_bounds__(kT) void sample_kernel(const uint16_t* __restrict__
   __shared__ unsigned long long red[4];
   __shared__ int s_pick;
   __shared__ bool s_last;
-  if (valid && *valid == 0) return;
+  // the first PRE partials of each thread are loaded before the position flag
+  // is tested (indices clamped, masked after)
+  constexpr int PRE = 8;
+  const int vflag = valid ? *valid : 1;
+  float pm[PRE];
+  int pa[PRE];
+#pragma unroll
+  for (int t = 0; t < PRE; ++t) {
+    const int i = min((int)threadIdx.x + t * kT, n_pre - 1);
+    pm[t] = pre_max[i];
+    pa[t] = pre_arg[i];
+  }
+  if (vflag == 0) return;
   ss::ArgMax a = {-INFINITY, 0x7fffffff};
-  for (int i = threadIdx.x; i < n_pre; i += kT) a = ss::better(a, ss::ArgMax{pre_max[i], pre_arg[i]});
+#pragma unroll
+  for (int t = 0; t < PRE; ++t)
+    if ((int)threadIdx.x + t * kT < n_pre) a = ss::better(a, ss::ArgMax{pm[t], pa[t]});
+  for (int i = threadIdx.x + PRE * kT; i < n_pre; i += kT) a = ss::better(a, ss::ArgMax{pre_max[i], pre_arg[i]});
   a = block_argmax(a, rv, ri);
   if (T == 0.0f) {
     if (blockIdx.x == 0 && threadIdx.x == 0) *token = a.i;
