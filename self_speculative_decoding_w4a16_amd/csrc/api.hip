@@ -43,7 +43,7 @@ int ok() {
 constexpr size_t kCounterBytes = 64 * 1024;
 constexpr size_t kSampleCounterOff = 16 * 1024;
 constexpr size_t kRejectCounterOff = 16 * 1024 + 256;
-constexpr size_t kAttnCounterOff = 20 * 1024;  // one per kv head (<= 1024)
+constexpr size_t kAttnCounterOff = 20 * 1024;  // draft attention: one per query head (<= 224)
 constexpr int kMaxTokens = 64;
 constexpr int kMaxGemvK = 28672;  // x (2 B) + half-group sums in 64 KiB of LDS
 constexpr int kMaxGamma = 64;
@@ -157,6 +157,7 @@ struct FwdWs {
   uint32_t* attn_counters;
   uint16_t *h, *xn, *qkv, *qrot, *attn, *act;
   float* attn_part;
+  int part_recs;  // partial records per query head in attn_part
   float* attn_ml;
   float* rope_cs;
   float* gemm_part;
@@ -199,6 +200,7 @@ size_t carve_fwd(const subspec_model* m, int mt, int cap, void* ws, FwdWs* o) {
   const size_t dsplits = (cap + draft_attn_keys_per_split() - 1) / draft_attn_keys_per_split();
   const size_t part_floats = (size_t)m->n_q_heads * std::max(vsplits * mt, dsplits) * (m->head_dim + 4);
   w.attn_part = (float*)c.take(part_floats * 4);
+  w.part_recs = (int)std::max(vsplits * mt, dsplits);
   w.attn_ml = (float*)c.take((size_t)mt * m->n_q_heads * 2 * 4);
   w.rope_cs = (float*)c.take((size_t)mt * m->head_dim * 4);
   w.gemm_part = (float*)c.take(max_gemm_partials(m, mt));
@@ -370,6 +372,8 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
     // keys of this launch: at most the capacity (dense), or the index plus the
     // speculative positions (sparse)
     at.max_keys = sparse ? std::min(st->capacity, st->index_cap + st->gamma_max) : st->capacity;
+    at.head_splits = std::min(draft_head_splits(at.max_keys), w.part_recs);
+    at.counters = w.attn_counters;
     {
       prof::Scope ps(SUBSPEC_K_ATTN_DRAFT, 0.0, s);
       HIPCHK(launch_decode_attention(at, w.valid, s));

@@ -20,6 +20,8 @@
 #include "internal.h"
 #include "profile.h"
 
+#include <stdlib.h>
+
 namespace {
 
 constexpr int D = 128;     // head dim handled by these kernels
@@ -329,12 +331,16 @@ struct DraftKeys {
 };
 
 // Key slots of the draft query of kv head hk (dense: slot t = position t).
+// Both scalars are read unconditionally (kv_len stands in for the absent
+// index length), so the loads need no branch and their latency overlaps
+// whatever follows until the first use.
 __device__ __forceinline__ DraftKeys draft_keys(const AttnArgs& a, int hk) {
   DraftKeys k;
-  k.kv0 = *a.kv_len;
-  k.pos = k.kv0 + a.pos_offset;
   const bool sparse = a.index != nullptr;
-  k.n_idx = sparse ? min(max(*a.n_index, 0), a.index_cap) : 0;
+  k.kv0 = *a.kv_len;
+  const int n_raw = *(sparse ? a.n_index : a.kv_len);
+  k.pos = k.kv0 + a.pos_offset;
+  k.n_idx = sparse ? min(max(n_raw, 0), a.index_cap) : 0;
   k.ilist = sparse ? a.index + (int64_t)hk * a.index_cap : nullptr;
   k.n_keys = sparse ? k.n_idx + a.pos_offset + 1 : k.pos + 1;
   return k;
@@ -532,9 +538,11 @@ __global__ __launch_bounds__(256) void draft_attn_kernel(AttnArgs a, const int32
   }
 }
 
-// Draft-step attention with one block per query head (short contexts: no
-// split partials, no merge launch): 512 threads = 8 waves; wave w takes the
-// 16-key chunks w, w + 8, ...  Lane (part kp = lane % 8, key kg = lane / 8)
+// Draft-step attention with S = a.head_splits blocks per query head (short
+// contexts; no merge launch): grid (query head, split), 512 threads = 8
+// waves; wave w of split s takes the 16-key chunks 8 s + w + 8 S i, so the
+// head's K/V reads are spread over S compute units (one unit alone cannot
+// pull them at HBM rate).  Lane (part kp = lane % 8, key kg = lane / 8)
 // holds 16 bytes of each half of the K and V rows of keys kg and 8 + kg of
 // the chunk, dims 8 kp .. +7 and 64 + 8 kp .. +7, so every load instruction
 // reads whole 128-byte rows of 8 keys; a score is the lane's partial dot
@@ -543,11 +551,14 @@ __global__ __launch_bounds__(256) void draft_attn_kernel(AttnArgs a, const int32
 // the keys it sees, rescaled only when a score exceeds m by more than 8 (in
 // log2 units; the weights stay below 2^8); lanes and waves are combined once
 // at the end.  Loads run 3 chunks ahead in a ring named statically.  Every
-// block of a kv head rotates the new key itself (its score needs it); the
-// group's first block appends the new K/V to the cache (the others never read
-// that slot from memory).
+// block of a kv head rotates the new key itself (its score needs it); split 0
+// scores it, and split 0 of the group's first head appends the new K/V to the
+// cache (no block reads that slot from memory).  With S > 1 each block writes
+// its partial (m, l, o[d]) with agent-coherent stores, waits for them to
+// complete and counts itself in counters[hq]; the block that sees the count
+// reach S reads the S partials with agent-coherent loads, writes the merged
+// row and resets the counter, so no cache flush is needed.
 constexpr int DQW = 8;            // waves
-constexpr int DQR = 3;            // chunks in flight per wave
 constexpr int DQ_MAXKEYS = 2048;  // keys up to which the per-head kernel is used
 
 template <int CTRL>
@@ -561,6 +572,11 @@ __device__ __forceinline__ float oct_sum(float v) {
   return v + dpp<0x141>(v);  // row_half_mirror: lane i <-> 7 - i, the other quad
 }
 
+// SPARSE: keys from the index (else slot t = cache row t); DQR: chunks in
+// flight per wave (1-3, no more than the launch's bound on keys fills).
+// Both are compile-time so that every load is issued on every path and each
+// wait covers exactly what it needs.
+template <bool SPARSE, int DQR>
 __global__ __launch_bounds__(DQW * 64) void draft_attn_head_kernel(AttnArgs a, const int32_t* valid) {
   constexpr int KW = 16;
   constexpr int NP = DQW * 4;  // partials: 4 rows of 16 lanes per wave
@@ -570,13 +586,35 @@ __global__ __launch_bounds__(DQW * 64) void draft_attn_head_kernel(AttnArgs a, c
   __shared__ float pm[NP], pl[NP], pf[NP];
   __shared__ float po[NP][D];
 
-  const int hq = blockIdx.x, tid = threadIdx.x;
+  const int hq = blockIdx.x, split = blockIdx.y, S = gridDim.y, tid = threadIdx.x;
   const int G = a.n_q / a.n_kv, hk = hq / G;
   const int lane = tid & 63, wave = tid >> 6;
+  const int c_first = split * DQW + wave, c_step = DQW * S;  // this wave's chunks
   const uint16_t* kc = a.k_cache + (int64_t)hk * a.cap * D;
   const uint16_t* vc = a.v_cache + (int64_t)hk * a.cap * D;
   const int kp = lane & 7, kg = lane >> 3;
-  const bool sparse = a.index != nullptr;
+  constexpr bool sparse = SPARSE;
+  // position flag and kv_len: read first (scalar loads; kv_len stands in for
+  // an absent flag, so no branch), tested after the loads that do not depend
+  // on them are issued and the rotation is done
+  const int v_raw = *(valid ? valid : a.kv_len);
+  const int vflag = valid ? v_raw : 1;
+  const DraftKeys ks = draft_keys(a, hk);
+
+  // The new token's q, k and v rows and its RoPE factors are loaded first,
+  // by every thread (indices wrapped; used by threads 0-63: query pairs,
+  // 64-127: new-key pairs, 32 active lanes each, 128-191: the new value):
+  // they do not depend on kv_len, and the rotation then overlaps the K/V
+  // loads instead of waiting for them.
+  const int half = D / 2, i2 = tid & 63;
+  const bool rot = tid < 128 && i2 < half / 2;
+  const uint16_t* xrow = (tid < 64) ? a.qkv + (int64_t)hq * D : a.qkv + (int64_t)(a.n_q + hk) * D;
+  const uint32_t xlo = reinterpret_cast<const uint32_t*>(xrow)[i2 & 31];
+  const uint32_t xhi = reinterpret_cast<const uint32_t*>(xrow + half)[i2 & 31];
+  const f32x4_t cs = reinterpret_cast<const f32x4_t*>(a.rope_cs)[i2 & 31];
+  const uint32_t vin = reinterpret_cast<const uint32_t*>(a.qkv + (int64_t)(a.n_q + a.n_kv + hk) * D)[i2];
+  // keep these loads ahead of the K/V loads (loads complete in issue order)
+  __builtin_amdgcn_sched_barrier(0);
 
   // chunk loads: [key kg, key 8 + kg] x [half 0, half 1] of the K/V rows at
   // row(t) for slot t
@@ -602,11 +640,34 @@ __global__ __launch_bounds__(DQW * 64) void draft_attn_head_kernel(AttnArgs a, c
   auto dense_row = [&](int t) { return min(t, a.cap - 1); };
   if (!sparse) {
 #pragma unroll
-    for (int j = 0; j < DQR; ++j) load_rows(wave + j * DQW, ring[j], dense_row);
+    for (int j = 0; j < DQR; ++j) load_rows(c_first + j * c_step, ring[j], dense_row);
   }
-  const int vflag = valid ? *valid : 1;
-  const DraftKeys ks = draft_keys(a, hk);
-  if (vflag == 0 || ks.pos < 0 || ks.pos >= a.cap) return;
+
+  // ---- RoPE of the query (threads 0-63) and the new key (64-127) into LDS;
+  // new V (128-191)
+  uint32_t klo = 0, khi = 0;
+  if (rot) {
+    const float a1 = ss::lo_bf(xlo), b1 = ss::hi_bf(xlo);
+    const float a2 = ss::lo_bf(xhi), b2 = ss::hi_bf(xhi);
+    klo = ss::pack_bf(ss::f2bf(a1 * cs[0] - a2 * cs[1]), ss::f2bf(b1 * cs[2] - b2 * cs[3]));
+    khi = ss::pack_bf(ss::f2bf(a2 * cs[0] + a1 * cs[1]), ss::f2bf(b2 * cs[2] + b1 * cs[3]));
+    uint32_t* dst = (tid < 64) ? qp : knew;
+    dst[i2] = klo;
+    dst[half / 2 + i2] = khi;
+  } else if (tid >= 128 && tid < 192) {
+    vnew[tid - 128] = vin;
+  }
+  if (vflag == 0 || ks.pos < 0 || ks.pos >= a.cap) return;  // block-uniform
+  // the group's first block appends the new K/V to the cache
+  if (hq % G == 0 && split == 0) {
+    if (rot && tid >= 64) {
+      uint32_t* kdst = reinterpret_cast<uint32_t*>(a.k_cache + ((int64_t)hk * a.cap + ks.pos) * D);
+      kdst[i2] = klo;
+      kdst[half / 2 + i2] = khi;
+    } else if (tid >= 128 && tid < 192) {
+      reinterpret_cast<uint32_t*>(a.v_cache + ((int64_t)hk * a.cap + ks.pos) * D)[tid - 128] = vin;
+    }
+  }
   const int last = ks.n_keys - 1;  // slot of the new key
   const int n_chunks = (ks.n_keys + KW - 1) / KW;
   auto sparse_row = [&](int t) {  // slots past the index: the speculative positions
@@ -624,40 +685,11 @@ __global__ __launch_bounds__(DQW * 64) void draft_attn_head_kernel(AttnArgs a, c
   if (sparse) {
 #pragma unroll
     for (int j = 0; j < DQR; ++j) {
-      const int c = wave + j * DQW;
+      const int c = c_first + j * c_step;
       load_chunk(c < n_chunks ? c : 0, ring[j]);
     }
   }
 
-  // ---- RoPE of the query (threads 0-63) and the new key (64-127); new V (128-191)
-  if (tid < 128) {
-    const int i2 = tid & 63;  // pair (2 i2, 2 i2 + 1) of each half
-    const bool is_q = tid < 64;
-    const uint16_t* x = is_q ? a.qkv + (int64_t)hq * D : a.qkv + (int64_t)(a.n_q + hk) * D;
-    const int half = D / 2;
-    if (i2 < half / 2) {
-      const uint32_t xlo = reinterpret_cast<const uint32_t*>(x)[i2];
-      const uint32_t xhi = reinterpret_cast<const uint32_t*>(x + half)[i2];
-      const f32x4_t cs = reinterpret_cast<const f32x4_t*>(a.rope_cs)[i2];
-      const float a1 = ss::lo_bf(xlo), b1 = ss::hi_bf(xlo);
-      const float a2 = ss::lo_bf(xhi), b2 = ss::hi_bf(xhi);
-      const uint32_t lo = ss::pack_bf(ss::f2bf(a1 * cs[0] - a2 * cs[1]), ss::f2bf(b1 * cs[2] - b2 * cs[3]));
-      const uint32_t hi = ss::pack_bf(ss::f2bf(a2 * cs[0] + a1 * cs[1]), ss::f2bf(b2 * cs[2] + b1 * cs[3]));
-      uint32_t* dst = is_q ? qp : knew;
-      dst[i2] = lo;
-      dst[half / 2 + i2] = hi;
-      if (!is_q && hq % G == 0) {
-        uint32_t* kdst = reinterpret_cast<uint32_t*>(a.k_cache + ((int64_t)hk * a.cap + ks.pos) * D);
-        kdst[i2] = lo;
-        kdst[half / 2 + i2] = hi;
-      }
-    }
-  } else if (tid < 192) {
-    const int i = tid - 128;
-    const uint32_t v = reinterpret_cast<const uint32_t*>(a.qkv + (int64_t)(a.n_q + a.n_kv + hk) * D)[i];
-    vnew[i] = v;
-    if (hq % G == 0) reinterpret_cast<uint32_t*>(a.v_cache + ((int64_t)hk * a.cap + ks.pos) * D)[i] = v;
-  }
   __syncthreads();
 
   // scores in log2 units: exp(s / sqrt(128)) = 2^(s * log2(e) / sqrt(128))
@@ -716,16 +748,16 @@ __global__ __launch_bounds__(DQW * 64) void draft_attn_head_kernel(AttnArgs a, c
   // each buffer is refilled with chunk c + DQR * DQW right after use; the last
   // pass may run past the wave's chunks: those are skipped, their loads (of
   // chunk 0) still issued, so the loads in flight are the same on every path
-  for (int c = wave; c < n_chunks; c += DQR * DQW) {
+  for (int c = c_first; c < n_chunks; c += DQR * c_step) {
 #pragma unroll
     for (int j = 0; j < DQR; ++j) {
-      const int cj = c + j * DQW, cn = cj + DQR * DQW;
+      const int cj = c + j * c_step, cn = cj + DQR * c_step;
       if (j == 0 || cj < n_chunks) step(cj, ring[j]);
       load_chunk(cn < n_chunks ? cn : 0, ring[j]);
     }
   }
-  // the new key, from LDS: the 8 lanes of key group 0 in wave 0
-  if (wave == 0 && kg == 0) {
+  // the new key, from LDS: the 8 lanes of key group 0 in wave 0 of split 0
+  if (split == 0 && wave == 0 && kg == 0) {
     const u32x4* kn = reinterpret_cast<const u32x4*>(knew);
     const u32x4* vn = reinterpret_cast<const u32x4*>(vnew);
     const u32x4 z = {0u, 0u, 0u, 0u};
@@ -764,15 +796,66 @@ __global__ __launch_bounds__(DQW * 64) void draft_attn_head_kernel(AttnArgs a, c
     pf[tid] = (pm[tid] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(pm[tid] - M);
   }
   __syncthreads();
+  float L = 0.0f, O = 0.0f;
   if (tid < D) {
-    float L = 0.0f, O = 0.0f;
 #pragma unroll
     for (int q = 0; q < NP; ++q) {
       L += pf[q] * pl[q];
       O += pf[q] * po[q][tid];
     }
-    a.out[(int64_t)hq * D + tid] = ss::f2bf(O / L);
   }
+  if (S == 1) {
+    if (tid < D) a.out[(int64_t)hq * D + tid] = ss::f2bf(O / L);
+    return;
+  }
+  // ---- S > 1: partial out, count in, the last block of the head merges
+  __shared__ int is_last;
+  float* rec = a.part + (int64_t)hq * S * DREC;
+  if (tid < D) {
+    float* dst = rec + (int64_t)split * DREC;
+    __hip_atomic_store(dst + 4 + tid, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < NP; ++q) M = fmaxf(M, pm[q]);
+      __hip_atomic_store(dst, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(dst + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  // the partial's stores complete (reach the agent coherence point) before
+  // the block counts itself
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0)
+    is_last = __hip_atomic_fetch_add(a.counters + hq, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(S - 1);
+  __syncthreads();
+  if (!is_last) return;
+  if (tid < D) {
+    // all S (<= 8) partials are loaded at once (indices clamped), then merged
+    // in split order
+    float mv[8], lv[8], ov[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float* q = rec + (int64_t)min(t, S - 1) * DREC;
+      mv[t] = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      lv[t] = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ov[t] = __hip_atomic_load(q + 4 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    float Ms = -INFINITY, Ls = 0.0f, Os = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float mt = mv[t], lt = lv[t], ot = ov[t];
+      if (t >= S || mt == -INFINITY) continue;
+      const float Mn = fmaxf(Ms, mt);
+      const float fo = (Ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(Ms - Mn);
+      const float fn = __builtin_amdgcn_exp2f(mt - Mn);
+      Ls = Ls * fo + lt * fn;
+      Os = Os * fo + ot * fn;
+      Ms = Mn;
+    }
+    a.out[(int64_t)hq * D + tid] = ss::f2bf(Os / Ls);
+  }
+  if (tid == 0) __hip_atomic_store(a.counters + hq, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Merge of the draft step's split partials: grid (q head), 128 threads (one
@@ -948,7 +1031,22 @@ hipError_t launch_rope_append(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_decode_attention(const AttnArgs& a, const int32_t* valid, hipStream_t s) {
   if (a.max_keys <= DQ_MAXKEYS) {
-    SS_LAUNCH(draft_attn_head_kernel, dim3(a.n_q), dim3(DQW * 64), 0, s, a, valid);
+    const int S = a.head_splits;
+    if (S < 1 || S > 8 || (S > 1 && (!a.counters || !a.part))) return hipErrorInvalidValue;
+    // chunks of 16 keys per wave in the first round: what the bound on keys fills, 1 to 3
+    const int per_wave = (a.max_keys + 16 * DQW * S - 1) / (16 * DQW * S);
+    const dim3 grid(a.n_q, S), block(DQW * 64);
+    const bool sp = a.index != nullptr;
+    if (per_wave <= 1) {
+      if (sp) SS_LAUNCH((draft_attn_head_kernel<true, 1>), grid, block, 0, s, a, valid);
+      else SS_LAUNCH((draft_attn_head_kernel<false, 1>), grid, block, 0, s, a, valid);
+    } else if (per_wave == 2) {
+      if (sp) SS_LAUNCH((draft_attn_head_kernel<true, 2>), grid, block, 0, s, a, valid);
+      else SS_LAUNCH((draft_attn_head_kernel<false, 2>), grid, block, 0, s, a, valid);
+    } else {
+      if (sp) SS_LAUNCH((draft_attn_head_kernel<true, 3>), grid, block, 0, s, a, valid);
+      else SS_LAUNCH((draft_attn_head_kernel<false, 3>), grid, block, 0, s, a, valid);
+    }
     return hipGetLastError();
   }
   const dim3 grid(a.n_kv, a.splits), block(256);
@@ -975,6 +1073,21 @@ hipError_t launch_rows_attention(const AttnArgs& a, hipStream_t s) {
 
 int decode_attn_keys_per_split() { return DKPB; }
 int draft_attn_keys_per_split() { return DSK; }
+
+// Key splits per query head: one per 96 keys of the launch's bound, at most 8
+// (at the 7B shape with ~900 keys, 8 splits measured 6.8 us a layer against
+// 7.5 for 4 and 8.6 for 1).  SUBSPEC_DRAFT_HEAD_SPLITS overrides, for
+// measurements.
+int draft_head_splits(int max_keys) {
+  static int forced = -1;
+  if (forced < 0) {
+    const char* e = getenv("SUBSPEC_DRAFT_HEAD_SPLITS");
+    forced = e ? atoi(e) : 0;
+  }
+  if (forced > 0) return forced < 8 ? forced : 8;
+  const int s = (max_keys + 95) / 96;
+  return s < 1 ? 1 : (s > 8 ? 8 : s);
+}
 
 int attn_scores_max_pairs() { return SMAXP; }
 

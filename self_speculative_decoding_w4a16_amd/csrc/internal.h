@@ -88,15 +88,22 @@ struct AttnArgs {
   const int32_t* n_index;
   int index_cap;
   int max_keys;  // draft step: bound on the keys of the launch (picks the kernel)
+  // draft step, per-head kernel: key splits per query head (1: no partials);
+  // with more, the head's partials go to part[hq][split][d + 4] and the last
+  // block of the head to arrive (counters[hq], zero between launches) merges
+  int head_splits;
+  uint32_t* counters;
 };
 hipError_t launch_rope_append(const AttnArgs& a, hipStream_t s);
 // One query position (the draft step): RoPE + KV append + attention into
-// out [Hq d] (bf16).  Up to 2048 keys (a.max_keys) one block per query head
-// does it all; beyond, per-split partials (m, l, o[d]) in part[kv head][split]
-// [group head][d + 4] are merged by a second launch.
+// out [Hq d] (bf16).  Up to 2048 keys (a.max_keys) a.head_splits blocks per
+// query head do it all (the last one to finish merges); beyond, per-split
+// partials (m, l, o[d]) in part[kv head][split][group head][d + 4] are merged
+// by a second launch.
 hipError_t launch_decode_attention(const AttnArgs& a, const int32_t* valid, hipStream_t s);
 int decode_attn_keys_per_split();  // verify rows
 int draft_attn_keys_per_split();   // draft step
+int draft_head_splits(int max_keys);  // key splits per query head of the per-head kernel
 // m query rows at positions kv_len + pos_offset + j (q_rot and the cache already
 // written by rope_append): per-row split partials, then a merge into out.
 hipError_t launch_rows_attention(const AttnArgs& a, hipStream_t s);
