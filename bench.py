@@ -30,8 +30,10 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # the same run (FETCH_SIZE 524328 KiB -> x2.0, WRITE_SIZE 1048576 KiB -> x1.0).
 # Reported only while the kernel sources hash to the value they were taken on.
 TRAFFIC = {
-    "bf16_gate_up": {"fetch_kib": 132954.3, "write_kib": 74.2, "fetch_scale": 2.0,
-                     "write_scale": 1.0, "sources": "bd209cf3c4275ddb"},
+    "bf16_gate_up": {"fetch_kib": 132949.3, "write_kib": 74.2, "fetch_scale": 2.0,
+                     "write_scale": 1.0, "sources": "c8f4919567384671"},
+    "w4_gate_up": {"fetch_kib": 37403.7, "write_kib": 148.0, "fetch_scale": 2.0,
+                   "write_scale": 1.0, "sources": "c8f4919567384671"},
 }
 GEMV_SOURCES = ("csrc/gemv.hip", "csrc/common.h", "csrc/internal.h")
 
@@ -312,6 +314,7 @@ def main():
         "roofline": roof_iso([dominant], dominant) if dominant in iso else roof(dominant),
         "roofline_w4_gemv": roof_iso([n for n in ("w4_qkv", "w4_o", "w4_gate_up", "w4_down") if n in iso],
                                      "w4_gemv (byte-weighted over one draft step's W4 GEMVs)"),
+        "roofline_w4_gate_up": roof_iso(["w4_gate_up"], "w4_gate_up") if "w4_gate_up" in iso else None,
         "roofline_bf16_gemv": roof_iso([n for n in ("bf16_qkv", "bf16_o", "bf16_gate_up", "bf16_down",
                                                     "lm_head") if n in iso],
                                        "bf16_gemv (byte-weighted over one draft step's bf16 GEMVs)"),
@@ -363,7 +366,9 @@ def isolated_gemvs(dm, shape, dev, reps=3, only=None, graph=True):
         "gate_up": ("gate_up", H, F, True, 2, "gemv_kernel<{r},{w},1,2>"),
         "down": ("down", F, H, False, 1, "gemv_kernel<{r},{w},0,1>"),
     }
-    rows_per_wave = lambda n, silu: 4 if (2 * n if silu else n) >= 16384 else (2 if (n >= 4096 or silu) else 1)
+    # rows per wave as the library picks them (the W4 gate/up GEMV takes one gate and one up row)
+    rows_per_wave = lambda n, silu, w4: (2 if w4 and silu else 4 if (2 * n if silu else n) >= 16384
+                                         else (2 if (n >= 4096 or silu) else 1))
 
     def timed(lins, k, n_out, norm, epi):
         run = lambda lin: _lib.gemv(lin, x[k], y, norm_w=g if norm else None, eps=eps, epilogue=epi,
@@ -414,7 +419,7 @@ def isolated_gemvs(dm, shape, dev, reps=3, only=None, graph=True):
             by = wb + 2 * k + 2 * n_out * (2 if epi == 1 else 1)
             us = timed(lins, k, n_out, norm, epi)
             del copies, lins
-            r = rows_per_wave(n_out, epi == 2)
+            r = rows_per_wave(n_out, epi == 2, w4)
             out[f"{kind}_{site}"] = {"avg_us": round(us, 3), "bytes_per_launch": round(by),
                                      "gbs": round(by / (us * 1e-6) / 1e9, 1), "per_step": len(layers),
                                      "symbol": sym.format(r=r, w="true" if w4 else "false")}

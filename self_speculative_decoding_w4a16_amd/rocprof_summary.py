@@ -40,6 +40,7 @@ def describe(name):
 
 
 _ROLES = {
+    "draft_attn_head_kernel": "draft attention: RoPE, KV append, key splits per head, last block merges",
     "draft_attn_kernel": "draft attention: RoPE, KV append, 64-key split partials",
     "draft_merge_kernel": "draft attention: merge of the split partials",
     "rows_attn_kernel": "verify attention: per-row split partials",
