@@ -366,9 +366,8 @@ def isolated_gemvs(dm, shape, dev, reps=3, only=None, graph=True):
         "gate_up": ("gate_up", H, F, True, 2, "gemv_kernel<{r},{w},1,2>"),
         "down": ("down", F, H, False, 1, "gemv_kernel<{r},{w},0,1>"),
     }
-    # rows per wave as the library picks them (the W4 gate/up GEMV takes one gate and one up row)
-    rows_per_wave = lambda n, silu, w4: (2 if w4 and silu else 4 if (2 * n if silu else n) >= 16384
-                                         else (2 if (n >= 4096 or silu) else 1))
+    # rows per wave as the library picks them (the gate/up GEMVs take one gate and one up row)
+    rows_per_wave = lambda n, silu, w4: (2 if silu else 4 if n >= 16384 else (2 if n >= 4096 else 1))
 
     def timed(lins, k, n_out, norm, epi):
         run = lambda lin: _lib.gemv(lin, x[k], y, norm_w=g if norm else None, eps=eps, epilogue=epi,
