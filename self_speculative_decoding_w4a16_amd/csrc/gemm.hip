@@ -12,9 +12,15 @@
 //    owns one 16-row tile and all ceil(m/16) position tiles.  The block walks
 //    its k range in chunks of 128: the activation chunk X[0..16 TT)[kc..+128)
 //    is staged in LDS (double-buffered, one barrier a chunk) and read by all
-//    NW waves; each wave streams its weight rows straight into registers.
-//    Lane (r, g) of MFMA step s feeds k = kc + 32 s + 8 g .. +7 of row r.
-//  * Pipeline: the weights and activations of WD = 3 chunks are in flight per
+//    NW waves.  Each wave loads its weight chunk row-contiguously (load s:
+//    rows 4s .. 4s+3, 256 bytes of each, so every load instruction reads
+//    whole 128-byte lines of 4 rows) and passes it through a 4 KiB LDS tile
+//    of its own, XOR-swizzled by row so that both the row-wise writes and the
+//    MFMA-layout reads are free of bank conflicts: lane (r, g) of MFMA step s
+//    reads k = kc + 32 s + 8 g .. +7 of row r.  (Loading straight into the
+//    MFMA layout reads 16 rows x 64 bytes per instruction, which streamed
+//    ~10 % slower.)
+//  * Pipeline: the weights and activations of WD = 2 chunks are in flight per
 //    wave.  Every load in the loop is unconditional (buffer loads: offsets
 //    outside the resource return zeros), so the compiler's count of loads in
 //    flight is exact and each wait covers only the chunk about to be used.
@@ -34,7 +40,7 @@ namespace {
 
 constexpr int KC = 128;             // k per chunk
 constexpr int KS = KC / 32;         // MFMA steps (k = 32 each) per chunk
-constexpr int WD = 3;               // weight chunks in flight per wave
+constexpr int WD = 2;               // weight chunks in flight per wave
 constexpr int XROW = KC + 8;        // LDS row stride (bf16) of the staged activations
 constexpr int kTargetBlocks = 512;  // split k until the grid has two blocks per compute unit
 constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 (CDNA): raw 32-bit data
@@ -77,6 +83,7 @@ __global__ __launch_bounds__(NWR * SS_WAVE) void gemm_kernel(GemmArgs a, int spl
   constexpr int XPT = (16 * TT * KC / 8 + NWR * SS_WAVE - 1) / (NWR * SS_WAVE);  // 16-byte pieces per thread
   constexpr int XR = XPT * NWR * SS_WAVE * 8 / KC;
   __shared__ __align__(16) uint16_t xs[2][XR][XROW];
+  __shared__ __align__(16) uint8_t wt[NWR][16 * KC * 2];  // per-wave weight tile [16 rows][KC], swizzled
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -106,7 +113,8 @@ __global__ __launch_bounds__(NWR * SS_WAVE) void gemm_kernel(GemmArgs a, int spl
       const_cast<uint16_t*>(a.w + row0 * (int64_t)K), 0, rows * K * 2, kBufferWord3);
   const __amdgpu_buffer_rsrc_t xrs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x), 0, a.m * K * 2, kBufferWord3);
-  const int wlane = (r16 * K + 8 * g4) * 2;  // byte offset of lane (r, g) in a chunk
+  // lane l loads row 4 s + l / 16 (load s), bytes 16 (l % 16) .. +15 of the chunk
+  const int wlane = ((lane >> 4) * K + 8 * (lane & 15)) * 2;
   auto chunk_off = [&](int c) { return c < c1 ? c * KC * 2 : kOutside; };
 
   // activation staging: thread -> (position, 16 bytes) of the chunk
@@ -130,7 +138,7 @@ __global__ __launch_bounds__(NWR * SS_WAVE) void gemm_kernel(GemmArgs a, int spl
   auto load_w = [&](int c, u32x4 (&av)[KS]) {
     const int off = wlane + chunk_off(c);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) av[s] = __builtin_amdgcn_raw_buffer_load_b128(wrs, off + 64 * s, 0, 0);
+    for (int s = 0; s < KS; ++s) av[s] = __builtin_amdgcn_raw_buffer_load_b128(wrs, off + 4 * K * 2 * s, 0, 0);
   };
 
   f32x4_t acc[TT];
@@ -156,12 +164,22 @@ __global__ __launch_bounds__(NWR * SS_WAVE) void gemm_kernel(GemmArgs a, int spl
     const int buf = (c - c0) & 1;
     store_x(xn, buf ^ 1);  // chunk c + 1 (zeros past the range)
     load_x(c + WD, xc);    // chunk c is already in LDS
+    // weights of chunk c through this wave's tile: 16-byte piece k of row r
+    // sits at slot k ^ r of the row (the wave's own LDS ops run in order, so
+    // the previous chunk's reads are done before these writes land)
+    uint8_t* wtw = &wt[wave][0];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
+      const int row = 4 * s + (lane >> 4);
+      *reinterpret_cast<u32x4*>(wtw + KC * 2 * row + 16 * ((lane & 15) ^ row)) = w[s];
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const u32x4 av = *reinterpret_cast<const u32x4*>(wtw + KC * 2 * r16 + 16 * ((4 * s + g4) ^ r16));
 #pragma unroll
       for (int u = 0; u < TT; ++u) {
         const u32x4 b = *reinterpret_cast<const u32x4*>(&xs[buf][16 * u + r16][32 * s + 8 * g4]);
-        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w[s]),
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
                                                          __builtin_bit_cast(bf16x8_t, b), acc[u], 0, 0, 0);
       }
     }

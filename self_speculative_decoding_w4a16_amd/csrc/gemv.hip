@@ -525,7 +525,7 @@ hipError_t launch_one(const GemvArgs& a, hipStream_t s, int* blocks_out) {
 template <bool W4, int PRO, int EPI>
 hipError_t launch_r(int R, const GemvArgs& a, hipStream_t s, int* b) {
   if constexpr (EPI == EPI_SILU) {
-    if (R >= 4) return launch_one<4, W4, PRO, EPI>(a, s, b);
+    (void)R;  // always one gate and one up row per wave
     return launch_one<2, W4, PRO, EPI>(a, s, b);
   } else {
     if (R >= 4) return launch_one<4, W4, PRO, EPI>(a, s, b);
@@ -552,23 +552,21 @@ hipError_t launch_w(int R, int pro, int epi, const GemvArgs& a, hipStream_t s, i
 // gate/up GEMVs take one gate and one up row per wave: at the 7B shape that
 // measured faster than two of each (W4: 3 %, bf16: 3 %), as the row groups
 // then spread more evenly over the waves of the persistent grid.
-static int pick_r(bool w4, int64_t n, int epi) {
-  (void)w4;
+static int pick_r(int64_t n, int epi) {
   if (epi == EPI_SILU) return 2;
-  const int64_t rows = (epi == EPI_SILU) ? 2 * n : n;
-  if (rows >= 16384) return 4;
-  if (rows >= 4096 || epi == EPI_SILU) return 2;
+  if (n >= 16384) return 4;
+  if (n >= 4096) return 2;
   return 1;
 }
 
 // Upper bound on the blocks of a launch (sizes per-block partial buffers).
 int gemv_max_blocks(bool w4, int64_t n, int epi) {
-  const int R = pick_r(w4, n, epi);
+  const int R = pick_r(n, epi);
   const int RO = (epi == EPI_SILU) ? R / 2 : R;
   return (int)gemv_blocks((n + RO - 1) / RO, w4, 0, kThreads);
 }
 
 hipError_t launch_gemv(bool w4, int pro, int epi, const GemvArgs& a, hipStream_t s, int* blocks_out) {
-  const int R = pick_r(w4, a.n, epi);
+  const int R = pick_r(a.n, epi);
   return w4 ? launch_w<true>(R, pro, epi, a, s, blocks_out) : launch_w<false>(R, pro, epi, a, s, blocks_out);
 }
