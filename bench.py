@@ -30,10 +30,10 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # the same run (FETCH_SIZE 524328 KiB -> x2.0, WRITE_SIZE 1048576 KiB -> x1.0).
 # Reported only while the kernel sources hash to the value they were taken on.
 TRAFFIC = {
-    "bf16_gate_up": {"fetch_kib": 132949.3, "write_kib": 74.2, "fetch_scale": 2.0,
-                     "write_scale": 1.0, "sources": "c8f4919567384671"},
+    "bf16_gate_up": {"fetch_kib": 132909.9, "write_kib": 148.6, "fetch_scale": 2.0,
+                     "write_scale": 1.0, "sources": "7acf3a99ef5697ca"},
     "w4_gate_up": {"fetch_kib": 37403.7, "write_kib": 148.0, "fetch_scale": 2.0,
-                   "write_scale": 1.0, "sources": "c8f4919567384671"},
+                   "write_scale": 1.0, "sources": "7acf3a99ef5697ca"},
 }
 GEMV_SOURCES = ("csrc/gemv.hip", "csrc/common.h", "csrc/internal.h")
 
