@@ -107,6 +107,36 @@ def test_verify_row_equals_draft_decode_when_shared(cuda):
     assert int(dec.n_accepted.item()) == 4
 
 
+@pytest.mark.parametrize("cap", [256, 1024])
+def test_draft_steps_past_capacity_are_skipped(cuda, cap):
+    """Positions at or past the KV capacity are skipped on the device (token -1,
+    no K/V written, the draft attention's split blocks all leave before they
+    count in); the next in-range draft step still matches the oracle, so the
+    per-head arrival counters were left at zero."""
+    gamma = 4
+    log(f"draft steps past capacity, cap {cap}")
+    dm, dec, om, kv = _setup(TINY, 13, cap, gamma, cap - 2)
+    toks = token_ids(2, TINY.vocab, 5)
+    dec.reset(cap - 2, toks[0])
+    for step in range(gamma):
+        _lib.draft_step(dm.c, dec.c, step, 0.0, None, dec.ws)
+    torch.cuda.synchronize()
+    t = dec.tokens.cpu().numpy()
+    assert t[1] >= 0 and t[2] >= 0  # positions cap-2, cap-1
+    assert t[3] == -1 and t[4] == -1  # positions cap, cap+1: skipped
+    # an in-range step afterwards
+    kv_len = cap // 2
+    dec.k_cache.copy_(torch.from_numpy(kv[0]).to(torch.bfloat16))
+    dec.v_cache.copy_(torch.from_numpy(kv[1]).to(torch.bfloat16))
+    dec.reset(kv_len, toks[1])
+    _lib.draft_step(dm.c, dec.c, 0, 0.0, None, dec.ws)
+    torch.cuda.synchronize()
+    ref = forward(om, (kv[0].copy(), kv[1].copy()), kv_len, [int(toks[1])], draft=True)[0]
+    got = host(dec.draft_logits[0])
+    assert rel_err(got, ref) < TOL
+    _argmax_ok(int(dec.tokens[1].item()), got, ref)
+
+
 def test_greedy_generation_matches_oracle(cuda):
     log("greedy generation tiny")
     dm, dec, om, _ = _setup(TINY, 8, 256, 4, 0)
