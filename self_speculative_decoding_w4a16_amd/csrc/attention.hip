@@ -550,7 +550,8 @@ __global__ __launch_bounds__(256) void draft_attn_kernel(AttnArgs a, const int32
 // running softmax (reference max m, sum l) and an output partial o[16] over
 // the keys it sees, rescaled only when a score exceeds m by more than 8 (in
 // log2 units; the weights stay below 2^8); lanes and waves are combined once
-// at the end.  Loads run 3 chunks ahead in a ring named statically.  Every
+// at the end.  Loads run DQR (1-3) chunks ahead in a ring named statically,
+// the first ones issued before kv_len is known (dense keys).  Every
 // block of a kv head rotates the new key itself (its score needs it); split 0
 // scores it, and split 0 of the group's first head appends the new K/V to the
 // cache (no block reads that slot from memory).  With S > 1 each block writes
