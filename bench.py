@@ -63,8 +63,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ar", action="store_true")
     ap.add_argument("--site", default=None,
-                    help="only launch one draft GEMV site (e.g. bf16_gate_up) back to back, then "
-                         "copy 1 GiB device to device: the workload for HBM counter runs")
+                    help="only launch one draft GEMV site (e.g. bf16_gate_up), or one verify GEMM "
+                         "(verify_gate_up, verify_down: gamma+1 positions, store epilogue), back to "
+                         "back, then copy 1 GiB device to device: the workload for counter runs")
     return ap.parse_args()
 
 
@@ -95,6 +96,28 @@ def main():
     w = model_weights(shape, 0, dev)
     dm = DeviceModel(shape, w)
     torch.cuda.synchronize()
+    if args.site and args.site.startswith("verify_"):
+        # the verify GEMM of one site on every shared layer's weights, 2 rounds
+        name = {"verify_gate_up": "gate_up", "verify_down": "down", "verify_qkv": "qkv",
+                "verify_o": "o"}[args.site]
+        shared = [l for l in range(shape.n_layers) if l not in dm.substitute_layers]
+        mats = [dm.w["layers"][l][name] for l in shared]
+        m = wl.gamma + 1
+        k = mats[0].shape[1]
+        x = (torch.randn(m, k, device=dev, generator=torch.Generator(device=dev).manual_seed(9)) * 0.5).bfloat16()
+        y = torch.empty(m, mats[0].shape[0], device=dev, dtype=torch.bfloat16)
+        ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            for wmat in mats:
+                _lib.bf16_gemm(wmat, x, y, ws)
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        n, kk = mats[0].shape
+        print(json.dumps({"site": args.site, "m": m, "n": n, "k": kk, "launches": 2 * len(mats),
+                          "copy_bytes": 1 << 30}), flush=True)
+        return
     if args.site:
         iso = isolated_gemvs(dm, shape, dev, reps=1, only=args.site, graph=False)
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
