@@ -859,25 +859,27 @@ __global__ __launch_bounds__(DQW * 64) void draft_attn_head_kernel(AttnArgs a, c
   if (tid == 0) __hip_atomic_store(a.counters + hq, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Merge of the draft step's split partials: grid (q head), 128 threads (one
-// per dim); splits in order, 8 independent loads at a time.  Writes the
-// attention output (bf16) that the output projection reads.
-__global__ __launch_bounds__(128) void draft_merge_kernel(AttnArgs a, const int32_t* valid) {
-  const int vflag = valid ? *valid : 1;
-  const int hq = blockIdx.x, dd = threadIdx.x;
-  const int G = a.n_q / a.n_kv, hk = hq / G, g = hq % G;
-  const DraftKeys ks = draft_keys(a, hk);
-  if (vflag == 0 || ks.pos < 0 || ks.pos >= a.cap) return;
-  const int active = min((ks.n_keys + DSK - 1) / DSK, a.splits);
-  const int64_t sstride = (int64_t)G * DREC;
-  const float* base = a.part + ((int64_t)hk * a.splits * G + g) * DREC;
-  float M = -INFINITY, L = 0.0f, o = 0.0f;
-  for (int s0 = 0; s0 < active; s0 += 8) {
+// Merge of one row's split partials (m, l, o[D]) by a block of MP x D
+// threads: thread (dim dd, group p) merges splits p, p + MP, ... in order,
+// 8 independent loads at a time (so a long context costs active / (8 MP)
+// memory round trips, not active / 8), then the MP group results are
+// combined in group order through LDS.  Returns (M, L, o) in the threads of
+// group 0; natural-log units.
+constexpr int MP = 8;  // split groups per merge block
+constexpr int kSeqMergeSplits = 32;  // verify merges with at most this many splits walk them in one thread
+__device__ __forceinline__ void merge_rows(const float* base, int64_t sstride, int active, int dd, int p,
+                                           float& M, float& L, float& o) {
+  __shared__ float gm[MP], gl[MP], go[MP][D];
+  M = -INFINITY;
+  L = 0.0f;
+  o = 0.0f;
+  for (int s0 = p; s0 < active; s0 += 8 * MP) {
     float mv[8], lv[8], ov[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const bool ok = s0 + t < active;
-      const float* q = base + (ok ? s0 + t : 0) * sstride;
+      const int sp = s0 + t * MP;
+      const bool ok = sp < active;
+      const float* q = base + (ok ? sp : 0) * sstride;
       mv[t] = ok ? q[0] : -INFINITY;
       lv[t] = ok ? q[1] : 0.0f;
       ov[t] = ok ? q[4 + dd] : 0.0f;
@@ -896,19 +898,52 @@ __global__ __launch_bounds__(128) void draft_merge_kernel(AttnArgs a, const int3
     }
     M = Mb;
   }
-  a.out[(int64_t)hq * D + dd] = ss::f2bf(o / L);
+  go[p][dd] = o;
+  if (dd == 0) {
+    gm[p] = M;
+    gl[p] = L;
+  }
+  __syncthreads();
+  if (p == 0) {
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < MP; ++q) Mt = fmaxf(Mt, gm[q]);
+    float Lt = 0.0f, ot = 0.0f;
+#pragma unroll
+    for (int q = 0; q < MP; ++q) {
+      const float f = (gm[q] == -INFINITY) ? 0.0f : expf(gm[q] - Mt);
+      Lt += f * gl[q];
+      ot += f * go[q][dd];
+    }
+    M = Mt;
+    L = Lt;
+    o = ot;
+  }
 }
 
-// Merge of the verify partials: grid (q head, row), 128 threads (one per dim);
-// splits in order, batches of 4 independent loads.
-__global__ __launch_bounds__(128) void rows_merge_kernel(AttnArgs a) {
+// Merge of the draft step's split partials: grid (q head), MP x 128 threads.
+// Writes the attention output (bf16) that the output projection reads.
+__global__ __launch_bounds__(MP * D) void draft_merge_kernel(AttnArgs a, const int32_t* valid) {
+  const int vflag = valid ? *valid : 1;
+  const int hq = blockIdx.x, dd = threadIdx.x % D, p = threadIdx.x / D;
+  const int G = a.n_q / a.n_kv, hk = hq / G, g = hq % G;
+  const DraftKeys ks = draft_keys(a, hk);
+  if (vflag == 0 || ks.pos < 0 || ks.pos >= a.cap) return;
+  const int active = min((ks.n_keys + DSK - 1) / DSK, a.splits);
+  float M, L, o;
+  merge_rows(a.part + ((int64_t)hk * a.splits * G + g) * DREC, (int64_t)G * DREC, active, dd, p, M, L, o);
+  if (p == 0) a.out[(int64_t)hq * D + dd] = ss::f2bf(o / L);
+}
+
+// Merge of the verify partials, few splits (short contexts): grid (q head,
+// row), 128 threads (one per dim); splits in order, batches of 4 independent
+// loads, the first batch loaded before kv_len is known.
+__global__ __launch_bounds__(128) void rows_merge_seq_kernel(AttnArgs a) {
   constexpr int B = 4;  // splits per batch of independent loads
   const int hq = blockIdx.x, row = blockIdx.y, dd = threadIdx.x;
   const int G = a.n_q / a.n_kv, hk = hq / G, g = hq % G;
   const int64_t sstride = (int64_t)a.m * G * DREC;
   const float* base = a.part + (((int64_t)hk * a.splits * a.m + row) * G + g) * DREC;
-  // the first batch is loaded before kv_len is known (splits clamped to the
-  // grid's), masked once the row's active splits are
   float mv[B], lv[B], ov[B];
   auto load = [&](int s0) {
 #pragma unroll
@@ -947,6 +982,25 @@ __global__ __launch_bounds__(128) void rows_merge_kernel(AttnArgs a) {
     }
     M = Mb;
   }
+  a.out[((int64_t)row * a.n_q + hq) * D + dd] = ss::f2bf(o / L);
+  if (a.ml && dd == 0) {
+    a.ml[((int64_t)row * a.n_q + hq) * 2] = M;
+    a.ml[((int64_t)row * a.n_q + hq) * 2 + 1] = L;
+  }
+}
+
+// Merge of the verify partials, many splits (long contexts): grid (q head,
+// row), MP x 128 threads.
+__global__ __launch_bounds__(MP * D) void rows_merge_kernel(AttnArgs a) {
+  const int hq = blockIdx.x, row = blockIdx.y, dd = threadIdx.x % D, p = threadIdx.x / D;
+  const int G = a.n_q / a.n_kv, hk = hq / G, g = hq % G;
+  const int pos = *a.kv_len + a.pos_offset + row;
+  if (pos < 0 || pos >= a.cap) return;
+  const int active = (pos + DKPB) / DKPB;
+  float M, L, o;
+  merge_rows(a.part + (((int64_t)hk * a.splits * a.m + row) * G + g) * DREC, (int64_t)a.m * G * DREC, active,
+             dd, p, M, L, o);
+  if (p != 0) return;
   a.out[((int64_t)row * a.n_q + hq) * D + dd] = ss::f2bf(o / L);
   if (a.ml && dd == 0) {
     a.ml[((int64_t)row * a.n_q + hq) * 2] = M;
@@ -1060,7 +1114,7 @@ hipError_t launch_decode_attention(const AttnArgs& a, const int32_t* valid, hipS
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  SS_LAUNCH(draft_merge_kernel, dim3(a.n_q), dim3(D), 0, s, a, valid);
+  SS_LAUNCH(draft_merge_kernel, dim3(a.n_q), dim3(MP * D), 0, s, a, valid);
   return hipGetLastError();
 }
 
@@ -1068,7 +1122,12 @@ hipError_t launch_rows_attention(const AttnArgs& a, hipStream_t s) {
   SS_LAUNCH(rows_attn_kernel, dim3(a.n_kv, a.splits), dim3(RW * 64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  SS_LAUNCH(rows_merge_kernel, dim3(a.n_q, a.m), dim3(D), 0, s, a);
+  // few splits: one thread per dim walks them in order; many (long
+  // contexts): MP split groups per block cut the serial memory round trips
+  if (a.splits <= kSeqMergeSplits)
+    SS_LAUNCH(rows_merge_seq_kernel, dim3(a.n_q, a.m), dim3(D), 0, s, a);
+  else
+    SS_LAUNCH(rows_merge_kernel, dim3(a.n_q, a.m), dim3(MP * D), 0, s, a);
   return hipGetLastError();
 }
 
