@@ -1014,60 +1014,108 @@ __global__ __launch_bounds__(MP * D) void rows_merge_kernel(AttnArgs a) {
 // query heads h of KV head hk of the attention probability
 // exp(q_{r,h} . k_j / sqrt(d) - M_{r,h}) / L_{r,h} (0 past row r's causal
 // limit), with (M, L) the softmax statistics the merge wrote.  Grid (KV head,
-// block of SKB keys), one thread per key: the thread holds k_j (64 bf16
-// pairs) and dots it with the W x G queries staged in LDS as bf16 pairs.
-constexpr int SKB = 256;
-constexpr int SMAXP = 240;  // W x G pairs that fit the 64 KiB of LDS
+// block of SKB = 128 keys), 4 waves: the key tile is staged in LDS and the
+// scores of the P = W x G queries against it come from the matrix cores
+// (v_mfma_f32_16x16x32_bf16, query tiles of 16 spread over the waves); each
+// probability tile is summed over its 16 queries, then the waves' sums are
+// added in wave order.
+constexpr int SKB = 128;
+constexpr int SMAXP = 240;  // W x G queries (15 tiles of 16)
+constexpr int SW = 4;       // waves of the score kernel
 
-__global__ __launch_bounds__(SKB) void attn_scores_kernel(AttnArgs a, float* score, int window) {
-  extern __shared__ uint32_t qsm[];  // [P][D/2] query pairs, then [P][2] (M, L)
+__global__ __launch_bounds__(SW * 64) void attn_scores_kernel(AttnArgs a, float* score, int window) {
+  constexpr int KROW = D + 8;  // padded LDS row (bf16)
+  __shared__ __align__(16) uint16_t ks[SKB][KROW];
+  __shared__ float mls[SMAXP][2];
+  __shared__ float red[SW][SKB];
   const int hk = blockIdx.x, tid = threadIdx.x;
-  const int kv0 = *a.kv_len;
-  const int n_keys = min(kv0 + a.m, a.cap);
-  const int j0 = blockIdx.y * SKB;
-  if (kv0 < 0 || j0 >= n_keys) return;  // block-uniform
+  const int lane = tid & 63, wave = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
   const int G = a.n_q / a.n_kv;
   const int W = min(window, a.m), r0 = a.m - W;
-  const int P = W * G;
-  float* mls = reinterpret_cast<float*>(qsm + P * (D / 2));
-  for (int e = tid; e < P * (D / 2); e += SKB) {
-    const int p = e / (D / 2), w = e % (D / 2);
-    const int r = r0 + p / G, h = p % G;
-    qsm[e] = reinterpret_cast<const uint32_t*>(a.q_rot + ((int64_t)r * a.n_q + hk * G + h) * D)[w];
+  const int P = W * G, n_qt = (P + 15) / 16;
+  const int j0 = blockIdx.y * SKB;
+  // the key tile (rows clamped to the cache; keys past n_keys are never
+  // written out) is loaded before kv_len is read
+  constexpr int PER = SKB * (D / 8) / (SW * 64);  // 16-byte pieces per thread
+  u32x4 kv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid + SW * 64 * i, key = e / (D / 8), q = e % (D / 8);
+    const int64_t row = (int64_t)hk * a.cap + min(j0 + key, a.cap - 1);
+    kv[i] = reinterpret_cast<const u32x4*>(a.k_cache + row * D)[q];
   }
-  for (int p = tid; p < P; p += SKB) {
+  const int kv0 = *a.kv_len;
+  const int n_keys = min(kv0 + a.m, a.cap);
+  if (kv0 < 0 || j0 >= n_keys) return;  // block-uniform
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid + SW * 64 * i, key = e / (D / 8), q = e % (D / 8);
+    *reinterpret_cast<u32x4*>(&ks[key][8 * q]) = kv[i];
+  }
+  for (int p = tid; p < P; p += SW * 64) {
     const int r = r0 + p / G, h = p % G;
-    mls[2 * p] = a.ml[((int64_t)r * a.n_q + hk * G + h) * 2];
-    mls[2 * p + 1] = a.ml[((int64_t)r * a.n_q + hk * G + h) * 2 + 1];
+    mls[p][0] = a.ml[((int64_t)r * a.n_q + hk * G + h) * 2];
+    mls[p][1] = a.ml[((int64_t)r * a.n_q + hk * G + h) * 2 + 1];
   }
   __syncthreads();
-  const int j = j0 + tid;
-  if (j >= n_keys) return;
-  uint32_t kw[D / 2];
-  const u32x4* kp = reinterpret_cast<const u32x4*>(a.k_cache + ((int64_t)hk * a.cap + j) * D);
-#pragma unroll
-  for (int i = 0; i < D / 8; ++i) {
-    const u32x4 v = kp[i];
-    kw[4 * i] = v.x;
-    kw[4 * i + 1] = v.y;
-    kw[4 * i + 2] = v.z;
-    kw[4 * i + 3] = v.w;
-  }
+
   const float scale = 0.088388347648318440f;  // 1/sqrt(128)
-  float acc = 0.0f;
-  for (int p = 0; p < P; ++p) {
-    const int r = r0 + p / G;
-    if (j > kv0 + r) continue;  // past row r's causal limit
-    const uint32_t* q = qsm + p * (D / 2);
-    float d0 = 0.0f, d1 = 0.0f;
+  float acc[SKB / 16];  // this wave's sum for key 16 n + r16 (lanes g4 == 0)
 #pragma unroll
-    for (int w = 0; w < D / 2; w += 2) {
-      d0 = ss::dot2(kw[w], q[w], d0);
-      d1 = ss::dot2(kw[w + 1], q[w + 1], d1);
+  for (int n = 0; n < SKB / 16; ++n) acc[n] = 0.0f;
+  for (int t = wave; t < n_qt; t += SW) {
+    // A operand: lane -> query 16 t + r16, dims 32 st + 8 g4 .. +7
+    const int pa = 16 * t + r16;
+    const bool aok = pa < P;
+    const u32x4* qp = reinterpret_cast<const u32x4*>(
+        a.q_rot + ((int64_t)(r0 + (aok ? pa : 0) / G) * a.n_q + hk * G + (aok ? pa : 0) % G) * D);
+    u32x4 qa[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) qa[st] = aok ? qp[4 * st + g4] : u32x4{0u, 0u, 0u, 0u};
+    // this lane's queries 16 t + 4 g4 + i: (M, L) and causal limit
+    float mq[4], lq[4];
+    int lim[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = 16 * t + 4 * g4 + i;
+      const bool ok = p < P;
+      mq[i] = ok ? mls[p][0] : 0.0f;
+      lq[i] = ok ? mls[p][1] : 1.0f;
+      lim[i] = ok ? kv0 + r0 + p / G : -1;  // keys <= this row's position
     }
-    acc += expf((d0 + d1) * scale - mls[2 * p]) / mls[2 * p + 1];
+#pragma unroll
+    for (int n = 0; n < SKB / 16; ++n) {
+      f32x4_t sa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const u32x4 b = *reinterpret_cast<const u32x4*>(&ks[16 * n + r16][32 * st + 8 * g4]);
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[st]),
+                                                     __builtin_bit_cast(bf16x8_t, b), sa, 0, 0, 0);
+      }
+      const int j = j0 + 16 * n + r16;
+      float c = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (j <= lim[i]) c += expf(sa[i] * scale - mq[i]) / lq[i];
+      c += __shfl_xor(c, 16, 64);
+      c += __shfl_xor(c, 32, 64);
+      acc[n] += c;
+    }
   }
-  score[(int64_t)hk * a.cap + j] = acc;
+  if (g4 == 0) {
+#pragma unroll
+    for (int n = 0; n < SKB / 16; ++n) red[wave][16 * n + r16] = acc[n];
+  }
+  __syncthreads();
+  if (tid < SKB) {
+    const int j = j0 + tid;
+    if (j < n_keys) {
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < SW; ++w) v += red[w][tid];
+      score[(int64_t)hk * a.cap + j] = v;
+    }
+  }
 }
 
 }  // namespace
@@ -1155,7 +1203,6 @@ hipError_t launch_attn_scores(const AttnArgs& a, float* score, int window, hipSt
   const int G = a.n_q / a.n_kv;
   const int P = (window < a.m ? window : a.m) * G;
   if (P > SMAXP || P < 1 || !a.ml) return hipErrorInvalidValue;
-  const size_t lds = (size_t)P * (D / 2) * 4 + (size_t)P * 8;
-  SS_LAUNCH(attn_scores_kernel, dim3(a.n_kv, (a.cap + SKB - 1) / SKB), dim3(SKB), lds, s, a, score, window);
+  SS_LAUNCH(attn_scores_kernel, dim3(a.n_kv, (a.cap + SKB - 1) / SKB), dim3(SW * 64), 0, s, a, score, window);
   return hipGetLastError();
 }
