@@ -560,7 +560,8 @@ __global__ __launch_bounds__(256) void draft_attn_kernel(AttnArgs a, const int32
 // reach S reads the S partials with agent-coherent loads, writes the merged
 // row and resets the counter, so no cache flush is needed.
 constexpr int DQW = 8;            // waves
-constexpr int DQ_MAXKEYS = 2048;  // keys up to which the per-head kernel is used
+constexpr int DQ_MAXKEYS = 8192;  // keys up to which the per-head kernel is used
+constexpr int DQ_MAXSPLITS = 16;  // blocks per query head, at most
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -832,27 +833,29 @@ __global__ __launch_bounds__(DQW * 64) void draft_attn_head_kernel(AttnArgs a, c
   __syncthreads();
   if (!is_last) return;
   if (tid < D) {
-    // all S (<= 8) partials are loaded at once (indices clamped), then merged
-    // in split order
+    // the S (<= DQ_MAXSPLITS) partials, 8 loads in flight (indices clamped),
+    // merged in split order
+    float Ms = -INFINITY, Ls = 0.0f, Os = 0.0f;
+    for (int t0 = 0; t0 < S; t0 += 8) {
     float mv[8], lv[8], ov[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const float* q = rec + (int64_t)min(t, S - 1) * DREC;
+      const float* q = rec + (int64_t)min(t0 + t, S - 1) * DREC;
       mv[t] = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       lv[t] = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       ov[t] = __hip_atomic_load(q + 4 + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    float Ms = -INFINITY, Ls = 0.0f, Os = 0.0f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const float mt = mv[t], lt = lv[t], ot = ov[t];
-      if (t >= S || mt == -INFINITY) continue;
+      if (t0 + t >= S || mt == -INFINITY) continue;
       const float Mn = fmaxf(Ms, mt);
       const float fo = (Ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(Ms - Mn);
       const float fn = __builtin_amdgcn_exp2f(mt - Mn);
       Ls = Ls * fo + lt * fn;
       Os = Os * fo + ot * fn;
       Ms = Mn;
+    }
     }
     a.out[(int64_t)hq * D + tid] = ss::f2bf(Os / Ls);
   }
@@ -1135,7 +1138,7 @@ hipError_t launch_rope_append(const AttnArgs& a, hipStream_t s) {
 hipError_t launch_decode_attention(const AttnArgs& a, const int32_t* valid, hipStream_t s) {
   if (a.max_keys <= DQ_MAXKEYS) {
     const int S = a.head_splits;
-    if (S < 1 || S > 8 || (S > 1 && (!a.counters || !a.part))) return hipErrorInvalidValue;
+    if (S < 1 || S > DQ_MAXSPLITS || (S > 1 && (!a.counters || !a.part))) return hipErrorInvalidValue;
     // chunks of 16 keys per wave in the first round: what the bound on keys fills, 1 to 3
     const int per_wave = (a.max_keys + 16 * DQW * S - 1) / (16 * DQW * S);
     const dim3 grid(a.n_q, S), block(DQW * 64);
@@ -1184,15 +1187,16 @@ int draft_attn_keys_per_split() { return DSK; }
 
 // Key splits per query head: one per 96 keys of the launch's bound, at most 8
 // (at the 7B shape with ~900 keys, 8 splits measured 6.8 us a layer against
-// 7.5 for 4 and 8.6 for 1).  SUBSPEC_DRAFT_HEAD_SPLITS overrides, for
-// measurements.
+// 7.5 for 4 and 8.6 for 1; over a ~6000-key sparse index, 8 splits 21.4 us
+// against 26.9 for 16).  SUBSPEC_DRAFT_HEAD_SPLITS overrides (up to
+// DQ_MAXSPLITS), for measurements.
 int draft_head_splits(int max_keys) {
   static int forced = -1;
   if (forced < 0) {
     const char* e = getenv("SUBSPEC_DRAFT_HEAD_SPLITS");
     forced = e ? atoi(e) : 0;
   }
-  if (forced > 0) return forced < 8 ? forced : 8;
+  if (forced > 0) return forced < DQ_MAXSPLITS ? forced : DQ_MAXSPLITS;
   const int s = (max_keys + 95) / 96;
   return s < 1 ? 1 : (s > 8 ? 8 : s);
 }

@@ -96,7 +96,7 @@ struct AttnArgs {
 };
 hipError_t launch_rope_append(const AttnArgs& a, hipStream_t s);
 // One query position (the draft step): RoPE + KV append + attention into
-// out [Hq d] (bf16).  Up to 2048 keys (a.max_keys) a.head_splits blocks per
+// out [Hq d] (bf16).  Up to 8192 keys (a.max_keys) a.head_splits blocks per
 // query head do it all (the last one to finish merges); beyond, per-split
 // partials (m, l, o[d]) in part[kv head][split][group head][d + 4] are merged
 // by a second launch.
