@@ -510,7 +510,8 @@ int subspec_verify(const subspec_model* m, const subspec_state* st, int32_t n_to
     at.rope_cs = w.rope_cs;
     at.part = w.attn_part;
     at.out = w.attn;
-    at.splits = (st->capacity + decode_attn_keys_per_split() - 1) / decode_attn_keys_per_split();
+    at.split_keys = verify_attn_split_keys(st->capacity, m->n_kv_heads, mt * (m->n_q_heads / m->n_kv_heads));
+    at.splits = (st->capacity + at.split_keys - 1) / at.split_keys;
     if (st->kv_score) at.ml = w.attn_ml;
     {
       prof::Scope ps(SUBSPEC_K_ATTN_VERIFY, 0.0, s);

@@ -938,6 +938,197 @@ __global__ __launch_bounds__(MP * D) void draft_merge_kernel(AttnArgs a, const i
   if (p == 0) a.out[(int64_t)hq * D + dd] = ss::f2bf(o / L);
 }
 
+// Verify attention for long contexts: as rows_attn_kernel, but one block
+// walks a.split_keys / 128 consecutive 128-key tiles of its kv head, keeping
+// per query row a running (max, sum, o) across them, and the next tile's K/V
+// are loaded into registers while the current one is used from LDS, so the
+// loads overlap the arithmetic and the partials (and the merge) shrink by the
+// tile count.  Needs at most one query tile per wave (m x G <= 16 RW rows).
+__global__ __launch_bounds__(RW * 64) void rows_attn_long_kernel(AttnArgs a) {
+  constexpr int NT = 8;
+  constexpr int KROW = D + 8;
+  constexpr int VROW = DKPB + 8;
+  constexpr int NTH = RW * 64;
+  constexpr int PER = (DKPB / 2) * (D / 8) / NTH;
+  __shared__ __align__(16) uint16_t ks[DKPB][KROW];
+  __shared__ __align__(16) uint32_t vt[D][VROW / 2];
+  __shared__ __align__(16) uint16_t pt[RW][2][16][VROW];
+
+  const int hk = blockIdx.x, split = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
+  const int G = a.n_q / a.n_kv, Qn = a.m * G;
+  const int n_tiles = (Qn + 15) / 16;
+  const int kbase = split * a.split_keys;
+  const bool has_q = wave < n_tiles;  // this wave's query tile: wave
+  const int t = has_q ? wave : 0;
+
+  u32x4 qa[4];
+  {
+    const int qi = 16 * t + r16;
+    const bool qok = has_q && qi < Qn;
+    const int j = qok ? qi / G : 0, h = qok ? qi % G : 0;
+    const u32x4* qp = reinterpret_cast<const u32x4*>(a.q_rot + ((int64_t)j * a.n_q + hk * G + h) * D);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) qa[st] = qok ? qp[4 * st + g4] : u32x4{0u, 0u, 0u, 0u};
+  }
+  // K/V of tile tau into registers: thread -> (key pair kp, 16-byte piece q)
+  u32x4 k2[PER][2], v2[PER][2];
+  auto load_tile = [&](int tau) {
+    const int k0 = kbase + tau * DKPB;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + NTH * i, kp = e & (DKPB / 2 - 1), q = e / (DKPB / 2);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int64_t row = (int64_t)hk * a.cap + min(k0 + 2 * kp + u, a.cap - 1);
+        k2[i][u] = reinterpret_cast<const u32x4*>(a.k_cache + row * D)[q];
+        v2[i][u] = reinterpret_cast<const u32x4*>(a.v_cache + row * D)[q];
+      }
+    }
+  };
+  load_tile(0);
+  const int kv0 = *a.kv_len + a.pos_offset;  // position of row 0
+  const int n_keys = min(kv0 + a.m, a.cap);
+  if (kv0 < 0 || n_keys <= kbase) return;  // block-uniform
+  const int n_tau = min(a.split_keys / DKPB, (n_keys - kbase + DKPB - 1) / DKPB);
+
+  float Mr[4], Lr[4];
+  f32x4_t O[NT];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    Mr[i] = -INFINITY;
+    Lr[i] = 0.0f;
+  }
+#pragma unroll
+  for (int n = 0; n < NT; ++n) O[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const float scale = 0.088388347648318440f;  // 1/sqrt(128)
+  const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(&vt[0][0]);
+
+  for (int tau = 0; tau < n_tau; ++tau) {
+    const int k0 = kbase + tau * DKPB;
+    if (tau > 0) __syncthreads();  // every wave is done with the previous tile
+    // stage tile tau (keys past n_keys as zeros)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + NTH * i, kp = e & (DKPB / 2 - 1), q = e / (DKPB / 2);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (k0 + 2 * kp + u >= n_keys) {
+          k2[i][u] = u32x4{0u, 0u, 0u, 0u};
+          v2[i][u] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x4*>(&ks[2 * kp + u][8 * q]) = k2[i][u];
+      const uint32_t w0[4] = {v2[i][0].x, v2[i][0].y, v2[i][0].z, v2[i][0].w};
+      const uint32_t w1[4] = {v2[i][1].x, v2[i][1].y, v2[i][1].z, v2[i][1].w};
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        vt[8 * q + 2 * tt][kp] = (w0[tt] & 0xffffu) | (w1[tt] << 16);
+        vt[8 * q + 2 * tt + 1][kp] = (w0[tt] >> 16) | (w1[tt] & 0xffff0000u);
+      }
+    }
+    __syncthreads();
+    // the next tile's loads overlap this tile's arithmetic (past the block's
+    // tiles they read clamped rows that are never staged)
+    load_tile(tau + 1 < n_tau ? tau + 1 : tau);
+    if (!has_q) continue;
+    // S = Q K^T
+    f32x4_t sa[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      sa[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const u32x4 b = *reinterpret_cast<const u32x4*>(&ks[16 * n + r16][32 * st + 8 * g4]);
+        sa[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[st]),
+                                                        __builtin_bit_cast(bf16x8_t, b), sa[n], 0, 0, 0);
+      }
+    }
+    float mx[4], sm[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int qi = 16 * t + 4 * g4 + i;
+      const bool qv = qi < Qn;
+      const int last_key = kv0 + (qv ? qi / G : 0);
+      const bool any = qv && last_key < a.cap && k0 <= last_key;
+      float m = -INFINITY;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const bool ok = any && k0 + 16 * n + r16 <= last_key;
+        sa[n][i] = ok ? sa[n][i] * scale : -INFINITY;
+        m = fmaxf(m, sa[n][i]);
+      }
+      mx[i] = row16_max(m);
+      float l = 0.0f;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const float pv = (mx[i] == -INFINITY) ? 0.0f
+                                              : __builtin_amdgcn_exp2f((sa[n][i] - mx[i]) * 1.4426950408889634f);
+        sa[n][i] = pv;
+        l += pv;
+      }
+      sm[i] = row16_sum(l);
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = sa[n][i];
+        const uint16_t hi = ss::f2bf(pv);
+        pt[wave][0][4 * g4 + i][16 * n + r16] = hi;
+        pt[wave][1][4 * g4 + i][16 * n + r16] = ss::f2bf(pv - ss::bf2f(hi));
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    f32x4_t oa[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) oa[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const u32x4 ph = *reinterpret_cast<const u32x4*>(&pt[wave][0][r16][32 * st + 8 * g4]);
+      const u32x4 pl = *reinterpret_cast<const u32x4*>(&pt[wave][1][r16][32 * st + 8 * g4]);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const u32x4 b = *reinterpret_cast<const u32x4*>(vt16 + (16 * n + r16) * VROW + 32 * st + 8 * g4);
+        oa[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ph),
+                                                        __builtin_bit_cast(bf16x8_t, b), oa[n], 0, 0, 0);
+        oa[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pl),
+                                                        __builtin_bit_cast(bf16x8_t, b), oa[n], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();  // the P tile is rewritten by the next key tile
+    // fold the tile into the running (max, sum, o) of this lane's rows
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (mx[i] == -INFINITY) continue;
+      const float Mn = fmaxf(Mr[i], mx[i]);
+      const float fo = (Mr[i] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((Mr[i] - Mn) * 1.4426950408889634f);
+      const float fn = __builtin_amdgcn_exp2f((mx[i] - Mn) * 1.4426950408889634f);
+      Lr[i] = Lr[i] * fo + sm[i] * fn;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) O[n][i] = O[n][i] * fo + oa[n][i] * fn;
+      Mr[i] = Mn;
+    }
+  }
+  if (!has_q) return;
+  // partials of this lane's rows (every row has a key in each split up to its own)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int qi = 16 * t + 4 * g4 + i;
+    if (qi >= Qn || Mr[i] == -INFINITY) continue;
+    const int row = qi / G, h = qi % G;
+    float* dst = a.part + (((int64_t)(hk * a.splits + split) * a.m + row) * G + h) * DREC;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) dst[4 + 16 * n + r16] = O[n][i];
+    if (r16 == 0) {
+      dst[0] = Mr[i];
+      dst[1] = Lr[i];
+    }
+  }
+}
+
 // Merge of the verify partials, few splits (short contexts): grid (q head,
 // row), 128 threads (one per dim); splits in order, batches of 4 independent
 // loads, the first batch loaded before kv_len is known.
@@ -960,7 +1151,8 @@ __global__ __launch_bounds__(128) void rows_merge_seq_kernel(AttnArgs a) {
   load(0);
   const int pos = *a.kv_len + a.pos_offset + row;
   if (pos < 0 || pos >= a.cap) return;
-  const int active = (pos + DKPB) / DKPB;
+  const int kps = a.split_keys > 0 ? a.split_keys : DKPB;
+  const int active = (pos + kps) / kps;
   float M = -INFINITY, L = 0.0f, o = 0.0f;
   for (int s0 = 0; s0 < active; s0 += B) {
     if (s0 > 0) load(s0);
@@ -999,7 +1191,8 @@ __global__ __launch_bounds__(MP * D) void rows_merge_kernel(AttnArgs a) {
   const int G = a.n_q / a.n_kv, hk = hq / G, g = hq % G;
   const int pos = *a.kv_len + a.pos_offset + row;
   if (pos < 0 || pos >= a.cap) return;
-  const int active = (pos + DKPB) / DKPB;
+  const int kps = a.split_keys > 0 ? a.split_keys : DKPB;
+  const int active = (pos + kps) / kps;
   float M, L, o;
   merge_rows(a.part + (((int64_t)hk * a.splits * a.m + row) * G + g) * DREC, (int64_t)a.m * G * DREC, active,
              dd, p, M, L, o);
@@ -1170,7 +1363,12 @@ hipError_t launch_decode_attention(const AttnArgs& a, const int32_t* valid, hipS
 }
 
 hipError_t launch_rows_attention(const AttnArgs& a, hipStream_t s) {
-  SS_LAUNCH(rows_attn_kernel, dim3(a.n_kv, a.splits), dim3(RW * 64), 0, s, a);
+  if (a.split_keys > DKPB) {
+    if (a.split_keys % DKPB != 0 || a.m * (a.n_q / a.n_kv) > 16 * RW) return hipErrorInvalidValue;
+    SS_LAUNCH(rows_attn_long_kernel, dim3(a.n_kv, a.splits), dim3(RW * 64), 0, s, a);
+  } else {
+    SS_LAUNCH(rows_attn_kernel, dim3(a.n_kv, a.splits), dim3(RW * 64), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // few splits: one thread per dim walks them in order; many (long
@@ -1183,6 +1381,17 @@ hipError_t launch_rows_attention(const AttnArgs& a, hipStream_t s) {
 }
 
 int decode_attn_keys_per_split() { return DKPB; }
+
+// One 128-key tile per block while the grid has under ~1024 blocks; past
+// that (long contexts) a block walks up to 8 tiles, if its query tiles fit
+// one per wave.
+int verify_attn_split_keys(int cap, int n_kv, int rows_x_group) {
+  const int tiles = (cap + DKPB - 1) / DKPB;
+  int t = (tiles * n_kv + 1023) / 1024;
+  if (t > 8) t = 8;
+  if (t < 2 || rows_x_group > 16 * RW) return DKPB;
+  return DKPB * t;
+}
 int draft_attn_keys_per_split() { return DSK; }
 
 // Key splits per query head: one per 96 keys of the launch's bound, at most 8

@@ -80,6 +80,7 @@ struct AttnArgs {
   const float* rope_cs;  // [m][d/2][2] (cos, sin) of each row's position
   float* part;          // split partials [Hkv][splits][m][G][d + 4]
   int splits;           // grid splits over keys (128 keys each)
+  int split_keys;       // verify: keys per split block (0: 128; more: one block walks several 128-key tiles)
   uint16_t* out;        // [m][Hq d]
   float* ml;            // optional [m][Hq][2]: softmax (max, sum) of each row and head
   // sparse draft (draft step only; index == nullptr: dense): keys are
@@ -102,6 +103,9 @@ hipError_t launch_rope_append(const AttnArgs& a, hipStream_t s);
 // by a second launch.
 hipError_t launch_decode_attention(const AttnArgs& a, const int32_t* valid, hipStream_t s);
 int decode_attn_keys_per_split();  // verify rows
+// Keys per split block of the verify attention for a launch over `cap` keys,
+// `n_kv` KV heads and `rows_x_group` = query rows x GQA group.
+int verify_attn_split_keys(int cap, int n_kv, int rows_x_group);
 int draft_attn_keys_per_split();   // draft step
 int draft_head_splits(int max_keys);  // key splits per query head of the per-head kernel
 // m query rows at positions kv_len + pos_offset + j (q_rot and the cache already

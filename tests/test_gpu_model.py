@@ -46,7 +46,8 @@ def _setup(shape, seed, cap, gamma, kv_len, subs=None, T=0.0, Td=0.0, device="cu
     return dm, dec, om, kv
 
 
-@pytest.mark.parametrize("shape_name", ["tiny", "tiny_short", "layer7b", "layer7b_cap1024", "layer32b"])
+@pytest.mark.parametrize("shape_name", ["tiny", "tiny_short", "layer7b", "layer7b_cap1024", "layer7b_ctx40k",
+                                        "layer32b"])
 def test_draft_step_and_verify_match_oracle(cuda, shape_name):
     gamma = 16
     if shape_name == "tiny":
@@ -57,6 +58,9 @@ def test_draft_step_and_verify_match_oracle(cuda, shape_name):
         shape, kv_len, cap = QWEN7B.with_(n_layers=1, n_shared=0), 1024, 1088
     elif shape_name == "layer7b_cap1024":
         shape, kv_len, cap = QWEN7B.with_(n_layers=1, n_shared=0), 1000, 1024
+    elif shape_name == "layer7b_ctx40k":
+        # long context: the verify attention walks several 128-key tiles per block
+        shape, kv_len, cap = QWEN7B.with_(n_layers=1, n_shared=0), 40000, 40064
     else:  # one 32B-shaped layer at the 32B workload's context and draft length
         shape, kv_len, cap, gamma = QWEN32B.with_(n_layers=1, n_shared=0), 2048, 2112, 48
     log(f"draft/verify parity {shape_name}")
