@@ -347,7 +347,7 @@ def main():
         "cpu_baseline": cpu,
         "tau": round(tau, 4),
         "cycles_per_step": round(cycles_per_gen, 2),
-        "cycle_ms": {"draft_16_steps": round(draft_ms, 3), "verify": round(verify_ms, 3),
+        "cycle_ms": {"draft": round(draft_ms, 3), "draft_steps": gamma, "verify": round(verify_ms, 3),
                      "reject": round(reject_ms, 3)},
         "plain_ar_tokens_s": round(ar, 3) if ar else None,
         "kernels": kern,

@@ -44,7 +44,9 @@ _ROLES = {
     "draft_attn_kernel": "draft attention: RoPE, KV append, 64-key split partials",
     "draft_merge_kernel": "draft attention: merge of the split partials",
     "rows_attn_kernel": "verify attention: per-row split partials",
-    "rows_merge_kernel": "verify attention: merge of the split partials",
+    "rows_attn_long_kernel": "verify attention, long context: several key tiles per block",
+    "rows_merge_kernel": "verify attention: merge of many split partials (8 groups per block)",
+    "rows_merge_seq_kernel": "verify attention: merge of the split partials",
     "rope_append_kernel": "verify RoPE + KV append (sums QKV split-k partials)",
     "rmsnorm_rows_kernel": "verify residual add of split-k partials + RMSNorm",
     "gemm_reduce_kernel": "lm_head split-k reduction",
