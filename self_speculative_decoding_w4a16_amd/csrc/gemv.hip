@@ -8,11 +8,12 @@
 //    so that the 64 lanes of a wave read consecutive 16-byte slots (no bank
 //    conflicts).  An RMSNorm (and, for layer 0, the embedding gather) is
 //    computed in the prologue of every block, so it costs no extra launch.
-//  * Every lane streams 16-byte chunks of R rows (R = 1, 2, 4) with several
-//    chunks in flight; a wave covers whole rows, lane c takes chunks
-//    c, c+64, ...  Rows are contiguous, so each wave load reads R fully used,
-//    contiguous 1 KiB segments, for bf16 rows (8 weights a chunk) and W4 code
-//    rows (32 weights a chunk) alike.
+//  * Every lane streams 16-byte chunks of R rows (R = 1, 2, 4); a wave covers
+//    whole rows, lane c takes chunks c, c+64, ...  Rows are contiguous, so
+//    each wave load reads R fully used, contiguous 1 KiB segments, for bf16
+//    rows (8 weights a chunk) and W4 code rows (32 weights a chunk) alike.
+//    A wave's steps alternate between two register slots, so one step's
+//    loads are in flight for the whole time the other is consumed.
 //  * W4 dequantisation happens in registers: a nibble pair becomes the bf16
 //    pair (128+q_a, 128+q_b) with one and-or, and v_dot2_f32_bf16 multiplies
 //    it by the x pair.  Per chunk (32 weights of one 64-group)
@@ -84,16 +85,17 @@ __device__ __forceinline__ void group_rows(int64_t g, int64_t n, int64_t (&prow)
   }
 }
 
-// Weight pointers carried across loop iterations are kept in the global
-// address space explicitly, so loads through them are global_load (counted by
-// vmcnt only) and the next step's loads can stay in flight while the current
-// step is consumed.
-typedef const u32x4 __attribute__((address_space(1))) g_u32x4;
-typedef const uint32_t __attribute__((address_space(1))) g_u32;
+// Weight rows are read through buffer resources: a row's resource covers
+// exactly its bytes (none for rows past the end and for steps past the
+// wave's last group), so chunks outside it read as zeros without touching
+// memory and every step issues the same loads (no branch around them, which
+// would make the compiler wait for all loads in flight where the paths meet).
+typedef __amdgpu_buffer_rsrc_t Res;
+constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 (CDNA): raw 32-bit data
+constexpr int kNonTemporal = 2;           // buffer load cache policy: nt (streamed weights)
 
 // One step: unit u of row r is the 16-byte chunk (base + lane + 64u) of the
-// row; for W4 also the fp16 {scale, min} of its 64-group.  Indices past the
-// row end are clamped; their contribution is skipped.
+// row; for W4 also the fp16 {scale, min} of its 64-group.
 template <int R, int U, bool W4>
 struct Step {
   u32x4 v[U][R];
@@ -101,33 +103,93 @@ struct Step {
 };
 
 template <int R, int U, bool W4>
-__device__ __forceinline__ void load_step(Step<R, U, W4>& b, g_u32x4* const (&wp)[R],
-                                          g_u32* const (&mp)[R], int base, int lane, int n_units) {
+__device__ __forceinline__ void load_step(Step<R, U, W4>& b, const Res (&wr)[R], const Res (&mr)[R], int base,
+                                          int lane) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    int i = base + lane + u * SS_WAVE;
-    i = i < n_units ? i : n_units - 1;
+    const int i = base + lane + u * SS_WAVE;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      b.v[u][r] = __builtin_nontemporal_load(wp[r] + i);
-      if (W4) b.m[u][r] = mp[r][i >> 1];
+      b.v[u][r] = __builtin_amdgcn_raw_buffer_load_b128(wr[r], 16 * i, 0, kNonTemporal);
+      if (W4) b.m[u][r] = __builtin_amdgcn_raw_buffer_load_b32(mr[r], 4 * (i >> 1), 0, 0);
     }
   }
 }
 
 template <int R, bool W4>
-__device__ __forceinline__ void row_ptrs(const GemvArgs& a, const int64_t (&prow)[R], int K,
-                                         g_u32x4* (&wp)[R], g_u32* (&mp)[R]) {
+__device__ __forceinline__ void row_res(const GemvArgs& a, const int64_t (&prow)[R], const bool (&live)[R], int K,
+                                        Res (&wr)[R], Res (&mr)[R]) {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if (W4) {
-      wp[r] = (g_u32x4*)(a.codes + prow[r] * (K / 2));
-      mp[r] = (g_u32*)(a.meta) + prow[r] * (K / 64);
+      wr[r] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.codes) + prow[r] * (K / 2), 0,
+                                                live[r] ? K / 2 : 0, kBufferWord3);
+      mr[r] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.meta) + prow[r] * (K / 32), 0,
+                                                live[r] ? K / 16 : 0, kBufferWord3);
     } else {
-      wp[r] = (g_u32x4*)(a.w + prow[r] * K);
-      mp[r] = (g_u32*)(a.meta);
+      wr[r] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.w) + prow[r] * K, 0, live[r] ? 2 * K : 0,
+                                                kBufferWord3);
+      mr[r] = wr[r];
     }
   }
+}
+
+// Position of a wave in its walk over (row group, step): group g, first unit
+// `base` of the step, the group's physical rows, validity, first output row,
+// weight and meta resources and (residual epilogue) residual inputs.
+template <int R>
+struct Cursor {
+  int64_t g, out0;
+  int base;
+  int64_t prow[R];
+  bool rv[R];
+  Res wr[R], mr[R];
+  float rres[R];
+};
+
+template <int R, bool W4, int EPI>
+__device__ __forceinline__ void cursor_at(Cursor<R>& c, const GemvArgs& a, int64_t g, int64_t n_groups, int K) {
+  c.g = g;
+  c.base = 0;
+  group_rows<R, EPI>(g < n_groups ? g : 0, a.n, c.prow, c.rv, c.out0);
+  // past the wave's last group no row is valid: such steps read zeros and
+  // store nothing
+#pragma unroll
+  for (int r = 0; r < R; ++r) c.rv[r] = c.rv[r] && g < n_groups;
+  row_res<R, W4>(a, c.prow, c.rv, K, c.wr, c.mr);
+}
+
+// Residual inputs of the cursor's rows, loaded (through the vector memory
+// path, in order with the weights) for every step, so that no load depends on
+// a branch.
+template <int R, int EPI>
+__device__ __forceinline__ void load_rres(Cursor<R>& c, Res rr) {
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    c.rres[r] = (EPI == EPI_RESID)
+                    ? ss::bf2f(__builtin_amdgcn_raw_buffer_load_b16(rr, 2 * (int)c.prow[r], 0, 0))
+                    : 0.0f;
+}
+
+// The step after c: the next unit block of the same group, else the first of
+// the wave's next group.
+template <int R, int U, bool W4, int EPI>
+__device__ __forceinline__ Cursor<R> cursor_next(const Cursor<R>& c, const GemvArgs& a, Res rr,
+                                                 int64_t wave_stride, int64_t n_groups, int K, int n_units) {
+  Cursor<R> d;
+  d.g = c.g;
+  d.out0 = c.out0;
+  d.base = c.base + U * SS_WAVE;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    d.prow[r] = c.prow[r];
+    d.rv[r] = c.rv[r];
+    d.wr[r] = c.wr[r];
+    d.mr[r] = c.mr[r];
+  }
+  if (d.base >= n_units) cursor_at<R, W4, EPI>(d, a, c.g + wave_stride, n_groups, K);
+  load_rres<R, EPI>(d, rr);
+  return d;
 }
 
 // Sums each of a wave's R per-lane row accumulators over the 64 lanes in one
@@ -180,6 +242,78 @@ __device__ __forceinline__ void put_x(u32x4* smem4, float* xsum, int it, bool ok
   }
 }
 
+// Consumes one step: its dot products into the per-lane accumulators and, on
+// the group's last step, the row sums and the epilogue.
+template <int R, int U, bool W4, int EPI>
+__device__ __forceinline__ void consume(const GemvArgs& a, const Cursor<R>& c, const Step<R, U, W4>& cur,
+                                        float (&acc)[R], ss::ArgMax& best, const u32x4* smem4,
+                                        const float* xsum, int lane, int n_units, uint32_t mask,
+                                        uint32_t magic) {
+  constexpr int RO = (EPI == EPI_SILU) ? R / 2 : R;
+  // compute the current step
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    // chunks past the row end (zeros) are computed on x of chunk 0 and their
+    // result dropped: no branch, so no wait is placed where paths meet
+    const int i0 = c.base + lane + u * SS_WAVE;
+    const bool ok = i0 < n_units;
+    const int i = ok ? i0 : 0;
+    if (W4) {
+      const float xs = xsum[i];
+      const u32x4 x0 = smem4[w4_slot(i, 0)], x1 = smem4[w4_slot(i, 1)];
+      const u32x4 x2 = smem4[w4_slot(i, 2)], x3 = smem4[w4_slot(i, 3)];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const u32x4 cw = cur.v[u][r];
+        float d0 = w4_word_dot(cw.x, x0, 0.0f, mask, magic);
+        float d1 = w4_word_dot(cw.y, x1, 0.0f, mask, magic);
+        d0 = w4_word_dot(cw.z, x2, d0, mask, magic);
+        d1 = w4_word_dot(cw.w, x3, d1, mask, magic);
+        const float sc = ss::h2f((uint16_t)(cur.m[u][r] & 0xffffu));
+        const float mn = ss::h2f((uint16_t)(cur.m[u][r] >> 16));
+        const float t = sc * (d0 + d1) + (mn - 128.0f * sc) * xs;
+        acc[r] += ok ? t : 0.0f;
+      }
+    } else {
+      const u32x4 xq = smem4[i];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float t = bf16_chunk_dot(cur.v[u][r], xq, acc[r]);
+        acc[r] = ok ? t : acc[r];
+      }
+    }
+  }
+
+  if (c.base + U * SS_WAVE >= n_units) {  // last step of the group
+    constexpr int LPR = SS_WAVE / R;  // lanes per row after the butterfly
+    const float tot = reduce_rows<R>(acc, lane);
+    if (EPI == EPI_SILU) {
+      const float up_tot = __shfl_xor(tot, 32, SS_WAVE);  // up row r + R/2 sits 32 lanes away
+#pragma unroll
+      for (int r = 0; r < RO; ++r) {
+        if (lane == LPR * r && c.rv[r]) {
+          const float gt = ss::bf2f(ss::f2bf(tot));
+          const float up = ss::bf2f(ss::f2bf(up_tot));
+          a.y[c.out0 + r] = ss::f2bf(gt / (1.0f + expf(-gt)) * up);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (lane == LPR * r && c.rv[r]) {
+          float v = tot;
+          if (EPI == EPI_RESID) v = c.rres[r] + v;
+          const uint16_t b = ss::f2bf(v);
+          a.y[c.prow[r]] = b;
+          if (EPI == EPI_LOGITS) best = ss::better(best, ss::ArgMax{ss::bf2f(b), (int)c.prow[r]});
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  }
+}
+
 template <int R, bool W4, int PRO, int EPI, int NT>
 __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, uint32_t mask_arg,
                                                         uint32_t magic_arg) {
@@ -200,7 +334,6 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
   // 16-byte chunks per lane and row in one step: W4 chunks carry 4x the VALU
   // work of bf16 chunks, so W4 steps are shorter (better overlap)
   constexpr int U = W4 ? ((R >= 4) ? 1 : 2) : ((R >= 4) ? 2 : (R == 2 ? 4 : 8));
-  constexpr int RO = (EPI == EPI_SILU) ? R / 2 : R;
   const int64_t wave_stride = (int64_t)gridDim.x * kWaves;
   const uint32_t mask = __builtin_amdgcn_readfirstlane(mask_arg);
   uint32_t magic = magic_arg;
@@ -234,20 +367,22 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
   };
   if (PRO == PRO_X) load_prologue();
 
-  int64_t g = (int64_t)blockIdx.x * kWaves + wave;
-  int64_t prow[R], out0;
-  bool rv[R];
-  group_rows<R, EPI>(g < n_groups ? g : 0, a.n, prow, rv, out0);
-  g_u32x4* wp[R];
-  g_u32* mp[R];
-  row_ptrs<R, W4>(a, prow, K, wp, mp);
-  int base = 0;  // wave-uniform first unit of the current step
-  Step<R, U, W4> cur;
-  load_step<R, U, W4>(cur, wp, mp, base, lane, n_units);
-  // residual inputs of the group's rows, loaded with its first weights
-  float rres[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) rres[r] = (EPI == EPI_RESID) ? ss::bf2f(a.resid[prow[r]]) : 0.0f;
+  // Two step slots, A and B, alternate without register copies (a copy of a
+  // slot whose loads are in flight would wait for them): while one is
+  // consumed the other's loads are in flight.  The wave's step count T is
+  // known up front, so the loop runs only while both refills are real steps
+  // and the last one or two steps are consumed after it; no load is issued
+  // for a step past the end, and none sits behind a branch inside the loop.
+  const int64_t g0 = (int64_t)blockIdx.x * kWaves + wave;
+  const int spg = (n_units + U * SS_WAVE - 1) / (U * SS_WAVE);  // steps per group
+  const int64_t T = g0 < n_groups ? ((n_groups - 1 - g0) / wave_stride + 1) * spg : 0;
+  const Res rr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(EPI == EPI_RESID ? a.resid : a.y), 0,
+                                                    EPI == EPI_RESID ? (int)(2 * a.n) : 0, kBufferWord3);
+  Cursor<R> ca, cb;
+  Step<R, U, W4> sa, sb;
+  cursor_at<R, W4, EPI>(ca, a, g0, n_groups, K);
+  load_rres<R, EPI>(ca, rr);
+  load_step<R, U, W4>(sa, ca.wr, ca.mr, 0, lane);
   if (PRO != PRO_X) {
     load_prologue();
   } else {
@@ -318,6 +453,15 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
       }
     }
   }
+  // Prologue registers whose items lie past the end of x were never read; a
+  // use of every one here settles their loads before the loop, where the
+  // compiler would otherwise wait for all loads in flight (each step's
+  // included) before it reuses those registers.
+#pragma unroll
+  for (int t = 0; t < XB; ++t) {
+    asm volatile("" ::"v"(hv[t]));
+    if (PRO != PRO_X) asm volatile("" ::"v"(gv[t]));
+  }
   __syncthreads();
 
   // ------------------------------------------------ main loop over (row group, step)
@@ -325,105 +469,25 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.0f;
   ss::ArgMax best = {-INFINITY, 0x7fffffff};
-  while (g < n_groups) {
-    // coordinates of the next step (wave-uniform), and its loads, issued
-    // before the current step is consumed
-    int base1 = base + U * SS_WAVE;
-    int64_t g1 = g;
-    const bool end_of_group = base1 >= n_units;
-    int64_t prow1[R], out1 = out0;
-    bool rv1[R];
-    g_u32x4* wp1[R];
-    g_u32* mp1[R];
-    float rres1[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      prow1[r] = prow[r];
-      rv1[r] = rv[r];
-      wp1[r] = wp[r];
-      mp1[r] = mp[r];
-      rres1[r] = rres[r];
-    }
-    if (end_of_group) {
-      g1 = g + wave_stride;
-      base1 = 0;
-      group_rows<R, EPI>(g1 < n_groups ? g1 : 0, a.n, prow1, rv1, out1);
-      row_ptrs<R, W4>(a, prow1, K, wp1, mp1);
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-        if (EPI == EPI_RESID) rres1[r] = ss::bf2f(a.resid[prow1[r]]);
-    }
-    Step<R, U, W4> nxt;
-    if (g1 < n_groups) load_step<R, U, W4>(nxt, wp1, mp1, base1, lane, n_units);
-
-    // compute the current step
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = base + lane + u * SS_WAVE;
-      if (i < n_units) {
-        if (W4) {
-          const float xs = xsum[i];
-          const u32x4 x0 = smem4[w4_slot(i, 0)], x1 = smem4[w4_slot(i, 1)];
-          const u32x4 x2 = smem4[w4_slot(i, 2)], x3 = smem4[w4_slot(i, 3)];
-#pragma unroll
-          for (int r = 0; r < R; ++r) {
-            const u32x4 c = cur.v[u][r];
-            float d0 = w4_word_dot(c.x, x0, 0.0f, mask, magic);
-            float d1 = w4_word_dot(c.y, x1, 0.0f, mask, magic);
-            d0 = w4_word_dot(c.z, x2, d0, mask, magic);
-            d1 = w4_word_dot(c.w, x3, d1, mask, magic);
-            const float sc = ss::h2f((uint16_t)(cur.m[u][r] & 0xffffu));
-            const float mn = ss::h2f((uint16_t)(cur.m[u][r] >> 16));
-            acc[r] += sc * (d0 + d1) + (mn - 128.0f * sc) * xs;
-          }
-        } else {
-          const u32x4 xq = smem4[i];
-#pragma unroll
-          for (int r = 0; r < R; ++r) acc[r] = bf16_chunk_dot(cur.v[u][r], xq, acc[r]);
-        }
-      }
-    }
-
-    if (end_of_group) {
-      constexpr int LPR = SS_WAVE / R;  // lanes per row after the butterfly
-      const float tot = reduce_rows<R>(acc, lane);
-      if (EPI == EPI_SILU) {
-        const float up_tot = __shfl_xor(tot, 32, SS_WAVE);  // up row r + R/2 sits 32 lanes away
-#pragma unroll
-        for (int r = 0; r < RO; ++r) {
-          if (lane == LPR * r && rv[r]) {
-            const float gt = ss::bf2f(ss::f2bf(tot));
-            const float up = ss::bf2f(ss::f2bf(up_tot));
-            a.y[out0 + r] = ss::f2bf(gt / (1.0f + expf(-gt)) * up);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          if (lane == LPR * r && rv[r]) {
-            float v = tot;
-            if (EPI == EPI_RESID) v = rres[r] + v;
-            const uint16_t b = ss::f2bf(v);
-            a.y[prow[r]] = b;
-            if (EPI == EPI_LOGITS) best = ss::better(best, ss::ArgMax{ss::bf2f(b), (int)prow[r]});
-          }
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < R; ++r) acc[r] = 0.0f;
-    }
-    g = g1;
-    base = base1;
-    out0 = out1;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      prow[r] = prow1[r];
-      rv[r] = rv1[r];
-      wp[r] = wp1[r];
-      mp[r] = mp1[r];
-      rres[r] = rres1[r];
-    }
-    cur = nxt;
+  // steps t (in A) and t+1 (in B) per iteration, refilling B with t+1 and A
+  // with t+2 (both < T)
+  int64_t t = 0;
+  while (t + 2 < T) {
+    cb = cursor_next<R, U, W4, EPI>(ca, a, rr, wave_stride, n_groups, K, n_units);
+    load_step<R, U, W4>(sb, cb.wr, cb.mr, cb.base, lane);
+    consume<R, U, W4, EPI>(a, ca, sa, acc, best, smem4, xsum, lane, n_units, mask, magic);
+    ca = cursor_next<R, U, W4, EPI>(cb, a, rr, wave_stride, n_groups, K, n_units);
+    load_step<R, U, W4>(sa, ca.wr, ca.mr, ca.base, lane);
+    consume<R, U, W4, EPI>(a, cb, sb, acc, best, smem4, xsum, lane, n_units, mask, magic);
+    t += 2;
+  }
+  if (t + 2 == T) {  // steps T-2 (in A) and T-1
+    cb = cursor_next<R, U, W4, EPI>(ca, a, rr, wave_stride, n_groups, K, n_units);
+    load_step<R, U, W4>(sb, cb.wr, cb.mr, cb.base, lane);
+    consume<R, U, W4, EPI>(a, ca, sa, acc, best, smem4, xsum, lane, n_units, mask, magic);
+    consume<R, U, W4, EPI>(a, cb, sb, acc, best, smem4, xsum, lane, n_units, mask, magic);
+  } else if (t + 1 == T) {  // step T-1 (in A)
+    consume<R, U, W4, EPI>(a, ca, sa, acc, best, smem4, xsum, lane, n_units, mask, magic);
   }
   if (EPI == EPI_LOGITS) {
     best = ss::wave_argmax(best);
