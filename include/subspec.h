@@ -286,6 +286,16 @@ int subspec_bf16_gemm(const uint16_t *w, int64_t n, int64_t k, const uint16_t *x
 int subspec_sample(const uint16_t *logits, int32_t vocab, float temp, const uint32_t *u_code,
                    int32_t *token, void *ws, size_t ws_bytes, void *stream);
 
+/* Measurement helper: one streaming read of buf (bytes, a positive multiple
+ * of 16, 16-byte aligned device memory) by a read-only kernel, the HBM read
+ * ceiling that the weight-streaming kernels of the draft and verify passes
+ * are measured against (low-batch decode is bound by streaming weights from
+ * memory: "How speculative decoding makes LLMs go brrr", Module 2).  The
+ * device word *sink is XORed with every 32-bit word of buf (the caller zeroes
+ * it first to read the fold); nothing else is written.  Errors: EINVAL for
+ * null pointers, ESHAPE for bytes. */
+int subspec_hbm_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* Profiling (host side; off by default)                                     */
 /* ------------------------------------------------------------------------ */

@@ -85,6 +85,7 @@ _SIGS = {
                                     c_void_p, c_size_t, c_void_p]),
     "subspec_sample": (c_int32, [c_void_p, c_int32, c_float, c_void_p, c_void_p, c_void_p,
                                  c_size_t, c_void_p]),
+    "subspec_hbm_read": (c_int32, [c_void_p, c_int64, c_void_p, c_void_p]),
     "subspec_profile_start": (c_int32, [c_int32]),
     "subspec_profile_stop": (c_int32, []),
     "subspec_profile_read": (c_int32, [c_int32, POINTER(c_int64), POINTER(ctypes.c_double),
@@ -212,6 +213,12 @@ def w4_gemv(codes, meta, n, k, x, y, stream=None):
 def bf16_gemv(w, x, y, stream=None):
     n, k = w.shape
     check(lib().subspec_bf16_gemv(_p(w), n, k, _p(x), _p(y), _stream(stream)))
+
+
+def hbm_read(buf, sink, stream=None):
+    """One streaming read of the device tensor buf (the HBM read ceiling);
+    the int32 device scalar sink is XORed with every 32-bit word of buf."""
+    check(lib().subspec_hbm_read(_p(buf), buf.numel() * buf.element_size(), _p(sink), _stream(stream)))
 
 
 def linear(w=None, codes=None, meta=None, n=None, k=None):

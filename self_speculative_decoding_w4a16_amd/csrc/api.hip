@@ -15,6 +15,9 @@
 #include "internal.h"
 #include "profile.h"
 
+// HBM read ceiling (stream.hip): *sink ^= XOR of the buffer's 32-bit words
+hipError_t launch_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
+
 namespace {
 
 thread_local std::string g_err;
@@ -710,6 +713,14 @@ int subspec_sample(const uint16_t* logits, int32_t vocab, float temp, const uint
   HIPCHK(launch_rowmax(logits, vocab, pm, pa, nc, s));
   SampleWs sw{pm, pa, sums, (uint32_t*)((char*)ws + kSampleCounterOff)};
   HIPCHK(launch_sample(logits, vocab, temp, u_code, pm, pa, nc, token, nullptr, sw, s));
+  return ok();
+}
+
+int subspec_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return fail(SUBSPEC_EINVAL, "buf and sink must be set");
+  if (bytes < 16 || bytes % 16 != 0) return fail(SUBSPEC_ESHAPE, "bytes must be a positive multiple of 16");
+  if (reinterpret_cast<uintptr_t>(buf) % 16 != 0) return fail(SUBSPEC_EINVAL, "buf must be 16-byte aligned");
+  HIPCHK(launch_hbm_read(buf, bytes, sink, hs(stream)));
   return ok();
 }
 

@@ -47,6 +47,7 @@ _ROLES = {
     "rows_attn_long_kernel": "verify attention, long context: several key tiles per block",
     "rows_merge_kernel": "verify attention: merge of many split partials (8 groups per block)",
     "rows_merge_seq_kernel": "verify attention: merge of the split partials",
+    "hbm_read_kernel": "HBM read ceiling (read-only stream, measurement)",
     "rope_append_kernel": "verify RoPE + KV append (sums QKV split-k partials)",
     "rmsnorm_rows_kernel": "verify residual add of split-k partials + RMSNorm",
     "gemm_reduce_kernel": "lm_head split-k reduction",

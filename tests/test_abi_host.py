@@ -62,6 +62,17 @@ def test_gemv_gemm_sample_argument_errors():
     assert l.subspec_sample(p, 100, 1.0, p, p, p, 16, None) == _lib.EWORKSPACE
 
 
+def test_hbm_read_argument_errors():
+    l = _lib.lib()
+    p = V(4096)
+    assert l.subspec_hbm_read(None, 64, p, None) == _lib.EINVAL
+    assert l.subspec_hbm_read(p, 64, None, None) == _lib.EINVAL
+    assert l.subspec_hbm_read(p, 0, p, None) == _lib.ESHAPE
+    assert l.subspec_hbm_read(p, 40, p, None) == _lib.ESHAPE
+    assert l.subspec_hbm_read(V(4100), 64, p, None) == _lib.EINVAL
+    assert "aligned" in _lib.last_error()
+
+
 def test_fused_gemv_argument_errors():
     import ctypes
     l = _lib.lib()

@@ -271,3 +271,23 @@ def test_reject_matches_oracle(cuda, gamma, V, T, Td):
     if gamma and V <= 4096:
         assert len(seen_n) > 1
     assert int(buf[:65536].sum().item()) == 0
+
+
+@pytest.mark.parametrize("nbytes", [16, 16 * 1001, 3 * (1 << 20) + 16 * 37, 64 << 20])
+def test_hbm_read_fold(cuda, nbytes):
+    """The read-ceiling kernel reads every word once: its XOR fold equals the
+    XOR of all 32-bit words (ragged tails and a buffer of one word included),
+    and it accumulates into the sink."""
+    log(f"hbm read {nbytes} B")
+    g = torch.Generator(device=cuda)
+    g.manual_seed(nbytes)
+    buf = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=cuda, generator=g)
+    words = buf.cpu().numpy().view(np.uint32)
+    want = int(np.bitwise_xor.reduce(words))
+    sink = torch.zeros(1, dtype=torch.int32, device=cuda)
+    _lib.hbm_read(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink.cpu().numpy().view(np.uint32)[0]) == want
+    _lib.hbm_read(buf, sink)  # a second fold cancels the first
+    torch.cuda.synchronize()
+    assert int(sink.cpu().numpy().view(np.uint32)[0]) == 0
