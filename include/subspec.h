@@ -304,7 +304,7 @@ int subspec_hbm_read(const void *buf, int64_t bytes, uint32_t *sink, void *strea
  * that a class average is the average of one kernel at one shape. */
 enum {
   SUBSPEC_K_W4_QKV = 0,        /* draft QKV GEMV, 4-bit substitute layer           */
-  SUBSPEC_K_W4_O = 1,          /* draft O GEMV (+ attention split merge), 4-bit    */
+  SUBSPEC_K_W4_O = 1,          /* draft O GEMV + residual, 4-bit                   */
   SUBSPEC_K_W4_GATE_UP = 2,    /* draft gate/up GEMV with SiLU*up, 4-bit           */
   SUBSPEC_K_W4_DOWN = 3,       /* draft down GEMV + residual, 4-bit                */
   SUBSPEC_K_BF16_QKV = 4,      /* the same four on shared bf16 layers              */
