@@ -493,7 +493,8 @@ def cpu_baseline(shape, w, dm, wl, tau):
     """The oracle, untuned, on a bounded sample of the same workload: one
     draft token through one shared bf16 layer (if the model has any), one W4
     substitute layer and the lm_head, and one gamma+1-position verify through
-    one layer and the lm_head, at the workload's shapes and context length
+    one layer and the lm_head, each timed three times (median), at the
+    workload's shapes and context length
     (synthetic KV; the long-context workload drafts over its sparse index
     and its verify also computes the importance scores).  The per-layer
     times are scaled to the full model, a cycle is gamma draft steps +
@@ -543,10 +544,17 @@ def cpu_baseline(shape, w, dm, wl, tau):
                                ex["budget_permille"]) for _ in range(shape.n_kv_heads)]]
         sparse, scores = (index, kv_len), []
 
-    def timed(fn):
-        t = time.perf_counter()
-        fn()
-        return time.perf_counter() - t
+    spent = [0.0]
+
+    def timed(fn, reps=3):
+        # median of three runs (about 10 s of CPU work in all at the 7B shape)
+        ts = []
+        for _ in range(reps):
+            t = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t)
+        spent[0] += sum(ts)
+        return sorted(ts)[len(ts) // 2]
 
     t_lm1 = timed(lambda: forward(m0, (K0, K0), kv_len, toks[:1], draft=True))
     t_sh1 = timed(lambda: forward(m_sh, kv(), kv_len, toks[:1], draft=True)) if m_sh else 0.0
@@ -560,14 +568,14 @@ def cpu_baseline(shape, w, dm, wl, tau):
     t_draft = S * max(t_sh1 - t_lm1, 0) + (L - S) * max(t_w41 - t_lm1, 0) + t_lm1
     t_verify = L * max(t_v - t_lm, 0) + t_lm
     cycle = gamma * t_draft + t_verify + t_rej
-    sample_s = t_lm1 + t_sh1 + t_w41 + t_lm + t_v + t_rej
+    sample_s = spent[0]
     log(f"cpu baseline: draft step {t_draft:.2f}s, verify {t_verify:.2f}s, reject {t_rej:.2f}s "
         f"(sample {sample_s:.1f}s, quantise {t_quant:.1f}s)")
     layers = (f"one shared bf16 layer, one W4 layer" if S else "one W4 layer")
     return {"value": round(tau / cycle, 6), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": (f"oracle (NumPy float64) timed on {layers}, the lm_head and one reject "
-                       f"round at full {shape.name} shapes over {kv_len} positions of KV "
-                       f"({sample_s:.1f}s of CPU work), scaled to {L} layers and a gamma={gamma} "
+                       f"round at full {shape.name} shapes over {kv_len} positions of KV, median "
+                       f"of 3 runs each ({sample_s:.1f}s of CPU work in all), scaled to {L} layers and a gamma={gamma} "
                        f"cycle; tokens/s = tau of the GPU run / oracle cycle time"),
             "oracle_draft_step_s": round(t_draft, 3), "oracle_verify_s": round(t_verify, 3),
             "oracle_reject_s": round(t_rej, 3)}
