@@ -66,6 +66,20 @@ struct Carver {
 
 hipStream_t hs(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// compute units of the current device (queried once)
+int compute_units() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
 // ------------------------------------------------------------------ validation
 bool lin_is_bf16(const subspec_linear& l) { return l.w && !l.codes && !l.meta; }
 bool lin_is_w4(const subspec_linear& l) { return !l.w && l.codes && l.meta; }
@@ -375,7 +389,11 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
     // keys of this launch: at most the capacity (dense), or the index plus the
     // speculative positions (sparse)
     at.max_keys = sparse ? std::min(st->capacity, st->index_cap + st->gamma_max) : st->capacity;
-    at.head_splits = std::min(draft_head_splits(at.max_keys), w.part_recs);
+    // and no more blocks than compute units: a compute unit holding two of
+    // them doubles the launch's critical path (at the 32B shape, 40 heads:
+    // 8 splits 17.0 us a layer, 6 splits 12.8)
+    at.head_splits = std::min(std::min(draft_head_splits(at.max_keys), w.part_recs),
+                              std::max(1, compute_units() / std::max(1, m->n_q_heads)));
     at.counters = w.attn_counters;
     {
       prof::Scope ps(SUBSPEC_K_ATTN_DRAFT, 0.0, s);

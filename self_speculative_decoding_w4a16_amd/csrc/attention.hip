@@ -1400,7 +1400,8 @@ int draft_attn_keys_per_split() { return DSK; }
 // (at the 7B shape with ~900 keys, 8 splits measured 6.8 us a layer against
 // 7.5 for 4 and 8.6 for 1; over a ~6000-key sparse index, 8 splits 21.4 us
 // against 26.9 for 16).  SUBSPEC_DRAFT_HEAD_SPLITS overrides (up to
-// DQ_MAXSPLITS), for measurements.
+// DQ_MAXSPLITS), for measurements.  The caller also keeps the grid (query
+// heads x splits) within one block per compute unit.
 int draft_head_splits(int max_keys) {
   static int forced = -1;
   if (forced < 0) {
