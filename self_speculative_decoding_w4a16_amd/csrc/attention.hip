@@ -672,24 +672,41 @@ __global__ __launch_bounds__(DQW * 64) void draft_attn_head_kernel(AttnArgs a, c
   }
   const int last = ks.n_keys - 1;  // slot of the new key
   const int n_chunks = (ks.n_keys + KW - 1) / KW;
-  auto sparse_row = [&](int t) {  // slots past the index: the speculative positions
+  // sparse slot t -> cache row, split in two so that the index entry can be
+  // loaded a round before the K/V row it addresses (slots past the index are
+  // the speculative positions)
+  auto index_entry = [&](int t) {
     t = t < last ? t : 0;
-    const int ti = min(t, max(ks.n_idx - 1, 0));
-    const int ip = min(max(ks.ilist[ti], 0), a.cap - 1);
+    return ks.ilist[min(t, max(ks.n_idx - 1, 0))];
+  };
+  auto sparse_row_of = [&](int t, int entry) {
+    t = t < last ? t : 0;
+    const int ip = min(max(entry, 0), a.cap - 1);
     return t < ks.n_idx ? ip : ks.kv0 + (t - ks.n_idx);
   };
+  auto sparse_row = [&](int t) { return sparse_row_of(t, index_entry(t)); };
   auto load_chunk = [&](int c, Chunk& b) {
     if (sparse)
       load_rows(c, b, sparse_row);
     else
       load_rows(c, b, dense_row);
   };
+  // sparse: the index entries of each slot's next chunk, loaded a round
+  // ahead (a refill then issues its K/V loads without waiting for them)
+  int nidx[DQR][2];
+  auto clamp_chunk = [&](int c) { return c < n_chunks ? c : 0; };
+  auto load_entries = [&](int c, int (&e2)[2]) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) e2[e] = index_entry(c * KW + 8 * e + kg);
+  };
   if (sparse) {
 #pragma unroll
     for (int j = 0; j < DQR; ++j) {
       const int c = c_first + j * c_step;
-      load_chunk(c < n_chunks ? c : 0, ring[j]);
+      load_chunk(clamp_chunk(c), ring[j]);
     }
+#pragma unroll
+    for (int j = 0; j < DQR; ++j) load_entries(clamp_chunk(c_first + (j + DQR) * c_step), nidx[j]);
   }
 
   __syncthreads();
@@ -755,7 +772,14 @@ __global__ __launch_bounds__(DQW * 64) void draft_attn_head_kernel(AttnArgs a, c
     for (int j = 0; j < DQR; ++j) {
       const int cj = c + j * c_step, cn = cj + DQR * c_step;
       if (j == 0 || cj < n_chunks) step(cj, ring[j]);
-      load_chunk(cn < n_chunks ? cn : 0, ring[j]);
+      if (sparse) {
+        const int cc = clamp_chunk(cn);
+        const int e0 = nidx[j][0], e1 = nidx[j][1];
+        load_rows(cc, ring[j], [&](int t) { return sparse_row_of(t, (t - cc * KW) < 8 ? e0 : e1); });
+        load_entries(clamp_chunk(cn + DQR * c_step), nidx[j]);
+      } else {
+        load_chunk(clamp_chunk(cn), ring[j]);
+      }
     }
   }
   // the new key, from LDS: the 8 lanes of key group 0 in wave 0 of split 0
