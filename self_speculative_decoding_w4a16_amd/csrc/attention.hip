@@ -171,18 +171,22 @@ __global__ __launch_bounds__(RW * 64) void rows_attn_kernel(AttnArgs a) {
   load_q(wave < n_tiles ? wave : 0, qa);
 
   // ---- K tile, and V^T as pairs of consecutive keys (keys past n_keys are
-  // zeros): thread -> (key pair kp, 16-byte piece q) with the 64 lanes of a
-  // wave on 64 consecutive pairs, so the transposed stores hit distinct banks
+  // zeros).  V: thread -> (key pair kp, 16-byte piece q) with the 64 lanes of
+  // a wave on 64 consecutive pairs, so the transposed stores hit distinct
+  // banks.  K (stored row-major): thread -> (piece e % 16, key pair e / 16),
+  // so a wave load reads 4 whole 256-byte rows instead of 64 pieces.
   {
     constexpr int PER = (DKPB / 2) * (D / 8) / NTH;  // (pair, piece) items per thread
     u32x4 k2[PER][2], v2[PER][2];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = tid + NTH * i, kp = e & (DKPB / 2 - 1), q = e / (DKPB / 2);
+      const int kpk = e / (D / 8), qk = e & (D / 8 - 1);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int64_t row = (int64_t)hk * a.cap + min(k0 + 2 * kp + u, a.cap - 1);
-        k2[i][u] = reinterpret_cast<const u32x4*>(a.k_cache + row * D)[q];
+        const int64_t rowk = (int64_t)hk * a.cap + min(k0 + 2 * kpk + u, a.cap - 1);
+        k2[i][u] = reinterpret_cast<const u32x4*>(a.k_cache + rowk * D)[qk];
         v2[i][u] = reinterpret_cast<const u32x4*>(a.v_cache + row * D)[q];
       }
     }
@@ -191,15 +195,14 @@ __global__ __launch_bounds__(RW * 64) void rows_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = tid + NTH * i, kp = e & (DKPB / 2 - 1), q = e / (DKPB / 2);
+      const int kpk = e / (D / 8), qk = e & (D / 8 - 1);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        if (k0 + 2 * kp + u >= n_keys) {
-          k2[i][u] = u32x4{0u, 0u, 0u, 0u};
-          v2[i][u] = u32x4{0u, 0u, 0u, 0u};
-        }
+        if (k0 + 2 * kpk + u >= n_keys) k2[i][u] = u32x4{0u, 0u, 0u, 0u};
+        if (k0 + 2 * kp + u >= n_keys) v2[i][u] = u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-      for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x4*>(&ks[2 * kp + u][8 * q]) = k2[i][u];
+      for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x4*>(&ks[2 * kpk + u][8 * qk]) = k2[i][u];
       const uint32_t w0[4] = {v2[i][0].x, v2[i][0].y, v2[i][0].z, v2[i][0].w};
       const uint32_t w1[4] = {v2[i][1].x, v2[i][1].y, v2[i][1].z, v2[i][1].w};
 #pragma unroll
@@ -995,17 +998,22 @@ __global__ __launch_bounds__(RW * 64) void rows_attn_long_kernel(AttnArgs a) {
 #pragma unroll
     for (int st = 0; st < 4; ++st) qa[st] = qok ? qp[4 * st + g4] : u32x4{0u, 0u, 0u, 0u};
   }
-  // K/V of tile tau into registers: thread -> (key pair kp, 16-byte piece q)
+  // K/V of tile tau into registers.  V: thread -> (key pair kp, 16-byte
+  // piece q), the layout its transpose into LDS needs (a wave load touches 64
+  // rows).  K, stored row-major: thread -> (piece e % 16, key pair e / 16),
+  // so a wave load reads 4 whole 256-byte rows.
   u32x4 k2[PER][2], v2[PER][2];
   auto load_tile = [&](int tau) {
     const int k0 = kbase + tau * DKPB;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = tid + NTH * i, kp = e & (DKPB / 2 - 1), q = e / (DKPB / 2);
+      const int kpk = e / (D / 8), qk = e & (D / 8 - 1);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int64_t row = (int64_t)hk * a.cap + min(k0 + 2 * kp + u, a.cap - 1);
-        k2[i][u] = reinterpret_cast<const u32x4*>(a.k_cache + row * D)[q];
+        const int64_t rowk = (int64_t)hk * a.cap + min(k0 + 2 * kpk + u, a.cap - 1);
+        k2[i][u] = reinterpret_cast<const u32x4*>(a.k_cache + rowk * D)[qk];
         v2[i][u] = reinterpret_cast<const u32x4*>(a.v_cache + row * D)[q];
       }
     }
@@ -1035,15 +1043,14 @@ __global__ __launch_bounds__(RW * 64) void rows_attn_long_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = tid + NTH * i, kp = e & (DKPB / 2 - 1), q = e / (DKPB / 2);
+      const int kpk = e / (D / 8), qk = e & (D / 8 - 1);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        if (k0 + 2 * kp + u >= n_keys) {
-          k2[i][u] = u32x4{0u, 0u, 0u, 0u};
-          v2[i][u] = u32x4{0u, 0u, 0u, 0u};
-        }
+        if (k0 + 2 * kpk + u >= n_keys) k2[i][u] = u32x4{0u, 0u, 0u, 0u};
+        if (k0 + 2 * kp + u >= n_keys) v2[i][u] = u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-      for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x4*>(&ks[2 * kp + u][8 * q]) = k2[i][u];
+      for (int u = 0; u < 2; ++u) *reinterpret_cast<u32x4*>(&ks[2 * kpk + u][8 * qk]) = k2[i][u];
       const uint32_t w0[4] = {v2[i][0].x, v2[i][0].y, v2[i][0].z, v2[i][0].w};
       const uint32_t w1[4] = {v2[i][1].x, v2[i][1].y, v2[i][1].z, v2[i][1].w};
 #pragma unroll
