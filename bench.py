@@ -77,7 +77,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the "
-              "multi-GPU design is described in DESIGN.md and is not built.", file=sys.stderr)
+              "multi-GPU path (one decode per GPU, or tensor-parallel layers over xGMI) is not built.",
+              file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
