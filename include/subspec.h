@@ -56,7 +56,7 @@ enum {
   SUBSPEC_ESHAPE = -2,       /* dimensions the kernels do not support        */
   SUBSPEC_ECAPACITY = -3,    /* KV capacity or token buffer too small         */
   SUBSPEC_EHIP = -4,         /* a HIP runtime call failed                     */
-  SUBSPEC_EUNSUPPORTED = -5, /* a parameter value this build does not handle  */
+  SUBSPEC_EUNSUPPORTED = -5, /* a parameter value the library does not handle */
   SUBSPEC_EWORKSPACE = -6    /* workspace NULL or smaller than required       */
 };
 
