@@ -56,19 +56,30 @@ struct Plan {
 
 // Waves per block.  Small blocks (2 waves) keep many independent blocks in
 // flight, which streams best; the very wide matrices (lm_head) take 8 so that
-// the activations are not staged again for every 32 rows.
-int block_waves(int64_t n, int epi) { return (n >= 65536 && epi != GEPI_SILU) ? 8 : 2; }
+// the activations are not staged again for every 32 rows.  Past 32 positions
+// (three or four position tiles) the staged activations outweigh the 32
+// weight rows of a 2-wave block, and the gate/up GEMM shares them over 8
+// waves (32B shape, 49 positions: 150 -> 98 us; at 17 positions 8-wave
+// blocks were slower, 57 against 47 us).  Its sums do not depend on the
+// block shape (no k split); the split-k GEMMs keep 2-wave blocks, since
+// fewer row groups would mean more splits and other partial sums (4 waves
+// took the 32B down GEMM from 69 to 64 us, but changed every result that
+// depends on those sums, e.g. the prefill's KV cache).
+int block_waves(int64_t n, int epi, int m) {
+  if (epi == GEPI_SILU) return m > 32 ? 8 : 2;
+  return n >= 65536 ? 8 : 2;
+}
 
-int64_t rows_per_group(int64_t n, int epi) {
-  const int nw = block_waves(n, epi);
+int64_t rows_per_group(int64_t n, int epi, int m) {
+  const int nw = block_waves(n, epi, m);
   return epi == GEPI_SILU ? 16 * nw / 2 : 16 * nw;
 }
 
 Plan make_plan(int64_t n, int64_t k, int m, int epi) {
   Plan p;
   p.tt = (m + 15) / 16;
-  p.nw = block_waves(n, epi);
-  const int64_t rg = rows_per_group(n, epi);
+  p.nw = block_waves(n, epi, m);
+  const int64_t rg = rows_per_group(n, epi, m);
   p.groups = (n + rg - 1) / rg;
   const int chunks = (int)(k / KC);
   p.splits = 1;
@@ -280,9 +291,8 @@ hipError_t launch_nw(const GemmArgs& a, const Plan& p, hipStream_t s) {
 template <int EPI>
 hipError_t launch_tt(const GemmArgs& a, const Plan& p, hipStream_t s) {
   if (p.nw == 2) return launch_nw<2, EPI>(a, p, s);
-  if constexpr (EPI == GEPI_STORE || EPI == GEPI_PARTIAL) {
-    if (p.nw == 8) return launch_nw<8, EPI>(a, p, s);
-  }
+  if (p.nw == 4) return launch_nw<4, EPI>(a, p, s);
+  if (p.nw == 8) return launch_nw<8, EPI>(a, p, s);
   return hipErrorInvalidValue;
 }
 
