@@ -8,8 +8,11 @@ form and rounding open; the reading used here:
 
   * groups of 64 consecutive weights along the input (K) axis of each row;
   * lo = min, hi = max of the group (float32 values of the bf16 weights);
-  * scale s = fp16(fl32(fl32(hi - lo) / 15)); s := 1 when that is 0, and
-    saturates to the fp16 maximum instead of overflowing;
+  * scale s: the float32 span fl32(hi - lo) over 15, rounded to the nearest
+    fp16 value, then raised to the next fp16 value when 15 s falls below the
+    span (15 s is exact in float32), so that the 16 levels always reach hi;
+    s := 1 when it is 0 (a constant group); it saturates at the fp16
+    maximum instead of overflowing;
   * offset m = fp16(lo) (saturating);
   * code q = clamp(rint_even(fl32(fl32(x - m) / s)), 0, 15) with s, m the
     *stored* fp16 values read back as float32 (no fused multiply-add);
@@ -18,9 +21,18 @@ form and rounding open; the reading used here:
 Storage: ``codes`` uint8 [N][K/2], byte j = q[2j] | q[2j+1] << 4;
 ``meta`` float16 [N][K/64][2] = (s, m).
 
+The round-trip bound |x - w_hat| <= s/2 that the substitutes must meet
+holds for every group of bf16 values inside the fp16 range: 15 s covers the
+span, and fp16(lo) is lo itself (a bf16 value in the fp16 normal range is an
+fp16 value) or lies within half of the smallest fp16 step, 2**-25 <= s/2,
+below it.  Rounding the scale to nearest alone breaks it when s is an fp16
+subnormal (spans below about 1e-3): there 15 s can fall short of the span by
+a large fraction of a step, and the top codes clamp.
+
 Pinned by: the hand-built group whose values sit exactly on the 16 levels,
 the brute-force nearest level on small inputs, the round-trip bound
-|x - w_hat| <= s/2, the degenerate constant group and the byte packing.
+|x - w_hat| <= s/2 at every scale (including subnormal scales), the
+degenerate constant group and the byte packing.
 """
 import numpy as np
 
@@ -46,6 +58,9 @@ def quantize(w, group=GROUP):
     span = (hi - lo).astype(np.float32)                       # fl32 subtraction
     s32 = (span / np.float32(LEVELS)).astype(np.float32)       # fl32 division
     s16 = _to_fp16_saturating(s32)
+    short = (s16.astype(np.float32) * np.float32(LEVELS)) < span  # exact product
+    up = np.nextafter(s16, np.float16(np.inf))
+    s16 = np.where(short & np.isfinite(up), up, s16).astype(np.float16)
     s16 = np.where(s16 == 0, np.float16(1.0), s16)
     m16 = _to_fp16_saturating(lo)
     s = s16.astype(np.float32)[:, :, None]

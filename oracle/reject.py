@@ -20,8 +20,14 @@ Readings where the pages are silent:
     i.e. max(0, p - q) up to the positive factor St*Sd, kept to 41 bits; it
     is sampled with the same inverse CDF.  If its total is 0 the token is
     drawn from p instead and status bit 2 is set.
-  * status bit 1: a non-finite logit in a row that was read; bit 4: a draft
-    token with q(x) = 0 (then it is accepted iff p(x) > 0).
+  * status bit 1: a non-finite logit in a row that was read (such logits
+    carry no probability, see oracle.sampling); bit 4: a draft token with
+    q(x) = 0 (then it is accepted iff p(x) > 0).
+  * A draft token outside [0, V) (the device marks a draft step it had to
+    skip with -1) has q(x) = p(x) = 0: it is rejected, with status bit 4,
+    at any temperature.
+  * A draw whose total weight is 0 (residual and p both without mass, i.e.
+    a target row with no finite logit) gives token 0.
 
 Pinned by: q = p gives n = gamma; greedy gives the longest prefix of draft
 tokens equal to the target argmax; at least one token per round; exact
@@ -74,11 +80,15 @@ def reject(target_logits, draft_logits, draft_tokens, R, U, temp, draft_temp):
     gamma = len(draft_tokens)
     status = 0
     n = gamma
+    V = zt.shape[1]
     for i in range(gamma):
         x = int(draft_tokens[i])
         if not np.all(np.isfinite(zt[i])) or not np.all(np.isfinite(zd[i])):
             status |= STATUS_NONFINITE
-        if temp == 0:
+        if not 0 <= x < V:
+            status |= STATUS_Q_ZERO
+            ok = False
+        elif temp == 0:
             ok = x == argmax_lowest(zt[i])
         else:
             Wt, St = fixed_weights(zt[i], temp)

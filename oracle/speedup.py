@@ -2,7 +2,7 @@
 
 [SD] Module 4: under independent acceptance with rate alpha,
 tau = sum_{i=0..gamma} alpha^i = (1 - alpha^(gamma+1)) / (1 - alpha), so
-1 <= tau <= gamma+1; per-token latency L = (T_draft + T_verify) / tau.
+1 <= tau <= gamma+1.
 [SSR] section 2.2 and the back-solved denominators after section 7.1:
 speedup = tau / (D * t_draft / t_target + g_v), so tau / speedup is the
 implied denominator.  [SSL] section 1: S(k) = (alpha k + 1) / (k c + 1) with
@@ -25,10 +25,6 @@ def expected_accepted(alphas):
         run *= a
         total += run
     return total
-
-
-def latency_per_token(t_draft_total, t_verify, tau):
-    return (t_draft_total + t_verify) / tau
 
 
 def implied_denominator(tau, speedup):

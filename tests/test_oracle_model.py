@@ -19,6 +19,22 @@ def test_rmsnorm_constant_vector():
         np.testing.assert_array_equal(out, round_bf16(np.full(64, c / np.sqrt(c * c + 1e-6))))
 
 
+def test_rope_hand_computed(golden_dir):
+    import json, os
+    g = json.load(open(os.path.join(golden_dir, "rope_rmsnorm.json")))
+    for case in g["rope"]:
+        out = rope(np.array(case["x"], dtype=np.float64), case["pos"], case["theta"])
+        np.testing.assert_allclose(out, case["out"], rtol=0, atol=1e-12)
+
+
+def test_rmsnorm_hand_computed_with_weight(golden_dir):
+    import json, os
+    g = json.load(open(os.path.join(golden_dir, "rope_rmsnorm.json")))
+    for case in g["rmsnorm"]:
+        out = rmsnorm(np.array([case["h"]]), np.array(case["g"]), case["eps"])[0]
+        np.testing.assert_array_equal(out, case["out"])
+
+
 def test_rope_properties():
     rng = np.random.default_rng(0)
     q, k = rng.normal(size=128), rng.normal(size=128)

@@ -48,6 +48,32 @@ def test_round_trip_bound():
     assert (err <= s / 2 * (1 + 1e-6)).all()
 
 
+@pytest.mark.parametrize("std", [1e-7, 1e-6, 2e-6, 3e-5, 1e-3, 1.0, 300.0])
+def test_round_trip_bound_at_every_scale(std):
+    # Small spans put the scale among the fp16 subnormals (about 6e-8 apart):
+    # rounding it to nearest alone let 15 s fall short of the span there and
+    # the top codes clamp, up to ~2 s of error at std 1e-6.
+    w = _bf16_values((256, 512), std, 7)
+    codes, meta = quantize(w)
+    err = np.abs(w.astype(np.float64) - dequantize(codes, meta))
+    s = np.repeat(meta[:, :, 0].astype(np.float64), 64, axis=1)
+    assert (err <= s / 2 * (1 + 1e-6)).all()
+
+
+def test_scale_is_smallest_fp16_covering_span():
+    # brute force over every positive finite fp16 value: the scale is the
+    # smallest one whose 16 levels reach the group maximum (15 s >= span)
+    bits = np.arange(1, 0x7C00, dtype=np.uint16)
+    fp16 = np.sort(bits.view(np.float16).astype(np.float64))
+    for std, seed in [(1e-6, 1), (4e-6, 2), (1e-4, 3), (0.02, 4), (2.0, 5)]:
+        w = _bf16_values((32, 256), std, seed)
+        _, meta = quantize(w)
+        g = w.reshape(32, 4, 64).astype(np.float64)
+        span = g.max(axis=2) - g.min(axis=2)          # exact for these bf16 values
+        want = fp16[np.searchsorted(fp16 * 15.0, span, side="left")]
+        np.testing.assert_array_equal(meta[:, :, 0].astype(np.float64), want)
+
+
 def test_extremes_map_to_end_codes():
     w = _bf16_values((64, 512), 0.02, 3)
     codes, meta = quantize(w)

@@ -2,7 +2,7 @@
 import numpy as np
 from scipy import stats
 
-from oracle.reject import reject
+from oracle.reject import reject, STATUS_NONFINITE, STATUS_Q_ZERO, STATUS_ZERO_RESIDUAL
 from oracle.sampling import sample, softmax_f64
 from synth import uniform_codes, logits_pair
 
@@ -133,12 +133,96 @@ def test_gamma_zero_is_plain_sampling():
     assert n == 0 and out == [sample(zt[0], 1.0, 777)]
 
 
-def test_zero_residual_falls_back_to_p():
-    # p one-hot-like equal to q except on the drafted token -> D may vanish only when p <= q
+def test_rejection_of_greedy_draft_draws_from_p_without_drafted_token():
+    # q = onehot(0) (T_d = 0) against a uniform p: the residual max(0, p - q)
+    # is p restricted to tokens 1 and 2, each with half of the mass
     z = np.array([0.0, 0.0, 0.0], dtype=np.float32)
-    # draft with T_d = 0 puts q = onehot(0); target uniform: residual = p without token 0
     n, out, st = reject(np.stack([z, z]), z[None], [0], [TWO24 - 1], 0, 1.0, 0.0)
-    assert n == 0 and out[0] in (1, 2) and st == 0
+    assert n == 0 and out[0] == 1 and st == 0
+    lengths = _token_measure(lambda U: reject(np.stack([z, z]), z[None], [0], [TWO24 - 1], U, 1.0, 0.0)[1][0], 3)
+    np.testing.assert_allclose(lengths, [0.0, 0.5, 0.5], atol=1e-7)
+
+
+def _zero_residual_case(V=6, T=1.0):
+    # target = draft, so p = q and max(0, p - q) has no mass; the drafted
+    # token sits 40/T below the maximum, so exp(-40) * 2^40 < 1 gives it
+    # weight 0 on both sides: q(x) = p(x) = 0, it is rejected, and the
+    # residual draw has nothing to draw from
+    z = np.array([1.0, 0.5, -0.25, 2.0, 0.0, 2.0 - 40.0 * T][:V], dtype=np.float32)
+    return np.stack([z, z]), z[None].copy(), [V - 1]
+
+
+def test_zero_residual_falls_back_to_p():
+    zt, zd, toks = _zero_residual_case()
+    for U in (0, 1 << 20, 1 << 23, TWO24 - 1):
+        n, out, st = reject(zt, zd, toks, [0], U, 1.0, 1.0)
+        assert n == 0
+        assert st == STATUS_ZERO_RESIDUAL | STATUS_Q_ZERO
+        # the fallback draw is the plain draw from p = softmax(z_t) with the same u
+        assert out == [sample(zt[0], 1.0, U)]
+    law = _token_measure(lambda U: reject(zt, zd, toks, [0], U, 1.0, 1.0)[1][0], 6)
+    np.testing.assert_allclose(law, softmax_f64(zt[0], 1.0), atol=2e-6)
+
+
+def test_out_of_vocabulary_draft_token_is_rejected():
+    # the device marks a skipped draft step with token -1: q(x) = p(x) = 0
+    zt, zd = logits_pair(3, 40, 12)
+    zt, zd = zt.float().numpy(), zd.float().numpy()
+    am = [int(np.argmax(zt[i])) for i in range(4)]
+    for T, Td in [(0.0, 0.0), (0.0, 1.0), (1.0, 1.0), (1.0, 0.0)]:
+        toks = [am[0], -1, am[2]] if T == 0 else [sample(zd[0], Td, 5), -1, 3]
+        n, out, st = reject(zt, zd, toks, [0, 0, 0], 1234, T, Td)
+        assert n == 1 and out[0] == toks[0] and st & STATUS_Q_ZERO
+        if T == 0:
+            assert out[1] == am[1]
+        assert 0 <= out[1] < 40
+    n, out, st = reject(zt, zd, [40, 0, 0], [0, 0, 0], 99, 0.0, 0.0)
+    assert n == 0 and out == [am[0]] and st == STATUS_Q_ZERO
+
+
+def test_non_finite_logits_reduce_to_the_finite_row():
+    # a NaN or +-Inf logit carries no probability: the round decides exactly
+    # as on the rows with those entries removed, and flags status bit 1.
+    # Rows left finite hold -1e4 there (weight 0 at these temperatures, never
+    # the argmax), so removing those columns changes nothing for them either.
+    rng = np.random.default_rng(3)
+    V, gamma = 9, 2
+    bad = {1: np.nan, 4: np.inf, 6: -np.inf}
+    keep = [j for j in range(V) if j not in bad]
+    for trial in range(40):
+        zt = np.round(rng.normal(0, 1.0, (gamma + 1, V)) * 8).astype(np.float32) / 8
+        zd = (zt[:gamma] + np.round(rng.normal(0, 0.5, (gamma, V)) * 8) / 8).astype(np.float32)
+        zt[:, list(bad)] = -1e4
+        zd[:, list(bad)] = -1e4
+        T, Td = [(1.0, 1.0), (0.7, 0.0), (0.0, 0.0), (1.0, 0.5)][trial % 4]
+        zt_f, zd_f = zt[:, keep].copy(), zd[:, keep].copy()
+        rows = [(zt, r) for r in range(gamma + 1)] + [(zd, r) for r in range(gamma)]
+        for arr, r in rows:
+            if (trial + r) % 2 == 0:
+                for j, v in bad.items():
+                    arr[r, j] = v
+        Ud, _ = uniform_codes(gamma, 100 + trial)
+        toks_f = [sample(zd_f[i], Td, Ud[i]) for i in range(gamma)]
+        toks = [keep[t] for t in toks_f]
+        R, _ = uniform_codes(gamma, 200 + trial)
+        Uf = int(uniform_codes(1, 300 + trial)[0][0])
+        n_f, out_f, st_f = reject(zt_f, zd_f, toks_f, R, Uf, T, Td)
+        n, out, st = reject(zt, zd, toks, R, Uf, T, Td)
+        assert n == n_f and out == [keep[t] for t in out_f]
+        read_rows = [zt[r] for r in range(n + 1)] + [zd[r] for r in range(min(n + 1, gamma))]
+        expect_bad = any(not np.isfinite(z).all() for z in read_rows)
+        assert (st & STATUS_NONFINITE) == (STATUS_NONFINITE if expect_bad else 0)
+        assert (st & ~STATUS_NONFINITE) == st_f
+
+
+def test_target_row_without_finite_logit():
+    # no mass anywhere in p: nothing is accepted, and every draw gives token 0
+    V = 5
+    zt = np.full((2, V), np.nan, dtype=np.float32)
+    zd = np.array([[0.0, 1.0, 2.0, 3.0, 4.0]], dtype=np.float32)
+    for T, Td in [(1.0, 1.0), (0.0, 0.0), (1.0, 0.0)]:
+        n, out, st = reject(zt, zd, [4], [0], 77, T, Td)
+        assert n == 0 and out == [0] and st & STATUS_NONFINITE
 
 
 def test_chi_square_emitted_tokens():

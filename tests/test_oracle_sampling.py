@@ -67,3 +67,33 @@ def test_chi_square_sampling():
     counts = np.bincount([sample(z, 1.0, int(u)) for u in U], minlength=V)
     chi2, pval = stats.chisquare(counts, p * len(U))
     assert pval > 1e-3
+
+
+def test_non_finite_logits_carry_no_probability():
+    # a row with NaN / +-Inf entries draws exactly like the row without them
+    rng = np.random.default_rng(8)
+    V = 11
+    bad = {0: np.nan, 3: np.inf, 7: -np.inf, 10: np.nan}
+    keep = [j for j in range(V) if j not in bad]
+    U, _ = uniform_codes(300, 9)
+    for trial in range(30):
+        z = np.round(rng.normal(0, 2.0, V) * 8).astype(np.float32) / 8
+        zf = z[keep].copy()
+        for j, v in bad.items():
+            z[j] = v
+        for T in (0.0, 0.3, 1.0):
+            for u in U[10 * trial:10 * trial + 10]:
+                assert sample(z, T, u) == keep[sample(zf, T, u)]
+            p = softmax_f64(z, T)
+            np.testing.assert_array_equal(p[list(bad)], 0.0)
+            np.testing.assert_allclose(p[keep], softmax_f64(zf, T), rtol=1e-15, atol=0)
+
+
+def test_row_without_finite_logit_gives_token_zero():
+    for z in (np.full(6, np.nan, np.float32), np.array([np.inf, -np.inf, np.nan], np.float32)):
+        assert argmax_lowest(z) == 0
+        for T in (0.0, 0.5, 1.0):
+            for u in (0, 12345, TWO24 - 1):
+                assert sample(z, T, u) == 0
+        W, S = fixed_weights(z, 1.0)
+        assert S == 0 and (W == 0).all()
