@@ -52,11 +52,21 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// (value, index) max with the lowest index winning ties; NaN values lose.
+// (value, index) max with the lowest index winning ties.  Non-finite logits
+// (NaN, +-Inf) carry no probability and never win: cand() turns them into the
+// empty candidate {-inf, kNoIndex}, which every finite value beats; a
+// reduction that ends on kNoIndex had no finite value (token 0 by convention,
+// see argmax_token).
+constexpr int kNoIndex = 0x7fffffff;
 struct ArgMax {
   float v;
   int i;
 };
+__device__ __forceinline__ bool finite(float v) { return fabsf(v) < INFINITY; }
+__device__ __forceinline__ ArgMax cand(float v, int i) {
+  return finite(v) ? ArgMax{v, i} : ArgMax{-INFINITY, kNoIndex};
+}
+__device__ __forceinline__ int argmax_token(const ArgMax& a) { return a.i == kNoIndex ? 0 : a.i; }
 __device__ __forceinline__ ArgMax better(ArgMax a, ArgMax b) {
   if (b.v > a.v || (b.v == a.v && b.i < a.i)) return b;
   return a;
@@ -81,10 +91,13 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
 // ------------------------------------------------------- exact sampling weights
 // w = exp(fl32(fl32(z - M) / T)) in float32, then W = floor(w * 2^40) as an
 // integer, so that every later sum and comparison is exact and order-free.
+// M is the largest finite logit of the row; a non-finite z has weight 0.
 __device__ __forceinline__ unsigned long long fixed_weight(float z, float M, float T) {
-  float t = __fdiv_rn(__fsub_rn(z, M), T);
-  float w = expf(t);
-  return (unsigned long long)((double)w * 1099511627776.0);
+  const bool f = finite(z);
+  float t = __fdiv_rn(__fsub_rn(f ? z : M, M), T);
+  float w = fminf(fmaxf(expf(t), 0.0f), 1.0f);  // z <= M: no change; a NaN (M = -inf) becomes 0
+  const unsigned long long W = (unsigned long long)((double)w * 1099511627776.0);
+  return f ? W : 0ull;
 }
 
 // 128-bit unsigned helpers for the exact accept test.

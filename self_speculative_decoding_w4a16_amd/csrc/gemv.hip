@@ -305,7 +305,7 @@ __device__ __forceinline__ void consume(const GemvArgs& a, const Cursor<R>& c, c
           if (EPI == EPI_RESID) v = c.rres[r] + v;
           const uint16_t b = ss::f2bf(v);
           a.y[c.prow[r]] = b;
-          if (EPI == EPI_LOGITS) best = ss::better(best, ss::ArgMax{ss::bf2f(b), (int)c.prow[r]});
+          if (EPI == EPI_LOGITS) best = ss::better(best, ss::cand(ss::bf2f(b), (int)c.prow[r]));
         }
       }
     }
@@ -468,7 +468,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.0f;
-  ss::ArgMax best = {-INFINITY, 0x7fffffff};
+  ss::ArgMax best = {-INFINITY, ss::kNoIndex};
   // steps t (in A) and t+1 (in B) per iteration, refilling B with t+1 and A
   // with t+2 (both < T)
   int64_t t = 0;

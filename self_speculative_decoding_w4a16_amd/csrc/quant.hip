@@ -5,7 +5,8 @@
 //
 // One thread per (row, 64-group): it reads the 128 bytes of its group with
 // 16-byte loads, finds lo/hi, stores the fp16 {scale, min} and the 32 code
-// bytes.  Every operation that decides a code is a single correctly rounded
+// bytes.  The scale is rounded up where rounding to nearest would leave
+// 15 s below the span, so every weight is within s/2 of its level.  Every operation that decides a code is a single correctly rounded
 // float32 operation (no contraction), so codes are reproducible bit for bit.
 #include "common.h"
 #include "internal.h"
@@ -44,6 +45,9 @@ __global__ __launch_bounds__(256) void w4_quantize_kernel(const uint16_t* __rest
   }
   const float span = __fsub_rn(hi, lo);
   uint16_t s16 = ss::f2h_sat(__fdiv_rn(span, 15.0f));
+  // the 16 levels must reach hi: the smallest fp16 scale with 15 s >= span
+  // (15 s is exact in float32; s >= 0, so the next fp16 value up is s16 + 1)
+  if (__fmul_rn(ss::h2f(s16), 15.0f) < span && s16 < 0x7bffu) s16 = (uint16_t)(s16 + 1u);
   if ((s16 & 0x7fffu) == 0) s16 = 0x3c00u;  // scale 0 -> 1.0
   const uint16_t m16 = ss::f2h_sat(lo);
   const float s = ss::h2f(s16), m = ss::h2f(m16);

@@ -27,8 +27,7 @@ constexpr int kT = 256;
 constexpr int kRejChunk = 4096;
 
 __device__ __forceinline__ unsigned long long wt(float z, float M, float T) {
-  unsigned long long w = ss::fixed_weight(z, M, T);
-  return (z == z) ? w : 0ull;  // NaN logits carry no weight
+  return ss::fixed_weight(z, M, T);  // 0 for non-finite logits
 }
 
 // Residual weight max(0, Wt*Sd - Wd*St) >> shift.
@@ -40,7 +39,8 @@ __device__ __forceinline__ unsigned long long resid_w(unsigned long long Wt, uns
   return ss::shr128(ss::sub128(a, b), shift);
 }
 
-__device__ __forceinline__ int bitlen_minus1(unsigned long long v) { return 63 - __clzll(v); }
+// bit length of v minus one; 0 for v = 0 (a draft row without mass)
+__device__ __forceinline__ int bitlen_minus1(unsigned long long v) { return v ? 63 - __clzll(v) : 0; }
 
 // Block-wide (256 threads) sum of unsigned 64-bit values.
 __device__ unsigned long long block_sum_u64(unsigned long long v, unsigned long long* red) {
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kT) void rowmax_kernel(const uint16_t* __restrict__
   const int cs = (V + gridDim.x - 1) / gridDim.x;
   const int lo = blockIdx.x * cs, hi = min(V, lo + cs);
   ss::ArgMax a = {-INFINITY, 0x7fffffff};
-  for (int j = lo + threadIdx.x; j < hi; j += kT) a = ss::better(a, ss::ArgMax{ss::bf2f(z[j]), j});
+  for (int j = lo + threadIdx.x; j < hi; j += kT) a = ss::better(a, ss::cand(ss::bf2f(z[j]), j));
   a = block_argmax(a, rv, ri);
   if (threadIdx.x == 0) {
     part_max[blockIdx.x] = a.v;
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kT) void sample_kernel(const uint16_t* __restrict__
   for (int i = threadIdx.x + PRE * kT; i < n_pre; i += kT) a = ss::better(a, ss::ArgMax{pre_max[i], pre_arg[i]});
   a = block_argmax(a, rv, ri);
   if (T == 0.0f) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) *token = a.i;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *token = ss::argmax_token(a);
     return;
   }
   const float M = a.v;
@@ -199,8 +199,8 @@ __global__ __launch_bounds__(kT) void sample_kernel(const uint16_t* __restrict__
     s_chunk = S == 0 ? -1 : chunk;
   }
   __syncthreads();
-  if (s_chunk < 0) {  // no mass at all: fall back to the argmax
-    if (threadIdx.x == 0) *token = a.i;
+  if (s_chunk < 0) {  // no finite logit, no mass: token 0
+    if (threadIdx.x == 0) *token = ss::argmax_token(a);
     return;
   }
   const int clo = s_chunk * cs, chi = min(V, clo + cs);
@@ -230,8 +230,8 @@ __global__ __launch_bounds__(kT) void rej_rowmax_kernel(const uint16_t* zt, cons
   int bad = 0;
   for (int j = lo + threadIdx.x; j < hi; j += kT) {
     const float v = ss::bf2f(z[j]);
-    bad |= !(fabsf(v) < INFINITY);
-    a = ss::better(a, ss::ArgMax{v, j});
+    bad |= !ss::finite(v);
+    a = ss::better(a, ss::cand(v, j));
   }
   if (bad) atomicOr(&s_bad, 1);
   a = block_argmax(a, rv, ri);
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(kT) void rej_decide_kernel(const uint16_t* zt, cons
   const int C = (V + kRejChunk - 1) / kRejChunk;
   const int rows = 2 * gamma + 1;
   for (int r = threadIdx.x; r < rows; r += kT) {
-    RowStat s = {-INFINITY, 0x7fffffff, 0, 0ull};
+    RowStat s = {-INFINITY, ss::kNoIndex, 0, 0ull};
     for (int c = 0; c < C; ++c) {
       const ss::ArgMax b = {ws.row_max[r * C + c], ws.row_arg[r * C + c]};
       ss::ArgMax cur = {s.M, s.A};
@@ -291,6 +291,7 @@ __global__ __launch_bounds__(kT) void rej_decide_kernel(const uint16_t* zt, cons
       const float temp = r <= gamma ? T : Td;
       if (temp != 0.0f) s.S += ws.row_sum[r * C + c];
     }
+    s.A = ss::argmax_token(ss::ArgMax{s.M, s.A});  // no finite logit: token 0
     st[r] = s;
   }
   __syncthreads();
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(kT) void rej_decide_kernel(const uint16_t* zt, cons
         ok = (x == t.A);
         pp = ok ? 1.0f : 0.0f;
         qq = (Td == 0.0f) ? (x == d.A ? 1.0f : 0.0f)
-                          : (float)((double)wt(ss::bf2f(zd[(int64_t)i * V + x]), d.M, Td) / (double)d.S);
+             : d.S ? (float)((double)wt(ss::bf2f(zd[(int64_t)i * V + x]), d.M, Td) / (double)d.S) : 0.0f;
       } else {
         const unsigned long long Wt = wt(ss::bf2f(zt[(int64_t)i * V + x]), t.M, T);
         unsigned long long Wd, Sd;
@@ -327,8 +328,8 @@ __global__ __launch_bounds__(kT) void rej_decide_kernel(const uint16_t* zt, cons
         const ss::U128 lhs = ss::mul64((unsigned long long)r_codes[i] * Wd, t.S);
         const ss::U128 rhs = ss::shl128(ss::mul64(Wt, Sd), 24);
         ok = ss::lt128(lhs, rhs);
-        pp = (float)((double)Wt / (double)t.S);
-        qq = (float)((double)Wd / (double)Sd);
+        pp = t.S ? (float)((double)Wt / (double)t.S) : 0.0f;
+        qq = Sd ? (float)((double)Wd / (double)Sd) : 0.0f;
       }
       if (probs && blockIdx.x == 0) {
         probs[2 * i] = pp;
@@ -395,7 +396,7 @@ __global__ __launch_bounds__(kT) void rej_decide_kernel(const uint16_t* zt, cons
     unsigned long long S = 0;
     for (int i = 0; i < C; ++i) S += __builtin_nontemporal_load(ws.res_sum + i);
     bool fallback = false;
-    if (S == 0ull) {  // no residual mass: draw from p
+    if (S == 0ull && resid) {  // no residual mass: draw from p
       fallback = true;
       S = t.S;
     }
@@ -412,13 +413,15 @@ __global__ __launch_bounds__(kT) void rej_decide_kernel(const uint16_t* zt, cons
     }
     s_base = base;
     s_th = th;
-    s_chunk = chunk;
+    s_chunk = S == 0ull ? -1 : chunk;  // p without mass (no finite logit): token 0
     s_fallback = fallback;
   }
   __syncthreads();
   const int clo = s_chunk * kRejChunk, chi = min(V, clo + kRejChunk);
   int y;
-  if (s_fallback) {
+  if (s_chunk < 0) {
+    y = 0;
+  } else if (s_fallback) {
     y = scan_pick(clo, chi, s_base, s_th, [&](int j) { return wt(ss::bf2f(zrow_t[j]), t.M, T); }, red,
                   &s_pick);
   } else {

@@ -221,7 +221,7 @@ def test_sample_matches_oracle(cuda, V, T):
 REJECT_CASES = [
     (4, 1000, 1.0, 1.0), (4, 1000, 0.0, 0.0), (4, 1000, 0.6, 0.6), (4, 1000, 1.0, 0.0),
     (4, 1000, 0.0, 0.2), (16, 152064, 0.0, 0.0), (16, 152064, 1.0, 0.2), (48, 4096, 0.6, 0.6),
-    (0, 1000, 1.0, 1.0),
+    (48, 152064, 0.6, 0.6), (0, 1000, 1.0, 1.0),
 ]
 
 
