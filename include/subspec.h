@@ -246,6 +246,16 @@ int subspec_kv_rollback(const subspec_state *st, const int32_t *n_accepted,
  * L = capacity (SUBSPEC_ECAPACITY otherwise). */
 int subspec_kv_select(const subspec_model *m, const subspec_state *st, void *stream);
 
+/* Entries of every sparse index list that subspec_kv_select builds at
+ * kv_len = L ([SSL] section 3.1: sink + recent + important positions, about
+ * budget_permille / 1000 of the context): min(L, max(ceil(budget_permille *
+ * L / 1000), |sink| + |recent|)) with |sink| = min(n_sink, L) and |recent| =
+ * min(n_recent, L - |sink|).  Host-side arithmetic only (no device work);
+ * callers size kv_index with it (index_cap = the count at L = capacity).
+ * Returns -1 for L < 0, negative n_sink / n_recent or a budget outside
+ * [0, 1000]. */
+int64_t subspec_index_count(int64_t L, int32_t n_sink, int32_t n_recent, int32_t budget_permille);
+
 /* kv_len += delta (device), e.g. after a prefill chunk run through verify. */
 int subspec_kv_advance(const subspec_state *st, int32_t delta, void *stream);
 

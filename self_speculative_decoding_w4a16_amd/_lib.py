@@ -76,6 +76,7 @@ _SIGS = {
     "subspec_kv_rollback": (c_int32, [POINTER(State), c_void_p, c_void_p, c_void_p]),
     "subspec_kv_advance": (c_int32, [POINTER(State), c_int32, c_void_p]),
     "subspec_kv_select": (c_int32, [POINTER(Model), POINTER(State), c_void_p]),
+    "subspec_index_count": (c_int64, [c_int64, c_int32, c_int32, c_int32]),
     "subspec_w4_gemv": (c_int32, [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p,
                                   c_void_p]),
     "subspec_bf16_gemv": (c_int32, [c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
@@ -195,11 +196,11 @@ def kv_select(model, state, stream=None):
 
 
 def index_count(L, n_sink, n_recent, budget_permille):
-    """Entries of every sparse index list at kv_len = L (as subspec_kv_select)."""
-    s = min(n_sink, L)
-    rec = min(n_recent, L - s)
-    total = (budget_permille * L + 999) // 1000
-    return min(L, max(total, s + rec))
+    """Entries of every sparse index list at kv_len = L (subspec_index_count)."""
+    n = lib().subspec_index_count(L, n_sink, n_recent, budget_permille)
+    if n < 0:
+        raise SubspecError(EINVAL, last_error())
+    return n
 
 
 def kv_advance(state, delta, stream=None):

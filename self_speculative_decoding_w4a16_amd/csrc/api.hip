@@ -138,11 +138,14 @@ int check_model(const subspec_model* m) {
 
 // Entries of every sparse index list at kv_len = L: min(L, max(ceil(budget
 // * L), |sink| + |recent|)), non-decreasing in L.
-int64_t index_count(int64_t L, const subspec_state* st) {
-  const int64_t sk = std::min<int64_t>(st->n_sink, L);
-  const int64_t rec = std::min<int64_t>(st->n_recent, L - sk);
-  const int64_t total = ((int64_t)st->budget_permille * L + 999) / 1000;
+int64_t index_count_of(int64_t L, int64_t n_sink, int64_t n_recent, int64_t budget_permille) {
+  const int64_t sk = std::min<int64_t>(n_sink, L);
+  const int64_t rec = std::min<int64_t>(n_recent, L - sk);
+  const int64_t total = (budget_permille * L + 999) / 1000;
   return std::min<int64_t>(L, std::max<int64_t>(total, sk + rec));
+}
+int64_t index_count(int64_t L, const subspec_state* st) {
+  return index_count_of(L, st->n_sink, st->n_recent, st->budget_permille);
 }
 
 int check_state(const subspec_model* m, const subspec_state* st) {
@@ -280,6 +283,15 @@ int gemv_class(const subspec_linear& l, int site) {
 extern "C" {
 
 int subspec_abi_version(void) { return SUBSPEC_ABI_VERSION; }
+
+int64_t subspec_index_count(int64_t L, int32_t n_sink, int32_t n_recent, int32_t budget_permille) {
+  if (L < 0 || n_sink < 0 || n_recent < 0 || budget_permille < 0 || budget_permille > 1000) {
+    fail(SUBSPEC_EINVAL, "index_count: L, n_sink, n_recent must be >= 0 and budget_permille in [0, 1000]");
+    return -1;
+  }
+  ok();
+  return index_count_of(L, n_sink, n_recent, budget_permille);
+}
 
 const char* subspec_last_error(void) { return g_err.c_str(); }
 

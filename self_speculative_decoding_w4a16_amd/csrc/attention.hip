@@ -1430,16 +1430,9 @@ int draft_attn_keys_per_split() { return DSK; }
 // Key splits per query head: one per 96 keys of the launch's bound, at most 8
 // (at the 7B shape with ~900 keys, 8 splits measured 6.8 us a layer against
 // 7.5 for 4 and 8.6 for 1; over a ~6000-key sparse index, 8 splits 21.4 us
-// against 26.9 for 16).  SUBSPEC_DRAFT_HEAD_SPLITS overrides (up to
-// DQ_MAXSPLITS), for measurements.  The caller also keeps the grid (query
-// heads x splits) within one block per compute unit.
+// against 26.9 for 16).  The caller also keeps the grid (query heads x
+// splits) within one block per compute unit.
 int draft_head_splits(int max_keys) {
-  static int forced = -1;
-  if (forced < 0) {
-    const char* e = getenv("SUBSPEC_DRAFT_HEAD_SPLITS");
-    forced = e ? atoi(e) : 0;
-  }
-  if (forced > 0) return forced < DQ_MAXSPLITS ? forced : DQ_MAXSPLITS;
   const int s = (max_keys + 95) / 96;
   return s < 1 ? 1 : (s > 8 ? 8 : s);
 }

@@ -543,15 +543,9 @@ struct Occupancy {
 // matrix has fewer row groups.  `site_per_cu` (> 0) overrides the default
 // for a site measured faster with another count.
 int64_t gemv_blocks(int64_t n_groups, bool w4, int fit, int threads, int site_per_cu = 0) {
-  static int per_cu = -1;
-  if (per_cu < 0) {
-    const char* e = getenv("SUBSPEC_GEMV_BLOCKS_PER_CU");
-    per_cu = e ? atoi(e) : 0;
-    if (per_cu <= 0) per_cu = 0;
-  }
   const int waves = threads / SS_WAVE;
-  int want = threads == kThreads ? (per_cu > 0 ? per_cu : 4) * (w4 ? 1 : 2) : 1;
-  if (threads == kThreads && per_cu == 0 && site_per_cu > 0) want = site_per_cu;
+  int want = threads == kThreads ? 4 * (w4 ? 1 : 2) : 1;
+  if (threads == kThreads && site_per_cu > 0) want = site_per_cu;
   if (fit > 0 && want > fit) want = fit;
   const int64_t cap = (int64_t)device_cus() * want;
   const int64_t need = (n_groups + waves - 1) / waves;

@@ -172,10 +172,19 @@ class SpecDecoder:
         """Speculative decoding of at least n_generate tokens after ``prompt``.
         ``uniforms`` = (U_draft [C][gamma], R [C][gamma], U_final [C]) uint32
         device tensors, or None for greedy runs.  Returns (tokens, per-cycle n)."""
+        kv = len(prompt) - 1
+        if kv + self.gamma + 1 > self.capacity:
+            raise ValueError(f"prompt of {len(prompt)} tokens leaves no room for a cycle of "
+                             f"{self.gamma + 1} positions in a KV capacity of {self.capacity}")
         self.prefill(prompt)
         out, ns = [], []
         c = 0
         while len(out) < n_generate:
+            # a cycle writes positions kv .. kv + gamma; stop before the cache
+            # would overflow instead of letting rollback move past capacity
+            if kv + self.gamma + 1 > self.capacity:
+                raise ValueError(f"KV capacity {self.capacity} reached after {len(out)} of "
+                                 f"{n_generate} tokens (kv_len {kv}, gamma {self.gamma})")
             if uniforms is not None:
                 ud, rr, uf = uniforms
                 self.cycle(ud[c], rr[c], uf[c:c + 1])
@@ -184,6 +193,7 @@ class SpecDecoder:
             n = int(self.n_accepted.item())
             out += self.out_tokens[:n + 1].tolist()
             ns.append(n)
+            kv += n + 1
             if on_cycle:
                 on_cycle(c, n)
             c += 1

@@ -165,3 +165,16 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError):
         _lib.lib()
+
+
+def test_index_count_matches_the_oracle_rule():
+    # host-side arithmetic of the library (no device work): the list size of
+    # the sparse draft index equals what the oracle's selection rule keeps
+    from oracle.sparse import index_bounds
+    for L in (0, 1, 3, 4, 67, 68, 69, 500, 4096, 60011):
+        for sink, recent, budget in ((4, 64, 100), (0, 0, 1000), (4, 64, 0), (16, 8, 333), (4, 64, 1000)):
+            s, r, K = index_bounds(L, sink, recent, budget)
+            assert _lib.index_count(L, sink, recent, budget) == s + K + (L - r)
+    for bad in ((-1, 4, 64, 100), (10, -1, 64, 100), (10, 4, -1, 100), (10, 4, 64, 1001)):
+        with pytest.raises(_lib.SubspecError):
+            _lib.index_count(*bad)
