@@ -229,6 +229,26 @@ int subspec_reject(int32_t gamma, int32_t vocab, float temp, float draft_temp,
                    int32_t *n_accepted, int32_t *out_tokens, int32_t *status, float *probs,
                    void *ws, size_t ws_bytes, void *stream);
 
+/* subspec_reject without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, kernels and results as
+ * subspec_reject, minus ws / ws_bytes: the scratch (per-row partial maxima,
+ * flags and fixed-point sums, residual chunk sums, the arrival counter) is a
+ * static 1 MiB device array per GPU, held until the process ends; its device
+ * address is looked up once per device (hipGetSymbolAddress).  The call
+ * allocates nothing and clears the counter itself with a fill kernel.
+ * Limit: 1024 + 20 (2 gamma + 1) ceil(vocab / 4096) bytes (each array rounded
+ * up to 256 bytes) must fit in 1 MiB, else SUBSPEC_ECAPACITY and nothing is
+ * enqueued (gamma 64 fits vocab up to ~1.6M; gamma 16 up to 2^24 does not).
+ * Every call on one GPU uses that GPU's one array: calls that overlap on one
+ * GPU (two streams, or two threads) race and must be serialised by the
+ * caller. */
+int subspec_reject_noalloc(int32_t gamma, int32_t vocab, float temp, float draft_temp,
+                           const uint16_t *target_logits, const uint16_t *draft_logits,
+                           const int32_t *draft_tokens, const uint32_t *r_codes, const uint32_t *u_code,
+                           int32_t *n_accepted, int32_t *out_tokens, int32_t *status, float *probs,
+                           void *stream);
+
 /* Commit a round ([SD] Module 2: discard the K/V of rejected positions):
  * kv_len += n + 1 and tokens[0] = out_tokens[n], n = *n_accepted (device). */
 int subspec_kv_rollback(const subspec_state *st, const int32_t *n_accepted,

@@ -73,6 +73,9 @@ _SIGS = {
     "subspec_reject": (c_int32, [c_int32, c_int32, c_float, c_float, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_size_t, c_void_p]),
+    "subspec_reject_noalloc": (c_int32, [c_int32, c_int32, c_float, c_float, c_void_p, c_void_p,
+                                         c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_void_p, c_void_p]),
     "subspec_kv_rollback": (c_int32, [POINTER(State), c_void_p, c_void_p, c_void_p]),
     "subspec_kv_advance": (c_int32, [POINTER(State), c_int32, c_void_p]),
     "subspec_kv_select": (c_int32, [POINTER(Model), POINTER(State), c_void_p]),
@@ -184,6 +187,14 @@ def reject(gamma, vocab, temp, draft_temp, target_logits, draft_logits, draft_to
                                _p(draft_tokens), _p(r_codes), _p(u_code), _p(n_accepted),
                                _p(out_tokens), _p(status), _p(probs), _p(ws),
                                ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def reject_noalloc(gamma, vocab, temp, draft_temp, target_logits, draft_logits, draft_tokens, r_codes,
+                   u_code, n_accepted, out_tokens, status, probs, stream=None):
+    check(lib().subspec_reject_noalloc(gamma, vocab, temp, draft_temp, _p(target_logits),
+                                       _p(draft_logits), _p(draft_tokens), _p(r_codes), _p(u_code),
+                                       _p(n_accepted), _p(out_tokens), _p(status), _p(probs),
+                                       _stream(stream)))
 
 
 def kv_rollback(state, n_accepted, out_tokens, stream=None):

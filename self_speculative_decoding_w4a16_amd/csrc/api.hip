@@ -280,6 +280,18 @@ int gemv_class(const subspec_linear& l, int site) {
 
 }  // namespace
 
+// Error reporting for the entry points of other translation units.
+int noalloc_fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+int noalloc_ok() { return ok(); }
+
 extern "C" {
 
 int subspec_abi_version(void) { return SUBSPEC_ABI_VERSION; }
