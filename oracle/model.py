@@ -15,6 +15,14 @@ norm outputs, each GEMV/GEMM output, Q and K after RoPE, the KV cache,
 attention output, each residual sum, the SiLU*up product and the logits.
 A residual-add projection is rounded once: bf16(h + W x).
 
+Summation precision: the sums of every projection are float64 by default.
+``acc=np.float32`` evaluates the same definition with float32 sums (the
+definition fixes the storage points, not the order or precision of a sum;
+the GPU sums in float32 in its own order).  Over one layer the two agree to
+well inside the logits tolerance; over many random-init layers the bf16
+roundings they take differently compound, and their distance measures how
+far two equally valid evaluations of a deep model part.
+
 Pinned by: verify row j equals the one-token decode at the same position,
 attention equal to the masked full-matrix softmax, RMSNorm of a constant
 vector, RoPE's norm preservation and relative-position property, the W4
@@ -44,20 +52,23 @@ class OracleModel:
     final_norm: np.ndarray       # [H]
     lm_head: np.ndarray          # [V][H]
     layers: list                 # dicts: attn_norm, ffn_norm, qkv, o, gate_up, down
-    substitute: list = field(default_factory=list)  # per layer: None or dict name -> (codes, meta)
+    substitute: list = field(default_factory=list)  # per layer: None or dict name -> (codes, meta, bits)
 
-    def make_substitutes(self, layer_ids):
-        """Quantise every matrix of the listed layers (O1); others stay shared."""
+    def make_substitutes(self, layer_ids, bits=4):
+        """Quantise every matrix of the listed layers (O1) at ``bits`` (an int,
+        or a list giving each listed layer its width); others stay shared."""
         self.substitute = [None] * self.n_layers
-        for l in layer_ids:
-            self.substitute[l] = {name: quantize(self.layers[l][name])
+        layer_ids = list(layer_ids)
+        widths = bits if isinstance(bits, (list, tuple)) else [bits] * len(layer_ids)
+        for l, b in zip(layer_ids, widths):
+            self.substitute[l] = {name: quantize(self.layers[l][name], bits=b) + (b,)
                                   for name in ("qkv", "o", "gate_up", "down")}
 
     def weight(self, l, name, draft):
         """Float64 weight matrix used by the draft (substitute) or the target."""
         if draft and self.substitute and self.substitute[l] is not None:
-            codes, meta = self.substitute[l][name]
-            return dequantize(codes, meta)
+            codes, meta, bits = self.substitute[l][name]
+            return dequantize(codes, meta, bits=bits)
         return np.asarray(self.layers[l][name], dtype=np.float64)
 
 
@@ -73,9 +84,14 @@ def rmsnorm(h, g, eps):
     return round_bf16(h / np.sqrt(ms + eps) * np.asarray(g, dtype=np.float64))
 
 
-def linear(x, w):
-    """bf16(x W^T): rows of x against rows of W (float64 accumulate)."""
-    return round_bf16(np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T)
+def linear(x, w, acc=np.float64):
+    """bf16(x W^T): rows of x against rows of W (sums in float64, or acc)."""
+    return round_bf16((np.asarray(x, dtype=acc) @ np.asarray(w, dtype=acc).T).astype(np.float64))
+
+
+def project(x, w, acc=np.float64):
+    """x W^T with sums in float64 (or acc), not rounded."""
+    return (np.asarray(x, dtype=acc) @ np.asarray(w, dtype=acc).T).astype(np.float64)
 
 
 def rope(x, pos, theta):
@@ -104,7 +120,7 @@ def attend(q, K, V, n_keys):
 
 
 def forward(model, kv, kv_len, tokens, draft=False, keep_logits=True, sparse=None, scores=None,
-            score_window=16):
+            score_window=16, acc=np.float64):
     """Run tokens[j] at position kv_len + j, j = 0..n-1, through the decoder.
 
     Writes the K/V of those positions into ``kv`` and returns the logits
@@ -116,6 +132,7 @@ def forward(model, kv, kv_len, tokens, draft=False, keep_logits=True, sparse=Non
     speculative positions [base, kv_len + j] (sparse.py).
     ``scores``: a list that receives, per layer, the importance scores
     [n_kv_heads][kv_len + n] of this pass (sparse.py, importance_scores).
+    ``acc``: precision of the projection sums (float64, or float32).
     """
     K, V = kv
     n = len(tokens)
@@ -125,7 +142,7 @@ def forward(model, kv, kv_len, tokens, draft=False, keep_logits=True, sparse=Non
     for l in range(model.n_layers):
         lw = model.layers[l]
         x = rmsnorm(h, lw["attn_norm"], model.rms_eps)
-        qkv = linear(x, model.weight(l, "qkv", draft))
+        qkv = linear(x, model.weight(l, "qkv", draft), acc)
         attn = np.zeros((n, Hq * d))
         for j in range(n):
             pos = kv_len + j
@@ -154,13 +171,13 @@ def forward(model, kv, kv_len, tokens, draft=False, keep_logits=True, sparse=Non
         if scores is not None:
             scores.append(sc)
         attn = round_bf16(attn)
-        h = round_bf16(h + attn @ model.weight(l, "o", draft).T)
+        h = round_bf16(h + project(attn, model.weight(l, "o", draft), acc))
         x = rmsnorm(h, lw["ffn_norm"], model.rms_eps)
-        gu = linear(x, model.weight(l, "gate_up", draft))
+        gu = linear(x, model.weight(l, "gate_up", draft), acc)
         F = model.ffn
         act = round_bf16(silu(gu[:, :F]) * gu[:, F:])
-        h = round_bf16(h + act @ model.weight(l, "down", draft).T)
+        h = round_bf16(h + project(act, model.weight(l, "down", draft), acc))
     if not keep_logits:
         return None
     x = rmsnorm(h, model.final_norm, model.rms_eps)
-    return linear(x, model.lm_head)
+    return linear(x, model.lm_head, acc)

@@ -118,3 +118,23 @@ def test_self_draft_accepts_everything():
     U = (Ud.reshape(cycles, gamma), R.reshape(cycles, gamma), Uf)
     out, ns = speculative_generate(m, prompt, (gamma + 1) * cycles, gamma, 0.7, 0.7, U, 64)
     assert ns == [gamma] * cycles
+
+
+def test_float32_sums_agree_over_one_layer():
+    # the definition fixes the bf16 storage points, not the precision of the
+    # sums: float32 sums of one layer stay well inside the logits tolerance
+    from synth import model_weights, kv_history, token_ids
+    from synth.configs import QWEN7B
+    from tests.helpers import host, oracle_model
+    shape = QWEN7B.with_(n_layers=1, hidden=512, ffn=1024, n_q_heads=4, n_kv_heads=2, vocab=500,
+                         n_shared=0)
+    w = model_weights(shape, 3, "cpu")
+    om = oracle_model(shape, w, [0])
+    K, V = kv_history(1, 2, 20, 128, 24, 4, "cpu")
+    kv = lambda: (host(K).astype(np.float64), host(V).astype(np.float64))
+    toks = [int(t) for t in token_ids(3, 500, 5)]
+    for draft in (False, True):
+        a = forward(om, kv(), 20, toks, draft=draft)
+        b = forward(om, kv(), 20, toks, draft=draft, acc=np.float32)
+        rel = np.abs(a - b).max() / np.abs(a).max()
+        assert 0 < rel < 1e-2
