@@ -107,3 +107,77 @@ def test_constant_group_is_degenerate():
 def test_k_must_be_group_multiple():
     with pytest.raises(ValueError):
         quantize(np.zeros((1, 96), dtype=np.float32))
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_exact_levels_group_low_bits(bits):
+    # values on the 2**bits levels of lo = -1, s = 0.125: codes k % 2**bits
+    L = (1 << bits) - 1
+    k = np.arange(128)
+    q = k % (L + 1)
+    x = (-1.0 + 0.125 * q).astype(np.float32).reshape(1, 128)
+    codes, meta = quantize(x, bits=bits)
+    assert meta[0, 0, 0] == np.float16(0.125) and meta[0, 0, 1] == np.float16(-1.0)
+    np.testing.assert_array_equal(unpack_codes(codes, bits, 128)[0], q)
+    np.testing.assert_array_equal(dequantize(codes, meta, bits=bits)[0], x[0])
+    # the byte layouts, written out by hand from the codes
+    lo2 = [(q[4 * j] & 3) | ((q[4 * j + 1] & 3) << 2) | ((q[4 * j + 2] & 3) << 4) | ((q[4 * j + 3] & 3) << 6)
+           for j in range(32)]
+    if bits == 2:
+        assert codes.shape == (1, 32)
+        np.testing.assert_array_equal(codes[0], lo2)
+    else:
+        hi = [sum(((q[8 * j + t] >> 2) & 1) << t for t in range(8)) for j in range(16)]
+        assert codes.shape == (1, 48)
+        np.testing.assert_array_equal(codes[0], lo2 + hi)
+    # 2 bits of codes 0..3 repeating: every byte is 0b11100100
+    if bits == 2:
+        assert (codes == 0xE4).all()
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_brute_force_nearest_level_low_bits(bits):
+    w = _bf16_values((16, 256), 0.02, 21 + bits)
+    codes, meta = quantize(w, bits=bits)
+    q = unpack_codes(codes, bits, 256)
+    s = np.repeat(meta[:, :, 0].astype(np.float64), 64, axis=1)
+    m = np.repeat(meta[:, :, 1].astype(np.float64), 64, axis=1)
+    lv = np.arange(1 << bits)[None, None, :] * s[:, :, None] + m[:, :, None]
+    best = np.argmin(np.abs(w.astype(np.float64)[:, :, None] - lv), axis=2)
+    quotient = (w.astype(np.float64) - m) / s
+    near_half = np.abs(quotient - np.floor(quotient) - 0.5) < 1e-5
+    assert not ((best != q) & ~near_half).any()
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("std", [1e-7, 2e-6, 1e-3, 0.02, 5.0])
+def test_round_trip_bound_low_bits(bits, std):
+    w = _bf16_values((128, 512), std, 31)
+    codes, meta = quantize(w, bits=bits)
+    err = np.abs(w.astype(np.float64) - dequantize(codes, meta, bits=bits))
+    s = np.repeat(meta[:, :, 0].astype(np.float64), 64, axis=1)
+    assert (err <= s / 2 * (1 + 1e-6)).all()
+    if std < 1e-3:
+        return  # subnormal scales: the covering scale can leave hi below the top level
+    # the extremes sit on the end levels
+    q = unpack_codes(codes, bits, 512).reshape(128, 8, 64)
+    g = w.reshape(128, 8, 64)
+    assert (np.take_along_axis(q, g.argmin(axis=2)[:, :, None], 2) == 0).all()
+    assert (np.take_along_axis(q, g.argmax(axis=2)[:, :, None], 2) == (1 << bits) - 1).all()
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_scale_is_smallest_fp16_covering_span_low_bits(bits):
+    L = (1 << bits) - 1
+    fp16 = np.sort(np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64))
+    w = _bf16_values((32, 256), 0.02, 40 + bits)
+    _, meta = quantize(w, bits=bits)
+    g = w.reshape(32, 4, 64).astype(np.float64)
+    span = g.max(axis=2) - g.min(axis=2)
+    want = fp16[np.searchsorted(fp16 * L, span, side="left")]
+    np.testing.assert_array_equal(meta[:, :, 0].astype(np.float64), want)
+
+
+def test_bits_argument_checked():
+    with pytest.raises(ValueError):
+        quantize(np.zeros((1, 64), dtype=np.float32), bits=5)
