@@ -324,12 +324,14 @@ def main():
         log(f"plain bf16 autoregressive decode: {ar:.2f} tok/s")
 
     # ---------------------------------------------------------------- small workloads
-    tiny = layer = None
+    tiny = layer = lowbit = None
     if args.config == "full7b" and not args.no_small:
         tiny = tiny_rates(dev)
         log(f"tiny workload: {json.dumps(tiny)}")
         layer = layer7b_rates(dev)
         log(f"one 7B layer: {json.dumps(layer)}")
+        lowbit = lowbit_rates(dec, shape, w, wl, kv0, last, dev)
+        log(f"3- and 2-bit substitutes: {json.dumps(lowbit)}")
 
     # ---------------------------------------------------------------- CPU oracle
     cpu = None
@@ -382,6 +384,7 @@ def main():
         "speculative_over_plain_ar": round(tok_s / ar, 4) if ar else None,
         "tiny": tiny,
         "layer7b": layer,
+        "lowbit": lowbit,
         "kernels": kern,
     }
     # every rate also against the measured read ceiling
@@ -557,17 +560,18 @@ def hbm(bytes_, us, label, **extra):
     return out
 
 
-def model_bytes(shape, draft_w4_layers, kv_positions_draft, kv_positions_verify):
+def model_bytes(shape, draft_w4_layers, kv_positions_draft, kv_positions_verify, bits=4):
     """Algorithmic bytes of one draft step and one verify pass: every weight
-    read once (bf16 2 B, W4 0.5 B + 4 B of fp16 scale/min per 64 weights),
-    the lm_head, and the K/V rows each attention reads once."""
+    read once (bf16 2 B; a `bits`-bit substitute bits/8 B + 4 B of fp16
+    scale/min per 64 weights), the lm_head, and the K/V rows each attention
+    reads once."""
     H, F = shape.hidden, shape.ffn
     qkv = (shape.n_q_heads + 2 * shape.n_kv_heads) * shape.head_dim
     qd = shape.n_q_heads * shape.head_dim
     per_layer = qkv * H + H * qd + 2 * F * H + H * F
     kv_row = 2 * shape.n_kv_heads * shape.head_dim * 2  # K + V bytes per position and layer
     lm = 2.0 * shape.vocab * H
-    w4 = per_layer * (0.5 + 4 / 64)
+    w4 = per_layer * (bits / 8 + 4 / 64)
     draft = (draft_w4_layers * w4 + (shape.n_layers - draft_w4_layers) * 2.0 * per_layer + lm
              + shape.n_layers * kv_positions_draft * kv_row)
     verify = shape.n_layers * 2.0 * per_layer + lm + shape.n_layers * kv_positions_verify * kv_row
@@ -633,6 +637,51 @@ def layer7b_rates(dev, gamma=16, ctx=1024):
             "method": "(5-layer - 1-layer graph-replayed step) / 4, KV 1024 positions",
             "raw_us": {"draft_1": round(t[1][0], 2), "draft_5": round(t[5][0], 2),
                        "verify_1": round(t[1][1], 2), "verify_5": round(t[5][1], 2)}}
+
+
+def lowbit_rates(dec, shape, w, wl, kv0, last, dev):
+    """Substitutes at 3 and 2 bits (the paper note's substitute widths) on the
+    same model and KV state: one graph-replayed draft step and the isolated
+    gate/up and down GEMVs at each width, against their algorithmic bytes."""
+    import torch
+
+    from self_speculative_decoding_w4a16_amd import _lib
+    from self_speculative_decoding_w4a16_amd.engine import SpecDecoder
+    from self_speculative_decoding_w4a16_amd.model import DeviceModel
+    out = {}
+    H, F = shape.hidden, shape.ffn
+    for bits in (3, 2):
+        dm = DeviceModel(shape, w, bits=bits)
+        d = SpecDecoder(dm, dec.capacity, wl.gamma, 0.0, 0.0, graphs=False)
+        d.k_cache.copy_(dec.k_cache)
+        d.v_cache.copy_(dec.v_cache)
+        d.reset(kv0, last)
+        n_sub = len(dm.substitute_layers)
+        draft_b, _, layer_b, _, _ = model_bytes(shape, n_sub, kv0 + 1, kv0 + 1, bits=bits)
+        us = replay_us(lambda: _lib.draft_step(dm.c, d.c, 0, 0.0, None, d.ws))
+        sites = {}
+        x = {H: torch.randn(H, device=dev).bfloat16(), F: torch.randn(F, device=dev).bfloat16()}
+        y = torch.empty(F, dtype=torch.bfloat16, device=dev)
+        g = dm.w["final_norm"]
+        resid = torch.zeros(H, dtype=torch.bfloat16, device=dev)
+        for site, k, nout, epi in (("gate_up", H, F, 2), ("down", F, H, 1)):
+            lins = [_lib.linear(codes=dm.q[l][site][0], meta=dm.q[l][site][1], bits=bits)
+                    for l in dm.substitute_layers]
+            reps = max(1, int((1 << 30) // (n_sub * (2 if epi == 2 else 1) * nout * k * (bits / 8 + 4 / 64))))
+
+            def run(lins=lins, k=k, epi=epi):
+                for _ in range(reps):
+                    for lin in lins:
+                        _lib.gemv(lin, x[k], y, norm_w=g if epi == 2 else None, eps=1e-6, epilogue=epi,
+                                  resid=resid if epi == 1 else None)
+            t = replay_us(run, reps=2) / (reps * len(lins))
+            by = (2 if epi == 2 else 1) * nout * k * (bits / 8 + 4 / 64) + 2 * k + 2 * nout * (2 if epi == 1 else 1)
+            sites[site] = hbm(by, t, f"{bits}-bit {site} GEMV")
+        out[f"w{bits}"] = {"draft_step": hbm(draft_b, us, f"draft step with {bits}-bit substitutes"),
+                           "layer_weight_bytes": round(layer_b), **sites}
+        del d, dm
+        torch.cuda.empty_cache()
+    return out
 
 
 def tiny_rates(dev, reps=200):

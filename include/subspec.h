@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define SUBSPEC_ABI_VERSION 1
+#define SUBSPEC_ABI_VERSION 2
 
 enum {
   SUBSPEC_OK = 0,
@@ -80,14 +80,17 @@ const char *subspec_last_error(void);
 /* One linear layer y = W x with W of shape [n][k] (row n = output n).
  * Exactly one of the two forms is set:
  *   bf16:  w     = bf16 [n][k] row-major, codes = meta = NULL;
- *   W4:    codes = uint8 [n][k/2], byte j of a row = q[2j] | q[2j+1] << 4,
- *          meta  = fp16 [n][k/64][2] = {scale, min} of each 64-group along k;
- *          the weight is q * scale + min (see subspec_quantize); w = NULL.   */
+ *   low-bit: codes = uint8 rows of `bits`-bit codes in the layout of
+ *          subspec_quantize ([n][k/2] at 4 bits, [n][k/4] at 2, [n][3k/8]
+ *          at 3), meta = fp16 [n][k/64][2] = {scale, min} of each 64-group
+ *          along k; the weight is q * scale + min; w = NULL.
+ *   bits:  4, 3 or 2 for the low-bit form (0 reads as 4); ignored for bf16. */
 typedef struct {
   const uint16_t *w;
   const uint8_t *codes;
   const uint16_t *meta;
   int64_t n, k;
+  int32_t bits;
 } subspec_linear;
 
 /* One decoder layer ([SSN] Method details: a substitute keeps the layer's
@@ -172,13 +175,24 @@ int subspec_workspace_init(void *ws, size_t ws_bytes, void *stream);
 /* Substitute construction  ([SSN] Method details; [SSR] section 2.2)        */
 /* ------------------------------------------------------------------------ */
 
-/* Quantise a bf16 [n][k] matrix to 4-bit uniform asymmetric codes, groups of
- * `group` = 64 consecutive weights along k.  Per group: lo/hi = min/max,
- * scale = fp16(fl32(fl32(hi-lo)/15)) (1 if that is 0; saturating), min =
- * fp16(lo) (saturating), code = clamp(rint_even(fl32(fl32(x-min)/scale)),
- * 0, 15) using the stored fp16 values, no fused multiply-add.
- * Outputs: codes uint8 [n][k/2], meta fp16 [n][k/64][2].  k % 64 == 0,
- * bits == 4, group == 64; otherwise SUBSPEC_EUNSUPPORTED / SUBSPEC_ESHAPE. */
+/* Quantise a bf16 [n][k] matrix to `bits`-bit uniform asymmetric codes
+ * (bits = 4, 3 or 2; L = 2^bits - 1), groups of `group` = 64 consecutive
+ * weights along k ([SSN]: substitutes at 2/3 bits; [SSR] section 2.2: 4).
+ * Per group: lo/hi = min/max, scale = the smallest fp16 value s with
+ * L s >= fl32(hi - lo), found as fp16(fl32(fl32(hi-lo)/L)) raised by one fp16
+ * step when L s falls short (1 if it is 0; saturating at the fp16 maximum),
+ * min = fp16(lo) (saturating), code = clamp(rint_even(fl32(fl32(x-min)/
+ * scale)), 0, L) using the stored fp16 values, no fused multiply-add; every
+ * weight in the fp16 range is then within scale/2 of its level.
+ * Outputs: meta fp16 [n][k/64][2] = {scale, min}; codes uint8, per row:
+ *   4 bits: k/2 bytes, byte j = q[2j] | q[2j+1] << 4;
+ *   2 bits: k/4 bytes, byte j = q[4j] | q[4j+1] << 2 | q[4j+2] << 4 | q[4j+3] << 6;
+ *   3 bits: 3k/8 bytes: the low two bits of every code in the 2-bit layout
+ *           (k/4 bytes), then the third bits (k/8 bytes) in 4-byte words of
+ *           32 weights whose bytes hold weights 0-7, 16-23, 8-15, 24-31 of
+ *           the word (bit t of a byte: its t-th weight).
+ * k % 64 == 0 (k % 128 == 0 at 3 bits, so rows stay 16-byte aligned),
+ * group == 64; otherwise SUBSPEC_EUNSUPPORTED / SUBSPEC_ESHAPE. */
 int subspec_quantize(const uint16_t *w, int64_t n, int64_t k, int32_t group, int32_t bits,
                      uint8_t *codes, uint16_t *meta, void *stream);
 
@@ -284,7 +298,8 @@ int subspec_kv_advance(const subspec_state *st, int32_t delta, void *stream);
 /* ------------------------------------------------------------------------ */
 
 /* y[n] = bf16( sum_k (q[n][k] * scale + min) * x[k] ) at batch 1 (the draft's
- * W4A16 GEMV).  x bf16 [k], y bf16 [n]; k % 64 == 0. */
+ * W4A16 GEMV, 4-bit codes; subspec_gemv takes every width).  x bf16 [k],
+ * y bf16 [n]; k % 64 == 0. */
 int subspec_w4_gemv(const uint8_t *codes, const uint16_t *meta, int64_t n, int64_t k,
                     const uint16_t *x, uint16_t *y, void *stream);
 
@@ -300,7 +315,7 @@ int subspec_bf16_gemv(const uint16_t *w, int64_t n, int64_t k, const uint16_t *x
  *   epilogue 2: y[n] = bf16( SiLU(g) * u ), g = bf16((W x')[n]),
  *               u = bf16((W x')[F + n]), for n < F = w->n / 2 (gate rows
  *               first, then the up rows)
- * w: bf16 (w set) or W4 (codes + meta set) weights [n][k]; x, norm_w bf16 [k];
+ * w: bf16 (w set) or low-bit (codes + meta + bits) weights [n][k]; x, norm_w bf16 [k];
  * resid, y bf16.  k % 64 == 0, k <= 28672 (k <= 6144 with norm_w).  Errors:
  * EINVAL for bad pointers, epilogue or linear; ESHAPE / EUNSUPPORTED for k. */
 int subspec_gemv(const subspec_linear *w, const uint16_t *x, const uint16_t *norm_w, float eps,

@@ -24,8 +24,12 @@ Storage (``codes`` uint8, one row of bytes per output row; ``meta`` float16
   * 4 bits: [N][K/2], byte j = q[2j] | q[2j+1] << 4;
   * 2 bits: [N][K/4], byte j = q[4j] | q[4j+1] << 2 | q[4j+2] << 4 | q[4j+3] << 6;
   * 3 bits: [N][3K/8], two planes per row: the low two bits of every code in
-    the 2-bit layout (K/4 bytes), then the third bit of every code, byte j =
-    sum_t bit2(q[8j+t]) << t (K/8 bytes).
+    the 2-bit layout (K/4 bytes), then the third bit of every code (K/8
+    bytes) in 4-byte words of 32 weights whose bytes hold weights 0-7, 16-23,
+    8-15 and 24-31 of the word (bit t of a byte: its t-th weight).  With that
+    byte order, bits e and e + 16 of a word belong to the same pair of
+    weights as the 2-bit fields e and e + 8 of a 16-weight word, so a decoder
+    pairs both planes with the same activations.
 
 The round-trip bound |x - w_hat| <= s/2 that the substitutes must meet
 holds for every group of bf16 values inside the fp16 range: L s covers the
@@ -46,6 +50,7 @@ import numpy as np
 GROUP = 64
 FP16_MAX = np.float32(65504.0)
 BITS = (2, 3, 4)
+HI_BYTE_BLOCK = (0, 16, 8, 24)  # 3-bit third-bit plane: first weight of each byte of a 32-weight word
 
 
 def _to_fp16_saturating(v):
@@ -105,8 +110,11 @@ def pack_codes(q, bits):
     lo2 = _pack2(q & 3)
     b = (q >> 2) & 1
     hi = np.zeros((q.shape[0], q.shape[1] // 8), dtype=np.uint8)
-    for t in range(8):
-        hi |= (b[:, t::8] << t).astype(np.uint8)
+    for j in range(q.shape[1] // 8):
+        w, byte = divmod(j, 4)
+        first = 32 * w + HI_BYTE_BLOCK[byte]
+        for t in range(8):
+            hi[:, j] |= (b[:, first + t] << t).astype(np.uint8)
     return np.concatenate([lo2, hi], axis=1)
 
 
@@ -127,8 +135,11 @@ def unpack_codes(codes, bits=4, k=None):
         q[:, t::4] = (lo2 >> (2 * t)) & 3
     if bits == 3:
         hi = codes[:, k // 4:k // 4 + k // 8]
-        for t in range(8):
-            q[:, t::8] |= ((hi >> t) & 1) << 2
+        for j in range(k // 8):
+            w, byte = divmod(j, 4)
+            first = 32 * w + HI_BYTE_BLOCK[byte]
+            for t in range(8):
+                q[:, first + t] |= ((hi[:, j] >> t) & 1) << 2
     return q
 
 

@@ -32,7 +32,7 @@ class SubspecError(RuntimeError):
 
 class Linear(ctypes.Structure):
     _fields_ = [("w", c_void_p), ("codes", c_void_p), ("meta", c_void_p),
-                ("n", c_int64), ("k", c_int64)]
+                ("n", c_int64), ("k", c_int64), ("bits", c_int32)]
 
 
 class Layer(ctypes.Structure):
@@ -165,6 +165,11 @@ def workspace_init(ws, stream=None):
     check(lib().subspec_workspace_init(_p(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def code_row_bytes(k, bits):
+    """Bytes of one row of codes at ``bits`` (layout of subspec_quantize)."""
+    return {4: k // 2, 2: k // 4, 3: 3 * k // 8}[bits]
+
+
 def quantize(w, codes, meta, group=64, bits=4, stream=None):
     n, k = w.shape
     check(lib().subspec_quantize(_p(w), n, k, group, bits, _p(codes), _p(meta), _stream(stream)))
@@ -233,14 +238,15 @@ def hbm_read(buf, sink, stream=None):
     check(lib().subspec_hbm_read(_p(buf), buf.numel() * buf.element_size(), _p(sink), _stream(stream)))
 
 
-def linear(w=None, codes=None, meta=None, n=None, k=None):
-    """A subspec_linear for bf16 weights w [n][k] or W4 codes [n][k/2] + meta."""
+def linear(w=None, codes=None, meta=None, n=None, k=None, bits=4):
+    """A subspec_linear for bf16 weights w [n][k], or low-bit codes + meta
+    [n][k/64][2] at ``bits`` = 4, 3 or 2 (k from meta when not given)."""
     if w is not None:
         n, k = w.shape
-        return Linear(_p(w), None, None, n, k)
+        return Linear(_p(w), None, None, n, k, 0)
     n = codes.shape[0] if n is None else n
-    k = 2 * codes.shape[1] if k is None else k
-    return Linear(None, _p(codes), _p(meta), n, k)
+    k = 64 * meta.shape[1] if k is None else k
+    return Linear(None, _p(codes), _p(meta), n, k, bits)
 
 
 GEMV_STORE, GEMV_RESID, GEMV_SILU = 0, 1, 2

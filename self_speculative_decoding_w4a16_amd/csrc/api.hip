@@ -82,7 +82,13 @@ int compute_units() {
 
 // ------------------------------------------------------------------ validation
 bool lin_is_bf16(const subspec_linear& l) { return l.w && !l.codes && !l.meta; }
-bool lin_is_w4(const subspec_linear& l) { return !l.w && l.codes && l.meta; }
+bool lin_is_w4(const subspec_linear& l) {  // any low-bit form (4, 3 or 2 bits)
+  return !l.w && l.codes && l.meta && (l.bits == 0 || l.bits == 2 || l.bits == 3 || l.bits == 4);
+}
+// weight width the GEMV kernels take: 16 (bf16), 4, 3 or 2
+int lin_bits(const subspec_linear& l) { return lin_is_w4(l) ? (l.bits == 0 ? 4 : l.bits) : 16; }
+// bytes of one row of codes
+double code_row_bytes(int bits, double k) { return bits == 4 ? k / 2 : (bits == 2 ? k / 4 : 3 * k / 8); }
 
 int check_linear(const subspec_linear& l, int64_t n, int64_t k, bool allow_w4, const char* what,
                  int layer) {
@@ -90,9 +96,13 @@ int check_linear(const subspec_linear& l, int64_t n, int64_t k, bool allow_w4, c
     return fail(SUBSPEC_ESHAPE, "layer %d %s: shape [%lld][%lld], expected [%lld][%lld]", layer,
                 what, (long long)l.n, (long long)l.k, (long long)n, (long long)k);
   if (lin_is_bf16(l)) return SUBSPEC_OK;
-  if (allow_w4 && lin_is_w4(l)) return SUBSPEC_OK;
+  if (allow_w4 && lin_is_w4(l)) {
+    if (lin_bits(l) == 3 && k % 128 != 0)
+      return fail(SUBSPEC_ESHAPE, "layer %d %s: 3-bit codes need k %% 128 == 0", layer, what);
+    return SUBSPEC_OK;
+  }
   return fail(SUBSPEC_EINVAL, "layer %d %s: set exactly one of w (bf16)%s", layer, what,
-              allow_w4 ? " or codes+meta (W4)" : "");
+              allow_w4 ? " or codes+meta with bits 4, 3 or 2" : "");
 }
 
 int check_model(const subspec_model* m) {
@@ -267,7 +277,7 @@ void set_linear(GemvArgs& a, const subspec_linear& l) {
 // each counted once.
 double gemv_bytes(const subspec_linear& l, int64_t n_out, bool resid) {
   const double n = (double)l.n, k = (double)l.k;
-  const double wb = lin_is_w4(l) ? n * k / 2 + n * (k / 64) * 4 : 2 * n * k;
+  const double wb = lin_is_w4(l) ? n * code_row_bytes(lin_bits(l), k) + n * (k / 64) * 4 : 2 * n * k;
   return wb + 2 * k + 2 * (double)n_out * (resid ? 2 : 1);
 }
 double gemm_bytes(int64_t n_phys, int64_t k, int m, int64_t n_out, bool resid) {
@@ -333,11 +343,12 @@ int subspec_workspace_init(void* ws, size_t ws_bytes, void* stream) {
 int subspec_quantize(const uint16_t* w, int64_t n, int64_t k, int32_t group, int32_t bits,
                      uint8_t* codes, uint16_t* meta, void* stream) {
   if (!w || !codes || !meta) return fail(SUBSPEC_EINVAL, "w, codes and meta must be set");
-  if (bits != 4) return fail(SUBSPEC_EUNSUPPORTED, "only bits = 4 is built");
+  if (bits != 4 && bits != 3 && bits != 2) return fail(SUBSPEC_EUNSUPPORTED, "bits must be 4, 3 or 2");
   if (group != 64) return fail(SUBSPEC_EUNSUPPORTED, "only group = 64 is built");
   if (n < 1 || k < 1) return fail(SUBSPEC_EINVAL, "n and k must be positive");
   if (k % 64 != 0) return fail(SUBSPEC_ESHAPE, "k must be a multiple of 64");
-  HIPCHK(launch_w4_quantize(w, n, k, codes, meta, hs(stream)));
+  if (bits == 3 && k % 128 != 0) return fail(SUBSPEC_ESHAPE, "3-bit codes need k %% 128 == 0");
+  HIPCHK(launch_quantize(w, n, k, bits, codes, meta, hs(stream)));
   return ok();
 }
 
@@ -382,7 +393,7 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
     a.valid = w.valid;
     {
       prof::Scope ps(gemv_class(L.qkv_d, 0), gemv_bytes(L.qkv_d, qkv, false), s);
-      HIPCHK(launch_gemv(lin_is_w4(L.qkv_d), l == 0 ? PRO_EMBED_NORM : PRO_NORM, EPI_STORE, a, s, nullptr));
+      HIPCHK(launch_gemv(lin_bits(L.qkv_d), l == 0 ? PRO_EMBED_NORM : PRO_NORM, EPI_STORE, a, s, nullptr));
     }
 
     AttnArgs at{};
@@ -434,7 +445,7 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
     o.x = w.attn;
     {
       prof::Scope ps(gemv_class(L.o_d, 1), gemv_bytes(L.o_d, H, true), s);
-      HIPCHK(launch_gemv(lin_is_w4(L.o_d), PRO_X, EPI_RESID, o, s, nullptr));
+      HIPCHK(launch_gemv(lin_bits(L.o_d), PRO_X, EPI_RESID, o, s, nullptr));
     }
 
     GemvArgs g{};
@@ -448,7 +459,7 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
     g.valid = w.valid;
     {
       prof::Scope ps(gemv_class(L.gate_up_d, 2), gemv_bytes(L.gate_up_d, F, false), s);
-      HIPCHK(launch_gemv(lin_is_w4(L.gate_up_d), PRO_NORM, EPI_SILU, g, s, nullptr));
+      HIPCHK(launch_gemv(lin_bits(L.gate_up_d), PRO_NORM, EPI_SILU, g, s, nullptr));
     }
 
     GemvArgs dn{};
@@ -461,7 +472,7 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
     dn.valid = w.valid;
     {
       prof::Scope ps(gemv_class(L.down_d, 3), gemv_bytes(L.down_d, H, true), s);
-      HIPCHK(launch_gemv(lin_is_w4(L.down_d), PRO_X, EPI_RESID, dn, s, nullptr));
+      HIPCHK(launch_gemv(lin_bits(L.down_d), PRO_X, EPI_RESID, dn, s, nullptr));
     }
   }
   uint16_t* logits = st->draft_logits + (int64_t)step * m->vocab;
@@ -480,7 +491,7 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
   {
     const subspec_linear lml{m->lm_head, nullptr, nullptr, m->vocab, H};
     prof::Scope ps(SUBSPEC_K_LM_HEAD, gemv_bytes(lml, m->vocab, false), s);
-    HIPCHK(launch_gemv(false, PRO_NORM, EPI_LOGITS, lm, s, &lm_blocks));
+    HIPCHK(launch_gemv(16, PRO_NORM, EPI_LOGITS, lm, s, &lm_blocks));
   }
   SampleWs sw{w.logit_max, w.logit_arg, w.sample_sums, w.sample_counter};
   {
@@ -668,7 +679,7 @@ int subspec_w4_gemv(const uint8_t* codes, const uint16_t* meta, int64_t n, int64
   a.k = k;
   a.x = x;
   a.y = y;
-  HIPCHK(launch_gemv(true, PRO_X, EPI_STORE, a, hs(stream), nullptr));
+  HIPCHK(launch_gemv(4, PRO_X, EPI_STORE, a, hs(stream), nullptr));
   return ok();
 }
 
@@ -676,9 +687,10 @@ int subspec_gemv(const subspec_linear* w, const uint16_t* x, const uint16_t* nor
                  int32_t epilogue, const uint16_t* resid, uint16_t* y, void* stream) {
   if (!w || !x || !y) return fail(SUBSPEC_EINVAL, "w, x and y must be set");
   if (!lin_is_bf16(*w) && !lin_is_w4(*w))
-    return fail(SUBSPEC_EINVAL, "set exactly one of w (bf16) or codes+meta (W4)");
+    return fail(SUBSPEC_EINVAL, "set exactly one of w (bf16) or codes+meta with bits 4, 3 or 2");
   if (w->n < 1 || w->k < 1) return fail(SUBSPEC_EINVAL, "n and k must be positive");
   if (w->k % 64 != 0) return fail(SUBSPEC_ESHAPE, "k must be a multiple of 64");
+  if (lin_bits(*w) == 3 && w->k % 128 != 0) return fail(SUBSPEC_ESHAPE, "3-bit codes need k %% 128 == 0");
   if (w->k > kMaxGemvK) return fail(SUBSPEC_EUNSUPPORTED, "k above %d", kMaxGemvK);
   if (norm_w && w->k > kMaxNormK) return fail(SUBSPEC_EUNSUPPORTED, "k above %d with norm_w", kMaxNormK);
   if (epilogue < 0 || epilogue > 2) return fail(SUBSPEC_EINVAL, "epilogue must be 0, 1 or 2");
@@ -701,7 +713,7 @@ int subspec_gemv(const subspec_linear* w, const uint16_t* x, const uint16_t* nor
     return fail(SUBSPEC_EUNSUPPORTED, "epilogue 2 is fused with the norm prologue only");
   if (pro == PRO_NORM && epi == EPI_RESID)
     return fail(SUBSPEC_EUNSUPPORTED, "epilogue 1 is fused with the plain prologue only");
-  HIPCHK(launch_gemv(lin_is_w4(*w), pro, epi, a, hs(stream), nullptr));
+  HIPCHK(launch_gemv(lin_bits(*w), pro, epi, a, hs(stream), nullptr));
   return ok();
 }
 
@@ -717,7 +729,7 @@ int subspec_bf16_gemv(const uint16_t* w, int64_t n, int64_t k, const uint16_t* x
   a.k = k;
   a.x = x;
   a.y = y;
-  HIPCHK(launch_gemv(false, PRO_X, EPI_STORE, a, hs(stream), nullptr));
+  HIPCHK(launch_gemv(16, PRO_X, EPI_STORE, a, hs(stream), nullptr));
   return ok();
 }
 

@@ -20,6 +20,12 @@
 //        sum_k (q_k s + m) x_k = s * sum_k (128+q_k) x_k + (m - 128 s) * sum_k x_k
 //    so the scale and min are applied once per 32 weights; sum_k x_k comes
 //    from LDS.
+//  * 2- and 3-bit substitutes (the paper note's low-bit substitute layers)
+//    take the same path with 16-byte units of 64 weights (one group): two-bit
+//    fields become (128 + q) bf16 pairs with one and-or each, x pairs
+//    (x[e], x[e+8]) of every 16-weight word; a 3-bit code is the 2-bit plane
+//    plus 4 x a 1-bit plane, whose byte order makes its fields pair the same
+//    x, so sum q x = d_lo + 4 d_hi - 640 sum x.
 //  * Epilogues: store, residual add (bf16(resid + acc)), SiLU(gate)*up with
 //    gate row n and up row F+n in the same wave, and logits with a per-block
 //    (max, argmax) partial for the sampler.
@@ -47,6 +53,37 @@ __device__ __forceinline__ float w4_word_dot(uint32_t cw, u32x4 xq, float d, uin
   return d;
 }
 
+// 2-bit word: fields e and e+8 (bits 2e, 16+2e) of a 16-weight word, dotted
+// with x pairs (x[e], x[e+8]) held in two slots (e < 4, e >= 4).
+__device__ __forceinline__ float w2_word_dot(uint32_t cw, u32x4 xa, u32x4 xb, float d, uint32_t mask,
+                                             uint32_t magic) {
+  d = ss::dot2((cw & mask) | magic, xa.x, d);
+  d = ss::dot2(((cw >> 2) & mask) | magic, xa.y, d);
+  d = ss::dot2(((cw >> 4) & mask) | magic, xa.z, d);
+  d = ss::dot2(((cw >> 6) & mask) | magic, xa.w, d);
+  d = ss::dot2(((cw >> 8) & mask) | magic, xb.x, d);
+  d = ss::dot2(((cw >> 10) & mask) | magic, xb.y, d);
+  d = ss::dot2(((cw >> 12) & mask) | magic, xb.z, d);
+  d = ss::dot2(((cw >> 14) & mask) | magic, xb.w, d);
+  return d;
+}
+
+// 1-bit word (the third bit of 3-bit codes) of 32 weights: its bytes hold
+// weights 0-7, 16-23, 8-15, 24-31, so fields j and j+16 (j < 8) are weights
+// j and j+8 of the first 16-weight word and fields 8+j, 24+j those of the
+// second: the pairs of the 2-bit plane's slots xs[0..3].
+__device__ __forceinline__ float w1_word_dot(uint32_t hw, const u32x4* xs, float d, uint32_t mask,
+                                             uint32_t magic) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    d = ss::dot2(((hw >> (4 * j)) & mask) | magic, xs[j].x, d);
+    d = ss::dot2(((hw >> (4 * j + 1)) & mask) | magic, xs[j].y, d);
+    d = ss::dot2(((hw >> (4 * j + 2)) & mask) | magic, xs[j].z, d);
+    d = ss::dot2(((hw >> (4 * j + 3)) & mask) | magic, xs[j].w, d);
+  }
+  return d;
+}
+
 __device__ __forceinline__ float bf16_chunk_dot(u32x4 w, u32x4 xq, float d) {
   d = ss::dot2(w.x, xq.x, d);
   d = ss::dot2(w.y, xq.y, d);
@@ -55,13 +92,35 @@ __device__ __forceinline__ float bf16_chunk_dot(u32x4 w, u32x4 xq, float d) {
   return d;
 }
 
-// W4: x[32c + 8w .. 32c + 8w + 7] (word w of 32-value chunk c) lives in LDS
-// slot w4_slot(c, w): lanes of a wave reading the same word of consecutive
-// chunks hit consecutive 16-byte slots (no bank conflicts).
-__host__ __device__ __forceinline__ int w4_slot(int c, int w) {
-  return ((c >> 6) << 8) + (w << 6) + (c & 63);
+// Weight widths: WB = 16 (bf16), 4, 3 or 2 bits.  Quantised units are 16
+// bytes of codes: 32 weights at 4 bits, 64 (one group) at 2 and 3 bits.
+template <int WB>
+__host__ __device__ constexpr int unit_weights() {
+  return WB == 16 ? 8 : (WB == 4 ? 32 : 64);
 }
-__host__ __device__ __forceinline__ int w4_slots(int K) { return ((K / 32 + 63) / 64) * 256; }
+// 16-byte LDS slots of x per unit: 4 (4-bit: pairs (x[k], x[k+4]) of each
+// 8-weight word), 8 (2- and 3-bit: pairs (x[e], x[e+8]) of each 16-weight
+// word; the 3-bit third-bit plane reads the same slots).
+template <int WB>
+__host__ __device__ constexpr int slots_per_unit() {
+  return WB == 4 ? 4 : 8;
+}
+// Slot w of unit c: lanes of a wave reading the same slot of consecutive
+// units hit consecutive 16-byte slots (no bank conflicts).
+template <int WB>
+__host__ __device__ __forceinline__ int xslot(int c, int w) {
+  return ((c >> 6) * 64 * slots_per_unit<WB>()) + (w << 6) + (c & 63);
+}
+template <int WB>
+__host__ __device__ __forceinline__ int xslots(int K) {
+  return ((K / unit_weights<WB>() + 63) / 64) * 64 * slots_per_unit<WB>();
+}
+// Bytes of one row of codes (the 3-bit third-bit plane follows the 2-bit
+// plane of the row, at byte K/4).
+template <int WB>
+__host__ __device__ __forceinline__ int code_row_bytes(int K) {
+  return WB == 4 ? K / 2 : (WB == 2 ? K / 4 : 3 * K / 8);
+}
 
 // Physical rows of row group g (R rows; in SiLU mode R/2 gate rows + the
 // matching R/2 up rows).  Rows past the end are clamped to row 0 (always a
@@ -96,34 +155,40 @@ constexpr int kNonTemporal = 2;           // buffer load cache policy: nt (strea
 
 // One step: unit u of row r is the 16-byte chunk (base + lane + 64u) of the
 // row; for W4 also the fp16 {scale, min} of its 64-group.
-template <int R, int U, bool W4>
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <int R, int U, int WB>
 struct Step {
   u32x4 v[U][R];
   uint32_t m[U][R];
+  u32x2 h[U][R];  // 3-bit: the unit's 8 bytes of the third-bit plane
 };
 
-template <int R, int U, bool W4>
-__device__ __forceinline__ void load_step(Step<R, U, W4>& b, const Res (&wr)[R], const Res (&mr)[R], int base,
-                                          int lane) {
+template <int R, int U, int WB>
+__device__ __forceinline__ void load_step(Step<R, U, WB>& b, const Res (&wr)[R], const Res (&mr)[R], int base,
+                                          int lane, int hoff) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int i = base + lane + u * SS_WAVE;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       b.v[u][r] = __builtin_amdgcn_raw_buffer_load_b128(wr[r], 16 * i, 0, kNonTemporal);
-      if (W4) b.m[u][r] = __builtin_amdgcn_raw_buffer_load_b32(mr[r], 4 * (i >> 1), 0, 0);
+      if (WB != 16) b.m[u][r] = __builtin_amdgcn_raw_buffer_load_b32(mr[r], 4 * (WB == 4 ? i >> 1 : i), 0, 0);
+      if (WB == 3) b.h[u][r] = __builtin_amdgcn_raw_buffer_load_b64(wr[r], hoff + 8 * i, 0, kNonTemporal);
     }
   }
 }
 
-template <int R, bool W4>
+template <int R, int WB>
 __device__ __forceinline__ void row_res(const GemvArgs& a, const int64_t (&prow)[R], const bool (&live)[R], int K,
                                         Res (&wr)[R], Res (&mr)[R]) {
+  constexpr bool W4 = WB != 16;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if (W4) {
-      wr[r] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.codes) + prow[r] * (K / 2), 0,
-                                                live[r] ? K / 2 : 0, kBufferWord3);
+      const int rb = code_row_bytes<WB>(K);
+      wr[r] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.codes) + prow[r] * rb, 0,
+                                                live[r] ? rb : 0, kBufferWord3);
       mr[r] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.meta) + prow[r] * (K / 32), 0,
                                                 live[r] ? K / 16 : 0, kBufferWord3);
     } else {
@@ -147,7 +212,7 @@ struct Cursor {
   float rres[R];
 };
 
-template <int R, bool W4, int EPI>
+template <int R, int WB, int EPI>
 __device__ __forceinline__ void cursor_at(Cursor<R>& c, const GemvArgs& a, int64_t g, int64_t n_groups, int K) {
   c.g = g;
   c.base = 0;
@@ -156,7 +221,7 @@ __device__ __forceinline__ void cursor_at(Cursor<R>& c, const GemvArgs& a, int64
   // store nothing
 #pragma unroll
   for (int r = 0; r < R; ++r) c.rv[r] = c.rv[r] && g < n_groups;
-  row_res<R, W4>(a, c.prow, c.rv, K, c.wr, c.mr);
+  row_res<R, WB>(a, c.prow, c.rv, K, c.wr, c.mr);
 }
 
 // Residual inputs of the cursor's rows, loaded (through the vector memory
@@ -173,7 +238,7 @@ __device__ __forceinline__ void load_rres(Cursor<R>& c, Res rr) {
 
 // The step after c: the next unit block of the same group, else the first of
 // the wave's next group.
-template <int R, int U, bool W4, int EPI>
+template <int R, int U, int WB, int EPI>
 __device__ __forceinline__ Cursor<R> cursor_next(const Cursor<R>& c, const GemvArgs& a, Res rr,
                                                  int64_t wave_stride, int64_t n_groups, int K, int n_units) {
   Cursor<R> d;
@@ -187,7 +252,7 @@ __device__ __forceinline__ Cursor<R> cursor_next(const Cursor<R>& c, const GemvA
     d.wr[r] = c.wr[r];
     d.mr[r] = c.mr[r];
   }
-  if (d.base >= n_units) cursor_at<R, W4, EPI>(d, a, c.g + wave_stride, n_groups, K);
+  if (d.base >= n_units) cursor_at<R, WB, EPI>(d, a, c.g + wave_stride, n_groups, K);
   load_rres<R, EPI>(d, rr);
   return d;
 }
@@ -220,35 +285,65 @@ __device__ __forceinline__ float reduce_rows(const float (&acc)[R], int lane) {
 }
 
 // Stores item `it` (x[8it .. 8it+7], bf16) into LDS: as consecutive pairs
-// for bf16 weights; for W4 as the pairs (x0,x4),(x1,x5),(x2,x6),(x3,x7) in
-// slot w4_slot(it/4, it%4), plus the sum of the chunk's 32 values, reduced
-// over the four lanes that hold the chunk.  Every lane of the wave calls it.
-template <bool W4>
+// for bf16 weights; for 4-bit as the pairs (x0,x4),(x1,x5),(x2,x6),(x3,x7)
+// in slot xslot(it/4, it%4); for 2- and 3-bit as the pairs of the unit's
+// slots (the partner item's values from the neighbouring lane); plus the sum of the
+// unit's values, reduced over the lanes that hold the unit.  Every lane of
+// the wave calls it (the lane exchanges need all of them).
+template <int WB>
 __device__ __forceinline__ void put_x(u32x4* smem4, float* xsum, int it, bool ok, const uint16_t (&xb)[8]) {
-  if (W4) {
-    float xs = 0.0f;
+  if (WB == 16) {
+    if (ok)
+      smem4[it] = u32x4{ss::pack_bf(xb[0], xb[1]), ss::pack_bf(xb[2], xb[3]), ss::pack_bf(xb[4], xb[5]),
+                        ss::pack_bf(xb[6], xb[7])};
+    return;
+  }
+  float xs = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xs += ss::bf2f(xb[i]);
-    xs += __shfl_xor(xs, 1, SS_WAVE);
-    xs += __shfl_xor(xs, 2, SS_WAVE);
+  for (int i = 0; i < 8; ++i) xs += ss::bf2f(xb[i]);
+  xs += __shfl_xor(xs, 1, SS_WAVE);
+  xs += __shfl_xor(xs, 2, SS_WAVE);
+  if (WB == 4) {
     if (ok) {
-      smem4[w4_slot(it >> 2, it & 3)] = u32x4{ss::pack_bf(xb[0], xb[4]), ss::pack_bf(xb[1], xb[5]),
-                                             ss::pack_bf(xb[2], xb[6]), ss::pack_bf(xb[3], xb[7])};
+      smem4[xslot<4>(it >> 2, it & 3)] = u32x4{ss::pack_bf(xb[0], xb[4]), ss::pack_bf(xb[1], xb[5]),
+                                               ss::pack_bf(xb[2], xb[6]), ss::pack_bf(xb[3], xb[7])};
       if ((it & 3) == 0) xsum[it >> 2] = xs;
     }
-  } else if (ok) {
-    smem4[it] = u32x4{ss::pack_bf(xb[0], xb[1]), ss::pack_bf(xb[2], xb[3]), ss::pack_bf(xb[4], xb[5]),
-                      ss::pack_bf(xb[6], xb[7])};
+    return;
+  }
+  xs += __shfl_xor(xs, 4, SS_WAVE);
+  // 2-bit plane: item 2w holds x[16w .. +7], item 2w+1 x[16w+8 .. +15] of the
+  // unit; slot 2w takes pairs e = 0..3 (written by the even item), slot
+  // 2w+1 pairs e = 4..7 (the odd item)
+  const uint32_t w0 = ss::pack_bf(xb[0], xb[1]), w1 = ss::pack_bf(xb[2], xb[3]);
+  const uint32_t w2 = ss::pack_bf(xb[4], xb[5]), w3 = ss::pack_bf(xb[6], xb[7]);
+  uint16_t p[8];
+  {
+    const uint32_t q0 = __shfl_xor(w0, 1, SS_WAVE), q1 = __shfl_xor(w1, 1, SS_WAVE);
+    const uint32_t q2 = __shfl_xor(w2, 1, SS_WAVE), q3 = __shfl_xor(w3, 1, SS_WAVE);
+    p[0] = (uint16_t)q0; p[1] = (uint16_t)(q0 >> 16); p[2] = (uint16_t)q1; p[3] = (uint16_t)(q1 >> 16);
+    p[4] = (uint16_t)q2; p[5] = (uint16_t)(q2 >> 16); p[6] = (uint16_t)q3; p[7] = (uint16_t)(q3 >> 16);
+  }
+  const int c = it >> 3, a = it & 7;
+  if (ok) {
+    const bool odd = a & 1;
+    u32x4 v;
+    if (!odd) v = u32x4{ss::pack_bf(xb[0], p[0]), ss::pack_bf(xb[1], p[1]), ss::pack_bf(xb[2], p[2]),
+                        ss::pack_bf(xb[3], p[3])};
+    else v = u32x4{ss::pack_bf(p[4], xb[4]), ss::pack_bf(p[5], xb[5]), ss::pack_bf(p[6], xb[6]),
+                   ss::pack_bf(p[7], xb[7])};
+    smem4[xslot<WB>(c, a)] = v;
+    if (a == 0) xsum[c] = xs;
   }
 }
 
 // Consumes one step: its dot products into the per-lane accumulators and, on
 // the group's last step, the row sums and the epilogue.
-template <int R, int U, bool W4, int EPI>
-__device__ __forceinline__ void consume(const GemvArgs& a, const Cursor<R>& c, const Step<R, U, W4>& cur,
+template <int R, int U, int WB, int EPI>
+__device__ __forceinline__ void consume(const GemvArgs& a, const Cursor<R>& c, const Step<R, U, WB>& cur,
                                         float (&acc)[R], ss::ArgMax& best, const u32x4* smem4,
                                         const float* xsum, int lane, int n_units, uint32_t mask,
-                                        uint32_t magic) {
+                                        uint32_t magic, uint32_t mask2, uint32_t mask1) {
   constexpr int RO = (EPI == EPI_SILU) ? R / 2 : R;
   // compute the current step
 #pragma unroll
@@ -258,10 +353,34 @@ __device__ __forceinline__ void consume(const GemvArgs& a, const Cursor<R>& c, c
     const int i0 = c.base + lane + u * SS_WAVE;
     const bool ok = i0 < n_units;
     const int i = ok ? i0 : 0;
-    if (W4) {
+    if (WB == 2 || WB == 3) {
       const float xs = xsum[i];
-      const u32x4 x0 = smem4[w4_slot(i, 0)], x1 = smem4[w4_slot(i, 1)];
-      const u32x4 x2 = smem4[w4_slot(i, 2)], x3 = smem4[w4_slot(i, 3)];
+      u32x4 xl[8];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) xl[w] = smem4[xslot<WB>(i, w)];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const u32x4 cw = cur.v[u][r];
+        float d0 = w2_word_dot(cw.x, xl[0], xl[1], 0.0f, mask2, magic);
+        float d1 = w2_word_dot(cw.y, xl[2], xl[3], 0.0f, mask2, magic);
+        d0 = w2_word_dot(cw.z, xl[4], xl[5], d0, mask2, magic);
+        d1 = w2_word_dot(cw.w, xl[6], xl[7], d1, mask2, magic);
+        const float sc = ss::h2f((uint16_t)(cur.m[u][r] & 0xffffu));
+        const float mn = ss::h2f((uint16_t)(cur.m[u][r] >> 16));
+        float t;
+        if (WB == 3) {
+          float e0 = w1_word_dot(cur.h[u][r].x, xl, 0.0f, mask1, magic);
+          float e1 = w1_word_dot(cur.h[u][r].y, xl + 4, 0.0f, mask1, magic);
+          t = sc * ((d0 + d1) + 4.0f * (e0 + e1)) + (mn - 640.0f * sc) * xs;
+        } else {
+          t = sc * (d0 + d1) + (mn - 128.0f * sc) * xs;
+        }
+        acc[r] += ok ? t : 0.0f;
+      }
+    } else if (WB == 4) {
+      const float xs = xsum[i];
+      const u32x4 x0 = smem4[xslot<4>(i, 0)], x1 = smem4[xslot<4>(i, 1)];
+      const u32x4 x2 = smem4[xslot<4>(i, 2)], x3 = smem4[xslot<4>(i, 3)];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const u32x4 cw = cur.v[u][r];
@@ -314,9 +433,10 @@ __device__ __forceinline__ void consume(const GemvArgs& a, const Cursor<R>& c, c
   }
 }
 
-template <int R, bool W4, int PRO, int EPI, int NT>
+template <int R, int WB, int PRO, int EPI, int NT>
 __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, uint32_t mask_arg,
-                                                        uint32_t magic_arg) {
+                                                        uint32_t magic_arg, uint32_t mask2_arg, uint32_t mask1_arg) {
+  constexpr bool W4 = WB != 16;  // quantised weights (4, 3 or 2 bits)
   extern __shared__ u32x4 smem4[];
   constexpr int kWaves = NT / SS_WAVE;
   __shared__ float red[kWaves];
@@ -330,10 +450,14 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
   const int tid = threadIdx.x, lane = tid & (SS_WAVE - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / SS_WAVE);  // wave-uniform: rows in SGPRs
   const int K = (int)a.k;
-  const int n_units = W4 ? K / 32 : K / 8;  // 16-byte chunks per row
+  const int n_units = K / unit_weights<WB>();  // 16-byte chunks of codes per row
   // 16-byte chunks per lane and row in one step: W4 chunks carry 4x the VALU
-  // work of bf16 chunks, so W4 steps are shorter (better overlap)
-  constexpr int U = W4 ? ((R >= 4) ? 1 : 2) : ((R >= 4) ? 2 : (R == 2 ? 4 : 8));
+  // work of bf16 chunks, so W4 steps are shorter (better overlap); 2/3-bit
+  // units hold a whole group (twice the weights of a 4-bit unit)
+  constexpr int U = WB == 16 ? ((R >= 4) ? 2 : (R == 2 ? 4 : 8)) : (WB == 4 ? ((R >= 4) ? 1 : 2) : 1);
+  const int hoff = K / 4;  // 3-bit: byte offset of the third-bit plane in a row
+  const uint32_t mask2 = __builtin_amdgcn_readfirstlane(mask2_arg);  // 0x00030003: 2-bit fields
+  const uint32_t mask1 = __builtin_amdgcn_readfirstlane(mask1_arg);  // 0x00010001: 1-bit fields
   const int64_t wave_stride = (int64_t)gridDim.x * kWaves;
   const uint32_t mask = __builtin_amdgcn_readfirstlane(mask_arg);
   uint32_t magic = magic_arg;
@@ -350,7 +474,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
   if (PRO == PRO_EMBED_NORM) src = a.embed + (int64_t)min(max(*a.token, 0), a.vocab - 1) * K;
   const u32x4* src4 = reinterpret_cast<const u32x4*>(src);
   const u32x4* g4 = reinterpret_cast<const u32x4*>(a.norm_w);
-  float* xsum = reinterpret_cast<float*>(smem4 + (W4 ? w4_slots(K) : K / 8));
+  float* xsum = reinterpret_cast<float*>(smem4 + (W4 ? xslots<WB>(K) : K / 8));
   // items: 8 consecutive values of x (one 16-byte quad); for W4 the four
   // items of a 32-value chunk sit in four consecutive lanes
   constexpr int NI = (3 * kThreads + NT - 1) / NT;  // items per thread held when normalising
@@ -379,10 +503,10 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
   const Res rr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(EPI == EPI_RESID ? a.resid : a.y), 0,
                                                     EPI == EPI_RESID ? (int)(2 * a.n) : 0, kBufferWord3);
   Cursor<R> ca, cb;
-  Step<R, U, W4> sa, sb;
-  cursor_at<R, W4, EPI>(ca, a, g0, n_groups, K);
+  Step<R, U, WB> sa, sb;
+  cursor_at<R, WB, EPI>(ca, a, g0, n_groups, K);
   load_rres<R, EPI>(ca, rr);
-  load_step<R, U, W4>(sa, ca.wr, ca.mr, 0, lane);
+  load_step<R, U, WB>(sa, ca.wr, ca.mr, 0, lane, hoff);
   if (PRO != PRO_X) {
     load_prologue();
   } else {
@@ -428,7 +552,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
         xb[2 * i] = ss::f2bf(ss::lo_bf(wv[i]) * inv * ss::lo_bf(gw[i]));
         xb[2 * i + 1] = ss::f2bf(ss::hi_bf(wv[i]) * inv * ss::hi_bf(gw[i]));
       }
-      put_x<W4>(smem4, xsum, it, ok, xb);
+      put_x<WB>(smem4, xsum, it, ok, xb);
     }
   } else {
     // the first XB items per thread are the ones loaded up front (all of x up
@@ -449,7 +573,7 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
           xb[2 * i] = (uint16_t)(wv[i] & 0xffffu);
           xb[2 * i + 1] = (uint16_t)(wv[i] >> 16);
         }
-        put_x<W4>(smem4, xsum, it, it < n_items, xb);
+        put_x<WB>(smem4, xsum, it, it < n_items, xb);
       }
     }
   }
@@ -473,21 +597,21 @@ __global__ __launch_bounds__(NT) void gemv_kernel(GemvArgs a, int64_t n_groups, 
   // with t+2 (both < T)
   int64_t t = 0;
   while (t + 2 < T) {
-    cb = cursor_next<R, U, W4, EPI>(ca, a, rr, wave_stride, n_groups, K, n_units);
-    load_step<R, U, W4>(sb, cb.wr, cb.mr, cb.base, lane);
-    consume<R, U, W4, EPI>(a, ca, sa, acc, best, smem4, xsum, lane, n_units, mask, magic);
-    ca = cursor_next<R, U, W4, EPI>(cb, a, rr, wave_stride, n_groups, K, n_units);
-    load_step<R, U, W4>(sa, ca.wr, ca.mr, ca.base, lane);
-    consume<R, U, W4, EPI>(a, cb, sb, acc, best, smem4, xsum, lane, n_units, mask, magic);
+    cb = cursor_next<R, U, WB, EPI>(ca, a, rr, wave_stride, n_groups, K, n_units);
+    load_step<R, U, WB>(sb, cb.wr, cb.mr, cb.base, lane, hoff);
+    consume<R, U, WB, EPI>(a, ca, sa, acc, best, smem4, xsum, lane, n_units, mask, magic, mask2, mask1);
+    ca = cursor_next<R, U, WB, EPI>(cb, a, rr, wave_stride, n_groups, K, n_units);
+    load_step<R, U, WB>(sa, ca.wr, ca.mr, ca.base, lane, hoff);
+    consume<R, U, WB, EPI>(a, cb, sb, acc, best, smem4, xsum, lane, n_units, mask, magic, mask2, mask1);
     t += 2;
   }
   if (t + 2 == T) {  // steps T-2 (in A) and T-1
-    cb = cursor_next<R, U, W4, EPI>(ca, a, rr, wave_stride, n_groups, K, n_units);
-    load_step<R, U, W4>(sb, cb.wr, cb.mr, cb.base, lane);
-    consume<R, U, W4, EPI>(a, ca, sa, acc, best, smem4, xsum, lane, n_units, mask, magic);
-    consume<R, U, W4, EPI>(a, cb, sb, acc, best, smem4, xsum, lane, n_units, mask, magic);
+    cb = cursor_next<R, U, WB, EPI>(ca, a, rr, wave_stride, n_groups, K, n_units);
+    load_step<R, U, WB>(sb, cb.wr, cb.mr, cb.base, lane, hoff);
+    consume<R, U, WB, EPI>(a, ca, sa, acc, best, smem4, xsum, lane, n_units, mask, magic, mask2, mask1);
+    consume<R, U, WB, EPI>(a, cb, sb, acc, best, smem4, xsum, lane, n_units, mask, magic, mask2, mask1);
   } else if (t + 1 == T) {  // step T-1 (in A)
-    consume<R, U, W4, EPI>(a, ca, sa, acc, best, smem4, xsum, lane, n_units, mask, magic);
+    consume<R, U, WB, EPI>(a, ca, sa, acc, best, smem4, xsum, lane, n_units, mask, magic, mask2, mask1);
   }
   if (EPI == EPI_LOGITS) {
     best = ss::wave_argmax(best);
@@ -552,17 +676,19 @@ int64_t gemv_blocks(int64_t n_groups, bool w4, int fit, int threads, int site_pe
   return need < cap ? need : cap;
 }
 
-size_t gemv_lds(bool w4, int64_t k) {
-  return w4 ? (size_t)w4_slots((int)k) * 16 + (size_t)(k / 32) * 4 : (size_t)k * 2;
+template <int WB>
+size_t gemv_lds(int64_t k) {
+  return WB != 16 ? (size_t)xslots<WB>((int)k) * 16 + (size_t)(k / unit_weights<WB>()) * 4 : (size_t)k * 2;
 }
 
-template <int R, bool W4, int PRO, int EPI, int NT>
+template <int R, int WB, int PRO, int EPI, int NT>
 hipError_t launch_nt(const GemvArgs& a, hipStream_t s, int* blocks_out) {
+  constexpr bool W4 = WB != 16;
   constexpr int RO = (EPI == EPI_SILU) ? R / 2 : R;
   static Occupancy occ;
   const int64_t n_groups = (a.n + RO - 1) / RO;
-  const size_t lds = gemv_lds(W4, a.k);
-  const int fit = occ.get(reinterpret_cast<const void*>(&gemv_kernel<R, W4, PRO, EPI, NT>), NT, lds);
+  const size_t lds = gemv_lds<WB>(a.k);
+  const int fit = occ.get(reinterpret_cast<const void*>(&gemv_kernel<R, WB, PRO, EPI, NT>), NT, lds);
   // the narrow QKV and O projections (n <= 8192) of bf16 layers, and the W4
   // QKV projection, run faster with two blocks per compute unit than with
   // the default 8 (bf16) or 4 (W4): at the 7B shape bf16 QKV 8.2 against
@@ -571,8 +697,8 @@ hipError_t launch_nt(const GemvArgs& a, hipStream_t s, int* blocks_out) {
   const bool narrow = (EPI == EPI_STORE || EPI == EPI_RESID) && a.n <= 8192 && (!W4 || EPI == EPI_STORE);
   const int64_t blocks = gemv_blocks(n_groups, W4, fit, NT, narrow ? 2 : 0);
   if (blocks_out) *blocks_out = (int)blocks;
-  SS_LAUNCH((gemv_kernel<R, W4, PRO, EPI, NT>), dim3((unsigned)blocks), dim3(NT), lds, s, a, n_groups,
-            0x000F000Fu, 0x43004300u);
+  SS_LAUNCH((gemv_kernel<R, WB, PRO, EPI, NT>), dim3((unsigned)blocks), dim3(NT), lds, s, a, n_groups,
+            0x000F000Fu, 0x43004300u, 0x00030003u, 0x00010001u);
   return hipGetLastError();
 }
 
@@ -580,34 +706,36 @@ hipError_t launch_nt(const GemvArgs& a, hipStream_t s, int* blocks_out) {
 // unit: x is staged in LDS once per 16 waves instead of once per 4.
 constexpr int64_t kLongK = 8192;
 
-template <int R, bool W4, int PRO, int EPI>
+template <int R, int WB, int PRO, int EPI>
 hipError_t launch_one(const GemvArgs& a, hipStream_t s, int* blocks_out) {
   if constexpr (PRO == PRO_X && EPI != EPI_LOGITS) {
-    if (a.k > kLongK) return launch_nt<R, W4, PRO, EPI, 1024>(a, s, blocks_out);
+    if (a.k > kLongK) return launch_nt<R, WB, PRO, EPI, 1024>(a, s, blocks_out);
   }
-  return launch_nt<R, W4, PRO, EPI, kThreads>(a, s, blocks_out);
+  return launch_nt<R, WB, PRO, EPI, kThreads>(a, s, blocks_out);
 }
 
-template <bool W4, int PRO, int EPI>
+template <int WB, int PRO, int EPI>
 hipError_t launch_r(int R, const GemvArgs& a, hipStream_t s, int* b) {
   if constexpr (EPI == EPI_SILU) {
     (void)R;  // always one gate and one up row per wave
-    return launch_one<2, W4, PRO, EPI>(a, s, b);
+    return launch_one<2, WB, PRO, EPI>(a, s, b);
   } else {
-    if (R >= 4) return launch_one<4, W4, PRO, EPI>(a, s, b);
-    if (R == 2) return launch_one<2, W4, PRO, EPI>(a, s, b);
-    return launch_one<1, W4, PRO, EPI>(a, s, b);
+    if (R >= 4) return launch_one<4, WB, PRO, EPI>(a, s, b);
+    if (R == 2) return launch_one<2, WB, PRO, EPI>(a, s, b);
+    return launch_one<1, WB, PRO, EPI>(a, s, b);
   }
 }
 
-template <bool W4>
+template <int WB>
 hipError_t launch_w(int R, int pro, int epi, const GemvArgs& a, hipStream_t s, int* b) {
-  if (pro == PRO_X && epi == EPI_STORE) return launch_r<W4, PRO_X, EPI_STORE>(R, a, s, b);
-  if (pro == PRO_X && epi == EPI_RESID) return launch_r<W4, PRO_X, EPI_RESID>(R, a, s, b);
-  if (pro == PRO_NORM && epi == EPI_STORE) return launch_r<W4, PRO_NORM, EPI_STORE>(R, a, s, b);
-  if (pro == PRO_EMBED_NORM && epi == EPI_STORE) return launch_r<W4, PRO_EMBED_NORM, EPI_STORE>(R, a, s, b);
-  if (pro == PRO_NORM && epi == EPI_SILU) return launch_r<W4, PRO_NORM, EPI_SILU>(R, a, s, b);
-  if (pro == PRO_NORM && epi == EPI_LOGITS) return launch_r<W4, PRO_NORM, EPI_LOGITS>(R, a, s, b);
+  if (pro == PRO_X && epi == EPI_STORE) return launch_r<WB, PRO_X, EPI_STORE>(R, a, s, b);
+  if (pro == PRO_X && epi == EPI_RESID) return launch_r<WB, PRO_X, EPI_RESID>(R, a, s, b);
+  if (pro == PRO_NORM && epi == EPI_STORE) return launch_r<WB, PRO_NORM, EPI_STORE>(R, a, s, b);
+  if (pro == PRO_EMBED_NORM && epi == EPI_STORE) return launch_r<WB, PRO_EMBED_NORM, EPI_STORE>(R, a, s, b);
+  if (pro == PRO_NORM && epi == EPI_SILU) return launch_r<WB, PRO_NORM, EPI_SILU>(R, a, s, b);
+  if constexpr (WB == 16 || WB == 4) {
+    if (pro == PRO_NORM && epi == EPI_LOGITS) return launch_r<WB, PRO_NORM, EPI_LOGITS>(R, a, s, b);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -632,7 +760,13 @@ int gemv_max_blocks(bool w4, int64_t n, int epi) {
   return (int)gemv_blocks((n + RO - 1) / RO, w4, 0, kThreads);
 }
 
-hipError_t launch_gemv(bool w4, int pro, int epi, const GemvArgs& a, hipStream_t s, int* blocks_out) {
+hipError_t launch_gemv(int wb, int pro, int epi, const GemvArgs& a, hipStream_t s, int* blocks_out) {
   const int R = pick_r(a.n, epi);
-  return w4 ? launch_w<true>(R, pro, epi, a, s, blocks_out) : launch_w<false>(R, pro, epi, a, s, blocks_out);
+  switch (wb) {
+    case 16: return launch_w<16>(R, pro, epi, a, s, blocks_out);
+    case 4: return launch_w<4>(R, pro, epi, a, s, blocks_out);
+    case 3: return launch_w<3>(R, pro, epi, a, s, blocks_out);
+    case 2: return launch_w<2>(R, pro, epi, a, s, blocks_out);
+  }
+  return hipErrorInvalidValue;
 }

@@ -34,7 +34,8 @@ struct GemvArgs {
 };
 
 int gemv_max_blocks(bool w4, int64_t n, int epi);  // blocks of one launch (logits partials)
-hipError_t launch_gemv(bool w4, int pro, int epi, const GemvArgs& a, hipStream_t s, int* blocks_out);
+// wb: weight width, 16 (bf16 w), 4, 3 or 2 (codes + meta; see subspec_quantize)
+hipError_t launch_gemv(int wb, int pro, int epi, const GemvArgs& a, hipStream_t s, int* blocks_out);
 
 // ------------------------------------------------------------------ GEMM (verify)
 // GEPI_PARTIAL: fp32 partial sums [split][m][n] for the caller to reduce
@@ -61,8 +62,8 @@ hipError_t launch_gemm_reduce(const float* part, int splits, int m, int64_t n, u
                               hipStream_t s);
 
 // ------------------------------------------------------------------ quantise
-hipError_t launch_w4_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
-                              uint16_t* meta, hipStream_t s);
+hipError_t launch_quantize(const uint16_t* w, int64_t n, int64_t k, int bits, uint8_t* codes,
+                           uint16_t* meta, hipStream_t s);
 
 // ------------------------------------------------------------------ attention
 struct AttnArgs {

@@ -1,8 +1,9 @@
-"""Device-resident model: bf16 target weights, 4-bit substitute copies built
-with the library's quantiser, and the C structs that describe them.
+"""Device-resident model: bf16 target weights, low-bit substitute copies
+(4 bits by default, or 3 / 2 bits per layer) built with the library's
+quantiser, and the C structs that describe them.
 
 The draft is the target itself with the layers [n_shared, n_layers) replaced
-by their 4-bit substitutes and the layers [0, n_shared) shared bit for bit
+by their substitutes and the layers [0, n_shared) shared bit for bit
 ("SubSpec: Speculate Deep and Accurate" paper note, Method details).  Torch
 only allocates device memory here; the quantisation runs in the HIP kernel.
 """
@@ -16,35 +17,38 @@ MATS = ("qkv", "o", "gate_up", "down")
 
 
 class DeviceModel:
-    def __init__(self, shape, weights, substitute_layers=None, stream=None):
+    def __init__(self, shape, weights, substitute_layers=None, stream=None, bits=4):
         """``weights``: dict from synth.model_weights (bf16 tensors on the GPU).
         ``substitute_layers``: indices quantised for the draft (default: all
-        layers from ``shape.n_shared`` on)."""
+        layers from ``shape.n_shared`` on).  ``bits``: code width of the
+        substitutes, 4, 3 or 2 (an int, or a dict layer -> width)."""
         self.shape = shape
         self.w = weights
         L = len(weights["layers"])
         if substitute_layers is None:
             substitute_layers = range(shape.n_shared, L)
         self.substitute_layers = sorted(set(substitute_layers))
+        self.bits = {l: (bits[l] if isinstance(bits, dict) else bits) for l in self.substitute_layers}
         self.q = [None] * L
         for l in self.substitute_layers:
             self.q[l] = {}
+            b = self.bits[l]
             for name in MATS:
                 wt = weights["layers"][l][name]
                 n, k = wt.shape
-                codes = torch.empty((n, k // 2), dtype=torch.uint8, device=wt.device)
+                codes = torch.empty((n, _lib.code_row_bytes(k, b)), dtype=torch.uint8, device=wt.device)
                 meta = torch.empty((n, k // 64, 2), dtype=torch.float16, device=wt.device)
-                _lib.quantize(wt, codes, meta, stream=stream)
+                _lib.quantize(wt, codes, meta, bits=b, stream=stream)
                 self.q[l][name] = (codes, meta)
         self._build_structs()
 
     def _lin_bf16(self, t):
         n, k = t.shape
-        return _lib.Linear(t.data_ptr(), None, None, n, k)
+        return _lib.Linear(t.data_ptr(), None, None, n, k, 0)
 
-    def _lin_w4(self, codes, meta):
-        n, kh = codes.shape
-        return _lib.Linear(None, codes.data_ptr(), meta.data_ptr(), n, 2 * kh)
+    def _lin_w4(self, codes, meta, bits):
+        n = codes.shape[0]
+        return _lib.Linear(None, codes.data_ptr(), meta.data_ptr(), n, 64 * meta.shape[1], bits)
 
     def _build_structs(self):
         s = self.shape
@@ -57,7 +61,7 @@ class DeviceModel:
             for name in MATS:
                 setattr(st, name, self._lin_bf16(lw[name]))
                 if self.q[l] is not None:
-                    setattr(st, name + "_d", self._lin_w4(*self.q[l][name]))
+                    setattr(st, name + "_d", self._lin_w4(*self.q[l][name], self.bits[l]))
                 else:
                     setattr(st, name + "_d", self._lin_bf16(lw[name]))
         self.c = _lib.Model(L, s.hidden, s.ffn, s.n_q_heads, s.n_kv_heads, s.head_dim, s.vocab,

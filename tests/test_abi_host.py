@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared():
         assert hasattr(l, name), name
     assert set(_declared()) == set(_lib.EXPORTS)
-    assert _lib.abi_version() == 1
+    assert _lib.abi_version() == 2  # subspec_linear carries the code width
 
 
 V = ctypes.c_void_p
@@ -41,8 +41,11 @@ def test_quantize_argument_errors():
     l = _lib.lib()
     p = V(4096)
     assert l.subspec_quantize(None, 4, 64, 64, 4, p, p, None) == _lib.EINVAL
-    assert l.subspec_quantize(p, 4, 64, 64, 3, p, p, None) == _lib.EUNSUPPORTED
+    assert l.subspec_quantize(p, 4, 64, 64, 5, p, p, None) == _lib.EUNSUPPORTED
     assert "bits" in _lib.last_error()
+    assert l.subspec_quantize(p, 4, 64, 64, 1, p, p, None) == _lib.EUNSUPPORTED
+    assert l.subspec_quantize(p, 4, 64, 64, 3, p, p, None) == _lib.ESHAPE  # 3 bits: k % 128
+    assert "128" in _lib.last_error()
     assert l.subspec_quantize(p, 4, 64, 32, 4, p, p, None) == _lib.EUNSUPPORTED
     assert l.subspec_quantize(p, 4, 96, 64, 4, p, p, None) == _lib.ESHAPE
     assert l.subspec_quantize(p, 0, 64, 64, 4, p, p, None) == _lib.EINVAL
@@ -80,6 +83,8 @@ def test_fused_gemv_argument_errors():
     bf = _lib.Linear(p, None, None, 8, 128)
     both = _lib.Linear(p, p, p, 8, 128)
     odd = _lib.Linear(p, None, None, 7, 128)
+    bad_bits = _lib.Linear(None, p, p, 8, 128, 5)
+    three_64 = _lib.Linear(None, p, p, 8, 64, 3)
     wide = _lib.Linear(p, None, None, 8, 8192)
     g = lambda lin, *a: l.subspec_gemv(ctypes.byref(lin), *a)
     assert g(both, p, None, 0.0, 0, None, p, None) == _lib.EINVAL
@@ -91,6 +96,8 @@ def test_fused_gemv_argument_errors():
     assert g(bf, p, None, 0.0, 2, None, p, None) == _lib.EUNSUPPORTED  # SiLU needs the norm
     assert g(bf, None, p, 1e-6, 0, None, p, None) == _lib.EINVAL
     assert l.subspec_gemv(None, p, p, 1e-6, 0, None, p, None) == _lib.EINVAL
+    assert g(bad_bits, p, None, 0.0, 0, None, p, None) == _lib.EINVAL   # width 5
+    assert g(three_64, p, None, 0.0, 0, None, p, None) == _lib.ESHAPE   # 3 bits: k % 128
 
 
 def test_reject_argument_errors():
