@@ -23,6 +23,7 @@ from .model import forward, new_kv
 from .reject import reject
 from .sampling import sample
 from .sparse import build_index
+from .adaptive import Controller, entropy
 
 
 def prefill(model, kv, prompt):
@@ -98,3 +99,50 @@ def autoregressive_generate(model, prompt, n_generate, temp, U, capacity):
         out.append(last)
         kv_len += 1
     return out
+
+
+def adaptive_speculative_cycle(model, kv, kv_len, last_token, ctl, temp, draft_temp, U_draft, R, U_final,
+                               entropies=None):
+    """One cycle with the entropy-adaptive draft length ([SSL] section 3.3,
+    oracle/adaptive.py): tokens are drafted one at a time until the
+    controller stops (gamma_eff <= gamma_max), the gamma_eff + 1 positions are
+    verified and judged, and the controller's centres are updated with the
+    outcome.  ``entropies``: the entropies to feed the controller instead of
+    the oracle's own (teacher forcing on another evaluation's values)."""
+    toks = [int(last_token)]
+    dlogits = []
+    for i in range(ctl.gamma_max):
+        z = forward(model, kv, kv_len + i, [toks[i]], draft=True)[0]
+        dlogits.append(z)
+        toks.append(sample(z.astype(np.float32), draft_temp, U_draft[i]))
+        h = entropy(z) if entropies is None else float(entropies[i])
+        if not ctl.after_token(h):
+            break
+    g = ctl.gamma_eff
+    tlogits = forward(model, kv, kv_len, toks[:g + 1], draft=False)
+    n, out, status = reject(tlogits, np.array(dlogits[:g]), toks[1:g + 1], R[:g], U_final, temp, draft_temp)
+    ctl.after_round(n)
+    return n, out, status, toks[:g + 1], np.array(dlogits[:g]), tlogits, g
+
+
+def adaptive_generate(model, prompt, n_generate, gamma_max, c, temp, draft_temp, uniforms, capacity,
+                      beta=None):
+    """Speculative decoding with the entropy-adaptive draft length; returns
+    (tokens[:n_generate], per-cycle n, per-cycle gamma_eff)."""
+    U_draft, R, U_final = uniforms
+    ctl = Controller(gamma_max, c) if beta is None else Controller(gamma_max, c, beta)
+    kv = new_kv(model, capacity)
+    kv_len = prefill(model, kv, prompt)
+    committed = list(prompt)
+    out, ns, gs = [], [], []
+    c_i = 0
+    while len(out) < n_generate:
+        n, emitted, _, _, _, _, g = adaptive_speculative_cycle(
+            model, kv, kv_len, committed[-1], ctl, temp, draft_temp, U_draft[c_i], R[c_i], U_final[c_i])
+        kv_len += n + 1
+        committed += emitted
+        out += emitted
+        ns.append(n)
+        gs.append(g)
+        c_i += 1
+    return out[:n_generate], ns, gs
