@@ -42,7 +42,10 @@ constexpr int KC = 128;             // k per chunk
 constexpr int KS = KC / 32;         // MFMA steps (k = 32 each) per chunk
 constexpr int WD = 2;               // weight chunks in flight per wave
 constexpr int XROW = KC + 8;        // LDS row stride (bf16) of the staged activations
-constexpr int kTargetBlocks = 512;  // split k until the grid has two blocks per compute unit
+// split k until the grid has about 1.5 blocks per compute unit: the 7B verify
+// pass (17 positions) measured 3.32 ms at 384 against 3.46 at 512, 3.50 at
+// 320, 3.33 at 448 and 3.56 at 256 (graph-replayed passes)
+constexpr int kTargetBlocks = 384;
 constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 (CDNA): raw 32-bit data
 constexpr int kOutside = 0x40000000;      // byte offset past every resource: loads zeros
 constexpr int kNonTemporal = 2;           // buffer load cache policy: nt (streamed weights)
