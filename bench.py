@@ -324,7 +324,7 @@ def main():
         log(f"plain bf16 autoregressive decode: {ar:.2f} tok/s")
 
     # ---------------------------------------------------------------- small workloads
-    tiny = layer = lowbit = None
+    tiny = layer = lowbit = None  # noqa: F841
     if args.config == "full7b" and not args.no_small:
         tiny = tiny_rates(dev)
         log(f"tiny workload: {json.dumps(tiny)}")
@@ -332,6 +332,10 @@ def main():
         log(f"one 7B layer: {json.dumps(layer)}")
         lowbit = lowbit_rates(dec, shape, w, wl, kv0, last, dev)
         log(f"3- and 2-bit substitutes: {json.dumps(lowbit)}")
+    adapt = None
+    if not sparse and not args.no_small and not stochastic:
+        adapt = adaptive_rates(dec, dm, wl, kv0, last, draft_pass["avg_us"] / verify_pass["avg_us"])
+        log(f"adaptive draft length: {json.dumps(adapt)}")
 
     # ---------------------------------------------------------------- CPU oracle
     cpu = None
@@ -385,6 +389,7 @@ def main():
         "tiny": tiny,
         "layer7b": layer,
         "lowbit": lowbit,
+        "adaptive_length": adapt,
         "kernels": kern,
     }
     # every rate also against the measured read ceiling
@@ -682,6 +687,52 @@ def lowbit_rates(dec, shape, w, wl, kv0, last, dev):
         del d, dm
         torch.cuda.empty_cache()
     return out
+
+
+def adaptive_rates(dec, dm, wl, kv0, last, c, steps=2):
+    """Greedy speculative decoding of the same workload with the entropy-
+    adaptive draft length (gamma as the longest draft; c = measured draft-step
+    over verify-pass time): tokens/s, tau and the mean draft length, cycles
+    replayed from recorded graphs as in the headline run."""
+    import time
+
+    import numpy as np
+    import torch
+
+    from self_speculative_decoding_w4a16_amd import _lib
+    from self_speculative_decoding_w4a16_amd.engine import SpecDecoder
+    G = wl.generate
+    d = SpecDecoder(dm, dec.capacity, wl.gamma, wl.temp, wl.draft_temp, graphs=True,
+                    adaptive=dict(c=c, beta=0.125))
+    d.k_cache.copy_(dec.k_cache)
+    d.v_cache.copy_(dec.v_cache)
+
+    def gen():
+        d.reset(kv0, last)
+        _lib.control_init(d.ctl)
+        out, ns, gs = [], [], []
+        while len(out) < G:
+            d.cycle()
+            n = int(d.n_accepted.item())
+            out += d.out_tokens[:n + 1].tolist()
+            ns.append(n)
+            gs.append(d.last_draft_len())
+        return out[:G], ns, gs
+    gen()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    all_ns, all_gs = [], []
+    for _ in range(steps):
+        _, ns, gs = gen()
+        all_ns += ns
+        all_gs += gs
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    del d
+    torch.cuda.empty_cache()
+    return {"tokens_s": round(steps * G / el, 3), "tau": round(float(np.mean([n + 1 for n in all_ns])), 4),
+            "mean_draft_len": round(float(np.mean(all_gs)), 3), "max_draft_len": wl.gamma, "c": round(c, 4),
+            "beta": 0.125}
 
 
 def tiny_rates(dev, reps=200):

@@ -161,6 +161,9 @@ typedef struct {
   int32_t index_cap;
   int32_t use_index;
   int32_t n_sink, n_recent, score_window, budget_permille;
+  const int32_t *draft_len; /* device int32 or NULL: with the entropy-adaptive
+                               draft length (subspec_control), draft steps
+                               with step >= *draft_len are skipped (token -1) */
 } subspec_state;
 
 /* Bytes of workspace needed for calls on `m` with at most `max_tokens`
@@ -262,6 +265,58 @@ int subspec_reject_noalloc(int32_t gamma, int32_t vocab, float temp, float draft
                            const int32_t *draft_tokens, const uint32_t *r_codes, const uint32_t *u_code,
                            int32_t *n_accepted, int32_t *out_tokens, int32_t *status, float *probs,
                            void *stream);
+
+/* The rejection round of a draft that may have stopped early: as
+ * subspec_reject, but only the first min(*gamma_len, gamma) draft tokens are
+ * judged (gamma_len: device int32, the round's draft length); if they are all
+ * accepted the bonus token is drawn from target row *gamma_len.  Used with
+ * the entropy-adaptive draft length ([SSL] section 3.3). */
+int subspec_reject_len(int32_t gamma, int32_t vocab, float temp, float draft_temp,
+                       const uint16_t *target_logits, const uint16_t *draft_logits,
+                       const int32_t *draft_tokens, const uint32_t *r_codes, const uint32_t *u_code,
+                       const int32_t *gamma_len, int32_t *n_accepted, int32_t *out_tokens, int32_t *status,
+                       float *probs, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Entropy-adaptive draft length  ([SSL] section 3.3)                        */
+/* ------------------------------------------------------------------------ */
+
+/* Controller state (device buffers owned by the caller).  Each draft token's
+ * entropy H_i (of softmax(logits) at temperature 1) is compared with two EMA
+ * centres - the mean entropy of accepted and of rejected draft tokens -
+ * giving p_i = d_rej / (d_acc + d_rej) (d: distance to a centre; 1/2 if both
+ * are 0; 1 while a centre is unseen); after token i the draft goes on only
+ * if some longer length k, with the undrafted tokens at p_i, has
+ * E(k) = (1 + sum_{m<=k} prod_{j<=m} p_j) / (k c + 1) > E(i).
+ *   draft_len  device int32: the round's draft length (gamma_max at its start)
+ *   state      device double [8]: h_acc, h_rej, seen_acc, seen_rej, running
+ *              product, running 1 + sum, last round's length, spare
+ *   entropy    device float [gamma_max]: entropies of the round's tokens
+ *   c          C_d / C_v, draft-step cost over verify-pass cost (> 0)
+ *   beta       EMA rate in (0, 1]
+ *   gamma_max  longest draft (>= 1)                                         */
+typedef struct {
+  int32_t *draft_len;
+  double *state;
+  float *entropy;
+  double c, beta;
+  int32_t gamma_max;
+} subspec_control;
+
+/* Zero the centres and start a round (a fill kernel; capture-safe). */
+int subspec_control_init(const subspec_control *ctl, void *stream);
+
+/* After draft step `step`: the entropy of draft_logits[step] and the
+ * controller's decision; lowers *draft_len to step + 1 when the draft should
+ * stop.  Does nothing for a step that was not drafted (step >= *draft_len).
+ * Needs st->draft_len == ctl->draft_len; workspace as for draft steps. */
+int subspec_draft_control(const subspec_model *m, const subspec_state *st, int32_t step,
+                          const subspec_control *ctl, void *ws, size_t ws_bytes, void *stream);
+
+/* After the rejection round (n = *n_accepted, device): tokens 1..n update the
+ * accepted centre in order, token n + 1 (if drafted) the rejected centre;
+ * records the round's length in state[6] and starts the next round. */
+int subspec_control_update(const subspec_control *ctl, const int32_t *n_accepted, void *stream);
 
 /* Commit a round ([SD] Module 2: discard the K/V of rejected positions):
  * kv_len += n + 1 and tokens[0] = out_tokens[n], n = *n_accepted (device). */

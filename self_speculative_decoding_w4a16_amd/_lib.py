@@ -56,7 +56,12 @@ class State(ctypes.Structure):
                 ("kv_score", c_void_p), ("kv_index", c_void_p), ("kv_index_len", c_void_p),
                 ("index_cap", c_int32), ("use_index", c_int32),
                 ("n_sink", c_int32), ("n_recent", c_int32), ("score_window", c_int32),
-                ("budget_permille", c_int32)]
+                ("budget_permille", c_int32), ("draft_len", c_void_p)]
+
+
+class Control(ctypes.Structure):
+    _fields_ = [("draft_len", c_void_p), ("state", c_void_p), ("entropy", c_void_p),
+                ("c", ctypes.c_double), ("beta", ctypes.c_double), ("gamma_max", c_int32)]
 
 
 _SIGS = {
@@ -73,6 +78,13 @@ _SIGS = {
     "subspec_reject": (c_int32, [c_int32, c_int32, c_float, c_float, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_size_t, c_void_p]),
+    "subspec_reject_len": (c_int32, [c_int32, c_int32, c_float, c_float, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_size_t, c_void_p]),
+    "subspec_control_init": (c_int32, [POINTER(Control), c_void_p]),
+    "subspec_draft_control": (c_int32, [POINTER(Model), POINTER(State), c_int32, POINTER(Control), c_void_p,
+                                        c_size_t, c_void_p]),
+    "subspec_control_update": (c_int32, [POINTER(Control), c_void_p, c_void_p]),
     "subspec_reject_noalloc": (c_int32, [c_int32, c_int32, c_float, c_float, c_void_p, c_void_p,
                                          c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                          c_void_p, c_void_p]),
@@ -192,6 +204,27 @@ def reject(gamma, vocab, temp, draft_temp, target_logits, draft_logits, draft_to
                                _p(draft_tokens), _p(r_codes), _p(u_code), _p(n_accepted),
                                _p(out_tokens), _p(status), _p(probs), _p(ws),
                                ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def reject_len(gamma, vocab, temp, draft_temp, target_logits, draft_logits, draft_tokens, r_codes,
+               u_code, gamma_len, n_accepted, out_tokens, status, probs, ws, stream=None):
+    check(lib().subspec_reject_len(gamma, vocab, temp, draft_temp, _p(target_logits), _p(draft_logits),
+                                   _p(draft_tokens), _p(r_codes), _p(u_code), _p(gamma_len), _p(n_accepted),
+                                   _p(out_tokens), _p(status), _p(probs), _p(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def control_init(ctl, stream=None):
+    check(lib().subspec_control_init(ctypes.byref(ctl), _stream(stream)))
+
+
+def draft_control(model, state, step, ctl, ws, stream=None):
+    check(lib().subspec_draft_control(ctypes.byref(model), ctypes.byref(state), step, ctypes.byref(ctl), _p(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def control_update(ctl, n_accepted, stream=None):
+    check(lib().subspec_control_update(ctypes.byref(ctl), _p(n_accepted), _stream(stream)))
 
 
 def reject_noalloc(gamma, vocab, temp, draft_temp, target_logits, draft_logits, draft_tokens, r_codes,

@@ -47,6 +47,7 @@ constexpr size_t kCounterBytes = 64 * 1024;
 constexpr size_t kSampleCounterOff = 16 * 1024;
 constexpr size_t kRejectCounterOff = 16 * 1024 + 256;
 constexpr size_t kAttnCounterOff = 20 * 1024;  // draft attention: one per query head (<= 224)
+constexpr size_t kControlCounterOff = 16 * 1024 + 512;  // draft-length controller
 constexpr int kMaxTokens = 64;
 constexpr int kMaxGemvK = 28672;  // x (2 B) + half-group sums in 64 KiB of LDS
 constexpr int kMaxGamma = 64;
@@ -329,6 +330,7 @@ size_t subspec_workspace_bytes(const subspec_model* m, int32_t max_tokens, int32
   }
   size_t b = carve_fwd(m, max_tokens, capacity, nullptr, nullptr);
   b = std::max(b, carve_reject(kMaxGamma, m->vocab, nullptr, nullptr));
+  b = std::max(b, kCounterBytes + (size_t)control_chunks(m->vocab) * 3 * sizeof(double));
   ok();
   return b;
 }
@@ -374,7 +376,7 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
   {
     prof::Scope ps(SUBSPEC_K_MISC, 0.0, s);
     HIPCHK(launch_pos_guard(st->kv_len, st->tokens + step, step, st->capacity, m->vocab, w.valid, tok_out,
-                            (int)d, m->rope_theta, w.rope_cs, s));
+                            (int)d, m->rope_theta, w.rope_cs, st->draft_len, s));
   }
   for (int l = 0; l < m->n_layers; ++l) {
     const subspec_layer& L = m->layers[l];
@@ -615,11 +617,11 @@ int subspec_verify(const subspec_model* m, const subspec_state* st, int32_t n_to
   return ok();
 }
 
-int subspec_reject(int32_t gamma, int32_t vocab, float temp, float draft_temp,
-                   const uint16_t* target_logits, const uint16_t* draft_logits,
-                   const int32_t* draft_tokens, const uint32_t* r_codes, const uint32_t* u_code,
-                   int32_t* n_accepted, int32_t* out_tokens, int32_t* status, float* probs,
-                   void* ws, size_t ws_bytes, void* stream) {
+int subspec_reject_len(int32_t gamma, int32_t vocab, float temp, float draft_temp,
+                       const uint16_t* target_logits, const uint16_t* draft_logits,
+                       const int32_t* draft_tokens, const uint32_t* r_codes, const uint32_t* u_code,
+                       const int32_t* gamma_len, int32_t* n_accepted, int32_t* out_tokens, int32_t* status,
+                       float* probs, void* ws, size_t ws_bytes, void* stream) {
   if (gamma < 0 || gamma > kMaxGamma) return fail(SUBSPEC_EINVAL, "gamma outside [0, %d]", kMaxGamma);
   if (vocab < 1 || vocab > (1 << 24)) return fail(SUBSPEC_EINVAL, "vocab outside [1, 2^24]");
   if (!(temp >= 0.0f) || !(draft_temp >= 0.0f)) return fail(SUBSPEC_EINVAL, "temperatures must be >= 0");
@@ -635,8 +637,17 @@ int subspec_reject(int32_t gamma, int32_t vocab, float temp, float draft_temp,
   carve_reject(gamma, vocab, ws, &rw);
   prof::Scope ps(SUBSPEC_K_REJECT, 2.0 * (2 * gamma + 1) * vocab, hs(stream));
   HIPCHK(launch_reject(gamma, vocab, temp, draft_temp, target_logits, draft_logits, draft_tokens,
-                       r_codes, u_code, n_accepted, out_tokens, status, probs, rw, hs(stream)));
+                       r_codes, u_code, n_accepted, out_tokens, status, probs, rw, hs(stream), gamma_len));
   return ok();
+}
+
+int subspec_reject(int32_t gamma, int32_t vocab, float temp, float draft_temp,
+                   const uint16_t* target_logits, const uint16_t* draft_logits,
+                   const int32_t* draft_tokens, const uint32_t* r_codes, const uint32_t* u_code,
+                   int32_t* n_accepted, int32_t* out_tokens, int32_t* status, float* probs,
+                   void* ws, size_t ws_bytes, void* stream) {
+  return subspec_reject_len(gamma, vocab, temp, draft_temp, target_logits, draft_logits, draft_tokens, r_codes,
+                            u_code, nullptr, n_accepted, out_tokens, status, probs, ws, ws_bytes, stream);
 }
 
 int subspec_kv_rollback(const subspec_state* st, const int32_t* n_accepted,
@@ -657,6 +668,56 @@ int subspec_kv_select(const subspec_model* m, const subspec_state* st, void* str
   HIPCHK(launch_kv_select(st->kv_score, st->capacity, st->kv_len, m->n_layers * m->n_kv_heads, st->n_sink,
                           st->n_recent, st->budget_permille, st->kv_index, st->index_cap, st->kv_index_len,
                           hs(stream)));
+  return ok();
+}
+
+static int control_args(const subspec_control* ctl, ControlArgs* o) {
+  if (!ctl || !ctl->draft_len || !ctl->state || !ctl->entropy)
+    return fail(SUBSPEC_EINVAL, "control: draft_len, state and entropy must be set");
+  if (ctl->gamma_max < 1 || ctl->gamma_max > kMaxGamma)
+    return fail(SUBSPEC_EINVAL, "control: gamma_max outside [1, %d]", kMaxGamma);
+  if (!(ctl->c > 0.0) || !(ctl->beta > 0.0 && ctl->beta <= 1.0))
+    return fail(SUBSPEC_EINVAL, "control: c must be > 0 and beta in (0, 1]");
+  *o = ControlArgs{ctl->draft_len, ctl->state, ctl->entropy, ctl->c, ctl->beta, ctl->gamma_max};
+  return SUBSPEC_OK;
+}
+
+int subspec_control_init(const subspec_control* ctl, void* stream) {
+  ControlArgs c;
+  int r;
+  if ((r = control_args(ctl, &c))) return r;
+  HIPCHK(launch_control_init(c, hs(stream)));
+  return ok();
+}
+
+int subspec_draft_control(const subspec_model* m, const subspec_state* st, int32_t step,
+                          const subspec_control* ctl, void* ws, size_t ws_bytes, void* stream) {
+  ControlArgs c;
+  int r;
+  if ((r = check_model(m)) || (r = check_state(m, st)) || (r = control_args(ctl, &c))) return r;
+  if (!st->draft_logits) return fail(SUBSPEC_EINVAL, "state.draft_logits must be set");
+  if (st->draft_len != ctl->draft_len)
+    return fail(SUBSPEC_EINVAL, "state.draft_len must be the controller's draft_len");
+  if (ctl->gamma_max > st->gamma_max) return fail(SUBSPEC_EINVAL, "control gamma_max above the state's");
+  if (step < 0 || step >= ctl->gamma_max)
+    return fail(SUBSPEC_EINVAL, "step %d outside [0, gamma_max = %d)", step, ctl->gamma_max);
+  const size_t part_bytes = (size_t)control_chunks(m->vocab) * 3 * sizeof(double);
+  if ((r = need_ws(ws, ws_bytes, kCounterBytes + part_bytes))) return r;
+  char* base = (char*)ws;
+  prof::Scope ps(SUBSPEC_K_SAMPLE, 2.0 * m->vocab, hs(stream));
+  HIPCHK(launch_draft_control(c, step, st->draft_logits + (int64_t)step * m->vocab, m->vocab,
+                              (double*)(base + kCounterBytes), (uint32_t*)(base + kControlCounterOff),
+                              hs(stream)));
+  return ok();
+}
+
+int subspec_control_update(const subspec_control* ctl, const int32_t* n_accepted, void* stream) {
+  ControlArgs c;
+  int r;
+  if ((r = control_args(ctl, &c))) return r;
+  if (!n_accepted) return fail(SUBSPEC_EINVAL, "n_accepted must be set");
+  prof::Scope ps(SUBSPEC_K_MISC, 0.0, hs(stream));
+  HIPCHK(launch_control_update(c, n_accepted, hs(stream)));
   return ok();
 }
 

@@ -134,11 +134,12 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_kv_rollback(int32_t* kv_len, int32_t* tokens, const int32_t* n_accepted,
                               const int32_t* out_tokens, hipStream_t s);
 hipError_t launch_kv_advance(int32_t* kv_len, int32_t delta, hipStream_t s);
-// Draft step: position check (valid, token_out = -1 when out of range) and
-// the RoPE table (cos, sin) [d/2][2] of position kv_len + step.
+// Draft step: position check (valid, token_out = -1 when out of range, or
+// when step >= *draft_len with draft_len set) and the RoPE table (cos, sin)
+// [d/2][2] of position kv_len + step.
 hipError_t launch_pos_guard(const int32_t* kv_len, const int32_t* token_in, int step, int cap,
                             int vocab, int32_t* valid, int32_t* token_out, int d, float theta,
-                            float* rope_cs, hipStream_t s);
+                            float* rope_cs, const int32_t* draft_len, hipStream_t s);
 // RoPE table [m][d/2][2] of positions kv_len + pos_offset + j.
 hipError_t launch_rope_table(const int32_t* kv_len, int pos_offset, int m, int d, float theta,
                              float* rope_cs, hipStream_t s);
@@ -167,7 +168,28 @@ struct RejectWs {
 };
 int reject_chunks(int vocab);
 size_t reject_ws_bytes(int gamma, int vocab);
+// gamma_len (optional, device): the round judges only the first
+// min(*gamma_len, gamma) draft tokens (a draft stopped early)
 hipError_t launch_reject(int gamma, int vocab, float temp, float draft_temp, const uint16_t* zt,
                          const uint16_t* zd, const int32_t* toks, const uint32_t* r_codes,
                          const uint32_t* u_code, int32_t* n_out, int32_t* out_tokens,
-                         int32_t* status, float* probs, const RejectWs& ws, hipStream_t s);
+                         int32_t* status, float* probs, const RejectWs& ws, hipStream_t s,
+                         const int32_t* gamma_len = nullptr);
+
+// ------------------------------------------------------------------ adaptive draft length
+struct ControlArgs {
+  int32_t* draft_len;   // device: draft length of the round (gamma_max at its start)
+  double* state;        // device [8]: h_acc, h_rej, seen_acc, seen_rej, P, A, last length, spare
+  float* entropy;       // device [gamma_max]: entropy of each drafted token
+  double c, beta;       // C_d / C_v, EMA rate
+  int gamma_max;
+};
+int control_chunks(int vocab);
+// After draft step `step`: entropy of the step's logits and the controller's
+// continue/stop decision (may lower *draft_len to step + 1); nothing when the
+// step was not drafted (step >= *draft_len).
+hipError_t launch_draft_control(const ControlArgs& c, int step, const uint16_t* logits, int vocab,
+                                double* part, uint32_t* counter, hipStream_t s);
+// After the rejection round: EMA updates from n accepted, then a fresh round.
+hipError_t launch_control_update(const ControlArgs& c, const int32_t* n_accepted, hipStream_t s);
+hipError_t launch_control_init(const ControlArgs& c, hipStream_t s);

@@ -136,12 +136,12 @@ __device__ __forceinline__ void rope_angle(int p, int i, int d, float theta, flo
 // every layer's attention uses: d/2 threads.
 __global__ void pos_guard_kernel(const int32_t* kv_len, const int32_t* token_in, int step, int cap,
                                  int vocab, int32_t* valid, int32_t* token_out, int d, float theta,
-                                 float* rope_cs) {
+                                 float* rope_cs, const int32_t* draft_len) {
   const int pos = *kv_len + step;
   if (threadIdx.x < d / 2) rope_angle(pos, threadIdx.x, d, theta, rope_cs);
   if (threadIdx.x == 0) {
     const int t = *token_in;
-    const int ok = pos >= 0 && pos < cap && t >= 0 && t < vocab;
+    const int ok = pos >= 0 && pos < cap && t >= 0 && t < vocab && (!draft_len || step < *draft_len);
     *valid = ok;
     if (!ok) *token_out = -1;
   }
@@ -215,9 +215,9 @@ hipError_t launch_kv_advance(int32_t* kv_len, int32_t delta, hipStream_t s) {
 
 hipError_t launch_pos_guard(const int32_t* kv_len, const int32_t* token_in, int step, int cap,
                             int vocab, int32_t* valid, int32_t* token_out, int d, float theta,
-                            float* rope_cs, hipStream_t s) {
+                            float* rope_cs, const int32_t* draft_len, hipStream_t s) {
   SS_LAUNCH(pos_guard_kernel, dim3(1), dim3(64), 0, s, kv_len, token_in, step, cap, vocab, valid,
-            token_out, d, theta, rope_cs);
+            token_out, d, theta, rope_cs, draft_len);
   return hipGetLastError();
 }
 

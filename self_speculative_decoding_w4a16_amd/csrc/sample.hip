@@ -271,7 +271,8 @@ __global__ __launch_bounds__(kT) void rej_decide_kernel(const uint16_t* zt, cons
                                                         const int32_t* toks, const uint32_t* r_codes,
                                                         const uint32_t* u_code, int32_t* n_out,
                                                         int32_t* out_tokens, int32_t* status_out,
-                                                        float* probs, RejectWs ws) {
+                                                        float* probs, RejectWs ws,
+                                                        const int32_t* gamma_len) {
   __shared__ RowStat st[129];
   __shared__ int s_n, s_status;
   __shared__ unsigned long long red[4];
@@ -296,9 +297,11 @@ __global__ __launch_bounds__(kT) void rej_decide_kernel(const uint16_t* zt, cons
   }
   __syncthreads();
   const bool writer = (T == 0.0f) ? (blockIdx.x == 0) : false;
+  // a draft stopped early: only its first g tokens are judged (g <= gamma)
+  const int g = gamma_len ? min(max(*gamma_len, 0), gamma) : gamma;
   if (threadIdx.x == 0) {
-    int status = 0, n = gamma;
-    for (int i = 0; i < gamma; ++i) {
+    int status = 0, n = g;
+    for (int i = 0; i < g; ++i) {
       const int x = toks[i];
       const RowStat& t = st[i];
       const RowStat& d = st[gamma + 1 + i];
@@ -357,7 +360,7 @@ __global__ __launch_bounds__(kT) void rej_decide_kernel(const uint16_t* zt, cons
   }
   // stochastic: residual (n < gamma) or bonus (n == gamma) draw from row n
   const RowStat t = st[n];
-  const bool resid = n < gamma;
+  const bool resid = n < g;
   RowStat d = {0.f, 0, 0, 1ull};
   if (resid) d = st[gamma + 1 + n];
   const bool dgreedy = (Td == 0.0f);
@@ -468,7 +471,8 @@ size_t reject_ws_bytes(int gamma, int vocab) {
 hipError_t launch_reject(int gamma, int vocab, float temp, float draft_temp, const uint16_t* zt,
                          const uint16_t* zd, const int32_t* toks, const uint32_t* r_codes,
                          const uint32_t* u_code, int32_t* n_out, int32_t* out_tokens,
-                         int32_t* status, float* probs, const RejectWs& ws, hipStream_t s) {
+                         int32_t* status, float* probs, const RejectWs& ws, hipStream_t s,
+                         const int32_t* gamma_len) {
   const int C = reject_chunks(vocab), rows = 2 * gamma + 1;
   SS_LAUNCH(rej_rowmax_kernel, dim3(C, rows), dim3(kT), 0, s, zt, zd, gamma, vocab, ws);
   hipError_t e = hipGetLastError();
@@ -481,6 +485,6 @@ hipError_t launch_reject(int gamma, int vocab, float temp, float draft_temp, con
   }
   const int blocks = temp == 0.0f ? 1 : C;
   SS_LAUNCH(rej_decide_kernel, dim3(blocks), dim3(kT), 0, s, zt, zd, gamma, vocab, temp,
-                     draft_temp, toks, r_codes, u_code, n_out, out_tokens, status, probs, ws);
+                     draft_temp, toks, r_codes, u_code, n_out, out_tokens, status, probs, ws, gamma_len);
   return hipGetLastError();
 }

@@ -15,6 +15,13 @@ With ``sparse`` the draft reads a sparse KV index ("The second ledger of
 speculative decoding", sections 3.1-3.2): every verify writes importance
 scores, and after the rollback the index is rebuilt; the first cycle after
 a reset drafts densely.
+
+With ``adaptive`` the draft length follows the entropy controller of the
+same blog's section 3.3: after every draft step the library measures the
+token's entropy and decides on the device whether the draft goes on; later
+steps skip themselves, the rejection round judges only the drafted tokens,
+and the controller's class centres are updated from its outcome.  gamma is
+then the longest draft.
 """
 import torch
 
@@ -23,9 +30,11 @@ from . import _lib
 
 class SpecDecoder:
     def __init__(self, model, capacity, gamma, temp=0.0, draft_temp=0.0, max_tokens=64,
-                 device="cuda", sparse=None, graphs=False):
+                 device="cuda", sparse=None, graphs=False, adaptive=None):
         """``sparse``: None (dense drafting) or dict(n_sink, n_recent, window,
-        budget_permille).  ``graphs``: replay recorded cycles (see above)."""
+        budget_permille).  ``graphs``: replay recorded cycles (see above).
+        ``adaptive``: None (fixed length gamma) or dict(c = C_d / C_v,
+        beta = EMA rate)."""
         s = model.shape
         self.model = model
         self.gamma = gamma
@@ -60,6 +69,19 @@ class SpecDecoder:
         self.c = _lib.State(self.k_cache.data_ptr(), self.v_cache.data_ptr(), capacity,
                             self.kv_len.data_ptr(), self.tokens.data_ptr(),
                             self.draft_logits.data_ptr(), gamma)
+        self.adaptive = dict(adaptive) if adaptive else None
+        self.ctl = None
+        if self.adaptive:
+            if sparse:
+                raise ValueError("the adaptive draft length is built for dense drafting")
+            self.draft_len = torch.full((1,), gamma, dtype=torch.int32, device=device)
+            self.ctl_state = torch.zeros(8, dtype=torch.float64, device=device)
+            self.entropy = torch.zeros(max(gamma, 1), dtype=torch.float32, device=device)
+            self.ctl = _lib.Control(self.draft_len.data_ptr(), self.ctl_state.data_ptr(),
+                                    self.entropy.data_ptr(), float(self.adaptive["c"]),
+                                    float(self.adaptive.get("beta", 0.125)), gamma)
+            self.c.draft_len = self.draft_len.data_ptr()
+            _lib.control_init(self.ctl)
         self.sparse = dict(sparse) if sparse else None
         if self.sparse:
             sp = self.sparse
@@ -112,14 +134,26 @@ class SpecDecoder:
     def draft(self, u_draft=None):
         for i in range(self.gamma):
             _lib.draft_step(self.model.c, self.c, i, self.draft_temp, u_draft, self.ws)
+            if self.ctl is not None:
+                _lib.draft_control(self.model.c, self.c, i, self.ctl, self.ws)
 
     def verify(self):
         _lib.verify(self.model.c, self.c, self.gamma + 1, self.tokens, self.target_logits, self.ws)
 
     def reject(self, r_codes=None, u_code=None):
+        if self.ctl is not None:
+            _lib.reject_len(self.gamma, self.model.shape.vocab, self.temp, self.draft_temp,
+                            self.target_logits, self.draft_logits, self.tokens[1:], r_codes, u_code,
+                            self.draft_len, self.n_accepted, self.out_tokens, self.status, self.probs, self.ws)
+            _lib.control_update(self.ctl, self.n_accepted)
+            return
         _lib.reject(self.gamma, self.model.shape.vocab, self.temp, self.draft_temp,
                     self.target_logits, self.draft_logits, self.tokens[1:], r_codes, u_code,
                     self.n_accepted, self.out_tokens, self.status, self.probs, self.ws)
+
+    def last_draft_len(self):
+        """Draft length of the last completed cycle (adaptive length only)."""
+        return int(self.ctl_state[6].item())
 
     def commit(self):
         _lib.kv_rollback(self.c, self.n_accepted, self.out_tokens)
