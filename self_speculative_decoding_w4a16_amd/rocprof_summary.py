@@ -1,13 +1,17 @@
 """Summarise a rocprofv3 ``--kernel-trace --stats`` output directory.
 
 Usage: python -m self_speculative_decoding_w4a16_amd.rocprof_summary DIR [TOP]
+       python -m self_speculative_decoding_w4a16_amd.rocprof_summary --counters DIR [REGEX]
 
 Prints one row per kernel (calls, total ms, average / min / max microseconds,
 share of GPU time), with the library's template kernels named by the launch
-site they serve (for example ``gemv_kernel<4, false, 1, 2, 256>`` is the bf16
+site they serve (for example ``gemv_kernel<2, 16, 1, 2, 256>`` is the bf16
 gate/up GEMV with the RMSNorm prologue and the SiLU*up epilogue, 256-thread
 blocks; ``gemm_kernel<2, 2, 3>`` the verify GEMM with 2-wave blocks, up to 32
 positions, writing split-k partial sums).
+
+With --counters: a ``--pmc`` run's per-dispatch counter values (mean, min,
+max over the dispatches of each kernel whose name matches REGEX).
 """
 import csv
 import glob
@@ -21,12 +25,13 @@ _GEPI = {0: "store", 1: "resid", 2: "silu*up", 3: "split-k partials"}
 
 def describe(name):
     """Short name and launch role of one kernel symbol."""
-    m = re.search(r"gemv_kernel<(\d+), (true|false), (\d+), (\d+)(?:, (\d+))?>", name)
+    m = re.search(r"gemv_kernel<(\d+), (\d+|true|false), (\d+), (\d+)(?:, (\d+))?>", name)
     if m:
-        r, w4, pro, epi = int(m[1]), m[2] == "true", int(m[3]), int(m[4])
+        r, wb, pro, epi = int(m[1]), m[2], int(m[3]), int(m[4])
+        width = {"16": "bf16", "false": "bf16", "4": "W4", "true": "W4", "3": "W3", "2": "W2"}.get(wb, wb)
         nt = f",{m[5]}" if m[5] else ""
-        return (f"gemv_kernel<{r},{m[2]},{pro},{epi}{nt}>",
-                f"{'W4' if w4 else 'bf16'} GEMV, {r} rows/wave, {_PRO.get(pro, pro)} -> {_EPI.get(epi, epi)}")
+        return (f"gemv_kernel<{r},{wb},{pro},{epi}{nt}>",
+                f"{width} GEMV, {r} rows/wave, {_PRO.get(pro, pro)} -> {_EPI.get(epi, epi)}")
     m = re.search(r"gemm_kernel<(\d+), (\d+), (\d+)>", name)
     if m:
         nw, tt, epi = int(m[1]), int(m[2]), int(m[3])
@@ -61,6 +66,10 @@ _ROLES = {
     "attn_scores_kernel": "sparse draft: importance scores",
     "kv_select_kernel": "sparse draft: index rebuild (radix select)",
     "w4_quantize_kernel": "W4 g64 quantiser",
+    "quantize_kernel": "low-bit g64 quantiser",
+    "draft_control_kernel": "adaptive draft length: entropy + stop decision",
+    "control_update_kernel": "adaptive draft length: EMA centres",
+    "rej_rowsum_kernel": "rejection: fixed-point row sums",
 }
 
 
@@ -91,5 +100,28 @@ def main(argv):
     print(f"total GPU kernel time {total / 1e6:.3f} ms over {sum(int(r['Calls']) for r in rows)} launches")
 
 
+def counters(path, regex=".*"):
+    """Per-dispatch counter values of a --pmc run, per kernel and counter."""
+    files = glob.glob(path + "/**/*counter_collection.csv", recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {path}")
+    vals = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            name = r.get("Kernel_Name") or r.get("Kernel-Name") or r.get("KernelName") or ""
+            if not re.search(regex, name):
+                continue
+            key = (describe(name)[0], r.get("Counter_Name") or r.get("Counter-Name") or "")
+            vals.setdefault(key, {}).setdefault(r.get("Dispatch_Id") or r.get("Dispatch-Id"), 0.0)
+            vals[key][r.get("Dispatch_Id") or r.get("Dispatch-Id")] += float(r.get("Counter_Value") or 0.0)
+    print(f"{'kernel':34s} {'counter':14s} {'dispatches':>10s} {'mean':>14s} {'min':>14s} {'max':>14s}")
+    for (k, c), d in sorted(vals.items()):
+        v = list(d.values())
+        print(f"{k:34s} {c:14s} {len(v):10d} {sum(v) / len(v):14.1f} {min(v):14.1f} {max(v):14.1f}")
+
+
 if __name__ == "__main__":
-    main(sys.argv)
+    if len(sys.argv) > 1 and sys.argv[1] == "--counters":
+        counters(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else ".*")
+    else:
+        main(sys.argv)

@@ -127,7 +127,9 @@ def test_exact_levels_group_low_bits(bits):
         assert codes.shape == (1, 32)
         np.testing.assert_array_equal(codes[0], lo2)
     else:
-        hi = [sum(((q[8 * j + t] >> 2) & 1) << t for t in range(8)) for j in range(16)]
+        # third-bit words of 32 weights, bytes holding weights 0-7, 16-23, 8-15, 24-31
+        first = [32 * (j // 4) + (0, 16, 8, 24)[j % 4] for j in range(16)]
+        hi = [sum(((q[first[j] + t] >> 2) & 1) << t for t in range(8)) for j in range(16)]
         assert codes.shape == (1, 48)
         np.testing.assert_array_equal(codes[0], lo2 + hi)
     # 2 bits of codes 0..3 repeating: every byte is 0b11100100
