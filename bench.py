@@ -27,13 +27,13 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # HBM traffic per launch of a draft GEMV site, from two rocprofv3 --pmc runs of
 # `bench.py --site NAME` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each
 # scaled by what the same counter reads for a 1 GiB device-to-device copy in
-# the same run (FETCH_SIZE 524328 KiB -> x2.0, WRITE_SIZE 1048576 KiB -> x1.0).
+# the same run (FETCH_SIZE 524316 KiB -> x2.0, WRITE_SIZE 1048576 KiB -> x1.0).
 # Reported only while the kernel sources hash to the value they were taken on.
 TRAFFIC = {
-    "bf16_gate_up": {"fetch_kib": 132735.6, "write_kib": 148.3, "fetch_scale": 2.0,
-                     "write_scale": 1.0, "sources": "25a1e40af342e8bb"},
-    "w4_gate_up": {"fetch_kib": 37468.3, "write_kib": 148.0, "fetch_scale": 2.0,
-                   "write_scale": 1.0, "sources": "25a1e40af342e8bb"},
+    "bf16_gate_up": {"fetch_kib": 132734.8, "write_kib": 148.3, "fetch_scale": 2.0,
+                     "write_scale": 1.0, "sources": "dc99951ee3026795"},
+    "w4_gate_up": {"fetch_kib": 37469.7, "write_kib": 148.0, "fetch_scale": 2.0,
+                   "write_scale": 1.0, "sources": "dc99951ee3026795"},
 }
 GEMV_SOURCES = ("csrc/gemv.hip", "csrc/common.h", "csrc/internal.h")
 
@@ -332,6 +332,10 @@ def main():
         log(f"one 7B layer: {json.dumps(layer)}")
         lowbit = lowbit_rates(dec, shape, w, wl, kv0, last, dev)
         log(f"3- and 2-bit substitutes: {json.dumps(lowbit)}")
+    batch = None
+    if args.config == "full7b" and not args.no_small:
+        batch = batch_rates(dm, shape, dev)
+        log(f"4-bit skinny GEMM (batch of drafts): {json.dumps(batch)}")
     adapt = None
     if not sparse and not args.no_small and not stochastic:
         adapt = adaptive_rates(dec, dm, wl, kv0, last, draft_pass["avg_us"] / verify_pass["avg_us"])
@@ -390,6 +394,7 @@ def main():
         "layer7b": layer,
         "lowbit": lowbit,
         "adaptive_length": adapt,
+        "batch_w4_gemm": batch,
         "kernels": kern,
     }
     # every rate also against the measured read ceiling
@@ -521,7 +526,7 @@ def isolated_gemvs(dm, shape, dev, reps=3, only=None, graph=True):
             r = rows_per_wave(n_out, epi == 2, w4)
             out[f"{kind}_{site}"] = {"avg_us": round(us, 3), "bytes_per_launch": round(by),
                                      "gbs": round(by / (us * 1e-6) / 1e9, 1), "per_step": len(layers),
-                                     "symbol": sym.format(r=r, w="true" if w4 else "false")}
+                                     "symbol": sym.format(r=r, w="4" if w4 else "16")}
     if only and only != "lm_head":
         return out
     lm = _lib.linear(w=dm.w["lm_head"])
@@ -529,7 +534,7 @@ def isolated_gemvs(dm, shape, dev, reps=3, only=None, graph=True):
     us = timed([lm], H, shape.vocab, True, 0)
     out["lm_head"] = {"avg_us": round(us, 3), "bytes_per_launch": round(by),
                       "gbs": round(by / (us * 1e-6) / 1e9, 1), "per_step": 1,
-                      "symbol": "gemv_kernel<4,false,1,0>"}
+                      "symbol": "gemv_kernel<4,16,1,0>"}
     return out
 
 
@@ -733,6 +738,39 @@ def adaptive_rates(dec, dm, wl, kv0, last, c, steps=2):
     return {"tokens_s": round(steps * G / el, 3), "tau": round(float(np.mean([n + 1 for n in all_ns])), 4),
             "mean_draft_len": round(float(np.mean(all_gs)), 3), "max_draft_len": wl.gamma, "c": round(c, 4),
             "beta": 0.125}
+
+
+def batch_rates(dm, shape, dev):
+    """The 4-bit skinny GEMM (matrix cores) that drafts m sequences at once on
+    shared substitutes, at the gate/up and down shapes of the substitute
+    layers, m = 1, 4, 8, 16: microseconds per launch (graph-replayed over all
+    substitute layers, >= 1 GiB a round) and the weight stream's rate; the
+    per-token weight bytes fall as 1/m."""
+    import torch
+
+    from self_speculative_decoding_w4a16_amd import _lib
+    H, F = shape.hidden, shape.ffn
+    out = {}
+    sub = dm.substitute_layers
+    for site, k, n in (("gate_up", H, 2 * F), ("down", F, H)):
+        lins = [_lib.linear(codes=dm.q[l][site][0], meta=dm.q[l][site][1]) for l in sub]
+        wb = n * k * (0.5 + 4 / 64)
+        reps = max(1, int((1 << 30) // (wb * len(lins))))
+        for m in (1, 4, 8, 16):
+            x = torch.randn(m, k, device=dev).bfloat16()
+            y = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+            buf = torch.zeros(_lib.w4_gemm_workspace_bytes(n, k, m), dtype=torch.uint8, device=dev)
+
+            def run():
+                for _ in range(reps):
+                    for lin in lins:
+                        _lib.w4_gemm(lin, x, y, buf)
+            us = replay_us(run, reps=2) / (reps * len(lins))
+            by = wb + 2 * m * (k + n)
+            out[f"{site}_m{m}"] = {"avg_us": round(us, 3), "gbs": round(by / (us * 1e-6) / 1e9, 1),
+                                   "frac": round(by / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                   "weight_bytes_per_token": round(wb / m)}
+    return out
 
 
 def tiny_rates(dev, reps=200):

@@ -246,6 +246,25 @@ int subspec_reject(int32_t gamma, int32_t vocab, float temp, float draft_temp,
                    int32_t *n_accepted, int32_t *out_tokens, int32_t *status, float *probs,
                    void *ws, size_t ws_bytes, void *stream);
 
+/* `batch` independent rejection rounds in one launch set (the rounds of B
+ * sequences decoded together with shared substitutes; [SSR] section 10.3,
+ * batch > 1).  Each round is exactly subspec_reject_len on its slice: every
+ * pointer is [batch] x its one-round extent, consecutive:
+ *   target_logits [B][gamma+1][vocab], draft_logits [B][gamma][vocab],
+ *   draft_tokens and r_codes [B][gamma], u_codes [B], gamma_len [B] (device;
+ *   NULL = gamma for every round), n_accepted and status [B], out_tokens
+ *   [B][gamma+1], probs [B][gamma][2] (optional).
+ * 1 <= batch <= 4096; workspace of subspec_reject_workspace_bytes(batch, gamma,
+ * vocab) bytes (zero-filled once, like every workspace). */
+int subspec_reject_batch(int32_t batch, int32_t gamma, int32_t vocab, float temp, float draft_temp,
+                         const uint16_t *target_logits, const uint16_t *draft_logits,
+                         const int32_t *draft_tokens, const uint32_t *r_codes, const uint32_t *u_codes,
+                         const int32_t *gamma_len, int32_t *n_accepted, int32_t *out_tokens, int32_t *status,
+                         float *probs, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes subspec_reject_batch needs (0 on invalid arguments). */
+size_t subspec_reject_workspace_bytes(int32_t batch, int32_t gamma, int32_t vocab);
+
 /* subspec_reject without a workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc).  Same arguments, kernels and results as
@@ -357,6 +376,16 @@ int subspec_kv_advance(const subspec_state *st, int32_t delta, void *stream);
  * y bf16 [n]; k % 64 == 0. */
 int subspec_w4_gemv(const uint8_t *codes, const uint16_t *meta, int64_t n, int64_t k,
                     const uint16_t *x, uint16_t *y, void *stream);
+
+/* Y[t][n] = bf16( sum_k X[t][k] (q[n][k] * scale + min) ) for t < m <= 16 on
+ * the matrix cores: the draft of up to 16 sequences decoded together, which
+ * share the 4-bit substitutes ([SSR] section 10.3, item 11; the weights
+ * stream once for all m).  w: 4-bit codes + meta [n][k]; X bf16 [m][k], Y bf16
+ * [m][n]; k % 128 == 0.  Workspace: subspec_w4_gemm_workspace_bytes(n, k, m)
+ * (fp32 split-k partials). */
+int subspec_w4_gemm(const subspec_linear *w, const uint16_t *x, int32_t m, uint16_t *y, void *ws,
+                    size_t ws_bytes, void *stream);
+size_t subspec_w4_gemm_workspace_bytes(int64_t n, int64_t k, int32_t m);
 
 /* y[n] = bf16( sum_k w[n][k] x[k] ), bf16 weights at batch 1; k % 8 == 0. */
 int subspec_bf16_gemv(const uint16_t *w, int64_t n, int64_t k, const uint16_t *x, uint16_t *y,

@@ -81,6 +81,10 @@ _SIGS = {
     "subspec_reject_len": (c_int32, [c_int32, c_int32, c_float, c_float, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_size_t, c_void_p]),
+    "subspec_reject_batch": (c_int32, [c_int32, c_int32, c_int32, c_float, c_float, c_void_p, c_void_p,
+                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                       c_void_p, c_void_p, c_size_t, c_void_p]),
+    "subspec_reject_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
     "subspec_control_init": (c_int32, [POINTER(Control), c_void_p]),
     "subspec_draft_control": (c_int32, [POINTER(Model), POINTER(State), c_int32, POINTER(Control), c_void_p,
                                         c_size_t, c_void_p]),
@@ -94,6 +98,8 @@ _SIGS = {
     "subspec_index_count": (c_int64, [c_int64, c_int32, c_int32, c_int32]),
     "subspec_w4_gemv": (c_int32, [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p,
                                   c_void_p]),
+    "subspec_w4_gemm": (c_int32, [POINTER(Linear), c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "subspec_w4_gemm_workspace_bytes": (c_size_t, [c_int64, c_int64, c_int32]),
     "subspec_bf16_gemv": (c_int32, [c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
     "subspec_gemv": (c_int32, [POINTER(Linear), c_void_p, c_void_p, c_float, c_int32, c_void_p,
                                c_void_p, c_void_p]),
@@ -214,6 +220,21 @@ def reject_len(gamma, vocab, temp, draft_temp, target_logits, draft_logits, draf
                                    ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def reject_workspace_bytes(batch, gamma, vocab):
+    n = lib().subspec_reject_workspace_bytes(batch, gamma, vocab)
+    if n == 0:
+        raise SubspecError(EINVAL, last_error())
+    return n
+
+
+def reject_batch(batch, gamma, vocab, temp, draft_temp, target_logits, draft_logits, draft_tokens, r_codes,
+                 u_codes, gamma_len, n_accepted, out_tokens, status, probs, ws, stream=None):
+    check(lib().subspec_reject_batch(batch, gamma, vocab, temp, draft_temp, _p(target_logits), _p(draft_logits),
+                                     _p(draft_tokens), _p(r_codes), _p(u_codes), _p(gamma_len), _p(n_accepted),
+                                     _p(out_tokens), _p(status), _p(probs), _p(ws), ws.numel() * ws.element_size(),
+                                     _stream(stream)))
+
+
 def control_init(ctl, stream=None):
     check(lib().subspec_control_init(ctypes.byref(ctl), _stream(stream)))
 
@@ -258,6 +279,19 @@ def kv_advance(state, delta, stream=None):
 
 def w4_gemv(codes, meta, n, k, x, y, stream=None):
     check(lib().subspec_w4_gemv(_p(codes), _p(meta), n, k, _p(x), _p(y), _stream(stream)))
+
+
+def w4_gemm_workspace_bytes(n, k, m):
+    b = lib().subspec_w4_gemm_workspace_bytes(n, k, m)
+    if b == 0:
+        raise SubspecError(EINVAL, last_error())
+    return b
+
+
+def w4_gemm(lin, x, y, ws, stream=None):
+    """Y [m][n] = X [m][k] W^T on 4-bit weights (m <= 16), matrix cores."""
+    check(lib().subspec_w4_gemm(ctypes.byref(lin), _p(x), x.shape[0], _p(y), _p(ws),
+                                ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def bf16_gemv(w, x, y, stream=None):

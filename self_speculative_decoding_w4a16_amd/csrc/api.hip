@@ -46,6 +46,8 @@ int ok() {
 constexpr size_t kCounterBytes = 64 * 1024;
 constexpr size_t kSampleCounterOff = 16 * 1024;
 constexpr size_t kRejectCounterOff = 16 * 1024 + 256;
+constexpr size_t kRejectBatchCounterOff = 32 * 1024;  // batched rejection: one per element
+constexpr int kMaxRejectBatch = 4096;                   // its counters fill [32 KiB, 48 KiB)
 constexpr size_t kAttnCounterOff = 20 * 1024;  // draft attention: one per query head (<= 224)
 constexpr size_t kControlCounterOff = 16 * 1024 + 512;  // draft-length controller
 constexpr int kMaxTokens = 64;
@@ -247,16 +249,16 @@ size_t carve_fwd(const subspec_model* m, int mt, int cap, void* ws, FwdWs* o) {
 struct RejWsL {
   RejectWs r;
 };
-size_t carve_reject(int gamma, int vocab, void* ws, RejectWs* o) {
+size_t carve_reject(int gamma, int vocab, void* ws, RejectWs* o, int batch = 1) {
   Carver c{(char*)ws, kCounterBytes};
-  const size_t C = (size_t)reject_chunks(vocab), rows = (size_t)(2 * gamma + 1);
+  const size_t C = (size_t)reject_chunks(vocab), rows = (size_t)(2 * gamma + 1), B = (size_t)batch;
   RejectWs r{};
-  r.counter = ws ? (uint32_t*)((char*)ws + kRejectCounterOff) : nullptr;
-  r.row_max = (float*)c.take(rows * C * 4);
-  r.row_arg = (int32_t*)c.take(rows * C * 4);
-  r.row_bad = (int32_t*)c.take(rows * C * 4);
-  r.row_sum = (unsigned long long*)c.take(rows * C * 8);
-  r.res_sum = (unsigned long long*)c.take(C * 8);
+  r.counter = ws ? (uint32_t*)((char*)ws + (batch > 1 ? kRejectBatchCounterOff : kRejectCounterOff)) : nullptr;
+  r.row_max = (float*)c.take(B * rows * C * 4);
+  r.row_arg = (int32_t*)c.take(B * rows * C * 4);
+  r.row_bad = (int32_t*)c.take(B * rows * C * 4);
+  r.row_sum = (unsigned long long*)c.take(B * rows * C * 8);
+  r.res_sum = (unsigned long long*)c.take(B * C * 8);
   if (o) *o = r;
   return c.off;
 }
@@ -650,6 +652,40 @@ int subspec_reject(int32_t gamma, int32_t vocab, float temp, float draft_temp,
                             u_code, nullptr, n_accepted, out_tokens, status, probs, ws, ws_bytes, stream);
 }
 
+size_t subspec_reject_workspace_bytes(int32_t batch, int32_t gamma, int32_t vocab) {
+  if (batch < 1 || batch > kMaxRejectBatch || gamma < 0 || gamma > kMaxGamma || vocab < 1 || vocab > (1 << 24)) {
+    fail(SUBSPEC_EINVAL, "batch in [1, %d], gamma in [0, %d], vocab in [1, 2^24]", kMaxRejectBatch, kMaxGamma);
+    return 0;
+  }
+  ok();
+  return carve_reject(gamma, vocab, nullptr, nullptr, batch);
+}
+
+int subspec_reject_batch(int32_t batch, int32_t gamma, int32_t vocab, float temp, float draft_temp,
+                         const uint16_t* target_logits, const uint16_t* draft_logits, const int32_t* draft_tokens,
+                         const uint32_t* r_codes, const uint32_t* u_codes, const int32_t* gamma_len,
+                         int32_t* n_accepted, int32_t* out_tokens, int32_t* status, float* probs, void* ws,
+                         size_t ws_bytes, void* stream) {
+  if (batch < 1 || batch > kMaxRejectBatch) return fail(SUBSPEC_EINVAL, "batch outside [1, %d]", kMaxRejectBatch);
+  if (gamma < 0 || gamma > kMaxGamma) return fail(SUBSPEC_EINVAL, "gamma outside [0, %d]", kMaxGamma);
+  if (vocab < 1 || vocab > (1 << 24)) return fail(SUBSPEC_EINVAL, "vocab outside [1, 2^24]");
+  if (!(temp >= 0.0f) || !(draft_temp >= 0.0f)) return fail(SUBSPEC_EINVAL, "temperatures must be >= 0");
+  if (!target_logits || !n_accepted || !out_tokens || !status)
+    return fail(SUBSPEC_EINVAL, "target_logits, n_accepted, out_tokens and status must be set");
+  if (gamma > 0 && (!draft_logits || !draft_tokens))
+    return fail(SUBSPEC_EINVAL, "draft_logits and draft_tokens must be set when gamma > 0");
+  if (temp > 0.0f && (!u_codes || (gamma > 0 && !r_codes)))
+    return fail(SUBSPEC_EINVAL, "r_codes and u_codes must be set when temp > 0");
+  int r;
+  if ((r = need_ws(ws, ws_bytes, carve_reject(gamma, vocab, nullptr, nullptr, batch)))) return r;
+  RejectWs rw;
+  carve_reject(gamma, vocab, ws, &rw, batch);
+  prof::Scope ps(SUBSPEC_K_REJECT, 2.0 * batch * (2 * gamma + 1) * vocab, hs(stream));
+  HIPCHK(launch_reject(gamma, vocab, temp, draft_temp, target_logits, draft_logits, draft_tokens, r_codes, u_codes,
+                       n_accepted, out_tokens, status, probs, rw, hs(stream), gamma_len, batch));
+  return ok();
+}
+
 int subspec_kv_rollback(const subspec_state* st, const int32_t* n_accepted,
                         const int32_t* out_tokens, void* stream) {
   if (!st || !st->kv_len || !st->tokens) return fail(SUBSPEC_EINVAL, "state kv_len/tokens NULL");
@@ -775,6 +811,30 @@ int subspec_gemv(const subspec_linear* w, const uint16_t* x, const uint16_t* nor
   if (pro == PRO_NORM && epi == EPI_RESID)
     return fail(SUBSPEC_EUNSUPPORTED, "epilogue 1 is fused with the plain prologue only");
   HIPCHK(launch_gemv(lin_bits(*w), pro, epi, a, hs(stream), nullptr));
+  return ok();
+}
+
+size_t subspec_w4_gemm_workspace_bytes(int64_t n, int64_t k, int32_t m) {
+  if (n < 1 || k < 128 || k % 128 != 0 || m < 1 || m > 16) {
+    fail(SUBSPEC_EINVAL, "n >= 1, k a positive multiple of 128, 1 <= m <= 16");
+    return 0;
+  }
+  ok();
+  return kCounterBytes + (size_t)gemm_w4_splits(n, k) * m * n * 4;
+}
+
+int subspec_w4_gemm(const subspec_linear* w, const uint16_t* x, int32_t m, uint16_t* y, void* ws, size_t ws_bytes,
+                    void* stream) {
+  if (!w || !x || !y) return fail(SUBSPEC_EINVAL, "w, x and y must be set");
+  if (!lin_is_w4(*w) || lin_bits(*w) != 4) return fail(SUBSPEC_EINVAL, "w must be 4-bit codes + meta");
+  if (w->n < 1 || w->k < 1) return fail(SUBSPEC_EINVAL, "n and k must be positive");
+  if (w->k % 128 != 0) return fail(SUBSPEC_ESHAPE, "k must be a multiple of 128");
+  if (m < 1 || m > 16) return fail(SUBSPEC_EINVAL, "m outside [1, 16]");
+  int r;
+  if ((r = need_ws(ws, ws_bytes, kCounterBytes + (size_t)gemm_w4_splits(w->n, w->k) * m * w->n * 4))) return r;
+  prof::Scope ps(SUBSPEC_K_W4_GATE_UP, w->n * code_row_bytes(4, (double)w->k) + w->n * (w->k / 64) * 4.0 +
+                 2.0 * m * (w->k + w->n), hs(stream));
+  HIPCHK(launch_gemm_w4(w->codes, w->meta, w->n, w->k, x, m, y, (float*)((char*)ws + kCounterBytes), hs(stream)));
   return ok();
 }
 

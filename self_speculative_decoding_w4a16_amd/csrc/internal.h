@@ -61,6 +61,13 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s, int* splits_ou
 hipError_t launch_gemm_reduce(const float* part, int splits, int m, int64_t n, uint16_t* y, int64_t ldy,
                               hipStream_t s);
 
+// Skinny GEMM on 4-bit weights (matrix cores): Y[t][n] = bf16(sum_k X[t][k] w[n][k])
+// for t < m <= 16; k % 128 == 0.  With k split over blocks it writes fp32
+// partials (gemm_w4_splits x m x n floats at part) and reduces them in order.
+int gemm_w4_splits(int64_t n, int64_t k);
+hipError_t launch_gemm_w4(const uint8_t* codes, const uint16_t* meta, int64_t n, int64_t k, const uint16_t* x, int m,
+                          uint16_t* y, float* part, hipStream_t s);
+
 // ------------------------------------------------------------------ quantise
 hipError_t launch_quantize(const uint16_t* w, int64_t n, int64_t k, int bits, uint8_t* codes,
                            uint16_t* meta, hipStream_t s);
@@ -158,23 +165,25 @@ hipError_t launch_sample(const uint16_t* logits, int vocab, float temp, const ui
 hipError_t launch_rowmax(const uint16_t* logits, int vocab, float* part_max, int32_t* part_arg,
                          int n_chunks, hipStream_t s);
 
-struct RejectWs {
-  float* row_max;                    // [rows][chunks]
-  int32_t* row_arg;                  // [rows][chunks]
-  int32_t* row_bad;                  // [rows][chunks] non-finite flags
-  unsigned long long* row_sum;       // [rows][chunks]
-  unsigned long long* res_sum;       // [chunks]
-  uint32_t* counter;
+struct RejectWs {                    // per batch element b, at offset b x the one-element size:
+  float* row_max;                    // [batch][rows][chunks]
+  int32_t* row_arg;                  // [batch][rows][chunks]
+  int32_t* row_bad;                  // [batch][rows][chunks] non-finite flags
+  unsigned long long* row_sum;       // [batch][rows][chunks]
+  unsigned long long* res_sum;       // [batch][chunks]
+  uint32_t* counter;                 // [batch] arrival counters (zero between launches)
 };
 int reject_chunks(int vocab);
 size_t reject_ws_bytes(int gamma, int vocab);
-// gamma_len (optional, device): the round judges only the first
-// min(*gamma_len, gamma) draft tokens (a draft stopped early)
+// gamma_len (optional, device [batch]): each round judges only the first
+// min(*gamma_len, gamma) draft tokens (a draft stopped early).  batch
+// independent rounds (grid z): every pointer argument is [batch] x its
+// one-round extent, consecutive.
 hipError_t launch_reject(int gamma, int vocab, float temp, float draft_temp, const uint16_t* zt,
                          const uint16_t* zd, const int32_t* toks, const uint32_t* r_codes,
                          const uint32_t* u_code, int32_t* n_out, int32_t* out_tokens,
                          int32_t* status, float* probs, const RejectWs& ws, hipStream_t s,
-                         const int32_t* gamma_len = nullptr);
+                         const int32_t* gamma_len = nullptr, int batch = 1);
 
 // ------------------------------------------------------------------ adaptive draft length
 struct ControlArgs {

@@ -216,12 +216,28 @@ __device__ __forceinline__ const uint16_t* row_ptr(const uint16_t* zt, const uin
   return r <= gamma ? zt + (int64_t)r * V : zd + (int64_t)(r - gamma - 1) * V;
 }
 
+// Batch element b = blockIdx.z: its scratch rows (each element has its own
+// [rows][C] arrays, [C] residual sums and arrival counter).
+__device__ __forceinline__ RejectWs ws_at(RejectWs ws, int b, int rows, int C) {
+  const int64_t rc = (int64_t)rows * C;
+  ws.row_max += b * rc;
+  ws.row_arg += b * rc;
+  ws.row_bad += b * rc;
+  ws.row_sum += b * rc;
+  ws.res_sum += (int64_t)b * C;
+  ws.counter += b;
+  return ws;
+}
+
 __global__ __launch_bounds__(kT) void rej_rowmax_kernel(const uint16_t* zt, const uint16_t* zd,
                                                         int gamma, int V, RejectWs ws) {
   __shared__ float rv[4];
   __shared__ int ri[4];
   __shared__ int s_bad;
-  const int c = blockIdx.x, r = blockIdx.y, C = gridDim.x;
+  const int c = blockIdx.x, r = blockIdx.y, C = gridDim.x, bz = blockIdx.z;
+  zt += (int64_t)bz * (gamma + 1) * V;
+  zd += (int64_t)bz * gamma * V;
+  ws = ws_at(ws, bz, 2 * gamma + 1, C);
   const uint16_t* z = row_ptr(zt, zd, gamma, V, r);
   const int lo = c * kRejChunk, hi = min(V, lo + kRejChunk);
   if (threadIdx.x == 0) s_bad = 0;
@@ -246,9 +262,12 @@ __global__ __launch_bounds__(kT) void rej_rowsum_kernel(const uint16_t* zt, cons
                                                         int gamma, int V, float T, float Td,
                                                         RejectWs ws) {
   __shared__ unsigned long long red[4];
-  const int c = blockIdx.x, r = blockIdx.y, C = gridDim.x;
+  const int c = blockIdx.x, r = blockIdx.y, C = gridDim.x, bz = blockIdx.z;
   const float temp = r <= gamma ? T : Td;
   if (temp == 0.0f) return;
+  zt += (int64_t)bz * (gamma + 1) * V;
+  zd += (int64_t)bz * gamma * V;
+  ws = ws_at(ws, bz, 2 * gamma + 1, C);
   float M = -INFINITY;
   for (int i = 0; i < C; ++i) M = fmaxf(M, ws.row_max[r * C + i]);
   const uint16_t* z = row_ptr(zt, zd, gamma, V, r);
@@ -280,6 +299,20 @@ __global__ __launch_bounds__(kT) void rej_decide_kernel(const uint16_t* zt, cons
   __shared__ bool s_last;
   const int C = (V + kRejChunk - 1) / kRejChunk;
   const int rows = 2 * gamma + 1;
+  {  // batch element blockIdx.z: its logits, tokens, uniforms, outputs and scratch
+    const int bz = blockIdx.z;
+    zt += (int64_t)bz * (gamma + 1) * V;
+    zd += (int64_t)bz * gamma * V;
+    toks += (int64_t)bz * gamma;
+    if (r_codes) r_codes += (int64_t)bz * gamma;
+    if (u_code) u_code += bz;
+    if (gamma_len) gamma_len += bz;
+    n_out += bz;
+    out_tokens += (int64_t)bz * (gamma + 1);
+    status_out += bz;
+    if (probs) probs += (int64_t)bz * 2 * gamma;
+    ws = ws_at(ws, bz, rows, C);
+  }
   for (int r = threadIdx.x; r < rows; r += kT) {
     RowStat s = {-INFINITY, ss::kNoIndex, 0, 0ull};
     for (int c = 0; c < C; ++c) {
@@ -472,19 +505,19 @@ hipError_t launch_reject(int gamma, int vocab, float temp, float draft_temp, con
                          const uint16_t* zd, const int32_t* toks, const uint32_t* r_codes,
                          const uint32_t* u_code, int32_t* n_out, int32_t* out_tokens,
                          int32_t* status, float* probs, const RejectWs& ws, hipStream_t s,
-                         const int32_t* gamma_len) {
+                         const int32_t* gamma_len, int batch) {
   const int C = reject_chunks(vocab), rows = 2 * gamma + 1;
-  SS_LAUNCH(rej_rowmax_kernel, dim3(C, rows), dim3(kT), 0, s, zt, zd, gamma, vocab, ws);
+  SS_LAUNCH(rej_rowmax_kernel, dim3(C, rows, batch), dim3(kT), 0, s, zt, zd, gamma, vocab, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (temp != 0.0f || draft_temp != 0.0f) {
-    SS_LAUNCH(rej_rowsum_kernel, dim3(C, rows), dim3(kT), 0, s, zt, zd, gamma, vocab, temp,
+    SS_LAUNCH(rej_rowsum_kernel, dim3(C, rows, batch), dim3(kT), 0, s, zt, zd, gamma, vocab, temp,
                        draft_temp, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int blocks = temp == 0.0f ? 1 : C;
-  SS_LAUNCH(rej_decide_kernel, dim3(blocks), dim3(kT), 0, s, zt, zd, gamma, vocab, temp,
+  SS_LAUNCH(rej_decide_kernel, dim3(blocks, 1, batch), dim3(kT), 0, s, zt, zd, gamma, vocab, temp,
                      draft_temp, toks, r_codes, u_code, n_out, out_tokens, status, probs, ws, gamma_len);
   return hipGetLastError();
 }
