@@ -40,9 +40,12 @@ are judged by the chain rule of reject.py against the target rows of its
 depth-1..D nodes and the draft rows of its depth-1..D-1 nodes.
 
 Readings where the pages are silent (integer arithmetic as in reject.py):
-  * the residual of a multi-step round is residual_weights applied again to
-    the previous residual; a residual without mass is replaced by p_root
-    (status bit 2) and the round goes on;
+  * the residual of a multi-step round is taken again from the previous
+    residual, max(0, W S_d - W_d S) shifted right by bitlength(S_d) - 1 when
+    W are p_root's own weights (below 2^40, the shift of reject.py) and by
+    one bit more when W is already a residual (below 2^41), so every weight
+    stays below 2^41 and every sum below 2^59; a residual without mass is
+    replaced by p_root (status bit 2) and the round goes on;
   * a child outside [0, V) is skipped: not tested, the residual unchanged,
     status bit 4;
   * with fewer than k finite logits at the root, the greedy children past
@@ -180,6 +183,20 @@ def draft_tree(model, kv, kv_len, root_token, k, D, draft_temp, U_draft, acc=np.
     return tokens, dlogits
 
 
+def _residual(W, S, Wd, Sd, from_p):
+    """max(0, p_c - q) as weights below 2^41: residual_weights' shift for p's
+    own weights (below 2^40), one bit more for a residual (below 2^41)."""
+    if from_p:
+        return residual_weights(W, S, Wd, Sd)
+    shift = max(int(Sd).bit_length() - 1, 0) + 1
+    out = np.zeros(len(W), dtype=np.int64)
+    for j in range(len(W)):
+        d = int(W[j]) * int(Sd) - int(Wd[j]) * int(S)
+        if d > 0:
+            out[j] = d >> shift
+    return out
+
+
 def _onehot(V, x):
     W = np.zeros(V, dtype=np.int64)
     W[x] = 1
@@ -220,7 +237,7 @@ def tree_reject(tlogits, dlogits, tokens, k, D, R, U, temp, draft_temp):
             if accept_test(R[c], W[x], S, Wd[x], Sd):
                 chosen = c
                 break
-            W = residual_weights(W, S, Wd, Sd)
+            W = _residual(W, S, Wd, Sd, W is Wp)
             S = int(W.sum())
             if S == 0:
                 status |= STATUS_ZERO_RESIDUAL

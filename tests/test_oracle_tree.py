@@ -352,3 +352,24 @@ def test_accepted_chain_is_judged_like_its_path():
             n2, out2, st2 = reject(zt[1:], zd[1:], path[2:], Rc[k:], U, T, Td)
             assert (n, out) == (1 + n2, [path[1]] + out2), (T, Td, c)
             assert st == st2 | (STATUS_Q_ZERO if c else 0)
+
+
+def test_residual_weights_stay_below_2_41():
+    # children rejected one after another on a flat row: every residual's
+    # weights stay below 2^41 (their sums below 2^59), and the law stays p
+    from oracle.tree import _residual
+    from oracle.sampling import fixed_weights
+    rng = np.random.default_rng(1)
+    V = 64
+    for trial in range(20):
+        zt = (rng.normal(0, 0.3, V)).astype(np.float32)
+        zd = (zt + rng.normal(0, 0.3, V)).astype(np.float32)
+        W, S = fixed_weights(zt, 1.0)
+        Wp = W
+        Wd, Sd = fixed_weights(zd, 0.5 + trial % 3)
+        for c in range(8):
+            W = _residual(W, S, Wd, Sd, W is Wp)
+            S = int(W.sum())
+            assert W.max() < 1 << 41 and S < 1 << 59
+            if S == 0:
+                break
