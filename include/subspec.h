@@ -13,6 +13,8 @@
  *   [SSR] "SubSpec: the target's own low-bit shadow as the draft" (report),
  *         section 2.2 (4-bit substitutes, sharpened draft), section 3.2
  *         (greedy verification, Table 1).
+ *         Sections 6.3, 6.4, 3.7: SubSpec's static deep/narrow token tree
+ *         (k = 6, D = 48) verified the SpecInfer way.
  *   [SSL] "The second ledger of speculative decoding" (SparseSpec-L blog),
  *         section 3.1 (the draft reads a ~10% index of sink, recent and
  *         important positions, gathered from the dense cache) and section
@@ -48,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SUBSPEC_ABI_VERSION 2
+#define SUBSPEC_ABI_VERSION 3
 
 enum {
   SUBSPEC_OK = 0,
@@ -295,6 +297,68 @@ int subspec_reject_len(int32_t gamma, int32_t vocab, float temp, float draft_tem
                        const int32_t *draft_tokens, const uint32_t *r_codes, const uint32_t *u_code,
                        const int32_t *gamma_len, int32_t *n_accepted, int32_t *out_tokens, int32_t *status,
                        float *probs, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* The static token tree  ([SSR] sections 6.3, 6.4 and 3.7)                  */
+/* ------------------------------------------------------------------------ */
+
+/* SubSpec drafts a static tree, deep and narrow (k = 6, D = 48), and verifies
+ * every path in one target pass (SpecInfer's tree verification).  Reading
+ * (the pages name only k and D): k chains of depth D share the root, the last
+ * committed token tokens[0].  Node t = 1 + c D + d - 1 is chain c's node at
+ * depth d (1 <= d <= D): cache slot kv_len + t, position kv_len + d; it
+ * attends to slots [0, kv_len] and to its own chain's slots up to its own.
+ * The state's buffers hold the tree: tokens [1 + k D] (node order),
+ * draft_logits [1 + k (D - 1)][vocab] (row 0 the root, row
+ * 1 + c (D - 1) + d - 1 chain c's depth-d node).  kv_len + 1 + k D must not
+ * exceed the capacity (checked on the device: a tree that does not fit gets
+ * -1 children, and its round emits one token).  1 <= k <= 16, 1 <= D <= 64,
+ * 1 + k D <= 512; draft weights bf16 or 4-bit.  One cycle: tree_draft for
+ * level 0 .. D - 1, tree_verify, tree_reject, tree_commit. */
+
+/* Workspace bytes of the four calls below (0 on invalid arguments). */
+size_t subspec_tree_workspace_bytes(const subspec_model *m, int32_t k, int32_t depth, int32_t capacity);
+
+/* One draft pass over a level, all chains at once (the 4-bit GEMMs take the
+ * k rows in one weight stream).  Level 0 runs the root and writes its k
+ * children tokens[1 + c D]: its k largest logits when draft_temp == 0
+ * (larger first, lower index first on ties, token 0 past the finite ones),
+ * else k draws with u_codes[c] (inverse CDF, [SD] Module 1, as
+ * subspec_draft_step).  Level d >= 1 runs the depth-d nodes and writes chain
+ * c's next token tokens[1 + c D + d] (argmax, or a draw with
+ * u_codes[k + c (D - 1) + d - 1]).  u_codes: device uint32 [k D]. */
+int subspec_tree_draft(const subspec_model *m, const subspec_state *st, int32_t k, int32_t depth, int32_t level,
+                       float draft_temp, const uint32_t *u_codes, void *ws, size_t ws_bytes, void *stream);
+
+/* The target pass over all 1 + k D nodes (bf16 target weights, tree
+ * visibility); writes their K/V and logits bf16 [1 + k D][vocab]. */
+int subspec_tree_verify(const subspec_model *m, const subspec_state *st, int32_t k, int32_t depth, uint16_t *logits,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/* Judge one tree.  The root: SpecInfer's multi-step rejection over the k
+ * children in chain order - child c accepted when
+ * r_codes[c] / 2^24 < p_c(x_c) / q(x_c), p_0 = softmax(target row 0 / T),
+ * after a rejection p_{c+1} = norm(max(0, p_c - q)), q = softmax(draft row 0
+ * / T_d) (one-hot at x_c when draft_temp == 0); T = 0: the first child equal
+ * to the target's argmax.  No child accepted: one token drawn from the last
+ * p_c with u_code (n = 0).  Child c accepted: chain c's depth-2..D tokens are
+ * judged by the plain round (subspec_reject) over its depth-1..D target rows
+ * and depth-1..D-1 draft rows with r_codes[k ..] and u_code, and
+ * n = 1 + that round's n.  Outputs (device): n_accepted, chain (c, or -1),
+ * out_tokens [n + 1] (room for D + 1), status (subspec_reject's bits; a
+ * child outside the vocabulary is skipped with bit 4).  Integer arithmetic
+ * as subspec_reject; residuals after the first kept below 2^41 by one more
+ * bit of shift.  r_codes: [k + D - 1] (needed when temp > 0). */
+int subspec_tree_reject(int32_t k, int32_t depth, int32_t vocab, float temp, float draft_temp,
+                        const uint16_t *target_logits, const uint16_t *draft_logits, const int32_t *tokens,
+                        const uint32_t *r_codes, const uint32_t *u_code, int32_t *n_accepted, int32_t *chain,
+                        int32_t *out_tokens, int32_t *status, void *ws, size_t ws_bytes, void *stream);
+
+/* Commit a judged tree: the accepted chain's first n nodes' K/V move to
+ * slots kv_len + 1 .. kv_len + n (every layer and KV head), then
+ * kv_len += n + 1 and tokens[0] = out_tokens[n] (as subspec_kv_rollback). */
+int subspec_tree_commit(const subspec_model *m, const subspec_state *st, int32_t k, int32_t depth,
+                        const int32_t *n_accepted, const int32_t *chain, const int32_t *out_tokens, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* Entropy-adaptive draft length  ([SSL] section 3.3)                        */

@@ -108,6 +108,16 @@ _SIGS = {
     "subspec_sample": (c_int32, [c_void_p, c_int32, c_float, c_void_p, c_void_p, c_void_p,
                                  c_size_t, c_void_p]),
     "subspec_hbm_read": (c_int32, [c_void_p, c_int64, c_void_p, c_void_p]),
+    "subspec_tree_workspace_bytes": (c_size_t, [POINTER(Model), c_int32, c_int32, c_int32]),
+    "subspec_tree_draft": (c_int32, [POINTER(Model), POINTER(State), c_int32, c_int32, c_int32, c_float, c_void_p,
+                                     c_void_p, c_size_t, c_void_p]),
+    "subspec_tree_verify": (c_int32, [POINTER(Model), POINTER(State), c_int32, c_int32, c_void_p, c_void_p,
+                                      c_size_t, c_void_p]),
+    "subspec_tree_reject": (c_int32, [c_int32, c_int32, c_int32, c_float, c_float, c_void_p, c_void_p, c_void_p,
+                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_size_t, c_void_p]),
+    "subspec_tree_commit": (c_int32, [POINTER(Model), POINTER(State), c_int32, c_int32, c_void_p, c_void_p,
+                                      c_void_p, c_void_p]),
     "subspec_profile_start": (c_int32, [c_int32]),
     "subspec_profile_stop": (c_int32, []),
     "subspec_profile_read": (c_int32, [c_int32, POINTER(c_int64), POINTER(ctypes.c_double),
@@ -334,6 +344,36 @@ def bf16_gemm(w, x, y, ws, stream=None):
 def sample(logits, temp, u_code, token, ws, stream=None):
     check(lib().subspec_sample(_p(logits), logits.numel(), temp, _p(u_code), _p(token), _p(ws),
                                ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def tree_workspace_bytes(model, k, depth, capacity):
+    n = lib().subspec_tree_workspace_bytes(ctypes.byref(model), k, depth, capacity)
+    if n == 0:
+        raise SubspecError(EINVAL, last_error())
+    return n
+
+
+def tree_draft(model, state, k, depth, level, draft_temp, u_codes, ws, stream=None):
+    check(lib().subspec_tree_draft(ctypes.byref(model), ctypes.byref(state), k, depth, level, draft_temp,
+                                   _p(u_codes), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def tree_verify(model, state, k, depth, logits, ws, stream=None):
+    check(lib().subspec_tree_verify(ctypes.byref(model), ctypes.byref(state), k, depth, _p(logits), _p(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def tree_reject(k, depth, vocab, temp, draft_temp, target_logits, draft_logits, tokens, r_codes, u_code,
+                n_accepted, chain, out_tokens, status, ws, stream=None):
+    check(lib().subspec_tree_reject(k, depth, vocab, temp, draft_temp, _p(target_logits), _p(draft_logits),
+                                    _p(tokens), _p(r_codes), _p(u_code), _p(n_accepted), _p(chain),
+                                    _p(out_tokens), _p(status), _p(ws), ws.numel() * ws.element_size(),
+                                    _stream(stream)))
+
+
+def tree_commit(model, state, k, depth, n_accepted, chain, out_tokens, stream=None):
+    check(lib().subspec_tree_commit(ctypes.byref(model), ctypes.byref(state), k, depth, _p(n_accepted),
+                                    _p(chain), _p(out_tokens), _stream(stream)))
 
 
 def profile_start(max_records=200000):

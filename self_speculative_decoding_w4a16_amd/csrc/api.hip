@@ -51,6 +51,9 @@ constexpr int kMaxRejectBatch = 4096;                   // its counters fill [32
 constexpr size_t kAttnCounterOff = 20 * 1024;  // draft attention: one per query head (<= 224)
 constexpr size_t kControlCounterOff = 16 * 1024 + 512;  // draft-length controller
 constexpr int kMaxTokens = 64;
+constexpr int kMaxTreeK = 16;       // chains of a static tree (rows of a draft level: the 4-bit GEMM's m)
+constexpr int kMaxTreeD = 64;       // depth of a static tree
+constexpr int kMaxTreeRows = 512;   // nodes of one tree's verify pass (1 + k D)
 constexpr int kMaxGemvK = 28672;  // x (2 B) + half-group sums in 64 KiB of LDS
 constexpr int kMaxGamma = 64;
 constexpr int kMaxNormK = 6144;  // 3 items of 8 values per thread, 256 threads
@@ -189,6 +192,7 @@ struct FwdWs {
   uint32_t* sample_counter;
   uint32_t* attn_counters;
   uint16_t *h, *xn, *qkv, *qrot, *attn, *act;
+  uint16_t* gu;  // rows forward on 4-bit weights: gate/up outputs [mt][2F] before SiLU*up
   float* attn_part;
   int part_recs;  // partial records per query head in attn_part
   float* attn_ml;
@@ -209,6 +213,11 @@ size_t max_gemm_partials(const subspec_model* m, int mt) {
   b = std::max(b, gemm_partials_bytes(F, H, mt, GEPI_SILU));
   b = std::max(b, gemm_partials_bytes(H, F, mt, GEPI_RESID));
   b = std::max(b, gemm_partials_bytes(m->vocab, H, mt, GEPI_STORE));
+  if (mt <= 16) {  // a tree level's draft rows on 4-bit weights
+    const int64_t shapes[4][2] = {{qkv, H}, {H, qd}, {2 * F, H}, {H, F}};
+    for (const auto& sh : shapes)
+      b = std::max(b, (size_t)gemm_w4_splits(sh[0], sh[1]) * mt * sh[0] * 4);
+  }
   return b;
 }
 
@@ -227,6 +236,7 @@ size_t carve_fwd(const subspec_model* m, int mt, int cap, void* ws, FwdWs* o) {
   w.qrot = (uint16_t*)c.take((size_t)mt * qd * 2);
   w.attn = (uint16_t*)c.take((size_t)mt * qd * 2);
   w.act = (uint16_t*)c.take((size_t)mt * F * 2);
+  w.gu = (uint16_t*)c.take((size_t)std::min(mt, 16) * 2 * F * 2);
   // attention split partials: verify [Hkv][ceil(cap/128)][mt][G][d + 4],
   // draft step [Hkv][ceil(cap/64)][G][d + 4]
   const size_t vsplits = (cap + decode_attn_keys_per_split() - 1) / decode_attn_keys_per_split();
@@ -263,6 +273,27 @@ size_t carve_reject(int gamma, int vocab, void* ws, RejectWs* o, int batch = 1) 
   return c.off;
 }
 
+// Static tree rejection: every chain's own round (batched, gamma = D - 1),
+// their results, and the root's residual weights.
+struct TreeRejWs {
+  RejectWs r;
+  int32_t* chain_n;
+  int32_t* chain_out;
+  int32_t* chain_status;
+  unsigned long long* resid;
+};
+size_t carve_tree_reject(int k, int D, int vocab, void* ws, TreeRejWs* o) {
+  TreeRejWs t{};
+  size_t off = carve_reject(D - 1, vocab, ws, &t.r, k);
+  Carver c{(char*)ws, off};
+  t.chain_n = (int32_t*)c.take((size_t)k * 4);
+  t.chain_out = (int32_t*)c.take((size_t)k * D * 4);
+  t.chain_status = (int32_t*)c.take((size_t)k * 4);
+  t.resid = (unsigned long long*)c.take((size_t)vocab * 8);
+  if (o) *o = t;
+  return c.off;
+}
+
 int need_ws(void* ws, size_t have, size_t need) {
   if (!ws) return fail(SUBSPEC_EWORKSPACE, "workspace is NULL");
   if (have < need)
@@ -286,9 +317,169 @@ double gemv_bytes(const subspec_linear& l, int64_t n_out, bool resid) {
 double gemm_bytes(int64_t n_phys, int64_t k, int m, int64_t n_out, bool resid) {
   return 2.0 * n_phys * k + 2.0 * m * k + 2.0 * m * n_out * (resid ? 2 : 1);
 }
+double gemm_w4_bytes(int64_t n_phys, int64_t k, int m, int64_t n_out, bool resid) {
+  return (double)n_phys * k * (0.5 + 4.0 / 64) + 2.0 * m * k + 2.0 * m * n_out * (resid ? 2 : 1);
+}
 // site: 0 qkv, 1 o, 2 gate_up, 3 down
 int gemv_class(const subspec_linear& l, int site) {
   return (lin_is_w4(l) ? SUBSPEC_K_W4_QKV : SUBSPEC_K_BF16_QKV) + site;
+}
+
+// Rows of one forward pass over the shared cache: the verify pass (gamma + 1
+// or a prefill chunk of consecutive positions), a static tree's verify pass
+// (all its nodes) and a tree's draft level (one node per chain, on the draft
+// weights).  Row j takes the token tokens[j * tok_stride] and is node
+// node0 + j * node_stride (AttnArgs: slot, position and visible keys).
+struct RowsSpec {
+  const int32_t* tokens;
+  int tok_stride;
+  int m;
+  int node0, node_stride, tree_d;
+  bool draft;        // draft weights: bf16 shared layers, 4-bit substitutes on the matrix cores (m <= 16)
+  uint16_t* logits;  // [m][ld] or NULL
+  int64_t ld;
+};
+
+int rows_forward(const subspec_model* m, const subspec_state* st, const RowsSpec& rs, void* ws, hipStream_t s) {
+  FwdWs w;
+  carve_fwd(m, rs.m, st->capacity, ws, &w);
+  const int64_t H = m->hidden, F = m->ffn, d = m->head_dim;
+  const int64_t qd = (int64_t)m->n_q_heads * d;
+  const int64_t qkv = (int64_t)(m->n_q_heads + 2 * m->n_kv_heads) * d;
+  const int mt = rs.m;
+  {
+    prof::Scope ps(SUBSPEC_K_MISC, 0.0, s);
+    HIPCHK(launch_embed_rows(m->embed, rs.tokens, mt, (int)H, m->vocab, w.h, s, rs.tok_stride));
+    HIPCHK(launch_rope_table(st->kv_len, rs.node0, rs.node_stride, rs.tree_d, mt, (int)d, m->rope_theta, w.rope_cs,
+                             s));
+  }
+  // Narrow GEMMs (QKV, O, down) split k over blocks and leave fp32 partial
+  // sums; their consumers add them: RoPE for QKV, the residual + RMSNorm
+  // kernel for O and down (h = bf16(h + sum), then the next norm).  The
+  // 4-bit GEMM always leaves partials (also for one split).
+  const float* pend = nullptr;  // partial sums still to be added to h
+  int pend_splits = 0;
+  auto norm_into_xn = [&](const uint16_t* g) -> hipError_t {
+    const hipError_t e = launch_resid_rmsnorm_rows(w.h, pend, pend_splits, g, m->rms_eps, mt, (int)H, w.xn, s);
+    pend = nullptr;
+    pend_splits = 0;
+    return e;
+  };
+  for (int l = 0; l < m->n_layers; ++l) {
+    const subspec_layer& L = m->layers[l];
+    const subspec_linear& lq = rs.draft ? L.qkv_d : L.qkv;
+    const subspec_linear& lo = rs.draft ? L.o_d : L.o;
+    const subspec_linear& lg = rs.draft ? L.gate_up_d : L.gate_up;
+    const subspec_linear& ldn = rs.draft ? L.down_d : L.down;
+    {
+      prof::Scope ps(SUBSPEC_K_MISC, 0.0, s);
+      HIPCHK(norm_into_xn(L.attn_norm));
+    }
+    int q_splits = 1;
+    bool q_part = false;
+    if (lin_is_w4(lq)) {
+      prof::Scope ps(SUBSPEC_K_W4_QKV, gemm_w4_bytes(qkv, H, mt, qkv, false), s);
+      HIPCHK(launch_gemm_w4(lq.codes, lq.meta, qkv, H, w.xn, mt, w.qkv, w.gemm_part, s, &q_splits));
+      q_part = true;
+    } else {
+      GemmArgs q{lq.w, qkv, H, w.xn, mt, w.qkv, qkv, nullptr, w.gemm_part};
+      prof::Scope ps(SUBSPEC_K_GEMM_QKV, gemm_bytes(qkv, H, mt, qkv, false), s);
+      HIPCHK(launch_gemm(GEPI_STORE, q, s, &q_splits));
+      q_part = q_splits > 1;
+    }
+    AttnArgs at{};
+    at.qkv = w.qkv;
+    if (q_part) {
+      at.qkv_part = w.gemm_part;
+      at.qkv_splits = q_splits;
+    }
+    at.q_rot = w.qrot;
+    at.k_cache = st->k_cache + (int64_t)l * m->n_kv_heads * st->capacity * d;
+    at.v_cache = st->v_cache + (int64_t)l * m->n_kv_heads * st->capacity * d;
+    at.kv_len = st->kv_len;
+    at.pos_offset = rs.node0;
+    at.row_stride = rs.node_stride;
+    at.tree_d = rs.tree_d;
+    at.m = mt;
+    at.n_q = m->n_q_heads;
+    at.n_kv = m->n_kv_heads;
+    at.d = (int)d;
+    at.cap = st->capacity;
+    at.theta = m->rope_theta;
+    at.rope_cs = w.rope_cs;
+    at.part = w.attn_part;
+    at.out = w.attn;
+    at.split_keys = verify_attn_split_keys(st->capacity, m->n_kv_heads, mt * (m->n_q_heads / m->n_kv_heads));
+    at.splits = (st->capacity + at.split_keys - 1) / at.split_keys;
+    const bool scores = st->kv_score && !rs.draft && rs.tree_d == 0;
+    if (scores) at.ml = w.attn_ml;
+    {
+      prof::Scope ps(SUBSPEC_K_ATTN_VERIFY, 0.0, s);
+      HIPCHK(launch_rope_append(at, s));
+      HIPCHK(launch_rows_attention(at, s));
+    }
+    if (scores) {
+      prof::Scope ps(SUBSPEC_K_SCORES, 0.0, s);
+      HIPCHK(launch_attn_scores(at, st->kv_score + (int64_t)l * m->n_kv_heads * st->capacity,
+                                st->score_window, s));
+    }
+    if (lin_is_w4(lo)) {
+      prof::Scope ps(SUBSPEC_K_W4_O, gemm_w4_bytes(H, qd, mt, H, true), s);
+      HIPCHK(launch_gemm_w4(lo.codes, lo.meta, H, qd, w.attn, mt, w.h, w.gemm_part, s, &pend_splits));
+      pend = w.gemm_part;
+    } else {
+      GemmArgs o{lo.w, H, qd, w.attn, mt, w.h, H, w.h, w.gemm_part};
+      prof::Scope ps(SUBSPEC_K_GEMM_O, gemm_bytes(H, qd, mt, H, true), s);
+      HIPCHK(launch_gemm(GEPI_RESID, o, s, &pend_splits));
+      if (pend_splits > 1) pend = w.gemm_part;
+    }
+    {
+      prof::Scope ps(SUBSPEC_K_MISC, 0.0, s);
+      HIPCHK(norm_into_xn(L.ffn_norm));
+    }
+    if (lin_is_w4(lg)) {
+      prof::Scope ps(SUBSPEC_K_W4_GATE_UP, gemm_w4_bytes(2 * F, H, mt, F, false), s);
+      HIPCHK(launch_gemm_w4(lg.codes, lg.meta, 2 * F, H, w.xn, mt, w.gu, w.gemm_part, s));
+      HIPCHK(launch_silu_rows(w.gu, F, mt, w.act, s));
+    } else {
+      GemmArgs g{lg.w, F, H, w.xn, mt, w.act, F, nullptr, w.gemm_part};
+      prof::Scope ps(SUBSPEC_K_GEMM_GATE_UP, gemm_bytes(2 * F, H, mt, F, false), s);
+      HIPCHK(launch_gemm(GEPI_SILU, g, s, nullptr));
+    }
+    if (lin_is_w4(ldn)) {
+      prof::Scope ps(SUBSPEC_K_W4_DOWN, gemm_w4_bytes(H, F, mt, H, true), s);
+      HIPCHK(launch_gemm_w4(ldn.codes, ldn.meta, H, F, w.act, mt, w.h, w.gemm_part, s, &pend_splits));
+      pend = w.gemm_part;
+    } else {
+      GemmArgs dn{ldn.w, H, F, w.act, mt, w.h, H, w.h, w.gemm_part};
+      prof::Scope ps(SUBSPEC_K_GEMM_DOWN, gemm_bytes(H, F, mt, H, true), s);
+      HIPCHK(launch_gemm(GEPI_RESID, dn, s, &pend_splits));
+      if (pend_splits > 1) pend = w.gemm_part;
+    }
+  }
+  if (rs.logits) {
+    {
+      prof::Scope ps(SUBSPEC_K_MISC, 0.0, s);
+      HIPCHK(norm_into_xn(m->final_norm));
+    }
+    GemmArgs lm{m->lm_head, m->vocab, H, w.xn, mt, rs.logits, rs.ld, nullptr, w.gemm_part};
+    int lm_splits = 1;
+    prof::Scope ps(SUBSPEC_K_GEMM_LM_HEAD, gemm_bytes(m->vocab, H, mt, m->vocab, false), s);
+    HIPCHK(launch_gemm(GEPI_STORE, lm, s, &lm_splits));
+    if (lm_splits > 1) HIPCHK(launch_gemm_reduce(w.gemm_part, lm_splits, mt, m->vocab, rs.logits, rs.ld, s));
+  }
+  return ok();
+}
+
+// 4-bit substitutes only (the draft rows' GEMM on the matrix cores)
+int check_tree_draft_weights(const subspec_model* m) {
+  for (int l = 0; l < m->n_layers; ++l) {
+    const subspec_layer& L = m->layers[l];
+    for (const subspec_linear* x : {&L.qkv_d, &L.o_d, &L.gate_up_d, &L.down_d})
+      if (lin_is_w4(*x) && lin_bits(*x) != 4)
+        return fail(SUBSPEC_EUNSUPPORTED, "layer %d: tree drafting takes bf16 or 4-bit draft weights", l);
+  }
+  return SUBSPEC_OK;
 }
 
 }  // namespace
@@ -515,107 +706,139 @@ int subspec_verify(const subspec_model* m, const subspec_state* st, int32_t n_to
     return fail(SUBSPEC_EINVAL, "n_tokens %d outside [1, %d]", n_tokens, kMaxTokens);
   if (n_tokens > st->capacity) return fail(SUBSPEC_ECAPACITY, "n_tokens above the KV capacity");
   if ((r = need_ws(ws, ws_bytes, carve_fwd(m, n_tokens, st->capacity, nullptr, nullptr)))) return r;
-  FwdWs w;
-  carve_fwd(m, n_tokens, st->capacity, ws, &w);
+  RowsSpec rs{};
+  rs.tokens = tokens;
+  rs.tok_stride = 1;
+  rs.m = n_tokens;
+  rs.node0 = 0;
+  rs.node_stride = 1;
+  rs.tree_d = 0;
+  rs.draft = false;
+  rs.logits = logits;
+  rs.ld = m->vocab;
+  return rows_forward(m, st, rs, ws, hs(stream));
+}
+
+static int check_tree(int32_t k, int32_t D) {
+  if (k < 1 || k > kMaxTreeK) return fail(SUBSPEC_EINVAL, "tree width k = %d outside [1, %d]", k, kMaxTreeK);
+  if (D < 1 || D > kMaxTreeD) return fail(SUBSPEC_EINVAL, "tree depth %d outside [1, %d]", D, kMaxTreeD);
+  if (1 + k * D > kMaxTreeRows)
+    return fail(SUBSPEC_EINVAL, "tree of %d nodes above %d", 1 + k * D, kMaxTreeRows);
+  return SUBSPEC_OK;
+}
+
+size_t subspec_tree_workspace_bytes(const subspec_model* m, int32_t k, int32_t depth, int32_t capacity) {
+  if (check_model(m) || check_tree(k, depth)) return 0;
+  if (capacity < 1) {
+    fail(SUBSPEC_ECAPACITY, "capacity must be >= 1");
+    return 0;
+  }
+  size_t b = carve_fwd(m, 1 + k * depth, capacity, nullptr, nullptr);
+  b = std::max(b, carve_fwd(m, k, capacity, nullptr, nullptr));
+  b = std::max(b, carve_tree_reject(k, depth, m->vocab, nullptr, nullptr));
+  ok();
+  return b;
+}
+
+int subspec_tree_draft(const subspec_model* m, const subspec_state* st, int32_t k, int32_t depth, int32_t level,
+                       float draft_temp, const uint32_t* u_codes, void* ws, size_t ws_bytes, void* stream) {
+  int r;
+  if ((r = check_model(m)) || (r = check_state(m, st)) || (r = check_tree(k, depth)) ||
+      (r = check_tree_draft_weights(m)))
+    return r;
+  if (!st->draft_logits) return fail(SUBSPEC_EINVAL, "state.draft_logits must be set");
+  if (level < 0 || level >= depth) return fail(SUBSPEC_EINVAL, "level %d outside [0, depth = %d)", level, depth);
+  if (!(draft_temp >= 0.0f)) return fail(SUBSPEC_EINVAL, "draft_temp must be >= 0");
+  if (draft_temp > 0.0f && !u_codes) return fail(SUBSPEC_EINVAL, "u_codes needed when draft_temp > 0");
+  if (1 + k * depth > st->capacity) return fail(SUBSPEC_ECAPACITY, "a tree of %d nodes above the KV capacity", 1 + k * depth);
+  const int rows = level == 0 ? 1 : k;
+  if ((r = need_ws(ws, ws_bytes, carve_fwd(m, rows, st->capacity, nullptr, nullptr)))) return r;
   hipStream_t s = hs(stream);
-  const int64_t H = m->hidden, F = m->ffn, d = m->head_dim;
-  const int64_t qd = (int64_t)m->n_q_heads * d;
-  const int64_t qkv = (int64_t)(m->n_q_heads + 2 * m->n_kv_heads) * d;
-  const int mt = n_tokens;
+  RowsSpec rs{};
+  rs.m = rows;
+  rs.draft = true;
+  rs.tree_d = depth;
+  if (level == 0) {  // the root
+    rs.tokens = st->tokens;
+    rs.tok_stride = 1;
+    rs.node0 = 0;
+    rs.node_stride = 1;
+    rs.logits = st->draft_logits;
+    rs.ld = m->vocab;
+  } else {  // depth `level` of every chain: nodes level + c D, draft rows level + c (D - 1)
+    rs.tokens = st->tokens + level;
+    rs.tok_stride = depth;
+    rs.node0 = level;
+    rs.node_stride = depth;
+    rs.logits = st->draft_logits + (int64_t)level * m->vocab;
+    rs.ld = (int64_t)(depth - 1) * m->vocab;
+  }
+  if ((r = rows_forward(m, st, rs, ws, s))) return r;
   {
-    prof::Scope ps(SUBSPEC_K_MISC, 0.0, s);
-    HIPCHK(launch_embed_rows(m->embed, tokens, mt, (int)H, m->vocab, w.h, s));
-    HIPCHK(launch_rope_table(st->kv_len, 0, mt, (int)d, m->rope_theta, w.rope_cs, s));
+    prof::Scope ps(SUBSPEC_K_SAMPLE, 2.0 * rows * m->vocab, s);
+    HIPCHK(launch_tree_sample(rs.logits, rs.ld, rows, m->vocab, draft_temp, u_codes, level, k, depth, st->kv_len,
+                              st->capacity, st->tokens, s));
   }
-  // Narrow GEMMs (QKV, O, down) split k over blocks and leave fp32 partial
-  // sums; their consumers add them: RoPE for QKV, the residual + RMSNorm
-  // kernel for O and down (h = bf16(h + sum), then the next norm).
-  const float* pend = nullptr;  // partial sums still to be added to h
-  int pend_splits = 0;
-  auto norm_into_xn = [&](const uint16_t* g) -> hipError_t {
-    const hipError_t e = launch_resid_rmsnorm_rows(w.h, pend, pend_splits, g, m->rms_eps, mt, (int)H, w.xn, s);
-    pend = nullptr;
-    pend_splits = 0;
-    return e;
-  };
-  for (int l = 0; l < m->n_layers; ++l) {
-    const subspec_layer& L = m->layers[l];
-    {
-      prof::Scope ps(SUBSPEC_K_MISC, 0.0, s);
-      HIPCHK(norm_into_xn(L.attn_norm));
-    }
-    GemmArgs q{L.qkv.w, qkv, H, w.xn, mt, w.qkv, qkv, nullptr, w.gemm_part};
-    int q_splits = 1;
-    {
-      prof::Scope ps(SUBSPEC_K_GEMM_QKV, gemm_bytes(qkv, H, mt, qkv, false), s);
-      HIPCHK(launch_gemm(GEPI_STORE, q, s, &q_splits));
-    }
-    AttnArgs at{};
-    at.qkv = w.qkv;
-    if (q_splits > 1) {
-      at.qkv_part = w.gemm_part;
-      at.qkv_splits = q_splits;
-    }
-    at.q_rot = w.qrot;
-    at.k_cache = st->k_cache + (int64_t)l * m->n_kv_heads * st->capacity * d;
-    at.v_cache = st->v_cache + (int64_t)l * m->n_kv_heads * st->capacity * d;
-    at.kv_len = st->kv_len;
-    at.pos_offset = 0;
-    at.m = mt;
-    at.n_q = m->n_q_heads;
-    at.n_kv = m->n_kv_heads;
-    at.d = (int)d;
-    at.cap = st->capacity;
-    at.theta = m->rope_theta;
-    at.rope_cs = w.rope_cs;
-    at.part = w.attn_part;
-    at.out = w.attn;
-    at.split_keys = verify_attn_split_keys(st->capacity, m->n_kv_heads, mt * (m->n_q_heads / m->n_kv_heads));
-    at.splits = (st->capacity + at.split_keys - 1) / at.split_keys;
-    if (st->kv_score) at.ml = w.attn_ml;
-    {
-      prof::Scope ps(SUBSPEC_K_ATTN_VERIFY, 0.0, s);
-      HIPCHK(launch_rope_append(at, s));
-      HIPCHK(launch_rows_attention(at, s));
-    }
-    if (st->kv_score) {
-      prof::Scope ps(SUBSPEC_K_SCORES, 0.0, s);
-      HIPCHK(launch_attn_scores(at, st->kv_score + (int64_t)l * m->n_kv_heads * st->capacity,
-                                st->score_window, s));
-    }
-    GemmArgs o{L.o.w, H, qd, w.attn, mt, w.h, H, w.h, w.gemm_part};
-    {
-      prof::Scope ps(SUBSPEC_K_GEMM_O, gemm_bytes(H, qd, mt, H, true), s);
-      HIPCHK(launch_gemm(GEPI_RESID, o, s, &pend_splits));
-    }
-    if (pend_splits > 1) pend = w.gemm_part;
-    {
-      prof::Scope ps(SUBSPEC_K_MISC, 0.0, s);
-      HIPCHK(norm_into_xn(L.ffn_norm));
-    }
-    GemmArgs g{L.gate_up.w, F, H, w.xn, mt, w.act, F, nullptr, w.gemm_part};
-    {
-      prof::Scope ps(SUBSPEC_K_GEMM_GATE_UP, gemm_bytes(2 * F, H, mt, F, false), s);
-      HIPCHK(launch_gemm(GEPI_SILU, g, s, nullptr));
-    }
-    GemmArgs dn{L.down.w, H, F, w.act, mt, w.h, H, w.h, w.gemm_part};
-    {
-      prof::Scope ps(SUBSPEC_K_GEMM_DOWN, gemm_bytes(H, F, mt, H, true), s);
-      HIPCHK(launch_gemm(GEPI_RESID, dn, s, &pend_splits));
-    }
-    if (pend_splits > 1) pend = w.gemm_part;
-  }
-  if (logits) {
-    {
-      prof::Scope ps(SUBSPEC_K_MISC, 0.0, s);
-      HIPCHK(norm_into_xn(m->final_norm));
-    }
-    GemmArgs lm{m->lm_head, m->vocab, H, w.xn, mt, logits, m->vocab, nullptr, w.gemm_part};
-    int lm_splits = 1;
-    prof::Scope ps(SUBSPEC_K_GEMM_LM_HEAD, gemm_bytes(m->vocab, H, mt, m->vocab, false), s);
-    HIPCHK(launch_gemm(GEPI_STORE, lm, s, &lm_splits));
-    if (lm_splits > 1) HIPCHK(launch_gemm_reduce(w.gemm_part, lm_splits, mt, m->vocab, logits, m->vocab, s));
-  }
+  return ok();
+}
+
+int subspec_tree_verify(const subspec_model* m, const subspec_state* st, int32_t k, int32_t depth, uint16_t* logits,
+                        void* ws, size_t ws_bytes, void* stream) {
+  int r;
+  if ((r = check_model(m)) || (r = check_state(m, st)) || (r = check_tree(k, depth))) return r;
+  if (!logits) return fail(SUBSPEC_EINVAL, "logits is NULL");
+  const int n = 1 + k * depth;
+  if (n > st->capacity) return fail(SUBSPEC_ECAPACITY, "a tree of %d nodes above the KV capacity", n);
+  if ((r = need_ws(ws, ws_bytes, carve_fwd(m, n, st->capacity, nullptr, nullptr)))) return r;
+  RowsSpec rs{};
+  rs.tokens = st->tokens;
+  rs.tok_stride = 1;
+  rs.m = n;
+  rs.node0 = 0;
+  rs.node_stride = 1;
+  rs.tree_d = depth;
+  rs.draft = false;
+  rs.logits = logits;
+  rs.ld = m->vocab;
+  return rows_forward(m, st, rs, ws, hs(stream));
+}
+
+int subspec_tree_reject(int32_t k, int32_t depth, int32_t vocab, float temp, float draft_temp,
+                        const uint16_t* target_logits, const uint16_t* draft_logits, const int32_t* tokens,
+                        const uint32_t* r_codes, const uint32_t* u_code, int32_t* n_accepted, int32_t* chain,
+                        int32_t* out_tokens, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  int r;
+  if ((r = check_tree(k, depth))) return r;
+  if (vocab < 1 || vocab > (1 << 24)) return fail(SUBSPEC_EINVAL, "vocab outside [1, 2^24]");
+  if (!(temp >= 0.0f) || !(draft_temp >= 0.0f)) return fail(SUBSPEC_EINVAL, "temperatures must be >= 0");
+  if (!target_logits || !draft_logits || !tokens || !n_accepted || !chain || !out_tokens || !status)
+    return fail(SUBSPEC_EINVAL, "NULL buffer");
+  if (temp > 0.0f && (!r_codes || !u_code)) return fail(SUBSPEC_EINVAL, "r_codes and u_code needed when temp > 0");
+  TreeRejWs t;
+  if ((r = need_ws(ws, ws_bytes, carve_tree_reject(k, depth, vocab, nullptr, nullptr)))) return r;
+  carve_tree_reject(k, depth, vocab, ws, &t);
+  hipStream_t s = hs(stream);
+  prof::Scope ps(SUBSPEC_K_REJECT, 0.0, s);
+  // every chain's own round over its depth-1..D target rows and depth-1..D-1
+  // draft rows (the draft tokens of depths 2..D), sharing r_codes[k..] and u
+  HIPCHK(launch_reject(depth - 1, vocab, temp, draft_temp, target_logits + vocab, draft_logits + vocab, tokens + 2,
+                       r_codes ? r_codes + k : nullptr, u_code, t.chain_n, t.chain_out, t.chain_status, nullptr, t.r,
+                       s, nullptr, k, depth, 0, 0));
+  HIPCHK(launch_tree_root(target_logits, draft_logits, vocab, temp, draft_temp, tokens, k, depth, r_codes, u_code,
+                          t.chain_n, t.chain_out, t.chain_status, t.resid, n_accepted, chain, out_tokens, status, s));
+  return ok();
+}
+
+int subspec_tree_commit(const subspec_model* m, const subspec_state* st, int32_t k, int32_t depth,
+                        const int32_t* n_accepted, const int32_t* chain, const int32_t* out_tokens, void* stream) {
+  int r;
+  if ((r = check_model(m)) || (r = check_state(m, st)) || (r = check_tree(k, depth))) return r;
+  if (!n_accepted || !chain || !out_tokens) return fail(SUBSPEC_EINVAL, "NULL buffer");
+  hipStream_t s = hs(stream);
+  prof::Scope ps(SUBSPEC_K_MISC, 0.0, s);
+  HIPCHK(launch_tree_commit(st->k_cache, st->v_cache, m->n_layers * m->n_kv_heads, st->capacity, m->head_dim,
+                            st->kv_len, n_accepted, chain, depth, s));
+  HIPCHK(launch_kv_rollback(st->kv_len, st->tokens, n_accepted, out_tokens, s));
   return ok();
 }
 

@@ -26,6 +26,17 @@ namespace {
 
 constexpr int D = 128;     // head dim handled by these kernels
 
+// Row j of a rows launch (verify pass, tree levels) is node
+// t = pos_offset + j * row_stride at slot kv_len + t (AttnArgs).
+__device__ __forceinline__ int row_node(const AttnArgs& a, int j) {
+  return a.pos_offset + j * (a.row_stride > 1 ? a.row_stride : 1);
+}
+// Lowest slot of node t's own chain in the static tree (tree_d > 0); node t
+// sees slots <= kv_len and those from this one up to its own.  0 in a chain.
+__device__ __forceinline__ int chain_lo(const AttnArgs& a, int kvl, int t) {
+  return (a.tree_d > 0 && t > 0) ? kvl + 1 + ((t - 1) / a.tree_d) * a.tree_d : 0;
+}
+
 // RoPE + KV append of the verify rows: grid (row, head), 64 threads (pair
 // index i: values i and i + d/2).  With split-k partials of the QKV GEMM
 // (S of them; S < 0: a loop) the values are their sums in split order; every
@@ -88,7 +99,7 @@ __global__ __launch_bounds__(64) void rope_append_kernel(AttnArgs a) {
     o[i] = r0;
     o[i + half] = r1;
   } else {
-    const int pos = kvl + a.pos_offset + j;
+    const int pos = kvl + row_node(a, j);  // the row's slot
     if (pos < 0 || pos >= a.cap) return;
     uint16_t* kc = a.k_cache + ((int64_t)hk * a.cap + pos) * a.d;
     uint16_t* vc = a.v_cache + ((int64_t)hk * a.cap + pos) * a.d;
@@ -156,7 +167,8 @@ __global__ __launch_bounds__(RW * 64) void rows_attn_kernel(AttnArgs a) {
   const int n_tiles = (Qn + 15) / 16;
   // kv_len is read first and used after the tile loads are issued: the K/V
   // rows are clamped to the cache (not to kv_len) and masked when staged
-  const int kv0 = *a.kv_len + a.pos_offset;  // position of row 0
+  const int kvl = *a.kv_len;
+  const int kv0 = kvl + a.pos_offset;  // slot of row 0
 
   // A operand of a query tile: lane -> query 16 t + r16, dims 32 s + 8 g4 .. +7
   auto load_q = [&](int t, u32x4 (&qa)[4]) {
@@ -190,7 +202,7 @@ __global__ __launch_bounds__(RW * 64) void rows_attn_kernel(AttnArgs a) {
         v2[i][u] = reinterpret_cast<const u32x4*>(a.v_cache + row * D)[q];
       }
     }
-    const int n_keys = min(kv0 + a.m, a.cap);  // keys of the last row in range
+    const int n_keys = min(kvl + row_node(a, a.m - 1) + 1, a.cap);  // keys of the last row in range
     if (kv0 < 0 || n_keys <= 0 || split >= (n_keys + DKPB - 1) / DKPB) return;  // block-uniform
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -230,7 +242,7 @@ __global__ __launch_bounds__(RW * 64) void rows_attn_kernel(AttnArgs a) {
                                                         __builtin_bit_cast(bf16x8_t, b), sa[n], 0, 0, 0);
       }
     }
-    // causal mask, row max / sum; this lane's queries are 16 t + 4 g4 + i
+    // causal (or tree) mask, row max / sum; this lane's queries are 16 t + 4 g4 + i
     float mx[4], sm[4];
     int qrow[4];
     bool qv[4];
@@ -239,12 +251,15 @@ __global__ __launch_bounds__(RW * 64) void rows_attn_kernel(AttnArgs a) {
       const int qi = 16 * t + 4 * g4 + i;
       qv[i] = qi < Qn;
       qrow[i] = qv[i] ? qi / G : 0;
-      const int last_key = kv0 + qrow[i];  // this row's own position
+      const int tn = row_node(a, qrow[i]);
+      const int last_key = kvl + tn;  // this row's own slot
+      const int lo = chain_lo(a, kvl, tn);
       qv[i] = qv[i] && last_key < a.cap && k0 <= last_key;
       float m = -INFINITY;
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        const bool ok = qv[i] && k0 + 16 * n + r16 <= last_key;
+        const int key = k0 + 16 * n + r16;
+        const bool ok = qv[i] && key <= last_key && (key <= kvl || key >= lo);
         sa[n][i] = ok ? sa[n][i] * scale : -INFINITY;
         m = fmaxf(m, sa[n][i]);
       }
@@ -1019,8 +1034,9 @@ __global__ __launch_bounds__(RW * 64) void rows_attn_long_kernel(AttnArgs a) {
     }
   };
   load_tile(0);
-  const int kv0 = *a.kv_len + a.pos_offset;  // position of row 0
-  const int n_keys = min(kv0 + a.m, a.cap);
+  const int kvl = *a.kv_len;
+  const int kv0 = kvl + a.pos_offset;  // slot of row 0
+  const int n_keys = min(kvl + row_node(a, a.m - 1) + 1, a.cap);
   if (kv0 < 0 || n_keys <= kbase) return;  // block-uniform
   const int n_tau = min(a.split_keys / DKPB, (n_keys - kbase + DKPB - 1) / DKPB);
 
@@ -1081,12 +1097,15 @@ __global__ __launch_bounds__(RW * 64) void rows_attn_long_kernel(AttnArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int qi = 16 * t + 4 * g4 + i;
       const bool qv = qi < Qn;
-      const int last_key = kv0 + (qv ? qi / G : 0);
+      const int tn = row_node(a, qv ? qi / G : 0);
+      const int last_key = kvl + tn;
+      const int lo = chain_lo(a, kvl, tn);
       const bool any = qv && last_key < a.cap && k0 <= last_key;
       float m = -INFINITY;
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        const bool ok = any && k0 + 16 * n + r16 <= last_key;
+        const int key = k0 + 16 * n + r16;
+        const bool ok = any && key <= last_key && (key <= kvl || key >= lo);
         sa[n][i] = ok ? sa[n][i] * scale : -INFINITY;
         m = fmaxf(m, sa[n][i]);
       }
@@ -1144,12 +1163,15 @@ __global__ __launch_bounds__(RW * 64) void rows_attn_long_kernel(AttnArgs a) {
     }
   }
   if (!has_q) return;
-  // partials of this lane's rows (every row has a key in each split up to its own)
+  // partials of this lane's rows whose own slot is at or past this split (the
+  // merge reads every split up to the row's slot; in a tree a split can hold
+  // only other chains' keys: then the partial is (-inf, 0, 0))
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int qi = 16 * t + 4 * g4 + i;
-    if (qi >= Qn || Mr[i] == -INFINITY) continue;
+    if (qi >= Qn) continue;
     const int row = qi / G, h = qi % G;
+    if (kvl + row_node(a, row) < kbase) continue;
     float* dst = a.part + (((int64_t)(hk * a.splits + split) * a.m + row) * G + h) * DREC;
 #pragma unroll
     for (int n = 0; n < NT; ++n) dst[4 + 16 * n + r16] = O[n][i];
@@ -1180,7 +1202,7 @@ __global__ __launch_bounds__(128) void rows_merge_seq_kernel(AttnArgs a) {
     }
   };
   load(0);
-  const int pos = *a.kv_len + a.pos_offset + row;
+  const int pos = *a.kv_len + row_node(a, row);  // the row's slot: its last key
   if (pos < 0 || pos >= a.cap) return;
   const int kps = a.split_keys > 0 ? a.split_keys : DKPB;
   const int active = (pos + kps) / kps;
@@ -1220,7 +1242,7 @@ __global__ __launch_bounds__(128) void rows_merge_seq_kernel(AttnArgs a) {
 __global__ __launch_bounds__(MP * D) void rows_merge_kernel(AttnArgs a) {
   const int hq = blockIdx.x, row = blockIdx.y, dd = threadIdx.x % D, p = threadIdx.x / D;
   const int G = a.n_q / a.n_kv, hk = hq / G, g = hq % G;
-  const int pos = *a.kv_len + a.pos_offset + row;
+  const int pos = *a.kv_len + row_node(a, row);  // the row's slot: its last key
   if (pos < 0 || pos >= a.cap) return;
   const int kps = a.split_keys > 0 ? a.split_keys : DKPB;
   const int active = (pos + kps) / kps;

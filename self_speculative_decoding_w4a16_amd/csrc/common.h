@@ -131,4 +131,16 @@ __device__ __forceinline__ unsigned long long shr128(U128 a, int s) {  // result
   return (a.lo >> s) | (a.hi << (64 - s));
 }
 
+// Residual weight max(0, Wt*Sd - Wd*St) >> shift (exact, 128-bit products).
+__device__ __forceinline__ unsigned long long resid_w(unsigned long long Wt, unsigned long long Sd,
+                                                      unsigned long long Wd, unsigned long long St,
+                                                      int shift) {
+  const U128 a = mul64(Wt, Sd), b = mul64(Wd, St);
+  if (!lt128(b, a)) return 0ull;
+  return shr128(sub128(a, b), shift);
+}
+
+// bit length of v minus one; 0 for v = 0 (a draft row without mass)
+__device__ __forceinline__ int bitlen_minus1(unsigned long long v) { return v ? 63 - __clzll(v) : 0; }
+
 }  // namespace ss

@@ -52,9 +52,10 @@ constexpr int kNonTemporal = 2;           // buffer load cache policy: nt (strea
 
 struct Plan {
   int64_t groups;  // row groups (blocks along n)
-  int tt;          // position tiles
+  int tt;          // position tiles of one slice
   int splits;      // k splits (blocks along k)
   int nw;          // waves per block
+  int slices;      // slices of 64 positions (grid z; more than 64 positions: a tree's verify pass)
 };
 
 // Waves per block.  Small blocks (2 waves) keep many independent blocks in
@@ -80,14 +81,17 @@ int64_t rows_per_group(int64_t n, int epi, int m) {
 
 Plan make_plan(int64_t n, int64_t k, int m, int epi) {
   Plan p;
-  p.tt = (m + 15) / 16;
-  p.nw = block_waves(n, epi, m);
-  const int64_t rg = rows_per_group(n, epi, m);
+  const int ms = std::min(m, 64);  // positions of one slice
+  p.slices = (m + 63) / 64;
+  p.tt = (ms + 15) / 16;
+  p.nw = block_waves(n, epi, ms);
+  const int64_t rg = rows_per_group(n, epi, ms);
   p.groups = (n + rg - 1) / rg;
   const int chunks = (int)(k / KC);
+  const int64_t blocks = p.groups * p.slices;
   p.splits = 1;
-  if (epi != GEPI_SILU && p.groups < kTargetBlocks)
-    p.splits = (int)std::min<int64_t>(chunks, (kTargetBlocks + p.groups - 1) / p.groups);
+  if (epi != GEPI_SILU && blocks < kTargetBlocks)
+    p.splits = (int)std::min<int64_t>(chunks, (kTargetBlocks + blocks - 1) / blocks);
   return p;
 }
 
@@ -106,6 +110,9 @@ __global__ __launch_bounds__(NWR * SS_WAVE) void gemm_kernel(GemmArgs a, int spl
   const int chunks = K / KC;
   const int split = blockIdx.y;
   const int c0 = (int)((int64_t)chunks * split / splits), c1 = (int)((int64_t)chunks * (split + 1) / splits);
+  // this block's slice of at most 64 positions (rows of x and y)
+  const int zrow = blockIdx.z * 64;
+  const int mz = min(64, a.m - zrow);
 
   // this wave's 16 weight rows
   int64_t row0;  // first physical row of the tile
@@ -126,8 +133,8 @@ __global__ __launch_bounds__(NWR * SS_WAVE) void gemm_kernel(GemmArgs a, int spl
   const int rows = (int)std::max<int64_t>(0, std::min<int64_t>(16, a.n - out0));
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.w + row0 * (int64_t)K), 0, rows * K * 2, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t xrs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.x), 0, a.m * K * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.x + (int64_t)zrow * K), 0, mz * K * 2, kBufferWord3);
   // lane l loads row 4 s + l / 16 (load s), bytes 16 (l % 16) .. +15 of the chunk
   const int wlane = ((lane >> 4) * K + 8 * (lane & 15)) * 2;
   auto chunk_off = [&](int c) { return c < c1 ? c * KC * 2 : kOutside; };
@@ -225,15 +232,16 @@ __global__ __launch_bounds__(NWR * SS_WAVE) void gemm_kernel(GemmArgs a, int spl
 #pragma unroll
     for (int u = 0; u < TT; ++u) {
       const int tok = 16 * u + r16;
-      if (tok >= a.m) continue;
+      if (tok >= mz) continue;
+      const int64_t gt = zrow + tok;
       const f32x4_t uv = *reinterpret_cast<const f32x4_t*>(&up[((wave * TT + u) * SS_WAVE + lane) * 4]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t col = out0 + 4 * g4 + j;
         if (col < a.n) {
-          const float gt = ss::bf2f(ss::f2bf(acc[u][j]));
+          const float gv = ss::bf2f(ss::f2bf(acc[u][j]));
           const float upv = ss::bf2f(ss::f2bf(uv[j]));
-          a.y[(int64_t)tok * a.ldy + col] = ss::f2bf(gt / (1.0f + expf(-gt)) * upv);
+          a.y[gt * a.ldy + col] = ss::f2bf(gv / (1.0f + expf(-gv)) * upv);
         }
       }
     }
@@ -242,10 +250,11 @@ __global__ __launch_bounds__(NWR * SS_WAVE) void gemm_kernel(GemmArgs a, int spl
 #pragma unroll
   for (int u = 0; u < TT; ++u) {
     const int tok = 16 * u + r16;
-    if (tok >= a.m) continue;
+    if (tok >= mz) continue;
+    const int64_t gt = zrow + tok;  // position in the whole launch
     const int64_t col = out0 + 4 * g4;
     if (EPI == GEPI_PARTIAL) {
-      float* dst = a.partials + ((int64_t)split * a.m + tok) * a.n + col;
+      float* dst = a.partials + ((int64_t)split * a.m + gt) * a.n + col;
       if (col + 3 < a.n && (a.n & 3) == 0) {
         *reinterpret_cast<f32x4_t*>(dst) = acc[u];  // 16-byte aligned: n % 4 == 0, col % 4 == 0
       } else {
@@ -259,8 +268,8 @@ __global__ __launch_bounds__(NWR * SS_WAVE) void gemm_kernel(GemmArgs a, int spl
     for (int j = 0; j < 4; ++j) {
       if (col + j < a.n) {
         float v = acc[u][j];
-        if (EPI == GEPI_RESID) v += ss::bf2f(a.resid[(int64_t)tok * a.ldy + col + j]);
-        a.y[(int64_t)tok * a.ldy + col + j] = ss::f2bf(v);
+        if (EPI == GEPI_RESID) v += ss::bf2f(a.resid[gt * a.ldy + col + j]);
+        a.y[gt * a.ldy + col + j] = ss::f2bf(v);
       }
     }
   }
@@ -280,7 +289,7 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* part, int
 
 template <int NW, int EPI>
 hipError_t launch_nw(const GemmArgs& a, const Plan& p, hipStream_t s) {
-  const dim3 grid((unsigned)p.groups, (unsigned)p.splits), block(NW * SS_WAVE);
+  const dim3 grid((unsigned)p.groups, (unsigned)p.splits, (unsigned)p.slices), block(NW * SS_WAVE);
   switch (p.tt) {
     case 1: SS_LAUNCH((gemm_kernel<NW, 1, EPI>), grid, block, 0, s, a, p.splits); break;
     case 2: SS_LAUNCH((gemm_kernel<NW, 2, EPI>), grid, block, 0, s, a, p.splits); break;

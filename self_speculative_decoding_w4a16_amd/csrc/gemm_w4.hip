@@ -37,7 +37,7 @@ template <int NW>
 __global__ __launch_bounds__(NW * 64) void gemm_w4_kernel(const uint8_t* __restrict__ codes,
                                                           const uint16_t* __restrict__ meta, int64_t n, int K,
                                                           const uint16_t* __restrict__ x, int m, uint16_t* y,
-                                                          float* part, int splits) {
+                                                          float* part, int splits, int to_part) {
   // staged activations of one chunk: [step 4][lane group 4][position 16][8 bf16]
   __shared__ __align__(16) u32x4 xs[4 * 4 * 16];
   __shared__ float xsum[2][16];  // sum of x over each 64-group of the chunk, per position
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_w4_kernel(const uint8_t* __restr
     for (int i = 0; i < 4; ++i) {
       const int64_t row = row0 + orow + i;
       if (row < n) {
-        if (splits > 1)
+        if (splits > 1 || to_part)
           part[((int64_t)split * m + r) * n + row] = acc[i];
         else
           y[(int64_t)r * n + row] = ss::f2bf(acc[i]);
@@ -148,12 +148,14 @@ int gemm_w4_splits(int64_t n, int64_t k) {
 }
 
 hipError_t launch_gemm_w4(const uint8_t* codes, const uint16_t* meta, int64_t n, int64_t k, const uint16_t* x, int m,
-                          uint16_t* y, float* part, hipStream_t s) {
+                          uint16_t* y, float* part, hipStream_t s, int* splits_out) {
   constexpr int NW = 4;
   const int splits = gemm_w4_splits(n, k);
+  const int to_part = splits_out != nullptr;
+  if (to_part) *splits_out = splits;
   const dim3 grid((unsigned)((n + 16 * NW - 1) / (16 * NW)), (unsigned)splits), block(NW * 64);
-  SS_LAUNCH(gemm_w4_kernel<NW>, grid, block, 0, s, codes, meta, n, (int)k, x, m, y, part, splits);
+  SS_LAUNCH(gemm_w4_kernel<NW>, grid, block, 0, s, codes, meta, n, (int)k, x, m, y, part, splits, to_part);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || splits == 1) return e;
+  if (e != hipSuccess || splits == 1 || to_part) return e;
   return launch_gemm_reduce(part, splits, m, n, y, n, s);
 }

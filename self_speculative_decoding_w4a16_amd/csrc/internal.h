@@ -64,9 +64,12 @@ hipError_t launch_gemm_reduce(const float* part, int splits, int m, int64_t n, u
 // Skinny GEMM on 4-bit weights (matrix cores): Y[t][n] = bf16(sum_k X[t][k] w[n][k])
 // for t < m <= 16; k % 128 == 0.  With k split over blocks it writes fp32
 // partials (gemm_w4_splits x m x n floats at part) and reduces them in order.
+// With splits_out set it always writes the partials ([splits][m][n], also
+// for one split), reduces nothing and returns the count: the consumer adds
+// them (the rows forward's RoPE and residual + RMSNorm kernels).
 int gemm_w4_splits(int64_t n, int64_t k);
 hipError_t launch_gemm_w4(const uint8_t* codes, const uint16_t* meta, int64_t n, int64_t k, const uint16_t* x, int m,
-                          uint16_t* y, float* part, hipStream_t s);
+                          uint16_t* y, float* part, hipStream_t s, int* splits_out = nullptr);
 
 // ------------------------------------------------------------------ quantise
 hipError_t launch_quantize(const uint16_t* w, int64_t n, int64_t k, int bits, uint8_t* codes,
@@ -81,7 +84,14 @@ struct AttnArgs {
   uint16_t* k_cache;    // [Hkv][cap][d] of this layer
   uint16_t* v_cache;
   const int32_t* kv_len;
-  int pos_offset;       // position of row j = kv_len + pos_offset + j
+  int pos_offset;       // node of row 0; row j is node t = pos_offset + j * row_stride
+  int row_stride;       // 0 or 1: consecutive nodes
+  // tree_d = 0: a chain - node t at slot and position kv_len + t, seeing
+  // slots [0, kv_len + t].  tree_d = D > 0: the static tree of chains of
+  // depth D - node t (t >= 1 in chain (t - 1) / D at depth (t - 1) % D + 1)
+  // at slot kv_len + t and position kv_len + depth, seeing slots
+  // [0, kv_len] and its own chain's slots up to its own.
+  int tree_d;
   int m;                // query rows
   int n_q, n_kv, d, cap;
   float theta;
@@ -135,8 +145,16 @@ hipError_t launch_rmsnorm_rows(const uint16_t* h, const uint16_t* g, float eps, 
 // order; skipped when part is null), then out[r] = RMSNorm(h[r]) * g.  k <= 8192.
 hipError_t launch_resid_rmsnorm_rows(uint16_t* h, const float* part, int splits, const uint16_t* g, float eps,
                                      int rows, int k, uint16_t* out, hipStream_t s);
+// h[r] = embed[tokens[r * tok_stride]] (ids clamped into [0, vocab)).
 hipError_t launch_embed_rows(const uint16_t* embed, const int32_t* tokens, int rows, int k,
-                             int vocab, uint16_t* h, hipStream_t s);
+                             int vocab, uint16_t* h, hipStream_t s, int tok_stride = 1);
+// act[r][j] = bf16(silu(gu[r][j]) * gu[r][F + j]) for r < rows, j < F.
+hipError_t launch_silu_rows(const uint16_t* gu, int64_t F, int rows, uint16_t* act, hipStream_t s);
+// Static tree: move the accepted chain's K/V next to the prefix (every layer
+// and KV head of a [layers x KV heads][cap][d] cache); kv_len is not changed.
+hipError_t launch_tree_commit(uint16_t* k_cache, uint16_t* v_cache, int layers_x_kv_heads, int cap, int d,
+                              const int32_t* kv_len, const int32_t* n_accepted, const int32_t* chain, int D,
+                              hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_kv_rollback(int32_t* kv_len, int32_t* tokens, const int32_t* n_accepted,
                               const int32_t* out_tokens, hipStream_t s);
@@ -147,9 +165,11 @@ hipError_t launch_kv_advance(int32_t* kv_len, int32_t delta, hipStream_t s);
 hipError_t launch_pos_guard(const int32_t* kv_len, const int32_t* token_in, int step, int cap,
                             int vocab, int32_t* valid, int32_t* token_out, int d, float theta,
                             float* rope_cs, const int32_t* draft_len, hipStream_t s);
-// RoPE table [m][d/2][2] of positions kv_len + pos_offset + j.
-hipError_t launch_rope_table(const int32_t* kv_len, int pos_offset, int m, int d, float theta,
-                             float* rope_cs, hipStream_t s);
+// RoPE table [m][d/2][2] of the rows' positions: row j is node
+// t = pos_offset + j * row_stride at position kv_len + t (tree_d = 0) or
+// kv_len + depth(t) in the static tree of chains of depth tree_d.
+hipError_t launch_rope_table(const int32_t* kv_len, int pos_offset, int row_stride, int tree_d, int m, int d,
+                             float theta, float* rope_cs, hipStream_t s);
 
 // ------------------------------------------------------------------ sampling / rejection
 struct SampleWs {
@@ -178,12 +198,15 @@ size_t reject_ws_bytes(int gamma, int vocab);
 // gamma_len (optional, device [batch]): each round judges only the first
 // min(*gamma_len, gamma) draft tokens (a draft stopped early).  batch
 // independent rounds (grid z): every pointer argument is [batch] x its
-// one-round extent, consecutive.
+// one-round extent, consecutive - except that the draft tokens, r codes and
+// u codes of round b may start at b x tok_stride, r_stride, u_stride
+// (defaults gamma, gamma, 1; 0 shares one set: the chains of a tree).
 hipError_t launch_reject(int gamma, int vocab, float temp, float draft_temp, const uint16_t* zt,
                          const uint16_t* zd, const int32_t* toks, const uint32_t* r_codes,
                          const uint32_t* u_code, int32_t* n_out, int32_t* out_tokens,
                          int32_t* status, float* probs, const RejectWs& ws, hipStream_t s,
-                         const int32_t* gamma_len = nullptr, int batch = 1);
+                         const int32_t* gamma_len = nullptr, int batch = 1, int tok_stride = -1,
+                         int r_stride = -1, int u_stride = -1);
 
 // ------------------------------------------------------------------ adaptive draft length
 struct ControlArgs {
@@ -202,3 +225,23 @@ hipError_t launch_draft_control(const ControlArgs& c, int step, const uint16_t* 
 // After the rejection round: EMA updates from n accepted, then a fresh round.
 hipError_t launch_control_update(const ControlArgs& c, const int32_t* n_accepted, hipStream_t s);
 hipError_t launch_control_init(const ControlArgs& c, hipStream_t s);
+
+// ------------------------------------------------------------------ static token tree
+// k chains of depth D share the root; chain c's depth-d node is node
+// 1 + c D + d - 1 (node 0: the root).  Next level's tokens from a level's
+// logits (rows x [ld]): level 0 (one row) writes the k children to
+// tokens[1 + c D], level d >= 1 (k rows) chain c's next token to
+// tokens[1 + c D + d]; u (T_d > 0) holds the root's k draws, then chain c's
+// level-d draw at k + c (D - 1) + d - 1.  -1 tokens when the tree does not
+// fit the cache (kv_len + 1 + k D > cap).
+hipError_t launch_tree_sample(const uint16_t* logits, int64_t ld, int rows, int V, float Td, const uint32_t* u,
+                              int level, int k, int D, const int32_t* kv_len, int cap, int32_t* tokens,
+                              hipStream_t s);
+// The root's multi-step rejection and the round's result, from the root's
+// target and draft rows and every chain's own round (chain_n [k],
+// chain_out [k][D], chain_status [k]); resid: [V] 64-bit scratch.
+hipError_t launch_tree_root(const uint16_t* zt, const uint16_t* zd, int V, float T, float Td, const int32_t* tokens,
+                            int k, int D, const uint32_t* r_codes, const uint32_t* u_code, const int32_t* chain_n,
+                            const int32_t* chain_out, const int32_t* chain_status, unsigned long long* resid,
+                            int32_t* n_accepted, int32_t* chain, int32_t* out_tokens, int32_t* status,
+                            hipStream_t s);

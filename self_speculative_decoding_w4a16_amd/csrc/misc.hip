@@ -95,15 +95,49 @@ __global__ __launch_bounds__(1024) void rmsnorm_rows_kernel(uint16_t* __restrict
 }
 
 // Out-of-range token ids are clamped into [0, vocab) so a bad id cannot read
-// outside the table.
+// outside the table.  Row r takes tokens[r * stride].
 __global__ __launch_bounds__(256) void embed_rows_kernel(const uint16_t* __restrict__ embed,
-                                                         const int32_t* __restrict__ tokens, int k,
+                                                         const int32_t* __restrict__ tokens, int stride, int k,
                                                          int vocab, uint16_t* __restrict__ h) {
   const int row = blockIdx.x;
-  const int tok = min(max(tokens[row], 0), vocab - 1);
+  const int tok = min(max(tokens[(int64_t)row * stride], 0), vocab - 1);
   const u32x4* src = reinterpret_cast<const u32x4*>(embed + (int64_t)tok * k);
   u32x4* dst = reinterpret_cast<u32x4*>(h + (int64_t)row * k);
   for (int q = threadIdx.x; q < k / 8; q += 256) dst[q] = src[q];
+}
+
+// act[r][j] = bf16(silu(g) * u) of the bf16 gate/up outputs g = gu[r][j],
+// u = gu[r][F + j] (the 4-bit rows of a tree level; the bf16 GEMM does this
+// in its epilogue with the same arithmetic).
+__global__ __launch_bounds__(256) void silu_rows_kernel(const uint16_t* __restrict__ gu, int64_t F,
+                                                        uint16_t* __restrict__ act) {
+  const int row = blockIdx.y;
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= F) return;
+  const float g = ss::bf2f(gu[(int64_t)row * 2 * F + j]), u = ss::bf2f(gu[(int64_t)row * 2 * F + F + j]);
+  act[(int64_t)row * F + j] = ss::f2bf(g / (1.0f + expf(-g)) * u);
+}
+
+// Static tree commit: the accepted chain c's first n nodes (slots
+// kv_len + 1 + c D + i - 1, i = 1..n) move to slots kv_len + i, in every
+// layer and KV head: grid (layer x KV head), 256 threads, 16 bytes each.
+// kv_len itself moves afterwards (kv_rollback), once every block has read it.
+__global__ __launch_bounds__(256) void tree_commit_kernel(uint16_t* k_cache, uint16_t* v_cache, int cap, int d,
+                                                          const int32_t* kv_len, const int32_t* n_accepted,
+                                                          const int32_t* chain, int D) {
+  const int n = *n_accepted, c = *chain, kvl = *kv_len;
+  if (c <= 0 || n <= 0 || n > D) return;  // chain 0 is already in place
+  const int64_t base = (int64_t)blockIdx.x * cap * d;
+  const int pieces = d / 8;  // 16-byte pieces per row
+  for (int e = threadIdx.x; e < n * pieces; e += 256) {
+    const int i = 1 + e / pieces, q = e % pieces;
+    const int src = kvl + 1 + c * D + i - 1, dst = kvl + i;
+    if (src < 0 || src >= cap || dst < 0 || dst >= cap) continue;
+    reinterpret_cast<u32x4*>(k_cache + base + (int64_t)dst * d)[q] =
+        reinterpret_cast<const u32x4*>(k_cache + base + (int64_t)src * d)[q];
+    reinterpret_cast<u32x4*>(v_cache + base + (int64_t)dst * d)[q] =
+        reinterpret_cast<const u32x4*>(v_cache + base + (int64_t)src * d)[q];
+  }
 }
 
 __global__ __launch_bounds__(256) void zero_kernel(u32x4* p, size_t n16) {
@@ -147,10 +181,15 @@ __global__ void pos_guard_kernel(const int32_t* kv_len, const int32_t* token_in,
   }
 }
 
-// RoPE table of rows j < m at positions kv_len + pos_offset + j: grid m.
-__global__ void rope_table_kernel(const int32_t* kv_len, int pos_offset, int d, float theta, float* rope_cs) {
+// RoPE table of rows j < m: row j is node t = pos_offset + j * stride, at
+// position kv_len + t, or kv_len + its depth in a tree of chains of depth
+// tree_d: grid m.
+__global__ void rope_table_kernel(const int32_t* kv_len, int pos_offset, int stride, int tree_d, int d, float theta,
+                                  float* rope_cs) {
   const int j = blockIdx.x;
-  if (threadIdx.x < d / 2) rope_angle(*kv_len + pos_offset + j, threadIdx.x, d, theta, rope_cs + (int64_t)j * d);
+  const int t = pos_offset + j * stride;
+  const int dep = tree_d > 0 ? (t == 0 ? 0 : (t - 1) % tree_d + 1) : t;
+  if (threadIdx.x < d / 2) rope_angle(*kv_len + dep, threadIdx.x, d, theta, rope_cs + (int64_t)j * d);
 }
 
 }  // namespace
@@ -187,8 +226,22 @@ hipError_t launch_resid_rmsnorm_rows(uint16_t* h, const float* part, int splits,
 }
 
 hipError_t launch_embed_rows(const uint16_t* embed, const int32_t* tokens, int rows, int k,
-                             int vocab, uint16_t* h, hipStream_t s) {
-  SS_LAUNCH(embed_rows_kernel, dim3(rows), dim3(256), 0, s, embed, tokens, k, vocab, h);
+                             int vocab, uint16_t* h, hipStream_t s, int tok_stride) {
+  SS_LAUNCH(embed_rows_kernel, dim3(rows), dim3(256), 0, s, embed, tokens, tok_stride, k, vocab, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_rows(const uint16_t* gu, int64_t F, int rows, uint16_t* act, hipStream_t s) {
+  SS_LAUNCH(silu_rows_kernel, dim3((unsigned)((F + 255) / 256), rows), dim3(256), 0, s, gu, F, act);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_commit(uint16_t* k_cache, uint16_t* v_cache, int layers_x_kv_heads, int cap, int d,
+                              const int32_t* kv_len, const int32_t* n_accepted, const int32_t* chain, int D,
+                              hipStream_t s) {
+  if (d % 8 != 0) return hipErrorInvalidValue;
+  SS_LAUNCH(tree_commit_kernel, dim3(layers_x_kv_heads), dim3(256), 0, s, k_cache, v_cache, cap, d, kv_len,
+            n_accepted, chain, D);
   return hipGetLastError();
 }
 
@@ -221,8 +274,9 @@ hipError_t launch_pos_guard(const int32_t* kv_len, const int32_t* token_in, int 
   return hipGetLastError();
 }
 
-hipError_t launch_rope_table(const int32_t* kv_len, int pos_offset, int m, int d, float theta,
-                             float* rope_cs, hipStream_t s) {
-  SS_LAUNCH(rope_table_kernel, dim3(m), dim3(64), 0, s, kv_len, pos_offset, d, theta, rope_cs);
+hipError_t launch_rope_table(const int32_t* kv_len, int pos_offset, int row_stride, int tree_d, int m, int d,
+                             float theta, float* rope_cs, hipStream_t s) {
+  SS_LAUNCH(rope_table_kernel, dim3(m), dim3(64), 0, s, kv_len, pos_offset, row_stride < 1 ? 1 : row_stride,
+            tree_d, d, theta, rope_cs);
   return hipGetLastError();
 }

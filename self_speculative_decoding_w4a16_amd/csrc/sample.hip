@@ -30,17 +30,8 @@ __device__ __forceinline__ unsigned long long wt(float z, float M, float T) {
   return ss::fixed_weight(z, M, T);  // 0 for non-finite logits
 }
 
-// Residual weight max(0, Wt*Sd - Wd*St) >> shift.
-__device__ __forceinline__ unsigned long long resid_w(unsigned long long Wt, unsigned long long Sd,
-                                                      unsigned long long Wd, unsigned long long St,
-                                                      int shift) {
-  const ss::U128 a = ss::mul64(Wt, Sd), b = ss::mul64(Wd, St);
-  if (!ss::lt128(b, a)) return 0ull;
-  return ss::shr128(ss::sub128(a, b), shift);
-}
-
-// bit length of v minus one; 0 for v = 0 (a draft row without mass)
-__device__ __forceinline__ int bitlen_minus1(unsigned long long v) { return v ? 63 - __clzll(v) : 0; }
+using ss::resid_w;
+using ss::bitlen_minus1;
 
 // Block-wide (256 threads) sum of unsigned 64-bit values.
 __device__ unsigned long long block_sum_u64(unsigned long long v, unsigned long long* red) {
@@ -291,7 +282,8 @@ __global__ __launch_bounds__(kT) void rej_decide_kernel(const uint16_t* zt, cons
                                                         const uint32_t* u_code, int32_t* n_out,
                                                         int32_t* out_tokens, int32_t* status_out,
                                                         float* probs, RejectWs ws,
-                                                        const int32_t* gamma_len) {
+                                                        const int32_t* gamma_len, int tok_stride,
+                                                        int r_stride, int u_stride) {
   __shared__ RowStat st[129];
   __shared__ int s_n, s_status;
   __shared__ unsigned long long red[4];
@@ -303,9 +295,9 @@ __global__ __launch_bounds__(kT) void rej_decide_kernel(const uint16_t* zt, cons
     const int bz = blockIdx.z;
     zt += (int64_t)bz * (gamma + 1) * V;
     zd += (int64_t)bz * gamma * V;
-    toks += (int64_t)bz * gamma;
-    if (r_codes) r_codes += (int64_t)bz * gamma;
-    if (u_code) u_code += bz;
+    toks += (int64_t)bz * tok_stride;
+    if (r_codes) r_codes += (int64_t)bz * r_stride;
+    if (u_code) u_code += (int64_t)bz * u_stride;
     if (gamma_len) gamma_len += bz;
     n_out += bz;
     out_tokens += (int64_t)bz * (gamma + 1);
@@ -505,7 +497,7 @@ hipError_t launch_reject(int gamma, int vocab, float temp, float draft_temp, con
                          const uint16_t* zd, const int32_t* toks, const uint32_t* r_codes,
                          const uint32_t* u_code, int32_t* n_out, int32_t* out_tokens,
                          int32_t* status, float* probs, const RejectWs& ws, hipStream_t s,
-                         const int32_t* gamma_len, int batch) {
+                         const int32_t* gamma_len, int batch, int tok_stride, int r_stride, int u_stride) {
   const int C = reject_chunks(vocab), rows = 2 * gamma + 1;
   SS_LAUNCH(rej_rowmax_kernel, dim3(C, rows, batch), dim3(kT), 0, s, zt, zd, gamma, vocab, ws);
   hipError_t e = hipGetLastError();
@@ -518,6 +510,8 @@ hipError_t launch_reject(int gamma, int vocab, float temp, float draft_temp, con
   }
   const int blocks = temp == 0.0f ? 1 : C;
   SS_LAUNCH(rej_decide_kernel, dim3(blocks, 1, batch), dim3(kT), 0, s, zt, zd, gamma, vocab, temp,
-                     draft_temp, toks, r_codes, u_code, n_out, out_tokens, status, probs, ws, gamma_len);
+                     draft_temp, toks, r_codes, u_code, n_out, out_tokens, status, probs, ws, gamma_len,
+                     tok_stride < 0 ? gamma : tok_stride, r_stride < 0 ? gamma : r_stride,
+                     u_stride < 0 ? 1 : u_stride);
   return hipGetLastError();
 }

@@ -232,3 +232,138 @@ class SpecDecoder:
                 on_cycle(c, n)
             c += 1
         return out[:n_generate], ns
+
+
+class TreeDecoder:
+    """Speculative decoding with SubSpec's static deep/narrow token tree
+    ("SubSpec" report, sections 6.3, 6.4 and 3.7): k chains of depth D share
+    the root; one cycle drafts the tree level by level (all chains of a level
+    in one pass over the draft weights), verifies all 1 + k D nodes in one
+    target pass, judges the root by multi-step rejection and the accepted
+    chain by the plain round, and moves that chain's K/V next to the prefix.
+    Every step is a call into libsubspec; with ``graphs`` a whole cycle is
+    recorded once and replayed."""
+
+    def __init__(self, model, capacity, k, depth, temp=0.0, draft_temp=0.0, device="cuda", graphs=False):
+        s = model.shape
+        self.model = model
+        self.k, self.depth = int(k), int(depth)
+        self.temp, self.draft_temp = float(temp), float(draft_temp)
+        self.capacity = capacity
+        self.n_nodes = 1 + self.k * self.depth
+        L, V = model.n_layers, s.vocab
+        kv_shape = (L, s.n_kv_heads, capacity, s.head_dim)
+        self.k_cache = torch.zeros(kv_shape, dtype=torch.bfloat16, device=device)
+        self.v_cache = torch.zeros(kv_shape, dtype=torch.bfloat16, device=device)
+        self.kv_len = torch.zeros(1, dtype=torch.int32, device=device)
+        self.tokens = torch.zeros(self.n_nodes, dtype=torch.int32, device=device)
+        self.draft_logits = torch.zeros((1 + self.k * (self.depth - 1), V), dtype=torch.bfloat16, device=device)
+        self.target_logits = torch.zeros((self.n_nodes, V), dtype=torch.bfloat16, device=device)
+        self.n_accepted = torch.zeros(1, dtype=torch.int32, device=device)
+        self.chain = torch.zeros(1, dtype=torch.int32, device=device)
+        self.out_tokens = torch.zeros(self.depth + 1, dtype=torch.int32, device=device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+        self.max_tokens = 64
+        self.prefill_tokens = torch.zeros(self.max_tokens, dtype=torch.int32, device=device)
+        self.ud_buf = torch.zeros(self.k * self.depth, dtype=torch.int32, device=device)
+        self.r_buf = torch.zeros(self.k + self.depth - 1, dtype=torch.int32, device=device)
+        self.uf_buf = torch.zeros(1, dtype=torch.int32, device=device)
+        nbytes = max(_lib.workspace_bytes(model.c, self.max_tokens, capacity),
+                     _lib.tree_workspace_bytes(model.c, self.k, self.depth, capacity))
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _lib.workspace_init(self.ws)
+        self.c = _lib.State(self.k_cache.data_ptr(), self.v_cache.data_ptr(), capacity,
+                            self.kv_len.data_ptr(), self.tokens.data_ptr(),
+                            self.draft_logits.data_ptr(), self.depth)
+        self.use_graphs = graphs
+        self._graphs = {}
+        self._warm = set()
+
+    def reset(self, kv_len, last_token):
+        self.kv_len.fill_(int(kv_len))
+        self.tokens[0] = int(last_token)
+
+    def load_kv(self, k, v, kv_len, last_token):
+        n = k.shape[2]
+        self.k_cache[:, :, :n].copy_(k)
+        self.v_cache[:, :, :n].copy_(v)
+        self.reset(kv_len, last_token)
+
+    def prefill(self, prompt):
+        prompt = [int(t) for t in prompt]
+        self.reset(0, prompt[-1])
+        body = prompt[:-1]
+        for c0 in range(0, len(body), self.max_tokens):
+            chunk = body[c0:c0 + self.max_tokens]
+            self.prefill_tokens[:len(chunk)] = torch.tensor(chunk, dtype=torch.int32)
+            _lib.verify(self.model.c, self.c, len(chunk), self.prefill_tokens, None, self.ws)
+            _lib.kv_advance(self.c, len(chunk))
+
+    # ------------------------------------------------------------ one cycle
+    def draft(self, u_draft=None):
+        for level in range(self.depth):
+            _lib.tree_draft(self.model.c, self.c, self.k, self.depth, level, self.draft_temp, u_draft, self.ws)
+
+    def verify(self):
+        _lib.tree_verify(self.model.c, self.c, self.k, self.depth, self.target_logits, self.ws)
+
+    def reject(self, r_codes=None, u_code=None):
+        _lib.tree_reject(self.k, self.depth, self.model.shape.vocab, self.temp, self.draft_temp,
+                         self.target_logits, self.draft_logits, self.tokens, r_codes, u_code, self.n_accepted,
+                         self.chain, self.out_tokens, self.status, self.ws)
+
+    def commit(self):
+        _lib.tree_commit(self.model.c, self.c, self.k, self.depth, self.n_accepted, self.chain, self.out_tokens)
+
+    def _cycle_body(self, stochastic):
+        self.draft(self.ud_buf if stochastic else None)
+        self.verify()
+        self.reject(self.r_buf if stochastic else None, self.uf_buf if stochastic else None)
+        self.commit()
+
+    def cycle(self, u_draft=None, r_codes=None, u_code=None):
+        stochastic = u_draft is not None or r_codes is not None or u_code is not None
+        if stochastic:
+            if u_draft is not None:
+                self.ud_buf.copy_(u_draft[:self.ud_buf.numel()])
+            if r_codes is not None:
+                self.r_buf.copy_(r_codes[:self.r_buf.numel()])
+            if u_code is not None:
+                self.uf_buf.copy_(u_code.reshape(-1)[:1])
+        if not self.use_graphs or stochastic not in self._warm:
+            self._cycle_body(stochastic)
+            self._warm.add(stochastic)
+            return
+        g = self._graphs.get(stochastic)
+        if g is None:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self._cycle_body(stochastic)
+            self._graphs[stochastic] = g
+        g.replay()
+
+    def generate(self, prompt, n_generate, uniforms=None, on_cycle=None):
+        """At least n_generate tokens after ``prompt``; ``uniforms`` =
+        (U_draft [C][k D], R [C][k + D - 1], U [C]) device int32, or None
+        (greedy).  Returns (tokens, per-cycle n)."""
+        kv = len(prompt) - 1
+        self.prefill(prompt)
+        out, ns = [], []
+        c = 0
+        while len(out) < n_generate:
+            if kv + self.n_nodes > self.capacity:
+                raise ValueError(f"KV capacity {self.capacity} cannot hold another tree of {self.n_nodes} "
+                                 f"nodes after kv_len {kv}")
+            if uniforms is not None:
+                ud, rr, uf = uniforms
+                self.cycle(ud[c], rr[c], uf[c:c + 1])
+            else:
+                self.cycle()
+            n = int(self.n_accepted.item())
+            out += self.out_tokens[:n + 1].tolist()
+            ns.append(n)
+            kv += n + 1
+            if on_cycle:
+                on_cycle(c, n)
+            c += 1
+        return out[:n_generate], ns

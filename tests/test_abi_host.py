@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared():
         assert hasattr(l, name), name
     assert set(_declared()) == set(_lib.EXPORTS)
-    assert _lib.abi_version() == 2  # subspec_linear carries the code width
+    assert _lib.abi_version() == 3  # the static tree entry points
 
 
 V = ctypes.c_void_p
@@ -165,6 +165,38 @@ def test_draft_verify_argument_errors():
     assert l.subspec_verify(ctypes.byref(m), ctypes.byref(st_null), 4, V(p), None, ws, 1 << 30, None) == _lib.EINVAL
     assert l.subspec_kv_rollback(ctypes.byref(st), None, V(p), None) == _lib.EINVAL
     assert l.subspec_kv_advance(None, 1, None) == _lib.EINVAL
+
+
+def test_tree_argument_errors():
+    l = _lib.lib()
+    m, keep = _fake_model()
+    p = 4096
+    st = _lib.State(p, p, 1024, p, p, p, 4)
+    ws = V(p)
+    big = 1 << 40
+    by = ctypes.byref
+    assert l.subspec_tree_workspace_bytes(by(m), 6, 48, 1024) > 64 * 1024
+    assert l.subspec_tree_workspace_bytes(by(m), 17, 4, 1024) == 0  # k above 16
+    assert l.subspec_tree_workspace_bytes(by(m), 8, 64, 1024) == 0  # 513 nodes
+    assert l.subspec_tree_workspace_bytes(by(m), 2, 0, 1024) == 0
+    # level outside [0, depth), sampled children without uniforms, a tree above the capacity
+    assert l.subspec_tree_draft(by(m), by(st), 6, 8, 8, 0.0, None, ws, big, None) == _lib.EINVAL
+    assert l.subspec_tree_draft(by(m), by(st), 6, 8, 0, 0.5, None, ws, big, None) == _lib.EINVAL
+    st_small = _lib.State(p, p, 40, p, p, p, 4)
+    assert l.subspec_tree_draft(by(m), by(st_small), 6, 8, 0, 0.0, None, ws, big, None) == _lib.ECAPACITY
+    assert l.subspec_tree_verify(by(m), by(st_small), 6, 8, V(p), ws, big, None) == _lib.ECAPACITY
+    assert l.subspec_tree_verify(by(m), by(st), 6, 8, None, ws, big, None) == _lib.EINVAL
+    assert l.subspec_tree_verify(by(m), by(st), 6, 8, V(p), ws, 128, None) == _lib.EWORKSPACE
+    # 3-bit draft weights: the tree's draft rows take bf16 or 4-bit only
+    m3, keep3 = _fake_model()
+    keep3[0].qkv_d = _lib.Linear(None, p, p, (2 + 2) * 128, 256, 3)
+    assert l.subspec_tree_draft(by(m3), by(st), 2, 4, 0, 0.0, None, ws, big, None) == _lib.EUNSUPPORTED
+    tr = l.subspec_tree_reject
+    assert tr(6, 48, 1000, 1.0, 1.0, V(p), V(p), V(p), None, V(p), V(p), V(p), V(p), V(p), ws, big, None) == _lib.EINVAL
+    assert tr(6, 48, 1000, -1.0, 1.0, V(p), V(p), V(p), V(p), V(p), V(p), V(p), V(p), V(p), ws, big, None) == _lib.EINVAL
+    assert tr(0, 48, 1000, 0.0, 0.0, V(p), V(p), V(p), None, None, V(p), V(p), V(p), V(p), ws, big, None) == _lib.EINVAL
+    assert tr(6, 48, 1000, 0.0, 0.0, V(p), V(p), V(p), None, None, V(p), V(p), V(p), V(p), ws, 64, None) == _lib.EWORKSPACE
+    assert l.subspec_tree_commit(by(m), by(st), 6, 48, None, V(p), V(p), None) == _lib.EINVAL
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
