@@ -336,6 +336,10 @@ def main():
     if args.config == "full7b" and not args.no_small:
         batch = batch_rates(dm, shape, dev)
         log(f"4-bit skinny GEMM (batch of drafts): {json.dumps(batch)}")
+    tree = None
+    if args.config == "full7b" and not args.no_small and not stochastic:
+        tree = tree_rates(dec, dm, shape, wl, kv0, last)
+        log(f"static tree k=6 D=48: {json.dumps(tree)}")
     adapt = None
     if not sparse and not args.no_small and not stochastic:
         adapt = adaptive_rates(dec, dm, wl, kv0, last, draft_pass["avg_us"] / verify_pass["avg_us"])
@@ -395,6 +399,7 @@ def main():
         "lowbit": lowbit,
         "adaptive_length": adapt,
         "batch_w4_gemm": batch,
+        "tree": tree,
         "kernels": kern,
     }
     # every rate also against the measured read ceiling
@@ -771,6 +776,67 @@ def batch_rates(dm, shape, dev):
                                    "frac": round(by / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                                    "weight_bytes_per_token": round(wb / m)}
     return out
+
+
+def tree_rates(dec, dm, shape, wl, kv0, last, k=6, depth=48, G=64, steps=1):
+    """Greedy speculative decoding of the same model and prompt state with
+    SubSpec's static tree, k = 6 chains of depth 48 ("SubSpec" report,
+    sections 6.3 and 3.7): tokens/s and tau over graph-replayed cycles, and
+    the tau-independent passes - one draft level (k rows through the draft in
+    one weight stream) and the verify pass over all 1 + k D nodes (the GEMMs
+    in slices of 64 positions), each graph-replayed, against their
+    algorithmic bytes and the matrix-core peak."""
+    import time
+
+    import numpy as np
+    import torch
+
+    from self_speculative_decoding_w4a16_amd import _lib
+    from self_speculative_decoding_w4a16_amd.engine import TreeDecoder
+    nodes = 1 + k * depth
+    cap = kv0 + G + nodes + 64
+    t = TreeDecoder(dm, cap, k, depth, 0.0, 0.0, graphs=True)
+    t.k_cache[:, :, :kv0].copy_(dec.k_cache[:, :, :kv0])
+    t.v_cache[:, :, :kv0].copy_(dec.v_cache[:, :, :kv0])
+
+    def gen():
+        t.reset(kv0, last)
+        out, ns = [], []
+        while len(out) < G:
+            t.cycle()
+            n = int(t.n_accepted.item())
+            out += t.out_tokens[:n + 1].tolist()
+            ns.append(n)
+        return ns
+    gen()
+    gen()  # the first cycle runs eagerly, the second records the graph
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    all_ns = []
+    for _ in range(steps):
+        all_ns += gen()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    n_w4 = len(dm.substitute_layers)
+    t.reset(kv0, last)
+    t.draft()  # a drafted tree in place for the pass timings
+    lvl = replay_us(lambda: _lib.tree_draft(dm.c, t.c, k, depth, 1, 0.0, None, t.ws), reps=10)
+    root = replay_us(lambda: _lib.tree_draft(dm.c, t.c, k, depth, 0, 0.0, None, t.ws), reps=10)
+    ver = replay_us(t.verify, reps=5)
+    draft_b, _, _, bf, kv_row = model_bytes(shape, n_w4, kv0 + 2, 0)
+    _, verify_b, _, _, _ = model_bytes(shape, n_w4, 0, kv0 + nodes)
+    params = bf / 2 * shape.n_layers + shape.vocab * shape.hidden
+    tflops = 2.0 * params * nodes / (ver * 1e-6) / 1e12
+    del t
+    torch.cuda.empty_cache()
+    return {"k": k, "depth": depth, "nodes": nodes, "tokens_s": round(steps * G / el, 3),
+            "tau": round(float(np.mean([n + 1 for n in all_ns])), 4), "cycles": len(all_ns),
+            "cycle_ms": round(1000 * el / len(all_ns), 3),
+            "draft_level": hbm(draft_b, lvl, f"one tree draft level ({k} rows, every launch, graph-replayed)"),
+            "draft_root": hbm(draft_b, root, "the tree's root level (1 row, every launch, graph-replayed)"),
+            "verify_pass": hbm(verify_b, ver, f"tree verify pass ({nodes} positions, every launch, graph-replayed)",
+                               mfma_tflops=round(tflops, 1),
+                               mfma_frac=round(tflops / BF16_MFMA_PEAK_TFLOPS, 4))}
 
 
 def tiny_rates(dev, reps=200):
