@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SUBSPEC_ABI_VERSION 3
+#define SUBSPEC_ABI_VERSION 4
 
 enum {
   SUBSPEC_OK = 0,
@@ -297,6 +297,62 @@ int subspec_reject_len(int32_t gamma, int32_t vocab, float temp, float draft_tem
                        const int32_t *draft_tokens, const uint32_t *r_codes, const uint32_t *u_code,
                        const int32_t *gamma_len, int32_t *n_accepted, int32_t *out_tokens, int32_t *status,
                        float *probs, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Batched decoding: B sequences share the substitutes ([SSR] §10.3 item 11)  */
+/* ------------------------------------------------------------------------ */
+
+/* B independent sequences decoded together, so that every weight (bf16 or
+ * 4-bit) streams once per step for all of them: each has its own KV cache
+ * region, length and tokens.  Buffers (device): k_cache / v_cache bf16
+ * [L][batch][Hkv][capacity][d]; kv_len [batch]; tokens [batch][gamma_max + 1]
+ * ([b][0] the last committed token, [b][1..] drafts); draft_logits
+ * [batch][gamma_max][vocab].  1 <= batch <= 16 (the draft step's rows). */
+typedef struct {
+  uint16_t *k_cache, *v_cache;
+  int32_t capacity;
+  int32_t batch;
+  int32_t *kv_len;
+  int32_t *tokens;
+  uint16_t *draft_logits;
+  int32_t gamma_max;
+} subspec_batch_state;
+
+/* Workspace bytes for batch_draft_step / batch_verify of up to max_tokens
+ * positions per sequence and batch_reject with gamma = max_tokens - 1. */
+size_t subspec_batch_workspace_bytes(const subspec_model *m, int32_t batch, int32_t max_tokens, int32_t capacity);
+
+/* Draft step `step` of every sequence at once: row b runs tokens[b][step]
+ * at position kv_len[b] + step through the draft, writes its K/V there and
+ * draft_logits[b][step], and draws tokens[b][step + 1] (argmax, or the
+ * inverse CDF with u_codes[b gamma_max + step]); a sequence whose position
+ * is past its capacity gets token -1.  Draft weights bf16 or 4-bit. */
+int subspec_batch_draft_step(const subspec_model *m, const subspec_batch_state *st, int32_t step, float draft_temp,
+                             const uint32_t *u_codes, void *ws, size_t ws_bytes, void *stream);
+
+/* The target pass over n_tokens positions of every sequence: row j of
+ * sequence b runs tokens[b ld_tokens + j] at kv_len[b] + j (causal within the
+ * sequence), writes its K/V and, unless logits is NULL, logits
+ * [batch][n_tokens][vocab].  batch x n_tokens <= 512, n_tokens <= 64. */
+int subspec_batch_verify(const subspec_model *m, const subspec_batch_state *st, int32_t n_tokens,
+                         const int32_t *tokens, int64_t ld_tokens, uint16_t *logits, void *ws, size_t ws_bytes,
+                         void *stream);
+
+/* Every sequence's rejection round (subspec_reject's rule and arithmetic)
+ * over gamma = gamma_max drafts: target_logits [batch][gamma + 1][vocab],
+ * the state's draft logits and tokens, r_codes [batch][gamma], u_codes
+ * [batch]; outputs n_accepted [batch], out_tokens [batch][gamma + 1],
+ * status [batch]. */
+int subspec_batch_reject(const subspec_model *m, const subspec_batch_state *st, float temp, float draft_temp,
+                         const uint16_t *target_logits, const uint32_t *r_codes, const uint32_t *u_codes,
+                         int32_t *n_accepted, int32_t *out_tokens, int32_t *status, void *ws, size_t ws_bytes,
+                         void *stream);
+
+/* kv_len[b] += n_accepted[b] + 1 and tokens[b][0] = out_tokens[b][n] for
+ * every sequence (out_tokens [batch][gamma_max + 1]); with n_accepted NULL,
+ * kv_len[b] += delta (prefill). */
+int subspec_batch_rollback(const subspec_batch_state *st, const int32_t *n_accepted, const int32_t *out_tokens,
+                           int32_t delta, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* The static token tree  ([SSR] sections 6.3, 6.4 and 3.7)                  */

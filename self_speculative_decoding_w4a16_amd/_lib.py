@@ -59,6 +59,11 @@ class State(ctypes.Structure):
                 ("budget_permille", c_int32), ("draft_len", c_void_p)]
 
 
+class BatchState(ctypes.Structure):
+    _fields_ = [("k_cache", c_void_p), ("v_cache", c_void_p), ("capacity", c_int32), ("batch", c_int32),
+                ("kv_len", c_void_p), ("tokens", c_void_p), ("draft_logits", c_void_p), ("gamma_max", c_int32)]
+
+
 class Control(ctypes.Structure):
     _fields_ = [("draft_len", c_void_p), ("state", c_void_p), ("entropy", c_void_p),
                 ("c", ctypes.c_double), ("beta", ctypes.c_double), ("gamma_max", c_int32)]
@@ -108,6 +113,14 @@ _SIGS = {
     "subspec_sample": (c_int32, [c_void_p, c_int32, c_float, c_void_p, c_void_p, c_void_p,
                                  c_size_t, c_void_p]),
     "subspec_hbm_read": (c_int32, [c_void_p, c_int64, c_void_p, c_void_p]),
+    "subspec_batch_workspace_bytes": (c_size_t, [POINTER(Model), c_int32, c_int32, c_int32]),
+    "subspec_batch_draft_step": (c_int32, [POINTER(Model), POINTER(BatchState), c_int32, c_float, c_void_p, c_void_p,
+                                           c_size_t, c_void_p]),
+    "subspec_batch_verify": (c_int32, [POINTER(Model), POINTER(BatchState), c_int32, c_void_p, c_int64, c_void_p,
+                                       c_void_p, c_size_t, c_void_p]),
+    "subspec_batch_reject": (c_int32, [POINTER(Model), POINTER(BatchState), c_float, c_float, c_void_p, c_void_p,
+                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "subspec_batch_rollback": (c_int32, [POINTER(BatchState), c_void_p, c_void_p, c_int32, c_void_p]),
     "subspec_tree_workspace_bytes": (c_size_t, [POINTER(Model), c_int32, c_int32, c_int32]),
     "subspec_tree_draft": (c_int32, [POINTER(Model), POINTER(State), c_int32, c_int32, c_int32, c_float, c_void_p,
                                      c_void_p, c_size_t, c_void_p]),
@@ -344,6 +357,34 @@ def bf16_gemm(w, x, y, ws, stream=None):
 def sample(logits, temp, u_code, token, ws, stream=None):
     check(lib().subspec_sample(_p(logits), logits.numel(), temp, _p(u_code), _p(token), _p(ws),
                                ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def batch_workspace_bytes(model, batch, max_tokens, capacity):
+    n = lib().subspec_batch_workspace_bytes(ctypes.byref(model), batch, max_tokens, capacity)
+    if n == 0:
+        raise SubspecError(EINVAL, last_error())
+    return n
+
+
+def batch_draft_step(model, state, step, draft_temp, u_codes, ws, stream=None):
+    check(lib().subspec_batch_draft_step(ctypes.byref(model), ctypes.byref(state), step, draft_temp, _p(u_codes),
+                                         _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def batch_verify(model, state, n_tokens, tokens, ld_tokens, logits, ws, stream=None):
+    check(lib().subspec_batch_verify(ctypes.byref(model), ctypes.byref(state), n_tokens, _p(tokens), ld_tokens,
+                                     _p(logits), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def batch_reject(model, state, temp, draft_temp, target_logits, r_codes, u_codes, n_accepted, out_tokens, status,
+                 ws, stream=None):
+    check(lib().subspec_batch_reject(ctypes.byref(model), ctypes.byref(state), temp, draft_temp, _p(target_logits),
+                                     _p(r_codes), _p(u_codes), _p(n_accepted), _p(out_tokens), _p(status), _p(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def batch_rollback(state, n_accepted, out_tokens, delta=0, stream=None):
+    check(lib().subspec_batch_rollback(ctypes.byref(state), _p(n_accepted), _p(out_tokens), delta, _stream(stream)))
 
 
 def tree_workspace_bytes(model, k, depth, capacity):

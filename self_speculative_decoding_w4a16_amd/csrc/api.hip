@@ -333,25 +333,45 @@ int gemv_class(const subspec_linear& l, int site) {
 struct RowsSpec {
   const int32_t* tokens;
   int tok_stride;
-  int m;
+  int m;  // rows of each sequence
   int node0, node_stride, tree_d;
+  // seqs > 1: a batch of sequences (subspec_batch_state), m rows each; the
+  // token of row j of sequence z is tokens[z tok_seq_stride + j tok_stride]
+  int seqs;
+  int64_t tok_seq_stride;
   bool draft;        // draft weights: bf16 shared layers, 4-bit substitutes on the matrix cores (m <= 16)
   uint16_t* logits;  // [m][ld] or NULL
   int64_t ld;
 };
 
-int rows_forward(const subspec_model* m, const subspec_state* st, const RowsSpec& rs, void* ws, hipStream_t s) {
+// The cache, lengths and scores a row forward works on (one sequence's
+// subspec_state, or a subspec_batch_state's sequences).
+struct RowsCache {
+  uint16_t *k_cache, *v_cache;
+  int capacity;
+  int32_t* kv_len;
+  float* kv_score;  // importance scores (one sequence only) or NULL
+  int score_window;
+};
+RowsCache rows_cache(const subspec_state* st) {
+  return RowsCache{st->k_cache, st->v_cache, st->capacity, st->kv_len, st->kv_score, st->score_window};
+}
+
+int rows_forward(const subspec_model* m, const RowsCache& st, const RowsSpec& rs, void* ws, hipStream_t s) {
+  const int nseq = rs.seqs > 1 ? rs.seqs : 1;
+  const int mt = rs.m * nseq;  // rows of the whole launch
   FwdWs w;
-  carve_fwd(m, rs.m, st->capacity, ws, &w);
+  carve_fwd(m, mt, st.capacity, ws, &w);
   const int64_t H = m->hidden, F = m->ffn, d = m->head_dim;
   const int64_t qd = (int64_t)m->n_q_heads * d;
   const int64_t qkv = (int64_t)(m->n_q_heads + 2 * m->n_kv_heads) * d;
-  const int mt = rs.m;
+  const int rps = nseq > 1 ? rs.m : 0;
   {
     prof::Scope ps(SUBSPEC_K_MISC, 0.0, s);
-    HIPCHK(launch_embed_rows(m->embed, rs.tokens, mt, (int)H, m->vocab, w.h, s, rs.tok_stride));
-    HIPCHK(launch_rope_table(st->kv_len, rs.node0, rs.node_stride, rs.tree_d, mt, (int)d, m->rope_theta, w.rope_cs,
-                             s));
+    HIPCHK(launch_embed_rows(m->embed, rs.tokens, mt, (int)H, m->vocab, w.h, s, rs.tok_stride, rps,
+                             rs.tok_seq_stride));
+    HIPCHK(launch_rope_table(st.kv_len, rs.node0, rs.node_stride, rs.tree_d, mt, (int)d, m->rope_theta, w.rope_cs,
+                             s, rps));
   }
   // Narrow GEMMs (QKV, O, down) split k over blocks and leave fp32 partial
   // sums; their consumers add them: RoPE for QKV, the residual + RMSNorm
@@ -394,24 +414,26 @@ int rows_forward(const subspec_model* m, const subspec_state* st, const RowsSpec
       at.qkv_splits = q_splits;
     }
     at.q_rot = w.qrot;
-    at.k_cache = st->k_cache + (int64_t)l * m->n_kv_heads * st->capacity * d;
-    at.v_cache = st->v_cache + (int64_t)l * m->n_kv_heads * st->capacity * d;
-    at.kv_len = st->kv_len;
+    // layer l of the cache: [sequences][n_kv][capacity][d]
+    at.k_cache = st.k_cache + (int64_t)l * nseq * m->n_kv_heads * st.capacity * d;
+    at.v_cache = st.v_cache + (int64_t)l * nseq * m->n_kv_heads * st.capacity * d;
+    at.kv_len = st.kv_len;
     at.pos_offset = rs.node0;
     at.row_stride = rs.node_stride;
     at.tree_d = rs.tree_d;
-    at.m = mt;
+    at.m = rs.m;
+    at.seqs = nseq;
     at.n_q = m->n_q_heads;
     at.n_kv = m->n_kv_heads;
     at.d = (int)d;
-    at.cap = st->capacity;
+    at.cap = st.capacity;
     at.theta = m->rope_theta;
     at.rope_cs = w.rope_cs;
     at.part = w.attn_part;
     at.out = w.attn;
-    at.split_keys = verify_attn_split_keys(st->capacity, m->n_kv_heads, mt * (m->n_q_heads / m->n_kv_heads));
-    at.splits = (st->capacity + at.split_keys - 1) / at.split_keys;
-    const bool scores = st->kv_score && !rs.draft && rs.tree_d == 0;
+    at.split_keys = verify_attn_split_keys(st.capacity, m->n_kv_heads * nseq, rs.m * (m->n_q_heads / m->n_kv_heads));
+    at.splits = (st.capacity + at.split_keys - 1) / at.split_keys;
+    const bool scores = st.kv_score && !rs.draft && rs.tree_d == 0 && nseq == 1;
     if (scores) at.ml = w.attn_ml;
     {
       prof::Scope ps(SUBSPEC_K_ATTN_VERIFY, 0.0, s);
@@ -420,8 +442,7 @@ int rows_forward(const subspec_model* m, const subspec_state* st, const RowsSpec
     }
     if (scores) {
       prof::Scope ps(SUBSPEC_K_SCORES, 0.0, s);
-      HIPCHK(launch_attn_scores(at, st->kv_score + (int64_t)l * m->n_kv_heads * st->capacity,
-                                st->score_window, s));
+      HIPCHK(launch_attn_scores(at, st.kv_score + (int64_t)l * m->n_kv_heads * st.capacity, st.score_window, s));
     }
     if (lin_is_w4(lo)) {
       prof::Scope ps(SUBSPEC_K_W4_O, gemm_w4_bytes(H, qd, mt, H, true), s);
@@ -716,7 +737,145 @@ int subspec_verify(const subspec_model* m, const subspec_state* st, int32_t n_to
   rs.draft = false;
   rs.logits = logits;
   rs.ld = m->vocab;
-  return rows_forward(m, st, rs, ws, hs(stream));
+  return rows_forward(m, rows_cache(st), rs, ws, hs(stream));
+}
+
+constexpr int kMaxBatch = 16;
+
+static int check_batch(const subspec_model* m, const subspec_batch_state* st) {
+  if (!st) return fail(SUBSPEC_EINVAL, "batch state is NULL");
+  if (!st->k_cache || !st->v_cache || !st->kv_len || !st->tokens)
+    return fail(SUBSPEC_EINVAL, "batch state buffers k_cache, v_cache, kv_len, tokens must be set");
+  if (st->batch < 1 || st->batch > kMaxBatch) return fail(SUBSPEC_EINVAL, "batch %d outside [1, %d]", st->batch, kMaxBatch);
+  if (st->capacity < 1) return fail(SUBSPEC_ECAPACITY, "capacity must be >= 1");
+  if (st->gamma_max < 0 || st->gamma_max > kMaxGamma)
+    return fail(SUBSPEC_EINVAL, "gamma_max %d outside [0, %d]", st->gamma_max, kMaxGamma);
+  (void)m;
+  return SUBSPEC_OK;
+}
+
+static RowsCache batch_cache(const subspec_batch_state* st) {
+  return RowsCache{st->k_cache, st->v_cache, st->capacity, st->kv_len, nullptr, 0};
+}
+
+size_t subspec_batch_workspace_bytes(const subspec_model* m, int32_t batch, int32_t max_tokens, int32_t capacity) {
+  if (check_model(m)) return 0;
+  if (batch < 1 || batch > kMaxBatch || max_tokens < 1 || max_tokens > kMaxTokens ||
+      batch * max_tokens > kMaxTreeRows) {
+    fail(SUBSPEC_EINVAL, "batch in [1, %d], max_tokens in [1, %d], batch x max_tokens <= %d", kMaxBatch, kMaxTokens,
+         kMaxTreeRows);
+    return 0;
+  }
+  if (capacity < 1) {
+    fail(SUBSPEC_ECAPACITY, "capacity must be >= 1");
+    return 0;
+  }
+  size_t b = carve_fwd(m, batch * max_tokens, capacity, nullptr, nullptr);
+  b = std::max(b, carve_fwd(m, batch, capacity, nullptr, nullptr));
+  b = std::max(b, carve_reject(max_tokens - 1, m->vocab, nullptr, nullptr, batch));
+  ok();
+  return b;
+}
+
+int subspec_batch_draft_step(const subspec_model* m, const subspec_batch_state* st, int32_t step, float draft_temp,
+                             const uint32_t* u_codes, void* ws, size_t ws_bytes, void* stream) {
+  int r;
+  if ((r = check_model(m)) || (r = check_batch(m, st)) || (r = check_tree_draft_weights(m))) return r;
+  if (!st->draft_logits) return fail(SUBSPEC_EINVAL, "batch state draft_logits must be set");
+  if (step < 0 || step >= st->gamma_max)
+    return fail(SUBSPEC_EINVAL, "step %d outside [0, gamma_max = %d)", step, st->gamma_max);
+  if (!(draft_temp >= 0.0f)) return fail(SUBSPEC_EINVAL, "draft_temp must be >= 0");
+  if (draft_temp > 0.0f && !u_codes) return fail(SUBSPEC_EINVAL, "u_codes needed when draft_temp > 0");
+  if ((r = need_ws(ws, ws_bytes, carve_fwd(m, st->batch, st->capacity, nullptr, nullptr)))) return r;
+  hipStream_t s = hs(stream);
+  const int64_t ldt = st->gamma_max + 1;
+  RowsSpec rs{};
+  rs.tokens = st->tokens + step;  // row b: tokens[b][step]
+  rs.tok_stride = 1;
+  rs.m = 1;
+  rs.seqs = st->batch;
+  rs.tok_seq_stride = ldt;
+  rs.node0 = step;
+  rs.node_stride = 1;
+  rs.draft = true;
+  rs.logits = st->draft_logits + (int64_t)step * m->vocab;  // row b: draft_logits[b][step]
+  rs.ld = (int64_t)st->gamma_max * m->vocab;
+  if ((r = rows_forward(m, batch_cache(st), rs, ws, s))) return r;
+  RowsSampleArgs sa{};
+  sa.logits = rs.logits;
+  sa.ld = rs.ld;
+  sa.V = m->vocab;
+  sa.T = draft_temp;
+  sa.u = u_codes ? u_codes + step : nullptr;
+  sa.u_row = st->gamma_max;
+  sa.tokens = st->tokens + step + 1;
+  sa.t_row = ldt;
+  sa.nout = 1;
+  sa.kv_len = st->kv_len;
+  sa.kv_row = 1;
+  sa.need = step + 1;  // position kv_len + step inside the cache
+  sa.cap = st->capacity;
+  prof::Scope ps(SUBSPEC_K_SAMPLE, 2.0 * st->batch * m->vocab, s);
+  HIPCHK(launch_rows_sample(sa, st->batch, s));
+  return ok();
+}
+
+int subspec_batch_verify(const subspec_model* m, const subspec_batch_state* st, int32_t n_tokens,
+                         const int32_t* tokens, int64_t ld_tokens, uint16_t* logits, void* ws, size_t ws_bytes,
+                         void* stream) {
+  int r;
+  if ((r = check_model(m)) || (r = check_batch(m, st))) return r;
+  if (!tokens) return fail(SUBSPEC_EINVAL, "tokens is NULL");
+  if (n_tokens < 1 || n_tokens > kMaxTokens || st->batch * n_tokens > kMaxTreeRows)
+    return fail(SUBSPEC_EINVAL, "n_tokens %d outside [1, %d] or batch x n_tokens above %d", n_tokens, kMaxTokens,
+                kMaxTreeRows);
+  if (ld_tokens < n_tokens) return fail(SUBSPEC_EINVAL, "ld_tokens below n_tokens");
+  if (n_tokens > st->capacity) return fail(SUBSPEC_ECAPACITY, "n_tokens above the KV capacity");
+  if ((r = need_ws(ws, ws_bytes, carve_fwd(m, st->batch * n_tokens, st->capacity, nullptr, nullptr)))) return r;
+  RowsSpec rs{};
+  rs.tokens = tokens;
+  rs.tok_stride = 1;
+  rs.m = n_tokens;
+  rs.seqs = st->batch;
+  rs.tok_seq_stride = ld_tokens;
+  rs.node0 = 0;
+  rs.node_stride = 1;
+  rs.draft = false;
+  rs.logits = logits;
+  rs.ld = m->vocab;
+  return rows_forward(m, batch_cache(st), rs, ws, hs(stream));
+}
+
+int subspec_batch_reject(const subspec_model* m, const subspec_batch_state* st, float temp, float draft_temp,
+                         const uint16_t* target_logits, const uint32_t* r_codes, const uint32_t* u_codes,
+                         int32_t* n_accepted, int32_t* out_tokens, int32_t* status, void* ws, size_t ws_bytes,
+                         void* stream) {
+  int r;
+  if ((r = check_model(m)) || (r = check_batch(m, st))) return r;
+  if (!target_logits || !st->draft_logits || !n_accepted || !out_tokens || !status)
+    return fail(SUBSPEC_EINVAL, "NULL buffer");
+  if (!(temp >= 0.0f) || !(draft_temp >= 0.0f)) return fail(SUBSPEC_EINVAL, "temperatures must be >= 0");
+  if (temp > 0.0f && (!r_codes || !u_codes)) return fail(SUBSPEC_EINVAL, "r_codes and u_codes needed when temp > 0");
+  const int gamma = st->gamma_max;
+  RejectWs w;
+  if ((r = need_ws(ws, ws_bytes, carve_reject(gamma, m->vocab, nullptr, nullptr, st->batch)))) return r;
+  carve_reject(gamma, m->vocab, ws, &w, st->batch);
+  hipStream_t s = hs(stream);
+  prof::Scope ps(SUBSPEC_K_REJECT, 0.0, s);
+  HIPCHK(launch_reject(gamma, m->vocab, temp, draft_temp, target_logits, st->draft_logits, st->tokens + 1, r_codes,
+                       u_codes, n_accepted, out_tokens, status, nullptr, w, s, nullptr, st->batch, gamma + 1, gamma,
+                       1));
+  return ok();
+}
+
+int subspec_batch_rollback(const subspec_batch_state* st, const int32_t* n_accepted, const int32_t* out_tokens,
+                           int32_t delta, void* stream) {
+  int r;
+  if ((r = check_batch(nullptr, st))) return r;
+  if (n_accepted && !out_tokens) return fail(SUBSPEC_EINVAL, "out_tokens is NULL");
+  HIPCHK(launch_batch_rollback(st->kv_len, st->tokens, st->gamma_max + 1, n_accepted, out_tokens,
+                               st->gamma_max + 1, st->batch, delta, hs(stream)));
+  return ok();
 }
 
 static int check_tree(int32_t k, int32_t D) {
@@ -773,11 +932,32 @@ int subspec_tree_draft(const subspec_model* m, const subspec_state* st, int32_t 
     rs.logits = st->draft_logits + (int64_t)level * m->vocab;
     rs.ld = (int64_t)(depth - 1) * m->vocab;
   }
-  if ((r = rows_forward(m, st, rs, ws, s))) return r;
+  if ((r = rows_forward(m, rows_cache(st), rs, ws, s))) return r;
   {
     prof::Scope ps(SUBSPEC_K_SAMPLE, 2.0 * rows * m->vocab, s);
-    HIPCHK(launch_tree_sample(rs.logits, rs.ld, rows, m->vocab, draft_temp, u_codes, level, k, depth, st->kv_len,
-                              st->capacity, st->tokens, s));
+    RowsSampleArgs sa{};
+    sa.logits = rs.logits;
+    sa.ld = rs.ld;
+    sa.V = m->vocab;
+    sa.T = draft_temp;
+    sa.kv_len = st->kv_len;
+    sa.kv_row = 0;
+    sa.need = 1 + k * depth;  // the whole tree must fit
+    sa.cap = st->capacity;
+    if (level == 0) {  // the root's k children: tokens[1 + c D], draws u[c]
+      sa.nout = k;
+      sa.tokens = st->tokens + 1;
+      sa.t_out = depth;
+      sa.u = u_codes;
+      sa.u_out = 1;
+    } else {  // chain c's next token tokens[1 + c D + level], draw u[k + c (D - 1) + level - 1]
+      sa.nout = 1;
+      sa.tokens = st->tokens + 1 + level;
+      sa.t_row = depth;
+      sa.u = u_codes ? u_codes + k + level - 1 : nullptr;
+      sa.u_row = depth - 1;
+    }
+    HIPCHK(launch_rows_sample(sa, rows, s));
   }
   return ok();
 }
@@ -800,7 +980,7 @@ int subspec_tree_verify(const subspec_model* m, const subspec_state* st, int32_t
   rs.draft = false;
   rs.logits = logits;
   rs.ld = m->vocab;
-  return rows_forward(m, st, rs, ws, hs(stream));
+  return rows_forward(m, rows_cache(st), rs, ws, hs(stream));
 }
 
 int subspec_tree_reject(int32_t k, int32_t depth, int32_t vocab, float temp, float draft_temp,

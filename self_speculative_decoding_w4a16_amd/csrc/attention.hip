@@ -31,6 +31,25 @@ constexpr int D = 128;     // head dim handled by these kernels
 __device__ __forceinline__ int row_node(const AttnArgs& a, int j) {
   return a.pos_offset + j * (a.row_stride > 1 ? a.row_stride : 1);
 }
+// Sequence z of a batched launch (AttnArgs.seqs > 1): its kv_len, cache
+// heads and rows of every per-row buffer.  The QKV split-k partials keep
+// their layout [split][seqs m][columns]: their split stride is seqs m rows.
+__device__ __forceinline__ void seq_rebase(AttnArgs& a, int z) {
+  if (a.seqs <= 1) return;
+  const int G = a.n_q / a.n_kv;
+  const int64_t rows = (int64_t)z * a.m;
+  a.kv_len += z;
+  a.k_cache += (int64_t)z * a.n_kv * a.cap * a.d;
+  a.v_cache += (int64_t)z * a.n_kv * a.cap * a.d;
+  a.qkv += rows * (a.n_q + 2 * a.n_kv) * a.d;
+  if (a.qkv_part) a.qkv_part += rows * (a.n_q + 2 * a.n_kv) * a.d;
+  a.q_rot += rows * a.n_q * a.d;
+  a.out += rows * a.n_q * a.d;
+  a.rope_cs += rows * a.d;
+  a.part += (int64_t)z * a.n_kv * a.splits * a.m * G * (a.d + 4);
+}
+__device__ __forceinline__ int seq_count(const AttnArgs& a) { return a.seqs > 1 ? a.seqs : 1; }
+
 // Lowest slot of node t's own chain in the static tree (tree_d > 0); node t
 // sees slots <= kv_len and those from this one up to its own.  0 in a chain.
 __device__ __forceinline__ int chain_lo(const AttnArgs& a, int kvl, int t) {
@@ -43,8 +62,11 @@ __device__ __forceinline__ int chain_lo(const AttnArgs& a, int kvl, int t) {
 // load (kv_len, the RoPE table, the values) is issued before the first use.
 template <int S>
 __global__ __launch_bounds__(64) void rope_append_kernel(AttnArgs a) {
-  const int j = blockIdx.x;          // query row
+  const int z = blockIdx.x / a.m;    // sequence (batched launches)
+  const int j = blockIdx.x - z * a.m;  // query row of that sequence
   const int head = blockIdx.y;       // 0..Hq-1: q heads, Hq..Hq+Hkv-1: kv heads
+  const int64_t part_rows = (int64_t)a.m * seq_count(a);  // rows of one split of the QKV partials
+  seq_rebase(a, z);
   const int i = threadIdx.x;         // pair index 0..d/2-1
   const int half = a.d / 2;
   if (i >= half) return;
@@ -71,7 +93,7 @@ __global__ __launch_bounds__(64) void rope_append_kernel(AttnArgs a) {
       float pv[S > 0 ? S : 1][4];
 #pragma unroll
       for (int sp = 0; sp < S; ++sp) {
-        const float* ps = p + (int64_t)sp * a.m * rs;
+        const float* ps = p + (int64_t)sp * part_rows * rs;
         pv[sp][0] = ps[c0];
         pv[sp][1] = ps[c1];
         pv[sp][2] = ps[c2];
@@ -83,7 +105,7 @@ __global__ __launch_bounds__(64) void rope_append_kernel(AttnArgs a) {
         for (int e = 0; e < 4; ++e) acc[e] += pv[sp][e];
     } else {
       for (int sp = 0; sp < a.qkv_splits; ++sp) {
-        const float* ps = p + (int64_t)sp * a.m * rs;
+        const float* ps = p + (int64_t)sp * part_rows * rs;
         acc[0] += ps[c0];
         acc[1] += ps[c1];
         acc[2] += ps[c2];
@@ -161,6 +183,7 @@ __global__ __launch_bounds__(RW * 64) void rows_attn_kernel(AttnArgs a) {
   __shared__ __align__(16) uint16_t pt[RW][2][16][VROW];  // per wave: P hi, P lo
 
   const int hk = blockIdx.x, split = blockIdx.y, tid = threadIdx.x;
+  seq_rebase(a, blockIdx.z);
   const int lane = tid & 63, wave = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
   const int G = a.n_q / a.n_kv, Qn = a.m * G;
   const int k0 = split * DKPB;
@@ -997,6 +1020,7 @@ __global__ __launch_bounds__(RW * 64) void rows_attn_long_kernel(AttnArgs a) {
   __shared__ __align__(16) uint16_t pt[RW][2][16][VROW];
 
   const int hk = blockIdx.x, split = blockIdx.y, tid = threadIdx.x;
+  seq_rebase(a, blockIdx.z);
   const int lane = tid & 63, wave = tid >> 6, r16 = lane & 15, g4 = lane >> 4;
   const int G = a.n_q / a.n_kv, Qn = a.m * G;
   const int n_tiles = (Qn + 15) / 16;
@@ -1187,7 +1211,9 @@ __global__ __launch_bounds__(RW * 64) void rows_attn_long_kernel(AttnArgs a) {
 // loads, the first batch loaded before kv_len is known.
 __global__ __launch_bounds__(128) void rows_merge_seq_kernel(AttnArgs a) {
   constexpr int B = 4;  // splits per batch of independent loads
-  const int hq = blockIdx.x, row = blockIdx.y, dd = threadIdx.x;
+  const int hq = blockIdx.x, dd = threadIdx.x;
+  const int z = blockIdx.y / a.m, row = blockIdx.y - z * a.m;  // sequence, its row
+  seq_rebase(a, z);
   const int G = a.n_q / a.n_kv, hk = hq / G, g = hq % G;
   const int64_t sstride = (int64_t)a.m * G * DREC;
   const float* base = a.part + (((int64_t)hk * a.splits * a.m + row) * G + g) * DREC;
@@ -1240,7 +1266,9 @@ __global__ __launch_bounds__(128) void rows_merge_seq_kernel(AttnArgs a) {
 // Merge of the verify partials, many splits (long contexts): grid (q head,
 // row), MP x 128 threads.
 __global__ __launch_bounds__(MP * D) void rows_merge_kernel(AttnArgs a) {
-  const int hq = blockIdx.x, row = blockIdx.y, dd = threadIdx.x % D, p = threadIdx.x / D;
+  const int hq = blockIdx.x, dd = threadIdx.x % D, p = threadIdx.x / D;
+  const int z = blockIdx.y / a.m, row = blockIdx.y - z * a.m;  // sequence, its row
+  seq_rebase(a, z);
   const int G = a.n_q / a.n_kv, hk = hq / G, g = hq % G;
   const int pos = *a.kv_len + row_node(a, row);  // the row's slot: its last key
   if (pos < 0 || pos >= a.cap) return;
@@ -1369,8 +1397,10 @@ __global__ __launch_bounds__(SW * 64) void attn_scores_kernel(AttnArgs a, float*
 
 }  // namespace
 
+static int seq_count_host(const AttnArgs& a) { return a.seqs > 1 ? a.seqs : 1; }
+
 hipError_t launch_rope_append(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid(a.m, a.n_q + a.n_kv), block(64);
+  const dim3 grid(a.m * seq_count_host(a), a.n_q + a.n_kv), block(64);
   switch (a.qkv_part ? a.qkv_splits : 0) {
 #define SS_S(n) \
   case n: SS_LAUNCH(rope_append_kernel<n>, grid, block, 0, s, a); break;
@@ -1418,18 +1448,18 @@ hipError_t launch_decode_attention(const AttnArgs& a, const int32_t* valid, hipS
 hipError_t launch_rows_attention(const AttnArgs& a, hipStream_t s) {
   if (a.split_keys > DKPB) {
     if (a.split_keys % DKPB != 0 || a.m * (a.n_q / a.n_kv) > 16 * RW) return hipErrorInvalidValue;
-    SS_LAUNCH(rows_attn_long_kernel, dim3(a.n_kv, a.splits), dim3(RW * 64), 0, s, a);
+    SS_LAUNCH(rows_attn_long_kernel, dim3(a.n_kv, a.splits, seq_count_host(a)), dim3(RW * 64), 0, s, a);
   } else {
-    SS_LAUNCH(rows_attn_kernel, dim3(a.n_kv, a.splits), dim3(RW * 64), 0, s, a);
+    SS_LAUNCH(rows_attn_kernel, dim3(a.n_kv, a.splits, seq_count_host(a)), dim3(RW * 64), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // few splits: one thread per dim walks them in order; many (long
   // contexts): MP split groups per block cut the serial memory round trips
   if (a.splits <= kSeqMergeSplits)
-    SS_LAUNCH(rows_merge_seq_kernel, dim3(a.n_q, a.m), dim3(D), 0, s, a);
+    SS_LAUNCH(rows_merge_seq_kernel, dim3(a.n_q, a.m * seq_count_host(a)), dim3(D), 0, s, a);
   else
-    SS_LAUNCH(rows_merge_kernel, dim3(a.n_q, a.m), dim3(MP * D), 0, s, a);
+    SS_LAUNCH(rows_merge_kernel, dim3(a.n_q, a.m * seq_count_host(a)), dim3(MP * D), 0, s, a);
   return hipGetLastError();
 }
 

@@ -92,7 +92,12 @@ struct AttnArgs {
   // at slot kv_len + t and position kv_len + depth, seeing slots
   // [0, kv_len] and its own chain's slots up to its own.
   int tree_d;
-  int m;                // query rows
+  int m;                // query rows (of each sequence)
+  // seqs > 1: a batch of independent sequences, rows [z m, z m + m) of every
+  // per-row buffer belong to sequence z, whose kv_len is kv_len[z] and whose
+  // cache heads are z n_kv .. z n_kv + n_kv - 1 of the layer (the cache is
+  // [seqs][n_kv][cap][d] per layer); partials [seqs][n_kv][splits][m][G][d + 4]
+  int seqs;
   int n_q, n_kv, d, cap;
   float theta;
   const float* rope_cs;  // [m][d/2][2] (cos, sin) of each row's position
@@ -145,9 +150,16 @@ hipError_t launch_rmsnorm_rows(const uint16_t* h, const uint16_t* g, float eps, 
 // order; skipped when part is null), then out[r] = RMSNorm(h[r]) * g.  k <= 8192.
 hipError_t launch_resid_rmsnorm_rows(uint16_t* h, const float* part, int splits, const uint16_t* g, float eps,
                                      int rows, int k, uint16_t* out, hipStream_t s);
-// h[r] = embed[tokens[r * tok_stride]] (ids clamped into [0, vocab)).
+// h[r] = embed[tokens[r * tok_stride]] (ids clamped into [0, vocab)); with
+// rows_per_seq > 0 the token of row r is
+// tokens[(r / rows_per_seq) * seq_stride + (r % rows_per_seq) * tok_stride].
 hipError_t launch_embed_rows(const uint16_t* embed, const int32_t* tokens, int rows, int k,
-                             int vocab, uint16_t* h, hipStream_t s, int tok_stride = 1);
+                             int vocab, uint16_t* h, hipStream_t s, int tok_stride = 1, int rows_per_seq = 0,
+                             int64_t seq_stride = 0);
+// Batched decoding: kv_len[b] += n[b] + 1, tokens[b ld] = out[b out_ld + n[b]]
+// (or, with n_accepted NULL, kv_len[b] += delta).
+hipError_t launch_batch_rollback(int32_t* kv_len, int32_t* tokens, int64_t ld, const int32_t* n_accepted,
+                                 const int32_t* out_tokens, int64_t out_ld, int batch, int delta, hipStream_t s);
 // act[r][j] = bf16(silu(gu[r][j]) * gu[r][F + j]) for r < rows, j < F.
 hipError_t launch_silu_rows(const uint16_t* gu, int64_t F, int rows, uint16_t* act, hipStream_t s);
 // Static tree: move the accepted chain's K/V next to the prefix (every layer
@@ -168,8 +180,10 @@ hipError_t launch_pos_guard(const int32_t* kv_len, const int32_t* token_in, int 
 // RoPE table [m][d/2][2] of the rows' positions: row j is node
 // t = pos_offset + j * row_stride at position kv_len + t (tree_d = 0) or
 // kv_len + depth(t) in the static tree of chains of depth tree_d.
+// rows_per_seq > 0: row j belongs to sequence j / rows_per_seq, whose kv_len
+// is kv_len[j / rows_per_seq], and is node (j % rows_per_seq) of it.
 hipError_t launch_rope_table(const int32_t* kv_len, int pos_offset, int row_stride, int tree_d, int m, int d,
-                             float theta, float* rope_cs, hipStream_t s);
+                             float theta, float* rope_cs, hipStream_t s, int rows_per_seq = 0);
 
 // ------------------------------------------------------------------ sampling / rejection
 struct SampleWs {
@@ -228,15 +242,29 @@ hipError_t launch_control_init(const ControlArgs& c, hipStream_t s);
 
 // ------------------------------------------------------------------ static token tree
 // k chains of depth D share the root; chain c's depth-d node is node
-// 1 + c D + d - 1 (node 0: the root).  Next level's tokens from a level's
-// logits (rows x [ld]): level 0 (one row) writes the k children to
-// tokens[1 + c D], level d >= 1 (k rows) chain c's next token to
-// tokens[1 + c D + d]; u (T_d > 0) holds the root's k draws, then chain c's
-// level-d draw at k + c (D - 1) + d - 1.  -1 tokens when the tree does not
-// fit the cache (kv_len + 1 + k D > cap).
-hipError_t launch_tree_sample(const uint16_t* logits, int64_t ld, int rows, int V, float Td, const uint32_t* u,
-                              int level, int k, int D, const int32_t* kv_len, int cap, int32_t* tokens,
-                              hipStream_t s);
+// 1 + c D + d - 1 (node 0: the root).
+// Tokens from rows of logits (one 1024-thread block per row): row r writes
+// nout tokens tokens[r t_row + i t_out] - its nout largest logits (T = 0;
+// larger first, lower index first on ties, token 0 past the finite ones) or
+// nout inverse-CDF draws with u[r u_row + i u_out] (T > 0) - or -1 tokens
+// when kv_len[r kv_row] + need > cap (no room in the cache).  Static tree:
+// level 0 is one row with nout = k children at tokens[1 + c D]; level
+// d >= 1 is k rows (chains) writing tokens[1 + c D + d].
+struct RowsSampleArgs {
+  const uint16_t* logits;
+  int64_t ld;
+  int V;
+  float T;
+  const uint32_t* u;
+  int64_t u_row, u_out;
+  int32_t* tokens;
+  int64_t t_row, t_out;
+  int nout;
+  const int32_t* kv_len;
+  int64_t kv_row;
+  int need, cap;
+};
+hipError_t launch_rows_sample(const RowsSampleArgs& a, int rows, hipStream_t s);
 // The root's multi-step rejection and the round's result, from the root's
 // target and draft rows and every chain's own round (chain_n [k],
 // chain_out [k][D], chain_status [k]); resid: [V] 64-bit scratch.

@@ -95,12 +95,16 @@ __global__ __launch_bounds__(1024) void rmsnorm_rows_kernel(uint16_t* __restrict
 }
 
 // Out-of-range token ids are clamped into [0, vocab) so a bad id cannot read
-// outside the table.  Row r takes tokens[r * stride].
+// outside the table.  Row r takes tokens[r * stride], or with rows_per_seq
+// > 0 tokens[(r / rows_per_seq) * seq_stride + (r % rows_per_seq) * stride].
 __global__ __launch_bounds__(256) void embed_rows_kernel(const uint16_t* __restrict__ embed,
                                                          const int32_t* __restrict__ tokens, int stride, int k,
-                                                         int vocab, uint16_t* __restrict__ h) {
+                                                         int vocab, uint16_t* __restrict__ h, int rows_per_seq,
+                                                         int64_t seq_stride) {
   const int row = blockIdx.x;
-  const int tok = min(max(tokens[(int64_t)row * stride], 0), vocab - 1);
+  const int z = rows_per_seq > 0 ? row / rows_per_seq : 0;
+  const int j = row - z * rows_per_seq;
+  const int tok = min(max(tokens[(int64_t)z * seq_stride + (int64_t)j * stride], 0), vocab - 1);
   const u32x4* src = reinterpret_cast<const u32x4*>(embed + (int64_t)tok * k);
   u32x4* dst = reinterpret_cast<u32x4*>(h + (int64_t)row * k);
   for (int q = threadIdx.x; q < k / 8; q += 256) dst[q] = src[q];
@@ -154,6 +158,22 @@ __global__ void kv_rollback_kernel(int32_t* kv_len, int32_t* tokens, const int32
 
 __global__ void kv_advance_kernel(int32_t* kv_len, int32_t delta) { *kv_len += delta; }
 
+// Batched decoding: sequence b moves by n[b] + 1 and takes its last emitted
+// token (tokens [B][ld], out [B][out_ld]); with n NULL every kv_len moves by
+// delta.  One thread per sequence.
+__global__ void batch_rollback_kernel(int32_t* kv_len, int32_t* tokens, int64_t ld, const int32_t* n_accepted,
+                                      const int32_t* out_tokens, int64_t out_ld, int batch, int delta) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= batch) return;
+  if (!n_accepted) {
+    kv_len[b] += delta;
+    return;
+  }
+  const int n = n_accepted[b];
+  kv_len[b] += n + 1;
+  tokens[(int64_t)b * ld] = out_tokens[(int64_t)b * out_ld + n];
+}
+
 // valid = (0 <= kv_len + step < cap) and the input token is a vocabulary id;
 // when not, the draft step does nothing but set its output token to -1.
 // RoPE angles of position p, pair i < d/2: p * theta^(-2i/d) in float64,
@@ -185,11 +205,12 @@ __global__ void pos_guard_kernel(const int32_t* kv_len, const int32_t* token_in,
 // position kv_len + t, or kv_len + its depth in a tree of chains of depth
 // tree_d: grid m.
 __global__ void rope_table_kernel(const int32_t* kv_len, int pos_offset, int stride, int tree_d, int d, float theta,
-                                  float* rope_cs) {
+                                  float* rope_cs, int rows_per_seq) {
   const int j = blockIdx.x;
-  const int t = pos_offset + j * stride;
+  const int z = rows_per_seq > 0 ? j / rows_per_seq : 0;  // the row's sequence
+  const int t = pos_offset + (j - z * rows_per_seq) * stride;
   const int dep = tree_d > 0 ? (t == 0 ? 0 : (t - 1) % tree_d + 1) : t;
-  if (threadIdx.x < d / 2) rope_angle(*kv_len + dep, threadIdx.x, d, theta, rope_cs + (int64_t)j * d);
+  if (threadIdx.x < d / 2) rope_angle(kv_len[z] + dep, threadIdx.x, d, theta, rope_cs + (int64_t)j * d);
 }
 
 }  // namespace
@@ -226,8 +247,10 @@ hipError_t launch_resid_rmsnorm_rows(uint16_t* h, const float* part, int splits,
 }
 
 hipError_t launch_embed_rows(const uint16_t* embed, const int32_t* tokens, int rows, int k,
-                             int vocab, uint16_t* h, hipStream_t s, int tok_stride) {
-  SS_LAUNCH(embed_rows_kernel, dim3(rows), dim3(256), 0, s, embed, tokens, tok_stride, k, vocab, h);
+                             int vocab, uint16_t* h, hipStream_t s, int tok_stride, int rows_per_seq,
+                             int64_t seq_stride) {
+  SS_LAUNCH(embed_rows_kernel, dim3(rows), dim3(256), 0, s, embed, tokens, tok_stride, k, vocab, h, rows_per_seq,
+            seq_stride);
   return hipGetLastError();
 }
 
@@ -261,6 +284,13 @@ hipError_t launch_kv_rollback(int32_t* kv_len, int32_t* tokens, const int32_t* n
   return hipGetLastError();
 }
 
+hipError_t launch_batch_rollback(int32_t* kv_len, int32_t* tokens, int64_t ld, const int32_t* n_accepted,
+                                 const int32_t* out_tokens, int64_t out_ld, int batch, int delta, hipStream_t s) {
+  SS_LAUNCH(batch_rollback_kernel, dim3((batch + 63) / 64), dim3(64), 0, s, kv_len, tokens, ld, n_accepted, out_tokens,
+            out_ld, batch, delta);
+  return hipGetLastError();
+}
+
 hipError_t launch_kv_advance(int32_t* kv_len, int32_t delta, hipStream_t s) {
   SS_LAUNCH(kv_advance_kernel, dim3(1), dim3(1), 0, s, kv_len, delta);
   return hipGetLastError();
@@ -275,8 +305,8 @@ hipError_t launch_pos_guard(const int32_t* kv_len, const int32_t* token_in, int 
 }
 
 hipError_t launch_rope_table(const int32_t* kv_len, int pos_offset, int row_stride, int tree_d, int m, int d,
-                             float theta, float* rope_cs, hipStream_t s) {
+                             float theta, float* rope_cs, hipStream_t s, int rows_per_seq) {
   SS_LAUNCH(rope_table_kernel, dim3(m), dim3(64), 0, s, kv_len, pos_offset, row_stride < 1 ? 1 : row_stride,
-            tree_d, d, theta, rope_cs);
+            tree_d, d, theta, rope_cs, rows_per_seq);
   return hipGetLastError();
 }

@@ -5,10 +5,11 @@
 // 6.3, 6.4 and 3.7).  Here the tree is k chains sharing the root (the last
 // committed token); chain c's node at depth d is node t = 1 + c D + d - 1.
 //
-//  tree_sample   the tokens of the next level from a level's draft logits:
+//  rows_sample   the tokens of the next level from a level's draft logits:
 //                the root's k children (its k largest logits when T_d = 0,
 //                else k draws from its distribution) or each chain's next
-//                token (argmax or one draw).
+//                token (argmax or one draw); also each sequence's token of
+//                a batched draft step.
 //  tree_root     SpecInfer's multi-step speculative sampling at the root:
 //                child c is accepted when r_c < p_c(x_c) / q(x_c), with
 //                p_{c+1} = norm(max(0, p_c - q)) after a rejection (q one-hot
@@ -103,31 +104,28 @@ __device__ int seg_pick(unsigned long long th, unsigned long long base, unsigned
   return t;
 }
 
-__global__ __launch_bounds__(kTB) void tree_sample_kernel(const uint16_t* __restrict__ logits, int64_t ld, int V,
-                                                          float Td, const uint32_t* __restrict__ u, int level, int k,
-                                                          int D, const int32_t* kv_len, int cap, int32_t* tokens) {
+__global__ __launch_bounds__(kTB) void rows_sample_kernel(RowsSampleArgs a) {
   __shared__ float rv[kTW];
   __shared__ int ri[kTW];
   __shared__ unsigned long long red[kTW];
   __shared__ int s_tok;
-  const int r = blockIdx.x, tid = threadIdx.x;
-  const uint16_t* z = logits + (int64_t)r * ld;
+  const int r = blockIdx.x, tid = threadIdx.x, V = a.V;
+  const uint16_t* z = a.logits + (int64_t)r * a.ld;
   const int seg = (V + kTB - 1) / kTB;
   const int lo = min(V, tid * seg), hi = min(V, lo + seg);
-  const bool fits = *kv_len + 1 + k * D <= cap;
-  const int nout = level == 0 ? k : 1;
-  auto out_slot = [&](int i) { return level == 0 ? tokens + 1 + i * D : tokens + 1 + r * D + level; };
-  if (!fits) {  // the tree does not fit the cache: no candidates (the round skips them)
-    if (tid < nout) *out_slot(tid) = -1;
+  const bool fits = a.kv_len[(int64_t)r * a.kv_row] + a.need <= a.cap;
+  auto out_slot = [&](int i) { return a.tokens + (int64_t)r * a.t_row + (int64_t)i * a.t_out; };
+  if (!fits) {  // past the cache: no candidate (the round skips it)
+    if (tid < a.nout) *out_slot(tid) = -1;
     return;
   }
-  ss::ArgMax a = {-INFINITY, ss::kNoIndex};
-  for (int j = lo; j < hi; ++j) a = ss::better(a, ss::cand(ss::bf2f(z[j]), j));
-  a = block_argmax_1k(a, rv, ri);
-  if (Td == 0.0f) {
-    if (tid == 0) *out_slot(0) = ss::argmax_token(a);
-    ss::ArgMax prev = a;
-    for (int c = 1; c < nout; ++c) {  // next in (larger value, lower index) order
+  ss::ArgMax am = {-INFINITY, ss::kNoIndex};
+  for (int j = lo; j < hi; ++j) am = ss::better(am, ss::cand(ss::bf2f(z[j]), j));
+  am = block_argmax_1k(am, rv, ri);
+  if (a.T == 0.0f) {
+    if (tid == 0) *out_slot(0) = ss::argmax_token(am);
+    ss::ArgMax prev = am;
+    for (int c = 1; c < a.nout; ++c) {  // next in (larger value, lower index) order
       ss::ArgMax b = {-INFINITY, ss::kNoIndex};
       if (prev.i != ss::kNoIndex) {
         for (int j = lo; j < hi; ++j) {
@@ -141,18 +139,18 @@ __global__ __launch_bounds__(kTB) void tree_sample_kernel(const uint16_t* __rest
     }
     return;
   }
-  const float M = a.v;
+  const float M = am.v, T = a.T;
   unsigned long long mine = 0;
-  for (int j = lo; j < hi; ++j) mine += wt(ss::bf2f(z[j]), M, Td);
+  for (int j = lo; j < hi; ++j) mine += wt(ss::bf2f(z[j]), M, T);
   unsigned long long S;
   const unsigned long long base = block_excl_1k(mine, red, &S);
-  for (int i = 0; i < nout; ++i) {
-    const uint32_t uc = u[level == 0 ? i : k + r * (D - 1) + level - 1];
+  for (int i = 0; i < a.nout; ++i) {
+    const uint32_t uc = a.u[(int64_t)r * a.u_row + (int64_t)i * a.u_out];
     int tok = 0;
     if (S > 0) {
       if (tid == 0) s_tok = V - 1;
       const unsigned long long th = ss::shr128(ss::mul64((unsigned long long)uc, S), 24);
-      tok = seg_pick(th, base, mine, lo, hi, [&](int j) { return wt(ss::bf2f(z[j]), M, Td); }, &s_tok);
+      tok = seg_pick(th, base, mine, lo, hi, [&](int j) { return wt(ss::bf2f(z[j]), M, T); }, &s_tok);
     }
     if (tid == 0) *out_slot(i) = tok;
   }
@@ -278,10 +276,8 @@ __global__ __launch_bounds__(kTB) void tree_root_kernel(const uint16_t* __restri
 
 }  // namespace
 
-hipError_t launch_tree_sample(const uint16_t* logits, int64_t ld, int rows, int V, float Td, const uint32_t* u,
-                              int level, int k, int D, const int32_t* kv_len, int cap, int32_t* tokens,
-                              hipStream_t s) {
-  SS_LAUNCH(tree_sample_kernel, dim3(rows), dim3(kTB), 0, s, logits, ld, V, Td, u, level, k, D, kv_len, cap, tokens);
+hipError_t launch_rows_sample(const RowsSampleArgs& a, int rows, hipStream_t s) {
+  SS_LAUNCH(rows_sample_kernel, dim3(rows), dim3(kTB), 0, s, a);
   return hipGetLastError();
 }
 

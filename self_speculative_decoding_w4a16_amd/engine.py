@@ -367,3 +367,136 @@ class TreeDecoder:
                 on_cycle(c, n)
             c += 1
         return out[:n_generate], ns
+
+
+class BatchDecoder:
+    """B independent sequences decoded together on shared weights ("SubSpec"
+    report, section 10.3, item 11: the substitutes serve several users): every
+    draft step runs the B rows through the draft in one weight stream (4-bit
+    layers on the matrix-core skinny GEMM), one verify pass covers the
+    gamma + 1 positions of every sequence, and each sequence has its own
+    rejection round and rollback.  Every step is a call into libsubspec; with
+    ``graphs`` a whole cycle is recorded once and replayed."""
+
+    def __init__(self, model, batch, capacity, gamma, temp=0.0, draft_temp=0.0, device="cuda", graphs=False):
+        s = model.shape
+        self.model = model
+        self.batch, self.gamma = int(batch), int(gamma)
+        self.temp, self.draft_temp = float(temp), float(draft_temp)
+        self.capacity = capacity
+        L, V, B = model.n_layers, s.vocab, self.batch
+        self.k_cache = torch.zeros((L, B, s.n_kv_heads, capacity, s.head_dim), dtype=torch.bfloat16, device=device)
+        self.v_cache = torch.zeros_like(self.k_cache)
+        self.kv_len = torch.zeros(B, dtype=torch.int32, device=device)
+        self.tokens = torch.zeros((B, gamma + 1), dtype=torch.int32, device=device)
+        self.draft_logits = torch.zeros((B, max(gamma, 1), V), dtype=torch.bfloat16, device=device)
+        self.target_logits = torch.zeros((B, gamma + 1, V), dtype=torch.bfloat16, device=device)
+        self.n_accepted = torch.zeros(B, dtype=torch.int32, device=device)
+        self.out_tokens = torch.zeros((B, gamma + 1), dtype=torch.int32, device=device)
+        self.status = torch.zeros(B, dtype=torch.int32, device=device)
+        self.zeros = torch.zeros(B, dtype=torch.int32, device=device)
+        self.chunk = max(1, min(64, 512 // B))
+        self.prefill_tokens = torch.zeros((B, self.chunk), dtype=torch.int32, device=device)
+        self.ud_buf = torch.zeros((B, max(gamma, 1)), dtype=torch.int32, device=device)
+        self.r_buf = torch.zeros((B, max(gamma, 1)), dtype=torch.int32, device=device)
+        self.uf_buf = torch.zeros(B, dtype=torch.int32, device=device)
+        nbytes = _lib.batch_workspace_bytes(model.c, B, max(gamma + 1, self.chunk), capacity)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _lib.workspace_init(self.ws)
+        self.c = _lib.BatchState(self.k_cache.data_ptr(), self.v_cache.data_ptr(), capacity, B,
+                                 self.kv_len.data_ptr(), self.tokens.data_ptr(), self.draft_logits.data_ptr(), gamma)
+        self.use_graphs = graphs
+        self._graphs = {}
+        self._warm = set()
+
+    def reset(self, kv_len, last_tokens):
+        self.kv_len.copy_(torch.as_tensor(kv_len, dtype=torch.int32).expand(self.batch))
+        self.tokens[:, 0] = torch.as_tensor(last_tokens, dtype=torch.int32)
+
+    def prefill(self, prompts):
+        """prompts: B token lists of one length P; afterwards kv_len = P - 1
+        and tokens[b][0] = prompts[b][-1]."""
+        P = len(prompts[0])
+        if any(len(p) != P for p in prompts):
+            raise ValueError("batched prefill takes prompts of one length")
+        self.reset(0, [p[-1] for p in prompts])
+        body = torch.tensor([list(p[:-1]) for p in prompts], dtype=torch.int32)
+        for c0 in range(0, P - 1, self.chunk):
+            n = min(self.chunk, P - 1 - c0)
+            self.prefill_tokens[:, :n].copy_(body[:, c0:c0 + n])
+            _lib.batch_verify(self.model.c, self.c, n, self.prefill_tokens, self.chunk, None, self.ws)
+            _lib.batch_rollback(self.c, None, None, n)
+
+    def draft(self, u_draft=None):
+        for i in range(self.gamma):
+            _lib.batch_draft_step(self.model.c, self.c, i, self.draft_temp, u_draft, self.ws)
+
+    def verify(self):
+        _lib.batch_verify(self.model.c, self.c, self.gamma + 1, self.tokens, self.gamma + 1, self.target_logits, self.ws)
+
+    def reject(self, r_codes=None, u_codes=None):
+        _lib.batch_reject(self.model.c, self.c, self.temp, self.draft_temp, self.target_logits, r_codes, u_codes,
+                          self.n_accepted, self.out_tokens, self.status, self.ws)
+
+    def commit(self):
+        _lib.batch_rollback(self.c, self.n_accepted, self.out_tokens)
+
+    def ar_step(self):
+        """One plain autoregressive step of every sequence on the draft
+        weights (the target itself when nothing is substituted): step 0 of the
+        draft, then kv_len += 1 and tokens[b][0] = tokens[b][1]."""
+        _lib.batch_draft_step(self.model.c, self.c, 0, self.draft_temp, None, self.ws)
+        _lib.batch_rollback(self.c, self.zeros, self.tokens[:, 1:])
+
+    def _cycle_body(self, stochastic):
+        self.draft(self.ud_buf if stochastic else None)
+        self.verify()
+        self.reject(self.r_buf if stochastic else None, self.uf_buf if stochastic else None)
+        self.commit()
+
+    def cycle(self, u_draft=None, r_codes=None, u_codes=None):
+        stochastic = u_draft is not None or r_codes is not None or u_codes is not None
+        if stochastic:
+            if u_draft is not None:
+                self.ud_buf.copy_(u_draft)
+            if r_codes is not None:
+                self.r_buf.copy_(r_codes)
+            if u_codes is not None:
+                self.uf_buf.copy_(u_codes)
+        if not self.use_graphs or stochastic not in self._warm:
+            self._cycle_body(stochastic)
+            self._warm.add(stochastic)
+            return
+        g = self._graphs.get(stochastic)
+        if g is None:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self._cycle_body(stochastic)
+            self._graphs[stochastic] = g
+        g.replay()
+
+    def generate(self, prompts, n_generate, uniforms=None):
+        """At least n_generate tokens for every sequence; ``uniforms`` =
+        (U_draft [C][B][gamma], R [C][B][gamma], U [C][B]) device int32, or
+        None (greedy).  Returns (per-sequence tokens, per-cycle n lists)."""
+        kv = len(prompts[0]) - 1
+        self.prefill(prompts)
+        outs = [[] for _ in range(self.batch)]
+        ns = []
+        c = 0
+        lens = [kv] * self.batch
+        while min(len(o) for o in outs) < n_generate:
+            if max(lens) + self.gamma + 1 > self.capacity:
+                raise ValueError(f"KV capacity {self.capacity} reached")
+            if uniforms is not None:
+                self.cycle(uniforms[0][c], uniforms[1][c], uniforms[2][c])
+            else:
+                self.cycle()
+            n = self.n_accepted.tolist()
+            out = self.out_tokens.tolist()
+            for b in range(self.batch):
+                outs[b] += out[b][:n[b] + 1]
+                lens[b] += n[b] + 1
+            ns.append(n)
+            c += 1
+        return [o[:n_generate] for o in outs], ns

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared():
         assert hasattr(l, name), name
     assert set(_declared()) == set(_lib.EXPORTS)
-    assert _lib.abi_version() == 3  # the static tree entry points
+    assert _lib.abi_version() == 4  # batched decoding entry points
 
 
 V = ctypes.c_void_p
@@ -197,6 +197,30 @@ def test_tree_argument_errors():
     assert tr(0, 48, 1000, 0.0, 0.0, V(p), V(p), V(p), None, None, V(p), V(p), V(p), V(p), ws, big, None) == _lib.EINVAL
     assert tr(6, 48, 1000, 0.0, 0.0, V(p), V(p), V(p), None, None, V(p), V(p), V(p), V(p), ws, 64, None) == _lib.EWORKSPACE
     assert l.subspec_tree_commit(by(m), by(st), 6, 48, None, V(p), V(p), None) == _lib.EINVAL
+
+
+def test_batch_argument_errors():
+    l = _lib.lib()
+    m, keep = _fake_model()
+    p = 4096
+    by = ctypes.byref
+    big = 1 << 40
+    ws = V(p)
+    assert l.subspec_batch_workspace_bytes(by(m), 4, 17, 1024) > 64 * 1024
+    assert l.subspec_batch_workspace_bytes(by(m), 17, 17, 1024) == 0  # batch above 16
+    assert l.subspec_batch_workspace_bytes(by(m), 16, 64, 1024) == 0  # 1024 rows
+    st = _lib.BatchState(p, p, 1024, 4, p, p, p, 4)
+    assert l.subspec_batch_draft_step(by(m), by(st), 4, 0.0, None, ws, big, None) == _lib.EINVAL  # step >= gamma
+    assert l.subspec_batch_draft_step(by(m), by(st), 0, 0.5, None, ws, big, None) == _lib.EINVAL  # no uniforms
+    assert l.subspec_batch_draft_step(by(m), by(st), 0, 0.0, None, ws, 128, None) == _lib.EWORKSPACE
+    bad = _lib.BatchState(p, p, 1024, 0, p, p, p, 4)
+    assert l.subspec_batch_draft_step(by(m), by(bad), 0, 0.0, None, ws, big, None) == _lib.EINVAL
+    assert l.subspec_batch_verify(by(m), by(st), 0, V(p), 5, None, ws, big, None) == _lib.EINVAL
+    assert l.subspec_batch_verify(by(m), by(st), 5, V(p), 4, None, ws, big, None) == _lib.EINVAL  # ld < n
+    assert l.subspec_batch_verify(by(m), by(st), 5, None, 5, None, ws, big, None) == _lib.EINVAL
+    assert l.subspec_batch_reject(by(m), by(st), 1.0, 1.0, V(p), None, V(p), V(p), V(p), V(p), ws, big,
+                                  None) == _lib.EINVAL
+    assert l.subspec_batch_rollback(by(st), V(p), None, 0, None) == _lib.EINVAL
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
