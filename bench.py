@@ -336,6 +336,9 @@ def main():
     if args.config == "full7b" and not args.no_small:
         batch = batch_rates(dm, shape, dev)
         log(f"4-bit skinny GEMM (batch of drafts): {json.dumps(batch)}")
+    bdec = None
+    if args.config == "full7b" and not args.no_small and not stochastic:
+        bdec = batch_decode_rates(dm, w, shape, wl, dev)
     tree = None
     if args.config == "full7b" and not args.no_small and not stochastic:
         tree = tree_rates(dec, dm, shape, wl, kv0, last)
@@ -400,6 +403,7 @@ def main():
         "adaptive_length": adapt,
         "batch_w4_gemm": batch,
         "tree": tree,
+        "batch_decode": bdec,
         "kernels": kern,
     }
     # every rate also against the measured read ceiling
@@ -837,6 +841,58 @@ def tree_rates(dec, dm, shape, wl, kv0, last, k=6, depth=48, G=64, steps=1):
             "verify_pass": hbm(verify_b, ver, f"tree verify pass ({nodes} positions, every launch, graph-replayed)",
                                mfma_tflops=round(tflops, 1),
                                mfma_frac=round(tflops / BF16_MFMA_PEAK_TFLOPS, 4))}
+
+
+def batch_decode_rates(dm, w, shape, wl, dev, G=32, batches=(1, 2, 4, 8, 16)):
+    """Batched decoding of B sequences on the same model (the SubSpec
+    report's open question of where sharing the substitutes among 2-8 users
+    stops paying, section 10.3, item 11): greedy speculative decoding with
+    gamma = 16 (graph-replayed cycles) against plain batched bf16
+    autoregressive decoding (graph-replayed steps), total tokens/s over all B
+    sequences, B random prompts of the workload's prompt length."""
+    import time
+
+    import numpy as np
+    import torch
+
+    from self_speculative_decoding_w4a16_amd import _lib
+    from self_speculative_decoding_w4a16_amd.engine import BatchDecoder
+    from self_speculative_decoding_w4a16_amd.model import DeviceModel
+    from synth import token_ids
+    full = DeviceModel(shape, w, substitute_layers=[])
+    P, gamma = wl.prompt, wl.gamma
+    cap = P + G + 2 * (gamma + 1) + 64
+    out = {}
+    for B in batches:
+        prompts = [[int(t) for t in token_ids(P, shape.vocab, 900 + b)] for b in range(B)]
+        d = BatchDecoder(dm, B, cap, gamma, graphs=True)
+        d.generate(prompts, gamma + 1)  # eager cycle, then the recorded graph
+        d.generate(prompts, gamma + 1)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        toks, ns = d.generate(prompts, G)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        emitted = sum(sum(n[b] + 1 for n in ns) for b in range(B))
+        d.prefill(prompts)
+        t_step = replay_us(lambda: _lib.batch_draft_step(dm.c, d.c, 0, 0.0, None, d.ws), reps=10)
+        d.prefill(prompts)
+        t_ver = replay_us(d.verify, reps=5)
+        del d
+        a = BatchDecoder(full, B, cap, 1)
+        a.prefill(prompts)
+        t_ar = replay_us(a.ar_step, reps=G)
+        del a
+        torch.cuda.empty_cache()
+        out[f"B{B}"] = {"spec_tokens_s": round(emitted / el, 2),
+                        "tau": round(float(np.mean([n + 1 for c in ns for n in c])), 4),
+                        "ar_tokens_s": round(B / (t_ar * 1e-6), 2),
+                        "ar_step_us": round(t_ar, 1), "draft_step_us": round(t_step, 1),
+                        "verify_pass_us": round(t_ver, 1)}
+        log(f"batch B={B}: {json.dumps(out[f'B{B}'])}")
+    del full
+    torch.cuda.empty_cache()
+    return out
 
 
 def tiny_rates(dev, reps=200):
