@@ -307,7 +307,8 @@ int subspec_reject_len(int32_t gamma, int32_t vocab, float temp, float draft_tem
  * region, length and tokens.  Buffers (device): k_cache / v_cache bf16
  * [L][batch][Hkv][capacity][d]; kv_len [batch]; tokens [batch][gamma_max + 1]
  * ([b][0] the last committed token, [b][1..] drafts); draft_logits
- * [batch][gamma_max][vocab].  1 <= batch <= 16 (the draft step's rows). */
+ * [batch][gamma_max][vocab].  1 <= batch <= 16 (the draft step's rows);
+ * the draft step takes vocab <= 524288. */
 typedef struct {
   uint16_t *k_cache, *v_cache;
   int32_t capacity;
@@ -369,7 +370,7 @@ int subspec_batch_rollback(const subspec_batch_state *st, const int32_t *n_accep
  * 1 + c (D - 1) + d - 1 chain c's depth-d node).  kv_len + 1 + k D must not
  * exceed the capacity (checked on the device: a tree that does not fit gets
  * -1 children, and its round emits one token).  1 <= k <= 16, 1 <= D <= 64,
- * 1 + k D <= 512; draft weights bf16 or 4-bit.  One cycle: tree_draft for
+ * 1 + k D <= 512; vocab <= 524288; draft weights bf16 or 4-bit.  One cycle: tree_draft for
  * level 0 .. D - 1, tree_verify, tree_reject, tree_commit. */
 
 /* Workspace bytes of the four calls below (0 on invalid arguments). */

@@ -741,6 +741,7 @@ int subspec_verify(const subspec_model* m, const subspec_state* st, int32_t n_to
 }
 
 constexpr int kMaxBatch = 16;
+constexpr int kMaxRowsVocab = 524288;  // vocabulary of the one-block-per-row samplers (64 chunks of 8192)
 
 static int check_batch(const subspec_model* m, const subspec_batch_state* st) {
   if (!st) return fail(SUBSPEC_EINVAL, "batch state is NULL");
@@ -781,6 +782,7 @@ int subspec_batch_draft_step(const subspec_model* m, const subspec_batch_state* 
                              const uint32_t* u_codes, void* ws, size_t ws_bytes, void* stream) {
   int r;
   if ((r = check_model(m)) || (r = check_batch(m, st)) || (r = check_tree_draft_weights(m))) return r;
+  if (m->vocab > kMaxRowsVocab) return fail(SUBSPEC_EUNSUPPORTED, "vocab above %d", kMaxRowsVocab);
   if (!st->draft_logits) return fail(SUBSPEC_EINVAL, "batch state draft_logits must be set");
   if (step < 0 || step >= st->gamma_max)
     return fail(SUBSPEC_EINVAL, "step %d outside [0, gamma_max = %d)", step, st->gamma_max);
@@ -905,6 +907,7 @@ int subspec_tree_draft(const subspec_model* m, const subspec_state* st, int32_t 
   if ((r = check_model(m)) || (r = check_state(m, st)) || (r = check_tree(k, depth)) ||
       (r = check_tree_draft_weights(m)))
     return r;
+  if (m->vocab > kMaxRowsVocab) return fail(SUBSPEC_EUNSUPPORTED, "vocab above %d", kMaxRowsVocab);
   if (!st->draft_logits) return fail(SUBSPEC_EINVAL, "state.draft_logits must be set");
   if (level < 0 || level >= depth) return fail(SUBSPEC_EINVAL, "level %d outside [0, depth = %d)", level, depth);
   if (!(draft_temp >= 0.0f)) return fail(SUBSPEC_EINVAL, "draft_temp must be >= 0");
@@ -989,7 +992,7 @@ int subspec_tree_reject(int32_t k, int32_t depth, int32_t vocab, float temp, flo
                         int32_t* out_tokens, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
   int r;
   if ((r = check_tree(k, depth))) return r;
-  if (vocab < 1 || vocab > (1 << 24)) return fail(SUBSPEC_EINVAL, "vocab outside [1, 2^24]");
+  if (vocab < 1 || vocab > kMaxRowsVocab) return fail(SUBSPEC_EINVAL, "vocab outside [1, %d]", kMaxRowsVocab);
   if (!(temp >= 0.0f) || !(draft_temp >= 0.0f)) return fail(SUBSPEC_EINVAL, "temperatures must be >= 0");
   if (!target_logits || !draft_logits || !tokens || !n_accepted || !chain || !out_tokens || !status)
     return fail(SUBSPEC_EINVAL, "NULL buffer");

@@ -22,8 +22,12 @@
 // Arithmetic: the integer weights of the plain round (floor(w 2^40) of
 // exp((z - M) / T) in float32), 128-bit accept tests, residuals kept below
 // 2^41 (the first shifted by bitlength(S_d) - 1, later ones by one bit more),
-// inverse CDF in ascending token order.  One block of 1024 threads per row;
-// thread i owns the contiguous segment [i s, i s + s) of the vocabulary.
+// inverse CDF in ascending token order.  One block of 1024 threads per row.
+// Every pass over the vocabulary is coalesced: the row is cut into chunks of
+// 8192 tokens and thread t takes the 8 tokens 8 t .. 8 t + 7 of each chunk,
+// so a wave reads 1 KiB of consecutive logits; a draw keeps the per-wave
+// weight sums of every chunk (a chunk, then a wave in it, then a lane's 8
+// tokens locate the threshold in ascending token order).
 #include "common.h"
 #include "internal.h"
 #include "profile.h"
@@ -32,6 +36,9 @@ namespace {
 
 constexpr int kTB = 1024;
 constexpr int kTW = kTB / 64;
+constexpr int kPiece = 8;                 // tokens per thread and chunk
+constexpr int kChunk = kTB * kPiece;      // 8192 tokens
+constexpr int kMaxChunks = 64;            // vocabularies up to 524288 tokens
 
 __device__ __forceinline__ unsigned long long wt(float z, float M, float T) { return ss::fixed_weight(z, M, T); }
 
@@ -60,97 +67,138 @@ __device__ unsigned long long block_sum_1k(unsigned long long v, unsigned long l
   return t;
 }
 
-// Exclusive prefix of the threads' values (thread order) and their total.
-__device__ unsigned long long block_excl_1k(unsigned long long v, unsigned long long* red,
-                                            unsigned long long* total) {
+// first token of this thread's piece of chunk c
+__device__ __forceinline__ int piece0(int c) { return c * kChunk + kPiece * (int)threadIdx.x; }
+
+// Per-wave weight sums of every chunk (wsum[c][wave]) and the row's total.
+template <typename W>
+__device__ unsigned long long chunk_sums(int V, W weight, unsigned long long* wsum, unsigned long long* red) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  unsigned long long incl = v;
+  const int nch = (V + kChunk - 1) / kChunk;
+  unsigned long long tot = 0;
+  for (int c = 0; c < nch; ++c) {
+    const int j0 = piece0(c);
+    unsigned long long s = 0;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const unsigned long long t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
+    for (int e = 0; e < kPiece; ++e)
+      if (j0 + e < V) s += weight(j0 + e);
+    s = ss::wave_sum_u64(s);
+    if (lane == 0) wsum[c * kTW + w] = s;
+    tot += s;
   }
-  __syncthreads();
-  if (lane == 63) red[w] = incl;
-  __syncthreads();
-  unsigned long long off = 0, tot = 0;
-  for (int i = 0; i < kTW; ++i) {
-    if (i < w) off += red[i];
-    tot += red[i];
-  }
-  *total = tot;
-  return off + incl - v;
+  return block_sum_1k(lane == 0 ? tot : 0ull, red);
 }
 
-// Smallest j whose inclusive prefix weight exceeds th (0 <= th < total):
-// the thread whose segment [lo, hi) holds it walks the segment.
-template <typename F>
-__device__ int seg_pick(unsigned long long th, unsigned long long base, unsigned long long mine, int lo, int hi,
-                        F weight, int* s_tok) {
+// Smallest token whose inclusive prefix weight exceeds th (0 <= th < total),
+// from the per-wave chunk sums: thread 0 finds the chunk and the wave, that
+// wave scans its lanes' piece sums, the lane holding th walks its 8 tokens.
+template <typename W>
+__device__ int draw_token(unsigned long long th, int V, W weight, const unsigned long long* wsum, int* s_cw,
+                          unsigned long long* s_base, int* s_tok) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int nch = (V + kChunk - 1) / kChunk;
   __syncthreads();
-  if (mine > 0 && base <= th && th - base < mine) {
-    unsigned long long c = base;
-    for (int j = lo; j < hi; ++j) {
-      c += weight(j);
-      if (c > th) {
-        *s_tok = j;
+  if (threadIdx.x == 0) {
+    unsigned long long base = 0;
+    int cw = nch * kTW - 1;
+    for (int i = 0; i < nch * kTW; ++i) {
+      if (base + wsum[i] > th) {
+        cw = i;
         break;
+      }
+      base += wsum[i];
+    }
+    *s_cw = cw;
+    *s_base = base;
+    *s_tok = V - 1;
+  }
+  __syncthreads();
+  const int cw = *s_cw;
+  if (w == cw % kTW) {
+    const int j0 = (cw / kTW) * kChunk + kPiece * (int)threadIdx.x;
+    unsigned long long mine = 0;
+#pragma unroll
+    for (int e = 0; e < kPiece; ++e)
+      if (j0 + e < V) mine += weight(j0 + e);
+    unsigned long long incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const unsigned long long t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    const unsigned long long base = *s_base + incl - mine;
+    if (mine > 0 && base <= th && th - base < mine) {
+      unsigned long long c = base;
+      for (int e = 0; e < kPiece && j0 + e < V; ++e) {
+        c += weight(j0 + e);
+        if (c > th) {
+          *s_tok = j0 + e;
+          break;
+        }
       }
     }
   }
   __syncthreads();
   const int t = *s_tok;
-  __syncthreads();  // read by every thread before s_tok is set again
+  __syncthreads();  // read by every thread before the shared slots are set again
   return t;
+}
+
+// Argmax (and, with prev, the best token after prev in (larger value,
+// lower index) order) over a row, coalesced.
+__device__ ss::ArgMax row_argmax(const uint16_t* z, int V, const ss::ArgMax* prev, float* rv, int* ri) {
+  ss::ArgMax a = {-INFINITY, ss::kNoIndex};
+  const int nch = (V + kChunk - 1) / kChunk;
+  for (int c = 0; c < nch; ++c) {
+    const int j0 = piece0(c);
+#pragma unroll
+    for (int e = 0; e < kPiece; ++e) {
+      const int j = j0 + e;
+      if (j >= V) break;
+      const ss::ArgMax cj = ss::cand(ss::bf2f(z[j]), j);
+      if (prev && !(cj.i != ss::kNoIndex && (cj.v < prev->v || (cj.v == prev->v && cj.i > prev->i)))) continue;
+      a = ss::better(a, cj);
+    }
+  }
+  return block_argmax_1k(a, rv, ri);
 }
 
 __global__ __launch_bounds__(kTB) void rows_sample_kernel(RowsSampleArgs a) {
   __shared__ float rv[kTW];
   __shared__ int ri[kTW];
   __shared__ unsigned long long red[kTW];
-  __shared__ int s_tok;
+  __shared__ unsigned long long wsum[kMaxChunks * kTW];
+  __shared__ int s_cw, s_tok;
+  __shared__ unsigned long long s_base;
   const int r = blockIdx.x, tid = threadIdx.x, V = a.V;
   const uint16_t* z = a.logits + (int64_t)r * a.ld;
-  const int seg = (V + kTB - 1) / kTB;
-  const int lo = min(V, tid * seg), hi = min(V, lo + seg);
   const bool fits = a.kv_len[(int64_t)r * a.kv_row] + a.need <= a.cap;
   auto out_slot = [&](int i) { return a.tokens + (int64_t)r * a.t_row + (int64_t)i * a.t_out; };
   if (!fits) {  // past the cache: no candidate (the round skips it)
     if (tid < a.nout) *out_slot(tid) = -1;
     return;
   }
-  ss::ArgMax am = {-INFINITY, ss::kNoIndex};
-  for (int j = lo; j < hi; ++j) am = ss::better(am, ss::cand(ss::bf2f(z[j]), j));
-  am = block_argmax_1k(am, rv, ri);
+  const ss::ArgMax am = row_argmax(z, V, nullptr, rv, ri);
   if (a.T == 0.0f) {
     if (tid == 0) *out_slot(0) = ss::argmax_token(am);
     ss::ArgMax prev = am;
     for (int c = 1; c < a.nout; ++c) {  // next in (larger value, lower index) order
       ss::ArgMax b = {-INFINITY, ss::kNoIndex};
-      if (prev.i != ss::kNoIndex) {
-        for (int j = lo; j < hi; ++j) {
-          const ss::ArgMax cj = ss::cand(ss::bf2f(z[j]), j);
-          if (cj.i != ss::kNoIndex && (cj.v < prev.v || (cj.v == prev.v && cj.i > prev.i))) b = ss::better(b, cj);
-        }
-      }
-      b = block_argmax_1k(b, rv, ri);
+      if (prev.i != ss::kNoIndex) b = row_argmax(z, V, &prev, rv, ri);
       if (tid == 0) *out_slot(c) = ss::argmax_token(b);
       prev = b;
     }
     return;
   }
   const float M = am.v, T = a.T;
-  unsigned long long mine = 0;
-  for (int j = lo; j < hi; ++j) mine += wt(ss::bf2f(z[j]), M, T);
-  unsigned long long S;
-  const unsigned long long base = block_excl_1k(mine, red, &S);
+  auto weight = [&](int j) { return wt(ss::bf2f(z[j]), M, T); };
+  const unsigned long long S = chunk_sums(V, weight, wsum, red);
   for (int i = 0; i < a.nout; ++i) {
     const uint32_t uc = a.u[(int64_t)r * a.u_row + (int64_t)i * a.u_out];
     int tok = 0;
     if (S > 0) {
-      if (tid == 0) s_tok = V - 1;
       const unsigned long long th = ss::shr128(ss::mul64((unsigned long long)uc, S), 24);
-      tok = seg_pick(th, base, mine, lo, hi, [&](int j) { return wt(ss::bf2f(z[j]), M, T); }, &s_tok);
+      tok = draw_token(th, V, weight, wsum, &s_cw, &s_base, &s_tok);
     }
     if (tid == 0) *out_slot(i) = tok;
   }
@@ -168,17 +216,25 @@ __global__ __launch_bounds__(kTB) void tree_root_kernel(const uint16_t* __restri
   __shared__ float rv[kTW];
   __shared__ int ri[kTW];
   __shared__ unsigned long long red[kTW];
-  __shared__ int s_tok;
+  __shared__ unsigned long long wsum[kMaxChunks * kTW];
+  __shared__ int s_cw, s_tok;
+  __shared__ unsigned long long s_base;
   const int tid = threadIdx.x;
-  const int seg = (V + kTB - 1) / kTB;
-  const int lo = min(V, tid * seg), hi = min(V, lo + seg);
+  const int nch = (V + kChunk - 1) / kChunk;
+  // the root's target and draft rows: max / argmax and non-finite flags
   ss::ArgMax at = {-INFINITY, ss::kNoIndex}, ad = {-INFINITY, ss::kNoIndex};
   int bad = 0;
-  for (int j = lo; j < hi; ++j) {
-    const float a = ss::bf2f(zt[j]), b = ss::bf2f(zd[j]);
-    bad |= !ss::finite(a) || !ss::finite(b);
-    at = ss::better(at, ss::cand(a, j));
-    ad = ss::better(ad, ss::cand(b, j));
+  for (int c = 0; c < nch; ++c) {
+    const int j0 = piece0(c);
+#pragma unroll
+    for (int e = 0; e < kPiece; ++e) {
+      const int j = j0 + e;
+      if (j >= V) break;
+      const float a = ss::bf2f(zt[j]), b = ss::bf2f(zd[j]);
+      bad |= !ss::finite(a) || !ss::finite(b);
+      at = ss::better(at, ss::cand(a, j));
+      ad = ss::better(ad, ss::cand(b, j));
+    }
   }
   at = block_argmax_1k(at, rv, ri);
   ad = block_argmax_1k(ad, rv, ri);
@@ -200,15 +256,20 @@ __global__ __launch_bounds__(kTB) void tree_root_kernel(const uint16_t* __restri
   } else {
     const float Mt = at.v, Md = ad.v;
     auto wp = [&](int j) { return wt(ss::bf2f(zt[j]), Mt, T); };
-    unsigned long long mine = 0;
-    for (int j = lo; j < hi; ++j) mine += wp(j);
-    const unsigned long long St = block_sum_1k(mine, red);
-    unsigned long long Sd = 1;
-    if (Td != 0.0f) {
-      unsigned long long md = 0;
-      for (int j = lo; j < hi; ++j) md += wt(ss::bf2f(zd[j]), Md, Td);
-      Sd = block_sum_1k(md, red);
+    auto wq = [&](int j) { return wt(ss::bf2f(zd[j]), Md, Td); };
+    unsigned long long mine = 0, md = 0;
+    for (int c = 0; c < nch; ++c) {
+      const int j0 = piece0(c);
+#pragma unroll
+      for (int e = 0; e < kPiece; ++e) {
+        const int j = j0 + e;
+        if (j >= V) break;
+        mine += wp(j);
+        if (Td != 0.0f) md += wq(j);
+      }
     }
+    const unsigned long long St = block_sum_1k(mine, red);
+    const unsigned long long Sd = Td != 0.0f ? block_sum_1k(md, red) : 1ull;
     bool from_p = true;  // the current weights are p's own (else the residual array)
     unsigned long long S = St;
     for (int c = 0; c < k; ++c) {
@@ -217,7 +278,7 @@ __global__ __launch_bounds__(kTB) void tree_root_kernel(const uint16_t* __restri
         status |= 4;
         continue;
       }
-      const unsigned long long Wdx = Td == 0.0f ? 1ull : wt(ss::bf2f(zd[x]), Md, Td);
+      const unsigned long long Wdx = Td == 0.0f ? 1ull : wq(x);
       if (Wdx == 0ull) status |= 4;
       const unsigned long long Wx = from_p ? wp(x) : resid[x];
       const ss::U128 lhs = ss::mul64((unsigned long long)r_codes[c] * Wdx, S);
@@ -229,12 +290,18 @@ __global__ __launch_bounds__(kTB) void tree_root_kernel(const uint16_t* __restri
       // rejected: the next p is norm(max(0, p - q)), kept below 2^41
       const int shift = ss::bitlen_minus1(Sd) + (from_p ? 0 : 1);
       unsigned long long loc = 0;
-      for (int j = lo; j < hi; ++j) {
-        const unsigned long long Wj = from_p ? wp(j) : resid[j];
-        const unsigned long long Wdj = Td == 0.0f ? (j == x ? 1ull : 0ull) : wt(ss::bf2f(zd[j]), Md, Td);
-        const unsigned long long w = ss::resid_w(Wj, Sd, Wdj, S, shift);
-        resid[j] = w;
-        loc += w;
+      for (int cc = 0; cc < nch; ++cc) {
+        const int j0 = piece0(cc);
+#pragma unroll
+        for (int e = 0; e < kPiece; ++e) {
+          const int j = j0 + e;
+          if (j >= V) break;
+          const unsigned long long Wj = from_p ? wp(j) : resid[j];
+          const unsigned long long Wdj = Td == 0.0f ? (j == x ? 1ull : 0ull) : wq(j);
+          const unsigned long long w = ss::resid_w(Wj, Sd, Wdj, S, shift);
+          resid[j] = w;
+          loc += w;
+        }
       }
       const unsigned long long Sn = block_sum_1k(loc, red);
       if (Sn == 0ull) {  // no residual mass: back to p
@@ -247,14 +314,11 @@ __global__ __launch_bounds__(kTB) void tree_root_kernel(const uint16_t* __restri
       }
     }
     if (chosen < 0) {  // every child rejected (or skipped): one draw from the last p
-      unsigned long long m2 = 0;
-      for (int j = lo; j < hi; ++j) m2 += from_p ? wp(j) : resid[j];
-      unsigned long long tot;
-      const unsigned long long base = block_excl_1k(m2, red, &tot);
+      auto wl = [&](int j) { return from_p ? wp(j) : resid[j]; };
+      const unsigned long long tot = chunk_sums(V, wl, wsum, red);
       if (tot > 0ull) {
-        if (tid == 0) s_tok = V - 1;
         const unsigned long long th = ss::shr128(ss::mul64((unsigned long long)*u_code, tot), 24);
-        y = seg_pick(th, base, m2, lo, hi, [&](int j) { return from_p ? wp(j) : resid[j]; }, &s_tok);
+        y = draw_token(th, V, wl, wsum, &s_cw, &s_base, &s_tok);
       }
     }
   }
