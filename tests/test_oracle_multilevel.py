@@ -99,12 +99,12 @@ def test_middle_tokens_are_plain_rounds_of_the_4bit_model():
 
 
 def _peaky(seed):
-    """A 1-layer model with 6 tokens and a large lm_head (peaky, distinct
-    distributions), and as the 2-bit level a different random model."""
+    """A 1-layer model with 6 tokens and a larger lm_head (distributions far
+    from uniform), and as the 2-bit level a different random model."""
     shape = QWEN7B.with_(n_layers=1, hidden=64, ffn=128, n_q_heads=4, n_kv_heads=2, head_dim=16, vocab=6,
                          n_shared=0)
     w = model_weights(shape, seed, "cpu")
-    w["lm_head"] = w["lm_head"] * 60
+    w["lm_head"] = w["lm_head"] * 6
     om4 = oracle_model(shape, w, [0])
     w2 = model_weights(shape, seed + 100, "cpu")
     w2["lm_head"] = w["lm_head"]
@@ -130,5 +130,6 @@ def test_first_emitted_token_is_distributed_as_the_target():
                                       U2[s], R2[s], F2[s], R[s], U[s])
         counts[out[0]] += 1
     keep = p * N >= 5
+    assert keep.sum() >= 4
     chi = stats.chisquare(counts[keep], p[keep] / p[keep].sum() * counts[keep].sum())
     assert chi.pvalue > 1e-3, (counts, p * N)
