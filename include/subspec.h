@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SUBSPEC_ABI_VERSION 4
+#define SUBSPEC_ABI_VERSION 5
 
 enum {
   SUBSPEC_OK = 0,
@@ -297,6 +297,31 @@ int subspec_reject_len(int32_t gamma, int32_t vocab, float temp, float draft_tem
                        const int32_t *draft_tokens, const uint32_t *r_codes, const uint32_t *u_code,
                        const int32_t *gamma_len, int32_t *n_accepted, int32_t *out_tokens, int32_t *status,
                        float *probs, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Multi-level substitutes  ([SSR] §10.3 item 9)                             */
+/* ------------------------------------------------------------------------ */
+
+/* A 2-bit substitute drafts for the 4-bit draft, which drafts for the bf16
+ * target.  Reading: nested speculation - the 4-bit draft's gamma tokens come
+ * from inner rounds: draft steps of a model with 2-bit substitutes (the same
+ * shared layers and cache), one pass of the 4-bit draft over the drafted
+ * positions (subspec_draft_verify), the plain round (subspec_reject with
+ * p = 4-bit, q = 2-bit), and the round's last token appended after its
+ * accepted drafts (subspec_draft_append); the outer round then judges the
+ * gamma tokens against the target with q = the 4-bit logits those passes
+ * computed. */
+
+/* The draft weights' pass over n_tokens (<= 16) positions: tokens[j] at
+ * position kv_len + pos_offset + j (causal), bf16 shared layers and 4-bit
+ * substitutes; writes their K/V and, unless NULL, logits [n_tokens][vocab]. */
+int subspec_draft_verify(const subspec_model *m, const subspec_state *st, int32_t pos_offset, int32_t n_tokens,
+                         const int32_t *tokens, uint16_t *logits, void *ws, size_t ws_bytes, void *stream);
+
+/* tokens[at + n] = out_tokens[n] with n = *n_accepted (device): a round's
+ * last token placed after its accepted drafts. */
+int subspec_draft_append(const subspec_state *st, int32_t at, const int32_t *n_accepted, const int32_t *out_tokens,
+                         void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* Batched decoding: B sequences share the substitutes ([SSR] §10.3 item 11)  */

@@ -113,6 +113,9 @@ _SIGS = {
     "subspec_sample": (c_int32, [c_void_p, c_int32, c_float, c_void_p, c_void_p, c_void_p,
                                  c_size_t, c_void_p]),
     "subspec_hbm_read": (c_int32, [c_void_p, c_int64, c_void_p, c_void_p]),
+    "subspec_draft_verify": (c_int32, [POINTER(Model), POINTER(State), c_int32, c_int32, c_void_p, c_void_p,
+                                       c_void_p, c_size_t, c_void_p]),
+    "subspec_draft_append": (c_int32, [POINTER(State), c_int32, c_void_p, c_void_p, c_void_p]),
     "subspec_batch_workspace_bytes": (c_size_t, [POINTER(Model), c_int32, c_int32, c_int32]),
     "subspec_batch_draft_step": (c_int32, [POINTER(Model), POINTER(BatchState), c_int32, c_float, c_void_p, c_void_p,
                                            c_size_t, c_void_p]),
@@ -357,6 +360,15 @@ def bf16_gemm(w, x, y, ws, stream=None):
 def sample(logits, temp, u_code, token, ws, stream=None):
     check(lib().subspec_sample(_p(logits), logits.numel(), temp, _p(u_code), _p(token), _p(ws),
                                ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def draft_verify(model, state, pos_offset, n_tokens, tokens, logits, ws, stream=None):
+    check(lib().subspec_draft_verify(ctypes.byref(model), ctypes.byref(state), pos_offset, n_tokens, _p(tokens),
+                                     _p(logits), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def draft_append(state, at, n_accepted, out_tokens, stream=None):
+    check(lib().subspec_draft_append(ctypes.byref(state), at, _p(n_accepted), _p(out_tokens), _stream(stream)))
 
 
 def batch_workspace_bytes(model, batch, max_tokens, capacity):

@@ -740,6 +740,36 @@ int subspec_verify(const subspec_model* m, const subspec_state* st, int32_t n_to
   return rows_forward(m, rows_cache(st), rs, ws, hs(stream));
 }
 
+int subspec_draft_verify(const subspec_model* m, const subspec_state* st, int32_t pos_offset, int32_t n_tokens,
+                         const int32_t* tokens, uint16_t* logits, void* ws, size_t ws_bytes, void* stream) {
+  int r;
+  if ((r = check_model(m)) || (r = check_state(m, st)) || (r = check_tree_draft_weights(m))) return r;
+  if (!tokens) return fail(SUBSPEC_EINVAL, "tokens is NULL");
+  if (n_tokens < 1 || n_tokens > 16) return fail(SUBSPEC_EINVAL, "n_tokens %d outside [1, 16]", n_tokens);
+  if (pos_offset < 0 || pos_offset + n_tokens > st->capacity)
+    return fail(SUBSPEC_ECAPACITY, "positions past the KV capacity");
+  if ((r = need_ws(ws, ws_bytes, carve_fwd(m, n_tokens, st->capacity, nullptr, nullptr)))) return r;
+  RowsSpec rs{};
+  rs.tokens = tokens;
+  rs.tok_stride = 1;
+  rs.m = n_tokens;
+  rs.node0 = pos_offset;
+  rs.node_stride = 1;
+  rs.tree_d = 0;
+  rs.draft = true;
+  rs.logits = logits;
+  rs.ld = m->vocab;
+  return rows_forward(m, rows_cache(st), rs, ws, hs(stream));
+}
+
+int subspec_draft_append(const subspec_state* st, int32_t at, const int32_t* n_accepted, const int32_t* out_tokens,
+                         void* stream) {
+  if (!st || !st->tokens || !n_accepted || !out_tokens) return fail(SUBSPEC_EINVAL, "NULL buffer");
+  if (at < 0) return fail(SUBSPEC_EINVAL, "at must be >= 0");
+  HIPCHK(launch_token_append(st->tokens + at, n_accepted, out_tokens, hs(stream)));
+  return ok();
+}
+
 constexpr int kMaxBatch = 16;
 constexpr int kMaxRowsVocab = 524288;  // vocabulary of the one-block-per-row samplers (64 chunks of 8192)
 

@@ -158,6 +158,12 @@ __global__ void kv_rollback_kernel(int32_t* kv_len, int32_t* tokens, const int32
 
 __global__ void kv_advance_kernel(int32_t* kv_len, int32_t delta) { *kv_len += delta; }
 
+// A round's last token appended after its accepted drafts: dst[n] = out[n].
+__global__ void token_append_kernel(int32_t* dst, const int32_t* n_accepted, const int32_t* out_tokens) {
+  const int n = *n_accepted;
+  dst[n] = out_tokens[n];
+}
+
 // Batched decoding: sequence b moves by n[b] + 1 and takes its last emitted
 // token (tokens [B][ld], out [B][out_ld]); with n NULL every kv_len moves by
 // delta.  One thread per sequence.
@@ -288,6 +294,11 @@ hipError_t launch_batch_rollback(int32_t* kv_len, int32_t* tokens, int64_t ld, c
                                  const int32_t* out_tokens, int64_t out_ld, int batch, int delta, hipStream_t s) {
   SS_LAUNCH(batch_rollback_kernel, dim3((batch + 63) / 64), dim3(64), 0, s, kv_len, tokens, ld, n_accepted, out_tokens,
             out_ld, batch, delta);
+  return hipGetLastError();
+}
+
+hipError_t launch_token_append(int32_t* dst, const int32_t* n_accepted, const int32_t* out_tokens, hipStream_t s) {
+  SS_LAUNCH(token_append_kernel, dim3(1), dim3(1), 0, s, dst, n_accepted, out_tokens);
   return hipGetLastError();
 }
 

@@ -500,3 +500,141 @@ class BatchDecoder:
             ns.append(n)
             c += 1
         return [o[:n_generate] for o in outs], ns
+
+
+class MultiLevelDecoder:
+    """Multi-level substitutes ("SubSpec" report, section 10.3, item 9): the
+    4-bit draft's gamma tokens come from inner rounds in which a model with
+    2-bit substitutes drafts up to gamma2 tokens, the 4-bit draft runs them
+    in one pass and the plain round keeps the accepted ones plus one drawn
+    token; the bf16 target then verifies the gamma tokens with q = their
+    4-bit logits.  All levels share one KV cache.  Every step is a call into
+    libsubspec; the host reads each inner round's length (one sync a round)."""
+
+    def __init__(self, model4, model2, capacity, gamma, gamma2, temp=0.0, mid_temp=0.0, draft_temp=0.0,
+                 device="cuda"):
+        s = model4.shape
+        self.m4, self.m2 = model4, model2
+        self.gamma, self.gamma2 = int(gamma), int(gamma2)
+        self.temp, self.mid_temp, self.draft_temp = float(temp), float(mid_temp), float(draft_temp)
+        self.capacity = capacity
+        L, V = model4.n_layers, s.vocab
+        g_all = self.gamma + self.gamma2
+        kv_shape = (L, s.n_kv_heads, capacity, s.head_dim)
+        self.k_cache = torch.zeros(kv_shape, dtype=torch.bfloat16, device=device)
+        self.v_cache = torch.zeros(kv_shape, dtype=torch.bfloat16, device=device)
+        self.kv_len = torch.zeros(1, dtype=torch.int32, device=device)
+        self.tokens = torch.zeros(g_all + 1, dtype=torch.int32, device=device)
+        self.inner_logits = torch.zeros((g_all, V), dtype=torch.bfloat16, device=device)  # 2-bit, by step
+        self.mid_logits = torch.zeros((g_all + 1, V), dtype=torch.bfloat16, device=device)  # 4-bit, by position
+        self.target_logits = torch.zeros((self.gamma + 1, V), dtype=torch.bfloat16, device=device)
+        self.n_accepted = torch.zeros(1, dtype=torch.int32, device=device)
+        self.out_tokens = torch.zeros(self.gamma + 1, dtype=torch.int32, device=device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+        self.in_n = torch.zeros(1, dtype=torch.int32, device=device)
+        self.in_out = torch.zeros(self.gamma2 + 1, dtype=torch.int32, device=device)
+        self.in_status = torch.zeros(1, dtype=torch.int32, device=device)
+        self.probs = torch.zeros((max(g_all, 1), 2), dtype=torch.float32, device=device)
+        self.u2_buf = torch.zeros(g_all, dtype=torch.int32, device=device)
+        self.r2_buf = torch.zeros(max(self.gamma2, 1), dtype=torch.int32, device=device)
+        self.f2_buf = torch.zeros(1, dtype=torch.int32, device=device)
+        self.r_buf = torch.zeros(max(self.gamma, 1), dtype=torch.int32, device=device)
+        self.uf_buf = torch.zeros(1, dtype=torch.int32, device=device)
+        self.max_tokens = 64
+        self.prefill_tokens = torch.zeros(self.max_tokens, dtype=torch.int32, device=device)
+        nbytes = _lib.workspace_bytes(model4.c, self.max_tokens, capacity)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _lib.workspace_init(self.ws)
+        ptrs = (self.k_cache.data_ptr(), self.v_cache.data_ptr(), capacity, self.kv_len.data_ptr(),
+                self.tokens.data_ptr())
+        self.c = _lib.State(*ptrs, self.mid_logits.data_ptr(), g_all)
+        self.c2 = _lib.State(*ptrs, self.inner_logits.data_ptr(), g_all)
+        self.rounds = []  # (base, drafted, n, status) of the last cycle's inner rounds
+
+    def reset(self, kv_len, last_token):
+        self.kv_len.fill_(int(kv_len))
+        self.tokens[0] = int(last_token)
+
+    def prefill(self, prompt):
+        prompt = [int(t) for t in prompt]
+        self.reset(0, prompt[-1])
+        body = prompt[:-1]
+        for c0 in range(0, len(body), self.max_tokens):
+            chunk = body[c0:c0 + self.max_tokens]
+            self.prefill_tokens[:len(chunk)] = torch.tensor(chunk, dtype=torch.int32)
+            _lib.verify(self.m4.c, self.c, len(chunk), self.prefill_tokens, None, self.ws)
+            _lib.kv_advance(self.c, len(chunk))
+
+    # ------------------------------------------------------------ one cycle
+    def inner_round(self, base, g):
+        """Draft g tokens after middle token `base` with the 2-bit model, run
+        the 4-bit draft over them, judge them; returns the round's n (host)."""
+        stoch = self.draft_temp > 0
+        for i in range(g):
+            _lib.draft_step(self.m2.c, self.c2, base + i, self.draft_temp, self.u2_buf if stoch else None, self.ws)
+        _lib.draft_verify(self.m4.c, self.c, base, g + 1, self.tokens[base:], self.mid_logits[base:], self.ws)
+        stoch_p = self.mid_temp > 0
+        _lib.reject(g, self.m4.shape.vocab, self.mid_temp, self.draft_temp, self.mid_logits[base:],
+                    self.inner_logits[base:], self.tokens[base + 1:], self.r2_buf if stoch_p else None,
+                    self.f2_buf if stoch_p else None, self.in_n, self.in_out, self.in_status, self.probs, self.ws)
+        _lib.draft_append(self.c, base + 1, self.in_n, self.in_out)
+        return int(self.in_n.item())
+
+    def middle(self, cycle_uniforms=None):
+        """The gamma middle tokens (tokens[1..gamma]) and their 4-bit logits
+        (mid_logits[0..gamma)); cycle_uniforms = (U2 [gamma][gamma2],
+        R2 [gamma][gamma2], F2 [gamma]) host int arrays, or None."""
+        base, r = 0, 0
+        self.rounds = []
+        while base < self.gamma:
+            g = min(self.gamma2, self.gamma - base)
+            if cycle_uniforms is not None:
+                U2, R2, F2 = cycle_uniforms
+                self.u2_buf[base:base + g] = torch.as_tensor(U2[r][:g], dtype=torch.int32)
+                self.r2_buf[:g] = torch.as_tensor(R2[r][:g], dtype=torch.int32)
+                self.f2_buf[0] = int(F2[r])
+            n = self.inner_round(base, g)
+            self.rounds.append((base, g, n, int(self.in_status.item())))
+            base += min(n + 1, self.gamma - base)
+            r += 1
+
+    def verify(self):
+        _lib.verify(self.m4.c, self.c, self.gamma + 1, self.tokens, self.target_logits, self.ws)
+
+    def reject(self, r_codes=None, u_code=None):
+        _lib.reject(self.gamma, self.m4.shape.vocab, self.temp, self.mid_temp, self.target_logits, self.mid_logits,
+                    self.tokens[1:], r_codes, u_code, self.n_accepted, self.out_tokens, self.status, self.probs,
+                    self.ws)
+
+    def commit(self):
+        _lib.kv_rollback(self.c, self.n_accepted, self.out_tokens)
+
+    def cycle(self, cycle_uniforms=None):
+        """cycle_uniforms = (U2, R2, F2, R [gamma], U) host int arrays, or None."""
+        self.middle(None if cycle_uniforms is None else cycle_uniforms[:3])
+        self.verify()
+        if cycle_uniforms is not None and self.temp > 0:
+            self.r_buf[:self.gamma] = torch.as_tensor(cycle_uniforms[3][:self.gamma], dtype=torch.int32)
+            self.uf_buf[0] = int(cycle_uniforms[4])
+            self.reject(self.r_buf, self.uf_buf)
+        else:
+            self.reject()
+        self.commit()
+
+    def generate(self, prompt, n_generate, uniforms=None):
+        """uniforms = (U2 [C][gamma][gamma2], R2, F2 [C][gamma], R [C][gamma],
+        U [C]) host int arrays, or None (greedy)."""
+        kv = len(prompt) - 1
+        self.prefill(prompt)
+        out, ns = [], []
+        c = 0
+        while len(out) < n_generate:
+            if kv + self.gamma + self.gamma2 + 1 > self.capacity:
+                raise ValueError(f"KV capacity {self.capacity} reached")
+            self.cycle(None if uniforms is None else tuple(u[c] for u in uniforms))
+            n = int(self.n_accepted.item())
+            out += self.out_tokens[:n + 1].tolist()
+            ns.append(n)
+            kv += n + 1
+            c += 1
+        return out[:n_generate], ns

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared():
         assert hasattr(l, name), name
     assert set(_declared()) == set(_lib.EXPORTS)
-    assert _lib.abi_version() == 4  # batched decoding entry points
+    assert _lib.abi_version() == 5  # multi-level substitutes
 
 
 V = ctypes.c_void_p
