@@ -343,6 +343,9 @@ def main():
     if args.config == "full7b" and not args.no_small and not stochastic:
         tree = tree_rates(dec, dm, shape, wl, kv0, last)
         log(f"static tree k=6 D=48: {json.dumps(tree)}")
+    mlev = None
+    if args.config == "full7b" and not args.no_small and not stochastic:
+        mlev = multilevel_rates(dec, dm, w, shape, wl, kv0, last)
     adapt = None
     if not sparse and not args.no_small and not stochastic:
         adapt = adaptive_rates(dec, dm, wl, kv0, last, draft_pass["avg_us"] / verify_pass["avg_us"])
@@ -404,6 +407,7 @@ def main():
         "batch_w4_gemm": batch,
         "tree": tree,
         "batch_decode": bdec,
+        "multilevel": mlev,
         "kernels": kern,
     }
     # every rate also against the measured read ceiling
@@ -891,6 +895,67 @@ def batch_decode_rates(dm, w, shape, wl, dev, G=32, batches=(1, 2, 4, 8, 16)):
                         "verify_pass_us": round(t_ver, 1)}
         log(f"batch B={B}: {json.dumps(out[f'B{B}'])}")
     del full
+    torch.cuda.empty_cache()
+    return out
+
+
+def multilevel_rates(dec, dm, w, shape, wl, kv0, last, gamma2s=(4, 8), G=32):
+    """Multi-level substitutes ("SubSpec" report, section 10.3, item 9):
+    greedy decoding of the same model and prompt state in which a 2-bit
+    substitute model drafts gamma2 tokens at a time for the 4-bit draft, whose
+    gamma = 16 middle tokens the bf16 target verifies.  Eager host loop (one
+    sync per inner round): tokens/s, the outer tau, the inner rounds' mean
+    kept fraction n / g and rounds per cycle, and one 2-bit draft step
+    (graph-replayed) against the 4-bit one."""
+    import time
+
+    import numpy as np
+    import torch
+
+    from self_speculative_decoding_w4a16_amd import _lib
+    from self_speculative_decoding_w4a16_amd.engine import MultiLevelDecoder
+    from self_speculative_decoding_w4a16_amd.model import DeviceModel
+    dm2 = DeviceModel(shape, w, bits=2)
+    gamma = wl.gamma
+    out = {}
+    for g2 in gamma2s:
+        cap = kv0 + G + gamma + g2 + 64
+        d = MultiLevelDecoder(dm, dm2, cap, gamma, g2)
+        d.k_cache[:, :, :kv0].copy_(dec.k_cache[:, :, :kv0])
+        d.v_cache[:, :, :kv0].copy_(dec.v_cache[:, :, :kv0])
+
+        def gen():
+            d.reset(kv0, last)
+            n_out, ns, rounds = 0, [], []
+            while n_out < G:
+                d.cycle()
+                n = int(d.n_accepted.item())
+                n_out += n + 1
+                ns.append(n)
+                rounds.append(list(d.rounds))
+            return ns, rounds
+        gen()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ns, rounds = gen()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        kept = [n / g for rs in rounds for (_, g, n, _) in rs]
+        d.reset(kv0, last)
+        step2 = replay_us(lambda: _lib.draft_step(dm2.c, d.c2, 0, 0.0, None, d.ws), reps=10)
+        step4 = replay_us(lambda: _lib.draft_step(dm.c, d.c, 0, 0.0, None, d.ws), reps=10)
+        pass4 = replay_us(lambda: _lib.draft_verify(dm.c, d.c, 0, g2 + 1, d.tokens, d.mid_logits, d.ws), reps=10)
+        out[f"gamma2_{g2}"] = {"tokens_s": round(sum(n + 1 for n in ns) / el, 3),
+                               "tau": round(float(np.mean([n + 1 for n in ns])), 4),
+                               "inner_kept_frac": round(float(np.mean(kept)), 4),
+                               "inner_rounds_per_cycle": round(float(np.mean([len(r) for r in rounds])), 2),
+                               "cycle_ms": round(1000 * el / len(ns), 3),
+                               "draft_step_2bit_us": round(step2, 1), "draft_step_4bit_us": round(step4, 1),
+                               "pass_4bit_us": round(pass4, 1)}
+        log(f"multi-level gamma2={g2}: {json.dumps(out[f'gamma2_{g2}'])}")
+        del d
+        torch.cuda.empty_cache()
+    del dm2
     torch.cuda.empty_cache()
     return out
 
