@@ -7,18 +7,23 @@
 //
 //  * v_mfma_f32_16x16x32_bf16 with A = 16 positions x 32 k of x and B = 32 k
 //    x 16 weight rows as (128 + q) bf16 values (one and-or per pair of
-//    nibbles, exact).  Each MFMA's 32 k lie in one 64-group, so the group's
-//    scale and min apply after its two MFMAs:
+//    nibbles, exact), with the group's scale and min applied to the sums of
+//    its k:
 //        sum_k (q s + m) x = s * sum_k (128 + q) x + (m - 128 s) * sum_k x,
-//    the group sums of x coming from two more MFMAs with B = ones.
-//  * Lane (r, g) of a wave (r = lane % 16, g = lane / 16) covers, per
-//    128-k chunk, k = kc + 64 h + 16 g + 8 w + j for MFMA step 2 h + w (h, w
-//    in 0..1, j < 8): for each of the wave's RT tiles of 16 weight rows, two
-//    8-byte pieces of the codes of tile row r, whose eight nibbles of a step
-//    come out as the pairs (q0, q4), (q1, q5), (q2, q6), (q3, q7); the same
-//    lane loads the activations of position r at those k straight from
-//    memory (x is small and stays in the caches), pairs them the same way,
-//    and uses them for all RT tiles - so no LDS and no barrier.
+//    the group sums of x coming from MFMAs with B = ones.
+//  * Lane (r, g) of a wave (r = lane % 16, g = lane / 16) loads, per 128-k
+//    chunk (two 64-groups) and for each of the wave's RT tiles of 16 weight
+//    rows, the 16 code bytes 16 g .. 16 g + 15 of the chunk in tile row r
+//    (so one load instruction reads 16 rows x 64 contiguous bytes), i.e.
+//    k = kc + 32 g + 8 st + j for MFMA step st < 4, j < 8; a code word's
+//    eight nibbles come out as the pairs (q0, q4), (q1, q5), (q2, q6),
+//    (q3, q7).  The same lane loads the activations of position r at those k
+//    straight from memory (x is small and stays in the caches), pairs them
+//    the same way, and uses them for all RT tiles - so no LDS and no barrier.
+//  * Lanes g = 0, 1 hold the chunk's first group and g = 2, 3 its second;
+//    every step runs two MFMAs per tile, one with the activations of the
+//    second group's lanes zeroed and one with the first group's zeroed, so
+//    each accumulates one group's sums.
 //  * A = activations, B = weights: lane (r, g) of tile t ends with
 //    positions 4 g + i of the tile's row r, so it applies only its own row's
 //    scale/min (one 8-byte load per tile and chunk).
@@ -44,9 +49,9 @@ constexpr int kTargetBlocks = 512;
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 struct Slot {
-  u32x2 pc[RT][2];  // codes of the chunk's two groups, row r of each tile
-  u32x2 mt[RT];     // scale/min of the two groups, row r of each tile
-  u32x4 xv[4];      // activations of position r for the four MFMA steps
+  u32x4 pc[RT];  // 16 code bytes of the chunk, row r of each tile
+  u32x2 mt[RT];  // scale/min of the chunk's two groups, row r of each tile
+  u32x4 xv[4];   // activations of position r for the four MFMA steps
 };
 
 __global__ __launch_bounds__(64) void gemm_w4_kernel(const uint8_t* __restrict__ codes,
@@ -77,52 +82,51 @@ __global__ __launch_bounds__(64) void gemm_w4_kernel(const uint8_t* __restrict__
     const bool in = c < c1;
     const int kc = c * KC;
 #pragma unroll
-    for (int st = 0; st < 4; ++st)  // step 2 h + w: k = kc + 64 h + 16 g + 8 w .. + 7
-      sl.xv[st] = __builtin_amdgcn_raw_buffer_load_b128(
-          xrs, in ? xbase + (kc + 64 * (st >> 1) + 16 * g + 8 * (st & 1)) * 2 : kOutside, 0, 0);
+    for (int st = 0; st < 4; ++st)  // step st: k = kc + 32 g + 8 st .. + 7
+      sl.xv[st] = __builtin_amdgcn_raw_buffer_load_b128(xrs, in ? xbase + (kc + 32 * g + 8 * st) * 2 : kOutside, 0, 0);
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int rr = 16 * t + r;
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        sl.pc[t][h] =
-            __builtin_amdgcn_raw_buffer_load_b64(crs, in ? rr * (K / 2) + kc / 2 + 32 * h + 8 * g : kOutside, 0, 0);
+      sl.pc[t] = __builtin_amdgcn_raw_buffer_load_b128(crs, in ? rr * (K / 2) + kc / 2 + 16 * g : kOutside, 0, 0);
       sl.mt[t] = __builtin_amdgcn_raw_buffer_load_b64(mrs, in ? rr * (K / 16) + 4 * (kc / 64) : kOutside, 0, 0);
     }
   };
   f32x4_t acc[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const bool first = g < 2;  // this lane's k lie in the chunk's first group
   auto compute = [&](const Slot& sl) {
+    const f32x4_t zf = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t s0 = zf, s1 = zf, d0[RT], d1[RT];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      u32x4 b[2];
-      f32x4_t ds = {0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < RT; ++t) d0[t] = d1[t] = zf;
 #pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const u32x4 v = sl.xv[2 * h + w];  // (x0,x1) (x2,x3) (x4,x5) (x6,x7) -> (x0,x4) (x1,x5) (x2,x6) (x3,x7)
-        b[w] = u32x4{(v.x & 0xffffu) | (v.z << 16), (v.x >> 16) | (v.z & 0xffff0000u),
-                     (v.y & 0xffffu) | (v.w << 16), (v.y >> 16) | (v.w & 0xffff0000u)};
-        ds = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b[w]),
-                                                     __builtin_bit_cast(bf16x8_t, ones), ds, 0, 0, 0);
-      }
+    for (int st = 0; st < 4; ++st) {
+      const u32x4 v = sl.xv[st];  // (x0,x1) (x2,x3) (x4,x5) (x6,x7) -> (x0,x4) (x1,x5) (x2,x6) (x3,x7)
+      const u32x4 b = u32x4{(v.x & 0xffffu) | (v.z << 16), (v.x >> 16) | (v.z & 0xffff0000u),
+                            (v.y & 0xffffu) | (v.w << 16), (v.y >> 16) | (v.w & 0xffff0000u)};
+      const u32x4 zu = {0u, 0u, 0u, 0u};
+      const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, first ? b : zu);
+      const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, first ? zu : b);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0, __builtin_bit_cast(bf16x8_t, ones), s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1, __builtin_bit_cast(bf16x8_t, ones), s1, 0, 0, 0);
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
-        f32x4_t d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          const uint32_t cw = w ? sl.pc[t][h].y : sl.pc[t][h].x;
-          const u32x4 av = u32x4{(cw & mask) | magic, ((cw >> 4) & mask) | magic, ((cw >> 8) & mask) | magic,
-                                 ((cw >> 12) & mask) | magic};
-          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b[w]),
-                                                      __builtin_bit_cast(bf16x8_t, av), d, 0, 0, 0);
-        }
-        const uint32_t smw = h ? sl.mt[t].y : sl.mt[t].x;
-        const float sc = ss::h2f((uint16_t)(smw & 0xffffu));
-        const float mn = ss::h2f((uint16_t)(smw >> 16));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[t][i] += sc * d[i] + (mn - 128.0f * sc) * ds[i];
+        const uint32_t cw = sl.pc[t][st];
+        const bf16x8_t av = __builtin_bit_cast(
+            bf16x8_t, u32x4{(cw & mask) | magic, ((cw >> 4) & mask) | magic, ((cw >> 8) & mask) | magic,
+                            ((cw >> 12) & mask) | magic});
+        d0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0, av, d0[t], 0, 0, 0);
+        d1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1, av, d1[t], 0, 0, 0);
       }
+    }
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const float sc0 = ss::h2f((uint16_t)(sl.mt[t].x & 0xffffu)), mn0 = ss::h2f((uint16_t)(sl.mt[t].x >> 16));
+      const float sc1 = ss::h2f((uint16_t)(sl.mt[t].y & 0xffffu)), mn1 = ss::h2f((uint16_t)(sl.mt[t].y >> 16));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[t][i] += (sc0 * d0[t][i] + (mn0 - 128.0f * sc0) * s0[i]) + (sc1 * d1[t][i] + (mn1 - 128.0f * sc1) * s1[i]);
     }
   };
 
