@@ -354,7 +354,11 @@ def main():
     # ---------------------------------------------------------------- CPU oracle
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(shape, w, dm, wl, tau)
+        osample = OracleSample(shape, w, wl)
+        cpu = cpu_baseline(osample, dm, wl, tau)
+        oracle_beside(osample, cpu, wl, lowbit, batch, bdec, tree, mlev, adapt)
+        cpu.pop("_cycle_parts")
+        del osample
 
     line = {
         "metric": "spec-decode tokens/s @7B shape \u03b3=16; W4 GEMV & verify HBM GB/s vs peak",
@@ -1003,96 +1007,251 @@ def tiny_rates(dev, reps=200):
             "reject_bytes": 2 * (2 * gamma + 1) * V}
 
 
-def cpu_baseline(shape, w, dm, wl, tau):
-    """The oracle, untuned, on a bounded sample of the same workload: one
-    draft token through one shared bf16 layer (if the model has any), one W4
-    substitute layer and the lm_head, and one gamma+1-position verify through
-    one layer and the lm_head, each timed three times (median), at the
-    workload's shapes and context length
-    (synthetic KV; the long-context workload drafts over its sparse index
-    and its verify also computes the importance scores).  The per-layer
-    times are scaled to the full model, a cycle is gamma draft steps +
-    verify + reject, and tokens/s = tau (of the GPU run) / cycle."""
-    import numpy as np
+class OracleSample:
+    """The oracle, untuned (NumPy float64), on bounded samples at the
+    workload's full shapes: host copies of one shared bf16 layer (if the model
+    has any), one substitute layer (4, 3 or 2 bits) and the lm_head, over a
+    synthetic KV history.  Every timing is the median of `reps` runs; `spent`
+    sums the CPU time of all of them."""
 
-    from oracle.model import OracleModel, forward
-    from oracle.reject import reject
-    from oracle.sparse import select_index
-    from synth import kv_history, logits_pair, token_ids
+    def __init__(self, shape, w, wl):
+        import numpy as np
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        cores = os.cpu_count()
-    host = lambda t: t.detach().float().cpu().numpy()
-    log("cpu baseline: copying sampled layers to host")
-    gamma = wl.gamma
-    L, S = shape.n_layers, shape.n_shared
-    base = dict(n_layers=0, hidden=shape.hidden, ffn=shape.ffn, n_q_heads=shape.n_q_heads,
-                n_kv_heads=shape.n_kv_heads, head_dim=shape.head_dim, vocab=shape.vocab,
-                rope_theta=shape.rope_theta, rms_eps=shape.rms_eps, embed=host(w["embed"]),
-                final_norm=host(w["final_norm"]), lm_head=host(w["lm_head"]), layers=[])
-    m0 = OracleModel(**base)
-    m_sh = None
-    if S > 0:
-        m_sh = OracleModel(**{**base, "n_layers": 1,
-                              "layers": [{k: host(v) for k, v in w["layers"][0].items()}]})
-    m_w4 = OracleModel(**{**base, "n_layers": 1,
-                          "layers": [{k: host(v) for k, v in w["layers"][S].items()}]})
-    t0 = time.perf_counter()
-    m_w4.make_substitutes([0])
-    t_quant = time.perf_counter() - t0
-    kv_len = max(wl.prompt, 600)
-    cap = kv_len + gamma + 2
-    K, V = kv_history(1, shape.n_kv_heads, kv_len, shape.head_dim, cap, 44, "cpu")
-    K, V = host(K).astype(np.float64), host(V).astype(np.float64)
-    kv = lambda: (K.copy(), V.copy())
-    toks = [int(t) for t in token_ids(gamma + 1, shape.vocab, 45)]
-    K0 = np.zeros((0, shape.n_kv_heads, cap, shape.head_dim))
-    sparse, scores = None, None
-    ex = wl.extra
-    if "budget_permille" in ex:
-        rng = np.random.default_rng(46)
-        index = [[select_index(rng.random(kv_len), kv_len, ex["n_sink"], ex["n_recent"],
-                               ex["budget_permille"]) for _ in range(shape.n_kv_heads)]]
-        sparse, scores = (index, kv_len), []
+        from oracle.model import OracleModel
+        from synth import kv_history, token_ids
+        try:
+            from threadpoolctl import threadpool_info
+            self.cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # noqa: BLE001
+            self.cores = os.cpu_count()
+        self.host = lambda t: t.detach().float().cpu().numpy()
+        log("oracle sample: copying sampled layers to host")
+        self.shape, self.wl, self.w = shape, wl, w
+        S = shape.n_shared
+        self.base = dict(n_layers=0, hidden=shape.hidden, ffn=shape.ffn, n_q_heads=shape.n_q_heads,
+                         n_kv_heads=shape.n_kv_heads, head_dim=shape.head_dim, vocab=shape.vocab,
+                         rope_theta=shape.rope_theta, rms_eps=shape.rms_eps, embed=self.host(w["embed"]),
+                         final_norm=self.host(w["final_norm"]), lm_head=self.host(w["lm_head"]), layers=[])
+        self.lm = OracleModel(**self.base)
+        self.shared = None
+        if S > 0:
+            self.shared = self._one_layer(0)
+        self.sub = {}
+        t0 = time.perf_counter()
+        self.sub[4] = self._one_layer(S, bits=4)
+        self.t_quant = time.perf_counter() - t0
+        self.kv_len = max(wl.prompt, 600)
+        self.cap = self.kv_len + wl.gamma + 2
+        K, V = kv_history(1, shape.n_kv_heads, self.kv_len, shape.head_dim, self.cap, 44, "cpu")
+        self.K, self.V = self.host(K).astype(np.float64), self.host(V).astype(np.float64)
+        self.K0 = np.zeros((0, shape.n_kv_heads, self.cap, shape.head_dim))
+        self.toks = [int(t) for t in token_ids(max(wl.gamma + 1, 64), shape.vocab, 45)]
+        self.spent = 0.0
 
-    spent = [0.0]
+    def _one_layer(self, l, bits=None):
+        from oracle.model import OracleModel
+        m = OracleModel(**{**self.base, "n_layers": 1,
+                           "layers": [{k: self.host(v) for k, v in self.w["layers"][l].items()}]})
+        if bits:
+            m.make_substitutes([0], bits=bits)
+        return m
 
-    def timed(fn, reps=3):
-        # median of three runs (about 10 s of CPU work in all at the 7B shape)
+    def substitute(self, bits):
+        if bits not in self.sub:
+            self.sub[bits] = self._one_layer(self.shape.n_shared, bits=bits)
+        return self.sub[bits]
+
+    def kv(self):
+        return (self.K.copy(), self.V.copy())
+
+    def timed(self, fn, reps=3):
         ts = []
         for _ in range(reps):
             t = time.perf_counter()
             fn()
             ts.append(time.perf_counter() - t)
-        spent[0] += sum(ts)
+        self.spent += sum(ts)
         return sorted(ts)[len(ts) // 2]
 
-    t_lm1 = timed(lambda: forward(m0, (K0, K0), kv_len, toks[:1], draft=True))
-    t_sh1 = timed(lambda: forward(m_sh, kv(), kv_len, toks[:1], draft=True)) if m_sh else 0.0
-    t_w41 = timed(lambda: forward(m_w4, kv(), kv_len, toks[:1], draft=True, sparse=sparse))
-    t_lm = timed(lambda: forward(m0, (K0, K0), kv_len, toks, draft=False))
-    t_v = timed(lambda: forward(m_sh or m_w4, kv(), kv_len, toks, draft=False, scores=scores))
+    def draft_step_s(self, bits=4, reps=3, sparse=None):
+        """One draft token through the whole model: shared layers at the
+        shared layer's time, substitute layers at the sampled one's."""
+        from oracle.model import forward
+        L, S = self.shape.n_layers, self.shape.n_shared
+        if not hasattr(self, "_t_lm1"):
+            self._t_lm1 = self.timed(lambda: forward(self.lm, (self.K0, self.K0), self.kv_len, self.toks[:1],
+                                                     draft=True), reps)
+            self._t_sh1 = self.timed(lambda: forward(self.shared, self.kv(), self.kv_len, self.toks[:1],
+                                                     draft=True), reps) if self.shared else 0.0
+        m = self.substitute(bits)
+        t_sub = self.timed(lambda: forward(m, self.kv(), self.kv_len, self.toks[:1], draft=True, sparse=sparse),
+                           reps)
+        return S * max(self._t_sh1 - self._t_lm1, 0) + (L - S) * max(t_sub - self._t_lm1, 0) + self._t_lm1
+
+    def rows_pass_s(self, rows, draft, bits=4, reps=1, lm_rows=None):
+        """`rows` consecutive positions through the whole model (draft or
+        target weights); the lm_head timed on lm_rows of them and scaled."""
+        from oracle.model import forward
+        L, S = self.shape.n_layers, self.shape.n_shared
+        lm_rows = lm_rows or rows
+        toks = (self.toks * (rows // len(self.toks) + 1))[:rows]
+        t_lm = self.timed(lambda: forward(self.lm, (self.K0, self.K0), self.kv_len, toks[:lm_rows], draft=draft),
+                          reps)
+        t_sh = self.timed(lambda: forward(self.shared, self.kv(), self.kv_len, toks[:lm_rows], draft=draft),
+                          reps) if self.shared else t_lm
+        layer_sh = max(t_sh - t_lm, 0) * (rows / lm_rows)
+        m = self.substitute(bits) if draft else (self.shared or self.substitute(bits))
+        layer_sub = layer_sh
+        if draft or not self.shared:
+            t_sub = self.timed(lambda: forward(m, self.kv(), self.kv_len, toks[:lm_rows], draft=draft), reps)
+            layer_sub = max(t_sub - t_lm, 0) * (rows / lm_rows)
+        return S * layer_sh + (L - S) * layer_sub + t_lm * rows / lm_rows
+
+
+def cpu_baseline(o, dm, wl, tau):
+    """The headline's oracle line: a cycle is gamma draft steps (one draft
+    token through one shared bf16 layer, one W4 substitute layer and the
+    lm_head, scaled to the model) + one gamma+1-position verify (one layer and
+    the lm_head, scaled) + one reject round, each the median of three runs at
+    the workload's shapes and context length (synthetic KV; the long-context
+    workload drafts over its sparse index and its verify also computes the
+    importance scores); tokens/s = tau (of the GPU run) / cycle."""
+    import numpy as np
+
+    from oracle.model import forward
+    from oracle.reject import reject
+    from oracle.sparse import select_index
+    from synth import logits_pair
+
+    shape = o.shape
+    gamma = wl.gamma
+    L, S = shape.n_layers, shape.n_shared
+    sparse, scores = None, None
+    ex = wl.extra
+    if "budget_permille" in ex:
+        rng = np.random.default_rng(46)
+        index = [[select_index(rng.random(o.kv_len), o.kv_len, ex["n_sink"], ex["n_recent"],
+                               ex["budget_permille"]) for _ in range(shape.n_kv_heads)]]
+        sparse, scores = (index, o.kv_len), []
+    spent0 = o.spent
+    t_draft = o.draft_step_s(4, sparse=sparse)
+    toks = o.toks[:gamma + 1]
+    t_lm = o.timed(lambda: forward(o.lm, (o.K0, o.K0), o.kv_len, toks, draft=False))
+    t_v = o.timed(lambda: forward(o.shared or o.sub[4], o.kv(), o.kv_len, toks, draft=False, scores=scores))
     zt, zd = logits_pair(gamma, shape.vocab, 46)
-    zt, zd = host(zt), host(zd)
+    zt, zd = o.host(zt), o.host(zd)
     am = [int(np.argmax(zt[i])) for i in range(gamma)]
-    t_rej = timed(lambda: reject(zt, zd, am, [0] * gamma, 0, wl.temp, wl.draft_temp))
-    t_draft = S * max(t_sh1 - t_lm1, 0) + (L - S) * max(t_w41 - t_lm1, 0) + t_lm1
+    t_rej = o.timed(lambda: reject(zt, zd, am, [0] * gamma, 0, wl.temp, wl.draft_temp))
     t_verify = L * max(t_v - t_lm, 0) + t_lm
     cycle = gamma * t_draft + t_verify + t_rej
-    sample_s = spent[0]
+    sample_s = o.spent - spent0
     log(f"cpu baseline: draft step {t_draft:.2f}s, verify {t_verify:.2f}s, reject {t_rej:.2f}s "
-        f"(sample {sample_s:.1f}s, quantise {t_quant:.1f}s)")
-    layers = (f"one shared bf16 layer, one W4 layer" if S else "one W4 layer")
-    return {"value": round(tau / cycle, 6), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+        f"(sample {sample_s:.1f}s, quantise {o.t_quant:.1f}s)")
+    layers = ("one shared bf16 layer, one W4 layer" if S else "one W4 layer")
+    return {"value": round(tau / cycle, 6), "unit": "tokens/s", "cores": int(o.cores), "kind": "oracle",
             "sample": (f"oracle (NumPy float64) timed on {layers}, the lm_head and one reject "
-                       f"round at full {shape.name} shapes over {kv_len} positions of KV, median "
+                       f"round at full {shape.name} shapes over {o.kv_len} positions of KV, median "
                        f"of 3 runs each ({sample_s:.1f}s of CPU work in all), scaled to {L} layers and a gamma={gamma} "
                        f"cycle; tokens/s = tau of the GPU run / oracle cycle time"),
             "oracle_draft_step_s": round(t_draft, 3), "oracle_verify_s": round(t_verify, 3),
-            "oracle_reject_s": round(t_rej, 3)}
+            "oracle_reject_s": round(t_rej, 3), "_cycle_parts": (t_draft, t_verify, t_rej)}
+
+
+def oracle_beside(o, cpu, wl, lowbit, batch, bdec, tree, mlev, adapt):
+    """The oracle beside every widened row, on bounded samples at the 7B
+    shapes (one run each; the headline's draft step, verify and reject
+    from cpu_baseline): the static tree's cycle (48 draft levels of 6 rows,
+    one 289-node verify with the lm_head timed on 8 rows and scaled, the
+    tree's round at the full vocabulary), the 3- and 2-bit draft steps, the
+    4-bit skinny GEMM at m = 8 (dequantise + product), batched decoding
+    (the oracle decodes the sequences one by one: its tokens/s is the
+    headline's), multi-level substitutes (the GPU run's inner rounds per
+    cycle of gamma2 2-bit steps and one 4-bit pass of gamma2 + 1 rows) and
+    the adaptive length (the GPU run's mean draft length)."""
+    import numpy as np
+
+    from oracle.model import linear
+    from oracle.quant import dequantize
+    from oracle.tree import n_nodes, node, tree_forward, tree_reject
+    from synth import logits_pair, normal_tensor, token_ids, uniform_codes
+    shape = o.shape
+    L, S = shape.n_layers, shape.n_shared
+    t_draft, t_verify, t_rej = cpu["_cycle_parts"]
+    note = lambda s0: f"{o.spent - s0:.1f}s of CPU work"
+    if lowbit:
+        for bits in (3, 2):
+            s0 = o.spent
+            t = o.draft_step_s(bits, reps=1)
+            lowbit[f"w{bits}"]["cpu_baseline"] = {"kind": "oracle", "cores": int(o.cores),
+                                                  "draft_step_s": round(t, 3),
+                                                  "sample": f"one {bits}-bit layer scaled to the model, {note(s0)}"}
+    if batch:
+        s0 = o.spent
+        H, F = shape.hidden, shape.ffn
+        codes, meta, bits = o.sub[4].substitute[0]["gate_up"]
+        x = o.host(normal_tensor((8, H), 1.0, 61, "cpu")).astype(np.float64)
+        t = o.timed(lambda: linear(x, dequantize(codes, meta, bits=bits)), reps=1)
+        batch["cpu_baseline"] = {"kind": "oracle", "cores": int(o.cores), "gate_up_m8_s": round(t, 3),
+                                 "sample": f"dequantise + product at {2 * F}x{H}, m = 8, {note(s0)}"}
+    if bdec:
+        bdec["cpu_baseline"] = {"kind": "oracle", "cores": int(o.cores), "unit": "tokens/s",
+                                "value_per_sequence_cycle": cpu["value"],
+                                "sample": "the oracle runs each sequence's plain cycle in turn: "
+                                          "its tokens/s at every B is the headline's oracle line"}
+    if tree:
+        s0 = o.spent
+        k, D = tree["k"], tree["depth"]
+        nn = n_nodes(k, D)
+        toks = [int(t) for t in token_ids(nn, shape.vocab, 47)]
+        kvt = lambda: (np.concatenate([o.K, np.zeros((1, shape.n_kv_heads, nn, shape.head_dim))], axis=2),
+                       np.concatenate([o.V, np.zeros((1, shape.n_kv_heads, nn, shape.head_dim))], axis=2))
+        lvl_nodes = [node(c, 1, D) for c in range(k)]
+        t_lm = o.timed(lambda: tree_forward(o.lm, (o.K0, o.K0), o.kv_len, lvl_nodes, toks[:k], D, draft=True),
+                       reps=1)
+        t_sub = o.timed(lambda: tree_forward(o.sub[4], kvt(), o.kv_len, lvl_nodes, toks[:k], D, draft=True),
+                        reps=1)
+        t_sh = o.timed(lambda: tree_forward(o.shared, kvt(), o.kv_len, lvl_nodes, toks[:k], D, draft=True),
+                       reps=1) if o.shared else t_lm
+        t_level = S * max(t_sh - t_lm, 0) + (L - S) * max(t_sub - t_lm, 0) + t_lm
+        rows8 = list(range(8))
+        t_vlm = o.timed(lambda: tree_forward(o.lm, (o.K0, o.K0), o.kv_len, rows8, toks[:8], D), reps=1)
+        t_v1 = o.timed(lambda: tree_forward(o.shared or o.sub[4], kvt(), o.kv_len, list(range(nn)), toks, D,
+                                            logit_rows=rows8), reps=1)
+        t_tverify = L * max(t_v1 - t_vlm, 0) + t_vlm * nn / 8
+        zt, zd = logits_pair(nn - 1, shape.vocab, 48)
+        zt, zd = o.host(zt), o.host(zd)
+        zt = np.concatenate([zt, zt[:1]])[:nn]
+        R, _ = uniform_codes(k + D - 1, 49)
+        t_trej = o.timed(lambda: tree_reject(zt, zd[:1 + k * (D - 1)], toks, k, D, list(R), 5, 0.0, 0.0), reps=1)
+        cycle = D * t_level + t_tverify + t_trej
+        tree["cpu_baseline"] = {"kind": "oracle", "cores": int(o.cores), "unit": "tokens/s",
+                                "value": round(tree["tau"] / cycle, 6), "draft_level_s": round(t_level, 3),
+                                "verify_pass_s": round(t_tverify, 3), "reject_s": round(t_trej, 4),
+                                "sample": (f"one draft level ({k} rows) through one shared and one W4 layer "
+                                           f"and the lm_head, the {nn}-node verify through one layer (lm_head on "
+                                           f"8 rows, scaled), the tree's round at V = {shape.vocab}; scaled to "
+                                           f"{L} layers and a {D}-level cycle; tokens/s = tau of the GPU run / "
+                                           f"oracle cycle; {note(s0)}")}
+    if mlev:
+        s0 = o.spent
+        t2 = o.draft_step_s(2, reps=1)
+        out = {}
+        for key, r in mlev.items():
+            g2 = int(key.split("_")[1])
+            t_pass = o.rows_pass_s(g2 + 1, draft=True, bits=4, reps=1)
+            cycle = r["inner_rounds_per_cycle"] * (g2 * t2 + t_pass) + t_verify + t_rej
+            out[key] = {"value": round(r["tau"] / cycle, 6), "pass_4bit_s": round(t_pass, 3)}
+        mlev["cpu_baseline"] = {"kind": "oracle", "cores": int(o.cores), "unit": "tokens/s",
+                                "draft_step_2bit_s": round(t2, 3), **out,
+                                "sample": (f"one 2-bit draft step and one 4-bit pass per inner round (one layer "
+                                           f"each, scaled), the GPU run's rounds per cycle, the headline's verify "
+                                           f"and reject; {note(s0)}")}
+    if adapt:
+        cycle = adapt["mean_draft_len"] * t_draft + t_verify + t_rej
+        adapt["cpu_baseline"] = {"kind": "oracle", "cores": int(o.cores), "unit": "tokens/s",
+                                 "value": round(adapt["tau"] / cycle, 6),
+                                 "sample": "the headline's oracle step times at the GPU run's mean draft length"}
+
 
 
 if __name__ == "__main__":
