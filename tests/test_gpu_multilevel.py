@@ -45,15 +45,41 @@ def _uniforms(cycles, gamma, gamma2, seed):
             R.reshape(cycles, gamma), U)
 
 
+def _memo_weights(om):
+    """The oracle's weight matrices converted once per test (the same
+    float64 values; the oracle dequantises on every call)."""
+    cache, orig = {}, om.weight
+
+    def weight(l, name, draft):
+        key = (l, name, bool(draft and om.substitute and om.substitute[l] is not None))
+        if key not in cache:
+            cache[key] = orig(l, name, draft)
+        return cache[key]
+    om.weight = weight
+    return om
+
+
 @pytest.mark.parametrize("T,T_mid,T2", [(0.0, 0.0, 0.0), (1.0, 1.0, 1.0), (0.0, 0.6, 0.0), (0.8, 0.0, 1.0)])
 def test_multilevel_cycles_teacher_forced(cuda, T, T_mid, T2):
     log(f"multi-level cycles T={T} T_mid={T_mid} T2={T2}")
-    gamma, gamma2, cycles, ctx = 6, 3, 3, 40
-    shape = TINY
-    w = model_weights(shape, 9, cuda)
+    _check_cycles(TINY, 9, 40, 256, 6, 3, T, T_mid, T2, 3, cuda)
+
+
+@pytest.mark.parametrize("T,T_mid,T2", [(0.0, 0.0, 0.0), (1.0, 1.0, 1.0)])
+def test_multilevel_cycle_7b_layer(cuda, T, T_mid, T2):
+    """One Qwen2.5-7B-shaped layer (4-bit and 2-bit substitutes, vocab
+    152064) at 1000 KV positions, the bench's gamma = 16 and gamma2 = 4."""
+    log(f"multi-level cycle 7B layer T={T} T_mid={T_mid} T2={T2}")
+    _check_cycles(QWEN7B.with_(n_layers=1, n_shared=0), 5, 1000, 1040, 16, 4, T, T_mid, T2, 1, cuda)
+
+
+def _check_cycles(shape, seed, ctx, cap, gamma, gamma2, T, T_mid, T2, cycles, cuda):
+    w = model_weights(shape, seed, cuda)
     dm4, dm2, om4, om2 = _models(shape, w)
-    dec = MultiLevelDecoder(dm4, dm2, 256, gamma, gamma2, T, T_mid, T2)
-    K, V = kv_history(shape.n_layers, shape.n_kv_heads, ctx, shape.head_dim, 256, 16, cuda)
+    _memo_weights(om4)
+    _memo_weights(om2)
+    dec = MultiLevelDecoder(dm4, dm2, cap, gamma, gamma2, T, T_mid, T2)
+    K, V = kv_history(shape.n_layers, shape.n_kv_heads, ctx, shape.head_dim, cap, 16, cuda)
     dec.k_cache.copy_(K)
     dec.v_cache.copy_(V)
     kv_o = (host(K).astype(np.float64), host(V).astype(np.float64))
@@ -91,6 +117,7 @@ def test_multilevel_cycles_teacher_forced(cuda, T, T_mid, T2):
             assert toks[base + 1 + n] == out_ref[-1]  # the round's last token appended
             base += min(n + 1, gamma - base)
             r += 1
+        log(f"  cycle {c}: {r} inner rounds")
         # the outer round over the gamma middle tokens
         dec.verify()
         if T > 0:
