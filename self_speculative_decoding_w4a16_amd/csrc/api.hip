@@ -460,8 +460,12 @@ int rows_forward(const subspec_model* m, const RowsCache& st, const RowsSpec& rs
     }
     if (lin_is_w4(lg)) {
       prof::Scope ps(SUBSPEC_K_W4_GATE_UP, gemm_w4_bytes(2 * F, H, mt, F, false), s);
-      HIPCHK(launch_gemm_w4(lg.codes, lg.meta, 2 * F, H, w.xn, mt, w.gu, w.gemm_part, s));
-      HIPCHK(launch_silu_rows(w.gu, F, mt, w.act, s));
+      if (gemm_w4_splits(2 * F, H) == 1) {  // SiLU * up in the GEMM's epilogue
+        HIPCHK(launch_gemm_w4_silu(lg.codes, lg.meta, F, H, w.xn, mt, w.act, s));
+      } else {
+        HIPCHK(launch_gemm_w4(lg.codes, lg.meta, 2 * F, H, w.xn, mt, w.gu, w.gemm_part, s));
+        HIPCHK(launch_silu_rows(w.gu, F, mt, w.act, s));
+      }
     } else {
       GemmArgs g{lg.w, F, H, w.xn, mt, w.act, F, nullptr, w.gemm_part};
       prof::Scope ps(SUBSPEC_K_GEMM_GATE_UP, gemm_bytes(2 * F, H, mt, F, false), s);

@@ -27,6 +27,9 @@
 //  * A = activations, B = weights: lane (r, g) of tile t ends with
 //    positions 4 g + i of the tile's row r, so it applies only its own row's
 //    scale/min (one 8-byte load per tile and chunk).
+//  * The gate/up projection can end in SiLU(gate) * up: its blocks then take
+//    RT/2 tiles of gate rows and the RT/2 tiles of the matching up rows, so a
+//    lane holds both factors of its outputs.
 //  * Pipeline: the codes, scale/min pairs and activations of WD chunks are
 //    in flight per lane (register slots named statically, every load
 //    unconditional: offsets outside a buffer resource read zeros).
@@ -54,17 +57,23 @@ struct Slot {
   u32x4 xv[4];   // activations of position r for the four MFMA steps
 };
 
+// SILU: the gate/up projection (n = 2 silu_f rows) ending in SiLU(gate) * up
+template <bool SILU>
 __global__ __launch_bounds__(64) void gemm_w4_kernel(const uint8_t* __restrict__ codes,
                                                      const uint16_t* __restrict__ meta, int64_t n, int K,
                                                      const uint16_t* __restrict__ x, int m, uint16_t* y,
-                                                     float* part, int splits, int to_part) {
+                                                     float* part, int splits, int to_part, int64_t silu_f) {
   const int lane = threadIdx.x;
   const int r = lane & 15, g = lane >> 4;
   const int chunks = K / KC;
   const int split = blockIdx.y;
   const int c0 = (int)((int64_t)chunks * split / splits), c1 = (int)((int64_t)chunks * (split + 1) / splits);
-  const int64_t row0 = (int64_t)blockIdx.x * 16 * RT;
-  const int rows = (int)std::max<int64_t>(0, std::min<int64_t>(16 * RT, n - row0));
+  // rows row0 + 16 t + r of tile t; with SILU the first RT/2 tiles are gate
+  // rows from row0 and the others the matching up rows, silu_f rows further
+  // (one resource spans both)
+  constexpr int HT = RT / 2;
+  const int64_t row0 = (int64_t)blockIdx.x * 16 * (SILU ? HT : RT);
+  const int rows = (int)std::max<int64_t>(0, std::min<int64_t>(SILU ? silu_f + 16 * HT : 16 * RT, n - row0));
   const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(codes + row0 * (K / 2)), 0, rows * (K / 2), kBufferWord3);
   const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -86,7 +95,7 @@ __global__ __launch_bounds__(64) void gemm_w4_kernel(const uint8_t* __restrict__
       sl.xv[st] = __builtin_amdgcn_raw_buffer_load_b128(xrs, in ? xbase + (kc + 32 * g + 8 * st) * 2 : kOutside, 0, 0);
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      const int rr = 16 * t + r;
+      const int rr = (SILU && t >= HT) ? (int)silu_f + 16 * (t - HT) + r : 16 * t + r;
       sl.pc[t] = __builtin_amdgcn_raw_buffer_load_b128(crs, in ? rr * (K / 2) + kc / 2 + 16 * g : kOutside, 0, 0);
       sl.mt[t] = __builtin_amdgcn_raw_buffer_load_b64(mrs, in ? rr * (K / 16) + 4 * (kc / 64) : kOutside, 0, 0);
     }
@@ -151,6 +160,24 @@ __global__ __launch_bounds__(64) void gemm_w4_kernel(const uint8_t* __restrict__
     if (c + j < c1) step(c + j, j);
 
   // lane holds positions 4 g + i of row r of each tile
+  if constexpr (SILU) {
+    // act[pos][j] = SiLU(gate) * up, both rounded to bf16 first (as the
+    // unfused gate/up store and SiLU kernel do)
+#pragma unroll
+    for (int t = 0; t < HT; ++t) {
+      const int64_t j = row0 + 16 * t + r;
+      if (j >= silu_f) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pos = 4 * g + i;
+        if (pos < m) {
+          const float gt = ss::bf2f(ss::f2bf(acc[t][i])), up = ss::bf2f(ss::f2bf(acc[t + HT][i]));
+          y[(int64_t)pos * silu_f + j] = ss::f2bf(gt / (1.0f + expf(-gt)) * up);
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     const int64_t row = row0 + 16 * t + r;
@@ -183,8 +210,18 @@ hipError_t launch_gemm_w4(const uint8_t* codes, const uint16_t* meta, int64_t n,
   const int to_part = splits_out != nullptr;
   if (to_part) *splits_out = splits;
   const dim3 grid((unsigned)((n + 16 * RT - 1) / (16 * RT)), (unsigned)splits), block(64);
-  SS_LAUNCH(gemm_w4_kernel, grid, block, 0, s, codes, meta, n, (int)k, x, m, y, part, splits, to_part);
+  SS_LAUNCH(gemm_w4_kernel<false>, grid, block, 0, s, codes, meta, n, (int)k, x, m, y, part, splits, to_part,
+            (int64_t)0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1 || to_part) return e;
   return launch_gemm_reduce(part, splits, m, n, y, n, s);
+}
+
+hipError_t launch_gemm_w4_silu(const uint8_t* codes, const uint16_t* meta, int64_t F, int64_t k, const uint16_t* x,
+                               int m, uint16_t* act, hipStream_t s) {
+  if (gemm_w4_splits(2 * F, k) != 1) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((F + 8 * RT - 1) / (8 * RT))), block(64);
+  SS_LAUNCH(gemm_w4_kernel<true>, grid, block, 0, s, codes, meta, 2 * F, (int)k, x, m, act, (float*)nullptr, 1, 0,
+            F);
+  return hipGetLastError();
 }

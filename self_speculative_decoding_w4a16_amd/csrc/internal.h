@@ -70,6 +70,11 @@ hipError_t launch_gemm_reduce(const float* part, int splits, int m, int64_t n, u
 int gemm_w4_splits(int64_t n, int64_t k);
 hipError_t launch_gemm_w4(const uint8_t* codes, const uint16_t* meta, int64_t n, int64_t k, const uint16_t* x, int m,
                           uint16_t* y, float* part, hipStream_t s, int* splits_out = nullptr);
+// The gate/up projection (2F rows: gate rows, then up rows) ending in
+// act[t][j] = bf16(SiLU(gate) * up); only while it needs no k split
+// (gemm_w4_splits(2F, k) == 1), else hipErrorInvalidValue.
+hipError_t launch_gemm_w4_silu(const uint8_t* codes, const uint16_t* meta, int64_t F, int64_t k, const uint16_t* x,
+                               int m, uint16_t* act, hipStream_t s);
 
 // ------------------------------------------------------------------ quantise
 hipError_t launch_quantize(const uint16_t* w, int64_t n, int64_t k, int bits, uint8_t* codes,
