@@ -314,13 +314,20 @@ int subspec_reject_len(int32_t gamma, int32_t vocab, float temp, float draft_tem
 
 /* The draft weights' pass over n_tokens (<= 16) positions: tokens[j] at
  * position kv_len + pos_offset + j (causal), bf16 shared layers and 4-bit
- * substitutes; writes their K/V and, unless NULL, logits [n_tokens][vocab]. */
+ * substitutes; writes their K/V (slots past the capacity are skipped on the
+ * device) and, unless NULL, logits [n_tokens][vocab].  Errors: EINVAL for a
+ * NULL tokens or n_tokens outside [1, 16], ECAPACITY when pos_offset +
+ * n_tokens exceeds the capacity, EWORKSPACE for a short workspace. */
 int subspec_draft_verify(const subspec_model *m, const subspec_state *st, int32_t pos_offset, int32_t n_tokens,
                          const int32_t *tokens, uint16_t *logits, void *ws, size_t ws_bytes, void *stream);
 
 /* tokens[at + n] = out_tokens[n] with n = *n_accepted (device): a round's
- * last token placed after its accepted drafts. */
-int subspec_draft_append(const subspec_state *st, int32_t at, const int32_t *n_accepted, const int32_t *out_tokens,
+ * last token placed after its accepted drafts.  A device n outside
+ * [0, max_n] writes nothing.  Errors: EINVAL for NULL buffers, at < 0,
+ * max_n < 0 or at + max_n > gamma_max (the tokens buffer holds gamma_max + 1
+ * entries). */
+int subspec_draft_append(const subspec_state *st, int32_t at, int32_t max_n, const int32_t *n_accepted,
+                         const int32_t *out_tokens,
                          void *stream);
 
 /* ------------------------------------------------------------------------ */

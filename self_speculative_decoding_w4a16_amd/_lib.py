@@ -115,7 +115,7 @@ _SIGS = {
     "subspec_hbm_read": (c_int32, [c_void_p, c_int64, c_void_p, c_void_p]),
     "subspec_draft_verify": (c_int32, [POINTER(Model), POINTER(State), c_int32, c_int32, c_void_p, c_void_p,
                                        c_void_p, c_size_t, c_void_p]),
-    "subspec_draft_append": (c_int32, [POINTER(State), c_int32, c_void_p, c_void_p, c_void_p]),
+    "subspec_draft_append": (c_int32, [POINTER(State), c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
     "subspec_batch_workspace_bytes": (c_size_t, [POINTER(Model), c_int32, c_int32, c_int32]),
     "subspec_batch_draft_step": (c_int32, [POINTER(Model), POINTER(BatchState), c_int32, c_float, c_void_p, c_void_p,
                                            c_size_t, c_void_p]),
@@ -367,8 +367,9 @@ def draft_verify(model, state, pos_offset, n_tokens, tokens, logits, ws, stream=
                                      _p(logits), _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def draft_append(state, at, n_accepted, out_tokens, stream=None):
-    check(lib().subspec_draft_append(ctypes.byref(state), at, _p(n_accepted), _p(out_tokens), _stream(stream)))
+def draft_append(state, at, max_n, n_accepted, out_tokens, stream=None):
+    check(lib().subspec_draft_append(ctypes.byref(state), at, max_n, _p(n_accepted), _p(out_tokens),
+                                     _stream(stream)))
 
 
 def batch_workspace_bytes(model, batch, max_tokens, capacity):

@@ -766,11 +766,12 @@ int subspec_draft_verify(const subspec_model* m, const subspec_state* st, int32_
   return rows_forward(m, rows_cache(st), rs, ws, hs(stream));
 }
 
-int subspec_draft_append(const subspec_state* st, int32_t at, const int32_t* n_accepted, const int32_t* out_tokens,
-                         void* stream) {
+int subspec_draft_append(const subspec_state* st, int32_t at, int32_t max_n, const int32_t* n_accepted,
+                         const int32_t* out_tokens, void* stream) {
   if (!st || !st->tokens || !n_accepted || !out_tokens) return fail(SUBSPEC_EINVAL, "NULL buffer");
-  if (at < 0) return fail(SUBSPEC_EINVAL, "at must be >= 0");
-  HIPCHK(launch_token_append(st->tokens + at, n_accepted, out_tokens, hs(stream)));
+  if (at < 0 || max_n < 0 || at + max_n > st->gamma_max)
+    return fail(SUBSPEC_EINVAL, "at %d + max_n %d outside the tokens buffer (gamma_max %d)", at, max_n, st->gamma_max);
+  HIPCHK(launch_token_append(st->tokens + at, max_n, n_accepted, out_tokens, hs(stream)));
   return ok();
 }
 

@@ -176,8 +176,9 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_kv_rollback(int32_t* kv_len, int32_t* tokens, const int32_t* n_accepted,
                               const int32_t* out_tokens, hipStream_t s);
 hipError_t launch_kv_advance(int32_t* kv_len, int32_t delta, hipStream_t s);
-// dst[*n_accepted] = out_tokens[*n_accepted] (one thread)
-hipError_t launch_token_append(int32_t* dst, const int32_t* n_accepted, const int32_t* out_tokens, hipStream_t s);
+// dst[n] = out_tokens[n] for n = *n_accepted in [0, max_n] (one thread)
+hipError_t launch_token_append(int32_t* dst, int max_n, const int32_t* n_accepted, const int32_t* out_tokens,
+                               hipStream_t s);
 // Draft step: position check (valid, token_out = -1 when out of range, or
 // when step >= *draft_len with draft_len set) and the RoPE table (cos, sin)
 // [d/2][2] of position kv_len + step.

@@ -159,9 +159,9 @@ __global__ void kv_rollback_kernel(int32_t* kv_len, int32_t* tokens, const int32
 __global__ void kv_advance_kernel(int32_t* kv_len, int32_t delta) { *kv_len += delta; }
 
 // A round's last token appended after its accepted drafts: dst[n] = out[n].
-__global__ void token_append_kernel(int32_t* dst, const int32_t* n_accepted, const int32_t* out_tokens) {
+__global__ void token_append_kernel(int32_t* dst, int max_n, const int32_t* n_accepted, const int32_t* out_tokens) {
   const int n = *n_accepted;
-  dst[n] = out_tokens[n];
+  if (n >= 0 && n <= max_n) dst[n] = out_tokens[n];
 }
 
 // Batched decoding: sequence b moves by n[b] + 1 and takes its last emitted
@@ -297,8 +297,9 @@ hipError_t launch_batch_rollback(int32_t* kv_len, int32_t* tokens, int64_t ld, c
   return hipGetLastError();
 }
 
-hipError_t launch_token_append(int32_t* dst, const int32_t* n_accepted, const int32_t* out_tokens, hipStream_t s) {
-  SS_LAUNCH(token_append_kernel, dim3(1), dim3(1), 0, s, dst, n_accepted, out_tokens);
+hipError_t launch_token_append(int32_t* dst, int max_n, const int32_t* n_accepted, const int32_t* out_tokens,
+                               hipStream_t s) {
+  SS_LAUNCH(token_append_kernel, dim3(1), dim3(1), 0, s, dst, max_n, n_accepted, out_tokens);
   return hipGetLastError();
 }
 

@@ -577,7 +577,7 @@ class MultiLevelDecoder:
         _lib.reject(g, self.m4.shape.vocab, self.mid_temp, self.draft_temp, self.mid_logits[base:],
                     self.inner_logits[base:], self.tokens[base + 1:], self.r2_buf if stoch_p else None,
                     self.f2_buf if stoch_p else None, self.in_n, self.in_out, self.in_status, self.probs, self.ws)
-        _lib.draft_append(self.c, base + 1, self.in_n, self.in_out)
+        _lib.draft_append(self.c, base + 1, g, self.in_n, self.in_out)
         return int(self.in_n.item())
 
     def middle(self, cycle_uniforms=None):

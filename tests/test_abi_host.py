@@ -167,6 +167,29 @@ def test_draft_verify_argument_errors():
     assert l.subspec_kv_advance(None, 1, None) == _lib.EINVAL
 
 
+def test_multilevel_argument_errors():
+    l = _lib.lib()
+    m, keep = _fake_model()
+    p = 4096
+    st = _lib.State(p, p, 1024, p, p, p, 4)
+    ws = V(p)
+    dv = lambda st_, off, n, toks=V(p), nbytes=1 << 30: l.subspec_draft_verify(
+        ctypes.byref(m), ctypes.byref(st_), off, n, toks, None, ws, nbytes, None)
+    assert dv(st, 0, 0) == _lib.EINVAL
+    assert dv(st, 0, 17) == _lib.EINVAL
+    assert dv(st, 0, 4, toks=None) == _lib.EINVAL
+    st_small = _lib.State(p, p, 8, p, p, p, 4)
+    assert dv(st_small, 0, 9) == _lib.ECAPACITY
+    assert dv(st_small, -1, 2) == _lib.ECAPACITY
+    assert dv(st, 0, 4, nbytes=128) == _lib.EWORKSPACE
+    ap = lambda at, max_n, n=V(p): l.subspec_draft_append(ctypes.byref(st), at, max_n, n, V(p), None)
+    assert ap(-1, 2) == _lib.EINVAL
+    assert ap(0, -1) == _lib.EINVAL
+    assert ap(2, 3) == _lib.EINVAL  # past the gamma_max + 1 = 5 tokens
+    assert ap(1, 2, n=None) == _lib.EINVAL
+    assert "tokens buffer" in _lib.last_error() or "NULL" in _lib.last_error()
+
+
 def test_tree_argument_errors():
     l = _lib.lib()
     m, keep = _fake_model()
