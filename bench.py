@@ -326,7 +326,7 @@ def main():
     # ---------------------------------------------------------------- small workloads
     tiny = layer = lowbit = None  # noqa: F841
     if args.config == "full7b" and not args.no_small:
-        tiny = tiny_rates(dev)
+        tiny = tiny_rates(dev, oracle=not args.no_cpu_baseline)
         log(f"tiny workload: {json.dumps(tiny)}")
         layer = layer7b_rates(dev)
         log(f"one 7B layer: {json.dumps(layer)}")
@@ -356,7 +356,7 @@ def main():
     if not args.no_cpu_baseline:
         osample = OracleSample(shape, w, wl)
         cpu = cpu_baseline(osample, dm, wl, tau)
-        oracle_beside(osample, cpu, wl, lowbit, batch, bdec, tree, mlev, adapt)
+        oracle_beside(osample, cpu, wl, layer, lowbit, batch, bdec, tree, mlev, adapt)
         cpu.pop("_cycle_parts")
         del osample
 
@@ -621,8 +621,13 @@ def pass_rates(dec, shape, wl, kv0, last, n_w4, sparse_keys=None):
     dec.reset(kv0, last)
     t_v = replay_us(dec.verify)
     dec.reset(kv0, last)
+    # matrix-core work of the verify pass: 2 flops per weight and position
+    _, _, _, bf, _ = model_bytes(shape, n_w4, 0, 0)
+    params = bf / 2 * shape.n_layers + shape.vocab * shape.hidden
+    tflops = 2.0 * params * (gamma + 1) / (t_v * 1e-6) / 1e12
     return (hbm(draft_b, t_d, "draft step (every launch of one draft token, graph-replayed)"),
-            hbm(verify_b, t_v, f"verify pass ({gamma + 1} positions, every launch, graph-replayed)"))
+            hbm(verify_b, t_v, f"verify pass ({gamma + 1} positions, every launch, graph-replayed)",
+                mfma_tflops=round(tflops, 2), mfma_frac=round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)))
 
 
 def layer7b_rates(dev, gamma=16, ctx=1024):
@@ -964,7 +969,7 @@ def multilevel_rates(dec, dm, w, shape, wl, kv0, last, gamma2s=(4, 8), G=32):
     return out
 
 
-def tiny_rates(dev, reps=200):
+def tiny_rates(dev, reps=200, oracle=True):
     """The tiny workload: one 512x512 W4 GEMV at batch 1 and one rejection round
     with V = 1000, gamma = 4.  Both are far too small to stream from HBM (the
     GEMV's 147 KB sit in cache): microseconds per call, back to back in a
@@ -1001,10 +1006,35 @@ def tiny_rates(dev, reps=200):
             _lib.reject(gamma, V, 1.0, 1.0, zt, zd, toks, rr, uf, n_out, out, st, None, ws)
     us_r = replay_us(rejects, reps=5) / 50
     gb = n * k * (0.5 + 4 / 64) + 2 * k + 2 * n
-    return {"w4_gemv_512x512_us": round(us_g, 3),
-            "w4_gemv_512x512_gbs": round(gb / (us_g * 1e-6) / 1e9, 1), "latency_bound": True,
-            "reject_v1000_gamma4_us": round(us_r, 3),
-            "reject_bytes": 2 * (2 * gamma + 1) * V}
+    out = {"w4_gemv_512x512_us": round(us_g, 3),
+           "w4_gemv_512x512_gbs": round(gb / (us_g * 1e-6) / 1e9, 1), "latency_bound": True,
+           "reject_v1000_gamma4_us": round(us_r, 3),
+           "reject_bytes": 2 * (2 * gamma + 1) * V}
+    if oracle:
+        # the oracle on one host core, the same calls: dequantise + product, one round
+        from threadpoolctl import threadpool_limits
+
+        from oracle.model import linear
+        from oracle.quant import dequantize, quantize
+        from oracle.reject import reject as oreject
+        host = lambda t: t.detach().float().cpu().numpy()
+        wc, wm = quantize(host(w))
+        xh = host(x).astype(np.float64)
+        zth, zdh = host(zt), host(zd)
+        th = [int(t) for t in toks.tolist()]
+
+        def per_call_us(fn, n_calls):
+            t0 = time.perf_counter()
+            for _ in range(n_calls):
+                fn()
+            return 1e6 * (time.perf_counter() - t0) / n_calls
+        with threadpool_limits(1):
+            o_g = per_call_us(lambda: linear(xh, dequantize(wc, wm)), 5)
+            o_r = per_call_us(lambda: oreject(zth, zdh, th, list(Ud), 12345, 1.0, 1.0), 20)
+        out["cpu_baseline"] = {"kind": "oracle", "cores": 1, "w4_gemv_512x512_us": round(o_g, 1),
+                               "reject_v1000_gamma4_us": round(o_r, 1),
+                               "sample": "the same two calls on one host core (5 and 20 calls)"}
+    return out
 
 
 class OracleSample:
@@ -1086,6 +1116,7 @@ class OracleSample:
         m = self.substitute(bits)
         t_sub = self.timed(lambda: forward(m, self.kv(), self.kv_len, self.toks[:1], draft=True, sparse=sparse),
                            reps)
+        self.sub_layer_s = {**getattr(self, "sub_layer_s", {}), bits: max(t_sub - self._t_lm1, 0)}
         return S * max(self._t_sh1 - self._t_lm1, 0) + (L - S) * max(t_sub - self._t_lm1, 0) + self._t_lm1
 
     def rows_pass_s(self, rows, draft, bits=4, reps=1, lm_rows=None):
@@ -1143,6 +1174,7 @@ def cpu_baseline(o, dm, wl, tau):
     am = [int(np.argmax(zt[i])) for i in range(gamma)]
     t_rej = o.timed(lambda: reject(zt, zd, am, [0] * gamma, 0, wl.temp, wl.draft_temp))
     t_verify = L * max(t_v - t_lm, 0) + t_lm
+    o.verify_layer_s = max(t_v - t_lm, 0)
     cycle = gamma * t_draft + t_verify + t_rej
     sample_s = o.spent - spent0
     log(f"cpu baseline: draft step {t_draft:.2f}s, verify {t_verify:.2f}s, reject {t_rej:.2f}s "
@@ -1157,7 +1189,7 @@ def cpu_baseline(o, dm, wl, tau):
             "oracle_reject_s": round(t_rej, 3), "_cycle_parts": (t_draft, t_verify, t_rej)}
 
 
-def oracle_beside(o, cpu, wl, lowbit, batch, bdec, tree, mlev, adapt):
+def oracle_beside(o, cpu, wl, layer, lowbit, batch, bdec, tree, mlev, adapt):
     """The oracle beside every widened row, on bounded samples at the 7B
     shapes (one run each; the headline's draft step, verify and reject
     from cpu_baseline): the static tree's cycle (48 draft levels of 6 rows,
@@ -1178,6 +1210,13 @@ def oracle_beside(o, cpu, wl, lowbit, batch, bdec, tree, mlev, adapt):
     L, S = shape.n_layers, shape.n_shared
     t_draft, t_verify, t_rej = cpu["_cycle_parts"]
     note = lambda s0: f"{o.spent - s0:.1f}s of CPU work"
+    if layer:
+        layer["cpu_baseline"] = {"kind": "oracle", "cores": int(o.cores),
+                                 "draft_w4_layer_s": round(o.sub_layer_s[4], 4),
+                                 "verify_layer_s": round(o.verify_layer_s, 4),
+                                 "sample": (f"the headline's oracle samples: one W4 layer of a draft step and one "
+                                            f"layer of a {wl.gamma + 1}-position verify at {o.kv_len} KV positions, "
+                                            f"median of 3")}
     if lowbit:
         for bits in (3, 2):
             s0 = o.spent
