@@ -558,8 +558,9 @@ int subspec_bf16_gemv(const uint16_t *w, int64_t n, int64_t k, const uint16_t *x
 int subspec_gemv(const subspec_linear *w, const uint16_t *x, const uint16_t *norm_w, float eps,
                  int32_t epilogue, const uint16_t *resid, uint16_t *y, void *stream);
 
-/* Y[t][n] = bf16( sum_k X[t][k] W[n][k] ) for t < m <= 64 (the verify GEMM
- * on matrix cores).  X bf16 [m][k], Y bf16 [m][n]; k % 128 == 0. */
+/* Y[t][n] = bf16( sum_k X[t][k] W[n][k] ) for t < m <= 512 (the verify GEMM
+ * on matrix cores: slices of 64 positions, or of 128 past 64, each streaming
+ * the weights once).  X bf16 [m][k], Y bf16 [m][n]; k % 128 == 0. */
 int subspec_bf16_gemm(const uint16_t *w, int64_t n, int64_t k, const uint16_t *x, int32_t m,
                       uint16_t *y, void *ws, size_t ws_bytes, void *stream);
 

@@ -1299,7 +1299,7 @@ int subspec_bf16_gemm(const uint16_t* w, int64_t n, int64_t k, const uint16_t* x
                       uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
   if (!w || !x || !y) return fail(SUBSPEC_EINVAL, "w, x and y must be set");
   if (n < 1 || k < 1) return fail(SUBSPEC_EINVAL, "n and k must be positive");
-  if (m < 1 || m > kMaxTokens) return fail(SUBSPEC_EINVAL, "m outside [1, %d]", kMaxTokens);
+  if (m < 1 || m > kMaxTreeRows) return fail(SUBSPEC_EINVAL, "m outside [1, %d]", kMaxTreeRows);
   if (k % 128 != 0) return fail(SUBSPEC_ESHAPE, "k must be a multiple of 128");
   const size_t need = kCounterBytes + align256(gemm_partials_bytes(n, k, m, GEPI_STORE));
   int r;

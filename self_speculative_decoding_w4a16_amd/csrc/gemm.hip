@@ -55,7 +55,7 @@ struct Plan {
   int tt;          // position tiles of one slice
   int splits;      // k splits (blocks along k)
   int nw;          // waves per block
-  int slices;      // slices of 64 positions (grid z; more than 64 positions: a tree's verify pass)
+  int slices;      // slices of slice_rows(m) positions (grid z)
 };
 
 // Waves per block.  Small blocks (2 waves) keep many independent blocks in
@@ -70,6 +70,7 @@ struct Plan {
 // took the 32B down GEMM from 69 to 64 us, but changed every result that
 // depends on those sums, e.g. the prefill's KV cache).
 int block_waves(int64_t n, int epi, int m) {
+  if (m > 64) return 8;  // slices of 128 positions (a tree's or a batch's verify pass)
   if (epi == GEPI_SILU) return m > 32 ? 8 : 2;
   return n >= 65536 ? 8 : 2;
 }
@@ -79,12 +80,17 @@ int64_t rows_per_group(int64_t n, int epi, int m) {
   return epi == GEPI_SILU ? 16 * nw / 2 : 16 * nw;
 }
 
+// Positions of one slice (grid z): up to 64, or 128 past 64 positions, so
+// that a 289-node tree verify pass streams the weights 3 times, not 5.
+int slice_rows(int m) { return m > 64 ? 128 : 64; }
+
 Plan make_plan(int64_t n, int64_t k, int m, int epi) {
   Plan p;
-  const int ms = std::min(m, 64);  // positions of one slice
-  p.slices = (m + 63) / 64;
-  p.tt = (ms + 15) / 16;
-  p.nw = block_waves(n, epi, ms);
+  const int sl = slice_rows(m);
+  const int ms = std::min(m, sl);  // positions of one slice
+  p.slices = (m + sl - 1) / sl;
+  p.tt = sl == 128 ? 8 : (ms + 15) / 16;
+  p.nw = block_waves(n, epi, m);
   const int64_t rg = rows_per_group(n, epi, ms);
   p.groups = (n + rg - 1) / rg;
   const int chunks = (int)(k / KC);
@@ -110,9 +116,11 @@ __global__ __launch_bounds__(NWR * SS_WAVE) void gemm_kernel(GemmArgs a, int spl
   const int chunks = K / KC;
   const int split = blockIdx.y;
   const int c0 = (int)((int64_t)chunks * split / splits), c1 = (int)((int64_t)chunks * (split + 1) / splits);
-  // this block's slice of at most 64 positions (rows of x and y)
-  const int zrow = blockIdx.z * 64;
-  const int mz = min(64, a.m - zrow);
+  // this block's slice of at most 64 (or, with 8 position tiles, 128)
+  // positions: rows of x and y
+  constexpr int SL = TT > 4 ? 128 : 64;
+  const int zrow = blockIdx.z * SL;
+  const int mz = min(SL, a.m - zrow);
 
   // this wave's 16 weight rows
   int64_t row0;  // first physical row of the tile
@@ -295,6 +303,12 @@ hipError_t launch_nw(const GemmArgs& a, const Plan& p, hipStream_t s) {
     case 2: SS_LAUNCH((gemm_kernel<NW, 2, EPI>), grid, block, 0, s, a, p.splits); break;
     case 3: SS_LAUNCH((gemm_kernel<NW, 3, EPI>), grid, block, 0, s, a, p.splits); break;
     case 4: SS_LAUNCH((gemm_kernel<NW, 4, EPI>), grid, block, 0, s, a, p.splits); break;
+    case 8:
+      if constexpr (NW == 8) {
+        SS_LAUNCH((gemm_kernel<NW, 8, EPI>), grid, block, 0, s, a, p.splits);
+        break;
+      }
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -170,7 +170,7 @@ def test_fused_gemv_gate_up_full_shape_sampled_rows(cuda, w4):
     assert rel_err(host(y)[rows], ref) < TOL
 
 
-@pytest.mark.parametrize("m", [1, 5, 17, 33, 49, 64])
+@pytest.mark.parametrize("m", [1, 5, 17, 33, 49, 64, 65, 130, 289, 512])
 def test_bf16_gemm_small(cuda, m):
     n, k = 1000, 640
     log(f"gemm m={m} {n}x{k}")
@@ -200,6 +200,25 @@ def test_bf16_gemm_full_shapes(cuda, name):
         ref = linear(host(x), host(w[rows]))
         assert rel_err(host(y)[:, rows], ref) < TOL
     assert int(buf[:16384].sum().item()) == 0
+
+
+@pytest.mark.parametrize("name", ["gate_up", "down"])
+def test_bf16_gemm_full_shapes_many_positions(cuda, name):
+    """289 positions (a k = 6, D = 48 tree's verify pass): three slices of up
+    to 128 positions, sampled rows and positions against the oracle."""
+    n, k = SHAPES_7B[name]
+    m = 289
+    log(f"gemm full {name} m={m}")
+    w = normal_tensor((n, k), 0.02, 32, cuda)
+    x = normal_tensor((m, k), 1.0, 33, cuda)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=cuda)
+    _lib.bf16_gemm(w, x, y, ws(1 << 28, cuda))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.r_[0, n - 1, rng.integers(0, n, 128)])
+    pos = np.unique(np.r_[0, 127, 128, 255, 256, m - 1, rng.integers(0, m, 16)])
+    ref = linear(host(x)[pos], host(w[rows]))
+    assert rel_err(host(y)[np.ix_(pos, rows)], ref) < TOL
 
 
 @pytest.mark.parametrize("V,T", [(1000, 0.0), (1000, 1.0), (1000, 0.2), (152064, 0.2), (152064, 1.0), (7, 1.0)])
