@@ -57,7 +57,7 @@ def test_gemv_gemm_sample_argument_errors():
     assert l.subspec_w4_gemv(p, p, 8, 96, p, p, None) == _lib.ESHAPE
     assert l.subspec_w4_gemv(p, p, 8, 64 * 1024, p, p, None) == _lib.EUNSUPPORTED
     assert l.subspec_bf16_gemv(p, 8, 12, p, p, None) == _lib.ESHAPE
-    assert l.subspec_bf16_gemm(p, 8, 128, p, 65, p, p, 1 << 20, None) == _lib.EINVAL
+    assert l.subspec_bf16_gemm(p, 8, 128, p, 513, p, p, 1 << 20, None) == _lib.EINVAL
     assert l.subspec_bf16_gemm(p, 8, 100, p, 4, p, p, 1 << 20, None) == _lib.ESHAPE
     assert l.subspec_bf16_gemm(p, 4096, 4096, p, 17, p, None, 0, None) == _lib.EWORKSPACE
     assert l.subspec_sample(p, 0, 1.0, p, p, p, 1 << 20, None) == _lib.EINVAL
