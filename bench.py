@@ -68,6 +68,10 @@ def parse():
                     help="only launch one draft GEMV site (e.g. bf16_gate_up), or one verify GEMM "
                          "(verify_gate_up, verify_down: gamma+1 positions, store epilogue), back to "
                          "back, then copy 1 GiB device to device: the workload for counter runs")
+    ap.add_argument("--only", default=None, choices=["tree", "batch_decode", "multilevel", "batch_w4_gemm", "lowbit",
+                                                      "adaptive_length"],
+                    help="only one widened row's section of the 7B workload, from the same prompt state: "
+                         "prints {section: result} (the workload for that row's kernel-trace profile)")
     return ap.parse_args()
 
 
@@ -155,6 +159,26 @@ def main():
         kv0, last = len(prompt) - 1, prompt[-1]
 
     stochastic = wl.temp > 0 or wl.draft_temp > 0
+    if args.only:
+        if args.config != "full7b" or stochastic:
+            print("--only runs the widened rows of the greedy 7B workload (--config full7b)", file=sys.stderr)
+            sys.exit(2)
+        n_w4 = len(dm.substitute_layers)
+        if args.only == "tree":
+            r = tree_rates(dec, dm, shape, wl, kv0, last)
+        elif args.only == "batch_decode":
+            r = batch_decode_rates(dm, w, shape, wl, dev)
+        elif args.only == "multilevel":
+            r = multilevel_rates(dec, dm, w, shape, wl, kv0, last)
+        elif args.only == "batch_w4_gemm":
+            r = batch_rates(dm, shape, dev)
+        elif args.only == "lowbit":
+            r = lowbit_rates(dec, shape, w, wl, kv0, last, dev)
+        else:
+            draft_pass, verify_pass = pass_rates(dec, shape, wl, kv0, last, n_w4)
+            r = adaptive_rates(dec, dm, wl, kv0, last, draft_pass["avg_us"] / verify_pass["avg_us"])
+        print(json.dumps({args.only: r}), flush=True)
+        return
     uni = None
     if stochastic:
         C = G + 1

@@ -32,6 +32,11 @@ def describe(name):
         nt = f",{m[5]}" if m[5] else ""
         return (f"gemv_kernel<{r},{wb},{pro},{epi}{nt}>",
                 f"{width} GEMV, {r} rows/wave, {_PRO.get(pro, pro)} -> {_EPI.get(epi, epi)}")
+    m = re.search(r"gemm_w4_kernel<(true|false)>", name)
+    if m:
+        return (f"gemm_w4_kernel<{m[1]}>",
+                "W4 skinny GEMM (matrix cores, <= 16 positions), " + ("SiLU*up epilogue" if m[1] == "true"
+                                                                      else "store / split-k partials"))
     m = re.search(r"gemm_kernel<(\d+), (\d+), (\d+)>", name)
     if m:
         nw, tt, epi = int(m[1]), int(m[2]), int(m[3])
@@ -70,6 +75,13 @@ _ROLES = {
     "draft_control_kernel": "adaptive draft length: entropy + stop decision",
     "control_update_kernel": "adaptive draft length: EMA centres",
     "rej_rowsum_kernel": "rejection: fixed-point row sums",
+    "rows_sample_kernel": "tree / batch: per-row argmax or exact draw (one block per row)",
+    "tree_root_kernel": "tree: the root's multi-step rejection + the accepted chain's round",
+    "tree_commit_kernel": "tree: accepted chain's K/V moved next to the prefix",
+    "silu_rows_kernel": "rows forward: SiLU(gate) * up (split-k gate/up)",
+    "batch_rollback_kernel": "batched decoding: per-sequence KV rollback",
+    "token_append_kernel": "multi-level: a round's last token appended",
+    "zero_kernel": "fill (arrival counters)",
 }
 
 
