@@ -18,3 +18,18 @@ def oracle_model(shape, w, substitute_layers=()):
     )
     m.make_substitutes(list(substitute_layers))
     return m
+
+
+def memo_weights(om):
+    """The oracle's weight matrices converted once (the same float64 values;
+    the oracle dequantises substitutes on every call), for tests that run
+    many forwards of one large layer."""
+    cache, orig = {}, om.weight
+
+    def weight(l, name, draft):
+        key = (l, name, bool(draft and om.substitute and om.substitute[l] is not None))
+        if key not in cache:
+            cache[key] = orig(l, name, draft)
+        return cache[key]
+    om.weight = weight
+    return om

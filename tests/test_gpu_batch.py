@@ -14,7 +14,7 @@ from oracle.sampling import sample as osample
 from self_speculative_decoding_w4a16_amd import _lib
 from synth import logits_pair, normal_tensor, uniform_codes
 from tests.gpu_util import codes_i32, log, rel_err, ws
-from tests.helpers import host
+from tests.helpers import host, memo_weights, oracle_model
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
@@ -126,7 +126,7 @@ def _batch_setup(shape, seed, B, cap, gamma, ctxs, T=0.0, Td=0.0, device="cuda")
     w = model_weights(shape, seed, device)
     dm = DeviceModel(shape, w)
     dec = BatchDecoder(dm, B, cap, gamma, T, Td)
-    om = oracle_model(shape, w, dm.substitute_layers)
+    om = memo_weights(oracle_model(shape, w, dm.substitute_layers))
     kvs = []
     for b in range(B):
         K, V = kv_history(shape.n_layers, shape.n_kv_heads, ctxs[b], shape.head_dim, cap, seed + 11 + b, device)
@@ -138,7 +138,7 @@ def _batch_setup(shape, seed, B, cap, gamma, ctxs, T=0.0, Td=0.0, device="cuda")
 
 @pytest.mark.parametrize("shape_name,B,gamma,T,Td", [("tiny", 3, 4, 0.0, 0.0), ("tiny", 4, 3, 1.0, 1.0),
                                                      ("tiny", 2, 5, 0.6, 0.0), ("tiny", 5, 4, 0.0, 0.5),
-                                                     ("layer7b", 8, 4, 0.0, 0.0)])
+                                                     ("layer7b", 8, 4, 0.0, 0.0), ("layer7b", 16, 16, 1.0, 0.2)])
 def test_batch_cycles_teacher_forced(cuda, shape_name, B, gamma, T, Td):
     """Every sequence of a batched cycle against the oracle run on that
     sequence alone, teacher-forced on the GPU's tokens: draft and verify

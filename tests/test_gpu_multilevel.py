@@ -17,7 +17,7 @@ from self_speculative_decoding_w4a16_amd.model import DeviceModel
 from synth import model_weights, kv_history, token_ids, uniform_codes
 from synth.configs import QWEN7B
 from tests.gpu_util import log, rel_err
-from tests.helpers import host, oracle_model
+from tests.helpers import host, memo_weights, oracle_model
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
@@ -45,20 +45,6 @@ def _uniforms(cycles, gamma, gamma2, seed):
             R.reshape(cycles, gamma), U)
 
 
-def _memo_weights(om):
-    """The oracle's weight matrices converted once per test (the same
-    float64 values; the oracle dequantises on every call)."""
-    cache, orig = {}, om.weight
-
-    def weight(l, name, draft):
-        key = (l, name, bool(draft and om.substitute and om.substitute[l] is not None))
-        if key not in cache:
-            cache[key] = orig(l, name, draft)
-        return cache[key]
-    om.weight = weight
-    return om
-
-
 @pytest.mark.parametrize("T,T_mid,T2", [(0.0, 0.0, 0.0), (1.0, 1.0, 1.0), (0.0, 0.6, 0.0), (0.8, 0.0, 1.0)])
 def test_multilevel_cycles_teacher_forced(cuda, T, T_mid, T2):
     log(f"multi-level cycles T={T} T_mid={T_mid} T2={T2}")
@@ -76,8 +62,8 @@ def test_multilevel_cycle_7b_layer(cuda, T, T_mid, T2):
 def _check_cycles(shape, seed, ctx, cap, gamma, gamma2, T, T_mid, T2, cycles, cuda):
     w = model_weights(shape, seed, cuda)
     dm4, dm2, om4, om2 = _models(shape, w)
-    _memo_weights(om4)
-    _memo_weights(om2)
+    memo_weights(om4)
+    memo_weights(om2)
     dec = MultiLevelDecoder(dm4, dm2, cap, gamma, gamma2, T, T_mid, T2)
     K, V = kv_history(shape.n_layers, shape.n_kv_heads, ctx, shape.head_dim, cap, 16, cuda)
     dec.k_cache.copy_(K)

@@ -14,7 +14,7 @@ from self_speculative_decoding_w4a16_amd.model import DeviceModel
 from synth import model_weights, kv_history, token_ids, uniform_codes
 from synth.configs import QWEN7B
 from tests.gpu_util import codes_i32, log, rel_err
-from tests.helpers import host, oracle_model
+from tests.helpers import host, memo_weights, oracle_model
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
@@ -30,7 +30,7 @@ def _setup(shape, seed, cap, k, D, kv_len, T=0.0, Td=0.0, device="cuda", graphs=
     K, V = kv_history(shape.n_layers, shape.n_kv_heads, kv_len, shape.head_dim, cap, seed + 7, device)
     dec.k_cache.copy_(K)
     dec.v_cache.copy_(V)
-    om = oracle_model(shape, w, dm.substitute_layers)
+    om = memo_weights(oracle_model(shape, w, dm.substitute_layers))
     kv = (host(K).astype(np.float64), host(V).astype(np.float64))
     return dm, dec, om, kv
 
@@ -130,21 +130,22 @@ def test_tree_cycles_tiny_teacher_forced(cuda, k, D, T, Td):
     log(f"  (n, chain) per cycle: {ns}")
 
 
-@pytest.mark.parametrize("k,D", [(6, 8), (6, 48)])
-def test_tree_cycle_7b_layer(cuda, k, D):
+@pytest.mark.parametrize("k,D,T,Td", [(6, 8, 0.0, 0.0), (6, 48, 0.0, 0.0), (6, 8, 1.0, 1.0)])
+def test_tree_cycle_7b_layer(cuda, k, D, T, Td):
     """One Qwen2.5-7B-shaped layer (vocab 152064) at 1000 KV positions: a
-    greedy tree of k chains; with k = 6, D = 48 the verify pass runs 289
-    positions (the GEMMs in five slices of 64)."""
-    log(f"tree cycle 7B layer k={k} D={D}")
+    tree of k chains, greedy or drawn; with k = 6, D = 48 the verify pass
+    runs 289 positions (the GEMMs in three slices of up to 128)."""
+    log(f"tree cycle 7B layer k={k} D={D} T={T} Td={Td}")
     shape = QWEN7B.with_(n_layers=1, n_shared=0)
     ctx = 1000
     cap = ctx + n_nodes(k, D) + 16
-    dm, dec, om, kv = _setup(shape, 3, cap, k, D, ctx)
+    dm, dec, om, kv = _setup(shape, 3, cap, k, D, ctx, T, Td)
     dec.reset(ctx, int(token_ids(1, shape.vocab, 11)[0]))
     kv_o = (kv[0].copy(), kv[1].copy())
     levels = None if D <= 8 else [0, 1, D // 2, D - 1]
     rows = None if D <= 8 else sorted({0, 1, 2, D, D + 1, 2 * D, 3 * D + 7, 5 * D + 1, n_nodes(k, D) - 1})
-    n, chain = _check_tree_cycle(dec, om, kv_o, k, D, 0.0, 0.0, levels_checked=levels, verify_rows=rows)
+    uh, ud = _uniforms(k, D, 1, 77, cuda) if (T > 0 or Td > 0) else (None, None)
+    n, chain = _check_tree_cycle(dec, om, kv_o, k, D, T, Td, uh, ud, levels_checked=levels, verify_rows=rows)
     log(f"  n={n} chain={chain}")
 
 
