@@ -21,7 +21,9 @@ same blog's section 3.3: after every draft step the library measures the
 token's entropy and decides on the device whether the draft goes on; later
 steps skip themselves, the rejection round judges only the drafted tokens,
 and the controller's class centres are updated from its outcome.  gamma is
-then the longest draft.
+then the longest draft.  With graphs the draft is recorded in segments of
+1, 1, 2, 4, 8 ... steps and the host reads the device draft length after
+each, so the segments past the stop are not launched.
 """
 import torch
 
@@ -131,11 +133,14 @@ class SpecDecoder:
             self.c.kv_score = score
 
     # ------------------------------------------------------------ one cycle
-    def draft(self, u_draft=None):
-        for i in range(self.gamma):
+    def _draft_steps(self, a, b, u_draft):
+        for i in range(a, b):
             _lib.draft_step(self.model.c, self.c, i, self.draft_temp, u_draft, self.ws)
             if self.ctl is not None:
                 _lib.draft_control(self.model.c, self.c, i, self.ctl, self.ws)
+
+    def draft(self, u_draft=None):
+        self._draft_steps(0, self.gamma, u_draft)
 
     def verify(self):
         _lib.verify(self.model.c, self.c, self.gamma + 1, self.tokens, self.target_logits, self.ws)
@@ -175,6 +180,46 @@ class SpecDecoder:
         self.reject(self.r_buf if stochastic else None, self.uf_buf if stochastic else None)
         self.commit()
 
+    def _replay(self, key, body):
+        """body() eagerly the first time, recorded into a HIP graph the
+        second, replayed from then on."""
+        if key not in self._warm:
+            body()
+            self._warm.add(key)
+            return
+        g = self._graphs.get(key)
+        if g is None:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                body()
+            self._graphs[key] = g
+        g.replay()
+
+    def _segments(self):
+        """Draft steps in segments [0, 1), [1, 2), [2, 4), [4, 8), ..."""
+        segs, a, b = [], 0, 1
+        while a < self.gamma:
+            segs.append((a, min(b, self.gamma)))
+            a, b = b, 2 * b
+        return segs
+
+    def _cycle_segmented(self, stochastic):
+        """Adaptive length with graphs: the draft runs as recorded segments and
+        the host reads the device draft length after each, so the segments
+        after the controller's stop are not launched at all (they would only
+        skip themselves); then verify, reject and commit as one graph."""
+        u = self.ud_buf if stochastic else None
+        for a, b in self._segments():
+            self._replay(("draft", stochastic, a), lambda a=a, b=b: self._draft_steps(a, b, u))
+            if b < self.gamma and int(self.draft_len.item()) <= b:
+                break
+
+        def tail():
+            self.verify()
+            self.reject(self.r_buf if stochastic else None, self.uf_buf if stochastic else None)
+            self.commit()
+        self._replay(("tail", stochastic), tail)
+
     def cycle(self, u_draft=None, r_codes=None, u_code=None):
         """One speculative cycle; uniform codes (device int32) are copied into
         the decoder's own buffers first."""
@@ -186,6 +231,9 @@ class SpecDecoder:
                 self.r_buf[:self.gamma].copy_(r_codes[:self.gamma])
             if u_code is not None:
                 self.uf_buf.copy_(u_code.reshape(-1)[:1])
+        if self.use_graphs and self.ctl is not None:
+            self._cycle_segmented(stochastic)
+            return
         key = (stochastic, int(self.c.use_index))
         if not self.use_graphs or key not in self._warm:
             self._cycle_body(stochastic)

@@ -112,11 +112,11 @@ def test_reject_over_a_shortened_draft(cuda, T, Td):
             assert (n, out[:n + 1].tolist(), int(st.item())) == ref, (g, uf)
 
 
-def _adaptive_setup(seed, T, Td, c):
+def _adaptive_setup(seed, T, Td, c, graphs=False):
     gmax, cap, ctx = 8, 256, 40
     w = model_weights(TINY, seed, "cuda")
     dm = DeviceModel(TINY, w)
-    dec = SpecDecoder(dm, cap, gmax, T, Td, adaptive=dict(c=c, beta=0.125))
+    dec = SpecDecoder(dm, cap, gmax, T, Td, adaptive=dict(c=c, beta=0.125), graphs=graphs)
     K, V = kv_history(TINY.n_layers, TINY.n_kv_heads, ctx, TINY.head_dim, cap, seed + 1, "cuda")
     dec.load_kv(K, V, ctx, int(token_ids(1, TINY.vocab, seed + 2)[0]))
     om = oracle_model(TINY, w, dm.substitute_layers)
@@ -124,14 +124,16 @@ def _adaptive_setup(seed, T, Td, c):
     return dm, dec, om, kv_o, gmax
 
 
-@pytest.mark.parametrize("T,Td,c", [(0.0, 0.0, 0.3), (1.0, 1.0, 0.2), (0.0, 0.2, 0.5)])
-def test_adaptive_cycles_teacher_forced(cuda, T, Td, c):
+@pytest.mark.parametrize("T,Td,c,graphs", [(0.0, 0.0, 0.3, False), (1.0, 1.0, 0.2, False), (0.0, 0.2, 0.5, False),
+                                            (1.0, 1.0, 0.2, True), (0.0, 0.0, 0.3, True)])
+def test_adaptive_cycles_teacher_forced(cuda, T, Td, c, graphs):
     """Cycles with the device controller, the oracle teacher-forced on the
     GPU's tokens and entropies: the same draft length every cycle, drafted
     logits within TOL, the decision bit-exact from the GPU's logits, and the
-    centres equal after every round."""
-    log(f"adaptive cycles T={T} Td={Td} c={c}")
-    dm, dec, om, kv_o, gmax = _adaptive_setup(41, T, Td, c)
+    centres equal after every round.  With graphs the draft runs as replayed
+    segments that stop at the controller's draft length."""
+    log(f"adaptive cycles T={T} Td={Td} c={c} graphs={graphs}")
+    dm, dec, om, kv_o, gmax = _adaptive_setup(41, T, Td, c, graphs)
     cycles = 10
     Ud, _ = uniform_codes(cycles * gmax, 42)
     R, _ = uniform_codes(cycles * gmax, 43)
