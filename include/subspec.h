@@ -359,7 +359,8 @@ size_t subspec_batch_workspace_bytes(const subspec_model *m, int32_t batch, int3
  * at position kv_len[b] + step through the draft, writes its K/V there and
  * draft_logits[b][step], and draws tokens[b][step + 1] (argmax, or the
  * inverse CDF with u_codes[b gamma_max + step]); a sequence whose position
- * is past its capacity gets token -1.  Draft weights bf16 or 4-bit. */
+ * is past its capacity gets token -1.  Draft weights bf16 or 4-bit.  With
+ * batch = 1 this is subspec_draft_step on the same buffers. */
 int subspec_batch_draft_step(const subspec_model *m, const subspec_batch_state *st, int32_t step, float draft_temp,
                              const uint32_t *u_codes, void *ws, size_t ws_bytes, void *stream);
 

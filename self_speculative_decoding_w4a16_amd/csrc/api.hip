@@ -824,6 +824,20 @@ int subspec_batch_draft_step(const subspec_model* m, const subspec_batch_state* 
   if (!(draft_temp >= 0.0f)) return fail(SUBSPEC_EINVAL, "draft_temp must be >= 0");
   if (draft_temp > 0.0f && !u_codes) return fail(SUBSPEC_EINVAL, "u_codes needed when draft_temp > 0");
   if ((r = need_ws(ws, ws_bytes, carve_fwd(m, st->batch, st->capacity, nullptr, nullptr)))) return r;
+  if (st->batch == 1) {
+    // one sequence: its buffers are a single-sequence state's, and the
+    // single-sequence draft step (fused GEMVs, per-head split attention)
+    // computes the same row
+    subspec_state one{};
+    one.k_cache = st->k_cache;
+    one.v_cache = st->v_cache;
+    one.capacity = st->capacity;
+    one.kv_len = st->kv_len;
+    one.tokens = st->tokens;
+    one.draft_logits = st->draft_logits;
+    one.gamma_max = st->gamma_max;
+    return subspec_draft_step(m, &one, step, draft_temp, u_codes, ws, ws_bytes, stream);
+  }
   hipStream_t s = hs(stream);
   const int64_t ldt = st->gamma_max + 1;
   RowsSpec rs{};

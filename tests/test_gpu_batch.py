@@ -136,7 +136,7 @@ def _batch_setup(shape, seed, B, cap, gamma, ctxs, T=0.0, Td=0.0, device="cuda")
     return dm, dec, om, kvs
 
 
-@pytest.mark.parametrize("shape_name,B,gamma,T,Td", [("tiny", 3, 4, 0.0, 0.0), ("tiny", 4, 3, 1.0, 1.0),
+@pytest.mark.parametrize("shape_name,B,gamma,T,Td", [("tiny", 1, 4, 1.0, 1.0), ("tiny", 3, 4, 0.0, 0.0), ("tiny", 4, 3, 1.0, 1.0),
                                                      ("tiny", 2, 5, 0.6, 0.0), ("tiny", 5, 4, 0.0, 0.5),
                                                      ("layer7b", 8, 4, 0.0, 0.0), ("layer7b", 16, 16, 1.0, 0.2)])
 def test_batch_cycles_teacher_forced(cuda, shape_name, B, gamma, T, Td):
