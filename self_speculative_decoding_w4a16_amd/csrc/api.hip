@@ -984,7 +984,14 @@ int subspec_tree_draft(const subspec_model* m, const subspec_state* st, int32_t 
     rs.logits = st->draft_logits + (int64_t)level * m->vocab;
     rs.ld = (int64_t)(depth - 1) * m->vocab;
   }
-  if ((r = rows_forward(m, rows_cache(st), rs, ws, s))) return r;
+  if (level == 0 && !st->use_index && !st->draft_len) {
+    // the root is one row: the single-sequence draft step (fused GEMVs)
+    // writes its K/V at slot kv_len and its logits in draft_logits row 0;
+    // its own argmax in tokens[1] is replaced by the root's children below
+    if ((r = subspec_draft_step(m, st, 0, 0.0f, nullptr, ws, ws_bytes, stream))) return r;
+  } else if ((r = rows_forward(m, rows_cache(st), rs, ws, s))) {
+    return r;
+  }
   {
     prof::Scope ps(SUBSPEC_K_SAMPLE, 2.0 * rows * m->vocab, s);
     RowsSampleArgs sa{};
