@@ -825,7 +825,7 @@ def tree_rates(dec, dm, shape, wl, kv0, last, k=6, depth=48, G=64, steps=1):
     sections 6.3 and 3.7): tokens/s and tau over graph-replayed cycles, and
     the tau-independent passes - one draft level (k rows through the draft in
     one weight stream) and the verify pass over all 1 + k D nodes (the GEMMs
-    in slices of 64 positions), each graph-replayed, against their
+    in slices of up to 128 positions), each graph-replayed, against their
     algorithmic bytes and the matrix-core peak."""
     import time
 

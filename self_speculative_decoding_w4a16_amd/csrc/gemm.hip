@@ -1,15 +1,17 @@
 // Verify GEMM on the matrix cores: Y[t][n] = sum_k X[t][k] W[n][k] for the
-// gamma+1 <= 64 positions of one verify pass.  The weights are loaded once for
-// all positions ("How speculative decoding makes LLMs go brrr", Module 2), so
+// gamma+1 positions of one verify pass (and the rows of a tree's or a batch's
+// pass).  The weights are loaded once for every slice of up to 64 positions
+// (128 past 64) ("How speculative decoding makes LLMs go brrr", Module 2), so
 // the pass stays bound by streaming W from HBM; MFMA keeps the arithmetic off
-// the critical path (arithmetic intensity <= 64 flop/byte, far below the
+// the critical path (arithmetic intensity <= 128 flop/byte, below the
 // matrix-core ridge).
 //
 //  * v_mfma_f32_16x16x32_bf16: A = 16 weight rows x 32 k, B = 32 k x 16
 //    positions, D = 16 rows x 16 positions (lane l holds rows 4(l/16)..+3 of
 //    position l%16).
-//  * A block has NW waves (2, or 8 for the very wide lm_head); each wave
-//    owns one 16-row tile and all ceil(m/16) position tiles.  The block walks
+//  * A block has NW waves (2, or 8 for the very wide lm_head and past 64
+//    positions); each wave owns one 16-row tile and all position tiles of
+//    its slice (up to 4, or 8 past 64 positions).  The block walks
 //    its k range in chunks of 128: the activation chunk X[0..16 TT)[kc..+128)
 //    is staged in LDS (double-buffered, one barrier a chunk) and read by all
 //    NW waves.  Each wave loads its weight chunk row-contiguously (load s:
