@@ -7,12 +7,16 @@ import numpy as np
 import pytest
 import torch
 
-from oracle.model import linear
+from oracle.cycle import autoregressive_generate
+from oracle.model import forward, linear
 from oracle.quant import dequantize, quantize as oq
 from oracle.reject import reject as oreject
 from oracle.sampling import sample as osample
 from self_speculative_decoding_w4a16_amd import _lib
-from synth import logits_pair, normal_tensor, uniform_codes
+from self_speculative_decoding_w4a16_amd.engine import BatchDecoder
+from self_speculative_decoding_w4a16_amd.model import DeviceModel
+from synth import kv_history, logits_pair, model_weights, normal_tensor, token_ids, uniform_codes
+from synth.configs import QWEN7B
 from tests.gpu_util import codes_i32, log, rel_err, ws
 from tests.helpers import host, memo_weights, oracle_model
 
@@ -108,13 +112,6 @@ def test_w4_gemm_gate_up_shape_sampled(cuda):
 
 
 # ---------------------------------------------------------------- batched decoding
-from oracle.cycle import autoregressive_generate  # noqa: E402
-from oracle.model import forward, new_kv  # noqa: E402
-from self_speculative_decoding_w4a16_amd.engine import BatchDecoder  # noqa: E402
-from self_speculative_decoding_w4a16_amd.model import DeviceModel  # noqa: E402
-from synth import model_weights, kv_history, token_ids  # noqa: E402
-from synth.configs import QWEN7B  # noqa: E402
-from tests.helpers import oracle_model  # noqa: E402
 
 TINY = QWEN7B.with_(n_layers=3, hidden=256, ffn=512, n_q_heads=4, n_kv_heads=2, head_dim=128,
                     vocab=1000, n_shared=1)
