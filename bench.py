@@ -35,7 +35,7 @@ TRAFFIC = {
     "w4_gate_up": {"fetch_kib": 37469.8, "write_kib": 148.0, "fetch_scale": 2.0,
                    "write_scale": 1.0, "sources": "724c5b6449a9c9de"},
 }
-GEMV_SOURCES = ("csrc/gemv.hip", "csrc/common.h", "csrc/internal.h")
+GEMV_SOURCES = ("csrc/gemv.hip", "csrc/gemv_w4t.hip", "csrc/common.h", "csrc/internal.h")
 
 
 def sources_hash(files):
@@ -556,18 +556,25 @@ def isolated_gemvs(dm, shape, dev, reps=3, only=None, graph=True):
                 continue
             w4 = kind == "w4"
             mats = [dm.q[l][name] if w4 else (dm.w["layers"][l][name],) for l in layers]
+            lay = dm.layout[layers[0]][name] if w4 else 0
             wb = n_out * (2 if epi == 2 else 1) * k * (0.5 + 4 / 64 if w4 else 2.0)
             copies = [tuple(t.clone() for t in m) for _ in range(int((1 << 30) // (wb * len(mats))))
                       for m in mats]
-            lins = [_lib.linear(codes=m[0], meta=m[1]) if w4 else _lib.linear(w=m[0])
+            lins = [_lib.linear(codes=m[0], meta=m[1], layout=lay) if w4 else _lib.linear(w=m[0])
                     for m in mats + copies]
             by = wb + 2 * k + 2 * n_out * (2 if epi == 1 else 1)
             us = timed(lins, k, n_out, norm, epi)
             del copies, lins
             r = rows_per_wave(n_out, epi == 2, w4)
+            if lay:  # the tiled 4-bit GEMV: <tiles, chunks in flight, x items per thread, prologue, epilogue>
+                nx = next(v for v in (1, 2, 3, 5, 7) if v * 8 * 512 >= k)
+                tp = "1,4" if epi == 1 else "2,2"
+                symbol = f"gemv_w4t_kernel<{tp},{nx},{1 if norm else 0},{epi}>"
+            else:
+                symbol = sym.format(r=r, w="4" if w4 else "16")
             out[f"{kind}_{site}"] = {"avg_us": round(us, 3), "bytes_per_launch": round(by),
                                      "gbs": round(by / (us * 1e-6) / 1e9, 1), "per_step": len(layers),
-                                     "symbol": sym.format(r=r, w="4" if w4 else "16")}
+                                     "symbol": symbol}
     if only and only != "lm_head":
         return out
     lm = _lib.linear(w=dm.w["lm_head"])
@@ -721,8 +728,7 @@ def lowbit_rates(dec, shape, w, wl, kv0, last, dev):
         g = dm.w["final_norm"]
         resid = torch.zeros(H, dtype=torch.bfloat16, device=dev)
         for site, k, nout, epi in (("gate_up", H, F, 2), ("down", F, H, 1)):
-            lins = [_lib.linear(codes=dm.q[l][site][0], meta=dm.q[l][site][1], bits=bits)
-                    for l in dm.substitute_layers]
+            lins = [dm.linear_d(l, site) for l in dm.substitute_layers]
             reps = max(1, int((1 << 30) // (n_sub * (2 if epi == 2 else 1) * nout * k * (bits / 8 + 4 / 64))))
 
             def run(lins=lins, k=k, epi=epi):
@@ -799,7 +805,7 @@ def batch_rates(dm, shape, dev):
     out = {}
     sub = dm.substitute_layers
     for site, k, n in (("gate_up", H, 2 * F), ("down", F, H)):
-        lins = [_lib.linear(codes=dm.q[l][site][0], meta=dm.q[l][site][1]) for l in sub]
+        lins = [dm.linear_d(l, site) for l in sub]
         wb = n * k * (0.5 + 4 / 64)
         reps = max(1, int((1 << 30) // (wb * len(lins))))
         for m in (1, 4, 8, 16):

@@ -32,7 +32,7 @@ class SubspecError(RuntimeError):
 
 class Linear(ctypes.Structure):
     _fields_ = [("w", c_void_p), ("codes", c_void_p), ("meta", c_void_p),
-                ("n", c_int64), ("k", c_int64), ("bits", c_int32)]
+                ("n", c_int64), ("k", c_int64), ("bits", c_int32), ("layout", c_int32)]
 
 
 class Layer(ctypes.Structure):
@@ -76,6 +76,7 @@ _SIGS = {
     "subspec_workspace_init": (c_int32, [c_void_p, c_size_t, c_void_p]),
     "subspec_quantize": (c_int32, [c_void_p, c_int64, c_int64, c_int32, c_int32, c_void_p,
                                    c_void_p, c_void_p]),
+    "subspec_w4_tile": (c_int32, [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
     "subspec_draft_step": (c_int32, [POINTER(Model), POINTER(State), c_int32, c_float, c_void_p,
                                      c_void_p, c_size_t, c_void_p]),
     "subspec_verify": (c_int32, [POINTER(Model), POINTER(State), c_int32, c_void_p, c_void_p,
@@ -219,6 +220,13 @@ def quantize(w, codes, meta, group=64, bits=4, stream=None):
     check(lib().subspec_quantize(_p(w), n, k, group, bits, _p(codes), _p(meta), _stream(stream)))
 
 
+def w4_tile(codes, meta, tcodes, tmeta, stream=None):
+    """4-bit codes [n][k/2] + meta [n][k/64][2] -> the 16-row tiles of
+    subspec_w4_tile (same sizes)."""
+    n, k = codes.shape[0], 2 * codes.shape[1]
+    check(lib().subspec_w4_tile(_p(codes), _p(meta), n, k, _p(tcodes), _p(tmeta), _stream(stream)))
+
+
 def draft_step(model, state, step, draft_temp, u_codes, ws, stream=None):
     check(lib().subspec_draft_step(ctypes.byref(model), ctypes.byref(state), step, draft_temp,
                                    _p(u_codes), _p(ws), ws.numel() * ws.element_size(),
@@ -331,15 +339,16 @@ def hbm_read(buf, sink, stream=None):
     check(lib().subspec_hbm_read(_p(buf), buf.numel() * buf.element_size(), _p(sink), _stream(stream)))
 
 
-def linear(w=None, codes=None, meta=None, n=None, k=None, bits=4):
+def linear(w=None, codes=None, meta=None, n=None, k=None, bits=4, layout=0):
     """A subspec_linear for bf16 weights w [n][k], or low-bit codes + meta
-    [n][k/64][2] at ``bits`` = 4, 3 or 2 (k from meta when not given)."""
+    [n][k/64][2] at ``bits`` = 4, 3 or 2 (k from meta when not given);
+    ``layout`` 1: 4-bit codes + meta in the tiles of w4_tile."""
     if w is not None:
         n, k = w.shape
-        return Linear(_p(w), None, None, n, k, 0)
+        return Linear(_p(w), None, None, n, k, 0, 0)
     n = codes.shape[0] if n is None else n
     k = 64 * meta.shape[1] if k is None else k
-    return Linear(None, _p(codes), _p(meta), n, k, bits)
+    return Linear(None, _p(codes), _p(meta), n, k, bits, layout)
 
 
 GEMV_STORE, GEMV_RESID, GEMV_SILU = 0, 1, 2

@@ -96,6 +96,19 @@ int lin_bits(const subspec_linear& l) { return lin_is_w4(l) ? (l.bits == 0 ? 4 :
 // bytes of one row of codes
 double code_row_bytes(int bits, double k) { return bits == 4 ? k / 2 : (bits == 2 ? k / 4 : 3 * k / 8); }
 
+// layout 1 (16-row tiles of subspec_w4_tile): 4-bit only, n % 16 == 0,
+// k % 128 == 0, k within the tiled GEMV's prologue (kMaxTiledK)
+constexpr int64_t kMaxTiledK = 28672;
+int check_layout(const subspec_linear& l, const char* what, int layer) {
+  if (lin_is_bf16(l) || l.layout == 0) return SUBSPEC_OK;
+  if (l.layout != 1) return fail(SUBSPEC_EINVAL, "layer %d %s: layout must be 0 or 1", layer, what);
+  if (lin_bits(l) != 4) return fail(SUBSPEC_EINVAL, "layer %d %s: layout 1 needs 4-bit codes", layer, what);
+  if (l.n % 16 != 0 || l.k % 128 != 0 || l.k > kMaxTiledK)
+    return fail(SUBSPEC_ESHAPE, "layer %d %s: layout 1 needs n %% 16 == 0, k %% 128 == 0 and k <= %lld", layer,
+                what, (long long)kMaxTiledK);
+  return SUBSPEC_OK;
+}
+
 int check_linear(const subspec_linear& l, int64_t n, int64_t k, bool allow_w4, const char* what,
                  int layer) {
   if (l.n != n || l.k != k)
@@ -105,7 +118,7 @@ int check_linear(const subspec_linear& l, int64_t n, int64_t k, bool allow_w4, c
   if (allow_w4 && lin_is_w4(l)) {
     if (lin_bits(l) == 3 && k % 128 != 0)
       return fail(SUBSPEC_ESHAPE, "layer %d %s: 3-bit codes need k %% 128 == 0", layer, what);
-    return SUBSPEC_OK;
+    return check_layout(l, what, layer);
   }
   return fail(SUBSPEC_EINVAL, "layer %d %s: set exactly one of w (bf16)%s", layer, what,
               allow_w4 ? " or codes+meta with bits 4, 3 or 2" : "");
@@ -305,6 +318,7 @@ void set_linear(GemvArgs& a, const subspec_linear& l) {
   a.w = l.w;
   a.codes = l.codes;
   a.meta = l.meta;
+  a.tiled = l.layout;
 }
 
 // Algorithmic bytes of one launch: weights, input, output (and residual)
@@ -399,7 +413,7 @@ int rows_forward(const subspec_model* m, const RowsCache& st, const RowsSpec& rs
     bool q_part = false;
     if (lin_is_w4(lq)) {
       prof::Scope ps(SUBSPEC_K_W4_QKV, gemm_w4_bytes(qkv, H, mt, qkv, false), s);
-      HIPCHK(launch_gemm_w4(lq.codes, lq.meta, qkv, H, w.xn, mt, w.qkv, w.gemm_part, s, &q_splits));
+      HIPCHK(launch_gemm_w4(lq.codes, lq.meta, qkv, H, w.xn, mt, w.qkv, w.gemm_part, s, &q_splits, lq.layout));
       q_part = true;
     } else {
       GemmArgs q{lq.w, qkv, H, w.xn, mt, w.qkv, qkv, nullptr, w.gemm_part};
@@ -446,7 +460,7 @@ int rows_forward(const subspec_model* m, const RowsCache& st, const RowsSpec& rs
     }
     if (lin_is_w4(lo)) {
       prof::Scope ps(SUBSPEC_K_W4_O, gemm_w4_bytes(H, qd, mt, H, true), s);
-      HIPCHK(launch_gemm_w4(lo.codes, lo.meta, H, qd, w.attn, mt, w.h, w.gemm_part, s, &pend_splits));
+      HIPCHK(launch_gemm_w4(lo.codes, lo.meta, H, qd, w.attn, mt, w.h, w.gemm_part, s, &pend_splits, lo.layout));
       pend = w.gemm_part;
     } else {
       GemmArgs o{lo.w, H, qd, w.attn, mt, w.h, H, w.h, w.gemm_part};
@@ -461,9 +475,9 @@ int rows_forward(const subspec_model* m, const RowsCache& st, const RowsSpec& rs
     if (lin_is_w4(lg)) {
       prof::Scope ps(SUBSPEC_K_W4_GATE_UP, gemm_w4_bytes(2 * F, H, mt, F, false), s);
       if (gemm_w4_splits(2 * F, H) == 1) {  // SiLU * up in the GEMM's epilogue
-        HIPCHK(launch_gemm_w4_silu(lg.codes, lg.meta, F, H, w.xn, mt, w.act, s));
+        HIPCHK(launch_gemm_w4_silu(lg.codes, lg.meta, F, H, w.xn, mt, w.act, s, lg.layout));
       } else {
-        HIPCHK(launch_gemm_w4(lg.codes, lg.meta, 2 * F, H, w.xn, mt, w.gu, w.gemm_part, s));
+        HIPCHK(launch_gemm_w4(lg.codes, lg.meta, 2 * F, H, w.xn, mt, w.gu, w.gemm_part, s, nullptr, lg.layout));
         HIPCHK(launch_silu_rows(w.gu, F, mt, w.act, s));
       }
     } else {
@@ -473,7 +487,7 @@ int rows_forward(const subspec_model* m, const RowsCache& st, const RowsSpec& rs
     }
     if (lin_is_w4(ldn)) {
       prof::Scope ps(SUBSPEC_K_W4_DOWN, gemm_w4_bytes(H, F, mt, H, true), s);
-      HIPCHK(launch_gemm_w4(ldn.codes, ldn.meta, H, F, w.act, mt, w.h, w.gemm_part, s, &pend_splits));
+      HIPCHK(launch_gemm_w4(ldn.codes, ldn.meta, H, F, w.act, mt, w.h, w.gemm_part, s, &pend_splits, ldn.layout));
       pend = w.gemm_part;
     } else {
       GemmArgs dn{ldn.w, H, F, w.act, mt, w.h, H, w.h, w.gemm_part};
@@ -569,6 +583,15 @@ int subspec_quantize(const uint16_t* w, int64_t n, int64_t k, int32_t group, int
   if (k % 64 != 0) return fail(SUBSPEC_ESHAPE, "k must be a multiple of 64");
   if (bits == 3 && k % 128 != 0) return fail(SUBSPEC_ESHAPE, "3-bit codes need k %% 128 == 0");
   HIPCHK(launch_quantize(w, n, k, bits, codes, meta, hs(stream)));
+  return ok();
+}
+
+int subspec_w4_tile(const uint8_t* codes, const uint16_t* meta, int64_t n, int64_t k, uint8_t* tcodes,
+                    uint16_t* tmeta, void* stream) {
+  if (!codes || !meta || !tcodes || !tmeta) return fail(SUBSPEC_EINVAL, "codes, meta, tcodes and tmeta must be set");
+  if (n < 1 || k < 1) return fail(SUBSPEC_EINVAL, "n and k must be positive");
+  if (n % 16 != 0 || k % 128 != 0) return fail(SUBSPEC_ESHAPE, "n %% 16 == 0 and k %% 128 == 0 needed");
+  HIPCHK(launch_w4_tile(codes, meta, n, k, tcodes, tmeta, hs(stream)));
   return ok();
 }
 
@@ -1256,6 +1279,10 @@ int subspec_gemv(const subspec_linear* w, const uint16_t* x, const uint16_t* nor
   if (epilogue == 1 && !resid) return fail(SUBSPEC_EINVAL, "resid must be set for epilogue 1");
   if (epilogue == 2 && w->n % 2 != 0) return fail(SUBSPEC_ESHAPE, "epilogue 2 needs an even row count");
   if (norm_w && !(eps >= 0.0f)) return fail(SUBSPEC_EINVAL, "eps must be >= 0");
+  int r;
+  if ((r = check_layout(*w, "w", -1))) return r;
+  if (lin_is_w4(*w) && w->layout == 1 && epilogue == 2 && (w->n / 2) % 16 != 0)
+    return fail(SUBSPEC_ESHAPE, "layout 1 with epilogue 2 needs n %% 32 == 0");
   GemvArgs a{};
   set_linear(a, *w);
   a.n = epilogue == 2 ? w->n / 2 : w->n;
@@ -1293,10 +1320,12 @@ int subspec_w4_gemm(const subspec_linear* w, const uint16_t* x, int32_t m, uint1
   if (w->k % 128 != 0) return fail(SUBSPEC_ESHAPE, "k must be a multiple of 128");
   if (m < 1 || m > 16) return fail(SUBSPEC_EINVAL, "m outside [1, 16]");
   int r;
+  if ((r = check_layout(*w, "w", -1))) return r;
   if ((r = need_ws(ws, ws_bytes, kCounterBytes + (size_t)gemm_w4_splits(w->n, w->k) * m * w->n * 4))) return r;
   prof::Scope ps(SUBSPEC_K_W4_GATE_UP, w->n * code_row_bytes(4, (double)w->k) + w->n * (w->k / 64) * 4.0 +
                  2.0 * m * (w->k + w->n), hs(stream));
-  HIPCHK(launch_gemm_w4(w->codes, w->meta, w->n, w->k, x, m, y, (float*)((char*)ws + kCounterBytes), hs(stream)));
+  HIPCHK(launch_gemm_w4(w->codes, w->meta, w->n, w->k, x, m, y, (float*)((char*)ws + kCounterBytes), hs(stream),
+                        nullptr, w->layout));
   return ok();
 }
 

@@ -36,6 +36,10 @@
 //  * One wave per block, 16 RT rows; narrow matrices split k over blocks
 //    (fp32 partials, summed in split order by a second launch or by the
 //    caller's consumer).
+//  * Codes and meta row-major (subspec_quantize) or in 16-row tiles
+//    (subspec_w4_tile): the lane reads the same 16 bytes and scale/min pair
+//    either way, from one contiguous KiB per tile and chunk in the tiled
+//    layout.
 #include "common.h"
 #include "internal.h"
 #include "profile.h"
@@ -57,8 +61,9 @@ struct Slot {
   u32x4 xv[4];   // activations of position r for the four MFMA steps
 };
 
-// SILU: the gate/up projection (n = 2 silu_f rows) ending in SiLU(gate) * up
-template <bool SILU>
+// SILU: the gate/up projection (n = 2 silu_f rows) ending in SiLU(gate) * up;
+// TL: tiled codes and meta
+template <bool SILU, bool TL>
 __global__ __launch_bounds__(64) void gemm_w4_kernel(const uint8_t* __restrict__ codes,
                                                      const uint16_t* __restrict__ meta, int64_t n, int K,
                                                      const uint16_t* __restrict__ x, int m, uint16_t* y,
@@ -96,8 +101,14 @@ __global__ __launch_bounds__(64) void gemm_w4_kernel(const uint8_t* __restrict__
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int rr = (SILU && t >= HT) ? (int)silu_f + 16 * (t - HT) + r : 16 * t + r;
-      sl.pc[t] = __builtin_amdgcn_raw_buffer_load_b128(crs, in ? rr * (K / 2) + kc / 2 + 16 * g : kOutside, 0, 0);
-      sl.mt[t] = __builtin_amdgcn_raw_buffer_load_b64(mrs, in ? rr * (K / 16) + 4 * (kc / 64) : kOutside, 0, 0);
+      if constexpr (TL) {  // rows rr - r .. rr - r + 15 form one tile (silu_f % 16 == 0)
+        const int tb = (rr >> 4) * (K / KC) + kc / KC;
+        sl.pc[t] = __builtin_amdgcn_raw_buffer_load_b128(crs, in ? tb * 1024 + 16 * lane : kOutside, 0, 0);
+        sl.mt[t] = __builtin_amdgcn_raw_buffer_load_b64(mrs, in ? tb * 128 + 8 * r : kOutside, 0, 0);
+      } else {
+        sl.pc[t] = __builtin_amdgcn_raw_buffer_load_b128(crs, in ? rr * (K / 2) + kc / 2 + 16 * g : kOutside, 0, 0);
+        sl.mt[t] = __builtin_amdgcn_raw_buffer_load_b64(mrs, in ? rr * (K / 16) + 4 * (kc / 64) : kOutside, 0, 0);
+      }
     }
   };
   f32x4_t acc[RT];
@@ -205,23 +216,31 @@ int gemm_w4_splits(int64_t n, int64_t k) {
 }
 
 hipError_t launch_gemm_w4(const uint8_t* codes, const uint16_t* meta, int64_t n, int64_t k, const uint16_t* x, int m,
-                          uint16_t* y, float* part, hipStream_t s, int* splits_out) {
+                          uint16_t* y, float* part, hipStream_t s, int* splits_out, bool tiled) {
   const int splits = gemm_w4_splits(n, k);
   const int to_part = splits_out != nullptr;
   if (to_part) *splits_out = splits;
   const dim3 grid((unsigned)((n + 16 * RT - 1) / (16 * RT)), (unsigned)splits), block(64);
-  SS_LAUNCH(gemm_w4_kernel<false>, grid, block, 0, s, codes, meta, n, (int)k, x, m, y, part, splits, to_part,
-            (int64_t)0);
+  if (tiled)
+    SS_LAUNCH((gemm_w4_kernel<false, true>), grid, block, 0, s, codes, meta, n, (int)k, x, m, y, part, splits, to_part,
+              (int64_t)0);
+  else
+    SS_LAUNCH((gemm_w4_kernel<false, false>), grid, block, 0, s, codes, meta, n, (int)k, x, m, y, part, splits,
+              to_part, (int64_t)0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1 || to_part) return e;
   return launch_gemm_reduce(part, splits, m, n, y, n, s);
 }
 
 hipError_t launch_gemm_w4_silu(const uint8_t* codes, const uint16_t* meta, int64_t F, int64_t k, const uint16_t* x,
-                               int m, uint16_t* act, hipStream_t s) {
+                               int m, uint16_t* act, hipStream_t s, bool tiled) {
   if (gemm_w4_splits(2 * F, k) != 1) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((F + 8 * RT - 1) / (8 * RT))), block(64);
-  SS_LAUNCH(gemm_w4_kernel<true>, grid, block, 0, s, codes, meta, 2 * F, (int)k, x, m, act, (float*)nullptr, 1, 0,
-            F);
+  if (tiled)
+    SS_LAUNCH((gemm_w4_kernel<true, true>), grid, block, 0, s, codes, meta, 2 * F, (int)k, x, m, act,
+              (float*)nullptr, 1, 0, F);
+  else
+    SS_LAUNCH((gemm_w4_kernel<true, false>), grid, block, 0, s, codes, meta, 2 * F, (int)k, x, m, act,
+              (float*)nullptr, 1, 0, F);
   return hipGetLastError();
 }

@@ -31,11 +31,19 @@ struct GemvArgs {
   float* part_max;           // EPI_LOGITS: per-block max
   int32_t* part_arg;         // EPI_LOGITS: per-block argmax
   const int32_t* valid;      // optional device flag: skip everything if *valid == 0
+  int tiled;                 // 4-bit codes + meta in 16-row tiles (subspec_w4_tile)
 };
 
 int gemv_max_blocks(bool w4, int64_t n, int epi);  // blocks of one launch (logits partials)
 // wb: weight width, 16 (bf16 w), 4, 3 or 2 (codes + meta; see subspec_quantize)
 hipError_t launch_gemv(int wb, int pro, int epi, const GemvArgs& a, hipStream_t s, int* blocks_out);
+// 4-bit GEMV on 16-row tiles (a.tiled; matrix cores): prologue/epilogue
+// pairs it takes, and the launch (a.n % 16 == 0, a.k % 128 == 0, a.k <= 28672)
+bool gemv_w4t_supported(int pro, int epi);
+hipError_t launch_gemv_w4t(int pro, int epi, const GemvArgs& a, hipStream_t s);
+// row-major 4-bit codes + meta -> 16-row tiles (n % 16 == 0, k % 128 == 0)
+hipError_t launch_w4_tile(const uint8_t* codes, const uint16_t* meta, int64_t n, int64_t k, uint8_t* tcodes,
+                          uint16_t* tmeta, hipStream_t s);
 
 // ------------------------------------------------------------------ GEMM (verify)
 // GEPI_PARTIAL: fp32 partial sums [split][m][n] for the caller to reduce
@@ -62,19 +70,20 @@ hipError_t launch_gemm_reduce(const float* part, int splits, int m, int64_t n, u
                               hipStream_t s);
 
 // Skinny GEMM on 4-bit weights (matrix cores): Y[t][n] = bf16(sum_k X[t][k] w[n][k])
-// for t < m <= 16; k % 128 == 0.  With k split over blocks it writes fp32
+// for t < m <= 16; k % 128 == 0; codes + meta row-major, or in 16-row tiles
+// (tiled; n % 16 == 0).  With k split over blocks it writes fp32
 // partials (gemm_w4_splits x m x n floats at part) and reduces them in order.
 // With splits_out set it always writes the partials ([splits][m][n], also
 // for one split), reduces nothing and returns the count: the consumer adds
 // them (the rows forward's RoPE and residual + RMSNorm kernels).
 int gemm_w4_splits(int64_t n, int64_t k);
 hipError_t launch_gemm_w4(const uint8_t* codes, const uint16_t* meta, int64_t n, int64_t k, const uint16_t* x, int m,
-                          uint16_t* y, float* part, hipStream_t s, int* splits_out = nullptr);
+                          uint16_t* y, float* part, hipStream_t s, int* splits_out, bool tiled);
 // The gate/up projection (2F rows: gate rows, then up rows) ending in
 // act[t][j] = bf16(SiLU(gate) * up); only while it needs no k split
 // (gemm_w4_splits(2F, k) == 1), else hipErrorInvalidValue.
 hipError_t launch_gemm_w4_silu(const uint8_t* codes, const uint16_t* meta, int64_t F, int64_t k, const uint16_t* x,
-                               int m, uint16_t* act, hipStream_t s);
+                               int m, uint16_t* act, hipStream_t s, bool tiled);
 
 // ------------------------------------------------------------------ quantise
 hipError_t launch_quantize(const uint16_t* w, int64_t n, int64_t k, int bits, uint8_t* codes,

@@ -16,12 +16,18 @@ from . import _lib
 MATS = ("qkv", "o", "gate_up", "down")
 
 
+MAX_TILED_K = 28672
+
+
 class DeviceModel:
-    def __init__(self, shape, weights, substitute_layers=None, stream=None, bits=4):
+    def __init__(self, shape, weights, substitute_layers=None, stream=None, bits=4, tiled=True):
         """``weights``: dict from synth.model_weights (bf16 tensors on the GPU).
         ``substitute_layers``: indices quantised for the draft (default: all
         layers from ``shape.n_shared`` on).  ``bits``: code width of the
-        substitutes, 4, 3 or 2 (an int, or a dict layer -> width)."""
+        substitutes, 4, 3 or 2 (an int, or a dict layer -> width).
+        ``tiled``: keep 4-bit substitutes in the 16-row tiles of
+        subspec_w4_tile (the matrix-core draft GEMV) where the shape allows;
+        otherwise (and at 2 or 3 bits) row-major."""
         self.shape = shape
         self.w = weights
         L = len(weights["layers"])
@@ -30,8 +36,9 @@ class DeviceModel:
         self.substitute_layers = sorted(set(substitute_layers))
         self.bits = {l: (bits[l] if isinstance(bits, dict) else bits) for l in self.substitute_layers}
         self.q = [None] * L
+        self.layout = [None] * L
         for l in self.substitute_layers:
-            self.q[l] = {}
+            self.q[l], self.layout[l] = {}, {}
             b = self.bits[l]
             for name in MATS:
                 wt = weights["layers"][l][name]
@@ -39,16 +46,28 @@ class DeviceModel:
                 codes = torch.empty((n, _lib.code_row_bytes(k, b)), dtype=torch.uint8, device=wt.device)
                 meta = torch.empty((n, k // 64, 2), dtype=torch.float16, device=wt.device)
                 _lib.quantize(wt, codes, meta, bits=b, stream=stream)
+                lay = int(tiled and b == 4 and n % 16 == 0 and k % 128 == 0 and k <= MAX_TILED_K)
+                if lay:
+                    tc, tm = torch.empty_like(codes), torch.empty_like(meta)
+                    _lib.w4_tile(codes, meta, tc, tm, stream=stream)
+                    codes, meta = tc, tm
                 self.q[l][name] = (codes, meta)
+                self.layout[l][name] = lay
         self._build_structs()
 
     def _lin_bf16(self, t):
         n, k = t.shape
-        return _lib.Linear(t.data_ptr(), None, None, n, k, 0)
+        return _lib.Linear(t.data_ptr(), None, None, n, k, 0, 0)
 
-    def _lin_w4(self, codes, meta, bits):
+    def _lin_w4(self, codes, meta, bits, layout):
         n = codes.shape[0]
-        return _lib.Linear(None, codes.data_ptr(), meta.data_ptr(), n, 64 * meta.shape[1], bits)
+        return _lib.Linear(None, codes.data_ptr(), meta.data_ptr(), n, 64 * meta.shape[1], bits, layout)
+
+    def linear_d(self, l, name):
+        """The draft's subspec_linear of matrix ``name`` of layer ``l``."""
+        if self.q[l] is not None:
+            return self._lin_w4(*self.q[l][name], self.bits[l], self.layout[l][name])
+        return self._lin_bf16(self.w["layers"][l][name])
 
     def _build_structs(self):
         s = self.shape
@@ -60,10 +79,7 @@ class DeviceModel:
             st.ffn_norm = lw["ffn_norm"].data_ptr()
             for name in MATS:
                 setattr(st, name, self._lin_bf16(lw[name]))
-                if self.q[l] is not None:
-                    setattr(st, name + "_d", self._lin_w4(*self.q[l][name], self.bits[l]))
-                else:
-                    setattr(st, name + "_d", self._lin_bf16(lw[name]))
+                setattr(st, name + "_d", self.linear_d(l, name))
         self.c = _lib.Model(L, s.hidden, s.ffn, s.n_q_heads, s.n_kv_heads, s.head_dim, s.vocab,
                             s.rope_theta, s.rms_eps, self.w["embed"].data_ptr(),
                             self.w["final_norm"].data_ptr(), self.w["lm_head"].data_ptr(),
