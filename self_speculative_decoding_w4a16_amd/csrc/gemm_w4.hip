@@ -20,10 +20,14 @@
 //    (q3, q7).  The same lane loads the activations of position r at those k
 //    straight from memory (x is small and stays in the caches), pairs them
 //    the same way, and uses them for all RT tiles - so no LDS and no barrier.
-//  * Lanes g = 0, 1 hold the chunk's first group and g = 2, 3 its second;
+//  * Lanes g = 0, 1 hold the chunk's first group and g = 2, 3 its second.
+//    Up to 8 positions, A row p holds position p on the first group's
+//    lanes and row 8 + p on the second's (every other A value zero), so one
+//    MFMA per tile and step yields both groups' sums in separate D rows and
+//    a lane scales its four values with one group's scale/min; the two
+//    halves of each sum meet by a lane swap at the end.  Past 8 positions
 //    every step runs two MFMAs per tile, one with the activations of the
-//    second group's lanes zeroed and one with the first group's zeroed, so
-//    each accumulates one group's sums.
+//    second group's lanes zeroed and one with the first group's zeroed.
 //  * A = activations, B = weights: lane (r, g) of tile t ends with
 //    positions 4 g + i of the tile's row r, so it applies only its own row's
 //    scale/min (one 8-byte load per tile and chunk).
@@ -62,8 +66,8 @@ struct Slot {
 };
 
 // SILU: the gate/up projection (n = 2 silu_f rows) ending in SiLU(gate) * up;
-// TL: tiled codes and meta
-template <bool SILU, bool TL>
+// TL: tiled codes and meta; HALF: m <= 8 (one MFMA per tile and step)
+template <bool SILU, bool TL, bool HALF>
 __global__ __launch_bounds__(64) void gemm_w4_kernel(const uint8_t* __restrict__ codes,
                                                      const uint16_t* __restrict__ meta, int64_t n, int K,
                                                      const uint16_t* __restrict__ x, int m, uint16_t* y,
@@ -89,7 +93,11 @@ __global__ __launch_bounds__(64) void gemm_w4_kernel(const uint8_t* __restrict__
   uint32_t magic = 0x43004300u;
   asm volatile("" : "+v"(magic));
   const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 pairs
-  const int xbase = r < m ? r * K * 2 : kOutside;
+  // HALF: A row r is position r & 7 of the first group (r < 8: lanes g < 2)
+  // or of the second (r >= 8: lanes g >= 2); other lanes read zeros
+  const int xpos = HALF ? (r & 7) : r;
+  const bool xreal = HALF ? (xpos < m && (r < 8) == (g < 2)) : r < m;
+  const int xbase = xreal ? xpos * K * 2 : kOutside;
 
   // the loads of chunk c (zeros past the block's range)
   auto load_chunk = [&](int c, Slot& sl) {
@@ -115,7 +123,42 @@ __global__ __launch_bounds__(64) void gemm_w4_kernel(const uint8_t* __restrict__
 #pragma unroll
   for (int t = 0; t < RT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const bool first = g < 2;  // this lane's k lie in the chunk's first group
+  auto compute_half = [&](const Slot& sl) {
+    const f32x4_t zf = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t sx = zf, d[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) d[t] = zf;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const u32x4 v = sl.xv[st];  // (x0,x1) (x2,x3) (x4,x5) (x6,x7) -> (x0,x4) (x1,x5) (x2,x6) (x3,x7)
+      const bf16x8_t a = __builtin_bit_cast(
+          bf16x8_t, u32x4{(v.x & 0xffffu) | (v.z << 16), (v.x >> 16) | (v.z & 0xffff0000u),
+                          (v.y & 0xffffu) | (v.w << 16), (v.y >> 16) | (v.w & 0xffff0000u)});
+      sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, ones), sx, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const uint32_t cw = sl.pc[t][st];
+        const bf16x8_t av = __builtin_bit_cast(
+            bf16x8_t, u32x4{(cw & mask) | magic, ((cw >> 4) & mask) | magic, ((cw >> 8) & mask) | magic,
+                            ((cw >> 12) & mask) | magic});
+        d[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, av, d[t], 0, 0, 0);
+      }
+    }
+    // lane (r, g) holds D rows 4 g .. 4 g + 3: its own group's sums
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const uint32_t mw = first ? sl.mt[t].x : sl.mt[t].y;
+      const float sc = ss::h2f((uint16_t)(mw & 0xffffu)), mn = ss::h2f((uint16_t)(mw >> 16));
+      const float c0 = mn - 128.0f * sc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[t][i] += sc * d[t][i] + c0 * sx[i];
+    }
+  };
   auto compute = [&](const Slot& sl) {
+    if constexpr (HALF) {
+      compute_half(sl);
+      return;
+    }
     const f32x4_t zf = {0.f, 0.f, 0.f, 0.f};
     f32x4_t s0 = zf, s1 = zf, d0[RT], d1[RT];
 #pragma unroll
@@ -170,7 +213,13 @@ __global__ __launch_bounds__(64) void gemm_w4_kernel(const uint8_t* __restrict__
   for (int j = 0; j < WD - 1; ++j)
     if (c + j < c1) step(c + j, j);
 
-  // lane holds positions 4 g + i of row r of each tile
+  if constexpr (HALF) {  // the second group's half of position 4 g + i sits 32 lanes away
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[t][i] += __shfl_xor(acc[t][i], 32, SS_WAVE);
+  }
+  // lane holds positions 4 g + i of row r of each tile (HALF: lanes g < 2)
   if constexpr (SILU) {
     // act[pos][j] = SiLU(gate) * up, both rounded to bf16 first (as the
     // unfused gate/up store and SiLU kernel do)
@@ -215,19 +264,37 @@ int gemm_w4_splits(int64_t n, int64_t k) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(chunks, (kTargetBlocks + groups - 1) / groups));
 }
 
+namespace {
+
+template <bool SILU, bool TL, bool HALF>
+hipError_t launch_k(dim3 grid, const uint8_t* codes, const uint16_t* meta, int64_t n, int64_t k, const uint16_t* x,
+                    int m, uint16_t* y, float* part, int splits, int to_part, int64_t silu_f, hipStream_t s) {
+  SS_LAUNCH((gemm_w4_kernel<SILU, TL, HALF>), grid, dim3(64), 0, s, codes, meta, n, (int)k, x, m, y, part, splits,
+            to_part, silu_f);
+  return hipGetLastError();
+}
+
+template <bool SILU>
+hipError_t launch_sel(bool tiled, dim3 grid, const uint8_t* codes, const uint16_t* meta, int64_t n, int64_t k,
+                      const uint16_t* x, int m, uint16_t* y, float* part, int splits, int to_part, int64_t silu_f,
+                      hipStream_t s) {
+  if (tiled) {
+    if (m <= 8) return launch_k<SILU, true, true>(grid, codes, meta, n, k, x, m, y, part, splits, to_part, silu_f, s);
+    return launch_k<SILU, true, false>(grid, codes, meta, n, k, x, m, y, part, splits, to_part, silu_f, s);
+  }
+  if (m <= 8) return launch_k<SILU, false, true>(grid, codes, meta, n, k, x, m, y, part, splits, to_part, silu_f, s);
+  return launch_k<SILU, false, false>(grid, codes, meta, n, k, x, m, y, part, splits, to_part, silu_f, s);
+}
+
+}  // namespace
+
 hipError_t launch_gemm_w4(const uint8_t* codes, const uint16_t* meta, int64_t n, int64_t k, const uint16_t* x, int m,
                           uint16_t* y, float* part, hipStream_t s, int* splits_out, bool tiled) {
   const int splits = gemm_w4_splits(n, k);
   const int to_part = splits_out != nullptr;
   if (to_part) *splits_out = splits;
-  const dim3 grid((unsigned)((n + 16 * RT - 1) / (16 * RT)), (unsigned)splits), block(64);
-  if (tiled)
-    SS_LAUNCH((gemm_w4_kernel<false, true>), grid, block, 0, s, codes, meta, n, (int)k, x, m, y, part, splits, to_part,
-              (int64_t)0);
-  else
-    SS_LAUNCH((gemm_w4_kernel<false, false>), grid, block, 0, s, codes, meta, n, (int)k, x, m, y, part, splits,
-              to_part, (int64_t)0);
-  hipError_t e = hipGetLastError();
+  const dim3 grid((unsigned)((n + 16 * RT - 1) / (16 * RT)), (unsigned)splits);
+  hipError_t e = launch_sel<false>(tiled, grid, codes, meta, n, k, x, m, y, part, splits, to_part, 0, s);
   if (e != hipSuccess || splits == 1 || to_part) return e;
   return launch_gemm_reduce(part, splits, m, n, y, n, s);
 }
@@ -235,12 +302,6 @@ hipError_t launch_gemm_w4(const uint8_t* codes, const uint16_t* meta, int64_t n,
 hipError_t launch_gemm_w4_silu(const uint8_t* codes, const uint16_t* meta, int64_t F, int64_t k, const uint16_t* x,
                                int m, uint16_t* act, hipStream_t s, bool tiled) {
   if (gemm_w4_splits(2 * F, k) != 1) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((F + 8 * RT - 1) / (8 * RT))), block(64);
-  if (tiled)
-    SS_LAUNCH((gemm_w4_kernel<true, true>), grid, block, 0, s, codes, meta, 2 * F, (int)k, x, m, act,
-              (float*)nullptr, 1, 0, F);
-  else
-    SS_LAUNCH((gemm_w4_kernel<true, false>), grid, block, 0, s, codes, meta, 2 * F, (int)k, x, m, act,
-              (float*)nullptr, 1, 0, F);
-  return hipGetLastError();
+  const dim3 grid((unsigned)((F + 8 * RT - 1) / (8 * RT)));
+  return launch_sel<true>(tiled, grid, codes, meta, 2 * F, k, x, m, act, (float*)nullptr, 1, 0, F, s);
 }
