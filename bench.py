@@ -568,7 +568,7 @@ def isolated_gemvs(dm, shape, dev, reps=3, only=None, graph=True):
             r = rows_per_wave(n_out, epi == 2, w4)
             if lay:  # the tiled 4-bit GEMV: <tiles, chunks in flight, x items per thread, prologue, epilogue>
                 nx = next(v for v in (1, 2, 3, 5, 7) if v * 8 * 512 >= k)
-                tp = "1,4" if epi == 1 else "2,2"
+                tp = "1,4" if epi == 1 else ("2,3" if epi == 0 else "2,2")
                 symbol = f"gemv_w4t_kernel<{tp},{nx},{1 if norm else 0},{epi}>"
             else:
                 symbol = sym.format(r=r, w="4" if w4 else "16")

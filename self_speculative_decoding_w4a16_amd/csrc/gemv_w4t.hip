@@ -18,8 +18,8 @@
 //    second's, each scaled by its own group's scale and min:
 //        sum_k (q s + m) x = s * (sum_k (128 + q) x - 128 X) + m X,
 //    X = sum_k x over the group (from LDS).  Four MFMAs per KiB of codes
-//    replace the 64 v_dot2 of the VALU GEMV; the nibble extraction (7 VALU
-//    per code word) stays.
+//    replace the VALU GEMV's 16 v_dot2 per KiB and most of its per-chunk
+//    scale work; the nibble extraction (7 VALU per code word) stays.
 //  * A block of 8 waves takes units of T tiles (T = 2: a gate tile and its
 //    up tile for SiLU * up), persistent over the units; its waves split each
 //    unit's chunks (wave w: chunks w, w + 8, ...) and keep P chunks in flight
@@ -336,12 +336,15 @@ hipError_t launch_t(const GemvArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Store and SiLU sites take two tiles a unit (one x read per two MFMAs) with
-// two chunks in flight; residual sites (the narrow O and down projections)
-// one tile with four chunks in flight (more waves per row of tiles).
+// Store and SiLU sites take two tiles a unit (one x read per two MFMAs),
+// with three chunks in flight (store: the narrow QKV projection, 5.6 against
+// 5.8 us for two and 6.1 for four at the 7B shape) or two (SiLU: gate/up);
+// residual sites (the narrow O and down projections) one tile with four
+// chunks in flight (more waves per row of tiles).
 template <int NX, int PRO, int EPI>
 hipError_t launch_pe(const GemvArgs& a, hipStream_t s) {
   if constexpr (EPI == EPI_RESID) return launch_t<1, 4, NX, PRO, EPI>(a, s);
+  else if constexpr (EPI == EPI_STORE) return launch_t<2, 3, NX, PRO, EPI>(a, s);
   else return launch_t<2, 2, NX, PRO, EPI>(a, s);
 }
 

@@ -158,3 +158,33 @@ def test_tiled_w4_gemm_equals_rows(cuda, n, k, m):
     _lib.w4_gemm(_lib.linear(codes=tc, meta=tm, layout=1), x, y1, ws)
     torch.cuda.synchronize()
     assert torch.equal(y0, y1)
+
+
+@pytest.mark.parametrize("tiled", [True, False])
+def test_draft_step_on_either_layout_matches_oracle(cuda, tiled):
+    """One 7B-shaped substitute layer (layer 0: the embedding prologue on the
+    4-bit QKV site) through a draft step with the substitutes tiled or
+    row-major: logits within 1e-2 of the oracle either way."""
+    from oracle.model import forward
+    from self_speculative_decoding_w4a16_amd.engine import SpecDecoder
+    from self_speculative_decoding_w4a16_amd.model import DeviceModel
+    from synth import kv_history, model_weights, token_ids
+    from synth.configs import QWEN7B
+    from tests.helpers import oracle_model
+    shape, kv_len, cap = QWEN7B.with_(n_layers=1, n_shared=0), 700, 768
+    log(f"draft step, substitutes tiled={tiled}")
+    w = model_weights(shape, 9, cuda)
+    dm = DeviceModel(shape, w, tiled=tiled)
+    assert all(v == int(tiled) for v in dm.layout[0].values())
+    dec = SpecDecoder(dm, cap, 4)
+    K, V = kv_history(shape.n_layers, shape.n_kv_heads, kv_len, shape.head_dim, cap, 16, cuda)
+    dec.k_cache.copy_(K)
+    dec.v_cache.copy_(V)
+    tok = int(token_ids(1, shape.vocab, 12)[0])
+    dec.reset(kv_len, tok)
+    _lib.draft_step(dm.c, dec.c, 0, 0.0, None, dec.ws)
+    torch.cuda.synchronize()
+    om = oracle_model(shape, w, dm.substitute_layers)
+    kv = (host(K).astype(np.float64), host(V).astype(np.float64))
+    ref = forward(om, kv, kv_len, [tok], draft=True)[0]
+    assert rel_err(host(dec.draft_logits[0]), ref) < TOL
