@@ -566,10 +566,10 @@ def isolated_gemvs(dm, shape, dev, reps=3, only=None, graph=True):
             us = timed(lins, k, n_out, norm, epi)
             del copies, lins
             r = rows_per_wave(n_out, epi == 2, w4)
-            if lay:  # the tiled 4-bit GEMV: <tiles, chunks in flight, x items per thread, prologue, epilogue>
+            if lay:  # the tiled GEMV: <width, tiles, chunks in flight, x items per thread, prologue, epilogue>
                 nx = next(v for v in (1, 2, 3, 5, 7) if v * 8 * 512 >= k)
                 tp = "1,4" if epi == 1 else ("2,3" if epi == 0 else "2,2")
-                symbol = f"gemv_w4t_kernel<{tp},{nx},{1 if norm else 0},{epi}>"
+                symbol = f"gemv_w4t_kernel<4,{tp},{nx},{1 if norm else 0},{epi}>"
             else:
                 symbol = sym.format(r=r, w="4" if w4 else "16")
             out[f"{kind}_{site}"] = {"avg_us": round(us, 3), "bytes_per_launch": round(by),

@@ -87,10 +87,12 @@ const char *subspec_last_error(void);
  *          at 3), meta = fp16 [n][k/64][2] = {scale, min} of each 64-group
  *          along k; the weight is q * scale + min; w = NULL.
  *   bits:  4, 3 or 2 for the low-bit form (0 reads as 4); ignored for bf16.
- *   layout: 0 for the row-major codes and meta above; 1 for 4-bit codes and
- *          meta in the 16-row tiles of subspec_w4_tile (bits 4, n % 16 == 0,
- *          k % 128 == 0, k <= 28672; the draft step's GEMV then runs on the
- *          matrix cores).  Ignored for bf16. */
+ *   layout: 0 for the row-major codes and meta above; 1 for 4- or 2-bit
+ *          codes and meta in the 16-row tiles of subspec_tile_codes (n % 16
+ *          == 0, k % 128 == 0 at 4 bits and k % 256 == 0 at 2, k <= 28672;
+ *          the draft step's GEMV then runs on the matrix cores; the skinny
+ *          GEMM of subspec_w4_gemm and the row paths take 4 bits only).
+ *          Ignored for bf16. */
 typedef struct {
   const uint16_t *w;
   const uint8_t *codes;
@@ -206,22 +208,25 @@ int subspec_workspace_init(void *ws, size_t ws_bytes, void *stream);
 int subspec_quantize(const uint16_t *w, int64_t n, int64_t k, int32_t group, int32_t bits,
                      uint8_t *codes, uint16_t *meta, void *stream);
 
-/* The same 4-bit codes and meta in 16-row tiles (subspec_linear.layout = 1),
- * the storage order of the batch-1 draft GEMV on the matrix cores: a
- * storage choice of this library, not of the method (the substitute is the
- * [SSR] section 2.2 quantisation either way; the values are moved, not
- * changed).  For tile t (rows 16t .. 16t + 15) and chunk c (k = 128c ..
- * 128c + 127), with c_n = k / 128 chunks a row and b = (t c_n + c):
- *   tcodes[1024 b + 16 (16 g + r) + j] = codes[(16t + r) k/2 + 64 c + 16 g + j]
- *       for r < 16, g < 4, j < 16;
- *   tmeta dword 32 b + 2 r + e = meta dword (16t + r) k/64 + 2 c + e, e < 2
+/* The same 4- or 2-bit codes and meta in 16-row tiles
+ * (subspec_linear.layout = 1), the storage order of the batch-1 draft GEMV
+ * on the matrix cores: a storage choice of this library, not of the method
+ * (the substitute is the [SSR] section 2.2 / [SSN] low-bit quantisation
+ * either way; the values are moved, not changed).  A chunk is 64 bytes of a
+ * row: c_k = 512 / bits weights (128 at 4 bits, 256 at 2), e = 8 / bits
+ * 64-groups.  For tile t (rows 16t .. 16t + 15) and chunk c, with c_n =
+ * k / c_k chunks a row and b = (t c_n + c):
+ *   tcodes[1024 b + 16 (16 g + r) + j] = codes[(16t + r) R + 64 c + 16 g + j]
+ *       for r < 16, g < 4, j < 16, R = k bits / 8 code bytes a row;
+ *   tmeta dword 16 e b + e r + f = meta dword (16t + r) k/64 + e c + f, f < e
  *       (meta dword = {scale, min} of one 64-group).
- * codes, meta: the subspec_quantize output at bits 4 (device; not
- * modified); tcodes (n k/2 bytes), tmeta (n k/64 dwords): device outputs
+ * codes, meta: the subspec_quantize output at `bits` = 4 or 2 (device; not
+ * modified); tcodes (n R bytes), tmeta (n k/64 dwords): device outputs
  * owned by the caller, not overlapping the inputs.  n % 16 == 0 and
- * k % 128 == 0 (SUBSPEC_ESHAPE otherwise); NULL pointers: SUBSPEC_EINVAL. */
-int subspec_w4_tile(const uint8_t *codes, const uint16_t *meta, int64_t n, int64_t k, uint8_t *tcodes,
-                    uint16_t *tmeta, void *stream);
+ * k % c_k == 0 (SUBSPEC_ESHAPE otherwise); other widths:
+ * SUBSPEC_EUNSUPPORTED; NULL pointers: SUBSPEC_EINVAL. */
+int subspec_tile_codes(const uint8_t *codes, const uint16_t *meta, int64_t n, int64_t k, int32_t bits,
+                       uint8_t *tcodes, uint16_t *tmeta, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* The speculative cycle  ([SD] pseudo-code)                                 */

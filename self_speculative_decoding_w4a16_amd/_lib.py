@@ -76,7 +76,8 @@ _SIGS = {
     "subspec_workspace_init": (c_int32, [c_void_p, c_size_t, c_void_p]),
     "subspec_quantize": (c_int32, [c_void_p, c_int64, c_int64, c_int32, c_int32, c_void_p,
                                    c_void_p, c_void_p]),
-    "subspec_w4_tile": (c_int32, [c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
+    "subspec_tile_codes": (c_int32, [c_void_p, c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p,
+                                     c_void_p]),
     "subspec_draft_step": (c_int32, [POINTER(Model), POINTER(State), c_int32, c_float, c_void_p,
                                      c_void_p, c_size_t, c_void_p]),
     "subspec_verify": (c_int32, [POINTER(Model), POINTER(State), c_int32, c_void_p, c_void_p,
@@ -220,11 +221,11 @@ def quantize(w, codes, meta, group=64, bits=4, stream=None):
     check(lib().subspec_quantize(_p(w), n, k, group, bits, _p(codes), _p(meta), _stream(stream)))
 
 
-def w4_tile(codes, meta, tcodes, tmeta, stream=None):
-    """4-bit codes [n][k/2] + meta [n][k/64][2] -> the 16-row tiles of
-    subspec_w4_tile (same sizes)."""
-    n, k = codes.shape[0], 2 * codes.shape[1]
-    check(lib().subspec_w4_tile(_p(codes), _p(meta), n, k, _p(tcodes), _p(tmeta), _stream(stream)))
+def tile_codes(codes, meta, tcodes, tmeta, bits=4, stream=None):
+    """4- or 2-bit codes [n][k bits/8] + meta [n][k/64][2] -> the 16-row tiles
+    of subspec_tile_codes (same sizes)."""
+    n, k = codes.shape[0], 64 * meta.shape[1]
+    check(lib().subspec_tile_codes(_p(codes), _p(meta), n, k, bits, _p(tcodes), _p(tmeta), _stream(stream)))
 
 
 def draft_step(model, state, step, draft_temp, u_codes, ws, stream=None):
@@ -342,7 +343,7 @@ def hbm_read(buf, sink, stream=None):
 def linear(w=None, codes=None, meta=None, n=None, k=None, bits=4, layout=0):
     """A subspec_linear for bf16 weights w [n][k], or low-bit codes + meta
     [n][k/64][2] at ``bits`` = 4, 3 or 2 (k from meta when not given);
-    ``layout`` 1: 4-bit codes + meta in the tiles of w4_tile."""
+    ``layout`` 1: codes + meta in the tiles of tile_codes."""
     if w is not None:
         n, k = w.shape
         return Linear(_p(w), None, None, n, k, 0, 0)

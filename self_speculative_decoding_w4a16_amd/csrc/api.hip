@@ -96,16 +96,18 @@ int lin_bits(const subspec_linear& l) { return lin_is_w4(l) ? (l.bits == 0 ? 4 :
 // bytes of one row of codes
 double code_row_bytes(int bits, double k) { return bits == 4 ? k / 2 : (bits == 2 ? k / 4 : 3 * k / 8); }
 
-// layout 1 (16-row tiles of subspec_w4_tile): 4-bit only, n % 16 == 0,
-// k % 128 == 0, k within the tiled GEMV's prologue (kMaxTiledK)
+// layout 1 (16-row tiles of subspec_tile_codes): 4- or 2-bit codes, n % 16 == 0,
+// k a multiple of the width's chunk (128 or 256), k within the tiled GEMV's
+// prologue (kMaxTiledK)
 constexpr int64_t kMaxTiledK = 28672;
 int check_layout(const subspec_linear& l, const char* what, int layer) {
   if (lin_is_bf16(l) || l.layout == 0) return SUBSPEC_OK;
   if (l.layout != 1) return fail(SUBSPEC_EINVAL, "layer %d %s: layout must be 0 or 1", layer, what);
-  if (lin_bits(l) != 4) return fail(SUBSPEC_EINVAL, "layer %d %s: layout 1 needs 4-bit codes", layer, what);
-  if (l.n % 16 != 0 || l.k % 128 != 0 || l.k > kMaxTiledK)
-    return fail(SUBSPEC_ESHAPE, "layer %d %s: layout 1 needs n %% 16 == 0, k %% 128 == 0 and k <= %lld", layer,
-                what, (long long)kMaxTiledK);
+  const int kch = tile_chunk_k(lin_bits(l));
+  if (kch == 0) return fail(SUBSPEC_EINVAL, "layer %d %s: layout 1 needs 4- or 2-bit codes", layer, what);
+  if (l.n % 16 != 0 || l.k % kch != 0 || l.k > kMaxTiledK)
+    return fail(SUBSPEC_ESHAPE, "layer %d %s: layout 1 needs n %% 16 == 0, k %% %d == 0 and k <= %lld", layer, what,
+                kch, (long long)kMaxTiledK);
   return SUBSPEC_OK;
 }
 
@@ -586,12 +588,14 @@ int subspec_quantize(const uint16_t* w, int64_t n, int64_t k, int32_t group, int
   return ok();
 }
 
-int subspec_w4_tile(const uint8_t* codes, const uint16_t* meta, int64_t n, int64_t k, uint8_t* tcodes,
-                    uint16_t* tmeta, void* stream) {
+int subspec_tile_codes(const uint8_t* codes, const uint16_t* meta, int64_t n, int64_t k, int32_t bits,
+                       uint8_t* tcodes, uint16_t* tmeta, void* stream) {
   if (!codes || !meta || !tcodes || !tmeta) return fail(SUBSPEC_EINVAL, "codes, meta, tcodes and tmeta must be set");
   if (n < 1 || k < 1) return fail(SUBSPEC_EINVAL, "n and k must be positive");
-  if (n % 16 != 0 || k % 128 != 0) return fail(SUBSPEC_ESHAPE, "n %% 16 == 0 and k %% 128 == 0 needed");
-  HIPCHK(launch_w4_tile(codes, meta, n, k, tcodes, tmeta, hs(stream)));
+  const int kch = tile_chunk_k(bits);
+  if (kch == 0) return fail(SUBSPEC_EUNSUPPORTED, "bits must be 4 or 2");
+  if (n % 16 != 0 || k % kch != 0) return fail(SUBSPEC_ESHAPE, "n %% 16 == 0 and k %% %d == 0 needed", kch);
+  HIPCHK(launch_tile_codes(codes, meta, n, k, bits, tcodes, tmeta, hs(stream)));
   return ok();
 }
 

@@ -41,7 +41,7 @@
 //    (fp32 partials, summed in split order by a second launch or by the
 //    caller's consumer).
 //  * Codes and meta row-major (subspec_quantize) or in 16-row tiles
-//    (subspec_w4_tile): the lane reads the same 16 bytes and scale/min pair
+//    (subspec_tile_codes): the lane reads the same 16 bytes and scale/min pair
 //    either way, from one contiguous KiB per tile and chunk in the tiled
 //    layout.
 #include "common.h"

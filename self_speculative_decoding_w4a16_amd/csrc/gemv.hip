@@ -762,9 +762,9 @@ int gemv_max_blocks(bool w4, int64_t n, int epi) {
 
 hipError_t launch_gemv(int wb, int pro, int epi, const GemvArgs& a, hipStream_t s, int* blocks_out) {
   if (a.tiled) {
-    if (wb != 4 || !gemv_w4t_supported(pro, epi)) return hipErrorInvalidValue;
+    if ((wb != 4 && wb != 2) || !gemv_w4t_supported(pro, epi)) return hipErrorInvalidValue;
     if (blocks_out) *blocks_out = 0;
-    return launch_gemv_w4t(pro, epi, a, s);
+    return launch_gemv_w4t(wb, pro, epi, a, s);
   }
   const int R = pick_r(a.n, epi);
   switch (wb) {

@@ -1,33 +1,36 @@
-// Batch-1 GEMV of the draft step on 4-bit substitute weights stored in
+// Batch-1 GEMV of the draft step on 4- or 2-bit substitute weights stored in
 // 16-row tiles, on the matrix cores.  Low-batch decode streams the weights
 // from memory ("How speculative decoding makes LLMs go brrr", Module 2), so
 // the layout and the kernel are built around the weight stream:
 //
-//  * Tiled layout (subspec_w4_tile): the codes of rows 16 tau .. 16 tau + 15
-//    and k-chunk c (k = 128 c .. 128 c + 127, two 64-groups) are one
-//    contiguous KiB, the 16 bytes of lane l = 16 g + r at 16 l holding bytes
-//    64 c + 16 g .. + 15 of row 16 tau + r; the scale/min dwords of those rows
-//    and groups follow the same order (8 bytes per row: groups 2c, 2c + 1).
-//    Every wave load then reads one contiguous KiB, where the row-major
-//    layout needs 16 pieces of 64 bytes from 16 rows.
-//  * v_mfma_f32_16x16x32_bf16 with B = 32 k x 16 tile rows as (128 + q)
-//    bf16 values (one and-or per nibble pair, exact) and A = the activations
-//    in two rows: row 0 holds x on the lanes of the chunk's first 64-group
-//    (g = 0, 1), row 8 on those of its second (g = 2, 3), every other A value
-//    is 0.  So D row 0 is the first group's sum per tile row and D row 8 the
-//    second's, each scaled by its own group's scale and min:
+//  * Tiled layout (subspec_tile_codes): a chunk is 64 bytes of a row (128 k
+//    at 4 bits, two 64-groups; 256 k at 2 bits, four groups); the codes of
+//    rows 16 tau .. 16 tau + 15 and chunk c are one contiguous KiB, the 16
+//    bytes of lane l = 16 g + r at 16 l holding bytes 64 c + 16 g .. + 15 of
+//    row 16 tau + r; the scale/min dwords of those rows and groups follow in
+//    row order.  Every wave load then reads one contiguous KiB, where the
+//    row-major layout needs 16 pieces of 64 bytes from 16 rows.
+//  * v_mfma_f32_16x16x32_bf16 with B = 32 k x 16 tile rows as (128 + q) bf16
+//    values (one and-or per field pair, exact) and A = the activations on
+//    the lanes of one group per A row, every other A value 0: at 4 bits row
+//    0 holds x on the lanes of the chunk's first group (g = 0, 1) and row 8
+//    on its second's (g = 2, 3); at 2 bits row 4 g holds x on the lanes of
+//    group g.  So each D row holds one group's sums per tile row, scaled by
+//    that group's own scale and min:
 //        sum_k (q s + m) x = s * (sum_k (128 + q) x - 128 X) + m X,
-//    X = sum_k x over the group (from LDS).  Four MFMAs per KiB of codes
-//    replace the VALU GEMV's 16 v_dot2 per KiB and most of its per-chunk
-//    scale work; the nibble extraction (7 VALU per code word) stays.
+//    X = sum_k x over the group (from LDS).  Four MFMAs per KiB of 4-bit
+//    codes (eight at 2 bits) replace the VALU GEMV's v_dot2 and most of its
+//    per-chunk scale work; the field extraction (7 VALU per 4-bit code word,
+//    15 per 2-bit word) stays.
 //  * A block of 8 waves takes units of T tiles (T = 2: a gate tile and its
 //    up tile for SiLU * up), persistent over the units; its waves split each
 //    unit's chunks (wave w: chunks w, w + 8, ...) and keep P chunks in flight
 //    in register slots named statically, the ring running on across units.
 //    Each unit's wave partials meet in LDS (double-buffered, one barrier a
 //    unit).
-//  * x lives in LDS for the whole block in (x[k], x[k+4]) pair order, with
-//    its 64-group sums; the RMSNorm (and for layer 0 the embedding gather) is
+//  * x lives in LDS for the whole block in the pair order of the field
+//    extraction ((x[k], x[k+4]) at 4 bits, (x[k], x[k+8]) at 2), with its
+//    64-group sums; the RMSNorm (and for layer 0 the embedding gather) is
 //    computed in the prologue of every block, its loads issued before the
 //    first chunks so that their wait covers no weight load.
 #include "common.h"
@@ -40,6 +43,9 @@ constexpr int kW = 8;  // waves per block
 constexpr int kNT = kW * SS_WAVE;
 constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 (CDNA): raw 32-bit data
 constexpr int kOutside = 0x40000000;      // offset past every resource: loads zeros
+// zeros in LDS for the A operand of the lanes that carry no x: one 16-byte
+// slot per MFMA step of a chunk (up to 8 steps, at 2 bits)
+constexpr int kZero = 128;
 
 // offset, or one past every resource; kept in a register so the compiler
 // issues the load unconditionally instead of branching around it
@@ -49,23 +55,35 @@ __device__ __forceinline__ int sel_off(bool in, int off) {
   return o;
 }
 
+// Per code width WB (4 or 2 bits): k per 64-byte piece of a row (one
+// chunk), 64-groups per chunk, MFMA steps per chunk (one per 8 weights of a
+// lane's 16 code bytes), the field mask of one (128 + q) bf16 pair.
+template <int WB>
+struct Width {
+  static constexpr int KCH = 512 / WB;
+  static constexpr int GPC = 8 / WB;
+  static constexpr int NST = 16 / WB;
+  static constexpr uint32_t MASK = WB == 4 ? 0x000F000Fu : 0x00030003u;
+};
+
 template <int T>
 struct TSlot {
   u32x4 pc[T];     // 16 code bytes of the chunk, lane (r, g), each tile
   uint32_t mt[T];  // scale/min of the lane's group, row r, each tile
 };
 
-// T tiles per unit, P chunks in flight per wave, NX prologue items (8 values
-// of x) per thread: K <= 8 * kNT * NX.
-template <int T, int P, int NX, int PRO, int EPI>
+// WB-bit codes, T tiles per unit, P chunks in flight per wave, NX prologue
+// items (8 values of x) per thread: K <= 8 * kNT * NX.
+template <int WB, int T, int P, int NX, int PRO, int EPI>
 __global__ __launch_bounds__(kNT) void gemv_w4t_kernel(GemvArgs a, int G) {
+  using Wd = Width<WB>;
   extern __shared__ __align__(16) unsigned char smem[];
   const int K = (int)a.k;
-  const int chunks = K / 128;
-  u32x4* xs = reinterpret_cast<u32x4*>(smem);           // K/8 octets in pair order
+  const int chunks = K / Wd::KCH;
+  u32x4* xs = reinterpret_cast<u32x4*>(smem);           // K/8 16-byte slots of x pairs
   float* Xs = reinterpret_cast<float*>(smem + 2 * K);   // K/64 group sums
-  const int zoff = 2 * K + 4 * (K / 64);                 // 64 bytes of zeros
-  float* red = reinterpret_cast<float*>(smem + zoff + 64);  // [2][kW][16 T]
+  const int zoff = 2 * K + 4 * (K / 64);                 // kZero bytes of zeros
+  float* red = reinterpret_cast<float*>(smem + zoff + kZero);  // [2][kW][16 T]
   float* nred = red + 2 * kW * 16 * T;                    // [kW]
 
   const int vflag = a.valid ? *a.valid : 1;
@@ -78,8 +96,8 @@ __global__ __launch_bounds__(kNT) void gemv_w4t_kernel(GemvArgs a, int G) {
   const int ntl = b < units ? (units - b + G - 1) / G : 0;
   const int nc = (chunks - w + kW - 1) / kW;  // chunks >= 8 (K >= 1024) or waves past them idle
   const int F = ntl * (nc > 0 ? nc : 0);
-  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.codes), 0,
-                                                                       (int)(n_phys * (K / 2)), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.codes), 0, (int)(n_phys * (K / (8 / WB))), kBufferWord3);
   const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.meta), 0,
                                                                        (int)(n_phys * (K / 16)), kBufferWord3);
   // first row of tile t of unit index jj of this block
@@ -115,7 +133,10 @@ __global__ __launch_bounds__(kNT) void gemv_w4t_kernel(GemvArgs a, int G) {
       const bool ok = in && row < n_phys;
       const int tb = (int)(row >> 4) * chunks + c;  // tile-chunk KiB index
       sl.pc[t] = __builtin_amdgcn_raw_buffer_load_b128(crs, sel_off(ok, tb * 1024 + 16 * lane), 0, 0);
-      sl.mt[t] = __builtin_amdgcn_raw_buffer_load_b32(mrs, sel_off(ok, tb * 128 + 8 * r + 4 * (g >> 1)), 0, 0);
+      // the lane's group: g >> 1 (4 bits, two groups a chunk) or g (2 bits, four)
+      const int e = WB == 4 ? (g >> 1) : g;
+      sl.mt[t] = __builtin_amdgcn_raw_buffer_load_b32(mrs, sel_off(ok, 4 * (tb * 16 * Wd::GPC + Wd::GPC * r + e)), 0,
+                                                      0);
     }
     ++lf;
     if (++li == nc) {
@@ -179,12 +200,25 @@ __global__ __launch_bounds__(kNT) void gemv_w4t_kernel(GemvArgs a, int G) {
     s += __shfl_xor(s, 1, SS_WAVE);
     s += __shfl_xor(s, 2, SS_WAVE);
     s += __shfl_xor(s, 4, SS_WAVE);
+    u32x4 slot;
+    if (WB == 4) {  // the pairs (x[k], x[k+4]) of the 8-weight word at 8 o
+      slot = u32x4{xb[0] | (xb[4] << 16), xb[1] | (xb[5] << 16), xb[2] | (xb[6] << 16), xb[3] | (xb[7] << 16)};
+    } else {
+      // 2 bits: the 16-weight word at 16 (o >> 1) spans items o & ~1 and
+      // o | 1 (neighbouring lanes); slot o holds its pairs (x[k], x[k+8]) of
+      // k = 4 (o & 1) .. + 3, the fields of MFMA step o & 1 of that word
+      uint32_t p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = (uint32_t)__shfl_xor((int)xb[i], 1, SS_WAVE);
+      slot = (o & 1) ? u32x4{p[4] | (xb[4] << 16), p[5] | (xb[5] << 16), p[6] | (xb[6] << 16), p[7] | (xb[7] << 16)}
+                     : u32x4{xb[0] | (p[0] << 16), xb[1] | (p[1] << 16), xb[2] | (p[2] << 16), xb[3] | (p[3] << 16)};
+    }
     if (ok) {
-      xs[o] = u32x4{xb[0] | (xb[4] << 16), xb[1] | (xb[5] << 16), xb[2] | (xb[6] << 16), xb[3] | (xb[7] << 16)};
+      xs[o] = slot;
       if ((o & 7) == 0) Xs[o >> 3] = s;
     }
   }
-  if (tid < 4) reinterpret_cast<u32x4*>(smem + zoff)[tid] = u32x4{0u, 0u, 0u, 0u};
+  if (tid < kZero / 16) reinterpret_cast<u32x4*>(smem + zoff)[tid] = u32x4{0u, 0u, 0u, 0u};
   // registers of items past the end of x were never read: a use here settles
   // their loads before the loop (else the first reuse waits for every load)
 #pragma unroll
@@ -206,11 +240,13 @@ __global__ __launch_bounds__(kNT) void gemv_w4t_kernel(GemvArgs a, int G) {
     return;
   }
 
-  // A operand: lanes (r 0, g 0-1) and (r 8, g 2-3) read x, the rest zeros
-  const bool real = (r == 0 && g < 2) || (r == 8 && g >= 2);
-  const uint32_t abase = real ? (uint32_t)(64 * g) : (uint32_t)zoff;
-  const uint32_t astride = real ? 256u : 0u;
-  const uint32_t mask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
+  // A operand: 4 bits - lanes (r 0, g 0-1) and (r 8, g 2-3) read x (the
+  // chunk's two groups in D rows 0 and 8); 2 bits - lanes r = 4 g (its four
+  // groups in D rows 0, 4, 8, 12); every other lane reads zeros
+  const bool real = WB == 4 ? ((r == 0 && g < 2) || (r == 8 && g >= 2)) : r == 4 * g;
+  const uint32_t abase = real ? (uint32_t)(WB == 4 ? 64 * g : 128 * g) : (uint32_t)zoff;
+  const uint32_t astride = real ? (uint32_t)(2 * Wd::KCH) : 0u;
+  const uint32_t mask = __builtin_amdgcn_readfirstlane(Wd::MASK);
   uint32_t magic = 0x43004300u;
   asm volatile("" : "+v"(magic));
 
@@ -220,23 +256,28 @@ __global__ __launch_bounds__(kNT) void gemv_w4t_kernel(GemvArgs a, int G) {
   int cjj = 0, ci = 0;  // compute cursor
   auto compute = [&](const TSlot<T>& s) {
     const int c = w + kW * ci;
-    const float xg = Xs[2 * c + (g >> 1)];
+    const float xg = Xs[Wd::GPC * c + (WB == 4 ? (g >> 1) : g)];
     const f32x4_t zf = {0.f, 0.f, 0.f, 0.f};
     f32x4_t d[T];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
+    for (int st = 0; st < Wd::NST; ++st) {
       const bf16x8_t av =
           __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4*>(smem + abase + astride * c + 16 * st));
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        const uint32_t cw = s.pc[t][st];
+        // 4 bits: code word st, pairs (q_i, q_i+4) at bits 4 i, 16 + 4 i;
+        // 2 bits: code word st / 2, pairs (q_e, q_e+8) at bits 2 e, 16 + 2 e
+        // for e = 4 (st & 1) + i
+        const uint32_t cw = s.pc[t][WB == 4 ? st : st >> 1];
+        const int sh0 = WB == 4 ? 0 : 8 * (st & 1), sh = WB == 4 ? 4 : 2;
         const bf16x8_t bv = __builtin_bit_cast(
-            bf16x8_t, u32x4{(cw & mask) | magic, ((cw >> 4) & mask) | magic, ((cw >> 8) & mask) | magic,
-                            ((cw >> 12) & mask) | magic});
+            bf16x8_t, u32x4{((cw >> sh0) & mask) | magic, ((cw >> (sh0 + sh)) & mask) | magic,
+                            ((cw >> (sh0 + 2 * sh)) & mask) | magic, ((cw >> (sh0 + 3 * sh)) & mask) | magic});
         d[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, st == 0 ? zf : d[t], 0, 0, 0);
       }
     }
-    // D row 0 (lanes g = 0) and row 8 (g = 2) sit in component 0
+    // the lane's own group sums sit in component 0 (D row 4 g); for 4 bits
+    // only lanes g = 0 and 2 hold one (rows 0 and 8)
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const float sc = ss::h2f((uint16_t)(s.mt[t] & 0xffffu)), mn = ss::h2f((uint16_t)(s.mt[t] >> 16));
@@ -246,7 +287,9 @@ __global__ __launch_bounds__(kNT) void gemv_w4t_kernel(GemvArgs a, int G) {
       float* rb = red + (cjj & 1) * kW * 16 * T;
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        const float v = acc[t] + __shfl_xor(acc[t], 32, SS_WAVE);  // first group + second group
+        float v = acc[t];  // the groups of the chunk, summed into lanes g = 0
+        if (WB == 2) v += __shfl_xor(v, 16, SS_WAVE);
+        v += __shfl_xor(v, 32, SS_WAVE);
         if (g == 0) rb[w * 16 * T + 16 * t + r] = v;
         acc[t] = 0.0f;
       }
@@ -292,14 +335,15 @@ __global__ __launch_bounds__(kNT) void gemv_w4t_kernel(GemvArgs a, int G) {
     if (f + j < F) compute(sl[j]);
 }
 
-// Repack of row-major 4-bit codes and meta into 16-row tiles: thread i
-// writes the 16 code bytes and the 8 meta bytes of item i = (tile, chunk,
-// lane l = 16 g + r); the meta dwords go with the lanes g = 0, 1 (row r,
-// groups 2c and 2c + 1).
-__global__ __launch_bounds__(256) void w4_tile_kernel(const uint8_t* __restrict__ codes,
-                                                      const uint16_t* __restrict__ meta, int64_t n, int64_t k,
-                                                      uint8_t* __restrict__ tcodes, uint16_t* __restrict__ tmeta) {
-  const int64_t chunks = k / 128;
+// Repack of row-major BITS-bit codes and meta into 16-row tiles: thread i
+// writes the 16 code bytes of item i = (tile, chunk, lane l = 16 g + r) and,
+// for g < GPC (the chunk's groups), the meta dword of row r and group g.
+template <int BITS>
+__global__ __launch_bounds__(256) void tile_codes_kernel(const uint8_t* __restrict__ codes,
+                                                         const uint16_t* __restrict__ meta, int64_t n, int64_t k,
+                                                         uint8_t* __restrict__ tcodes, uint16_t* __restrict__ tmeta) {
+  using Wd = Width<BITS>;
+  const int64_t chunks = k / Wd::KCH;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (n / 16) * chunks * 64) return;
   const int l = (int)(i & 63), r = l & 15, g = l >> 4;
@@ -307,10 +351,10 @@ __global__ __launch_bounds__(256) void w4_tile_kernel(const uint8_t* __restrict_
   const int64_t tau = tc / chunks, c = tc - tau * chunks;
   const int64_t row = 16 * tau + r;
   *reinterpret_cast<u32x4*>(tcodes + tc * 1024 + 16 * l) =
-      *reinterpret_cast<const u32x4*>(codes + row * (k / 2) + 64 * c + 16 * g);
-  if (g < 2) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(meta) + row * (k / 64) + 2 * c + g;
-    reinterpret_cast<uint32_t*>(tmeta)[tc * 32 + 2 * r + g] = *src;
+      *reinterpret_cast<const u32x4*>(codes + row * (k / (8 / BITS)) + 64 * c + 16 * g);
+  if (g < Wd::GPC) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(meta) + row * (k / 64) + Wd::GPC * c + g;
+    reinterpret_cast<uint32_t*>(tmeta)[tc * 16 * Wd::GPC + Wd::GPC * r + g] = *src;
   }
 }
 
@@ -325,14 +369,14 @@ int w4t_cus() {
   return cus;
 }
 
-template <int T, int P, int NX, int PRO, int EPI>
+template <int WB, int T, int P, int NX, int PRO, int EPI>
 hipError_t launch_t(const GemvArgs& a, hipStream_t s) {
   const int K = (int)a.k;
-  const size_t lds = (size_t)(2 * K + 4 * (K / 64) + 64) + 4 * (2 * kW * 16 * T + kW);
+  const size_t lds = (size_t)(2 * K + 4 * (K / 64) + kZero) + 4 * (2 * kW * 16 * T + kW);
   const int units = EPI == EPI_SILU ? (int)(a.n / 16) : (int)((a.n + 16 * T - 1) / (16 * T));
   // two blocks per compute unit: 16 waves of at most 128 VGPRs
   const int G = std::max(1, std::min(units, 2 * w4t_cus()));
-  SS_LAUNCH((gemv_w4t_kernel<T, P, NX, PRO, EPI>), dim3((unsigned)G), dim3(kNT), lds, s, a, G);
+  SS_LAUNCH((gemv_w4t_kernel<WB, T, P, NX, PRO, EPI>), dim3((unsigned)G), dim3(kNT), lds, s, a, G);
   return hipGetLastError();
 }
 
@@ -341,21 +385,32 @@ hipError_t launch_t(const GemvArgs& a, hipStream_t s) {
 // 5.8 us for two and 6.1 for four at the 7B shape) or two (SiLU: gate/up);
 // residual sites (the narrow O and down projections) one tile with four
 // chunks in flight (more waves per row of tiles).
-template <int NX, int PRO, int EPI>
+template <int WB, int NX, int PRO, int EPI>
 hipError_t launch_pe(const GemvArgs& a, hipStream_t s) {
-  if constexpr (EPI == EPI_RESID) return launch_t<1, 4, NX, PRO, EPI>(a, s);
-  else if constexpr (EPI == EPI_STORE) return launch_t<2, 3, NX, PRO, EPI>(a, s);
-  else return launch_t<2, 2, NX, PRO, EPI>(a, s);
+  if constexpr (EPI == EPI_RESID) return launch_t<WB, 1, 4, NX, PRO, EPI>(a, s);
+  else if constexpr (EPI == EPI_STORE) return launch_t<WB, 2, 3, NX, PRO, EPI>(a, s);
+  else return launch_t<WB, 2, 2, NX, PRO, EPI>(a, s);
 }
 
-template <int NX>
+template <int WB, int NX>
 hipError_t launch_nx(int pro, int epi, const GemvArgs& a, hipStream_t s) {
-  if (pro == PRO_X && epi == EPI_STORE) return launch_pe<NX, PRO_X, EPI_STORE>(a, s);
-  if (pro == PRO_X && epi == EPI_RESID) return launch_pe<NX, PRO_X, EPI_RESID>(a, s);
-  if (pro == PRO_NORM && epi == EPI_STORE) return launch_pe<NX, PRO_NORM, EPI_STORE>(a, s);
-  if (pro == PRO_NORM && epi == EPI_SILU) return launch_pe<NX, PRO_NORM, EPI_SILU>(a, s);
-  if (pro == PRO_EMBED_NORM && epi == EPI_STORE) return launch_pe<NX, PRO_EMBED_NORM, EPI_STORE>(a, s);
+  if (pro == PRO_X && epi == EPI_STORE) return launch_pe<WB, NX, PRO_X, EPI_STORE>(a, s);
+  if (pro == PRO_X && epi == EPI_RESID) return launch_pe<WB, NX, PRO_X, EPI_RESID>(a, s);
+  if (pro == PRO_NORM && epi == EPI_STORE) return launch_pe<WB, NX, PRO_NORM, EPI_STORE>(a, s);
+  if (pro == PRO_NORM && epi == EPI_SILU) return launch_pe<WB, NX, PRO_NORM, EPI_SILU>(a, s);
+  if (pro == PRO_EMBED_NORM && epi == EPI_STORE) return launch_pe<WB, NX, PRO_EMBED_NORM, EPI_STORE>(a, s);
   return hipErrorInvalidValue;
+}
+
+template <int WB>
+hipError_t launch_w(int pro, int epi, const GemvArgs& a, hipStream_t s) {
+  const int items = (int)(a.k / 8);
+  const int nx = (items + kNT - 1) / kNT;
+  if (nx <= 1) return launch_nx<WB, 1>(pro, epi, a, s);
+  if (nx <= 2) return launch_nx<WB, 2>(pro, epi, a, s);
+  if (nx <= 3) return launch_nx<WB, 3>(pro, epi, a, s);
+  if (nx <= 5) return launch_nx<WB, 5>(pro, epi, a, s);
+  return launch_nx<WB, 7>(pro, epi, a, s);
 }
 
 }  // namespace
@@ -366,22 +421,22 @@ bool gemv_w4t_supported(int pro, int epi) {
          (pro == PRO_EMBED_NORM && epi == EPI_STORE);
 }
 
-hipError_t launch_gemv_w4t(int pro, int epi, const GemvArgs& a, hipStream_t s) {
-  if (a.k % 128 != 0 || a.n % 16 != 0 || a.k > 8 * kNT * 7) return hipErrorInvalidValue;
-  const int items = (int)(a.k / 8);
-  const int nx = (items + kNT - 1) / kNT;
-  if (nx <= 1) return launch_nx<1>(pro, epi, a, s);
-  if (nx <= 2) return launch_nx<2>(pro, epi, a, s);
-  if (nx <= 3) return launch_nx<3>(pro, epi, a, s);
-  if (nx <= 5) return launch_nx<5>(pro, epi, a, s);
-  return launch_nx<7>(pro, epi, a, s);
+int tile_chunk_k(int bits) { return bits == 4 ? Width<4>::KCH : (bits == 2 ? Width<2>::KCH : 0); }
+
+hipError_t launch_gemv_w4t(int wb, int pro, int epi, const GemvArgs& a, hipStream_t s) {
+  const int kch = tile_chunk_k(wb);
+  if (kch == 0 || a.k % kch != 0 || a.n % 16 != 0 || a.k > 8 * kNT * 7) return hipErrorInvalidValue;
+  return wb == 4 ? launch_w<4>(pro, epi, a, s) : launch_w<2>(pro, epi, a, s);
 }
 
-hipError_t launch_w4_tile(const uint8_t* codes, const uint16_t* meta, int64_t n, int64_t k, uint8_t* tcodes,
-                          uint16_t* tmeta, hipStream_t s) {
-  const int64_t items = (n / 16) * (k / 128) * 64;
+hipError_t launch_tile_codes(const uint8_t* codes, const uint16_t* meta, int64_t n, int64_t k, int bits,
+                             uint8_t* tcodes, uint16_t* tmeta, hipStream_t s) {
+  const int kch = tile_chunk_k(bits);
+  if (kch == 0 || k % kch != 0 || n % 16 != 0) return hipErrorInvalidValue;
+  const int64_t items = (n / 16) * (k / kch) * 64;
   if (items == 0) return hipSuccess;
-  SS_LAUNCH(w4_tile_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, codes, meta, n, k, tcodes,
-            tmeta);
+  const dim3 grid((unsigned)((items + 255) / 256)), block(256);
+  if (bits == 4) SS_LAUNCH(tile_codes_kernel<4>, grid, block, 0, s, codes, meta, n, k, tcodes, tmeta);
+  else SS_LAUNCH(tile_codes_kernel<2>, grid, block, 0, s, codes, meta, n, k, tcodes, tmeta);
   return hipGetLastError();
 }

@@ -31,19 +31,21 @@ struct GemvArgs {
   float* part_max;           // EPI_LOGITS: per-block max
   int32_t* part_arg;         // EPI_LOGITS: per-block argmax
   const int32_t* valid;      // optional device flag: skip everything if *valid == 0
-  int tiled;                 // 4-bit codes + meta in 16-row tiles (subspec_w4_tile)
+  int tiled;                 // codes + meta in 16-row tiles (subspec_tile_codes)
 };
 
 int gemv_max_blocks(bool w4, int64_t n, int epi);  // blocks of one launch (logits partials)
 // wb: weight width, 16 (bf16 w), 4, 3 or 2 (codes + meta; see subspec_quantize)
 hipError_t launch_gemv(int wb, int pro, int epi, const GemvArgs& a, hipStream_t s, int* blocks_out);
-// 4-bit GEMV on 16-row tiles (a.tiled; matrix cores): prologue/epilogue
-// pairs it takes, and the launch (a.n % 16 == 0, a.k % 128 == 0, a.k <= 28672)
+// 4- or 2-bit GEMV on 16-row tiles (a.tiled; matrix cores): prologue/epilogue
+// pairs it takes, and the launch (a.n % 16 == 0, a.k a multiple of the
+// width's chunk (tile_chunk_k), a.k <= 28672)
 bool gemv_w4t_supported(int pro, int epi);
-hipError_t launch_gemv_w4t(int pro, int epi, const GemvArgs& a, hipStream_t s);
-// row-major 4-bit codes + meta -> 16-row tiles (n % 16 == 0, k % 128 == 0)
-hipError_t launch_w4_tile(const uint8_t* codes, const uint16_t* meta, int64_t n, int64_t k, uint8_t* tcodes,
-                          uint16_t* tmeta, hipStream_t s);
+int tile_chunk_k(int bits);  // k per 64-byte row piece of a tile: 128 (4 bits), 256 (2 bits), 0 otherwise
+hipError_t launch_gemv_w4t(int wb, int pro, int epi, const GemvArgs& a, hipStream_t s);
+// row-major codes + meta -> 16-row tiles (bits 4 or 2; n % 16 == 0, k % tile_chunk_k(bits) == 0)
+hipError_t launch_tile_codes(const uint8_t* codes, const uint16_t* meta, int64_t n, int64_t k, int bits,
+                             uint8_t* tcodes, uint16_t* tmeta, hipStream_t s);
 
 // ------------------------------------------------------------------ GEMM (verify)
 // GEPI_PARTIAL: fp32 partial sums [split][m][n] for the caller to reduce

@@ -17,6 +17,7 @@ MATS = ("qkv", "o", "gate_up", "down")
 
 
 MAX_TILED_K = 28672
+TILE_K = {4: 128, 2: 256}  # k of one 64-byte tile chunk per code width
 
 
 class DeviceModel:
@@ -25,9 +26,9 @@ class DeviceModel:
         ``substitute_layers``: indices quantised for the draft (default: all
         layers from ``shape.n_shared`` on).  ``bits``: code width of the
         substitutes, 4, 3 or 2 (an int, or a dict layer -> width).
-        ``tiled``: keep 4-bit substitutes in the 16-row tiles of
-        subspec_w4_tile (the matrix-core draft GEMV) where the shape allows;
-        otherwise (and at 2 or 3 bits) row-major."""
+        ``tiled``: keep 4- and 2-bit substitutes in the 16-row tiles of
+        subspec_tile_codes (the matrix-core draft GEMV) where the shape
+        allows; otherwise (and at 3 bits) row-major."""
         self.shape = shape
         self.w = weights
         L = len(weights["layers"])
@@ -46,10 +47,10 @@ class DeviceModel:
                 codes = torch.empty((n, _lib.code_row_bytes(k, b)), dtype=torch.uint8, device=wt.device)
                 meta = torch.empty((n, k // 64, 2), dtype=torch.float16, device=wt.device)
                 _lib.quantize(wt, codes, meta, bits=b, stream=stream)
-                lay = int(tiled and b == 4 and n % 16 == 0 and k % 128 == 0 and k <= MAX_TILED_K)
+                lay = int(tiled and b in TILE_K and n % 16 == 0 and k % TILE_K[b] == 0 and k <= MAX_TILED_K)
                 if lay:
                     tc, tm = torch.empty_like(codes), torch.empty_like(meta)
-                    _lib.w4_tile(codes, meta, tc, tm, stream=stream)
+                    _lib.tile_codes(codes, meta, tc, tm, bits=b, stream=stream)
                     codes, meta = tc, tm
                 self.q[l][name] = (codes, meta)
                 self.layout[l][name] = lay

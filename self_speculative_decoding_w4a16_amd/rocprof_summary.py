@@ -32,11 +32,11 @@ def describe(name):
         nt = f",{m[5]}" if m[5] else ""
         return (f"gemv_kernel<{r},{wb},{pro},{epi}{nt}>",
                 f"{width} GEMV, {r} rows/wave, {_PRO.get(pro, pro)} -> {_EPI.get(epi, epi)}")
-    m = re.search(r"gemv_w4t_kernel<(\d+), (\d+), (\d+), (\d+), (\d+)>", name)
+    m = re.search(r"gemv_w4t_kernel<(\d+), (\d+), (\d+), (\d+), (\d+), (\d+)>", name)
     if m:
-        t, p, nx, pro, epi = (int(v) for v in m.groups())
-        return (f"gemv_w4t_kernel<{t},{p},{nx},{pro},{epi}>",
-                f"W4 GEMV on 16-row tiles (matrix cores), {t} tile(s)/unit, {p} chunks in flight, "
+        wb, t, p, nx, pro, epi = (int(v) for v in m.groups())
+        return (f"gemv_w4t_kernel<{wb},{t},{p},{nx},{pro},{epi}>",
+                f"W{wb} GEMV on 16-row tiles (matrix cores), {t} tile(s)/unit, {p} chunks in flight, "
                 f"{_PRO.get(pro, pro)} -> {_EPI.get(epi, epi)}")
     m = re.search(r"gemm_w4_kernel<(true|false)(?:, (true|false))?>", name)
     if m:
@@ -65,7 +65,7 @@ _ROLES = {
     "rows_merge_kernel": "verify attention: merge of many split partials (8 groups per block)",
     "rows_merge_seq_kernel": "verify attention: merge of the split partials",
     "hbm_read_kernel": "HBM read ceiling (read-only stream, measurement)",
-    "w4_tile_kernel": "4-bit codes + meta into 16-row tiles (model set-up)",
+    "tile_codes_kernel": "low-bit codes + meta into 16-row tiles (model set-up)",
     "rope_append_kernel": "verify RoPE + KV append (sums QKV split-k partials)",
     "rmsnorm_rows_kernel": "verify residual add of split-k partials + RMSNorm",
     "gemm_reduce_kernel": "lm_head split-k reduction",

@@ -51,25 +51,30 @@ def test_quantize_argument_errors():
     assert l.subspec_quantize(p, 0, 64, 64, 4, p, p, None) == _lib.EINVAL
 
 
-def test_w4_tile_and_layout_argument_errors():
+def test_tile_codes_and_layout_argument_errors():
     import ctypes
     l = _lib.lib()
     p = V(4096)
-    assert l.subspec_w4_tile(None, p, 16, 128, p, p, None) == _lib.EINVAL
-    assert l.subspec_w4_tile(p, p, 16, 128, p, None, None) == _lib.EINVAL
-    assert l.subspec_w4_tile(p, p, 8, 128, p, p, None) == _lib.ESHAPE    # n % 16
-    assert l.subspec_w4_tile(p, p, 16, 192, p, p, None) == _lib.ESHAPE   # k % 128
-    assert l.subspec_w4_tile(p, p, 0, 128, p, p, None) == _lib.EINVAL
+    assert l.subspec_tile_codes(None, p, 16, 128, 4, p, p, None) == _lib.EINVAL
+    assert l.subspec_tile_codes(p, p, 16, 128, 4, p, None, None) == _lib.EINVAL
+    assert l.subspec_tile_codes(p, p, 8, 128, 4, p, p, None) == _lib.ESHAPE     # n % 16
+    assert l.subspec_tile_codes(p, p, 16, 192, 4, p, p, None) == _lib.ESHAPE    # 4 bits: k % 128
+    assert l.subspec_tile_codes(p, p, 16, 128, 2, p, p, None) == _lib.ESHAPE    # 2 bits: k % 256
+    assert "256" in _lib.last_error()
+    assert l.subspec_tile_codes(p, p, 16, 256, 3, p, p, None) == _lib.EUNSUPPORTED
+    assert l.subspec_tile_codes(p, p, 0, 128, 4, p, p, None) == _lib.EINVAL
     g = lambda lin, *a: l.subspec_gemv(ctypes.byref(lin), *a)
     tiled = lambda n, k, bits=4, layout=1: _lib.Linear(None, p, p, n, k, bits, layout)
     assert g(tiled(16, 128, layout=2), p, None, 0.0, 0, None, p, None) == _lib.EINVAL
-    assert g(tiled(16, 128, bits=2), p, None, 0.0, 0, None, p, None) == _lib.EINVAL
-    assert "4-bit" in _lib.last_error()
-    assert g(tiled(24, 128), p, None, 0.0, 0, None, p, None) == _lib.ESHAPE    # n % 16
-    assert g(tiled(16, 192), p, None, 0.0, 0, None, p, None) == _lib.ESHAPE    # k % 128
-    assert g(tiled(48, 128), p, p, 1e-6, 2, None, p, None) == _lib.ESHAPE      # SiLU: F % 16
+    assert g(tiled(16, 256, bits=3), p, None, 0.0, 0, None, p, None) == _lib.EINVAL
+    assert "4- or 2-bit" in _lib.last_error()
+    assert g(tiled(24, 128), p, None, 0.0, 0, None, p, None) == _lib.ESHAPE     # n % 16
+    assert g(tiled(16, 192), p, None, 0.0, 0, None, p, None) == _lib.ESHAPE     # k % 128
+    assert g(tiled(16, 128, bits=2), p, None, 0.0, 0, None, p, None) == _lib.ESHAPE  # k % 256
+    assert g(tiled(48, 128), p, p, 1e-6, 2, None, p, None) == _lib.ESHAPE       # SiLU: F % 16
     ws = (ctypes.c_uint8 * 4096)()
     assert l.subspec_w4_gemm(ctypes.byref(tiled(24, 128)), p, 1, p, ws, 4096, None) == _lib.ESHAPE
+    assert l.subspec_w4_gemm(ctypes.byref(tiled(16, 256, bits=2)), p, 1, p, ws, 4096, None) == _lib.EINVAL
 
 
 def test_gemv_gemm_sample_argument_errors():

@@ -1,8 +1,8 @@
-"""4-bit substitutes in 16-row tiles: the repack is the permutation the
-header states (bit-exact), the matrix-core GEMV on tiles matches the oracle
-(RMSNorm prologue, store / residual / SiLU * up epilogues, short and long k,
-ragged last units, waves past the chunks), and the skinny GEMM reads tiles
-and rows to the same bits."""
+"""Low-bit substitutes in 16-row tiles: the repack is the permutation the
+header states (bit-exact, 4 and 2 bits), the matrix-core GEMV on tiles
+matches the oracle (RMSNorm prologue, store / residual / SiLU * up
+epilogues, short and long k, ragged last units, waves past the chunks, both
+widths), and the skinny GEMM reads 4-bit tiles and rows to the same bits."""
 import numpy as np
 import pytest
 import torch
@@ -19,27 +19,27 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-2
 
 
-def _quant(w):
+def _quant(w, bits=4):
     n, k = w.shape
-    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    codes = torch.empty((n, k * bits // 8), dtype=torch.uint8, device=w.device)
     meta = torch.empty((n, k // 64, 2), dtype=torch.float16, device=w.device)
-    _lib.quantize(w, codes, meta)
+    _lib.quantize(w, codes, meta, bits=bits)
     tc, tm = torch.empty_like(codes), torch.empty_like(meta)
-    _lib.w4_tile(codes, meta, tc, tm)
+    _lib.tile_codes(codes, meta, tc, tm, bits=bits)
     torch.cuda.synchronize()
     return codes, meta, tc, tm
 
 
-def _tile_ref(codes, meta):
+def _tile_ref(codes, meta, bits=4):
     """The tiled layout written out from its statement in include/subspec.h:
-    KiB (t, c) holds, at 16 (16 g + r), bytes 64 c + 16 g .. + 15 of row
-    16 t + r; meta dword 32 (t c_n + c) + 2 r + e is row 16 t + r's dword
-    2 c + e."""
-    n, kh = codes.shape
-    cn = kh // 64
-    tc = np.empty(n * kh, np.uint8)
-    md = meta.view(np.uint32).reshape(n, kh // 32)
-    tm = np.empty(n * kh // 32, np.uint32)
+    with e = 8 / bits groups a 64-byte chunk, KiB (t, c) holds, at
+    16 (16 g + r), bytes 64 c + 16 g .. + 15 of row 16 t + r; meta dword
+    16 e (t c_n + c) + e r + f is row 16 t + r's dword e c + f."""
+    n, rb = codes.shape
+    cn, e = rb // 64, 8 // bits
+    tc = np.empty(n * rb, np.uint8)
+    md = meta.view(np.uint32).reshape(n, -1)
+    tm = np.empty(md.size, np.uint32)
     for t in range(n // 16):
         for c in range(cn):
             b = t * cn + c
@@ -48,17 +48,18 @@ def _tile_ref(codes, meta):
                     tc[1024 * b + 16 * (16 * g + r):1024 * b + 16 * (16 * g + r) + 16] = \
                         codes[16 * t + r, 64 * c + 16 * g:64 * c + 16 * g + 16]
             for r in range(16):
-                for e in range(2):
-                    tm[32 * b + 2 * r + e] = md[16 * t + r, 2 * c + e]
+                for f in range(e):
+                    tm[16 * e * b + e * r + f] = md[16 * t + r, e * c + f]
     return tc, tm
 
 
-@pytest.mark.parametrize("n,k", [(16, 128), (48, 384), (160, 1024)])
-def test_tile_layout_bit_exact(cuda, n, k):
-    log(f"w4 tile {n}x{k}")
+@pytest.mark.parametrize("n,k,bits", [(16, 128, 4), (48, 384, 4), (160, 1024, 4), (16, 256, 2), (48, 768, 2),
+                                      (160, 1024, 2)])
+def test_tile_layout_bit_exact(cuda, n, k, bits):
+    log(f"tile {n}x{k} bits={bits}")
     w = normal_tensor((n, k), 0.02, 3, cuda)
-    codes, meta, tc, tm = _quant(w)
-    rc, rm = _tile_ref(codes.cpu().numpy(), meta.cpu().numpy().view(np.uint16))
+    codes, meta, tc, tm = _quant(w, bits)
+    rc, rm = _tile_ref(codes.cpu().numpy(), meta.cpu().numpy().view(np.uint16), bits)
     np.testing.assert_array_equal(tc.cpu().numpy().reshape(-1), rc)
     np.testing.assert_array_equal(tm.cpu().numpy().view(np.uint32).reshape(-1), rm)
 
@@ -96,20 +97,25 @@ CASES = [(512, 512, True, 0), (512, 256, True, 2), (1024, 640, False, 1), (80, 1
          (512, 14336, False, 1), (272, 28672, False, 1), (96, 12288, False, 0), (64, 6144, True, 2)]
 
 
-@pytest.mark.parametrize("n,k,norm,epilogue", CASES)
-def test_tiled_gemv_matches_oracle(cuda, n, k, norm, epilogue):
-    log(f"tiled gemv {n}x{k} norm={norm} epilogue={epilogue}")
+# 2 bits: chunks of 256 k (k = 256 is one chunk: waves past the chunks)
+CASES_2 = [(512, 256, True, 0), (512, 512, True, 2), (1024, 1280, False, 1), (80, 1024, False, 0),
+           (4608, 3584, True, 0), (3584, 18944, False, 1), (1024, 5120, True, 2), (272, 28672, False, 1)]
+
+
+@pytest.mark.parametrize("n,k,norm,epilogue,bits", [c + (4,) for c in CASES] + [c + (2,) for c in CASES_2])
+def test_tiled_gemv_matches_oracle(cuda, n, k, norm, epilogue, bits):
+    log(f"tiled gemv {n}x{k} bits={bits} norm={norm} epilogue={epilogue}")
     w = normal_tensor((n, k), 0.02, 50, cuda)
     x = normal_tensor((k,), 1.0, 51, cuda)
     g = normal_tensor((k,), 1.0, 52, cuda) if norm else None
     resid = normal_tensor((n,), 1.0, 53, cuda) if epilogue == 1 else None
-    _, _, tc, tm = _quant(w)
-    lin = _lib.linear(codes=tc, meta=tm, layout=1)
+    _, _, tc, tm = _quant(w, bits)
+    lin = _lib.linear(codes=tc, meta=tm, bits=bits, layout=1)
     y = torch.empty(n // 2 if epilogue == 2 else n, dtype=torch.bfloat16, device=cuda)
     _lib.gemv(lin, x, y, norm_w=g, eps=1e-6, epilogue=epilogue, resid=resid)
     torch.cuda.synchronize()
-    rc, rm = oq(host(w))
-    ref = _fused_ref(dequantize(rc, rm), host(x), None if g is None else host(g), 1e-6, epilogue,
+    rc, rm = oq(host(w), bits=bits)
+    ref = _fused_ref(dequantize(rc, rm, bits=bits), host(x), None if g is None else host(g), 1e-6, epilogue,
                      None if resid is None else host(resid))
     assert rel_err(host(y), ref) < TOL
 
@@ -160,11 +166,11 @@ def test_tiled_w4_gemm_equals_rows(cuda, n, k, m):
     assert torch.equal(y0, y1)
 
 
-@pytest.mark.parametrize("tiled", [True, False])
-def test_draft_step_on_either_layout_matches_oracle(cuda, tiled):
+@pytest.mark.parametrize("tiled,bits", [(True, 4), (False, 4), (True, 2)])
+def test_draft_step_on_either_layout_matches_oracle(cuda, tiled, bits):
     """One 7B-shaped substitute layer (layer 0: the embedding prologue on the
-    4-bit QKV site) through a draft step with the substitutes tiled or
-    row-major: logits within 1e-2 of the oracle either way."""
+    low-bit QKV site) through a draft step with the substitutes tiled or
+    row-major, at 4 or 2 bits: logits within 1e-2 of the oracle."""
     from oracle.model import forward
     from self_speculative_decoding_w4a16_amd.engine import SpecDecoder
     from self_speculative_decoding_w4a16_amd.model import DeviceModel
@@ -172,9 +178,9 @@ def test_draft_step_on_either_layout_matches_oracle(cuda, tiled):
     from synth.configs import QWEN7B
     from tests.helpers import oracle_model
     shape, kv_len, cap = QWEN7B.with_(n_layers=1, n_shared=0), 700, 768
-    log(f"draft step, substitutes tiled={tiled}")
+    log(f"draft step, substitutes tiled={tiled} bits={bits}")
     w = model_weights(shape, 9, cuda)
-    dm = DeviceModel(shape, w, tiled=tiled)
+    dm = DeviceModel(shape, w, tiled=tiled, bits=bits)
     assert all(v == int(tiled) for v in dm.layout[0].values())
     dec = SpecDecoder(dm, cap, 4)
     K, V = kv_history(shape.n_layers, shape.n_kv_heads, kv_len, shape.head_dim, cap, 16, cuda)
@@ -184,7 +190,8 @@ def test_draft_step_on_either_layout_matches_oracle(cuda, tiled):
     dec.reset(kv_len, tok)
     _lib.draft_step(dm.c, dec.c, 0, 0.0, None, dec.ws)
     torch.cuda.synchronize()
-    om = oracle_model(shape, w, dm.substitute_layers)
+    om = oracle_model(shape, w, [])
+    om.make_substitutes(dm.substitute_layers, bits=bits)
     kv = (host(K).astype(np.float64), host(V).astype(np.float64))
     ref = forward(om, kv, kv_len, [tok], draft=True)[0]
     assert rel_err(host(dec.draft_logits[0]), ref) < TOL
