@@ -250,7 +250,8 @@ def main():
         _lib.kv_select(dm.c, dec.c)
         torch.cuda.synchronize()
     draft_pass, verify_pass = pass_rates(dec, shape, wl, kv0, last, n_w4, sparse_keys)
-    log(f"draft step {draft_pass['avg_us']:.1f} us ({draft_pass['frac']:.3f} of peak), "
+    log(f"draft step {draft_pass['avg_us']:.1f} us ({draft_pass['frac']:.3f} of peak; "
+        f"{draft_pass['avg_us_attn_own_launch']:.1f} us with every attention in its own launch), "
         f"verify pass {verify_pass['avg_us']:.1f} us ({verify_pass['frac']:.3f})")
 
     # ---------------------------------------------------------------- kernels
@@ -276,9 +277,16 @@ def main():
             attn_bytes["attn_draft"] += sum((kv + i + 1) * kv_row for i in range(gamma))
         attn_bytes["attn_verify"] += (kv + gamma + 1) * kv_row
         kv += n + 1
+    raw = {name: _lib.profile_read(k) for k, name in enumerate(_lib.K_NAMES)}
+    # layers whose attention ran inside the QKV launch (low-bit tiled QKV,
+    # dense keys) take their share of the KV bytes there
+    n_own, n_in = raw["attn_draft"][0], raw["qkv_attn"][0]
+    own_frac = n_own / (n_own + n_in) if n_own + n_in else 1.0
+    attn_bytes["qkv_attn"] = attn_bytes["attn_draft"] * (1.0 - own_frac)
+    attn_bytes["attn_draft"] *= own_frac
     kern = {}
-    for k, name in enumerate(_lib.K_NAMES):
-        n, ms, by = _lib.profile_read(k)
+    for name in _lib.K_NAMES:
+        n, ms, by = raw[name]
         by += attn_bytes.get(name, 0.0)
         kern[name] = {"launches": n, "ms": ms, "bytes": by}
     for g, members in _lib.K_GROUPS.items():
@@ -322,6 +330,19 @@ def main():
             out.update(traffic=traffic_bytes(names[0]), avg_us=iso[names[0]]["avg_us"],
                        bytes_per_launch=iso[names[0]]["bytes_per_launch"], symbol=iso[names[0]]["symbol"])
         return out
+
+    # the draft attention inside the QKV launch: the launch's in-cycle time
+    # less the QKV GEMV's own (isolated, back to back) time
+    attn_in_qkv = None
+    if kern["qkv_attn"]["launches"] and "w4_qkv" in iso:
+        fa, q1 = kern["qkv_attn"]["avg_us"], iso["w4_qkv"]["avg_us"]
+        attn_in_qkv = {"launch_avg_us": fa, "qkv_gemv_alone_us": q1, "attn_added_us": round(fa - q1, 3),
+                       "attn_own_launch_avg_us": kern["attn_draft"]["avg_us"],
+                       "layers_per_step": round(kern["qkv_attn"]["launches"] /
+                                                max(1, kern["qkv_attn"]["launches"] +
+                                                    kern["attn_draft"]["launches"]) * shape.n_layers, 2),
+                       "draft_step_us": draft_pass["avg_us"],
+                       "draft_step_attn_own_launch_us": draft_pass.get("avg_us_attn_own_launch")}
 
     ceiling = stream_ceiling(dev)
     log(f"HBM read ceiling: {ceiling['achieved']} GB/s over {ceiling['bytes'] >> 30} GiB")
@@ -419,6 +440,7 @@ def main():
         "roofline_verify_pass": verify_pass,
         "roofline_draft_step": draft_pass,
         "roofline_attn_draft": roof("attn_draft"),
+        "attn_in_qkv_launch": attn_in_qkv,
         "stream_ceiling": ceiling,
         "isolated_gemv": iso,
         "cpu_baseline": cpu,
@@ -569,7 +591,7 @@ def isolated_gemvs(dm, shape, dev, reps=3, only=None, graph=True):
             if lay:  # the tiled GEMV: <width, tiles, chunks in flight, x items per thread, prologue, epilogue>
                 nx = next(v for v in (1, 2, 3, 5, 7) if v * 8 * 512 >= k)
                 tp = "1,4" if epi == 1 else ("2,3" if epi == 0 else "2,2")
-                symbol = f"gemv_w4t_kernel<4,{tp},{nx},{1 if norm else 0},{epi}>"
+                symbol = f"gemv_w4t_kernel<4,{tp},{nx},{1 if norm else 0},{epi},0>"
             else:
                 symbol = sym.format(r=r, w="4" if w4 else "16")
             out[f"{kind}_{site}"] = {"avg_us": round(us, 3), "bytes_per_launch": round(by),
@@ -649,6 +671,11 @@ def pass_rates(dec, shape, wl, kv0, last, n_w4, sparse_keys=None):
     draft_b, verify_b, _, _, _ = model_bytes(shape, n_w4, d_keys, kv0 + gamma + 1)
     u = dec.ud_buf if wl.draft_temp > 0 else None
     t_d = replay_us(lambda: _lib.draft_step(dec.model.c, dec.c, 0, dec.draft_temp, u, dec.ws))
+    # the same step with every layer's attention in a launch of its own
+    dec.reset(kv0, last)
+    dec.c.attn_own_launch = 1
+    t_d_own = replay_us(lambda: _lib.draft_step(dec.model.c, dec.c, 0, dec.draft_temp, u, dec.ws))
+    dec.c.attn_own_launch = 0
     dec.reset(kv0, last)
     t_v = replay_us(dec.verify)
     dec.reset(kv0, last)
@@ -656,7 +683,9 @@ def pass_rates(dec, shape, wl, kv0, last, n_w4, sparse_keys=None):
     _, _, _, bf, _ = model_bytes(shape, n_w4, 0, 0)
     params = bf / 2 * shape.n_layers + shape.vocab * shape.hidden
     tflops = 2.0 * params * (gamma + 1) / (t_v * 1e-6) / 1e12
-    return (hbm(draft_b, t_d, "draft step (every launch of one draft token, graph-replayed)"),
+    draft = hbm(draft_b, t_d, "draft step (every launch of one draft token, graph-replayed)")
+    draft["avg_us_attn_own_launch"] = round(t_d_own, 3)
+    return (draft,
             hbm(verify_b, t_v, f"verify pass ({gamma + 1} positions, every launch, graph-replayed)",
                 mfma_tflops=round(tflops, 2), mfma_frac=round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)))
 

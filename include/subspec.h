@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SUBSPEC_ABI_VERSION 6
+#define SUBSPEC_ABI_VERSION 7
 
 enum {
   SUBSPEC_OK = 0,
@@ -61,6 +61,10 @@ enum {
   SUBSPEC_EUNSUPPORTED = -5, /* a parameter value the library does not handle */
   SUBSPEC_EWORKSPACE = -6    /* workspace NULL or smaller than required       */
 };
+
+/* Byte offset in a workspace of the device word whose bit 0 records a
+ * bounded cross-block wait that gave up (see subspec_draft_step). */
+#define SUBSPEC_WS_WAIT_FAULT_OFFSET 65408
 
 /* status bits written by subspec_reject */
 enum {
@@ -173,6 +177,10 @@ typedef struct {
   const int32_t *draft_len; /* device int32 or NULL: with the entropy-adaptive
                                draft length (subspec_control), draft steps
                                with step >= *draft_len are skipped (token -1) */
+  int32_t attn_own_launch;  /* host flag: 0 -> a draft step runs a layer's
+                               attention in the QKV projection's launch where
+                               it can (see subspec_draft_step); nonzero -> in
+                               a launch of its own (same results, bit for bit) */
 } subspec_state;
 
 /* Bytes of workspace needed for calls on `m` with at most `max_tokens`
@@ -240,7 +248,16 @@ int subspec_tile_codes(const uint8_t *codes, const uint16_t *meta, int64_t n, in
  * CDF of softmax(logits / draft_temp) at u = u_codes[step] / 2^24
  * ([SSR] section 3.4: sharpened draft).  u_codes: device uint32 [> step].
  * Needs kv_len + step < capacity (checked on the device: out-of-range
- * positions are skipped and tokens[step+1] is set to -1). */
+ * positions are skipped and tokens[step+1] is set to -1).
+ * On a layer whose QKV substitute is 4- or 2-bit in 16-row tiles, with dense
+ * keys (use_index == 0), hidden size <= 8192 and capacity <= 2048 keys per
+ * 8 key splits (two 16-key chunks a wave of the per-head attention), the
+ * attention runs in the QKV GEMV's launch unless st->attn_own_launch is set:
+ * extra blocks wait for the counts the GEMV blocks leave in the workspace
+ * once a head's q/k/v rows are stored.  Those waits are bounded (0.2 s); a
+ * wait that gives up sets bit 0 of the workspace word at byte offset
+ * SUBSPEC_WS_WAIT_FAULT_OFFSET (the step's results are then undefined and
+ * the workspace must be re-initialised with subspec_workspace_init). */
 int subspec_draft_step(const subspec_model *m, const subspec_state *st, int32_t step,
                        float draft_temp, const uint32_t *u_codes, void *ws, size_t ws_bytes,
                        void *stream);
@@ -635,7 +652,9 @@ enum {
   SUBSPEC_K_MISC = 18,         /* norms, embedding, KV bookkeeping                 */
   SUBSPEC_K_SCORES = 19,       /* verify importance scores (sparse drafting)       */
   SUBSPEC_K_SELECT = 20,       /* sparse index rebuild                             */
-  SUBSPEC_K_CLASSES = 21
+  SUBSPEC_K_QKV_ATTN = 21,     /* draft QKV GEMV on low-bit tiles with the layer's
+                                  attention in the same launch                      */
+  SUBSPEC_K_CLASSES = 22
 };
 
 /* Start recording: from now on every kernel this library launches, on any

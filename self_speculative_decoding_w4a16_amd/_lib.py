@@ -56,7 +56,7 @@ class State(ctypes.Structure):
                 ("kv_score", c_void_p), ("kv_index", c_void_p), ("kv_index_len", c_void_p),
                 ("index_cap", c_int32), ("use_index", c_int32),
                 ("n_sink", c_int32), ("n_recent", c_int32), ("score_window", c_int32),
-                ("budget_permille", c_int32), ("draft_len", c_void_p)]
+                ("budget_permille", c_int32), ("draft_len", c_void_p), ("attn_own_launch", c_int32)]
 
 
 class BatchState(ctypes.Structure):
@@ -146,7 +146,7 @@ _SIGS = {
 K_NAMES = ("w4_qkv", "w4_o", "w4_gate_up", "w4_down",
            "bf16_qkv", "bf16_o", "bf16_gate_up", "bf16_down", "lm_head",
            "gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "gemm_lm_head",
-           "attn_draft", "attn_verify", "sample", "reject", "misc", "scores", "select")
+           "attn_draft", "attn_verify", "sample", "reject", "misc", "scores", "select", "qkv_attn")
 K = {name: i for i, name in enumerate(K_NAMES)}
 # Groups of classes: every draft GEMV on a 4-bit substitute, every draft GEMV
 # on bf16 weights, and every verify GEMM.

@@ -50,6 +50,12 @@ constexpr size_t kRejectBatchCounterOff = 32 * 1024;  // batched rejection: one 
 constexpr int kMaxRejectBatch = 4096;                   // its counters fill [32 KiB, 48 KiB)
 constexpr size_t kAttnCounterOff = 20 * 1024;  // draft attention: one per query head (<= 224)
 constexpr size_t kControlCounterOff = 16 * 1024 + 512;  // draft-length controller
+// draft step, QKV GEMV and attention in one launch: a count per 128-row group
+// of the QKV output, one a 128-byte line, the give-up word in the last line,
+// [48 KiB, 64 KiB)
+constexpr size_t kQkvReadyOff = 48 * 1024;
+static_assert(kQkvReadyOff + 4 * kReadyStride * kReadyLines == kCounterBytes, "ready lines");
+static_assert(kQkvReadyOff + 4 * kReadyStride * (kReadyLines - 1) == SUBSPEC_WS_WAIT_FAULT_OFFSET, "give-up word");
 constexpr int kMaxTokens = 64;
 constexpr int kMaxTreeK = 16;       // chains of a static tree (rows of a draft level: the 4-bit GEMM's m)
 constexpr int kMaxTreeD = 64;       // depth of a static tree
@@ -206,6 +212,7 @@ int check_state(const subspec_model* m, const subspec_state* st) {
 struct FwdWs {
   uint32_t* sample_counter;
   uint32_t* attn_counters;
+  uint32_t* qkv_ready;  // kReadyLines lines: the n_q + 2 n_kv counts, the give-up word last
   uint16_t *h, *xn, *qkv, *qrot, *attn, *act;
   uint16_t* gu;  // rows forward on 4-bit weights: gate/up outputs [mt][2F] before SiLU*up
   float* attn_part;
@@ -242,6 +249,7 @@ size_t carve_fwd(const subspec_model* m, int mt, int cap, void* ws, FwdWs* o) {
   char* base = (char*)ws;
   w.sample_counter = base ? (uint32_t*)(base + kSampleCounterOff) : nullptr;
   w.attn_counters = base ? (uint32_t*)(base + kAttnCounterOff) : nullptr;
+  w.qkv_ready = base ? (uint32_t*)(base + kQkvReadyOff) : nullptr;
   c.off = kCounterBytes;
   const int64_t H = m->hidden, F = m->ffn, qd = (int64_t)m->n_q_heads * m->head_dim;
   const int64_t qkv = (int64_t)(m->n_q_heads + 2 * m->n_kv_heads) * m->head_dim;
@@ -638,10 +646,7 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
     a.h_out = w.h;
     a.y = w.qkv;
     a.valid = w.valid;
-    {
-      prof::Scope ps(gemv_class(L.qkv_d, 0), gemv_bytes(L.qkv_d, qkv, false), s);
-      HIPCHK(launch_gemv(lin_bits(L.qkv_d), l == 0 ? PRO_EMBED_NORM : PRO_NORM, EPI_STORE, a, s, nullptr));
-    }
+    const int qkv_pro = l == 0 ? PRO_EMBED_NORM : PRO_NORM;
 
     AttnArgs at{};
     at.qkv = w.qkv;
@@ -677,9 +682,25 @@ int subspec_draft_step(const subspec_model* m, const subspec_state* st, int32_t 
     at.head_splits = std::min(std::min(draft_head_splits(at.max_keys), w.part_recs),
                               std::max(1, compute_units() / std::max(1, m->n_q_heads)));
     at.counters = w.attn_counters;
-    {
-      prof::Scope ps(SUBSPEC_K_ATTN_DRAFT, 0.0, s);
-      HIPCHK(launch_decode_attention(at, w.valid, s));
+
+    // the attention inside the QKV launch: low-bit tiled QKV weights, dense
+    // keys, at most two 16-key chunks a wave
+    const int ring = draft_head_ring(at);
+    const bool fused = !st->attn_own_launch && !sparse && a.tiled && (ring == 1 || ring == 2) &&
+                       m->n_q_heads + 2 * m->n_kv_heads < kReadyLines &&
+                       qkv_attn_supported(lin_bits(L.qkv_d), qkv_pro, qkv, H);
+    if (fused) {
+      prof::Scope ps(SUBSPEC_K_QKV_ATTN, gemv_bytes(L.qkv_d, qkv, false), s);
+      HIPCHK(launch_qkv_attn(lin_bits(L.qkv_d), qkv_pro, a, at, ring, w.qkv_ready, s));
+    } else {
+      {
+        prof::Scope ps(gemv_class(L.qkv_d, 0), gemv_bytes(L.qkv_d, qkv, false), s);
+        HIPCHK(launch_gemv(lin_bits(L.qkv_d), qkv_pro, EPI_STORE, a, s, nullptr));
+      }
+      {
+        prof::Scope ps(SUBSPEC_K_ATTN_DRAFT, 0.0, s);
+        HIPCHK(launch_decode_attention(at, w.valid, s));
+      }
     }
 
     GemvArgs o{};

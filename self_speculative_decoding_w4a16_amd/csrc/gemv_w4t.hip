@@ -34,6 +34,7 @@
 //    computed in the prologue of every block, its loads issued before the
 //    first chunks so that their wait covers no weight load.
 #include "common.h"
+#include "draft_attn.h"
 #include "internal.h"
 #include "profile.h"
 
@@ -74,8 +75,26 @@ struct TSlot {
 
 // WB-bit codes, T tiles per unit, P chunks in flight per wave, NX prologue
 // items (8 values of x) per thread: K <= 8 * kNT * NX.
-template <int WB, int T, int P, int NX, int PRO, int EPI>
-__global__ __launch_bounds__(kNT) void gemv_w4t_kernel(GemvArgs a, int G) {
+//
+// DQR > 0: the draft step's QKV projection and its attention in one launch.
+// Blocks [0, G) run the GEMV, storing its rows with agent-coherent stores and
+// counting each 16-row tile into the count of its 128-row group once those
+// stores are
+// complete; blocks G + S hq + s run the attention of query head hq over key
+// split s (draft_attn.h, DQR chunks in flight per wave), which waits for the
+// counts of the rows it reads.  The GEMV blocks come first in the grid and
+// wait for nothing.
+template <int WB, int T, int P, int NX, int PRO, int EPI, int DQR>
+__global__ __launch_bounds__(kNT) void gemv_w4t_kernel(GemvArgs a, int G, AttnArgs at, uint32_t* ready) {
+  constexpr bool SIG = DQR > 0;
+  static_assert(!SIG || (EPI == EPI_STORE && kNT == DQW * SS_WAVE), "the attention rides on the store epilogue");
+  if constexpr (SIG) {
+    if ((int)blockIdx.x >= G) {
+      const int j = (int)blockIdx.x - G, S = at.head_splits;
+      draft_attn_head<false, DQR, true>(at, a.valid, j / S, j - (j / S) * S, S, ready);
+      return;
+    }
+  }
   using Wd = Width<WB>;
   extern __shared__ __align__(16) unsigned char smem[];
   const int K = (int)a.k;
@@ -313,7 +332,23 @@ __global__ __launch_bounds__(kNT) void gemv_w4t_kernel(GemvArgs a, int G) {
 #pragma unroll
           for (int q = 0; q < kW; ++q) v += rb[q * 16 * T + tid];
           if (EPI == EPI_RESID) v = ss::bf2f(a.resid[row]) + v;
-          a.y[row] = ss::f2bf(v);
+          if constexpr (SIG)
+            __hip_atomic_store(a.y + row, ss::f2bf(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          else
+            a.y[row] = ss::f2bf(v);
+        }
+      }
+      if constexpr (SIG) {
+        // the unit's rows are stored by wave 0: once they are complete at the
+        // agent coherence point, each tile's 16 rows are counted in
+        if (w == 0) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          if (lane < 16 * T && (lane & 15) == 0) {
+            const int64_t row = tile_row(cjj, lane >> 4);
+            if (row < a.n)
+              __hip_atomic_fetch_add(ready + kReadyStride * (int)(row / D), 16u, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+          }
         }
       }
       ci = 0;
@@ -376,7 +411,8 @@ hipError_t launch_t(const GemvArgs& a, hipStream_t s) {
   const int units = EPI == EPI_SILU ? (int)(a.n / 16) : (int)((a.n + 16 * T - 1) / (16 * T));
   // two blocks per compute unit: 16 waves of at most 128 VGPRs
   const int G = std::max(1, std::min(units, 2 * w4t_cus()));
-  SS_LAUNCH((gemv_w4t_kernel<WB, T, P, NX, PRO, EPI>), dim3((unsigned)G), dim3(kNT), lds, s, a, G);
+  SS_LAUNCH((gemv_w4t_kernel<WB, T, P, NX, PRO, EPI, 0>), dim3((unsigned)G), dim3(kNT), lds, s, a, G, AttnArgs{},
+            nullptr);
   return hipGetLastError();
 }
 
@@ -413,7 +449,43 @@ hipError_t launch_w(int pro, int epi, const GemvArgs& a, hipStream_t s) {
   return launch_nx<WB, 7>(pro, epi, a, s);
 }
 
+template <int WB, int NX, int PRO>
+hipError_t launch_qa(int dqr, const GemvArgs& a, const AttnArgs& at, uint32_t* ready, hipStream_t s) {
+  constexpr int T = 2;
+  const int K = (int)a.k;
+  const size_t lds = (size_t)(2 * K + 4 * (K / 64) + kZero) + 4 * (2 * kW * 16 * T + kW);
+  const int units = (int)((a.n + 16 * T - 1) / (16 * T));
+  const int G = std::max(1, std::min(units, 2 * w4t_cus()));
+  const dim3 grid((unsigned)(G + at.n_q * at.head_splits)), block(kNT);
+  if (dqr == 1) SS_LAUNCH((gemv_w4t_kernel<WB, T, 3, NX, PRO, EPI_STORE, 1>), grid, block, lds, s, a, G, at, ready);
+  else SS_LAUNCH((gemv_w4t_kernel<WB, T, 3, NX, PRO, EPI_STORE, 2>), grid, block, lds, s, a, G, at, ready);
+  return hipGetLastError();
+}
+
+template <int WB, int NX>
+hipError_t launch_qa_pro(int pro, int dqr, const GemvArgs& a, const AttnArgs& at, uint32_t* ready, hipStream_t s) {
+  if (pro == PRO_NORM) return launch_qa<WB, NX, PRO_NORM>(dqr, a, at, ready, s);
+  if (pro == PRO_EMBED_NORM) return launch_qa<WB, NX, PRO_EMBED_NORM>(dqr, a, at, ready, s);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+bool qkv_attn_supported(int wb, int pro, int64_t n, int64_t k) {
+  const int kch = tile_chunk_k(wb);
+  return (wb == 4 || wb == 2) && (pro == PRO_NORM || pro == PRO_EMBED_NORM) && k % kch == 0 && n % D == 0 &&
+         (k / 8 + kNT - 1) / kNT <= 2;
+}
+
+hipError_t launch_qkv_attn(int wb, int pro, const GemvArgs& a, const AttnArgs& at, int dqr, uint32_t* ready,
+                           hipStream_t s) {
+  if (!a.tiled || !qkv_attn_supported(wb, pro, a.n, a.k) || (dqr != 1 && dqr != 2) || at.head_splits < 1 ||
+      a.n != (int64_t)(at.n_q + 2 * at.n_kv) * D)
+    return hipErrorInvalidValue;
+  const int nx = (int)((a.k / 8 + kNT - 1) / kNT);
+  if (wb == 4) return nx <= 1 ? launch_qa_pro<4, 1>(pro, dqr, a, at, ready, s) : launch_qa_pro<4, 2>(pro, dqr, a, at, ready, s);
+  return nx <= 1 ? launch_qa_pro<2, 1>(pro, dqr, a, at, ready, s) : launch_qa_pro<2, 2>(pro, dqr, a, at, ready, s);
+}
 
 bool gemv_w4t_supported(int pro, int epi) {
   return (pro == PRO_X && (epi == EPI_STORE || epi == EPI_RESID)) ||

@@ -147,6 +147,24 @@ int decode_attn_keys_per_split();  // verify rows
 int verify_attn_split_keys(int cap, int n_kv, int rows_x_group);
 int draft_attn_keys_per_split();   // draft step
 int draft_head_splits(int max_keys);  // key splits per query head of the per-head kernel
+// Chunks of 16 keys per wave the per-head draft attention keeps in flight
+// (1-3) for a launch, or 0 if the launch does not take the per-head form.
+int draft_head_ring(const AttnArgs& a);
+// The draft step's QKV GEMV on 4- or 2-bit tiles (prologue PRO_NORM or
+// PRO_EMBED_NORM, store epilogue; a.n = (n_q + 2 n_kv) 128) and the
+// per-head draft attention over dense keys (ring dqr 1 or 2) in one launch;
+// qkv_attn_supported tells the GEMV shapes it takes (k up to 8192).  ready:
+// kReadyLines 128-byte lines, the count of 128-row group g of the QKV output
+// (g < n_q + 2 n_kv < kReadyLines) at word kReadyStride g, zero on entry and
+// left zero; bit 0 of the last line's first word is set if a wait of the
+// attention blocks gave up.  (Counts sharing a line made the launch 21 us
+// instead of 11.8 at the 7B shape: the pollers and the GEMV's atomics meet
+// on one line.)
+constexpr int kReadyStride = 32;  // words: one count per 128-byte line
+constexpr int kReadyLines = 128;
+bool qkv_attn_supported(int wb, int pro, int64_t n, int64_t k);
+hipError_t launch_qkv_attn(int wb, int pro, const GemvArgs& a, const AttnArgs& at, int dqr, uint32_t* ready,
+                           hipStream_t s);
 // m query rows at positions kv_len + pos_offset + j (q_rot and the cache already
 // written by rope_append): per-row split partials, then a merge into out.
 hipError_t launch_rows_attention(const AttnArgs& a, hipStream_t s);

@@ -32,12 +32,14 @@ def describe(name):
         nt = f",{m[5]}" if m[5] else ""
         return (f"gemv_kernel<{r},{wb},{pro},{epi}{nt}>",
                 f"{width} GEMV, {r} rows/wave, {_PRO.get(pro, pro)} -> {_EPI.get(epi, epi)}")
-    m = re.search(r"gemv_w4t_kernel<(\d+), (\d+), (\d+), (\d+), (\d+), (\d+)>", name)
+    m = re.search(r"gemv_w4t_kernel<(\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)>", name)
     if m:
-        wb, t, p, nx, pro, epi = (int(v) for v in m.groups())
-        return (f"gemv_w4t_kernel<{wb},{t},{p},{nx},{pro},{epi}>",
-                f"W{wb} GEMV on 16-row tiles (matrix cores), {t} tile(s)/unit, {p} chunks in flight, "
+        wb, t, p, nx, pro, epi, dqr = (int(v) for v in m.groups())
+        role = (f"W{wb} GEMV on 16-row tiles (matrix cores), {t} tile(s)/unit, {p} chunks in flight, "
                 f"{_PRO.get(pro, pro)} -> {_EPI.get(epi, epi)}")
+        if dqr:
+            role += f", with the layer's draft attention in the same launch ({dqr} K/V chunk(s) a wave)"
+        return f"gemv_w4t_kernel<{wb},{t},{p},{nx},{pro},{epi},{dqr}>", role
     m = re.search(r"gemm_w4_kernel<(true|false)(?:, (true|false))?>", name)
     if m:
         tl = m[2] == "true"

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared():
         assert hasattr(l, name), name
     assert set(_declared()) == set(_lib.EXPORTS)
-    assert _lib.abi_version() == 6  # subspec_linear.layout (16-row tiles)
+    assert _lib.abi_version() == 7  # subspec_state.attn_own_launch
 
 
 V = ctypes.c_void_p
