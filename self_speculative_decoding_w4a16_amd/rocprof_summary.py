@@ -40,11 +40,12 @@ def describe(name):
         if dqr:
             role += f", with the layer's draft attention in the same launch ({dqr} K/V chunk(s) a wave)"
         return f"gemv_w4t_kernel<{wb},{t},{p},{nx},{pro},{epi},{dqr}>", role
-    m = re.search(r"gemm_w4_kernel<(true|false)(?:, (true|false))?>", name)
+    m = re.search(r"gemm_w4_kernel<(true|false), (true|false), (true|false)>", name)
     if m:
-        tl = m[2] == "true"
-        return (f"gemm_w4_kernel<{m[1]}{',' + m[2] if m[2] else ''}>",
-                "W4 skinny GEMM (matrix cores, <= 16 positions" + (", tiled" if tl else "") + "), " +
+        tl, half = m[2] == "true", m[3] == "true"
+        return (f"gemm_w4_kernel<{m[1]},{m[2]},{m[3]}>",
+                "W4 skinny GEMM (matrix cores, " + ("<= 8" if half else "<= 16") + " positions" +
+                (", tiled" if tl else "") + "), " +
                 ("SiLU*up epilogue" if m[1] == "true" else "store / split-k partials"))
     m = re.search(r"gemm_kernel<(\d+), (\d+), (\d+)>", name)
     if m:
