@@ -558,9 +558,9 @@ __global__ __launch_bounds__(256) void draft_attn_kernel(AttnArgs a, const int32
 
 // The per-head draft attention (short contexts): grid (query head, split),
 // the body in draft_attn.h.
-template <bool SPARSE, int DQR>
+template <bool SPARSE, int DQR, bool REFILL>
 __global__ __launch_bounds__(DQW * 64) void draft_attn_head_kernel(AttnArgs a, const int32_t* valid) {
-  draft_attn_head<SPARSE, DQR, false>(a, valid, blockIdx.x, blockIdx.y, gridDim.y, nullptr);
+  draft_attn_head<SPARSE, DQR, REFILL, false>(a, valid, blockIdx.x, blockIdx.y, gridDim.y, nullptr);
 }
 
 
@@ -1052,19 +1052,23 @@ hipError_t launch_decode_attention(const AttnArgs& a, const int32_t* valid, hipS
   if (a.max_keys <= DQ_MAXKEYS) {
     const int S = a.head_splits;
     if (S < 1 || S > DQ_MAXSPLITS || (S > 1 && (!a.counters || !a.part))) return hipErrorInvalidValue;
-    // chunks of 16 keys per wave in the first round: what the bound on keys fills, 1 to 3
+    // chunks of 16 keys per wave: what the bound on keys fills; up to 3 all
+    // loaded up front, beyond that a ring of 3 refilled after use
     const int per_wave = (a.max_keys + 16 * DQW * S - 1) / (16 * DQW * S);
     const dim3 grid(a.n_q, S), block(DQW * 64);
     const bool sp = a.index != nullptr;
     if (per_wave <= 1) {
-      if (sp) SS_LAUNCH((draft_attn_head_kernel<true, 1>), grid, block, 0, s, a, valid);
-      else SS_LAUNCH((draft_attn_head_kernel<false, 1>), grid, block, 0, s, a, valid);
+      if (sp) SS_LAUNCH((draft_attn_head_kernel<true, 1, false>), grid, block, 0, s, a, valid);
+      else SS_LAUNCH((draft_attn_head_kernel<false, 1, false>), grid, block, 0, s, a, valid);
     } else if (per_wave == 2) {
-      if (sp) SS_LAUNCH((draft_attn_head_kernel<true, 2>), grid, block, 0, s, a, valid);
-      else SS_LAUNCH((draft_attn_head_kernel<false, 2>), grid, block, 0, s, a, valid);
+      if (sp) SS_LAUNCH((draft_attn_head_kernel<true, 2, false>), grid, block, 0, s, a, valid);
+      else SS_LAUNCH((draft_attn_head_kernel<false, 2, false>), grid, block, 0, s, a, valid);
+    } else if (per_wave == 3) {
+      if (sp) SS_LAUNCH((draft_attn_head_kernel<true, 3, false>), grid, block, 0, s, a, valid);
+      else SS_LAUNCH((draft_attn_head_kernel<false, 3, false>), grid, block, 0, s, a, valid);
     } else {
-      if (sp) SS_LAUNCH((draft_attn_head_kernel<true, 3>), grid, block, 0, s, a, valid);
-      else SS_LAUNCH((draft_attn_head_kernel<false, 3>), grid, block, 0, s, a, valid);
+      if (sp) SS_LAUNCH((draft_attn_head_kernel<true, 3, true>), grid, block, 0, s, a, valid);
+      else SS_LAUNCH((draft_attn_head_kernel<false, 3, true>), grid, block, 0, s, a, valid);
     }
     return hipGetLastError();
   }

@@ -48,7 +48,10 @@ __device__ __forceinline__ DraftKeys draft_keys(const AttnArgs& a, int hk) {
 // the keys it sees, rescaled only when a score exceeds m by more than 8 (in
 // log2 units; the weights stay below 2^8); lanes and waves are combined once
 // at the end.  Loads run DQR (1-3) chunks ahead in a ring named statically,
-// the first ones issued before kv_len is known (dense keys).  Every
+// the first ones issued before kv_len is known (dense keys); a buffer is
+// refilled after use only where a wave has more chunks than the ring holds
+// (REFILL: more than 3 a wave), else every chunk is loaded up front and no
+// load is issued past the wave's last chunk.  Every
 // block of a kv head rotates the new key itself (its score needs it); split 0
 // scores it, and split 0 of the group's first head appends the new K/V to the
 // cache (no block reads that slot from memory).  With S > 1 each block writes
@@ -88,7 +91,7 @@ __device__ __forceinline__ float oct_sum(float v) {
 // flight per wave (1-3, no more than the launch's bound on keys fills).
 // Both are compile-time so that every load is issued on every path and each
 // wait covers exactly what it needs.
-template <bool SPARSE, int DQR, bool FUSED>
+template <bool SPARSE, int DQR, bool REFILL, bool FUSED>
 __device__ __forceinline__ void draft_attn_head(const AttnArgs& a, const int32_t* valid, int hq, int split, int S,
                                                 uint32_t* ready) {
   static_assert(!(SPARSE && FUSED), "the in-launch form attends over the dense cache only");
@@ -269,8 +272,10 @@ __device__ __forceinline__ void draft_attn_head(const AttnArgs& a, const int32_t
       const int c = c_first + j * c_step;
       load_chunk(clamp_chunk(c), ring[j]);
     }
+    if (REFILL) {
 #pragma unroll
-    for (int j = 0; j < DQR; ++j) load_entries(clamp_chunk(c_first + (j + DQR) * c_step), nidx[j]);
+      for (int j = 0; j < DQR; ++j) load_entries(clamp_chunk(c_first + (j + DQR) * c_step), nidx[j]);
+    }
   }
 
   __syncthreads();
@@ -328,22 +333,32 @@ __device__ __forceinline__ void draft_attn_head(const AttnArgs& a, const int32_t
       update(sa, sb, b.v[0], b.v[1], b.v[2], b.v[3]);
     }
   };
-  // each buffer is refilled with chunk c + DQR * DQW right after use; the last
-  // pass may run past the wave's chunks: those are skipped, their loads (of
-  // chunk 0) still issued, so the loads in flight are the same on every path
-  for (int c = c_first; c < n_chunks; c += DQR * c_step) {
+  if constexpr (REFILL) {
+    // each buffer is refilled with chunk c + DQR * DQW right after use; the last
+    // pass may run past the wave's chunks: those are skipped, their loads (of
+    // chunk 0) still issued, so the loads in flight are the same on every path
+    for (int c = c_first; c < n_chunks; c += DQR * c_step) {
+#pragma unroll
+      for (int j = 0; j < DQR; ++j) {
+        const int cj = c + j * c_step, cn = cj + DQR * c_step;
+        if (j == 0 || cj < n_chunks) step(cj, ring[j]);
+        if (sparse) {
+          const int cc = clamp_chunk(cn);
+          const int e0 = nidx[j][0], e1 = nidx[j][1];
+          load_rows(cc, ring[j], [&](int t) { return sparse_row_of(t, (t - cc * KW) < 8 ? e0 : e1); });
+          load_entries(clamp_chunk(cn + DQR * c_step), nidx[j]);
+        } else {
+          load_chunk(clamp_chunk(cn), ring[j]);
+        }
+      }
+    }
+  } else {
+    // the launch's bound on keys gives every wave at most DQR chunks, all of
+    // them in the ring already: one pass and no refill loads
 #pragma unroll
     for (int j = 0; j < DQR; ++j) {
-      const int cj = c + j * c_step, cn = cj + DQR * c_step;
-      if (j == 0 || cj < n_chunks) step(cj, ring[j]);
-      if (sparse) {
-        const int cc = clamp_chunk(cn);
-        const int e0 = nidx[j][0], e1 = nidx[j][1];
-        load_rows(cc, ring[j], [&](int t) { return sparse_row_of(t, (t - cc * KW) < 8 ? e0 : e1); });
-        load_entries(clamp_chunk(cn + DQR * c_step), nidx[j]);
-      } else {
-        load_chunk(clamp_chunk(cn), ring[j]);
-      }
+      const int cj = c_first + j * c_step;
+      if (cj < n_chunks) step(cj, ring[j]);
     }
   }
   // the new key, from LDS: the 8 lanes of key group 0 in wave 0 of split 0

@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kNT) void gemv_w4t_kernel(GemvArgs a, int G, AttnAr
   if constexpr (SIG) {
     if ((int)blockIdx.x >= G) {
       const int j = (int)blockIdx.x - G, S = at.head_splits;
-      draft_attn_head<false, DQR, true>(at, a.valid, j / S, j - (j / S) * S, S, ready);
+      draft_attn_head<false, DQR, false, true>(at, a.valid, j / S, j - (j / S) * S, S, ready);
       return;
     }
   }
