@@ -250,9 +250,10 @@ int subspec_tile_codes(const uint8_t *codes, const uint16_t *meta, int64_t n, in
  * Needs kv_len + step < capacity (checked on the device: out-of-range
  * positions are skipped and tokens[step+1] is set to -1).
  * On a layer whose QKV substitute is 4- or 2-bit in 16-row tiles, with dense
- * keys (use_index == 0), hidden size <= 8192 and capacity <= 2048 keys per
- * 8 key splits (two 16-key chunks a wave of the per-head attention), the
- * attention runs in the QKV GEMV's launch unless st->attn_own_launch is set:
+ * keys (use_index == 0), hidden size <= 8192 and capacity <= 256 keys per
+ * key split of the per-head attention (two 16-key chunks a wave; 2048 keys
+ * at 8 splits), the attention runs in the QKV GEMV's launch unless
+ * st->attn_own_launch is set:
  * extra blocks wait for the counts the GEMV blocks leave in the workspace
  * once a head's q/k/v rows are stored.  Those waits are bounded (0.2 s); a
  * wait that gives up sets bit 0 of the workspace word at byte offset
